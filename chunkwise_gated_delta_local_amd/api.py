@@ -1,0 +1,215 @@
+"""Thin ctypes binding of ``libgdr.so`` (include/gdr.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's HIP kernels. If
+the library has not been built, every call raises immediately: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_build", "libgdr.so")
+_lib = None
+
+GDR_F32, GDR_BF16 = 0, 1
+NUM_STAGES = 6
+STAGE_NAMES = ("chunk_table", "gate_cumsum", "build_solve", "wu", "state", "output")
+_DTYPES = {torch.float32: GDR_F32, torch.bfloat16: GDR_BF16}
+
+EXPORTED = ("gdr_validate", "gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_debug",
+            "gdr_chunk_fwd_stage_times", "gdr_status_string", "gdr_last_error_message")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seq_len", ctypes.c_int64),
+                ("num_qk_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
+                ("head_dim_qk", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+                ("chunk_size", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("beta_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32)]
+
+
+class Intermediates(ctypes.Structure):
+    _fields_ = [("G", ctypes.c_void_p), ("A", ctypes.c_void_p), ("W", ctypes.c_void_p),
+                ("U", ctypes.c_void_p), ("KT", ctypes.c_void_p), ("H", ctypes.c_void_p),
+                ("VN", ctypes.c_void_p), ("num_chunks", ctypes.c_int64)]
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("gdr status %d: %s" % (status, message))
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libgdr.so; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libgdr.so is not built (%s); run __graft_entry__.build() first" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, PP = ctypes.c_void_p, ctypes.POINTER(Problem)
+    fwd_args = [PP, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.gdr_validate.argtypes = [PP, P]
+    lib.gdr_chunk_fwd_workspace_size.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdr_chunk_fwd.argtypes = fwd_args
+    lib.gdr_chunk_fwd_debug.argtypes = fwd_args + [ctypes.POINTER(Intermediates)]
+    lib.gdr_chunk_fwd_stage_times.argtypes = fwd_args + [ctypes.POINTER(ctypes.c_float)]
+    for f in ("gdr_validate", "gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_debug",
+              "gdr_chunk_fwd_stage_times"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.gdr_status_string.argtypes = [ctypes.c_int]
+    lib.gdr_status_string.restype = ctypes.c_char_p
+    lib.gdr_last_error_message.argtypes = []
+    lib.gdr_last_error_message.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        raise GdrError(status, lib.gdr_last_error_message().decode())
+
+
+def make_problem(batch, seq_len, Nk, Nv, dk, dv, num_seqs, io_dtype=GDR_BF16, beta_dtype=None,
+                 chunk_size=64, out_dtype=None) -> Problem:
+    return Problem(int(batch), int(seq_len), int(Nk), int(Nv), int(dk), int(dv), int(chunk_size),
+                   int(num_seqs), int(io_dtype), int(io_dtype if beta_dtype is None else beta_dtype),
+                   int(io_dtype if out_dtype is None else out_dtype))
+
+
+def validate(problem: Problem, cu_seqlens_host=None) -> int:
+    """Host-only validation; returns the status code (0 = ok)."""
+    lib = load_library()
+    cu = None
+    if cu_seqlens_host is not None:
+        cu = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous()
+    return lib.gdr_validate(ctypes.byref(problem), None if cu is None else ctypes.c_void_p(cu.data_ptr()))
+
+
+def workspace_size(problem: Problem) -> int:
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.gdr_chunk_fwd_workspace_size(ctypes.byref(problem), ctypes.byref(n)))
+    return int(n.value)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu, chunk_size,
+             output_final_state, out_dtype):
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("expected q, k [B,T,Nk,dk] and v [B,T,Nv,dv]")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype, bfloat16 or float32")
+    B, T, Nk, dk = q.shape
+    Nv, dv = v.shape[2], v.shape[3]
+    if beta.shape != (B, T, Nv) or beta.dtype not in (q.dtype, torch.float32):
+        raise ValueError("beta must be [B,T,Nv] in the io dtype or float32")
+    if g is not None and (g.shape != (B, T, Nv) or g.dtype != torch.float32):
+        raise ValueError("g must be [B,T,Nv] float32")
+    cu_dev = cu_host = None
+    if cu_seqlens is not None:
+        cu_host = (cu_seqlens_cpu if cu_seqlens_cpu is not None else cu_seqlens).detach().to(
+            "cpu", torch.int32).contiguous()
+        cu_dev = cu_seqlens.detach().to(dev, torch.int32).contiguous()
+        N = cu_host.numel() - 1
+    else:
+        N = B
+    if initial_state is not None and (initial_state.shape != (N, Nv, dk, dv) or initial_state.dtype != torch.float32):
+        raise ValueError("initial_state must be [N,Nv,dk,dv] float32")
+    tensors = [q, k, v, beta, g, initial_state]
+    for t in tensors:
+        if t is not None and (t.device != dev or not t.is_contiguous()):
+            raise ValueError("all tensors must be contiguous and on the same device")
+    if scale is None:
+        scale = dk ** -0.5
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out_dtype not in (q.dtype, torch.float32):
+        raise ValueError("out_dtype must be the io dtype or float32")
+    prob = make_problem(B, T, Nk, Nv, dk, dv, N, _DTYPES[q.dtype], _DTYPES[beta.dtype], chunk_size,
+                        _DTYPES[out_dtype])
+    o = torch.empty(v.shape, dtype=out_dtype, device=dev)
+    S_T = torch.empty((N, Nv, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
+    ws = torch.empty(workspace_size(prob), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    args = [ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), ctypes.c_float(scale),
+            _ptr(initial_state), _ptr(cu_dev), _ptr(cu_host), _ptr(o), _ptr(S_T), _ptr(ws),
+            ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream)]
+    keep = (cu_dev, cu_host, ws)
+    return prob, args, o, S_T, keep
+
+
+def chunk_fwd(q, k, v, beta, g=None, scale=None, initial_state=None, output_final_state=True,
+              cu_seqlens=None, cu_seqlens_cpu=None, chunk_size=64, out_dtype=None):
+    """Chunked gated delta-rule forward. Returns (o, final_state or None).
+
+    out_dtype: dtype of o, the io dtype (default) or torch.float32."""
+    lib = load_library()
+    prob, args, o, S_T, keep = _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu,
+                                        chunk_size, output_final_state, out_dtype)
+    _check(lib.gdr_chunk_fwd(*args))
+    del keep
+    return o, S_T
+
+
+def num_chunks(B, T, cu_host) -> int:
+    if cu_host is None:
+        return B * ((T + 63) // 64)
+    lens = (cu_host[1:] - cu_host[:-1]).tolist()
+    return sum((n + 63) // 64 for n in lens)
+
+
+def chunk_fwd_debug(q, k, v, beta, g=None, scale=None, initial_state=None, output_final_state=True,
+                    cu_seqlens=None, cu_seqlens_cpu=None, chunk_size=64, out_dtype=None):
+    """As chunk_fwd, plus the kernels' intermediates in their stored layouts
+    (include/gdr.h, gdr_intermediates_t). Returns a dict."""
+    lib = load_library()
+    prob, args, o, S_T, keep = _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu,
+                                        chunk_size, output_final_state, out_dtype)
+    B, T, Nk, dk = q.shape
+    Nv, dv = v.shape[2], v.shape[3]
+    NT = num_chunks(B, T, keep[1])
+    dev, dt = q.device, q.dtype
+    out = dict(
+        G=torch.zeros((B * T, Nv), dtype=torch.float32, device=dev),
+        A=torch.zeros((B * T, Nv, 64), dtype=torch.float32, device=dev),
+        W=torch.zeros((NT, Nv, 4, dk // 32, 64, 8), dtype=torch.float32, device=dev),
+        U=torch.zeros((NT, Nv, 4, dv // 16, 64, 4), dtype=torch.float32, device=dev),
+        KT=torch.zeros((NT, Nk, dk // 16, 2, 64, 8), dtype=dt, device=dev),
+        H=torch.zeros((NT, Nv, dv // 16, dk // 32, 64, 8), dtype=torch.float32, device=dev),
+        VN=torch.zeros((NT, Nv, dv // 16, 2, 64, 8), dtype=torch.float32, device=dev),
+    )
+    dbg = Intermediates(*(_ptr(out[n]) for n in ("G", "A", "W", "U", "KT", "H", "VN")), 0)
+    _check(lib.gdr_chunk_fwd_debug(*args, ctypes.byref(dbg)))
+    out.update(o=o, S_T=S_T, num_chunks=int(dbg.num_chunks))
+    del keep
+    return out
+
+
+def chunk_fwd_stage_times(q, k, v, beta, g=None, scale=None, initial_state=None, output_final_state=True,
+                          cu_seqlens=None, cu_seqlens_cpu=None, chunk_size=64, out_dtype=None):
+    """Run once with HIP events between the stages; returns (o, S_T, stage_ms)."""
+    lib = load_library()
+    prob, args, o, S_T, keep = _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu,
+                                        chunk_size, output_final_state, out_dtype)
+    ms = (ctypes.c_float * NUM_STAGES)()
+    _check(lib.gdr_chunk_fwd_stage_times(*args, ms))
+    del keep
+    return o, S_T, [float(x) for x in ms]

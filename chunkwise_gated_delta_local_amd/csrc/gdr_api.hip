@@ -1,0 +1,280 @@
+// Host side of the C ABI declared in include/gdr.h: argument validation,
+// workspace plan, and the stage sequence on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "gdr.h"
+#include "gdr_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gdr_status_t fail(gdr_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+gdr_status_t fail(gdr_status_t st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Plan {
+    int64_t Ttot;
+    int32_t nt_cap;
+    size_t off_seq, off_start, off_len, off_first, off_G, off_A, off_W, off_U, off_KT, off_H, off_VN, total;
+    size_t sz_A, sz_W, sz_U, sz_KT, sz_H, sz_VN;   // bytes of the first NT chunks are a prefix
+};
+
+bool supported_dim(int d) { return d == 32 || d == 64 || d == 128; }
+
+gdr_status_t check_problem(const gdr_problem_t* p) {
+    if (!p) return fail(GDR_ERR_NULL, "problem is NULL");
+    if (p->batch < 1 || p->seq_len < 0)
+        return fail(GDR_ERR_SHAPE, "batch must be >= 1 and seq_len >= 0 (got %lld, %lld)",
+                    (long long)p->batch, (long long)p->seq_len);
+    if (p->num_qk_heads < 1 || p->num_v_heads < 1 || p->num_v_heads % p->num_qk_heads != 0)
+        return fail(GDR_ERR_SHAPE, "num_v_heads (%d) must be a positive multiple of num_qk_heads (%d)",
+                    p->num_v_heads, p->num_qk_heads);
+    if (p->num_v_heads > 65535 || p->num_qk_heads > 65535)
+        return fail(GDR_ERR_SHAPE, "more than 65535 heads");
+    if (p->head_dim_qk < 1 || p->head_dim_v < 1)
+        return fail(GDR_ERR_SHAPE, "head dims must be positive");
+    if (p->io_dtype != GDR_F32 && p->io_dtype != GDR_BF16)
+        return fail(GDR_ERR_DTYPE, "unknown io_dtype %d", p->io_dtype);
+    if (p->beta_dtype != p->io_dtype && p->beta_dtype != GDR_F32)
+        return fail(GDR_ERR_DTYPE, "beta_dtype must equal io_dtype or be GDR_F32");
+    if (p->out_dtype != p->io_dtype && p->out_dtype != GDR_F32)
+        return fail(GDR_ERR_DTYPE, "out_dtype must equal io_dtype or be GDR_F32");
+    if (!supported_dim(p->head_dim_qk) || !supported_dim(p->head_dim_v))
+        return fail(GDR_ERR_UNSUPPORTED, "head dims (%d, %d) not in {32, 64, 128}", p->head_dim_qk, p->head_dim_v);
+    if (p->chunk_size != 64)
+        return fail(GDR_ERR_UNSUPPORTED, "chunk_size %d not supported (64 only)", p->chunk_size);
+    if (p->num_seqs < 0) return fail(GDR_ERR_SHAPE, "num_seqs must be >= 0");
+    const int64_t Ttot = p->batch * p->seq_len;
+    if (p->seq_len > ((int64_t)1 << 31) - 1 || Ttot > ((int64_t)1 << 31) - 1 - 64)
+        return fail(GDR_ERR_SHAPE, "total tokens %lld exceed the int32 token index", (long long)Ttot);
+    return GDR_OK;
+}
+
+gdr_status_t check_seqlens(const gdr_problem_t* p, const int32_t* cu, bool varlen) {
+    if (!varlen) {
+        if (p->num_seqs != p->batch)
+            return fail(GDR_ERR_SHAPE, "num_seqs (%d) must equal batch (%lld) without cu_seqlens", p->num_seqs,
+                        (long long)p->batch);
+        return GDR_OK;
+    }
+    if (p->batch != 1) return fail(GDR_ERR_SEQLENS, "cu_seqlens requires batch == 1");
+    if (p->num_seqs < 1) return fail(GDR_ERR_SEQLENS, "cu_seqlens needs num_seqs >= 1");
+    if (!cu) return GDR_OK;   // device-only copy cannot be checked on the host
+    if (cu[0] != 0) return fail(GDR_ERR_SEQLENS, "cu_seqlens[0] = %d, expected 0", cu[0]);
+    for (int32_t n = 0; n < p->num_seqs; ++n)
+        if (cu[n + 1] < cu[n]) return fail(GDR_ERR_SEQLENS, "cu_seqlens decreases at %d", n);
+    if ((int64_t)cu[p->num_seqs] != p->seq_len)
+        return fail(GDR_ERR_SEQLENS, "cu_seqlens[N] = %d but seq_len = %lld", cu[p->num_seqs], (long long)p->seq_len);
+    return GDR_OK;
+}
+
+Plan make_plan(const gdr_problem_t* p) {
+    Plan pl;
+    pl.Ttot = p->batch * p->seq_len;
+    int64_t cap = pl.Ttot / 64 + p->num_seqs;
+    if (cap < 1) cap = 1;
+    pl.nt_cap = (int32_t)cap;
+    const size_t es = p->io_dtype == GDR_BF16 ? 2 : 4;
+    const size_t Nv = p->num_v_heads, Nk = p->num_qk_heads, dk = p->head_dim_qk, dv = p->head_dim_v;
+    const size_t T = (size_t)(pl.Ttot > 0 ? pl.Ttot : 1);
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+    pl.off_seq = take(cap * 4);
+    pl.off_start = take(cap * 4);
+    pl.off_len = take(cap * 4);
+    pl.off_first = take(((size_t)p->num_seqs + 1) * 4);
+    pl.off_G = take(T * Nv * 4);
+    pl.sz_A = T * Nv * 64 * 4;
+    pl.off_A = take(pl.sz_A);
+    pl.sz_W = Nv * 64 * dk * 4;            // per chunk
+    pl.off_W = take(cap * pl.sz_W);
+    pl.sz_U = Nv * 64 * dv * 4;
+    pl.off_U = take(cap * pl.sz_U);
+    pl.sz_KT = Nk * 64 * dk * es;
+    pl.off_KT = take(cap * pl.sz_KT);
+    pl.sz_H = Nv * dk * dv * 4;
+    pl.off_H = take(cap * pl.sz_H);
+    pl.sz_VN = Nv * 64 * dv * 4;
+    pl.off_VN = take(cap * pl.sz_VN);
+    pl.total = off;
+    return pl;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
+
+gdr_status_t run(const gdr_problem_t* p, const void* q, const void* k, const void* v, const float* g,
+                 const void* beta, float scale, const float* S0, const int32_t* cu_dev, const int32_t* cu_host,
+                 void* o, float* ST, void* ws, size_t ws_bytes, void* stream, hipEvent_t* events,
+                 Plan* plan_out, int32_t* nt_out) {
+    gdr_status_t st = check_problem(p);
+    if (st != GDR_OK) return st;
+    if ((cu_dev == nullptr) != (cu_host == nullptr))
+        return fail(GDR_ERR_NULL, "cu_seqlens_dev and cu_seqlens_host must both be given or both be NULL");
+    st = check_seqlens(p, cu_host, cu_host != nullptr);
+    if (st != GDR_OK) return st;
+    const int64_t Ttot = p->batch * p->seq_len;
+    if (Ttot > 0 && (!q || !k || !v || !beta || !o))
+        return fail(GDR_ERR_NULL, "q, k, v, beta and o are required");
+    const void* ptrs[] = {q, k, v, beta, g, S0, o, ST};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return fail(GDR_ERR_SHAPE, "tensor base address not 16-byte aligned");
+    Plan pl = make_plan(p);
+    if (!ws) return fail(GDR_ERR_WORKSPACE, "workspace is NULL");
+    if (((uintptr_t)ws & 255) != 0) return fail(GDR_ERR_WORKSPACE, "workspace not 256-byte aligned");
+    if (ws_bytes < pl.total)
+        return fail(GDR_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, pl.total);
+
+    int64_t nt = 0;
+    for (int32_t n = 0; n < p->num_seqs; ++n) {
+        const int64_t len = cu_host ? (int64_t)cu_host[n + 1] - cu_host[n] : p->seq_len;
+        nt += (len + 63) / 64;
+    }
+    if (nt > pl.nt_cap) return fail(GDR_ERR_SEQLENS, "chunk count %lld exceeds capacity", (long long)nt);
+
+    char* w = static_cast<char*>(ws);
+    gdr::LaunchArgs a;
+    a.bf16 = p->io_dtype == GDR_BF16;
+    a.dk = p->head_dim_qk;
+    a.dv = p->head_dim_v;
+    a.Nk = p->num_qk_heads;
+    a.Nv = p->num_v_heads;
+    a.N = p->num_seqs;
+    a.T_row = p->seq_len;
+    a.Ttot = Ttot;
+    a.nt = (int32_t)nt;
+    a.nt_cap = pl.nt_cap;
+    a.q = q; a.k = k; a.v = v; a.beta = beta;
+    a.beta_f32 = p->beta_dtype == GDR_F32;
+    a.out_f32 = p->out_dtype == GDR_F32;
+    a.g = g; a.S0 = S0; a.scale = scale;
+    a.cu_dev = cu_dev;
+    a.o = o; a.ST = ST;
+    a.chunk_seq = reinterpret_cast<int32_t*>(w + pl.off_seq);
+    a.chunk_start = reinterpret_cast<int32_t*>(w + pl.off_start);
+    a.chunk_len = reinterpret_cast<int32_t*>(w + pl.off_len);
+    a.seq_first = reinterpret_cast<int32_t*>(w + pl.off_first);
+    a.G = reinterpret_cast<float*>(w + pl.off_G);
+    a.A = w + pl.off_A; a.W = w + pl.off_W; a.U = w + pl.off_U; a.KT = w + pl.off_KT;
+    a.H = w + pl.off_H; a.VN = w + pl.off_VN;
+    a.stream = static_cast<hipStream_t>(stream);
+
+    hipError_t e = gdr::launch_forward(a, events);
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    if (plan_out) *plan_out = pl;
+    if (nt_out) *nt_out = (int32_t)nt;
+    g_err[0] = '\0';
+    return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdr_status_t gdr_validate(const gdr_problem_t* problem, const int32_t* cu_seqlens_host) {
+    gdr_status_t st = check_problem(problem);
+    if (st != GDR_OK) return st;
+    st = check_seqlens(problem, cu_seqlens_host, cu_seqlens_host != nullptr);
+    if (st == GDR_OK) g_err[0] = '\0';
+    return st;
+}
+
+gdr_status_t gdr_chunk_fwd_workspace_size(const gdr_problem_t* problem, size_t* bytes) {
+    if (!bytes) return fail(GDR_ERR_NULL, "bytes is NULL");
+    gdr_status_t st = check_problem(problem);
+    if (st != GDR_OK) return st;
+    *bytes = make_plan(problem).total;
+    return GDR_OK;
+}
+
+gdr_status_t gdr_chunk_fwd(const gdr_problem_t* p, const void* q, const void* k, const void* v, const float* g,
+                           const void* beta, float scale, const float* initial_state, const int32_t* cu_dev,
+                           const int32_t* cu_host, void* o, float* final_state, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return run(p, q, k, v, g, beta, scale, initial_state, cu_dev, cu_host, o, final_state, workspace,
+               workspace_bytes, stream, nullptr, nullptr, nullptr);
+}
+
+gdr_status_t gdr_chunk_fwd_debug(const gdr_problem_t* p, const void* q, const void* k, const void* v,
+                                 const float* g, const void* beta, float scale, const float* initial_state,
+                                 const int32_t* cu_dev, const int32_t* cu_host, void* o, float* final_state,
+                                 void* workspace, size_t workspace_bytes, void* stream, gdr_intermediates_t* dbg) {
+    if (!dbg) return fail(GDR_ERR_NULL, "dbg is NULL");
+    Plan pl;
+    int32_t nt = 0;
+    gdr_status_t st = run(p, q, k, v, g, beta, scale, initial_state, cu_dev, cu_host, o, final_state, workspace,
+                          workspace_bytes, stream, nullptr, &pl, &nt);
+    if (st != GDR_OK) return st;
+    dbg->num_chunks = nt;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const char* w = static_cast<const char*>(workspace);
+    const size_t Ttot = (size_t)pl.Ttot;
+    struct { void* dst; size_t off; size_t bytes; } copies[] = {
+        {dbg->G, pl.off_G, Ttot * (size_t)p->num_v_heads * 4},
+        {dbg->A, pl.off_A, Ttot > 0 ? pl.sz_A : 0},
+        {dbg->W, pl.off_W, (size_t)nt * pl.sz_W},
+        {dbg->U, pl.off_U, (size_t)nt * pl.sz_U},
+        {dbg->KT, pl.off_KT, (size_t)nt * pl.sz_KT},
+        {dbg->H, pl.off_H, (size_t)nt * pl.sz_H},
+        {dbg->VN, pl.off_VN, (size_t)nt * pl.sz_VN},
+    };
+    for (auto& c : copies) {
+        if (!c.dst || c.bytes == 0) continue;
+        hipError_t e = hipMemcpyAsync(c.dst, w + c.off, c.bytes, hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return fail(GDR_ERR_HIP, "intermediate copy failed: %s", hipGetErrorString(e));
+    }
+    return GDR_OK;
+}
+
+gdr_status_t gdr_chunk_fwd_stage_times(const gdr_problem_t* p, const void* q, const void* k, const void* v,
+                                       const float* g, const void* beta, float scale, const float* initial_state,
+                                       const int32_t* cu_dev, const int32_t* cu_host, void* o, float* final_state,
+                                       void* workspace, size_t workspace_bytes, void* stream, float* stage_ms) {
+    if (!stage_ms) return fail(GDR_ERR_NULL, "stage_ms is NULL");
+    hipEvent_t ev[GDR_NUM_STAGES + 1];
+    int made = 0;
+    for (; made < GDR_NUM_STAGES + 1; ++made)
+        if (hipEventCreate(&ev[made]) != hipSuccess) break;
+    gdr_status_t st = GDR_OK;
+    if (made < GDR_NUM_STAGES + 1) {
+        st = fail(GDR_ERR_HIP, "hipEventCreate failed");
+    } else {
+        st = run(p, q, k, v, g, beta, scale, initial_state, cu_dev, cu_host, o, final_state, workspace,
+                 workspace_bytes, stream, ev, nullptr, nullptr);
+        if (st == GDR_OK) {
+            hipError_t e = hipEventSynchronize(ev[GDR_NUM_STAGES]);
+            for (int i = 0; i < GDR_NUM_STAGES && e == hipSuccess; ++i)
+                e = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
+            if (e != hipSuccess) st = fail(GDR_ERR_HIP, "event timing failed: %s", hipGetErrorString(e));
+        }
+    }
+    for (int i = 0; i < made; ++i) (void)hipEventDestroy(ev[i]);
+    return st;
+}
+
+const char* gdr_status_string(gdr_status_t s) {
+    switch (s) {
+        case GDR_OK: return "ok";
+        case GDR_ERR_NULL: return "required pointer is NULL";
+        case GDR_ERR_SHAPE: return "invalid shape or alignment";
+        case GDR_ERR_DTYPE: return "invalid dtype";
+        case GDR_ERR_UNSUPPORTED: return "unsupported by this build";
+        case GDR_ERR_SEQLENS: return "invalid cu_seqlens";
+        case GDR_ERR_WORKSPACE: return "workspace missing or too small";
+        case GDR_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* gdr_last_error_message(void) { return g_err; }
+
+}  // extern "C"

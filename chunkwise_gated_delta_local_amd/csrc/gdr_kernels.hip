@@ -1,0 +1,627 @@
+// HIP kernels of the chunked gated delta-rule forward for gfx950.
+//
+// Method (FLA DeltaNet article on pnsm.cn, sections 2.3-2.4 and 3.1-3.4;
+// ChunkGatedDeltaRule math page, section 3, formulas (1)-(6)). Per chunk of
+// C = 64 tokens and value head h (q/k head kh = h / (Nv/Nk)):
+//   G     = chunk-local inclusive prefix sum of g                       (K1)
+//   L_ij  = beta_i (k_i . k_j) exp(G_i - G_j), i > j;  A = (I + L)^-1    (K2)
+//   W     = A diag(beta exp(G)) K,  U = A diag(beta) V                   (K3)
+//   h_c   = S;  V_new = U - W S;
+//   S    <- exp(G_last) S + (diag(exp(G_last - G)) K)^T V_new            (K4, sequential)
+//   O     = scale [diag(exp(G)) Q h_c + (Q K^T (.) D) V_new],
+//           D_ij = exp(G_i - G_j) for i >= j else 0                      (K5)
+// Intermediates live in the caller's workspace in fragment-major layouts
+// (gdr_device.hpp) chosen so that every matrix-core operand is read with
+// lane-contiguous vector loads and MFMA results feed later products in place.
+#include "gdr_device.hpp"
+#include "gdr_launch.hpp"
+
+namespace gdr {
+
+// ============================================================ chunk table
+// Builds, from the sequence offsets, the list of chunks (sequence id, first
+// token, length) numbered sequence by sequence, and the first chunk of each
+// sequence. One block; sequences are scanned 1024 at a time. Offsets are
+// clamped to [0, Ttot] and chunk indices to the table capacity, so inconsistent
+// offsets can never send a later kernel outside its buffers.
+__global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict__ cu, int64_t T_row,
+                                                       int32_t N, int64_t Ttot, int32_t cap,
+                                                       int32_t* __restrict__ chunk_seq,
+                                                       int32_t* __restrict__ chunk_start,
+                                                       int32_t* __restrict__ chunk_len,
+                                                       int32_t* __restrict__ seq_first) {
+    __shared__ int32_t scan[1024];
+    const int tid = threadIdx.x;
+    for (int32_t c = tid; c < cap; c += 1024) {       // entries no sequence reaches stay empty
+        chunk_seq[c] = 0;
+        chunk_start[c] = 0;
+        chunk_len[c] = 0;
+    }
+    __syncthreads();
+    int32_t base = 0;
+    for (int32_t n0 = 0; n0 < N; n0 += 1024) {
+        const int32_t n = n0 + tid;
+        int64_t s = 0, e = 0;
+        if (n < N) {
+            s = cu ? (int64_t)cu[n] : (int64_t)n * T_row;
+            e = cu ? (int64_t)cu[n + 1] : (int64_t)(n + 1) * T_row;
+            s = s < 0 ? 0 : (s > Ttot ? Ttot : s);
+            e = e < s ? s : (e > Ttot ? Ttot : e);
+        }
+        const int32_t nch = (int32_t)((e - s + kChunk - 1) / kChunk);
+        scan[tid] = nch;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {         // inclusive Hillis-Steele scan
+            int32_t add = tid >= off ? scan[tid - off] : 0;
+            __syncthreads();
+            scan[tid] += add;
+            __syncthreads();
+        }
+        const int32_t first = base + scan[tid] - nch;
+        if (n < N) {
+            seq_first[n] = first < cap ? first : cap;
+            for (int32_t j = 0; j < nch; ++j) {
+                const int32_t c = first + j;
+                if (c >= cap) break;
+                const int64_t cs = s + (int64_t)j * kChunk;
+                const int64_t ce = cs + kChunk < e ? cs + kChunk : e;
+                chunk_seq[c] = n;
+                chunk_start[c] = (int32_t)cs;
+                chunk_len[c] = (int32_t)(ce - cs);
+            }
+        }
+        base += scan[1023];
+        __syncthreads();
+    }
+    if (tid == 0) seq_first[N] = base < cap ? base : cap;
+}
+
+// ============================================================ K1: gate prefix sums
+// G[t, h] = sum of g over the tokens of t's chunk up to and including t, in
+// fp32 and in token order (ChunkGatedDeltaRule page, section 3, "G_i";
+// GLA notes, forward step 1, chunk-local cumulative log gate). One thread per
+// (chunk, head); neighbouring threads take neighbouring heads so every step
+// of the scan is a coalesced row read. g == NULL writes zeros (ungated rule).
+__global__ __launch_bounds__(256) void k_gate_cumsum(const float* __restrict__ g,
+                                                      const int32_t* __restrict__ chunk_start,
+                                                      const int32_t* __restrict__ chunk_len,
+                                                      int32_t NT, int32_t Nv, float* __restrict__ G) {
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= (int64_t)NT * Nv) return;
+    const int32_t c = (int32_t)(p / Nv), h = (int32_t)(p % Nv);
+    const int64_t s = chunk_start[c];
+    const int32_t L = chunk_len[c];
+    float acc = 0.f;
+    for (int32_t i = 0; i < L; ++i) {
+        const int64_t idx = (s + i) * Nv + h;
+        if (g) acc += g[idx];
+        G[idx] = acc;
+    }
+}
+
+// ============================================================ K2: A-build + solve
+// One workgroup (4 wavefronts) per (chunk, q/k head); it serves the Nv/Nk
+// value heads that share the key head, computing K K^T once (FLA DeltaNet
+// article, section 3.1: beta-scaled K K^T, strictly lower part).
+//   1. K chunk -> LDS; wave w forms the K K^T tiles of block row w on MFMA.
+//   2. Per value head: L = tril(beta_i (k_i.k_j) exp(G_i - G_j), -1) -> LDS (fp32).
+//   3. The four 16x16 diagonal blocks of A = (I + L)^-1 by forward substitution
+//      in fp32, one column per lane (ChunkGatedDeltaRule page, section 3.1,
+//      row-recursive correction; FLA DeltaNet article, section 3.2, 16x16
+//      blocks).
+//   4. Off-diagonal blocks by block substitution on MFMA, merging
+//      16 -> 32 -> 64 (FLA DeltaNet article, section 3.2):
+//        A_ij = -A_ii L_ij A_jj for the two 16-blocks below the diagonal of each
+//        32-block, then the lower-left 32x32 block = -A_bot L_bl A_top.
+//      Both operands are derived values, so each product takes the split
+//      (three-pass) form.
+//   5. A rows (fp32) -> global, zero above the diagonal and past the chunk end.
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void k_build_solve(const T* __restrict__ k, const void* __restrict__ beta,
+                                                      int beta_f32, const float* __restrict__ G,
+                                                      const int32_t* __restrict__ chunk_start,
+                                                      const int32_t* __restrict__ chunk_len,
+                                                      int32_t Nk, int32_t Nv, float* __restrict__ A_out) {
+    constexpr int KP = DK + 8;                 // padded LDS row (elements)
+    __shared__ __attribute__((aligned(16))) T Ks[kChunk * KP];
+    __shared__ float Lf[kChunk][kChunk + 1];
+    __shared__ float Af[kChunk][kChunk + 1];
+    __shared__ float bs[kChunk], gs[kChunk];
+
+    const int c = blockIdx.x, kh = blockIdx.y;
+    const int64_t s = chunk_start[c];
+    const int L = chunk_len[c];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, qd = lane >> 4;
+    typedef typename Vec<T>::v8 v8;
+
+    // 1. K rows of the chunk (zero past the chunk end)
+    for (int idx = tid; idx < kChunk * (DK / 8); idx += 256) {
+        const int row = idx / (DK / 8), seg = idx % (DK / 8);
+        v8 val = zero_pair<T>();
+        if (row < L) val = *reinterpret_cast<const v8*>(k + ((s + row) * Nk + kh) * DK + seg * 8);
+        *reinterpret_cast<v8*>(&Ks[row * KP + seg * 8]) = val;
+    }
+    __syncthreads();
+
+    // K K^T tiles of block row `wave`: kk[j] holds rows 16*wave + 4*qd + jj, column 16*j + r.
+    f32x4 kk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        kk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (j <= wave) {
+#pragma unroll
+            for (int kp = 0; kp < DK / 32; ++kp) {
+                v8 a = load_pair_row<T>(&Ks[(wave * 16 + r) * KP + kp * 32], qd);
+                v8 b = load_pair_row<T>(&Ks[(j * 16 + r) * KP + kp * 32], qd);
+                kk[j] = mfma_pair(a, b, kk[j]);
+            }
+        }
+    }
+
+    const int group = Nv / Nk;
+    for (int hh = 0; hh < group; ++hh) {
+        const int h = kh * group + hh;
+        if (tid < kChunk) {
+            bs[tid] = tid < L ? load_beta(beta, (s + tid) * Nv + h, beta_f32) : 0.f;
+            gs[tid] = tid < L ? G[(s + tid) * Nv + h] : 0.f;
+        }
+        for (int idx = tid; idx < kChunk * kChunk; idx += 256) {
+            Lf[idx >> 6][idx & 63] = 0.f;
+            Af[idx >> 6][idx & 63] = 0.f;
+        }
+        __syncthreads();
+
+        // 2. strictly lower L
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j <= wave) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int i = wave * 16 + 4 * qd + jj, col = j * 16 + r;
+                    float val = 0.f;
+                    if (i > col && i < L) val = bs[i] * kk[j][jj] * __expf(gs[i] - gs[col]);
+                    Lf[i][col] = val;
+                }
+            }
+        }
+        __syncthreads();
+
+        // 3. diagonal block `wave`: lane r < 16 owns column r of the block.
+        if (lane < 16) {
+            const int b0 = wave * 16;
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[i] = (i == lane) ? 1.f : 0.f;
+#pragma unroll
+            for (int i = 1; i < 16; ++i) {
+                float acc = 0.f;
+#pragma unroll
+                for (int m = 0; m < i; ++m) acc += Lf[b0 + i][b0 + m] * x[m];
+                if (i > lane) x[i] = -acc;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) Af[b0 + i][b0 + lane] = x[i];
+        }
+        __syncthreads();
+
+        // 4a. A_ij = -A_ii (L_ij A_jj) for (i, j) = (1, 0) [wave 0] and (3, 2) [wave 1];
+        //     contraction depth 16: pair elements 4..7 are zero.
+        if (wave < 2) {
+            const int bi = 2 * wave + 1, bj = 2 * wave;
+            float la[8], db[8], ai[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                la[e] = Lf[bi * 16 + r][bj * 16 + 4 * qd + e];
+                db[e] = Af[bj * 16 + 4 * qd + e][bj * 16 + r];
+                ai[e] = Af[bi * 16 + r][bi * 16 + 4 * qd + e];
+                la[4 + e] = db[4 + e] = ai[4 + e] = 0.f;
+            }
+            f32x4 t1 = mfma_dd<T>(split8<T>(la), split8<T>(db), f32x4{0.f, 0.f, 0.f, 0.f});   // L_ij A_jj
+            f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+            f32x4 t2 = mfma_dd<T>(split8<T>(ai), split_acc_pair<T>(t1, zero4), zero4);          // A_ii (L_ij A_jj)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) Af[bi * 16 + 4 * qd + jj][bj * 16 + r] = -t2[jj];
+        }
+        __syncthreads();
+
+        // 4b. lower-left 32x32 block = -A_bot (L_bl A_top); wave w < 2 takes column block w.
+        if (wave < 2) {
+            const int ct = wave;
+            float bt[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bt[e] = Af[4 * qd + e][ct * 16 + r];
+                bt[4 + e] = Af[16 + 4 * qd + e][ct * 16 + r];
+            }
+            const Split<T> b = split8<T>(bt);
+            f32x4 t1[2];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+                t1[rb] = mfma_dd<T>(load_split_row<T>(&Lf[32 + 16 * rb + r][0], qd), b, f32x4{0.f, 0.f, 0.f, 0.f});
+            const Split<T> b2 = split_acc_pair<T>(t1[0], t1[1]);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                f32x4 t2 = mfma_dd<T>(load_split_row<T>(&Af[32 + 16 * rb + r][32], qd), b2, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) Af[32 + 16 * rb + 4 * qd + jj][ct * 16 + r] = -t2[jj];
+            }
+        }
+        __syncthreads();
+
+        // 5. rows of A for the valid tokens (fp32)
+        for (int idx = tid; idx < kChunk * 16; idx += 256) {
+            const int row = idx >> 4, seg = idx & 15;
+            if (row < L) {
+                f32x4 val;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int col = seg * 4 + e;
+                    val[e] = (col <= row) ? Af[row][col] : 0.f;
+                }
+                *reinterpret_cast<f32x4*>(A_out + ((s + row) * Nv + h) * kChunk + seg * 4) = val;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ============================================================ K3: w/u products
+// One workgroup (4 wavefronts) per (chunk, q/k head). Formulas (1) and (2) of
+// the ChunkGatedDeltaRule page (FLA DeltaNet article, section 3.3, where
+// diag(beta) is absorbed into one operand):
+//   W = (A diag(beta exp(G))) K  -> stored as W^T tiles, which in accumulator
+//       layout are exactly the pair fragments the state pass reads;
+//   U = (A diag(beta)) V         -> stored as accumulator tiles.
+// The scaled A rows are derived (split operands); K and V are exact inputs.
+// K^T and V^T are staged in LDS so that the contraction over chunk positions
+// reads contiguous LDS rows; the key head's K^T is also written out once, as
+// pair fragments, for the state pass. W and U are stored in fp32.
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) void k_wu(const T* __restrict__ k, const T* __restrict__ v,
+                                             const void* __restrict__ beta, int beta_f32,
+                                             const float* __restrict__ G, const float* __restrict__ A,
+                                             const int32_t* __restrict__ chunk_start,
+                                             const int32_t* __restrict__ chunk_len, int32_t Nk, int32_t Nv,
+                                             float* __restrict__ Wf, float* __restrict__ Uf, T* __restrict__ KTf) {
+    constexpr int MP = kChunk + 8;             // padded LDS row over chunk positions
+    __shared__ __attribute__((aligned(16))) T KTs[DK * MP];
+    __shared__ __attribute__((aligned(16))) T VTs[DV * MP];
+    __shared__ float bs[kChunk], sc[kChunk];
+
+    const int c = blockIdx.x, kh = blockIdx.y;
+    const int64_t s = chunk_start[c];
+    const int L = chunk_len[c];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, qd = lane >> 4;
+    typedef typename Vec<T>::v8 v8;
+
+    // K^T of the chunk (zero past the chunk end); consecutive threads take consecutive positions.
+    for (int idx = tid; idx < kChunk * (DK / 8); idx += 256) {
+        const int m = idx & 63, seg = idx >> 6;
+        v8 val = zero_pair<T>();
+        if (m < L) val = *reinterpret_cast<const v8*>(k + ((s + m) * Nk + kh) * DK + seg * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) KTs[(seg * 8 + e) * MP + m] = val[e];
+    }
+    __syncthreads();
+
+    // K^T pair fragments for the state pass: [c][kh][db][tp]
+    for (int f = wave; f < (DK / 16) * 2; f += 4) {
+        const int db = f >> 1, tp = f & 1;
+        v8 val = load_pair_row<T>(&KTs[(db * 16 + r) * MP + tp * 32], qd);
+        store_frag<T>(KTf + (((int64_t)c * Nk + kh) * (DK / 16) * 2 + f) * 512, lane, val);
+    }
+
+    const int group = Nv / Nk;
+    const int tb = wave;                       // wave w owns chunk positions 16w..16w+15
+    const int i = tb * 16 + r;
+    for (int hh = 0; hh < group; ++hh) {
+        const int h = kh * group + hh;
+        __syncthreads();                       // previous head's readers are done with VTs / sc
+        if (tid < kChunk) {
+            const float bm = tid < L ? load_beta(beta, (s + tid) * Nv + h, beta_f32) : 0.f;
+            bs[tid] = bm;
+            sc[tid] = tid < L ? bm * __expf(G[(s + tid) * Nv + h]) : 0.f;
+        }
+        for (int idx = tid; idx < kChunk * (DV / 8); idx += 256) {
+            const int m = idx & 63, seg = idx >> 6;
+            v8 val = zero_pair<T>();
+            if (m < L) val = *reinterpret_cast<const v8*>(v + ((s + m) * Nv + h) * DV + seg * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) VTs[(seg * 8 + e) * MP + m] = val[e];
+        }
+        __syncthreads();
+
+        // Row i of A over positions m, scaled by beta_m (for U) and beta_m exp(G_m) (for W).
+        Split<T> aU[2], aW[2];
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+            float xa[8], xu[8], xw[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xa[e] = 0.f;
+            if (i < L) {
+                const float* row = A + ((s + i) * Nv + h) * kChunk + tp * 32;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    xa[e] = row[4 * qd + e];
+                    xa[4 + e] = row[16 + 4 * qd + e];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int m = tp * 32 + (e < 4 ? 4 * qd + e : 16 + 4 * qd + e - 4);
+                xu[e] = xa[e] * bs[m];
+                xw[e] = xa[e] * sc[m];
+            }
+            aU[tp] = split8<T>(xu);
+            aW[tp] = split8<T>(xw);
+        }
+        // W^T tiles (db, tb): rows dk, columns i
+#pragma unroll
+        for (int db = 0; db < DK / 16; ++db) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp)
+                acc = mfma_xd<T>(load_pair_row<T>(&KTs[(db * 16 + r) * MP + tp * 32], qd), aW[tp], acc);
+            float* dst = Wf + ((((int64_t)c * Nv + h) * 4 + tb) * (DK / 32) + (db >> 1)) * 512;
+            store_pair_half_f32(dst, lane, db & 1, acc);
+        }
+        // U tiles (tb, nb): rows i, columns dv
+#pragma unroll
+        for (int nb = 0; nb < DV / 16; ++nb) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp)
+                acc = mfma_dx<T>(aU[tp], load_pair_row<T>(&VTs[(nb * 16 + r) * MP + tp * 32], qd), acc);
+            store_tile_f32(Uf + ((((int64_t)c * Nv + h) * 4 + tb) * (DV / 16) + nb) * 256, lane, acc);
+        }
+    }
+}
+
+// ============================================================ K4: state pass
+// One wavefront per (sequence, value head, 16 columns of dv); it keeps its
+// dk x 16 slice of the state in fp32 accumulator registers for the whole
+// sequence and walks the chunks in order (FLA DeltaNet article, section 3.4,
+// chunk-serial state update; ChunkGatedDeltaRule page, formulas (3) and (6)):
+//   H     <- S (the state entering the chunk, fp32, for the output kernel)
+//   V_new  = U - W S
+//   S      = exp(G_last) S + K^T diag(exp(G_last - G)) V_new
+// S in accumulator layout is already the pair-fragment operand of W S, and
+// V_new in accumulator layout is already the operand of K^T V_new.
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(64) void k_state(const float* __restrict__ Wf, const float* __restrict__ Uf,
+                                               const T* __restrict__ KTf, const float* __restrict__ G,
+                                               const float* __restrict__ S0,
+                                               const int32_t* __restrict__ chunk_start,
+                                               const int32_t* __restrict__ chunk_len,
+                                               const int32_t* __restrict__ seq_first, int32_t Nk, int32_t Nv,
+                                               float* __restrict__ Hf, float* __restrict__ VNf, float* __restrict__ ST) {
+    constexpr int NDB = DK / 16, NKP = DK / 32, NNB = DV / 16;
+    const int n = blockIdx.x, h = blockIdx.y, nb = blockIdx.z;
+    const int lane = threadIdx.x, r = lane & 15, qd = lane >> 4;
+    const int kh = h / (Nv / Nk);
+    typedef typename Vec<float>::v8 f8;
+
+    f32x4 S[NDB];
+    const int64_t sbase = ((int64_t)n * Nv + h) * DK * DV;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            S[db][j] = S0 ? S0[sbase + (int64_t)(db * 16 + 4 * qd + j) * DV + nb * 16 + r] : 0.f;
+
+    const int c0 = seq_first[n], c1 = seq_first[n + 1];
+    for (int c = c0; c < c1; ++c) {
+        const int64_t s = chunk_start[c];
+        const int L = chunk_len[c];
+        if (L <= 0) continue;
+        const float g_last = G[(s + L - 1) * Nv + h];
+
+        // state entering the chunk, stored in fp32 and split for the products
+        Split<T> sb[NKP];
+        float* hdst = Hf + (((int64_t)c * Nv + h) * NNB + nb) * NKP * 512;
+#pragma unroll
+        for (int kp = 0; kp < NKP; ++kp) {
+            f8 raw = __builtin_shufflevector(S[2 * kp], S[2 * kp + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+            store_frag_f32(hdst + kp * 512, lane, raw);
+            sb[kp] = split_acc_pair<T>(S[2 * kp], S[2 * kp + 1]);
+        }
+
+        // V_new = U - W S for the 4 blocks of 16 chunk positions
+        f32x4 vn[4];
+        const float* wsrc = Wf + ((int64_t)c * Nv + h) * 4 * NKP * 512;
+        const float* usrc = Uf + ((int64_t)c * Nv + h) * 4 * NNB * 256;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kp = 0; kp < NKP; ++kp)
+                x = mfma_dd<T>(split_v8<T>(load_frag_f32(wsrc + (tb * NKP + kp) * 512, lane)), sb[kp], x);
+            vn[tb] = load_tile_f32(usrc + (tb * NNB + nb) * 256, lane) - x;
+        }
+        float* vdst = VNf + (((int64_t)c * Nv + h) * NNB + nb) * 2 * 512;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) store_pair_half_f32(vdst + (tb >> 1) * 512, lane, tb & 1, vn[tb]);
+
+        // decay each position to the chunk end; positions past the end contribute nothing
+        f32x4 vd[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = tb * 16 + 4 * qd + j;
+                vd[tb][j] = row < L ? vn[tb][j] * __expf(g_last - G[(s + row) * Nv + h]) : 0.f;
+            }
+        const Split<T> vb[2] = {split_acc_pair<T>(vd[0], vd[1]), split_acc_pair<T>(vd[2], vd[3])};
+
+        const float a_last = __expf(g_last);
+        const T* ksrc = KTf + ((int64_t)c * Nk + kh) * NDB * 2 * 512;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            f32x4 acc = S[db] * a_last;
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp) acc = mfma_xd<T>(load_frag<T>(ksrc + (db * 2 + tp) * 512, lane), vb[tp], acc);
+            S[db] = acc;
+        }
+    }
+    if (ST) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ST[sbase + (int64_t)(db * 16 + 4 * qd + j) * DV + nb * 16 + r] = S[db][j];
+    }
+}
+
+// ============================================================ K5: output
+// One workgroup (4 wavefronts) per (chunk, value head); wave w produces the
+// output rows 16w..16w+15 for all dv (ChunkGatedDeltaRule page, formulas (4)
+// and (5); FLA DeltaNet article, section 3.4 "chunk_fwd_o"):
+//   O = scale [ diag(exp(G)) Q H + (Q K^T (.) D) V_new ],  D_ij = exp(G_i - G_j), j <= i.
+// The score block is formed transposed (K Q^T) so that its accumulator tiles
+// are the pair-fragment operand of the product with V_new; the upper
+// triangle and positions past the chunk end are masked explicitly.
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) void k_output(const T* __restrict__ q, const T* __restrict__ k,
+                                                 const float* __restrict__ G, const float* __restrict__ Hf,
+                                                 const float* __restrict__ VNf, const int32_t* __restrict__ chunk_start,
+                                                 const int32_t* __restrict__ chunk_len, int32_t Nk, int32_t Nv,
+                                                 float scale, int out_f32, void* __restrict__ o) {
+    constexpr int NKP = DK / 32, NNB = DV / 16;
+    const int c = blockIdx.x, h = blockIdx.y;
+    const int64_t s = chunk_start[c];
+    const int L = chunk_len[c];
+    const int tid = threadIdx.x, tb = tid >> 6, lane = tid & 63, r = lane & 15, qd = lane >> 4;
+    if (tb * 16 >= L) return;                  // no valid rows in this wave's block
+    const int kh = h / (Nv / Nk);
+    typedef typename Vec<T>::v8 v8;
+
+    // Q rows 16*tb + r as pair fragments over dk (zero past the chunk end)
+    const int i = tb * 16 + r;
+    v8 qf[NKP];
+#pragma unroll
+    for (int kp = 0; kp < NKP; ++kp) {
+        qf[kp] = zero_pair<T>();
+        if (i < L) qf[kp] = load_pair_row<T>(q + ((s + i) * Nk + kh) * DK + kp * 32, qd);
+    }
+    const float g_i = i < L ? G[(s + i) * Nv + h] : 0.f;
+    float g_rows[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = tb * 16 + 4 * qd + j;
+        g_rows[j] = row < L ? G[(s + row) * Nv + h] : 0.f;
+    }
+
+    // inter-chunk part: Q H, rows scaled by exp(G_i)
+    f32x4 out[NNB];
+    const float* hsrc = Hf + ((int64_t)c * Nv + h) * NNB * NKP * 512;
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kp = 0; kp < NKP; ++kp)
+            acc = mfma_xd<T>(qf[kp], split_v8<T>(load_frag_f32(hsrc + (nb * NKP + kp) * 512, lane)), acc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] *= __expf(g_rows[j]);
+        out[nb] = acc;
+    }
+
+    // scores, transposed: pt[tj] rows j = 16*tj + 4*qd + jj, column i
+    f32x4 pt[4];
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) {
+        pt[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (tj <= tb) {
+            const int jr = tj * 16 + r;
+#pragma unroll
+            for (int kp = 0; kp < NKP; ++kp) {
+                v8 kf = zero_pair<T>();
+                if (jr < L) kf = load_pair_row<T>(k + ((s + jr) * Nk + kh) * DK + kp * 32, qd);
+                pt[tj] = mfma_pair(kf, qf[kp], pt[tj]);
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int j = tj * 16 + 4 * qd + jj;
+                float gj = j < L ? G[(s + j) * Nv + h] : 0.f;
+                pt[tj][jj] = (j <= i && i < L) ? pt[tj][jj] * __expf(g_i - gj) : 0.f;
+            }
+        }
+    }
+    const Split<T> pa[2] = {split_acc_pair<T>(pt[0], pt[1]), split_acc_pair<T>(pt[2], pt[3])};
+
+    // intra-chunk part: (Q K^T (.) D) V_new
+    const float* vsrc = VNf + ((int64_t)c * Nv + h) * NNB * 2 * 512;
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb) {
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp)
+            if (2 * tp <= tb)
+                out[nb] = mfma_dd<T>(pa[tp], split_v8<T>(load_frag_f32(vsrc + (nb * 2 + tp) * 512, lane)), out[nb]);
+    }
+
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = tb * 16 + 4 * qd + j;
+            if (row < L) {
+                const int64_t idx = ((s + row) * Nv + h) * DV + nb * 16 + r;
+                if (out_f32) reinterpret_cast<float*>(o)[idx] = scale * out[nb][j];
+                else reinterpret_cast<T*>(o)[idx] = to_t<T>(scale * out[nb][j]);
+            }
+        }
+}
+
+// ============================================================ launchers
+template <typename T, int DK, int DV>
+static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
+    hipStream_t st = a.stream;
+    auto mark = [&](int i) { if (ev) (void)hipEventRecord(ev[i], st); };
+    const int32_t cap = a.nt_cap;
+    mark(0);
+    k_chunk_table<<<1, 1024, 0, st>>>(a.cu_dev, a.T_row, a.N, a.Ttot, cap, a.chunk_seq, a.chunk_start,
+                                      a.chunk_len, a.seq_first);
+    mark(1);
+    const int32_t NT = a.nt;
+    if (NT > 0) {
+        const int64_t units = (int64_t)NT * a.Nv;
+        k_gate_cumsum<<<(unsigned)((units + 255) / 256), 256, 0, st>>>(a.g, a.chunk_start, a.chunk_len, NT, a.Nv, a.G);
+    }
+    mark(2);
+    if (NT > 0)
+        k_build_solve<T, DK><<<dim3(NT, a.Nk), 256, 0, st>>>((const T*)a.k, a.beta, a.beta_f32, a.G, a.chunk_start,
+                                                            a.chunk_len, a.Nk, a.Nv, (float*)a.A);
+    mark(3);
+    if (NT > 0)
+        k_wu<T, DK, DV><<<dim3(NT, a.Nk), 256, 0, st>>>((const T*)a.k, (const T*)a.v, a.beta, a.beta_f32, a.G,
+                                                       (const float*)a.A, a.chunk_start, a.chunk_len, a.Nk, a.Nv,
+                                                       (float*)a.W, (float*)a.U, (T*)a.KT);
+    mark(4);
+    if (a.N > 0)
+        k_state<T, DK, DV><<<dim3(a.N, a.Nv, DV / 16), 64, 0, st>>>((const float*)a.W, (const float*)a.U, (const T*)a.KT, a.G,
+                                                                   a.S0, a.chunk_start, a.chunk_len, a.seq_first,
+                                                                   a.Nk, a.Nv, (float*)a.H, (float*)a.VN, a.ST);
+    mark(5);
+    if (NT > 0)
+        k_output<T, DK, DV><<<dim3(NT, a.Nv), 256, 0, st>>>((const T*)a.q, (const T*)a.k, a.G, (const float*)a.H,
+                                                           (const float*)a.VN, a.chunk_start, a.chunk_len, a.Nk, a.Nv,
+                                                           a.scale, a.out_f32, a.o);
+    mark(6);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t dispatch_dims(const LaunchArgs& a, hipEvent_t* ev) {
+#define GDR_CASE(DKv, DVv) \
+    if (a.dk == DKv && a.dv == DVv) return launch_pipeline<T, DKv, DVv>(a, ev);
+    GDR_CASE(32, 32) GDR_CASE(32, 64) GDR_CASE(32, 128)
+    GDR_CASE(64, 32) GDR_CASE(64, 64) GDR_CASE(64, 128)
+    GDR_CASE(128, 32) GDR_CASE(128, 64) GDR_CASE(128, 128)
+#undef GDR_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_forward(const LaunchArgs& a, hipEvent_t* events) {
+    if (a.bf16) return dispatch_dims<bf16>(a, events);
+    return dispatch_dims<float>(a, events);
+}
+
+}  // namespace gdr

@@ -1,0 +1,35 @@
+// Internal interface between the host API (gdr_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+struct LaunchArgs {
+    bool bf16;                 // compute/io type: bf16 (true) or fp32
+    int dk, dv;
+    int32_t Nk, Nv, N;         // q/k heads, v heads, sequences
+    int64_t T_row, Ttot;       // tokens per batch row (fixed length), total tokens
+    int32_t nt, nt_cap;        // chunks used, chunk-table capacity
+    const void *q, *k, *v, *beta;
+    int beta_f32;
+    int out_f32;               // o in fp32 (else in the io type)
+    const float* g;            // NULL: ungated
+    const float* S0;           // NULL: zeros
+    float scale;
+    const int32_t* cu_dev;     // NULL: fixed length
+    void* o;
+    float* ST;                 // NULL: not written
+    // workspace regions
+    int32_t *chunk_seq, *chunk_start, *chunk_len, *seq_first;
+    float* G;
+    void *A, *W, *U, *KT, *H, *VN;
+    hipStream_t stream;
+};
+
+// Enqueues the whole forward on a.stream. events: NULL, or 7 events recorded
+// before the first and after every one of the six stages.
+hipError_t launch_forward(const LaunchArgs& a, hipEvent_t* events);
+
+}  // namespace gdr

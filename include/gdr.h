@@ -1,0 +1,211 @@
+/*
+ * gdr.h — C ABI of the chunked gated delta-rule forward for AMD MI355X (gfx950).
+ *
+ * The operation (FLA DeltaNet article on pnsm.cn, section 1 and sections
+ * 2.3–2.4; ChunkGatedDeltaRule math page "01 · 数学原理", sections 1 and 3):
+ * for every sequence n and value head h, with q/k head kh = h / (Nv / Nk),
+ *
+ *     S_t = exp(g_t) (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t                      (read after the write)
+ *
+ * starting from S_0 = initial_state[n, h] (zeros when absent); the state after
+ * the last token is returned as final_state[n, h]. The library computes this
+ * with the chunkwise WY/UT algorithm (chunk size C = 64) as five HIP kernels:
+ * gate prefix sums, A-build + triangular solve, w/u products, the sequential
+ * state pass, and the output.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers except cu_seqlens_host. Tensors
+ *   are dense row-major with 16-byte aligned base addresses; anything else is
+ *   GDR_ERR_SHAPE.
+ * - The caller owns every buffer (inputs, outputs, workspace). The library
+ *   never allocates or frees device memory and keeps no global state apart
+ *   from a thread-local error string.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *   the call returns without synchronising. Argument errors are detected on
+ *   the host BEFORE any device work is enqueued. Launch failures return
+ *   GDR_ERR_HIP; faults during execution surface at the caller's next
+ *   synchronisation.
+ * - Ttot = batch * seq_len is the total token count. Token row t of a
+ *   [Ttot, H, D] tensor holds token t of the flattened (batch, time) axis.
+ * - NaN/Inf in the inputs are not checked and propagate.
+ * - Calls that share a workspace must not overlap in time.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDR_F32 = 0,   /* IEEE binary32 */
+    GDR_BF16 = 1   /* bfloat16; conversions from fp32 round to nearest even */
+} gdr_dtype_t;
+
+typedef enum {
+    GDR_OK = 0,
+    GDR_ERR_NULL = 1,        /* a required pointer is NULL                        */
+    GDR_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes, misalignment  */
+    GDR_ERR_DTYPE = 3,       /* unknown dtype or a dtype combination not allowed  */
+    GDR_ERR_UNSUPPORTED = 4, /* valid problem outside this build (head dims, C)   */
+    GDR_ERR_SEQLENS = 5,     /* cu_seqlens malformed or inconsistent with sizes   */
+    GDR_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required           */
+    GDR_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed        */
+} gdr_status_t;
+
+/*
+ * Problem description. Shapes follow the pages' statement of the problem
+ * (FLA DeltaNet article, section 5; ChunkGatedDeltaRule page, section 1 I/O
+ * table; FLA notes on note.zhuruihan.top, "fused recurrent fwd" shapes):
+ *   q, k   [batch, seq_len, num_qk_heads, head_dim_qk]   io_dtype
+ *   v      [batch, seq_len, num_v_heads,  head_dim_v]    io_dtype
+ *   o      [batch, seq_len, num_v_heads,  head_dim_v]    out_dtype
+ *   beta   [batch, seq_len, num_v_heads]                 beta_dtype
+ *   g      [batch, seq_len, num_v_heads]                 fp32, log-domain gate (<= 0)
+ *   state  [num_seqs, num_v_heads, head_dim_qk, head_dim_v]  fp32
+ * Variable-length batches: batch = 1, seq_len = total tokens, and
+ * cu_seqlens (int32, num_seqs + 1 entries, cu[0] = 0, non-decreasing,
+ * cu[num_seqs] = seq_len) marks sequence n as tokens [cu[n], cu[n+1]).
+ * Zero-length sequences are allowed (their final state equals the initial).
+ * Without cu_seqlens each batch row is one sequence and num_seqs = batch.
+ * Values derived inside the method are carried at fp32 accuracy whatever the
+ * input type; out_dtype = GDR_F32 returns o without a final bf16 rounding.
+ */
+typedef struct {
+    int64_t batch;          /* B >= 1; must be 1 when cu_seqlens is given          */
+    int64_t seq_len;        /* T >= 0 per batch row (total tokens when varlen)     */
+    int32_t num_qk_heads;   /* Nk >= 1                                             */
+    int32_t num_v_heads;    /* Nv >= 1, Nv % Nk == 0; V-head h reads q/k head h/(Nv/Nk) */
+    int32_t head_dim_qk;    /* dk: 32, 64 or 128 in this build                     */
+    int32_t head_dim_v;     /* dv: 32, 64 or 128 in this build                     */
+    int32_t chunk_size;     /* C: 64 in this build                                 */
+    int32_t num_seqs;       /* N: batch, or len(cu_seqlens) - 1                    */
+    int32_t io_dtype;       /* gdr_dtype_t of q, k and v                           */
+    int32_t beta_dtype;     /* gdr_dtype_t of beta: io_dtype or GDR_F32            */
+    int32_t out_dtype;      /* gdr_dtype_t of o: io_dtype or GDR_F32               */
+} gdr_problem_t;
+
+/*
+ * Host-only check of a problem description (and of cu_seqlens_host when not
+ * NULL). Touches no device memory. Returns the first error found.
+ */
+gdr_status_t gdr_validate(const gdr_problem_t* problem, const int32_t* cu_seqlens_host);
+
+/*
+ * Workspace bytes needed by gdr_chunk_fwd / gdr_chunk_fwd_debug for this
+ * problem (an upper bound that holds for every cu_seqlens with the same
+ * num_seqs and total length). The workspace must be 256-byte aligned.
+ */
+gdr_status_t gdr_chunk_fwd_workspace_size(const gdr_problem_t* problem, size_t* bytes);
+
+/*
+ * Chunked gated delta-rule forward.
+ *   q, k, v, beta  required inputs (layouts above).
+ *   g              NULL for the ungated rule (identical to g == 0).
+ *   scale          multiplies the output; callers usually pass dk^-0.5 (the
+ *                  FLA article's default, section 5).
+ *   initial_state  NULL means zeros.
+ *   cu_seqlens_dev, cu_seqlens_host: both NULL (fixed length), or both point
+ *                  to the same num_seqs + 1 offsets (device and host copies;
+ *                  the host copy sizes the launch without a device sync).
+ *                  If the two copies differ the results are unspecified, but
+ *                  every kernel still stays inside its buffers.
+ *   o              output, written for every token.
+ *   final_state    NULL to skip; else written for every sequence.
+ *   workspace      device scratch of at least gdr_chunk_fwd_workspace_size.
+ */
+gdr_status_t gdr_chunk_fwd(const gdr_problem_t* problem,
+                           const void* q, const void* k, const void* v,
+                           const float* g, const void* beta, float scale,
+                           const float* initial_state,
+                           const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                           void* o, float* final_state,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Intermediates of the five kernels, for per-kernel parity checks. Each
+ * pointer is a caller-owned device buffer (NULL to skip) that receives a copy
+ * of the workspace region in the layout the kernels use; sizes follow from
+ * the problem and NT, the number of chunks (sum over sequences of
+ * ceil(len / 64), numbered sequence by sequence in token order). T below is
+ * the input type: bf16 when io_dtype is bf16, fp32 when it is fp32. Values
+ * derived inside the method are kept in fp32.
+ *
+ * Fragment conventions (64-lane wavefront, lane l = 16 * qd + r):
+ *   a "pair fragment" holds, for each lane, 8 values of a 16 x 32 block X
+ *   (rows r, contraction index m in [0, 32)) with element e of lane l equal to
+ *   X[r][m(qd, e)], where m(qd, e) = 4*qd + e for e < 4 and 16 + 4*qd + e - 4
+ *   for e >= 4. An "accumulator tile" holds 4 values of a 16 x 16 block Y per
+ *   lane, element j of lane l equal to Y[4*qd + j][r].
+ *
+ * Layouts (Nv = num_v_heads, Nk = num_qk_heads, c = chunk, i/j = position in
+ * the chunk, tb = i / 16, db/kp = 16/32-blocks of dk, nb = 16-block of dv,
+ * tp = 32-block of chunk positions):
+ *   G    [Ttot][Nv] fp32                  chunk-local inclusive prefix sum of g
+ *   A    [Ttot][Nv][64] fp32              row i of (I + L)^-1 for the token's chunk;
+ *                                         zero above the diagonal and past the chunk end
+ *   W    [NT][Nv][4 tb][dk/32 kp] fp32 pair fragments (rows i, m = dk index)
+ *   U    [NT][Nv][4 tb][dv/16 nb] fp32 accumulator tiles (rows i, columns dv)
+ *   KT   [NT][Nk][dk/16 db][2 tp] T pair fragments of K^T (rows dk, m = position)
+ *   H    [NT][Nv][dv/16 nb][dk/32 kp] fp32 pair fragments of the chunk's
+ *                                     entering state transposed (rows dv, m = dk)
+ *   VN   [NT][Nv][dv/16 nb][2 tp] fp32 pair fragments of V_new^T (rows dv, m = position)
+ * Chunk positions past the end of a sequence hold zeros in W, U, KT and VN.
+ */
+typedef struct {
+    float* G;
+    void* A;
+    void* W;
+    void* U;
+    void* KT;
+    void* H;
+    void* VN;
+    int64_t num_chunks;     /* out: NT */
+} gdr_intermediates_t;
+
+/* Same computation as gdr_chunk_fwd, then copies the intermediates
+ * (asynchronously, on the same stream) into the buffers of `dbg`. */
+gdr_status_t gdr_chunk_fwd_debug(const gdr_problem_t* problem,
+                                 const void* q, const void* k, const void* v,
+                                 const float* g, const void* beta, float scale,
+                                 const float* initial_state,
+                                 const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                                 void* o, float* final_state,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 gdr_intermediates_t* dbg);
+
+/* Number of kernel stages timed by gdr_chunk_fwd_stage_times. */
+#define GDR_NUM_STAGES 6
+
+/*
+ * Runs gdr_chunk_fwd once with HIP events recorded on `stream` between its
+ * kernel launches, waits for the last event, and writes the elapsed
+ * milliseconds of each stage to stage_ms[GDR_NUM_STAGES]: [0] chunk table,
+ * [1] gate prefix sums, [2] A-build + solve, [3] w/u, [4] state pass,
+ * [5] output. Unlike gdr_chunk_fwd this call blocks until the run finishes.
+ */
+gdr_status_t gdr_chunk_fwd_stage_times(const gdr_problem_t* problem,
+                                       const void* q, const void* k, const void* v,
+                                       const float* g, const void* beta, float scale,
+                                       const float* initial_state,
+                                       const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                                       void* o, float* final_state,
+                                       void* workspace, size_t workspace_bytes, void* stream,
+                                       float* stage_ms);
+
+/* Static description of a status code. */
+const char* gdr_status_string(gdr_status_t status);
+
+/* Detail message of the last error reported on the calling thread ("" if none). */
+const char* gdr_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

@@ -1,0 +1,85 @@
+"""Unpack the kernels' fragment-major intermediates into natural layouts.
+
+Follows the layout contract stated in include/gdr.h (gdr_intermediates_t):
+lane l = 16*qd + r; a pair fragment holds X[r][m(qd, e)] with
+m(qd, e) = 4*qd + e (e < 4) or 16 + 4*qd + e - 4 (e >= 4); an accumulator tile
+holds Y[4*qd + j][r].
+"""
+import numpy as np
+
+_QD = np.arange(64) // 16
+_R = np.arange(64) % 16
+_E = np.arange(8)
+M_OF = np.where(_E[None, :] < 4, 4 * _QD[:, None] + _E[None, :], 16 + 4 * _QD[:, None] + _E[None, :] - 4)  # [64, 8]
+
+
+def unpack_pair(frag):
+    """[..., 64, 8] -> X [..., 16, 32]."""
+    frag = np.asarray(frag)
+    X = np.zeros(frag.shape[:-2] + (16, 32), dtype=np.float64)
+    X[..., _R[:, None], M_OF] = frag
+    return X
+
+
+def unpack_tile(tile):
+    """[..., 64, 4] -> Y [..., 16, 16]."""
+    tile = np.asarray(tile)
+    Y = np.zeros(tile.shape[:-2] + (16, 16), dtype=np.float64)
+    rows = 4 * _QD[:, None] + np.arange(4)[None, :]
+    Y[..., rows, _R[:, None]] = tile
+    return Y
+
+
+def W_natural(W):
+    """[NT, Nv, 4, dk/32, 64, 8] -> [NT, Nv, 64, dk] (rows = chunk position)."""
+    X = unpack_pair(W)                                    # [NT, Nv, 4, nkp, 16, 32]
+    NT, Nv, _, nkp = X.shape[:4]
+    return X.transpose(0, 1, 2, 4, 3, 5).reshape(NT, Nv, 64, nkp * 32)
+
+
+def U_natural(U):
+    """[NT, Nv, 4, dv/16, 64, 4] -> [NT, Nv, 64, dv]."""
+    Y = unpack_tile(U)                                    # [NT, Nv, 4, nnb, 16, 16]
+    NT, Nv, _, nnb = Y.shape[:4]
+    return Y.transpose(0, 1, 2, 4, 3, 5).reshape(NT, Nv, 64, nnb * 16)
+
+
+def KT_natural(KT):
+    """[NT, Nk, dk/16, 2, 64, 8] -> K [NT, Nk, 64, dk]."""
+    X = unpack_pair(KT)                                   # [NT, Nk, ndb, 2, 16(dk), 32(pos)]
+    NT, Nk, ndb = X.shape[:3]
+    KTn = X.transpose(0, 1, 2, 4, 3, 5).reshape(NT, Nk, ndb * 16, 64)
+    return KTn.transpose(0, 1, 3, 2)
+
+
+def H_natural(H):
+    """[NT, Nv, dv/16, dk/32, 64, 8] -> S [NT, Nv, dk, dv]."""
+    X = unpack_pair(H)                                    # [NT, Nv, nnb, nkp, 16(dv), 32(dk)]
+    NT, Nv, nnb, nkp = X.shape[:4]
+    ST = X.transpose(0, 1, 2, 4, 3, 5).reshape(NT, Nv, nnb * 16, nkp * 32)
+    return ST.transpose(0, 1, 3, 2)
+
+
+def VN_natural(VN):
+    """[NT, Nv, dv/16, 2, 64, 8] -> V_new [NT, Nv, 64, dv]."""
+    X = unpack_pair(VN)                                   # [NT, Nv, nnb, 2, 16(dv), 32(pos)]
+    NT, Nv, nnb = X.shape[:3]
+    VT = X.transpose(0, 1, 2, 4, 3, 5).reshape(NT, Nv, nnb * 16, 64)
+    return VT.transpose(0, 1, 3, 2)
+
+
+def chunk_rows_to_tokens(X, chunks, Ttot):
+    """[NT, H, 64, D] chunk-position rows -> [Ttot, H, D] token rows (valid rows only)."""
+    NT, H, _, D = X.shape
+    out = np.zeros((Ttot, H, D))
+    for c, (_, s, L) in enumerate(chunks):
+        out[s:s + L] = X[c, :, :L].transpose(1, 0, 2)
+    return out
+
+
+def pad_rows_are_zero(X, chunks):
+    """True if every chunk position past a chunk's end holds zeros."""
+    for c, (_, s, L) in enumerate(chunks):
+        if np.any(X[c, :, L:] != 0):
+            return False
+    return True

@@ -1,0 +1,135 @@
+"""C-ABI library: loads, exports every declared symbol, validates on the host.
+
+No device work: gdr_validate and gdr_chunk_fwd_workspace_size are host-only,
+and gdr_chunk_fwd is only called with arguments it must reject before any
+launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from chunkwise_gated_delta_local_amd import api
+    if not os.path.exists(api.library_path()):
+        from chunkwise_gated_delta_local_amd.build import build
+        build()
+    return api.load_library()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "gdr.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 7, names
+    for n in names:
+        assert hasattr(lib, n), n
+    from chunkwise_gated_delta_local_amd import api
+    assert sorted(api.EXPORTED) == names
+
+
+def prob(**kw):
+    from chunkwise_gated_delta_local_amd import api
+    base = dict(batch=2, seq_len=100, Nk=2, Nv=4, dk=64, dv=64, num_seqs=2, io_dtype=api.GDR_BF16)
+    base.update(kw)
+    return api.make_problem(**base)
+
+
+def status(p, cu=None):
+    from chunkwise_gated_delta_local_amd import api
+    return api.validate(p, cu)
+
+
+def test_validate_accepts_good_problems(lib):
+    assert status(prob()) == 0
+    assert status(prob(batch=1, seq_len=10, num_seqs=3), [0, 0, 4, 10]) == 0
+    assert status(prob(batch=1, seq_len=0, num_seqs=1), [0, 0]) == 0
+    for d in (32, 64, 128):
+        assert status(prob(dk=d, dv=128 if d == 32 else 32)) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), 2), (dict(seq_len=-1), 2), (dict(Nk=3, Nv=4), 2), (dict(Nk=0), 2),
+    (dict(io_dtype=7), 3), (dict(beta_dtype=1, io_dtype=0), 3),
+    (dict(dk=48), 4), (dict(dv=256), 4), (dict(chunk_size=32), 4),
+    (dict(num_seqs=3), 2),
+])
+def test_validate_rejects(lib, kw, code):
+    assert status(prob(**kw)) == code
+
+
+@pytest.mark.parametrize("cu,code", [
+    ([1, 5, 10], 5), ([0, 6, 5], 5), ([0, 4, 9], 5),
+])
+def test_validate_rejects_bad_seqlens(lib, cu, code):
+    assert status(prob(batch=1, seq_len=10, num_seqs=2), cu) == code
+
+
+def test_varlen_requires_batch_one(lib):
+    assert status(prob(batch=2, seq_len=10, num_seqs=2), [0, 5, 10]) == 5
+
+
+def test_error_message_and_status_strings(lib):
+    assert status(prob(dk=48)) == 4
+    assert b"head dims" in lib.gdr_last_error_message()
+    for s in range(8):
+        assert lib.gdr_status_string(s)
+
+
+def test_workspace_size_grows_with_tokens(lib):
+    from chunkwise_gated_delta_local_amd import api
+    a = api.workspace_size(prob(seq_len=64))
+    b = api.workspace_size(prob(seq_len=6400))
+    assert 0 < a < b
+    assert api.workspace_size(prob(seq_len=0)) > 0
+
+
+def test_fwd_rejects_before_launch(lib):
+    """Bad arguments come back as status codes with no device work."""
+    from chunkwise_gated_delta_local_amd import api
+    if torch.cuda.is_available():
+        pytest.skip("passes placeholder addresses; host-logic test for machines without a GPU")
+    p = prob()
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(1 << 20)          # never dereferenced: rejected first
+    args = [ctypes.byref(p), fake, fake, fake, None, fake, ctypes.c_float(1.0), None, None, None, fake, None]
+    # missing workspace
+    assert lib.gdr_chunk_fwd(*args, None, ctypes.c_size_t(0), None) == 6
+    # too-small workspace
+    assert lib.gdr_chunk_fwd(*args, fake, ctypes.c_size_t(256), None) == 6
+    # misaligned tensor
+    bad = list(args)
+    bad[1] = ctypes.c_void_p((1 << 20) + 4)
+    assert lib.gdr_chunk_fwd(*bad, fake, ctypes.c_size_t(1 << 40), None) == 2
+    # only one of the two cu_seqlens copies
+    bad = list(args)
+    bad[8] = fake
+    assert lib.gdr_chunk_fwd(*bad, fake, ctypes.c_size_t(1 << 40), None) == 1
+    # required pointer missing
+    bad = list(args)
+    bad[2] = null
+    assert lib.gdr_chunk_fwd(*bad, fake, ctypes.c_size_t(1 << 40), None) == 1
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    from chunkwise_gated_delta_local_amd import api
+    q = torch.zeros(1, 8, 1, 32)
+    with pytest.raises(ValueError):
+        api.chunk_fwd(q, q, q, torch.zeros(1, 8, 1))
+
+
+def test_validate_out_dtype(lib):
+    from chunkwise_gated_delta_local_amd import api
+    assert status(prob(out_dtype=api.GDR_F32)) == 0
+    assert status(prob(io_dtype=api.GDR_F32, out_dtype=api.GDR_BF16)) == 3
+    assert status(prob(out_dtype=9)) == 3

@@ -1,0 +1,193 @@
+"""GPU parity: the HIP path against the fp64 oracle, element by element.
+
+Error metric: max |x - ref| / rms(ref) per tensor; bounds 2e-2 for bf16 inputs
+and 1e-4 for fp32 inputs (fp32 accumulation in both). Inputs are the seeded
+synthetic workloads of chunkwise_gated_delta_local_amd.synth; the oracle sees
+exactly the rounded values the GPU sees.
+"""
+import numpy as np
+import pytest
+import torch
+
+import frag_layout as fl
+from gpu_common import TOL, bf16_rounding_excess, oracle_inputs, rel_err, run_gpu
+from oracle import chunked_forward, recurrence
+from chunkwise_gated_delta_local_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_reference(inp, heads=None):
+    """Token recurrence (fp64) for all value heads, or for a sample of them
+    (every sequence); the sampled run pairs each value head with its own q/k
+    head. Returns (o_ref [Ttot, H, dv], S_ref [N, H, dk, dv], heads)."""
+    w = inp["workload"]
+    sub = dict(inp)
+    if heads is not None:
+        heads = list(heads)
+        kheads = [h // (w.Nv // w.Nk) for h in heads]
+        sub.update(q=inp["q"][:, :, kheads], k=inp["k"][:, :, kheads], v=inp["v"][:, :, heads],
+                   beta=inp["beta"][:, :, heads], g=None if inp["g"] is None else inp["g"][:, :, heads],
+                   S0=None if inp["S0"] is None else inp["S0"][:, heads])
+    x = oracle_inputs(sub)
+    o_ref, S_ref = recurrence(x["q"], x["k"], x["v"], x["beta"], x["g"], x["scale"], x["S0"], x["cu"])
+    return o_ref, S_ref, heads
+
+
+def to_np(t, heads, shape):
+    if heads is not None:
+        t = t[:, :, heads] if t.dim() == 4 and t.shape[0] != shape[0] else t[:, heads]
+    return t.detach().cpu().double().numpy().reshape(shape)
+
+
+def check_run(inp, ref, tol, label, beta_f32=False):
+    """fp32 output: the max|d|/rms bound. bf16 inputs also run with bf16
+    output, which must sit within one bf16 step of the exact value."""
+    o_ref, S_ref, heads = ref
+    o32, S = run_gpu(inp, beta_f32=beta_f32, out_f32=True)
+    o = to_np(o32[:, :, heads] if heads is not None else o32, None, o_ref.shape)
+    Sn = to_np(S[:, heads] if heads is not None else S, None, S_ref.shape)
+    eo, es = rel_err(o, o_ref), rel_err(Sn, S_ref)
+    msg = "%s fp32-out err o %.3e  S_T %.3e (tol %.0e)" % (label, eo, es, tol)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(Sn)), label
+    if inp["workload"].dtype == "bf16":
+        o16, S16 = run_gpu(inp, beta_f32=beta_f32)
+        assert torch.equal(S16, S), (label, "final state depends on the output dtype")
+        ob = to_np(o16[:, :, heads] if heads is not None else o16, None, o_ref.shape)
+        excess = bf16_rounding_excess(ob, o_ref)
+        msg += " | bf16-out err o %.3e, max error in bf16 steps %.3f" % (rel_err(ob, o_ref), excess)
+        assert excess <= 1.0, (label, "bf16 output", excess)
+    print(msg, flush=True)
+    assert eo <= tol, (label, "o", eo)
+    assert es <= tol, (label, "S_T", es)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_config_full_parity(cfg):
+    w = synth.WORKLOADS[cfg]
+    inp = synth.generate(w, seed=cfg)
+    check_run(inp, oracle_reference(inp), TOL[w.dtype], "cfg%d" % cfg)
+
+
+@pytest.mark.parametrize("cfg,heads", [(4, (0, 17)), (5, (0, 9, 31))])
+def test_config_full_size_sampled_heads(cfg, heads):
+    """Full-size workloads as the bench runs them; the oracle computes a sample
+    of value heads (every sequence) one by one."""
+    w = synth.WORKLOADS[cfg]
+    inp = synth.generate(w, seed=cfg)
+    check_run(inp, oracle_reference(inp, heads), TOL[w.dtype], "cfg%d" % cfg)
+
+
+EDGE = [
+    # name, workload kwargs
+    ("T1", dict(B=2, T=1, Nk=1, Nv=2, dk=64, dv=64, dtype="bf16")),
+    ("T63", dict(B=2, T=63, Nk=2, Nv=2, dk=64, dv=32, dtype="bf16")),
+    ("T64", dict(B=1, T=64, Nk=1, Nv=4, dk=32, dv=128, dtype="bf16")),
+    ("T65", dict(B=3, T=65, Nk=2, Nv=8, dk=128, dv=64, dtype="bf16")),
+    ("f32_d64", dict(B=1, T=200, Nk=2, Nv=4, dk=64, dv=64, dtype="f32")),
+    ("f32_d128_ungated", dict(B=1, T=130, Nk=1, Nv=1, dk=128, dv=128, dtype="f32", gated=False)),
+    ("varlen_zero_len", dict(B=1, T=0, Nk=2, Nv=4, dk=64, dv=64, dtype="bf16", lengths=(0, 5, 0, 64, 129, 1))),
+    ("gqa4", dict(B=1, T=300, Nk=1, Nv=4, dk=128, dv=128, dtype="bf16")),
+    ("near_one_decay", dict(B=1, T=1000, Nk=1, Nv=2, dk=128, dv=128, dtype="bf16", g_mean=6.0, s0="zero")),
+    ("strong_decay", dict(B=1, T=256, Nk=1, Nv=2, dk=64, dv=64, dtype="bf16", g_mean=-2.0)),
+]
+
+
+@pytest.mark.parametrize("name,kw", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(name, kw):
+    w = synth.custom(name, **kw)
+    inp = synth.generate(w, seed=100 + len(name))
+    check_run(inp, oracle_reference(inp), TOL[w.dtype], name)
+
+
+def test_beta_f32_with_bf16_io():
+    w = synth.custom("beta32", B=1, T=150, Nk=2, Nv=2, dk=64, dv=64, dtype="bf16")
+    inp = synth.generate(w, seed=7)
+    check_run(inp, oracle_reference(inp), TOL["bf16"], "beta_f32", beta_f32=True)
+
+
+def test_absent_gate_equals_zero_gate_bitwise():
+    w = synth.custom("g0", B=1, T=200, Nk=1, Nv=2, dk=64, dv=64, dtype="bf16")
+    inp = synth.generate(w, seed=8)
+    inp_zero = dict(inp, g=torch.zeros_like(inp["g"]))
+    inp_none = dict(inp, g=None)
+    o1, S1 = run_gpu(inp_zero)
+    o2, S2 = run_gpu(inp_none)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_absent_state_equals_zero_state_bitwise():
+    w = synth.custom("s0", B=2, T=100, Nk=1, Nv=2, dk=64, dv=64, dtype="bf16")
+    inp = synth.generate(w, seed=9)
+    o1, S1 = run_gpu(dict(inp, S0=torch.zeros_like(inp["S0"])))
+    o2, S2 = run_gpu(dict(inp, S0=None))
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_deterministic_bitwise():
+    w = synth.custom("det", B=1, T=500, Nk=2, Nv=4, dk=128, dv=128, dtype="bf16")
+    inp = synth.generate(w, seed=10)
+    o1, S1 = run_gpu(inp)
+    o2, S2 = run_gpu(inp)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_no_final_state_requested():
+    w = synth.custom("nofs", B=1, T=100, Nk=1, Nv=1, dk=64, dv=64, dtype="bf16")
+    inp = synth.generate(w, seed=11)
+    o, S = run_gpu(inp, output_final_state=False)
+    assert S is None
+    o2, S2 = run_gpu(inp)
+    assert torch.equal(o, o2)
+
+
+def test_empty_sequence_batch_returns_initial_state():
+    w = synth.custom("empty", B=1, T=0, Nk=1, Nv=2, dk=32, dv=32, dtype="bf16", lengths=(0, 0))
+    inp = synth.generate(w, seed=12)
+    o, S = run_gpu(inp)
+    assert o.numel() == 0
+    assert torch.equal(S.cpu(), inp["S0"])
+
+
+# ------------------------------------------------------------ per-kernel parity
+KERNEL_CASES = [
+    ("cfg2", synth.WORKLOADS[2], 2),
+    ("gqa_varlen", synth.custom("gqa_varlen", B=1, T=0, Nk=2, Nv=4, dk=128, dv=128, dtype="bf16",
+                                lengths=(1, 63, 64, 65, 130)), 21),
+    ("f32", synth.custom("f32k", B=1, T=150, Nk=1, Nv=2, dk=32, dv=64, dtype="f32"), 22),
+]
+
+
+@pytest.mark.parametrize("name,w,seed", KERNEL_CASES, ids=[c[0] for c in KERNEL_CASES])
+def test_intermediates_match_chunked_oracle(name, w, seed):
+    """Each of the five kernels against the chunked oracle's intermediate:
+    K1 -> G, K2 -> A, K3 -> W, U (and K^T), K4 -> H, V_new, S_T, K5 -> o."""
+    inp = synth.generate(w, seed=seed)
+    res = run_gpu(inp, debug=True, out_f32=True)
+    x = oracle_inputs(inp)
+    ref = chunked_forward(x["q"], x["k"], x["v"], x["beta"], x["g"], x["scale"], x["S0"], x["cu"],
+                          intermediates=True)
+    chunks = ref["chunks"]
+    Ttot = x["q"].shape[0]
+    tol = TOL[w.dtype]
+    assert res["num_chunks"] == len(chunks)
+    cpu = lambda t: t.detach().cpu().double().numpy()
+    errs = {}
+    errs["G"] = rel_err(cpu(res["G"]), ref["G"]) if w.gated else float(np.max(np.abs(cpu(res["G"]))))
+    errs["A"] = rel_err(cpu(res["A"]), ref["A"])
+    W = fl.W_natural(cpu(res["W"]))
+    U = fl.U_natural(cpu(res["U"]))
+    VN = fl.VN_natural(cpu(res["VN"]))
+    K = fl.KT_natural(cpu(res["KT"]))
+    assert fl.pad_rows_are_zero(W, chunks) and fl.pad_rows_are_zero(U, chunks)
+    assert fl.pad_rows_are_zero(VN, chunks) and fl.pad_rows_are_zero(K, chunks)
+    errs["W"] = rel_err(fl.chunk_rows_to_tokens(W, chunks, Ttot), ref["W"])
+    errs["U"] = rel_err(fl.chunk_rows_to_tokens(U, chunks, Ttot), ref["U"])
+    errs["K"] = rel_err(fl.chunk_rows_to_tokens(K, chunks, Ttot), x["k"])
+    errs["H"] = rel_err(fl.H_natural(cpu(res["H"])), ref["h"])
+    errs["V_new"] = rel_err(fl.chunk_rows_to_tokens(VN, chunks, Ttot), ref["V_new"])
+    errs["S_T"] = rel_err(cpu(res["S_T"]), ref["S_T"])
+    errs["o"] = rel_err(cpu(res["o"]).reshape(ref["o"].shape), ref["o"])
+    print(name, {k: "%.2e" % v for k, v in errs.items()}, flush=True)
+    for key, e in errs.items():
+        assert e <= tol, (name, key, e)
