@@ -1,0 +1,212 @@
+#!/usr/bin/env python
+"""Benchmark of the chunked gated delta-rule forward on one MI355X.
+
+One step is one complete forward pass (chunk table, gate prefix sums, A-build
++ solve, w/u products, state pass, output) over one batch of the long-context
+GQA workload: T = 65536 tokens, 16 q/k heads, 32 value heads, dk = dv = 128,
+bf16 q/k/v/beta, fp32 gates (g = logsigmoid(N(6, 1))) and state, S0 = 0,
+seeded synthetic data. Inputs are resident in HBM before the timed region.
+
+Prints one JSON line with the throughput (tokens/s), the roofline of the
+dominant kernel (its average duration measured with HIP events recorded on
+the launch stream inside the timed region), and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from chunkwise_gated_delta_local_amd import api, synth  # noqa: E402
+
+METRIC = "fwd tokens/s at Hv=32,dk=dv=128,T=64k bf16; % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ("chunkwise_gated_delta_local_amd/csrc/gdr_kernels.hip",
+                  "chunkwise_gated_delta_local_amd/csrc/gdr_device.hpp")
+STAGE_KERNELS = ("k_chunk_table", "k_gate_cumsum", "k_build_solve", "k_wu", "k_state", "k_output")
+
+
+def stage_algorithmic_bytes(w: synth.Workload, Ttot: int, N: int, NT: int, out_bytes: int) -> dict:
+    """Bytes each kernel must move by its own inputs and outputs: every tensor it
+    reads read once, every tensor it writes written once, in its stored type."""
+    es = 2 if w.dtype == "bf16" else 4
+    Nv, Nk, dk, dv = w.Nv, w.Nk, w.dk, w.dv
+    tv = Ttot * Nv                      # token-heads (value heads)
+    tk = Ttot * Nk                      # token-heads (q/k heads)
+    beta_b = es
+    return {
+        "k_chunk_table": 4 * (N + 1) + 16 * NT,
+        "k_gate_cumsum": tv * (4 + 4),                                        # g in, G out
+        "k_build_solve": tk * dk * es + tv * (beta_b + 4) + tv * 64 * 4,       # k, beta, G in; A out
+        "k_wu": tk * dk * es + tv * dv * es + tv * (beta_b + 4) + tv * 64 * 4  # k, v, beta, G, A in
+                + tv * (dk + dv) * 4 + NT * Nk * 64 * dk * es,                # W, U, K^T out
+        "k_state": tv * (dk + dv) * 4 + NT * Nk * 64 * dk * es + tv * 4       # W, U, K^T, G in
+                   + NT * Nv * dk * dv * 4 + tv * dv * 4 + N * Nv * dk * dv * 4,  # H, V_new, S_T out
+        "k_output": 2 * tk * dk * es + tv * 4 + NT * Nv * dk * dv * 4 + tv * dv * 4  # q, k, G, H, V_new in
+                    + tv * dv * out_bytes,                                    # o out
+    }
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when there is none or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_counters.txt" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                vals[key.strip()] = val.strip()
+    if vals.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp: dict, target_seconds: float) -> dict:
+    """The fp64 token-recurrence oracle on the host cores, on the first Ts tokens
+    (all heads) of the same workload; Ts is calibrated to about target_seconds."""
+    from oracle import recurrence
+
+    w = inp["workload"]
+    T = inp["q"].shape[1]
+    threads = len(os.sched_getaffinity(0))
+
+    def sample(ts):
+        f = lambda t: None if t is None else t[0, :ts].double().numpy()
+        return (f(inp["q"]), f(inp["k"]), f(inp["v"]), f(inp["beta"]), f(inp["g"]))
+
+    def run(ts):
+        q, k, v, b, g = sample(ts)
+        t0 = time.perf_counter()
+        recurrence(q, k, v, b, g, inp["scale"], None, np.array([0, ts]), threads=threads)
+        return time.perf_counter() - t0
+
+    probe = min(256, T)
+    dt = run(probe)
+    ts = int(min(T, max(probe, probe * target_seconds / max(dt, 1e-6))))
+    ts = max(64, (ts // 64) * 64) if ts < T else T
+    dt = run(ts)
+    return {
+        "value": ts / dt,
+        "unit": "tokens/s",
+        "cores": int(getattr(recurrence, "last_threads", threads)),
+        "kind": "oracle",
+        "sample": "tokens [0, %d) of the %d-token sequence, all %d value heads; fp64 C token "
+                  "recurrence, OpenMP over heads; %.1f s" % (ts, T, w.Nv, dt),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=5, help="synth.WORKLOADS index (default 5)")
+    ap.add_argument("--out-dtype", choices=("io", "f32"), default="io")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget; 0 skips it")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this implementation runs on one GPU only; --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+
+    w = synth.WORKLOADS[args.workload]
+    inp = synth.generate(w, seed=args.workload)
+    dev = torch.device("cuda:0")
+    d = {k: (None if inp[k] is None else inp[k].to(dev)) for k in ("q", "k", "v", "beta", "g", "S0", "cu_seqlens")}
+    out_dtype = torch.float32 if args.out_dtype == "f32" else None
+    fwd = api.Forward(d["q"], d["k"], d["v"], d["beta"], g=d["g"], scale=inp["scale"], initial_state=d["S0"],
+                      output_final_state=True, cu_seqlens=d["cu_seqlens"], cu_seqlens_cpu=inp["cu_seqlens"],
+                      out_dtype=out_dtype)
+    B, T = inp["q"].shape[:2]
+    Ttot = B * T
+    N = inp["N"]
+    NT = api.num_chunks(B, T, None if inp["cu_seqlens"] is None else inp["cu_seqlens"].to(torch.int32))
+
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(api.NUM_STAGES + 1)] for _ in range(K)]
+    for row in events:                     # create the HIP events before timing
+        for e in row:
+            e.record()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(K):
+        fwd.timed(events[s])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / K
+    stage_ms = np.array([[events[s][i].elapsed_time(events[s][i + 1]) for i in range(api.NUM_STAGES)]
+                         for s in range(K)]).mean(axis=0)
+
+    out_bytes = 4 if (args.out_dtype == "f32" or w.dtype == "f32") else 2
+    alg = stage_algorithmic_bytes(w, Ttot, N, NT, out_bytes)
+    dom = int(np.argmax(stage_ms))
+    kname = STAGE_KERNELS[dom]
+    achieved = alg[kname] / (stage_ms[dom] * 1e-3) / 1e9
+    traffic = counter_traffic(kname, "T65536_Nk16_Nv32_d128" if args.workload == 5 else "workload%d" % args.workload)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(inp, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": Ttot * K / (total_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": Ttot, "Nk": w.Nk, "Nv": w.Nv, "dk": w.dk, "dv": w.dv, "chunk": 64,
+                   "gated": w.gated, "g": "logsigmoid(N(%g,1))" % w.g_mean, "S0": w.s0,
+                   "out_dtype": "f32" if out_bytes == 4 else w.dtype, "seed": args.workload},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": alg[kname], "avg_ms": float(stage_ms[dom])},
+        "cpu_baseline": cpu,
+        "stage_ms": {STAGE_KERNELS[i]: float(stage_ms[i]) for i in range(api.NUM_STAGES)},
+        "end_to_end_hbm_frac": (24768.0 * Ttot / (ms_per_step * 1e-3) / 1e9) / HBM_PEAK_GBS
+        if args.workload == 5 and out_bytes == 2 else None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,7 +22,7 @@ STAGE_NAMES = ("chunk_table", "gate_cumsum", "build_solve", "wu", "state", "outp
 _DTYPES = {torch.float32: GDR_F32, torch.bfloat16: GDR_BF16}
 
 EXPORTED = ("gdr_validate", "gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_debug",
-            "gdr_chunk_fwd_stage_times", "gdr_status_string", "gdr_last_error_message")
+            "gdr_chunk_fwd_timed", "gdr_status_string", "gdr_last_error_message")
 
 
 class Problem(ctypes.Structure):
@@ -64,9 +64,9 @@ def load_library():
     lib.gdr_chunk_fwd_workspace_size.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
     lib.gdr_chunk_fwd.argtypes = fwd_args
     lib.gdr_chunk_fwd_debug.argtypes = fwd_args + [ctypes.POINTER(Intermediates)]
-    lib.gdr_chunk_fwd_stage_times.argtypes = fwd_args + [ctypes.POINTER(ctypes.c_float)]
+    lib.gdr_chunk_fwd_timed.argtypes = fwd_args + [P]
     for f in ("gdr_validate", "gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_debug",
-              "gdr_chunk_fwd_stage_times"):
+              "gdr_chunk_fwd_timed"):
         getattr(lib, f).restype = ctypes.c_int
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_status_string.restype = ctypes.c_char_p
@@ -203,13 +203,25 @@ def chunk_fwd_debug(q, k, v, beta, g=None, scale=None, initial_state=None, outpu
     return out
 
 
-def chunk_fwd_stage_times(q, k, v, beta, g=None, scale=None, initial_state=None, output_final_state=True,
-                          cu_seqlens=None, cu_seqlens_cpu=None, chunk_size=64, out_dtype=None):
-    """Run once with HIP events between the stages; returns (o, S_T, stage_ms)."""
-    lib = load_library()
-    prob, args, o, S_T, keep = _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu,
-                                        chunk_size, output_final_state, out_dtype)
-    ms = (ctypes.c_float * NUM_STAGES)()
-    _check(lib.gdr_chunk_fwd_stage_times(*args, ms))
-    del keep
-    return o, S_T, [float(x) for x in ms]
+class Forward:
+    """A prepared gdr_chunk_fwd call on fixed tensors, for repeated launches
+    (benchmarks). Outputs and workspace are allocated once; each call enqueues
+    the whole forward on the stream that was current at construction."""
+
+    def __init__(self, q, k, v, beta, g=None, scale=None, initial_state=None, output_final_state=True,
+                 cu_seqlens=None, cu_seqlens_cpu=None, chunk_size=64, out_dtype=None):
+        self.lib = load_library()
+        self.problem, self.args, self.o, self.final_state, self._keep = _prepare(
+            q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu, chunk_size,
+            output_final_state, out_dtype)
+        self.inputs = (q, k, v, beta, g, initial_state)       # keep alive while prepared
+
+    def __call__(self):
+        _check(self.lib.gdr_chunk_fwd(*self.args))
+
+    def timed(self, events):
+        """Enqueue one forward and record the NUM_STAGES + 1 torch.cuda.Event
+        objects around its stages (they must have been recorded once, so that
+        their HIP handles exist)."""
+        handles = (ctypes.c_void_p * (NUM_STAGES + 1))(*[e.cuda_event for e in events])
+        _check(self.lib.gdr_chunk_fwd_timed(*self.args, handles))

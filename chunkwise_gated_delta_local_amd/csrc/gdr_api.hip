@@ -235,30 +235,18 @@ gdr_status_t gdr_chunk_fwd_debug(const gdr_problem_t* p, const void* q, const vo
     return GDR_OK;
 }
 
-gdr_status_t gdr_chunk_fwd_stage_times(const gdr_problem_t* p, const void* q, const void* k, const void* v,
-                                       const float* g, const void* beta, float scale, const float* initial_state,
-                                       const int32_t* cu_dev, const int32_t* cu_host, void* o, float* final_state,
-                                       void* workspace, size_t workspace_bytes, void* stream, float* stage_ms) {
-    if (!stage_ms) return fail(GDR_ERR_NULL, "stage_ms is NULL");
+gdr_status_t gdr_chunk_fwd_timed(const gdr_problem_t* p, const void* q, const void* k, const void* v,
+                                 const float* g, const void* beta, float scale, const float* initial_state,
+                                 const int32_t* cu_dev, const int32_t* cu_host, void* o, float* final_state,
+                                 void* workspace, size_t workspace_bytes, void* stream, void* const* stage_events) {
+    if (!stage_events) return fail(GDR_ERR_NULL, "stage_events is NULL");
     hipEvent_t ev[GDR_NUM_STAGES + 1];
-    int made = 0;
-    for (; made < GDR_NUM_STAGES + 1; ++made)
-        if (hipEventCreate(&ev[made]) != hipSuccess) break;
-    gdr_status_t st = GDR_OK;
-    if (made < GDR_NUM_STAGES + 1) {
-        st = fail(GDR_ERR_HIP, "hipEventCreate failed");
-    } else {
-        st = run(p, q, k, v, g, beta, scale, initial_state, cu_dev, cu_host, o, final_state, workspace,
-                 workspace_bytes, stream, ev, nullptr, nullptr);
-        if (st == GDR_OK) {
-            hipError_t e = hipEventSynchronize(ev[GDR_NUM_STAGES]);
-            for (int i = 0; i < GDR_NUM_STAGES && e == hipSuccess; ++i)
-                e = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
-            if (e != hipSuccess) st = fail(GDR_ERR_HIP, "event timing failed: %s", hipGetErrorString(e));
-        }
+    for (int i = 0; i <= GDR_NUM_STAGES; ++i) {
+        if (!stage_events[i]) return fail(GDR_ERR_NULL, "stage_events[%d] is NULL", i);
+        ev[i] = static_cast<hipEvent_t>(stage_events[i]);
     }
-    for (int i = 0; i < made; ++i) (void)hipEventDestroy(ev[i]);
-    return st;
+    return run(p, q, k, v, g, beta, scale, initial_state, cu_dev, cu_host, o, final_state, workspace,
+               workspace_bytes, stream, ev, nullptr, nullptr);
 }
 
 const char* gdr_status_string(gdr_status_t s) {

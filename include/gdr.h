@@ -179,24 +179,26 @@ gdr_status_t gdr_chunk_fwd_debug(const gdr_problem_t* problem,
                                  void* workspace, size_t workspace_bytes, void* stream,
                                  gdr_intermediates_t* dbg);
 
-/* Number of kernel stages timed by gdr_chunk_fwd_stage_times. */
+/* Number of kernel stages of one forward call. */
 #define GDR_NUM_STAGES 6
 
 /*
- * Runs gdr_chunk_fwd once with HIP events recorded on `stream` between its
- * kernel launches, waits for the last event, and writes the elapsed
- * milliseconds of each stage to stage_ms[GDR_NUM_STAGES]: [0] chunk table,
- * [1] gate prefix sums, [2] A-build + solve, [3] w/u, [4] state pass,
- * [5] output. Unlike gdr_chunk_fwd this call blocks until the run finishes.
+ * As gdr_chunk_fwd, and also records the caller-created HIP events
+ * stage_events[0 .. GDR_NUM_STAGES] (hipEvent_t handles) on `stream`: [0]
+ * before the first kernel and [i] after stage i, the stages being [1] chunk
+ * table, [2] gate prefix sums, [3] A-build + solve, [4] w/u, [5] state pass,
+ * [6] output. Nothing is synchronised; the caller reads the elapsed times
+ * once the stream has passed the last event. Used to time each kernel inside
+ * a benchmark's timed region.
  */
-gdr_status_t gdr_chunk_fwd_stage_times(const gdr_problem_t* problem,
-                                       const void* q, const void* k, const void* v,
-                                       const float* g, const void* beta, float scale,
-                                       const float* initial_state,
-                                       const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
-                                       void* o, float* final_state,
-                                       void* workspace, size_t workspace_bytes, void* stream,
-                                       float* stage_ms);
+gdr_status_t gdr_chunk_fwd_timed(const gdr_problem_t* problem,
+                                 const void* q, const void* k, const void* v,
+                                 const float* g, const void* beta, float scale,
+                                 const float* initial_state,
+                                 const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                                 void* o, float* final_state,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 void* const* stage_events);
 
 /* Static description of a status code. */
 const char* gdr_status_string(gdr_status_t status);
