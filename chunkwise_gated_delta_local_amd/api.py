@@ -21,8 +21,9 @@ NUM_STAGES = 6
 STAGE_NAMES = ("chunk_table", "gate_cumsum", "build_solve", "wu", "state", "output")
 _DTYPES = {torch.float32: GDR_F32, torch.bfloat16: GDR_BF16}
 
-EXPORTED = ("gdr_validate", "gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_debug",
-            "gdr_chunk_fwd_timed", "gdr_status_string", "gdr_last_error_message")
+EXPORTED = ("gdr_validate", "gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd_debug_workspace_size",
+            "gdr_chunk_fwd", "gdr_chunk_fwd_debug", "gdr_chunk_fwd_timed", "gdr_status_string",
+            "gdr_last_error_message")
 
 
 class Problem(ctypes.Structure):
@@ -37,7 +38,7 @@ class Problem(ctypes.Structure):
 class Intermediates(ctypes.Structure):
     _fields_ = [("G", ctypes.c_void_p), ("A", ctypes.c_void_p), ("W", ctypes.c_void_p),
                 ("U", ctypes.c_void_p), ("KT", ctypes.c_void_p), ("H", ctypes.c_void_p),
-                ("VN", ctypes.c_void_p), ("num_chunks", ctypes.c_int64)]
+                ("VN", ctypes.c_void_p), ("T", ctypes.c_void_p), ("num_chunks", ctypes.c_int64)]
 
 
 class GdrError(RuntimeError):
@@ -62,11 +63,12 @@ def load_library():
     fwd_args = [PP, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.gdr_validate.argtypes = [PP, P]
     lib.gdr_chunk_fwd_workspace_size.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdr_chunk_fwd_debug_workspace_size.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
     lib.gdr_chunk_fwd.argtypes = fwd_args
     lib.gdr_chunk_fwd_debug.argtypes = fwd_args + [ctypes.POINTER(Intermediates)]
     lib.gdr_chunk_fwd_timed.argtypes = fwd_args + [P]
-    for f in ("gdr_validate", "gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_debug",
-              "gdr_chunk_fwd_timed"):
+    for f in ("gdr_validate", "gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd_debug_workspace_size",
+              "gdr_chunk_fwd", "gdr_chunk_fwd_debug", "gdr_chunk_fwd_timed"):
         getattr(lib, f).restype = ctypes.c_int
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_status_string.restype = ctypes.c_char_p
@@ -98,10 +100,11 @@ def validate(problem: Problem, cu_seqlens_host=None) -> int:
     return lib.gdr_validate(ctypes.byref(problem), None if cu is None else ctypes.c_void_p(cu.data_ptr()))
 
 
-def workspace_size(problem: Problem) -> int:
+def workspace_size(problem: Problem, debug: bool = False) -> int:
     lib = load_library()
     n = ctypes.c_size_t(0)
-    _check(lib.gdr_chunk_fwd_workspace_size(ctypes.byref(problem), ctypes.byref(n)))
+    fn = lib.gdr_chunk_fwd_debug_workspace_size if debug else lib.gdr_chunk_fwd_workspace_size
+    _check(fn(ctypes.byref(problem), ctypes.byref(n)))
     return int(n.value)
 
 
@@ -110,7 +113,7 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 def _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu, chunk_size,
-             output_final_state, out_dtype):
+             output_final_state, out_dtype, debug=False):
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:2] != q.shape[:2]:
         raise ValueError("expected q, k [B,T,Nk,dk] and v [B,T,Nv,dv]")
     dev = q.device
@@ -147,7 +150,7 @@ def _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu,
                         _DTYPES[out_dtype])
     o = torch.empty(v.shape, dtype=out_dtype, device=dev)
     S_T = torch.empty((N, Nv, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
-    ws = torch.empty(workspace_size(prob), dtype=torch.uint8, device=dev)
+    ws = torch.empty(workspace_size(prob, debug), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     args = [ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), ctypes.c_float(scale),
             _ptr(initial_state), _ptr(cu_dev), _ptr(cu_host), _ptr(o), _ptr(S_T), _ptr(ws),
@@ -182,7 +185,7 @@ def chunk_fwd_debug(q, k, v, beta, g=None, scale=None, initial_state=None, outpu
     (include/gdr.h, gdr_intermediates_t). Returns a dict."""
     lib = load_library()
     prob, args, o, S_T, keep = _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu,
-                                        chunk_size, output_final_state, out_dtype)
+                                        chunk_size, output_final_state, out_dtype, debug=True)
     B, T, Nk, dk = q.shape
     Nv, dv = v.shape[2], v.shape[3]
     NT = num_chunks(B, T, keep[1])
@@ -195,8 +198,9 @@ def chunk_fwd_debug(q, k, v, beta, g=None, scale=None, initial_state=None, outpu
         KT=torch.zeros((NT, Nk, dk // 16, 2, 64, 8), dtype=dt, device=dev),
         H=torch.zeros((NT, Nv, dv // 16, dk // 32, 64, 8), dtype=torch.float32, device=dev),
         VN=torch.zeros((NT, Nv, dv // 16, 2, 64, 8), dtype=torch.float32, device=dev),
+        T=torch.zeros((NT, Nv, 6, 2, 64, 8), dtype=dt, device=dev) if dt == torch.bfloat16 else None,
     )
-    dbg = Intermediates(*(_ptr(out[n]) for n in ("G", "A", "W", "U", "KT", "H", "VN")), 0)
+    dbg = Intermediates(*(_ptr(out[n]) for n in ("G", "A", "W", "U", "KT", "H", "VN", "T")), 0)
     _check(lib.gdr_chunk_fwd_debug(*args, ctypes.byref(dbg)))
     out.update(o=o, S_T=S_T, num_chunks=int(dbg.num_chunks))
     del keep

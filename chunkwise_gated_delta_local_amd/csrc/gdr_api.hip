@@ -25,8 +25,10 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Plan {
     int64_t Ttot;
     int32_t nt_cap;
-    size_t off_seq, off_start, off_len, off_first, off_G, off_A, off_W, off_U, off_KT, off_H, off_VN, total;
-    size_t sz_A, sz_W, sz_U, sz_KT, sz_H, sz_VN;   // bytes of the first NT chunks are a prefix
+    size_t off_seq, off_start, off_len, off_first, off_G, off_Tf, off_A, off_W, off_U, off_KT, off_H, off_VN;
+    size_t sz_Tf, sz_A, sz_W, sz_U, sz_KT, sz_H, sz_VN;   // per chunk except A (whole)
+    size_t production;         // bytes gdr_chunk_fwd needs
+    size_t reference;          // bytes gdr_chunk_fwd_debug needs (five separate kernels)
 };
 
 bool supported_dim(int d) { return d == 32 || d == 64 || d == 128; }
@@ -94,6 +96,10 @@ Plan make_plan(const gdr_problem_t* p) {
     pl.off_len = take(cap * 4);
     pl.off_first = take(((size_t)p->num_seqs + 1) * 4);
     pl.off_G = take(T * Nv * 4);
+    const bool bf = p->io_dtype == GDR_BF16;
+    pl.sz_Tf = bf ? Nv * 6 * 2 * 512 * es : 0;   // T = A diag(beta): 6 split pair fragments
+    pl.off_Tf = take(cap * pl.sz_Tf);
+    const size_t fused_end = off;
     pl.sz_A = T * Nv * 64 * 4;
     pl.off_A = take(pl.sz_A);
     pl.sz_W = Nv * 64 * dk * 4;            // per chunk
@@ -106,7 +112,8 @@ Plan make_plan(const gdr_problem_t* p) {
     pl.off_H = take(cap * pl.sz_H);
     pl.sz_VN = Nv * 64 * dv * 4;
     pl.off_VN = take(cap * pl.sz_VN);
-    pl.total = off;
+    pl.reference = off;
+    pl.production = bf ? fused_end : off;
     return pl;
 }
 
@@ -115,7 +122,7 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
 gdr_status_t run(const gdr_problem_t* p, const void* q, const void* k, const void* v, const float* g,
                  const void* beta, float scale, const float* S0, const int32_t* cu_dev, const int32_t* cu_host,
                  void* o, float* ST, void* ws, size_t ws_bytes, void* stream, hipEvent_t* events,
-                 Plan* plan_out, int32_t* nt_out) {
+                 bool reference, Plan* plan_out, int32_t* nt_out) {
     gdr_status_t st = check_problem(p);
     if (st != GDR_OK) return st;
     if ((cu_dev == nullptr) != (cu_host == nullptr))
@@ -131,8 +138,8 @@ gdr_status_t run(const gdr_problem_t* p, const void* q, const void* k, const voi
     Plan pl = make_plan(p);
     if (!ws) return fail(GDR_ERR_WORKSPACE, "workspace is NULL");
     if (((uintptr_t)ws & 255) != 0) return fail(GDR_ERR_WORKSPACE, "workspace not 256-byte aligned");
-    if (ws_bytes < pl.total)
-        return fail(GDR_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, pl.total);
+    const size_t need = reference ? pl.reference : pl.production;
+    if (ws_bytes < need) return fail(GDR_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
 
     int64_t nt = 0;
     for (int32_t n = 0; n < p->num_seqs; ++n) {
@@ -166,6 +173,8 @@ gdr_status_t run(const gdr_problem_t* p, const void* q, const void* k, const voi
     a.G = reinterpret_cast<float*>(w + pl.off_G);
     a.A = w + pl.off_A; a.W = w + pl.off_W; a.U = w + pl.off_U; a.KT = w + pl.off_KT;
     a.H = w + pl.off_H; a.VN = w + pl.off_VN;
+    a.Tf = pl.sz_Tf ? w + pl.off_Tf : nullptr;
+    a.reference = reference;
     a.stream = static_cast<hipStream_t>(stream);
 
     hipError_t e = gdr::launch_forward(a, events);
@@ -192,7 +201,15 @@ gdr_status_t gdr_chunk_fwd_workspace_size(const gdr_problem_t* problem, size_t* 
     if (!bytes) return fail(GDR_ERR_NULL, "bytes is NULL");
     gdr_status_t st = check_problem(problem);
     if (st != GDR_OK) return st;
-    *bytes = make_plan(problem).total;
+    *bytes = make_plan(problem).production;
+    return GDR_OK;
+}
+
+gdr_status_t gdr_chunk_fwd_debug_workspace_size(const gdr_problem_t* problem, size_t* bytes) {
+    if (!bytes) return fail(GDR_ERR_NULL, "bytes is NULL");
+    gdr_status_t st = check_problem(problem);
+    if (st != GDR_OK) return st;
+    *bytes = make_plan(problem).reference;
     return GDR_OK;
 }
 
@@ -201,7 +218,7 @@ gdr_status_t gdr_chunk_fwd(const gdr_problem_t* p, const void* q, const void* k,
                            const int32_t* cu_host, void* o, float* final_state, void* workspace,
                            size_t workspace_bytes, void* stream) {
     return run(p, q, k, v, g, beta, scale, initial_state, cu_dev, cu_host, o, final_state, workspace,
-               workspace_bytes, stream, nullptr, nullptr, nullptr);
+               workspace_bytes, stream, nullptr, false, nullptr, nullptr);
 }
 
 gdr_status_t gdr_chunk_fwd_debug(const gdr_problem_t* p, const void* q, const void* k, const void* v,
@@ -212,7 +229,7 @@ gdr_status_t gdr_chunk_fwd_debug(const gdr_problem_t* p, const void* q, const vo
     Plan pl;
     int32_t nt = 0;
     gdr_status_t st = run(p, q, k, v, g, beta, scale, initial_state, cu_dev, cu_host, o, final_state, workspace,
-                          workspace_bytes, stream, nullptr, &pl, &nt);
+                          workspace_bytes, stream, nullptr, true, &pl, &nt);
     if (st != GDR_OK) return st;
     dbg->num_chunks = nt;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -226,6 +243,7 @@ gdr_status_t gdr_chunk_fwd_debug(const gdr_problem_t* p, const void* q, const vo
         {dbg->KT, pl.off_KT, (size_t)nt * pl.sz_KT},
         {dbg->H, pl.off_H, (size_t)nt * pl.sz_H},
         {dbg->VN, pl.off_VN, (size_t)nt * pl.sz_VN},
+        {dbg->T, pl.off_Tf, (size_t)nt * pl.sz_Tf},
     };
     for (auto& c : copies) {
         if (!c.dst || c.bytes == 0) continue;
@@ -246,7 +264,7 @@ gdr_status_t gdr_chunk_fwd_timed(const gdr_problem_t* p, const void* q, const vo
         ev[i] = static_cast<hipEvent_t>(stage_events[i]);
     }
     return run(p, q, k, v, g, beta, scale, initial_state, cu_dev, cu_host, o, final_state, workspace,
-               workspace_bytes, stream, ev, nullptr, nullptr);
+               workspace_bytes, stream, ev, false, nullptr, nullptr);
 }
 
 const char* gdr_status_string(gdr_status_t s) {

@@ -13,10 +13,17 @@
 // Intermediates live in the caller's workspace in fragment-major layouts
 // (gdr_device.hpp) chosen so that every matrix-core operand is read with
 // lane-contiguous vector loads and MFMA results feed later products in place.
+#include <type_traits>
+
 #include "gdr_device.hpp"
 #include "gdr_launch.hpp"
 
 namespace gdr {
+
+// Lower-triangular pair fragments of T (16-row block tb, 32-position block tp).
+constexpr int kTPairs = 6;
+__constant__ int kTPairTb[kTPairs] = {0, 1, 2, 2, 3, 3};
+__constant__ int kTPairTp[kTPairs] = {0, 0, 0, 1, 0, 1};
 
 // ============================================================ chunk table
 // Builds, from the sequence offsets, the list of chunks (sequence id, first
@@ -49,7 +56,7 @@ __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict_
             e = e < s ? s : (e > Ttot ? Ttot : e);
         }
         const int32_t nch = (int32_t)((e - s + kChunk - 1) / kChunk);
-        scan[tid] = nch;
+        scan[tid] = nch;   // chunks of sequence n
         __syncthreads();
         for (int off = 1; off < 1024; off <<= 1) {         // inclusive Hillis-Steele scan
             int32_t add = tid >= off ? scan[tid - off] : 0;
@@ -58,22 +65,32 @@ __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict_
             __syncthreads();
         }
         const int32_t first = base + scan[tid] - nch;
-        if (n < N) {
-            seq_first[n] = first < cap ? first : cap;
-            for (int32_t j = 0; j < nch; ++j) {
-                const int32_t c = first + j;
-                if (c >= cap) break;
-                const int64_t cs = s + (int64_t)j * kChunk;
-                const int64_t ce = cs + kChunk < e ? cs + kChunk : e;
-                chunk_seq[c] = n;
-                chunk_start[c] = (int32_t)cs;
-                chunk_len[c] = (int32_t)(ce - cs);
-            }
-        }
+        if (n < N) seq_first[n] = first < cap ? first : cap;
         base += scan[1023];
         __syncthreads();
     }
     if (tid == 0) seq_first[N] = base < cap ? base : cap;
+    __syncthreads();
+    // Entries: chunk c belongs to the last sequence whose first chunk is <= c.
+    const int32_t total = base < cap ? base : cap;
+    for (int32_t c = tid; c < total; c += 1024) {
+        int32_t lo = 0, hi = N - 1;                       // seq_first is non-decreasing
+        while (lo < hi) {
+            const int32_t mid = (lo + hi + 1) >> 1;
+            if (seq_first[mid] <= c) lo = mid; else hi = mid - 1;
+        }
+        const int32_t n = lo;
+        int64_t s = cu ? (int64_t)cu[n] : (int64_t)n * T_row;
+        int64_t e = cu ? (int64_t)cu[n + 1] : (int64_t)(n + 1) * T_row;
+        s = s < 0 ? 0 : (s > Ttot ? Ttot : s);
+        e = e < s ? s : (e > Ttot ? Ttot : e);
+        const int64_t cs = s + (int64_t)(c - seq_first[n]) * kChunk;
+        const int64_t ce = cs + kChunk < e ? cs + kChunk : e;
+        const bool empty = !(ce > cs);
+        chunk_seq[c] = n;
+        chunk_start[c] = empty ? 0 : (int32_t)cs;          // empty entries point at token 0
+        chunk_len[c] = empty ? 0 : (int32_t)(ce - cs);
+    }
 }
 
 // ============================================================ K1: gate prefix sums
@@ -91,11 +108,14 @@ __global__ __launch_bounds__(256) void k_gate_cumsum(const float* __restrict__ g
     const int32_t c = (int32_t)(p / Nv), h = (int32_t)(p % Nv);
     const int64_t s = chunk_start[c];
     const int32_t L = chunk_len[c];
+    float x[kChunk];
+#pragma unroll
+    for (int32_t i = 0; i < kChunk; ++i) x[i] = (g && i < L) ? g[(s + i) * Nv + h] : 0.f;   // independent loads
     float acc = 0.f;
-    for (int32_t i = 0; i < L; ++i) {
-        const int64_t idx = (s + i) * Nv + h;
-        if (g) acc += g[idx];
-        G[idx] = acc;
+#pragma unroll
+    for (int32_t i = 0; i < kChunk; ++i) {
+        acc += x[i];
+        if (i < L) G[(s + i) * Nv + h] = acc;
     }
 }
 
@@ -115,13 +135,18 @@ __global__ __launch_bounds__(256) void k_gate_cumsum(const float* __restrict__ g
 //        32-block, then the lower-left 32x32 block = -A_bot L_bl A_top.
 //      Both operands are derived values, so each product takes the split
 //      (three-pass) form.
-//   5. A rows (fp32) -> global, zero above the diagonal and past the chunk end.
+//   5. A rows (fp32) -> global, zero above the diagonal and past the chunk end
+//      (when A_out is given), and/or T = A diag(beta) (FLA DeltaNet article,
+//      section 2.3: T absorbs diag(beta)) as split (hi, lo) pair fragments of
+//      its lower-triangular 16 x 32 blocks for the fused state pass (when Tf
+//      is given).
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void k_build_solve(const T* __restrict__ k, const void* __restrict__ beta,
                                                       int beta_f32, const float* __restrict__ G,
                                                       const int32_t* __restrict__ chunk_start,
                                                       const int32_t* __restrict__ chunk_len,
-                                                      int32_t Nk, int32_t Nv, float* __restrict__ A_out) {
+                                                      int32_t Nk, int32_t Nv, float* __restrict__ A_out,
+                                                      T* __restrict__ Tf) {
     constexpr int KP = DK + 8;                 // padded LDS row (elements)
     __shared__ __attribute__((aligned(16))) T Ks[kChunk * KP];
     __shared__ float Lf[kChunk][kChunk + 1];
@@ -249,7 +274,7 @@ __global__ __launch_bounds__(256) void k_build_solve(const T* __restrict__ k, co
         __syncthreads();
 
         // 5. rows of A for the valid tokens (fp32)
-        for (int idx = tid; idx < kChunk * 16; idx += 256) {
+        for (int idx = tid; A_out && idx < kChunk * 16; idx += 256) {
             const int row = idx >> 4, seg = idx & 15;
             if (row < L) {
                 f32x4 val;
@@ -259,6 +284,24 @@ __global__ __launch_bounds__(256) void k_build_solve(const T* __restrict__ k, co
                     val[e] = (col <= row) ? Af[row][col] : 0.f;
                 }
                 *reinterpret_cast<f32x4*>(A_out + ((s + row) * Nv + h) * kChunk + seg * 4) = val;
+            }
+        }
+        // T = A diag(beta) pair fragments: pair p covers rows 16*tb + r and positions 32*tp + m(qd, e)
+        // for (tb, tp) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1); rows past the chunk end are zero.
+        if (Tf) {
+            for (int p = wave; p < kTPairs; p += 4) {
+                const int tb = kTPairTb[p], tp = kTPairTp[p];
+                const int row = tb * 16 + r;
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int m = tp * 32 + (e < 4 ? 4 * qd + e : 16 + 4 * qd + e - 4);
+                    x[e] = (row < L && m <= row) ? Af[row][m] * bs[m] : 0.f;
+                }
+                const Split<T> sp = split8<T>(x);
+                T* dst = Tf + (((int64_t)c * Nv + h) * kTPairs + p) * 2 * 512;
+                store_frag<T>(dst, lane, sp.hi);
+                if constexpr (kSplitNeeded<T>) store_frag<T>(dst + 512, lane, sp.lo);
             }
         }
         __syncthreads();
@@ -570,17 +613,343 @@ __global__ __launch_bounds__(256) void k_output(const T* __restrict__ q, const T
         }
 }
 
+// ============================================================ K4 + K5 fused: state pass with output
+// Production path for bf16 inputs. One workgroup (4 wavefronts) per (sequence,
+// value head, 16 columns of dv) walks the sequence's chunks in order with the
+// state slice S (dk x 16, fp32) on chip, and produces the output of each chunk
+// as it goes, so neither the per-chunk states nor V_new ever reach HBM.
+// Per chunk (ChunkGatedDeltaRule page, formulas (3)-(6); FLA DeltaNet article,
+// sections 2.3-2.4), with T = A diag(beta) from the A-build kernel:
+//   Y     = K S_in                          (wave w: positions 16w..16w+15)
+//   Z     = V - diag(exp(G)) Y              so that V_new = U - W S_in = T Z
+//   V_new = T Z                             (T lower triangular: blocks <= w)
+//   S_out = exp(G_last) S_in + K^T diag(exp(G_last - G)) V_new   (wave w: dk tiles of w)
+//   O     = scale [diag(exp(G)) Q S_in + (Q K^T (.) D) V_new]      (wave w: rows of w)
+// Z, V_new and the new state are exchanged between the wavefronts through LDS
+// as split (hi, lo) bf16 pair fragments (three barriers per chunk). The K and Q
+// tiles of the chunk are staged in LDS (double-buffered) and the next chunk's
+// tiles, T fragments, V slice and gates are fetched while the current chunk is
+// computed. K^T operands are read from the K tile with transposing LDS reads.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void k_state_output(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                       const bf16* __restrict__ v, const float* __restrict__ G,
+                                                       const bf16* __restrict__ Tf, const float* __restrict__ S0,
+                                                       const int32_t* __restrict__ chunk_start,
+                                                       const int32_t* __restrict__ chunk_len,
+                                                       const int32_t* __restrict__ seq_first, int32_t Nk, int32_t Nv,
+                                                       float scale, int out_f32, void* __restrict__ o,
+                                                       float* __restrict__ ST) {
+    typedef bf16 T;
+    typedef Vec<T>::v8 v8;
+    constexpr int NKP = DK / 32, NDB = DK / 16;
+    constexpr int TPW = (NDB + 3) / 4;          // state tiles owned per wave
+    constexpr int KP = DK + 8;                  // padded LDS row (elements)
+    constexpr int NSEG = DK / 8;                // 16-byte segments per row
+    constexpr int LPT = kChunk * NSEG / 256;    // row segments loaded per thread
+    __shared__ __attribute__((aligned(16))) T Ks[2][kChunk * KP];
+    __shared__ __attribute__((aligned(16))) T Qs[2][kChunk * KP];
+    __shared__ __attribute__((aligned(16))) T Sb[NKP][2][512];
+    __shared__ __attribute__((aligned(16))) T Zb[2][2][512];
+    __shared__ __attribute__((aligned(16))) T Vb[2][2][512];
+    __shared__ __attribute__((aligned(16))) T Vtb[2][2][512];
+    __shared__ __attribute__((aligned(16))) T Tb[2][kTPairs * 2 * 512];   // T fragments of the chunk
+    __shared__ __attribute__((aligned(16))) T Vs[2][kChunk * 16];         // V slice: 64 rows x 16 columns
+    __shared__ float Gs[2][kChunk];
+
+    const int n = blockIdx.x, h = blockIdx.y, nb = blockIdx.z;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, qd = lane >> 4;
+    const int kh = h / (Nv / Nk);
+    const int c0 = seq_first[n], c1 = seq_first[n + 1];
+    const int64_t sbase = ((int64_t)n * Nv + h) * DK * DV;
+    const int ntp = (w >> 1) + 1;               // T pairs of wave w: positions 0..32*ntp-1
+    const int pbase = (w == 0) ? 0 : (w == 1 ? 1 : (w == 2 ? 2 : 4));
+
+    // state tiles owned by this wave
+    f32x4 S[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        const int db = w * TPW + t;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            S[t][j] = (db < NDB && S0) ? S0[sbase + (int64_t)(db * 16 + 4 * qd + j) * DV + nb * 16 + r] : 0.f;
+    }
+    auto publish_state = [&]() {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int db = w * TPW + t;
+            if (db < NDB) {
+                float x[8] = {S[t][0], S[t][1], S[t][2], S[t][3], 0.f, 0.f, 0.f, 0.f};
+                const Split<T> sp = split8<T>(x);
+                typename Vec<T>::v4 hi4 = {sp.hi[0], sp.hi[1], sp.hi[2], sp.hi[3]};
+                typename Vec<T>::v4 lo4 = {sp.lo[0], sp.lo[1], sp.lo[2], sp.lo[3]};
+                *reinterpret_cast<typename Vec<T>::v4*>(&Sb[db >> 1][0][lane * 8 + 4 * (db & 1)]) = hi4;
+                *reinterpret_cast<typename Vec<T>::v4*>(&Sb[db >> 1][1][lane * 8 + 4 * (db & 1)]) = lo4;
+            }
+        }
+    };
+    auto store_split_half = [&](T (*buf)[2][512], int tp, int half, const f32x4& x) {
+        float xx[8] = {x[0], x[1], x[2], x[3], 0.f, 0.f, 0.f, 0.f};
+        const Split<T> sp = split8<T>(xx);
+        typename Vec<T>::v4 hi4 = {sp.hi[0], sp.hi[1], sp.hi[2], sp.hi[3]};
+        typename Vec<T>::v4 lo4 = {sp.lo[0], sp.lo[1], sp.lo[2], sp.lo[3]};
+        *reinterpret_cast<typename Vec<T>::v4*>(&buf[tp][0][lane * 8 + 4 * half]) = hi4;
+        *reinterpret_cast<typename Vec<T>::v4*>(&buf[tp][1][lane * 8 + 4 * half]) = lo4;
+    };
+    auto load_split = [&](T (*buf)[2][512], int tp) {
+        Split<T> sp;
+        sp.hi = *reinterpret_cast<const v8*>(&buf[tp][0][lane * 8]);
+        sp.lo = *reinterpret_cast<const v8*>(&buf[tp][1][lane * 8]);
+        return sp;
+    };
+
+    // Operands of the next chunk, fetched into registers while the current
+    // chunk is computed and written to the other LDS buffer at the end of the
+    // step; computation reads only LDS. Every load reads a valid address (rows
+    // past the chunk end are clamped to its last row) with no branch around
+    // it, and rows past the end are zeroed when staged.
+    constexpr int TLD = kTPairs * 2 * 512 * 2 / 16 / 256;   // 16-byte T loads per thread (3)
+    struct Ahead {
+        v8 kr[LPT], qr[LPT], tr[TLD];
+        typename Vec<T>::v4 vr;
+        float g;
+        int L;
+        int64_t s;
+    };
+    auto fetch = [&](int c, Ahead& A) {
+        A.s = chunk_start[c];
+        A.L = chunk_len[c];
+        const int last = A.L > 0 ? A.L - 1 : 0;
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            const int idx = tid + 256 * i, row = min(idx / NSEG, last), seg = idx % NSEG;
+            A.kr[i] = *reinterpret_cast<const v8*>(k + ((A.s + row) * Nk + kh) * DK + seg * 8);
+            A.qr[i] = *reinterpret_cast<const v8*>(q + ((A.s + row) * Nk + kh) * DK + seg * 8);
+        }
+        const T* tsrc = Tf + ((int64_t)c * Nv + h) * kTPairs * 2 * 512;
+#pragma unroll
+        for (int i = 0; i < TLD; ++i) A.tr[i] = *reinterpret_cast<const v8*>(tsrc + (tid + 256 * i) * 8);
+        const int vrow = min(tid >> 2, last);
+        A.vr = *reinterpret_cast<const typename Vec<T>::v4*>(v + ((A.s + vrow) * Nv + h) * DV + nb * 16 + (tid & 3) * 4);
+        A.g = G[(A.s + min(tid & 63, last)) * Nv + h];   // rows past the end repeat G_last
+    };
+    auto stage = [&](const Ahead& A, int buf) {
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            const int idx = tid + 256 * i, row = idx / NSEG, seg = idx % NSEG;
+            const bool ok = row < A.L;
+            *reinterpret_cast<v8*>(&Ks[buf][row * KP + seg * 8]) = ok ? A.kr[i] : zero_pair<T>();
+            *reinterpret_cast<v8*>(&Qs[buf][row * KP + seg * 8]) = ok ? A.qr[i] : zero_pair<T>();
+        }
+#pragma unroll
+        for (int i = 0; i < TLD; ++i) *reinterpret_cast<v8*>(&Tb[buf][(tid + 256 * i) * 8]) = A.tr[i];
+        typename Vec<T>::v4 zero4 = {to_t<T>(0.f), to_t<T>(0.f), to_t<T>(0.f), to_t<T>(0.f)};
+        *reinterpret_cast<typename Vec<T>::v4*>(&Vs[buf][tid * 4]) = (tid >> 2) < A.L ? A.vr : zero4;
+        Gs[buf][tid & 63] = A.L > 0 ? A.g : 0.f;          // the four waves write the same values
+    };
+
+    if (c0 < c1) {
+        Ahead nxt;
+        fetch(c0, nxt);
+        stage(nxt, 0);
+        int cur_L = nxt.L;
+        int64_t cur_s = nxt.s;
+        publish_state();
+        __syncthreads();
+        for (int c = c0; c < c1; ++c) {
+            const int buf = (c - c0) & 1;
+            const bool more = c + 1 < c1;
+            if (more) fetch(c + 1, nxt);
+            const int L = cur_L;
+            const int64_t s = cur_s;
+            const T* Kb = Ks[buf];
+            const T* Qb = Qs[buf];
+
+            // ---- all LDS operands of the first phase, read in one batch
+            Split<T> BS[NKP];
+            v8 ka[NKP], qa[NKP], kj[4][NKP];
+#pragma unroll
+            for (int kp = 0; kp < NKP; ++kp) {
+                BS[kp] = load_split(Sb, kp);
+                ka[kp] = load_pair_row<T>(&Kb[(w * 16 + r) * KP + kp * 32], qd);
+                qa[kp] = load_pair_row<T>(&Qb[(w * 16 + r) * KP + kp * 32], qd);
+            }
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj)
+                if (tj < w)                       // tile tj == w reuses ka
+#pragma unroll
+                    for (int kp = 0; kp < NKP; ++kp) kj[tj][kp] = load_pair_row<T>(&Kb[(tj * 16 + r) * KP + kp * 32], qd);
+            float grow[4], gcol[4][4], vj[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                grow[j] = Gs[buf][w * 16 + 4 * qd + j];
+                vj[j] = to_f(Vs[buf][(w * 16 + 4 * qd + j) * 16 + r]);
+            }
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) gcol[tj][jj] = Gs[buf][tj * 16 + 4 * qd + jj];
+            const float g_last = L > 0 ? Gs[buf][L - 1] : 0.f;
+            const float g_i = Gs[buf][w * 16 + r];
+
+            // ---- Y = K S_in, Q S_in (hi and lo passes in separate chains), scores K Q^T
+            f32x4 Yh = {0.f, 0.f, 0.f, 0.f}, Yl = Yh, Qh = Yh, Ql = Yh;
+#pragma unroll
+            for (int kp = 0; kp < NKP; ++kp) {
+                Yh = mfma_pair(ka[kp], BS[kp].hi, Yh);
+                Qh = mfma_pair(qa[kp], BS[kp].hi, Qh);
+                Yl = mfma_pair(ka[kp], BS[kp].lo, Yl);
+                Ql = mfma_pair(qa[kp], BS[kp].lo, Ql);
+            }
+            f32x4 pt[4];
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj) {
+                pt[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (tj <= w)
+#pragma unroll
+                    for (int kp = 0; kp < NKP; ++kp) pt[tj] = mfma_pair(tj == w ? ka[kp] : kj[tj][kp], qa[kp], pt[tj]);
+            }
+
+            // ---- Z = V - exp(G) Y -> LDS
+            float eg[4];
+            f32x4 Z;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                eg[j] = __expf(grow[j]);
+                Z[j] = vj[j] - eg[j] * (Yh[j] + Yl[j]);
+            }
+            store_split_half(Zb, w >> 1, w & 1, Z);
+            // transposed K^T operands of the state update (independent of the exchange)
+            v8 kt[TPW][2];
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const int db = min(w * TPW + t, NDB - 1);
+#pragma unroll
+                for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int m = tp * 32 + (e < 4 ? 4 * qd + e : 16 + 4 * qd + e - 4);
+                        kt[t][tp][e] = Kb[m * KP + db * 16 + r];
+                    }
+            }
+            // scores: decay and mask (rows j, column i = 16w + r)
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int j = tj * 16 + 4 * qd + jj;
+                    pt[tj][jj] = (tj <= w && j <= w * 16 + r) ? pt[tj][jj] * __expf(g_i - gcol[tj][jj]) : 0.f;
+                }
+            __syncthreads();
+
+            // ---- V_new = T Z (only position blocks <= w contribute)
+            Split<T> tf[2], zf[2];
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp) {
+                if (tp < ntp) {
+                    tf[tp].hi = load_frag<T>(&Tb[buf][(pbase + tp) * 2 * 512], lane);
+                    tf[tp].lo = load_frag<T>(&Tb[buf][(pbase + tp) * 2 * 512 + 512], lane);
+                    zf[tp] = load_split(Zb, tp);
+                }
+            }
+            f32x4 Va = {0.f, 0.f, 0.f, 0.f}, Vb2 = Va;
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp) {
+                if (tp < ntp) {
+                    Va = mfma_pair(tf[tp].hi, zf[tp].hi, Va);
+                    Vb2 = mfma_pair(tf[tp].lo, zf[tp].hi, Vb2);
+                    Vb2 = mfma_pair(tf[tp].hi, zf[tp].lo, Vb2);
+                }
+            }
+            f32x4 VN, VD;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                VN[j] = Va[j] + Vb2[j];
+                VD[j] = VN[j] * __expf(g_last - grow[j]);
+            }
+            store_split_half(Vb, w >> 1, w & 1, VN);
+            store_split_half(Vtb, w >> 1, w & 1, VD);
+            __syncthreads();
+
+            // ---- S_out = exp(G_last) S_in + K^T V_decayed for the dk tiles of this wave
+            const Split<T> vt[2] = {load_split(Vtb, 0), load_split(Vtb, 1)};
+            Split<T> vn[2];
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp)
+                if (tp < ntp) vn[tp] = load_split(Vb, tp);
+            const float a_last = __expf(g_last);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const int db = w * TPW + t;
+                if (db < NDB) {
+                    f32x4 acc = S[t] * a_last, lo = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int tp = 0; tp < 2; ++tp) {
+                        acc = mfma_pair(kt[t][tp], vt[tp].hi, acc);
+                        lo = mfma_pair(kt[t][tp], vt[tp].lo, lo);
+                    }
+                    S[t] = acc + lo;
+                }
+            }
+
+            // ---- hand over the new state and the next chunk's tiles
+            publish_state();
+            if (more) {
+                stage(nxt, buf ^ 1);
+                cur_L = nxt.L;
+                cur_s = nxt.s;
+            }
+
+            // ---- O = scale [exp(G) Q S_in + (Q K^T (.) D) V_new] for rows 16w..16w+15
+            f32x4 out, ol = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) out[j] = eg[j] * (Qh[j] + Ql[j]);
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp) {
+                if (tp < ntp) {
+                    const Split<T> pa = split_acc_pair<T>(pt[2 * tp], pt[2 * tp + 1]);
+                    out = mfma_pair(pa.hi, vn[tp].hi, out);
+                    ol = mfma_pair(pa.lo, vn[tp].hi, ol);
+                    ol = mfma_pair(pa.hi, vn[tp].lo, ol);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = w * 16 + 4 * qd + j;
+                if (row < L) {
+                    const int64_t idx = ((s + row) * Nv + h) * DV + nb * 16 + r;
+                    const float val = scale * (out[j] + ol[j]);
+                    if (out_f32) reinterpret_cast<float*>(o)[idx] = val;
+                    else reinterpret_cast<T*>(o)[idx] = to_t<T>(val);
+                }
+            }
+            __syncthreads();
+        }
+    }
+    if (ST) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int db = w * TPW + t;
+            if (db < NDB) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ST[sbase + (int64_t)(db * 16 + 4 * qd + j) * DV + nb * 16 + r] = S[t][j];
+            }
+        }
+    }
+}
+
 // ============================================================ launchers
 template <typename T, int DK, int DV>
 static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
     hipStream_t st = a.stream;
     auto mark = [&](int i) { if (ev) (void)hipEventRecord(ev[i], st); };
     const int32_t cap = a.nt_cap;
+    const int32_t NT = a.nt;
+    constexpr bool kFused = std::is_same<T, bf16>::value;
+    const bool fused = kFused && !a.reference;
     mark(0);
     k_chunk_table<<<1, 1024, 0, st>>>(a.cu_dev, a.T_row, a.N, a.Ttot, cap, a.chunk_seq, a.chunk_start,
                                       a.chunk_len, a.seq_first);
     mark(1);
-    const int32_t NT = a.nt;
     if (NT > 0) {
         const int64_t units = (int64_t)NT * a.Nv;
         k_gate_cumsum<<<(unsigned)((units + 255) / 256), 256, 0, st>>>(a.g, a.chunk_start, a.chunk_len, NT, a.Nv, a.G);
@@ -588,19 +957,30 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
     mark(2);
     if (NT > 0)
         k_build_solve<T, DK><<<dim3(NT, a.Nk), 256, 0, st>>>((const T*)a.k, a.beta, a.beta_f32, a.G, a.chunk_start,
-                                                            a.chunk_len, a.Nk, a.Nv, (float*)a.A);
+                                                            a.chunk_len, a.Nk, a.Nv, fused ? nullptr : (float*)a.A,
+                                                            (T*)a.Tf);
     mark(3);
-    if (NT > 0)
+    if (NT > 0 && !fused)
         k_wu<T, DK, DV><<<dim3(NT, a.Nk), 256, 0, st>>>((const T*)a.k, (const T*)a.v, a.beta, a.beta_f32, a.G,
                                                        (const float*)a.A, a.chunk_start, a.chunk_len, a.Nk, a.Nv,
                                                        (float*)a.W, (float*)a.U, (T*)a.KT);
     mark(4);
-    if (a.N > 0)
-        k_state<T, DK, DV><<<dim3(a.N, a.Nv, DV / 16), 64, 0, st>>>((const float*)a.W, (const float*)a.U, (const T*)a.KT, a.G,
-                                                                   a.S0, a.chunk_start, a.chunk_len, a.seq_first,
-                                                                   a.Nk, a.Nv, (float*)a.H, (float*)a.VN, a.ST);
+    if (a.N > 0) {
+        if constexpr (kFused) {
+            if (fused) {
+                k_state_output<DK, DV><<<dim3(a.N, a.Nv, DV / 16), 256, 0, st>>>(
+                    (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.G, (const bf16*)a.Tf, a.S0,
+                    a.chunk_start, a.chunk_len, a.seq_first, a.Nk, a.Nv, a.scale, a.out_f32, a.o, a.ST);
+            }
+        }
+        if (!fused)
+            k_state<T, DK, DV><<<dim3(a.N, a.Nv, DV / 16), 64, 0, st>>>((const float*)a.W, (const float*)a.U,
+                                                                       (const T*)a.KT, a.G, a.S0, a.chunk_start,
+                                                                       a.chunk_len, a.seq_first, a.Nk, a.Nv,
+                                                                       (float*)a.H, (float*)a.VN, a.ST);
+    }
     mark(5);
-    if (NT > 0)
+    if (NT > 0 && !fused)
         k_output<T, DK, DV><<<dim3(NT, a.Nv), 256, 0, st>>>((const T*)a.q, (const T*)a.k, a.G, (const float*)a.H,
                                                            (const float*)a.VN, a.chunk_start, a.chunk_len, a.Nk, a.Nv,
                                                            a.scale, a.out_f32, a.o);

@@ -24,11 +24,15 @@ struct LaunchArgs {
     // workspace regions
     int32_t *chunk_seq, *chunk_start, *chunk_len, *seq_first;
     float* G;
-    void *A, *W, *U, *KT, *H, *VN;
+    void *A, *W, *U, *KT, *H, *VN;   // reference-pipeline intermediates
+    void* Tf;                        // T = A diag(beta) fragments (fused pipeline)
+    bool reference;                  // run the five separate kernels even for bf16
     hipStream_t stream;
 };
 
-// Enqueues the whole forward on a.stream. events: NULL, or 7 events recorded
+// Enqueues the whole forward on a.stream. bf16 inputs take the fused path
+// (state pass and output in one kernel) unless a.reference is set; fp32
+// inputs always take the five-kernel path. events: NULL, or 7 events recorded
 // before the first and after every one of the six stages.
 hipError_t launch_forward(const LaunchArgs& a, hipEvent_t* events);
 

@@ -10,9 +10,12 @@
  *
  * starting from S_0 = initial_state[n, h] (zeros when absent); the state after
  * the last token is returned as final_state[n, h]. The library computes this
- * with the chunkwise WY/UT algorithm (chunk size C = 64) as five HIP kernels:
+ * with the chunkwise WY/UT algorithm (chunk size C = 64) in five HIP kernels:
  * gate prefix sums, A-build + triangular solve, w/u products, the sequential
- * state pass, and the output.
+ * state pass, and the output. For bf16 inputs gdr_chunk_fwd fuses the w/u
+ * products and the output into the state pass (the products W S and U are
+ * formed there as T (V - diag(exp(G)) K S) with T = A diag(beta)); fp32 inputs
+ * and gdr_chunk_fwd_debug run the five kernels as separate launches.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -97,11 +100,18 @@ typedef struct {
 gdr_status_t gdr_validate(const gdr_problem_t* problem, const int32_t* cu_seqlens_host);
 
 /*
- * Workspace bytes needed by gdr_chunk_fwd / gdr_chunk_fwd_debug for this
- * problem (an upper bound that holds for every cu_seqlens with the same
- * num_seqs and total length). The workspace must be 256-byte aligned.
+ * Workspace bytes needed by gdr_chunk_fwd (and gdr_chunk_fwd_timed) for this
+ * problem: an upper bound that holds for every cu_seqlens with the same
+ * num_seqs and total length. The workspace must be 256-byte aligned.
  */
 gdr_status_t gdr_chunk_fwd_workspace_size(const gdr_problem_t* problem, size_t* bytes);
+
+/*
+ * Workspace bytes needed by gdr_chunk_fwd_debug, which runs the five kernels
+ * as separate launches and keeps every intermediate (much larger than the
+ * production workspace).
+ */
+gdr_status_t gdr_chunk_fwd_debug_workspace_size(const gdr_problem_t* problem, size_t* bytes);
 
 /*
  * Chunked gated delta-rule forward.
@@ -155,6 +165,9 @@ gdr_status_t gdr_chunk_fwd(const gdr_problem_t* problem,
  *   H    [NT][Nv][dv/16 nb][dk/32 kp] fp32 pair fragments of the chunk's
  *                                     entering state transposed (rows dv, m = dk)
  *   VN   [NT][Nv][dv/16 nb][2 tp] fp32 pair fragments of V_new^T (rows dv, m = position)
+ *   T    [NT][Nv][6 pairs][2 hi/lo] bf16 pair fragments of T = A diag(beta)
+ *        (rows i, m = position) for the blocks (tb, tp) = (0,0) (1,0) (2,0)
+ *        (2,1) (3,0) (3,1); T = hi + lo. bf16 inputs only (NULL otherwise).
  * Chunk positions past the end of a sequence hold zeros in W, U, KT and VN.
  */
 typedef struct {
@@ -165,11 +178,14 @@ typedef struct {
     void* KT;
     void* H;
     void* VN;
+    void* T;
     int64_t num_chunks;     /* out: NT */
 } gdr_intermediates_t;
 
-/* Same computation as gdr_chunk_fwd, then copies the intermediates
- * (asynchronously, on the same stream) into the buffers of `dbg`. */
+/* Same result as gdr_chunk_fwd, computed by the five kernels as separate
+ * launches; then copies the intermediates (asynchronously, on the same
+ * stream) into the buffers of `dbg`. The workspace must hold
+ * gdr_chunk_fwd_debug_workspace_size bytes. */
 gdr_status_t gdr_chunk_fwd_debug(const gdr_problem_t* problem,
                                  const void* q, const void* k, const void* v,
                                  const float* g, const void* beta, float scale,
@@ -187,9 +203,10 @@ gdr_status_t gdr_chunk_fwd_debug(const gdr_problem_t* problem,
  * stage_events[0 .. GDR_NUM_STAGES] (hipEvent_t handles) on `stream`: [0]
  * before the first kernel and [i] after stage i, the stages being [1] chunk
  * table, [2] gate prefix sums, [3] A-build + solve, [4] w/u, [5] state pass,
- * [6] output. Nothing is synchronised; the caller reads the elapsed times
- * once the stream has passed the last event. Used to time each kernel inside
- * a benchmark's timed region.
+ * [6] output. On the fused bf16 path stages [4] and [6] launch nothing (their
+ * work runs inside [5]). Nothing is synchronised; the caller reads the elapsed
+ * times once the stream has passed the last event. Used to time each kernel
+ * inside a benchmark's timed region.
  */
 gdr_status_t gdr_chunk_fwd_timed(const gdr_problem_t* problem,
                                  const void* q, const void* k, const void* v,

@@ -188,6 +188,27 @@ def test_intermediates_match_chunked_oracle(name, w, seed):
     errs["V_new"] = rel_err(fl.chunk_rows_to_tokens(VN, chunks, Ttot), ref["V_new"])
     errs["S_T"] = rel_err(cpu(res["S_T"]), ref["S_T"])
     errs["o"] = rel_err(cpu(res["o"]).reshape(ref["o"].shape), ref["o"])
+    if res["T"] is not None:
+        # T = A diag(beta) fragments (input of the fused state pass), natural per chunk
+        Tn = fl.T_natural(res["T"].detach().cpu().float().numpy())
+        T_ref = np.zeros_like(Tn)
+        for c, (_, s0, Lc) in enumerate(chunks):
+            A_c = ref["A"][s0:s0 + Lc, :, :Lc].transpose(1, 0, 2)          # [Nv, i, m]
+            T_ref[c, :, :Lc, :Lc] = A_c * x["beta"][s0:s0 + Lc].T[:, None, :]
+        errs["T"] = rel_err(Tn, T_ref)
     print(name, {k: "%.2e" % v for k, v in errs.items()}, flush=True)
     for key, e in errs.items():
         assert e <= tol, (name, key, e)
+
+
+@pytest.mark.parametrize("name,w,seed", KERNEL_CASES[:2], ids=[c[0] for c in KERNEL_CASES[:2]])
+def test_fused_path_matches_reference_path(name, w, seed):
+    """The production call (state pass and output fused) and the debug call
+    (five separate kernels) compute the same result to fp32-level accuracy."""
+    inp = synth.generate(w, seed=seed)
+    o1, S1 = run_gpu(inp, out_f32=True)
+    res = run_gpu(inp, debug=True, out_f32=True)
+    eo = rel_err(o1.cpu().double().numpy(), res["o"].cpu().double().numpy())
+    es = rel_err(S1.cpu().double().numpy(), res["S_T"].cpu().double().numpy())
+    print(name, "fused vs reference: o %.2e S_T %.2e" % (eo, es), flush=True)
+    assert eo < 1e-3 and es < 1e-3
