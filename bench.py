@@ -34,9 +34,12 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ("chunkwise_gated_delta_local_amd/csrc/gdr_kernels.hip",
                   "chunkwise_gated_delta_local_amd/csrc/gdr_device.hpp")
 STAGE_KERNELS = ("k_chunk_table", "k_gate_cumsum", "k_build_solve", "k_wu", "k_state", "k_output")
+FUSED_STAGE_KERNELS = ("k_chunk_table", "k_gate_cumsum", "k_build_solve", "(fused)", "k_state_output", "(fused)")
+T_FRAG_BYTES = 6 * 2 * 512 * 2          # T = A diag(beta) split fragments per (chunk, value head)
 
 
-def stage_algorithmic_bytes(w: synth.Workload, Ttot: int, N: int, NT: int, out_bytes: int) -> dict:
+def stage_algorithmic_bytes(w: synth.Workload, Ttot: int, N: int, NT: int, out_bytes: int,
+                            s0: bool) -> dict:
     """Bytes each kernel must move by its own inputs and outputs: every tensor it
     reads read once, every tensor it writes written once, in its stored type."""
     es = 2 if w.dtype == "bf16" else 4
@@ -44,6 +47,16 @@ def stage_algorithmic_bytes(w: synth.Workload, Ttot: int, N: int, NT: int, out_b
     tv = Ttot * Nv                      # token-heads (value heads)
     tk = Ttot * Nk                      # token-heads (q/k heads)
     beta_b = es
+    state = N * Nv * dk * dv * 4
+    if w.dtype == "bf16":               # fused path
+        return {
+            "k_chunk_table": 4 * (N + 1) + 16 * NT,
+            "k_gate_cumsum": tv * (4 + 4),
+            "k_build_solve": tk * dk * es + tv * (beta_b + 4) + NT * Nv * T_FRAG_BYTES,   # k, beta, G in; T out
+            "k_state_output": 2 * tk * dk * es + tv * dv * es + tv * 4 + NT * Nv * T_FRAG_BYTES  # q, k, v, G, T in
+                              + tv * dv * out_bytes + state * (2 if s0 else 1),                  # o, S_T out (S0 in)
+            "(fused)": 0,
+        }
     return {
         "k_chunk_table": 4 * (N + 1) + 16 * NT,
         "k_gate_cumsum": tv * (4 + 4),                                        # g in, G out
@@ -171,9 +184,10 @@ def main():
                          for s in range(K)]).mean(axis=0)
 
     out_bytes = 4 if (args.out_dtype == "f32" or w.dtype == "f32") else 2
-    alg = stage_algorithmic_bytes(w, Ttot, N, NT, out_bytes)
+    alg = stage_algorithmic_bytes(w, Ttot, N, NT, out_bytes, inp["S0"] is not None)
+    names = FUSED_STAGE_KERNELS if w.dtype == "bf16" else STAGE_KERNELS
     dom = int(np.argmax(stage_ms))
-    kname = STAGE_KERNELS[dom]
+    kname = names[dom]
     achieved = alg[kname] / (stage_ms[dom] * 1e-3) / 1e9
     traffic = counter_traffic(kname, "T65536_Nk16_Nv32_d128" if args.workload == 5 else "workload%d" % args.workload)
 
@@ -201,7 +215,7 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": alg[kname], "avg_ms": float(stage_ms[dom])},
         "cpu_baseline": cpu,
-        "stage_ms": {STAGE_KERNELS[i]: float(stage_ms[i]) for i in range(api.NUM_STAGES)},
+        "stage_ms": {("%d:%s" % (i, names[i])): float(stage_ms[i]) for i in range(api.NUM_STAGES)},
         "end_to_end_hbm_frac": (24768.0 * Ttot / (ms_per_step * 1e-3) / 1e9) / HBM_PEAK_GBS
         if args.workload == 5 and out_bytes == 2 else None,
     }
