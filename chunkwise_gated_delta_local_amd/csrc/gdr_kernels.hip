@@ -97,12 +97,25 @@ __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict_
 // G[t, h] = sum of g over the tokens of t's chunk up to and including t, in
 // fp32 and in token order (ChunkGatedDeltaRule page, section 3, "G_i";
 // GLA notes, forward step 1, chunk-local cumulative log gate). One thread per
-// (chunk, head); neighbouring threads take neighbouring heads so every step
-// of the scan is a coalesced row read. g == NULL writes zeros (ungated rule).
+// (chunk, head); neighbouring threads take neighbouring heads so every row
+// access is coalesced. g == NULL writes zeros (ungated rule).
+// When R is given, the decay factors the fused state pass needs are written
+// per token too, all of the form exp(non-positive), so none can overflow
+// (with b = t / 16 the 16-row block of position t in its chunk):
+//   R.x = exp(G_t)                      decay from the chunk start
+//   R.y = exp(G_last - G_t)             decay to the chunk end
+//   R.z = exp(G_t - G_{16b-1})          decay from the end of the previous block (G_{-1} = 0)
+//   R.w = exp(G_{16b+15} - G_t)         decay to the end of t's block (clamped to the chunk end)
+// so that exp(G_i - G_j) for j in an earlier block than i is a product of
+// R.z_i, R.z at the ends of the blocks in between, and R.w_j.
+// R and Gc are written chunk-major, [chunk][head][64 positions] (positions past
+// the chunk end: G_last for Gc, zeros for R), so the sequential pass reads the
+// factors of one (chunk, head) as one contiguous block.
 __global__ __launch_bounds__(256) void k_gate_cumsum(const float* __restrict__ g,
                                                       const int32_t* __restrict__ chunk_start,
                                                       const int32_t* __restrict__ chunk_len,
-                                                      int32_t NT, int32_t Nv, float* __restrict__ G) {
+                                                      int32_t NT, int32_t Nv, float* __restrict__ G,
+                                                      f32x4* __restrict__ R, float* __restrict__ Gc) {
     const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (p >= (int64_t)NT * Nv) return;
     const int32_t c = (int32_t)(p / Nv), h = (int32_t)(p % Nv);
@@ -115,7 +128,22 @@ __global__ __launch_bounds__(256) void k_gate_cumsum(const float* __restrict__ g
 #pragma unroll
     for (int32_t i = 0; i < kChunk; ++i) {
         acc += x[i];
+        x[i] = acc;                              // x now holds G (positions past the end repeat G_last)
         if (i < L) G[(s + i) * Nv + h] = acc;
+    }
+    if (R) {
+        const float g_last = L > 0 ? x[L - 1] : 0.f;
+        f32x4* Rc = R + ((int64_t)c * Nv + h) * kChunk;
+        float* Gcc = Gc + ((int64_t)c * Nv + h) * kChunk;
+#pragma unroll
+        for (int32_t i = 0; i < kChunk; ++i) {
+            const int b = i >> 4;
+            const float g_prev = b > 0 ? x[16 * b - 1] : 0.f;
+            const int e = min(16 * b + 15, L > 0 ? L - 1 : 0);
+            Rc[i] = i < L ? f32x4{__expf(x[i]), __expf(g_last - x[i]), __expf(x[i] - g_prev), __expf(x[e] - x[i])}
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
+            Gcc[i] = x[i];
+        }
     }
 }
 
@@ -626,14 +654,19 @@ __global__ __launch_bounds__(256) void k_output(const T* __restrict__ q, const T
 //   S_out = exp(G_last) S_in + K^T diag(exp(G_last - G)) V_new   (wave w: dk tiles of w)
 //   O     = scale [diag(exp(G)) Q S_in + (Q K^T (.) D) V_new]      (wave w: rows of w)
 // Z, V_new and the new state are exchanged between the wavefronts through LDS
-// as split (hi, lo) bf16 pair fragments (three barriers per chunk). The K and Q
-// tiles of the chunk are staged in LDS (double-buffered) and the next chunk's
-// tiles, T fragments, V slice and gates are fetched while the current chunk is
-// computed. K^T operands are read from the K tile with transposing LDS reads.
+// as split (hi, lo) bf16 pair fragments (three barriers per chunk). The next
+// chunk's K and Q tiles, T fragments, V slice and gate factors are fetched
+// with bounds-checked buffer loads (rows past the chunk end read as zero) while
+// the current chunk is computed, and staged into the other half of a
+// double-buffered LDS area at the end of the step; computation reads only LDS.
+// K^T operands come from the K tile through transposing LDS reads. The decay
+// exp(G_i - G_j) of the score block is a product of the precomputed factors R
+// outside the diagonal 16x16 blocks, where it is evaluated directly.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void k_state_output(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                                       const bf16* __restrict__ v, const float* __restrict__ G,
-                                                       const bf16* __restrict__ Tf, const float* __restrict__ S0,
+                                                       const bf16* __restrict__ v, const float* __restrict__ Gc,
+                                                       const f32x4* __restrict__ R, const bf16* __restrict__ Tf,
+                                                       const float* __restrict__ S0,
                                                        const int32_t* __restrict__ chunk_start,
                                                        const int32_t* __restrict__ chunk_len,
                                                        const int32_t* __restrict__ seq_first, int32_t Nk, int32_t Nv,
@@ -641,28 +674,54 @@ __global__ __launch_bounds__(256) void k_state_output(const bf16* __restrict__ q
                                                        float* __restrict__ ST) {
     typedef bf16 T;
     typedef Vec<T>::v8 v8;
+    typedef Vec<T>::v4 v4;
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    typedef int i4 __attribute__((ext_vector_type(4)));
+    typedef int i2 __attribute__((ext_vector_type(2)));
     constexpr int NKP = DK / 32, NDB = DK / 16;
     constexpr int TPW = (NDB + 3) / 4;          // state tiles owned per wave
     constexpr int KP = DK + 8;                  // padded LDS row (elements)
     constexpr int NSEG = DK / 8;                // 16-byte segments per row
     constexpr int LPT = kChunk * NSEG / 256;    // row segments loaded per thread
+    constexpr int TFRAG = kTPairs * 2 * 512;    // T elements per (chunk, head)
+    constexpr int TLD = TFRAG * 2 / 16 / 256;   // 16-byte T loads per thread
+    constexpr int RSRC = 0x00020000;            // buffer descriptor word 3 (raw 32-bit access)
     __shared__ __attribute__((aligned(16))) T Ks[2][kChunk * KP];
     __shared__ __attribute__((aligned(16))) T Qs[2][kChunk * KP];
+    __shared__ __attribute__((aligned(16))) T Tb[2][TFRAG];
+    __shared__ __attribute__((aligned(16))) T Vs[2][kChunk * 16];
+    __shared__ __attribute__((aligned(16))) f32x4 Rs[2][kChunk];
+    __shared__ float Gs[2][kChunk];
     __shared__ __attribute__((aligned(16))) T Sb[NKP][2][512];
     __shared__ __attribute__((aligned(16))) T Zb[2][2][512];
     __shared__ __attribute__((aligned(16))) T Vb[2][2][512];
     __shared__ __attribute__((aligned(16))) T Vtb[2][2][512];
-    __shared__ __attribute__((aligned(16))) T Tb[2][kTPairs * 2 * 512];   // T fragments of the chunk
-    __shared__ __attribute__((aligned(16))) T Vs[2][kChunk * 16];         // V slice: 64 rows x 16 columns
-    __shared__ float Gs[2][kChunk];
 
     const int n = blockIdx.x, h = blockIdx.y, nb = blockIdx.z;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, qd = lane >> 4;
     const int kh = h / (Nv / Nk);
     const int c0 = seq_first[n], c1 = seq_first[n + 1];
+    // The chunks of a sequence are consecutive 64-token pieces of its token
+    // range, so their start and length follow from the range without reading
+    // the chunk table inside the loop.
+    const int64_t seq_s = c0 < c1 ? (int64_t)chunk_start[c0] : 0;
+    const int64_t seq_e = c0 < c1 ? (int64_t)chunk_start[c1 - 1] + chunk_len[c1 - 1] : 0;
     const int64_t sbase = ((int64_t)n * Nv + h) * DK * DV;
     const int ntp = (w >> 1) + 1;               // T pairs of wave w: positions 0..32*ntp-1
     const int pbase = (w == 0) ? 0 : (w == 1 ? 1 : (w == 2 ? 2 : 4));
+    const int ob = out_f32 ? 4 : 2;
+
+    // lane-constant byte offsets of the bounds-checked loads and stores
+    int kq_off[LPT];
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+        const int idx = tid + 256 * i;
+        kq_off[i] = ((idx / NSEG) * Nk * DK + (idx % NSEG) * 8) * 2;
+    }
+    const int v_off = ((tid >> 2) * Nv * DV + (tid & 3) * 4) * 2;
+    int o_off[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o_off[j] = ((w * 16 + 4 * qd + j) * Nv * DV + r) * ob;
 
     // state tiles owned by this wave
     f32x4 S[TPW];
@@ -673,27 +732,13 @@ __global__ __launch_bounds__(256) void k_state_output(const bf16* __restrict__ q
         for (int j = 0; j < 4; ++j)
             S[t][j] = (db < NDB && S0) ? S0[sbase + (int64_t)(db * 16 + 4 * qd + j) * DV + nb * 16 + r] : 0.f;
     }
-    auto publish_state = [&]() {
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            const int db = w * TPW + t;
-            if (db < NDB) {
-                float x[8] = {S[t][0], S[t][1], S[t][2], S[t][3], 0.f, 0.f, 0.f, 0.f};
-                const Split<T> sp = split8<T>(x);
-                typename Vec<T>::v4 hi4 = {sp.hi[0], sp.hi[1], sp.hi[2], sp.hi[3]};
-                typename Vec<T>::v4 lo4 = {sp.lo[0], sp.lo[1], sp.lo[2], sp.lo[3]};
-                *reinterpret_cast<typename Vec<T>::v4*>(&Sb[db >> 1][0][lane * 8 + 4 * (db & 1)]) = hi4;
-                *reinterpret_cast<typename Vec<T>::v4*>(&Sb[db >> 1][1][lane * 8 + 4 * (db & 1)]) = lo4;
-            }
-        }
-    };
     auto store_split_half = [&](T (*buf)[2][512], int tp, int half, const f32x4& x) {
         float xx[8] = {x[0], x[1], x[2], x[3], 0.f, 0.f, 0.f, 0.f};
         const Split<T> sp = split8<T>(xx);
-        typename Vec<T>::v4 hi4 = {sp.hi[0], sp.hi[1], sp.hi[2], sp.hi[3]};
-        typename Vec<T>::v4 lo4 = {sp.lo[0], sp.lo[1], sp.lo[2], sp.lo[3]};
-        *reinterpret_cast<typename Vec<T>::v4*>(&buf[tp][0][lane * 8 + 4 * half]) = hi4;
-        *reinterpret_cast<typename Vec<T>::v4*>(&buf[tp][1][lane * 8 + 4 * half]) = lo4;
+        v4 hi4 = {sp.hi[0], sp.hi[1], sp.hi[2], sp.hi[3]};
+        v4 lo4 = {sp.lo[0], sp.lo[1], sp.lo[2], sp.lo[3]};
+        *reinterpret_cast<v4*>(&buf[tp][0][lane * 8 + 4 * half]) = hi4;
+        *reinterpret_cast<v4*>(&buf[tp][1][lane * 8 + 4 * half]) = lo4;
     };
     auto load_split = [&](T (*buf)[2][512], int tp) {
         Split<T> sp;
@@ -701,50 +746,76 @@ __global__ __launch_bounds__(256) void k_state_output(const bf16* __restrict__ q
         sp.lo = *reinterpret_cast<const v8*>(&buf[tp][1][lane * 8]);
         return sp;
     };
+    auto publish_state = [&]() {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int db = w * TPW + t;
+            if (db < NDB) store_split_half(Sb, db >> 1, db & 1, S[t]);
+        }
+    };
+    auto rsrc = [&](const void* base, int64_t elem_off, int elem_bytes, uint32_t bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(reinterpret_cast<const char*>(base)) + elem_off * elem_bytes, (short)0, (int)bytes, RSRC);
+    };
 
-    // Operands of the next chunk, fetched into registers while the current
-    // chunk is computed and written to the other LDS buffer at the end of the
-    // step; computation reads only LDS. Every load reads a valid address (rows
-    // past the chunk end are clamped to its last row) with no branch around
-    // it, and rows past the end are zeroed when staged.
-    constexpr int TLD = kTPairs * 2 * 512 * 2 / 16 / 256;   // 16-byte T loads per thread (3)
+    // Next chunk's operands, fetched into registers while the current chunk is
+    // computed: the K and Q tiles at the start of a step, the rest after its
+    // first barrier, so that the loads drain while the step computes. The gate
+    // values and factors are contiguous per (chunk, head); wave 0 and wave 1
+    // fetch them.
     struct Ahead {
-        v8 kr[LPT], qr[LPT], tr[TLD];
-        typename Vec<T>::v4 vr;
-        float g;
+        i4 kr[LPT], qr[LPT], tr[TLD], rr;
+        i2 vr;
+        int g;
         int L;
         int64_t s;
     };
-    auto fetch = [&](int c, Ahead& A) {
-        A.s = chunk_start[c];
-        A.L = chunk_len[c];
-        const int last = A.L > 0 ? A.L - 1 : 0;
+    auto fetch_kq = [&](int c, Ahead& A) {
+        A.s = seq_s + (int64_t)(c - c0) * kChunk;
+        A.L = (int)max((int64_t)0, min((int64_t)kChunk, seq_e - A.s));
+        const int L = A.L;
+        const uint32_t kq_bytes = L > 0 ? (uint32_t)((L - 1) * Nk * DK + DK) * 2u : 0u;
+        const auto rk = rsrc(k, (A.s * Nk + kh) * DK, 2, kq_bytes);
+        const auto rq = rsrc(q, (A.s * Nk + kh) * DK, 2, kq_bytes);
 #pragma unroll
         for (int i = 0; i < LPT; ++i) {
-            const int idx = tid + 256 * i, row = min(idx / NSEG, last), seg = idx % NSEG;
-            A.kr[i] = *reinterpret_cast<const v8*>(k + ((A.s + row) * Nk + kh) * DK + seg * 8);
-            A.qr[i] = *reinterpret_cast<const v8*>(q + ((A.s + row) * Nk + kh) * DK + seg * 8);
+            A.kr[i] = __builtin_bit_cast(i4, __builtin_amdgcn_raw_buffer_load_b128(rk, kq_off[i], 0, 0));
+            A.qr[i] = __builtin_bit_cast(i4, __builtin_amdgcn_raw_buffer_load_b128(rq, kq_off[i], 0, 0));
         }
-        const T* tsrc = Tf + ((int64_t)c * Nv + h) * kTPairs * 2 * 512;
+    };
+    auto fetch_rest = [&](int c, Ahead& A) {
+        const int L = A.L;
+        const auto rt = rsrc(Tf, ((int64_t)c * Nv + h) * TFRAG, 2, TFRAG * 2);
 #pragma unroll
-        for (int i = 0; i < TLD; ++i) A.tr[i] = *reinterpret_cast<const v8*>(tsrc + (tid + 256 * i) * 8);
-        const int vrow = min(tid >> 2, last);
-        A.vr = *reinterpret_cast<const typename Vec<T>::v4*>(v + ((A.s + vrow) * Nv + h) * DV + nb * 16 + (tid & 3) * 4);
-        A.g = G[(A.s + min(tid & 63, last)) * Nv + h];   // rows past the end repeat G_last
+        for (int i = 0; i < TLD; ++i)
+            A.tr[i] = __builtin_bit_cast(i4, __builtin_amdgcn_raw_buffer_load_b128(rt, (tid + 256 * i) * 16, 0, 0));
+        const auto rv = rsrc(v, (A.s * Nv + h) * DV + nb * 16, 2,
+                             L > 0 ? (uint32_t)((L - 1) * Nv * DV + 16) * 2u : 0u);
+        A.vr = __builtin_bit_cast(i2, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, 0, 0));
+        if (w == 0) {
+            const auto rg = rsrc(Gc, ((int64_t)c * Nv + h) * kChunk, 4, kChunk * 4);
+            A.g = __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(rg, lane * 4, 0, 0));
+        } else if (w == 1) {
+            const auto rr = rsrc(R, ((int64_t)c * Nv + h) * kChunk, 16, kChunk * 16);
+            A.rr = __builtin_bit_cast(i4, __builtin_amdgcn_raw_buffer_load_b128(rr, lane * 16, 0, 0));
+        }
+    };
+    auto fetch = [&](int c, Ahead& A) {
+        fetch_kq(c, A);
+        fetch_rest(c, A);
     };
     auto stage = [&](const Ahead& A, int buf) {
 #pragma unroll
         for (int i = 0; i < LPT; ++i) {
             const int idx = tid + 256 * i, row = idx / NSEG, seg = idx % NSEG;
-            const bool ok = row < A.L;
-            *reinterpret_cast<v8*>(&Ks[buf][row * KP + seg * 8]) = ok ? A.kr[i] : zero_pair<T>();
-            *reinterpret_cast<v8*>(&Qs[buf][row * KP + seg * 8]) = ok ? A.qr[i] : zero_pair<T>();
+            *reinterpret_cast<i4*>(&Ks[buf][row * KP + seg * 8]) = A.kr[i];
+            *reinterpret_cast<i4*>(&Qs[buf][row * KP + seg * 8]) = A.qr[i];
         }
 #pragma unroll
-        for (int i = 0; i < TLD; ++i) *reinterpret_cast<v8*>(&Tb[buf][(tid + 256 * i) * 8]) = A.tr[i];
-        typename Vec<T>::v4 zero4 = {to_t<T>(0.f), to_t<T>(0.f), to_t<T>(0.f), to_t<T>(0.f)};
-        *reinterpret_cast<typename Vec<T>::v4*>(&Vs[buf][tid * 4]) = (tid >> 2) < A.L ? A.vr : zero4;
-        Gs[buf][tid & 63] = A.L > 0 ? A.g : 0.f;          // the four waves write the same values
+        for (int i = 0; i < TLD; ++i) *reinterpret_cast<i4*>(&Tb[buf][(tid + 256 * i) * 8]) = A.tr[i];
+        *reinterpret_cast<i2*>(&Vs[buf][tid * 4]) = A.vr;
+        if (w == 0) Gs[buf][lane] = __builtin_bit_cast(float, A.g);
+        else if (w == 1) Rs[buf][lane] = __builtin_bit_cast(f32x4, A.rr);
     };
 
     if (c0 < c1) {
@@ -758,15 +829,15 @@ __global__ __launch_bounds__(256) void k_state_output(const bf16* __restrict__ q
         for (int c = c0; c < c1; ++c) {
             const int buf = (c - c0) & 1;
             const bool more = c + 1 < c1;
-            if (more) fetch(c + 1, nxt);
+            if (more) fetch_kq(c + 1, nxt);
             const int L = cur_L;
             const int64_t s = cur_s;
             const T* Kb = Ks[buf];
             const T* Qb = Qs[buf];
 
-            // ---- all LDS operands of the first phase, read in one batch
+            // ---- operands of the first phase, all read from LDS before any product
             Split<T> BS[NKP];
-            v8 ka[NKP], qa[NKP], kj[4][NKP];
+            v8 ka[NKP], qa[NKP], kj[3][NKP];
 #pragma unroll
             for (int kp = 0; kp < NKP; ++kp) {
                 BS[kp] = load_split(Sb, kp);
@@ -774,72 +845,90 @@ __global__ __launch_bounds__(256) void k_state_output(const bf16* __restrict__ q
                 qa[kp] = load_pair_row<T>(&Qb[(w * 16 + r) * KP + kp * 32], qd);
             }
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj)
-                if (tj < w)                       // tile tj == w reuses ka
+            for (int tj = 0; tj < 3; ++tj)
+                if (tj < w)
 #pragma unroll
                     for (int kp = 0; kp < NKP; ++kp) kj[tj][kp] = load_pair_row<T>(&Kb[(tj * 16 + r) * KP + kp * 32], qd);
-            float grow[4], gcol[4][4], vj[4];
+            f32x4 rrow[4], rj[3];
+            float gj[4], vrow[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                grow[j] = Gs[buf][w * 16 + 4 * qd + j];
-                vj[j] = to_f(Vs[buf][(w * 16 + 4 * qd + j) * 16 + r]);
+                rrow[j] = Rs[buf][w * 16 + 4 * qd + j];
+                gj[j] = Gs[buf][w * 16 + 4 * qd + j];
+                vrow[j] = to_f(Vs[buf][(w * 16 + 4 * qd + j) * 16 + r]);
             }
+            const f32x4 ri = Rs[buf][w * 16 + r];
+            const float gi = Gs[buf][w * 16 + r];
+            float bend[3];                          // R.z at the ends of blocks 1..3
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj)
+            for (int b = 0; b < 3; ++b) bend[b] = Rs[buf][16 * (b + 1) + 15].z;
+            float rw[3][4];
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) gcol[tj][jj] = Gs[buf][tj * 16 + 4 * qd + jj];
-            const float g_last = L > 0 ? Gs[buf][L - 1] : 0.f;
-            const float g_i = Gs[buf][w * 16 + r];
+            for (int tj = 0; tj < 3; ++tj)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) rw[tj][jj] = Rs[buf][tj * 16 + 4 * qd + jj].w;
+            // transposed K^T operands of the state update
+            v8 kt[TPW][2];
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const int db = min(w * TPW + t, NDB - 1);
+#pragma unroll
+                for (int tp = 0; tp < 2; ++tp) {
+                    const int row = tp * 32 + 4 * qd + ((lane & 15) >> 2), col = db * 16 + 4 * (lane & 3);
+                    typedef s4 __attribute__((address_space(3))) * lds_s4;
+                    s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&Kb[row * KP + col]));
+                    s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&Kb[(row + 16) * KP + col]));
+                    kt[t][tp] = concat<T>(__builtin_bit_cast(v4, lo), __builtin_bit_cast(v4, hi));
+                }
+            }
 
             // ---- Y = K S_in, Q S_in (hi and lo passes in separate chains), scores K Q^T
-            f32x4 Yh = {0.f, 0.f, 0.f, 0.f}, Yl = Yh, Qh = Yh, Ql = Yh;
+            f32x4 Yh = {0.f, 0.f, 0.f, 0.f}, Yl = Yh, Qh = Yh, Ql = Yh, pd = Yh;
+            f32x4 po[3];                               // earlier blocks tj < w
+#pragma unroll
+            for (int tj = 0; tj < 3; ++tj) po[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kp = 0; kp < NKP; ++kp) {
                 Yh = mfma_pair(ka[kp], BS[kp].hi, Yh);
                 Qh = mfma_pair(qa[kp], BS[kp].hi, Qh);
                 Yl = mfma_pair(ka[kp], BS[kp].lo, Yl);
                 Ql = mfma_pair(qa[kp], BS[kp].lo, Ql);
-            }
-            f32x4 pt[4];
+                pd = mfma_pair(ka[kp], qa[kp], pd);           // diagonal block (tj == w)
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj) {
-                pt[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (tj <= w)
-#pragma unroll
-                    for (int kp = 0; kp < NKP; ++kp) pt[tj] = mfma_pair(tj == w ? ka[kp] : kj[tj][kp], qa[kp], pt[tj]);
+                for (int tj = 0; tj < 3; ++tj)
+                    if (tj < w) po[tj] = mfma_pair(kj[tj][kp], qa[kp], po[tj]);
             }
-
             // ---- Z = V - exp(G) Y -> LDS
-            float eg[4];
             f32x4 Z;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                eg[j] = __expf(grow[j]);
-                Z[j] = vj[j] - eg[j] * (Yh[j] + Yl[j]);
-            }
+            for (int j = 0; j < 4; ++j) Z[j] = vrow[j] - rrow[j].x * (Yh[j] + Yl[j]);
             store_split_half(Zb, w >> 1, w & 1, Z);
-            // transposed K^T operands of the state update (independent of the exchange)
-            v8 kt[TPW][2];
+
+            // ---- score decay: diagonal block exp(G_i - G_j) (j <= i); earlier blocks
+            //      R.z_i * (R.z at the ends of the blocks in between) * R.w_j
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                const int db = min(w * TPW + t, NDB - 1);
-#pragma unroll
-                for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int m = tp * 32 + (e < 4 ? 4 * qd + e : 16 + 4 * qd + e - 4);
-                        kt[t][tp][e] = Kb[m * KP + db * 16 + r];
-                    }
+            for (int jj = 0; jj < 4; ++jj) {
+                const int jr = 4 * qd + jj;
+                const float d = __expf(gi - gj[jj]);
+                pd[jj] = jr <= r ? pd[jj] * d : 0.f;
             }
-            // scores: decay and mask (rows j, column i = 16w + r)
+            float gam = 1.f;
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj)
+            for (int tj = 2; tj >= 0; --tj) {
+                if (tj < w) {
+                    if (tj + 1 < w) gam *= bend[tj];
+                    const float fi = ri.z * gam;
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int j = tj * 16 + 4 * qd + jj;
-                    pt[tj][jj] = (tj <= w && j <= w * 16 + r) ? pt[tj][jj] * __expf(g_i - gcol[tj][jj]) : 0.f;
+                    for (int jj = 0; jj < 4; ++jj) po[tj][jj] *= fi * rw[tj][jj];
                 }
+            }
+            // score tiles by block index: tj < w earlier blocks, tj == w diagonal, tj > w zero
+            f32x4 pt[4];
+            const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj) pt[tj] = tj == w ? pd : (tj < w && tj < 3 ? po[tj < 3 ? tj : 0] : zero4);
             __syncthreads();
+            if (more) fetch_rest(c + 1, nxt);
 
             // ---- V_new = T Z (only position blocks <= w contribute)
             Split<T> tf[2], zf[2];
@@ -864,7 +953,7 @@ __global__ __launch_bounds__(256) void k_state_output(const bf16* __restrict__ q
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 VN[j] = Va[j] + Vb2[j];
-                VD[j] = VN[j] * __expf(g_last - grow[j]);
+                VD[j] = VN[j] * rrow[j].y;
             }
             store_split_half(Vb, w >> 1, w & 1, VN);
             store_split_half(Vtb, w >> 1, w & 1, VD);
@@ -876,7 +965,7 @@ __global__ __launch_bounds__(256) void k_state_output(const bf16* __restrict__ q
 #pragma unroll
             for (int tp = 0; tp < 2; ++tp)
                 if (tp < ntp) vn[tp] = load_split(Vb, tp);
-            const float a_last = __expf(g_last);
+            const float a_last = L > 0 ? Rs[buf][L - 1].x : 1.f;
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
                 const int db = w * TPW + t;
@@ -902,7 +991,7 @@ __global__ __launch_bounds__(256) void k_state_output(const bf16* __restrict__ q
             // ---- O = scale [exp(G) Q S_in + (Q K^T (.) D) V_new] for rows 16w..16w+15
             f32x4 out, ol = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) out[j] = eg[j] * (Qh[j] + Ql[j]);
+            for (int j = 0; j < 4; ++j) out[j] = rrow[j].x * (Qh[j] + Ql[j]);
 #pragma unroll
             for (int tp = 0; tp < 2; ++tp) {
                 if (tp < ntp) {
@@ -912,15 +1001,14 @@ __global__ __launch_bounds__(256) void k_state_output(const bf16* __restrict__ q
                     ol = mfma_pair(pa.hi, vn[tp].lo, ol);
                 }
             }
+            const auto ro = rsrc(o, (s * Nv + h) * DV + nb * 16, ob,
+                                 L > 0 ? (uint32_t)(((L - 1) * Nv * DV + 16) * ob) : 0u);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = w * 16 + 4 * qd + j;
-                if (row < L) {
-                    const int64_t idx = ((s + row) * Nv + h) * DV + nb * 16 + r;
-                    const float val = scale * (out[j] + ol[j]);
-                    if (out_f32) reinterpret_cast<float*>(o)[idx] = val;
-                    else reinterpret_cast<T*>(o)[idx] = to_t<T>(val);
-                }
+            for (int j = 0; j < 4; ++j) {               // rows past the chunk end fall outside ro
+                const float val = scale * (out[j] + ol[j]);
+                if (out_f32) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), ro, o_off[j], 0, 0);
+                else __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, to_t<T>(val)), ro,
+                                                           o_off[j], 0, 0);
             }
             __syncthreads();
         }
@@ -952,7 +1040,8 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
     mark(1);
     if (NT > 0) {
         const int64_t units = (int64_t)NT * a.Nv;
-        k_gate_cumsum<<<(unsigned)((units + 255) / 256), 256, 0, st>>>(a.g, a.chunk_start, a.chunk_len, NT, a.Nv, a.G);
+        k_gate_cumsum<<<(unsigned)((units + 255) / 256), 256, 0, st>>>(a.g, a.chunk_start, a.chunk_len, NT, a.Nv, a.G,
+                                                                        fused ? (f32x4*)a.R : nullptr, (float*)a.Gc);
     }
     mark(2);
     if (NT > 0)
@@ -969,7 +1058,8 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
         if constexpr (kFused) {
             if (fused) {
                 k_state_output<DK, DV><<<dim3(a.N, a.Nv, DV / 16), 256, 0, st>>>(
-                    (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.G, (const bf16*)a.Tf, a.S0,
+                    (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const float*)a.Gc, (const f32x4*)a.R,
+                    (const bf16*)a.Tf, a.S0,
                     a.chunk_start, a.chunk_len, a.seq_first, a.Nk, a.Nv, a.scale, a.out_f32, a.o, a.ST);
             }
         }
