@@ -132,6 +132,20 @@ def cpu_baseline(inp: dict, target_seconds: float) -> dict:
     }
 
 
+def copy_probe(mib: int) -> None:
+    """A streaming elementwise kernel that reads and writes `mib` MiB each, three
+    times: its FETCH_SIZE / WRITE_SIZE counter readings against the known byte
+    counts give the scale factor applied to the kernels' counter readings."""
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +154,8 @@ def main():
     ap.add_argument("--workload", type=int, default=5, help="synth.WORKLOADS index (default 5)")
     ap.add_argument("--out-dtype", choices=("io", "f32"), default="io")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget; 0 skips it")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB three times (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this implementation runs on one GPU only; --gpus %d is not supported" % args.gpus,
@@ -148,6 +164,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib)
+        return
 
     w = synth.WORKLOADS[args.workload]
     inp = synth.generate(w, seed=args.workload)

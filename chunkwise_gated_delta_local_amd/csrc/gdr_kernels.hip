@@ -642,28 +642,37 @@ __global__ __launch_bounds__(256) void k_output(const T* __restrict__ q, const T
 }
 
 // ============================================================ K4 + K5 fused: state pass with output
-// Production path for bf16 inputs. One workgroup (4 wavefronts) per (sequence,
-// value head, 16 columns of dv) walks the sequence's chunks in order with the
-// state slice S (dk x 16, fp32) on chip, and produces the output of each chunk
-// as it goes, so neither the per-chunk states nor V_new ever reach HBM.
+// Production path for bf16 inputs. One workgroup of eight wavefronts per
+// (sequence, value head, 16 columns of dv) walks the sequence's chunks in
+// order with the state slice S (dk x 16, fp32) on chip, and produces the output
+// of each chunk as it goes, so neither the per-chunk states nor V_new reach HBM.
 // Per chunk (ChunkGatedDeltaRule page, formulas (3)-(6); FLA DeltaNet article,
 // sections 2.3-2.4), with T = A diag(beta) from the A-build kernel:
-//   Y     = K S_in                          (wave w: positions 16w..16w+15)
-//   Z     = V - diag(exp(G)) Y              so that V_new = U - W S_in = T Z
-//   V_new = T Z                             (T lower triangular: blocks <= w)
-//   S_out = exp(G_last) S_in + K^T diag(exp(G_last - G)) V_new   (wave w: dk tiles of w)
-//   O     = scale [diag(exp(G)) Q S_in + (Q K^T (.) D) V_new]      (wave w: rows of w)
-// Z, V_new and the new state are exchanged between the wavefronts through LDS
-// as split (hi, lo) bf16 pair fragments (three barriers per chunk). The next
-// chunk's K and Q tiles, T fragments, V slice and gate factors are fetched
-// with bounds-checked buffer loads (rows past the chunk end read as zero) while
-// the current chunk is computed, and staged into the other half of a
-// double-buffered LDS area at the end of the step; computation reads only LDS.
-// K^T operands come from the K tile through transposing LDS reads. The decay
-// exp(G_i - G_j) of the score block is a product of the precomputed factors R
-// outside the diagonal 16x16 blocks, where it is evaluated directly.
+//   Y     = K S_in,  Z = V - diag(exp(G)) Y      so that V_new = U - W S_in = T Z
+//   V_new = T Z                                  (T lower triangular)
+//   S_out = exp(G_last) S_in + K^T diag(exp(G_last - G)) V_new
+//   O     = scale [diag(exp(G)) Q S_in + (Q K^T (.) D) V_new]
+// The wavefronts split into two roles that run side by side, one of each on
+// every SIMD:
+//   state waves  (0..3): wave w owns positions 16w..16w+15 for Y, Z, Q S_in and
+//                        V_new, and dk tiles of S for the update. This is the
+//                        sequential chain.
+//   output waves (4..7): wave 4+w computes the score block of positions
+//                        16w..16w+15 and their output, and moves the next
+//                        chunk's tiles from global memory into LDS.
+// Each chunk step has three phases separated by workgroup barriers:
+//   A  state: S_in (split) from LDS, Y, Z -> LDS      output: scores + decay
+//   B  state: Q S_in, V_new = T Z -> LDS               output: stage chunk c+1,
+//                                                       fetch chunk c+2
+//   C  state: S update, S_out (split) -> LDS           output: O -> global
+// K and Q tiles sit in LDS with the columns of every 32-block permuted so that
+// a pair fragment is one 16-byte read; K^T operands come from the same tile
+// through transposing LDS reads. Rows past the chunk end are zero (bounds-
+// checked buffer loads). The decay exp(G_i - G_j) of the score block is a
+// product of the precomputed factors R outside the diagonal 16x16 blocks,
+// where it is evaluated directly.
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void k_state_output(const bf16* __restrict__ q, const bf16* __restrict__ k,
+__global__ __launch_bounds__(512) void k_state_output(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                        const bf16* __restrict__ v, const float* __restrict__ Gc,
                                                        const f32x4* __restrict__ R, const bf16* __restrict__ Tf,
                                                        const float* __restrict__ S0,
@@ -678,13 +687,14 @@ __global__ __launch_bounds__(256) void k_state_output(const bf16* __restrict__ q
     typedef short s4 __attribute__((ext_vector_type(4)));
     typedef int i4 __attribute__((ext_vector_type(4)));
     typedef int i2 __attribute__((ext_vector_type(2)));
+    typedef s4 __attribute__((address_space(3))) * lds_s4;
     constexpr int NKP = DK / 32, NDB = DK / 16;
-    constexpr int TPW = (NDB + 3) / 4;          // state tiles owned per wave
-    constexpr int KP = DK + 8;                  // padded LDS row (elements)
+    constexpr int TPW = (NDB + 3) / 4;          // state tiles owned per state wave
+    constexpr int KP = DK + 8;                  // LDS row pitch of the K and Q tiles (elements)
     constexpr int NSEG = DK / 8;                // 16-byte segments per row
-    constexpr int LPT = kChunk * NSEG / 256;    // row segments loaded per thread
+    constexpr int LPT = kChunk * NSEG / 256;    // row segments fetched per output-wave thread
     constexpr int TFRAG = kTPairs * 2 * 512;    // T elements per (chunk, head)
-    constexpr int TLD = TFRAG * 2 / 16 / 256;   // 16-byte T loads per thread
+    constexpr int TLD = TFRAG * 2 / 16 / 256;   // 16-byte T loads per output-wave thread
     constexpr int RSRC = 0x00020000;            // buffer descriptor word 3 (raw 32-bit access)
     __shared__ __attribute__((aligned(16))) T Ks[2][kChunk * KP];
     __shared__ __attribute__((aligned(16))) T Qs[2][kChunk * KP];
@@ -696,42 +706,24 @@ __global__ __launch_bounds__(256) void k_state_output(const bf16* __restrict__ q
     __shared__ __attribute__((aligned(16))) T Zb[2][2][512];
     __shared__ __attribute__((aligned(16))) T Vb[2][2][512];
     __shared__ __attribute__((aligned(16))) T Vtb[2][2][512];
+    __shared__ __attribute__((aligned(16))) f32x4 QSx[4][64];
 
     const int n = blockIdx.x, h = blockIdx.y, nb = blockIdx.z;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, qd = lane >> 4;
+    const int tid = threadIdx.x;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave index, uniform
+    const int lane = tid & 63, r = lane & 15, qd = lane >> 4;
     const int kh = h / (Nv / Nk);
     const int c0 = seq_first[n], c1 = seq_first[n + 1];
     // The chunks of a sequence are consecutive 64-token pieces of its token
-    // range, so their start and length follow from the range without reading
-    // the chunk table inside the loop.
+    // range, so their start and length follow from the range.
     const int64_t seq_s = c0 < c1 ? (int64_t)chunk_start[c0] : 0;
     const int64_t seq_e = c0 < c1 ? (int64_t)chunk_start[c1 - 1] + chunk_len[c1 - 1] : 0;
-    const int64_t sbase = ((int64_t)n * Nv + h) * DK * DV;
-    const int ntp = (w >> 1) + 1;               // T pairs of wave w: positions 0..32*ntp-1
-    const int pbase = (w == 0) ? 0 : (w == 1 ? 1 : (w == 2 ? 2 : 4));
-    const int ob = out_f32 ? 4 : 2;
-
-    // lane-constant byte offsets of the bounds-checked loads and stores
-    int kq_off[LPT];
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-        const int idx = tid + 256 * i;
-        kq_off[i] = ((idx / NSEG) * Nk * DK + (idx % NSEG) * 8) * 2;
-    }
-    const int v_off = ((tid >> 2) * Nv * DV + (tid & 3) * 4) * 2;
-    int o_off[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o_off[j] = ((w * 16 + 4 * qd + j) * Nv * DV + r) * ob;
-
-    // state tiles owned by this wave
-    f32x4 S[TPW];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        const int db = w * TPW + t;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            S[t][j] = (db < NDB && S0) ? S0[sbase + (int64_t)(db * 16 + 4 * qd + j) * DV + nb * 16 + r] : 0.f;
-    }
+    auto chunk_s = [&](int c) { return seq_s + (int64_t)(c - c0) * kChunk; };
+    auto chunk_L = [&](int c) { return (int)min((int64_t)kChunk, seq_e - chunk_s(c)); };
+    auto rsrc = [&](const void* base, int64_t elem_off, int elem_bytes, uint32_t bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(reinterpret_cast<const char*>(base)) + elem_off * elem_bytes, (short)0, (int)bytes, RSRC);
+    };
     auto store_split_half = [&](T (*buf)[2][512], int tp, int half, const f32x4& x) {
         float xx[8] = {x[0], x[1], x[2], x[3], 0.f, 0.f, 0.f, 0.f};
         const Split<T> sp = split8<T>(xx);
@@ -746,282 +738,304 @@ __global__ __launch_bounds__(256) void k_state_output(const bf16* __restrict__ q
         sp.lo = *reinterpret_cast<const v8*>(&buf[tp][1][lane * 8]);
         return sp;
     };
-    auto publish_state = [&]() {
+    // pair fragment of row `row` of a K or Q tile, contraction block kp (one 16-byte read)
+    auto tile_pair = [&](const T* tile, int row, int kp) {
+        return *reinterpret_cast<const v8*>(&tile[row * KP + kp * 32 + 8 * qd]);
+    };
+    const int64_t sbase = ((int64_t)n * Nv + h) * DK * DV;
+
+    if (wv < 4) {
+        // ======================================================== state waves
+        const int w = wv;
+        const int ntp = (w >> 1) + 1;                       // T pairs of block w: positions < 32 * ntp
+        const int pbase = (w == 0) ? 0 : (w == 1 ? 1 : (w == 2 ? 2 : 4));
+        f32x4 S[TPW];
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const int db = w * TPW + t;
-            if (db < NDB) store_split_half(Sb, db >> 1, db & 1, S[t]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                S[t][j] = (db < NDB && S0) ? S0[sbase + (int64_t)(db * 16 + 4 * qd + j) * DV + nb * 16 + r] : 0.f;
         }
-    };
-    auto rsrc = [&](const void* base, int64_t elem_off, int elem_bytes, uint32_t bytes) {
-        return __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<char*>(reinterpret_cast<const char*>(base)) + elem_off * elem_bytes, (short)0, (int)bytes, RSRC);
-    };
-
-    // Next chunk's operands, fetched into registers while the current chunk is
-    // computed: the K and Q tiles at the start of a step, the rest after its
-    // first barrier, so that the loads drain while the step computes. The gate
-    // values and factors are contiguous per (chunk, head); wave 0 and wave 1
-    // fetch them.
-    struct Ahead {
-        i4 kr[LPT], qr[LPT], tr[TLD], rr;
-        i2 vr;
-        int g;
-        int L;
-        int64_t s;
-    };
-    auto fetch_kq = [&](int c, Ahead& A) {
-        A.s = seq_s + (int64_t)(c - c0) * kChunk;
-        A.L = (int)max((int64_t)0, min((int64_t)kChunk, seq_e - A.s));
-        const int L = A.L;
-        const uint32_t kq_bytes = L > 0 ? (uint32_t)((L - 1) * Nk * DK + DK) * 2u : 0u;
-        const auto rk = rsrc(k, (A.s * Nk + kh) * DK, 2, kq_bytes);
-        const auto rq = rsrc(q, (A.s * Nk + kh) * DK, 2, kq_bytes);
-#pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            A.kr[i] = __builtin_bit_cast(i4, __builtin_amdgcn_raw_buffer_load_b128(rk, kq_off[i], 0, 0));
-            A.qr[i] = __builtin_bit_cast(i4, __builtin_amdgcn_raw_buffer_load_b128(rq, kq_off[i], 0, 0));
-        }
-    };
-    auto fetch_rest = [&](int c, Ahead& A) {
-        const int L = A.L;
-        const auto rt = rsrc(Tf, ((int64_t)c * Nv + h) * TFRAG, 2, TFRAG * 2);
-#pragma unroll
-        for (int i = 0; i < TLD; ++i)
-            A.tr[i] = __builtin_bit_cast(i4, __builtin_amdgcn_raw_buffer_load_b128(rt, (tid + 256 * i) * 16, 0, 0));
-        const auto rv = rsrc(v, (A.s * Nv + h) * DV + nb * 16, 2,
-                             L > 0 ? (uint32_t)((L - 1) * Nv * DV + 16) * 2u : 0u);
-        A.vr = __builtin_bit_cast(i2, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, 0, 0));
-        if (w == 0) {
-            const auto rg = rsrc(Gc, ((int64_t)c * Nv + h) * kChunk, 4, kChunk * 4);
-            A.g = __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(rg, lane * 4, 0, 0));
-        } else if (w == 1) {
-            const auto rr = rsrc(R, ((int64_t)c * Nv + h) * kChunk, 16, kChunk * 16);
-            A.rr = __builtin_bit_cast(i4, __builtin_amdgcn_raw_buffer_load_b128(rr, lane * 16, 0, 0));
-        }
-    };
-    auto fetch = [&](int c, Ahead& A) {
-        fetch_kq(c, A);
-        fetch_rest(c, A);
-    };
-    auto stage = [&](const Ahead& A, int buf) {
-#pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            const int idx = tid + 256 * i, row = idx / NSEG, seg = idx % NSEG;
-            *reinterpret_cast<i4*>(&Ks[buf][row * KP + seg * 8]) = A.kr[i];
-            *reinterpret_cast<i4*>(&Qs[buf][row * KP + seg * 8]) = A.qr[i];
-        }
-#pragma unroll
-        for (int i = 0; i < TLD; ++i) *reinterpret_cast<i4*>(&Tb[buf][(tid + 256 * i) * 8]) = A.tr[i];
-        *reinterpret_cast<i2*>(&Vs[buf][tid * 4]) = A.vr;
-        if (w == 0) Gs[buf][lane] = __builtin_bit_cast(float, A.g);
-        else if (w == 1) Rs[buf][lane] = __builtin_bit_cast(f32x4, A.rr);
-    };
-
-    if (c0 < c1) {
-        Ahead nxt;
-        fetch(c0, nxt);
-        stage(nxt, 0);
-        int cur_L = nxt.L;
-        int64_t cur_s = nxt.s;
-        publish_state();
-        __syncthreads();
-        for (int c = c0; c < c1; ++c) {
-            const int buf = (c - c0) & 1;
-            const bool more = c + 1 < c1;
-            if (more) fetch_kq(c + 1, nxt);
-            const int L = cur_L;
-            const int64_t s = cur_s;
-            const T* Kb = Ks[buf];
-            const T* Qb = Qs[buf];
-
-            // ---- operands of the first phase, all read from LDS before any product
-            Split<T> BS[NKP];
-            v8 ka[NKP], qa[NKP], kj[3][NKP];
-#pragma unroll
-            for (int kp = 0; kp < NKP; ++kp) {
-                BS[kp] = load_split(Sb, kp);
-                ka[kp] = load_pair_row<T>(&Kb[(w * 16 + r) * KP + kp * 32], qd);
-                qa[kp] = load_pair_row<T>(&Qb[(w * 16 + r) * KP + kp * 32], qd);
-            }
-#pragma unroll
-            for (int tj = 0; tj < 3; ++tj)
-                if (tj < w)
-#pragma unroll
-                    for (int kp = 0; kp < NKP; ++kp) kj[tj][kp] = load_pair_row<T>(&Kb[(tj * 16 + r) * KP + kp * 32], qd);
-            f32x4 rrow[4], rj[3];
-            float gj[4], vrow[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                rrow[j] = Rs[buf][w * 16 + 4 * qd + j];
-                gj[j] = Gs[buf][w * 16 + 4 * qd + j];
-                vrow[j] = to_f(Vs[buf][(w * 16 + 4 * qd + j) * 16 + r]);
-            }
-            const f32x4 ri = Rs[buf][w * 16 + r];
-            const float gi = Gs[buf][w * 16 + r];
-            float bend[3];                          // R.z at the ends of blocks 1..3
-#pragma unroll
-            for (int b = 0; b < 3; ++b) bend[b] = Rs[buf][16 * (b + 1) + 15].z;
-            float rw[3][4];
-#pragma unroll
-            for (int tj = 0; tj < 3; ++tj)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) rw[tj][jj] = Rs[buf][tj * 16 + 4 * qd + jj].w;
-            // transposed K^T operands of the state update
-            v8 kt[TPW][2];
+        auto publish_state = [&]() {
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
-                const int db = min(w * TPW + t, NDB - 1);
+                const int db = w * TPW + t;
+                if (db < NDB) store_split_half(Sb, db >> 1, db & 1, S[t]);
+            }
+        };
+        if (c0 < c1) {
+            publish_state();
+            __syncthreads();
+            for (int c = c0; c < c1; ++c) {
+                const int buf = (c - c0) & 1;
+                const int L = chunk_L(c);
+                const T* Kb = Ks[buf];
+                const T* Qb = Qs[buf];
+
+                // ---- A: Y = K S_in (hi and lo passes), Z = V - exp(G) Y -> LDS
+                Split<T> BS[NKP];
+                v8 ka[NKP];
+#pragma unroll
+                for (int kp = 0; kp < NKP; ++kp) {
+                    BS[kp] = load_split(Sb, kp);
+                    ka[kp] = tile_pair(Kb, w * 16 + r, kp);
+                }
+                f32x4 Yh = {0.f, 0.f, 0.f, 0.f}, Yl = Yh;
+#pragma unroll
+                for (int kp = 0; kp < NKP; ++kp) {
+                    Yh = mfma_pair(ka[kp], BS[kp].hi, Yh);
+                    Yl = mfma_pair(ka[kp], BS[kp].lo, Yl);
+                }
+                f32x4 rrow[4];
+                float vrow[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    rrow[j] = Rs[buf][w * 16 + 4 * qd + j];
+                    vrow[j] = to_f(Vs[buf][(w * 16 + 4 * qd + j) * 16 + r]);
+                }
+                f32x4 Z;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Z[j] = vrow[j] - rrow[j].x * (Yh[j] + Yl[j]);
+                store_split_half(Zb, w >> 1, w & 1, Z);
+                __syncthreads();                                                    // barrier 1
+
+                // ---- B: Q S_in for the output waves; V_new = T Z -> LDS
+                Split<T> tf[2], zf[2];
 #pragma unroll
                 for (int tp = 0; tp < 2; ++tp) {
-                    const int row = tp * 32 + 4 * qd + ((lane & 15) >> 2), col = db * 16 + 4 * (lane & 3);
-                    typedef s4 __attribute__((address_space(3))) * lds_s4;
-                    s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&Kb[row * KP + col]));
-                    s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&Kb[(row + 16) * KP + col]));
-                    kt[t][tp] = concat<T>(__builtin_bit_cast(v4, lo), __builtin_bit_cast(v4, hi));
+                    if (tp < ntp) {
+                        tf[tp].hi = load_frag<T>(&Tb[buf][(pbase + tp) * 2 * 512], lane);
+                        tf[tp].lo = load_frag<T>(&Tb[buf][(pbase + tp) * 2 * 512 + 512], lane);
+                        zf[tp] = load_split(Zb, tp);
+                    }
                 }
-            }
-
-            // ---- Y = K S_in, Q S_in (hi and lo passes in separate chains), scores K Q^T
-            f32x4 Yh = {0.f, 0.f, 0.f, 0.f}, Yl = Yh, Qh = Yh, Ql = Yh, pd = Yh;
-            f32x4 po[3];                               // earlier blocks tj < w
+                v8 qa[NKP];
 #pragma unroll
-            for (int tj = 0; tj < 3; ++tj) po[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int kp = 0; kp < NKP; ++kp) qa[kp] = tile_pair(Qb, w * 16 + r, kp);
+                f32x4 Qh = {0.f, 0.f, 0.f, 0.f}, Ql = Qh;
 #pragma unroll
-            for (int kp = 0; kp < NKP; ++kp) {
-                Yh = mfma_pair(ka[kp], BS[kp].hi, Yh);
-                Qh = mfma_pair(qa[kp], BS[kp].hi, Qh);
-                Yl = mfma_pair(ka[kp], BS[kp].lo, Yl);
-                Ql = mfma_pair(qa[kp], BS[kp].lo, Ql);
-                pd = mfma_pair(ka[kp], qa[kp], pd);           // diagonal block (tj == w)
-#pragma unroll
-                for (int tj = 0; tj < 3; ++tj)
-                    if (tj < w) po[tj] = mfma_pair(kj[tj][kp], qa[kp], po[tj]);
-            }
-            // ---- Z = V - exp(G) Y -> LDS
-            f32x4 Z;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) Z[j] = vrow[j] - rrow[j].x * (Yh[j] + Yl[j]);
-            store_split_half(Zb, w >> 1, w & 1, Z);
-
-            // ---- score decay: diagonal block exp(G_i - G_j) (j <= i); earlier blocks
-            //      R.z_i * (R.z at the ends of the blocks in between) * R.w_j
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int jr = 4 * qd + jj;
-                const float d = __expf(gi - gj[jj]);
-                pd[jj] = jr <= r ? pd[jj] * d : 0.f;
-            }
-            float gam = 1.f;
-#pragma unroll
-            for (int tj = 2; tj >= 0; --tj) {
-                if (tj < w) {
-                    if (tj + 1 < w) gam *= bend[tj];
-                    const float fi = ri.z * gam;
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) po[tj][jj] *= fi * rw[tj][jj];
+                for (int kp = 0; kp < NKP; ++kp) {
+                    Qh = mfma_pair(qa[kp], BS[kp].hi, Qh);
+                    Ql = mfma_pair(qa[kp], BS[kp].lo, Ql);
                 }
-            }
-            // score tiles by block index: tj < w earlier blocks, tj == w diagonal, tj > w zero
-            f32x4 pt[4];
-            const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+                f32x4 Va = {0.f, 0.f, 0.f, 0.f}, Vl = Va;
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj) pt[tj] = tj == w ? pd : (tj < w && tj < 3 ? po[tj < 3 ? tj : 0] : zero4);
-            __syncthreads();
-            if (more) fetch_rest(c + 1, nxt);
-
-            // ---- V_new = T Z (only position blocks <= w contribute)
-            Split<T> tf[2], zf[2];
-#pragma unroll
-            for (int tp = 0; tp < 2; ++tp) {
-                if (tp < ntp) {
-                    tf[tp].hi = load_frag<T>(&Tb[buf][(pbase + tp) * 2 * 512], lane);
-                    tf[tp].lo = load_frag<T>(&Tb[buf][(pbase + tp) * 2 * 512 + 512], lane);
-                    zf[tp] = load_split(Zb, tp);
+                for (int tp = 0; tp < 2; ++tp) {
+                    if (tp < ntp) {
+                        Va = mfma_pair(tf[tp].hi, zf[tp].hi, Va);
+                        Vl = mfma_pair(tf[tp].lo, zf[tp].hi, Vl);
+                        Vl = mfma_pair(tf[tp].hi, zf[tp].lo, Vl);
+                    }
                 }
-            }
-            f32x4 Va = {0.f, 0.f, 0.f, 0.f}, Vb2 = Va;
+                f32x4 VN, VD;
 #pragma unroll
-            for (int tp = 0; tp < 2; ++tp) {
-                if (tp < ntp) {
-                    Va = mfma_pair(tf[tp].hi, zf[tp].hi, Va);
-                    Vb2 = mfma_pair(tf[tp].lo, zf[tp].hi, Vb2);
-                    Vb2 = mfma_pair(tf[tp].hi, zf[tp].lo, Vb2);
+                for (int j = 0; j < 4; ++j) {
+                    VN[j] = Va[j] + Vl[j];
+                    VD[j] = VN[j] * rrow[j].y;
                 }
-            }
-            f32x4 VN, VD;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                VN[j] = Va[j] + Vb2[j];
-                VD[j] = VN[j] * rrow[j].y;
-            }
-            store_split_half(Vb, w >> 1, w & 1, VN);
-            store_split_half(Vtb, w >> 1, w & 1, VD);
-            __syncthreads();
+                store_split_half(Vtb, w >> 1, w & 1, VD);
+                store_split_half(Vb, w >> 1, w & 1, VN);
+                QSx[w][lane] = Qh + Ql;
+                __syncthreads();                                                    // barrier 2
 
-            // ---- S_out = exp(G_last) S_in + K^T V_decayed for the dk tiles of this wave
-            const Split<T> vt[2] = {load_split(Vtb, 0), load_split(Vtb, 1)};
-            Split<T> vn[2];
+                // ---- C: S_out = exp(G_last) S_in + K^T V_decayed for the dk tiles of this wave
+                const Split<T> vt[2] = {load_split(Vtb, 0), load_split(Vtb, 1)};
+                v8 kt[TPW][2];
 #pragma unroll
-            for (int tp = 0; tp < 2; ++tp)
-                if (tp < ntp) vn[tp] = load_split(Vb, tp);
-            const float a_last = L > 0 ? Rs[buf][L - 1].x : 1.f;
+                for (int t = 0; t < TPW; ++t) {
+                    const int db = min(w * TPW + t, NDB - 1);
+                    const int col = (db >> 1) * 32 + 4 * (2 * (lane & 3) + (db & 1));   // permuted column slot
+#pragma unroll
+                    for (int tp = 0; tp < 2; ++tp) {
+                        const int row = tp * 32 + 4 * qd + ((lane & 15) >> 2);
+                        s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&Kb[row * KP + col]));
+                        s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&Kb[(row + 16) * KP + col]));
+                        kt[t][tp] = concat<T>(__builtin_bit_cast(v4, lo), __builtin_bit_cast(v4, hi));
+                    }
+                }
+                const float a_last = Rs[buf][L - 1].x;
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) {
+                    const int db = w * TPW + t;
+                    if (db < NDB) {
+                        f32x4 acc = S[t] * a_last, lo = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int tp = 0; tp < 2; ++tp) {
+                            acc = mfma_pair(kt[t][tp], vt[tp].hi, acc);
+                            lo = mfma_pair(kt[t][tp], vt[tp].lo, lo);
+                        }
+                        S[t] = acc + lo;
+                    }
+                }
+                publish_state();
+                __syncthreads();                                                    // barrier 3
+            }
+        }
+        if (ST) {
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
                 const int db = w * TPW + t;
                 if (db < NDB) {
-                    f32x4 acc = S[t] * a_last, lo = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int tp = 0; tp < 2; ++tp) {
-                        acc = mfma_pair(kt[t][tp], vt[tp].hi, acc);
-                        lo = mfma_pair(kt[t][tp], vt[tp].lo, lo);
-                    }
-                    S[t] = acc + lo;
+                    for (int j = 0; j < 4; ++j)
+                        ST[sbase + (int64_t)(db * 16 + 4 * qd + j) * DV + nb * 16 + r] = S[t][j];
                 }
             }
-
-            // ---- hand over the new state and the next chunk's tiles
-            publish_state();
-            if (more) {
-                stage(nxt, buf ^ 1);
-                cur_L = nxt.L;
-                cur_s = nxt.s;
-            }
-
-            // ---- O = scale [exp(G) Q S_in + (Q K^T (.) D) V_new] for rows 16w..16w+15
-            f32x4 out, ol = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) out[j] = rrow[j].x * (Qh[j] + Ql[j]);
-#pragma unroll
-            for (int tp = 0; tp < 2; ++tp) {
-                if (tp < ntp) {
-                    const Split<T> pa = split_acc_pair<T>(pt[2 * tp], pt[2 * tp + 1]);
-                    out = mfma_pair(pa.hi, vn[tp].hi, out);
-                    ol = mfma_pair(pa.lo, vn[tp].hi, ol);
-                    ol = mfma_pair(pa.hi, vn[tp].lo, ol);
-                }
-            }
-            const auto ro = rsrc(o, (s * Nv + h) * DV + nb * 16, ob,
-                                 L > 0 ? (uint32_t)(((L - 1) * Nv * DV + 16) * ob) : 0u);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {               // rows past the chunk end fall outside ro
-                const float val = scale * (out[j] + ol[j]);
-                if (out_f32) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), ro, o_off[j], 0, 0);
-                else __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, to_t<T>(val)), ro,
-                                                           o_off[j], 0, 0);
-            }
-            __syncthreads();
         }
+        return;
     }
-    if (ST) {
+
+    // ============================================================ output waves
+    if (c0 >= c1) return;
+    const int w = wv - 4;
+    const int ot = tid - 256;                      // thread index within the output waves
+    const int ntp = (w >> 1) + 1;
+    const int ob = out_f32 ? 4 : 2;
+    int kq_off[LPT], kq_dst[LPT];
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            const int db = w * TPW + t;
-            if (db < NDB) {
+    for (int i = 0; i < LPT; ++i) {
+        const int idx = ot + 256 * i, row = idx / NSEG, seg = idx % NSEG;
+        kq_off[i] = (row * Nk * DK + seg * 8) * 2;
+        const int s4i = seg & 3;                   // 8 columns = two 4-column groups of a 32-block
+        kq_dst[i] = row * KP + (seg >> 2) * 32 + 4 * (s4i < 2 ? 4 * s4i : 4 * (s4i - 2) + 1);
+    }
+    const int v_off = ((ot >> 2) * Nv * DV + (ot & 3) * 4) * 2;
+    int o_off[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) ST[sbase + (int64_t)(db * 16 + 4 * qd + j) * DV + nb * 16 + r] = S[t][j];
+    for (int j = 0; j < 4; ++j) o_off[j] = ((w * 16 + 4 * qd + j) * Nv * DV + r) * ob;
+
+    struct Fetch {
+        i4 kr[LPT], qr[LPT], tr[TLD], rr;
+        i2 vr;
+        int g;
+    };
+    auto fetch = [&](int c, Fetch& F) {
+        const int64_t s = chunk_s(c);
+        const int L = chunk_L(c);
+        const uint32_t kq_bytes = (uint32_t)((L - 1) * Nk * DK + DK) * 2u;
+        const auto rk = rsrc(k, (s * Nk + kh) * DK, 2, kq_bytes);
+        const auto rq = rsrc(q, (s * Nk + kh) * DK, 2, kq_bytes);
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            F.kr[i] = __builtin_bit_cast(i4, __builtin_amdgcn_raw_buffer_load_b128(rk, kq_off[i], 0, 0));
+            F.qr[i] = __builtin_bit_cast(i4, __builtin_amdgcn_raw_buffer_load_b128(rq, kq_off[i], 0, 0));
+        }
+        const auto rt = rsrc(Tf, ((int64_t)c * Nv + h) * TFRAG, 2, TFRAG * 2);
+#pragma unroll
+        for (int i = 0; i < TLD; ++i)
+            F.tr[i] = __builtin_bit_cast(i4, __builtin_amdgcn_raw_buffer_load_b128(rt, (ot + 256 * i) * 16, 0, 0));
+        const auto rv = rsrc(v, (s * Nv + h) * DV + nb * 16, 2, (uint32_t)((L - 1) * Nv * DV + 16) * 2u);
+        F.vr = __builtin_bit_cast(i2, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, 0, 0));
+        if (w == 0) {
+            const auto rr = rsrc(R, ((int64_t)c * Nv + h) * kChunk, 16, kChunk * 16);
+            F.rr = __builtin_bit_cast(i4, __builtin_amdgcn_raw_buffer_load_b128(rr, lane * 16, 0, 0));
+        } else if (w == 1) {
+            const auto rg = rsrc(Gc, ((int64_t)c * Nv + h) * kChunk, 4, kChunk * 4);
+            F.g = __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(rg, lane * 4, 0, 0));
+        }
+    };
+    auto stage = [&](const Fetch& F, int buf) {
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            const i2 k0 = {F.kr[i].x, F.kr[i].y}, k1 = {F.kr[i].z, F.kr[i].w};
+            const i2 q0 = {F.qr[i].x, F.qr[i].y}, q1 = {F.qr[i].z, F.qr[i].w};
+            *reinterpret_cast<i2*>(&Ks[buf][kq_dst[i]]) = k0;
+            *reinterpret_cast<i2*>(&Ks[buf][kq_dst[i] + 8]) = k1;
+            *reinterpret_cast<i2*>(&Qs[buf][kq_dst[i]]) = q0;
+            *reinterpret_cast<i2*>(&Qs[buf][kq_dst[i] + 8]) = q1;
+        }
+#pragma unroll
+        for (int i = 0; i < TLD; ++i) *reinterpret_cast<i4*>(&Tb[buf][(ot + 256 * i) * 8]) = F.tr[i];
+        *reinterpret_cast<i2*>(&Vs[buf][ot * 4]) = F.vr;
+        if (w == 0) Rs[buf][lane] = __builtin_bit_cast(f32x4, F.rr);
+        else if (w == 1) Gs[buf][lane] = __builtin_bit_cast(float, F.g);
+    };
+
+    Fetch F;
+    fetch(c0, F);
+    stage(F, 0);
+    if (c0 + 1 < c1) fetch(c0 + 1, F);
+    __syncthreads();
+    for (int c = c0; c < c1; ++c) {
+        const int buf = (c - c0) & 1;
+        const int64_t s = chunk_s(c);
+        const int L = chunk_L(c);
+        const T* Kb = Ks[buf];
+        const T* Qb = Qs[buf];
+
+        // ---- A: score block of positions 16w..16w+15 (transposed tiles K_j Q_i^T), decayed
+        v8 qa[NKP];
+#pragma unroll
+        for (int kp = 0; kp < NKP; ++kp) qa[kp] = tile_pair(Qb, w * 16 + r, kp);
+        f32x4 pd = {0.f, 0.f, 0.f, 0.f}, po[3];
+#pragma unroll
+        for (int tj = 0; tj < 3; ++tj) po[tj] = pd;
+#pragma unroll
+        for (int kp = 0; kp < NKP; ++kp) pd = mfma_pair(tile_pair(Kb, w * 16 + r, kp), qa[kp], pd);
+#pragma unroll
+        for (int tj = 0; tj < 3; ++tj) {
+            if (tj < w) {
+#pragma unroll
+                for (int kp = 0; kp < NKP; ++kp) po[tj] = mfma_pair(tile_pair(Kb, tj * 16 + r, kp), qa[kp], po[tj]);
             }
         }
+        const float gi = Gs[buf][w * 16 + r];
+        const float rzi = Rs[buf][w * 16 + r].z;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {                 // diagonal block: exp(G_i - G_j) for j <= i
+            const float d = __expf(gi - Gs[buf][w * 16 + 4 * qd + jj]);
+            pd[jj] = 4 * qd + jj <= r ? pd[jj] * d : 0.f;
+        }
+        float gam = rzi;                                 // earlier blocks: R.z_i (block ends between) R.w_j
+#pragma unroll
+        for (int tj = 2; tj >= 0; --tj) {
+            if (tj < w) {
+                if (tj + 1 < w) gam *= Rs[buf][16 * (tj + 1) + 15].z;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) po[tj][jj] *= gam * Rs[buf][tj * 16 + 4 * qd + jj].w;
+            }
+        }
+        const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+        Split<T> pa[2];
+        if (w == 0) pa[0] = split_acc_pair<T>(pd, zero4);
+        else if (w == 1) pa[0] = split_acc_pair<T>(po[0], pd);
+        else {
+            pa[0] = split_acc_pair<T>(po[0], po[1]);
+            pa[1] = w == 2 ? split_acc_pair<T>(pd, zero4) : split_acc_pair<T>(po[2], pd);
+        }
+        __syncthreads();                                                            // barrier 1
+
+        // ---- B: chunk c+1 into the other LDS half; fetch chunk c+2
+        if (c + 1 < c1) {
+            stage(F, buf ^ 1);
+            if (c + 2 < c1) fetch(c + 2, F);
+        }
+        __syncthreads();                                                            // barrier 2
+
+        // ---- C: O = scale [exp(G) Q S_in + P V_new] for positions 16w..16w+15
+        const f32x4 qs = QSx[w][lane];
+        f32x4 out, ol = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[j] = Rs[buf][w * 16 + 4 * qd + j].x * qs[j];
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+            if (tp < ntp) {
+                const Split<T> vn = load_split(Vb, tp);
+                out = mfma_pair(pa[tp].hi, vn.hi, out);
+                ol = mfma_pair(pa[tp].lo, vn.hi, ol);
+                ol = mfma_pair(pa[tp].hi, vn.lo, ol);
+            }
+        }
+        const auto ro = rsrc(o, (s * Nv + h) * DV + nb * 16, ob, (uint32_t)(((L - 1) * Nv * DV + 16) * ob));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {                   // rows past the chunk end fall outside ro
+            const float val = scale * (out[j] + ol[j]);
+            if (out_f32) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), ro, o_off[j], 0, 0);
+            else __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, to_t<T>(val)), ro,
+                                                       o_off[j], 0, 0);
+        }
+        __syncthreads();                                                            // barrier 3
     }
 }
 
@@ -1057,7 +1071,7 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
     if (a.N > 0) {
         if constexpr (kFused) {
             if (fused) {
-                k_state_output<DK, DV><<<dim3(a.N, a.Nv, DV / 16), 256, 0, st>>>(
+                k_state_output<DK, DV><<<dim3(a.N, a.Nv, DV / 16), 512, 0, st>>>(
                     (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const float*)a.Gc, (const f32x4*)a.R,
                     (const bf16*)a.Tf, a.S0,
                     a.chunk_start, a.chunk_len, a.seq_first, a.Nk, a.Nv, a.scale, a.out_f32, a.o, a.ST);
