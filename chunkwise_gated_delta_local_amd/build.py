@@ -5,6 +5,7 @@ off (``-Xclang -target-feature -Xclang -packed-fp32-ops``).
 """
 from __future__ import annotations
 
+import ctypes
 import os
 import subprocess
 import sys
@@ -43,6 +44,11 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join("%s:\n%s" % f for f in failed))
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
     subprocess.check_call([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
+    try:                                   # every symbol must resolve (a missing kernel stub shows here)
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW)
+    except OSError as e:
+        os.unlink(tmp)
+        raise RuntimeError("built library does not load: %s" % e)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

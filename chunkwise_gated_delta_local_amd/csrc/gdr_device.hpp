@@ -240,6 +240,24 @@ __device__ __forceinline__ void store_pair_half_f32(float* base, int lane, int h
     *reinterpret_cast<f32x4*>(base + lane * 8 + 4 * half) = x;
 }
 
+// Global -> LDS copies without registers: lane l's 16 (or 4) bytes at byte
+// offset voffset of the buffer land at lds_dst + 16 l (or 4 l); lds_dst is
+// wave-uniform. Completion is tracked by the issuing wave's vector memory counter.
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rs, const void* lds_dst, int voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_dst, 16, voffset, 0, 0, 0);
+}
+__device__ __forceinline__ void buffer_to_lds4(__amdgpu_buffer_rsrc_t rs, const void* lds_dst, int voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_dst, 4, voffset, 0, 0, 0);
+}
+
+// Workgroup barrier for LDS traffic: this wave's LDS operations complete, then
+// all waves of the workgroup meet. Unlike __syncthreads() it does not wait for
+// the wave's outstanding global loads, stores or global-to-LDS copies; a copy
+// whose data the other waves read after the barrier needs an explicit
+// vector-memory wait first (wait_vmem()).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ float load_beta(const void* beta, int64_t idx, int beta_f32) {
     return beta_f32 ? reinterpret_cast<const float*>(beta)[idx]
                     : (float)reinterpret_cast<const bf16*>(beta)[idx];

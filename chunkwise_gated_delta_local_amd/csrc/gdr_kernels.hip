@@ -658,21 +658,28 @@ __global__ __launch_bounds__(256) void k_output(const T* __restrict__ q, const T
 //                        V_new, and dk tiles of S for the update. This is the
 //                        sequential chain.
 //   output waves (4..7): wave 4+w computes the score block of positions
-//                        16w..16w+15 and their output, and moves the next
-//                        chunk's tiles from global memory into LDS.
+//                        16w..16w+15 and their output, and copies the next
+//                        chunk's tiles from global memory straight into LDS.
 // Each chunk step has three phases separated by workgroup barriers:
 //   A  state: S_in (split) from LDS, Y, Z -> LDS      output: scores + decay
-//   B  state: Q S_in, V_new = T Z -> LDS               output: stage chunk c+1,
-//                                                       fetch chunk c+2
-//   C  state: S update, S_out (split) -> LDS           output: O -> global
-// K and Q tiles sit in LDS with the columns of every 32-block permuted so that
-// a pair fragment is one 16-byte read; K^T operands come from the same tile
-// through transposing LDS reads. Rows past the chunk end are zero (bounds-
-// checked buffer loads). The decay exp(G_i - G_j) of the score block is a
+//   B  state: Q S_in, V_new = T Z -> LDS               output: -
+//   C  state: S update, S_out (split) -> LDS           output: O
+// and the output waves spread the copies of chunk c+1 over all three phases
+// (16-byte buffer loads to LDS, rows past the chunk end read as zero). K and Q
+// tiles are held fragment-major: one 1 KB block per (16 rows, 32 columns),
+// lane l's 16 bytes at a swizzled slot, so that every matrix-core operand is
+// one 16-byte LDS read; K^T operands come from the same blocks through
+// transposing LDS reads. The decay exp(G_i - G_j) of the score block is a
 // product of the precomputed factors R outside the diagonal 16x16 blocks,
 // where it is evaluated directly.
+//
+// Contraction orders: products over dk (K S, Q S, K Q^T) take the 32 indices
+// of a block as 8 qd + e for lane quarter qd and element e (so that a fragment
+// is 16 contiguous bytes of a row); products over positions (T Z, K^T V,
+// P V_new) use the stacked-accumulator order of gdr_device.hpp. The state is
+// written to LDS in the first order by the wave that updates it.
 template <int DK, int DV>
-__global__ __launch_bounds__(512) void k_state_output(const bf16* __restrict__ q, const bf16* __restrict__ k,
+__global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                        const bf16* __restrict__ v, const float* __restrict__ Gc,
                                                        const f32x4* __restrict__ R, const bf16* __restrict__ Tf,
                                                        const float* __restrict__ S0,
@@ -685,27 +692,27 @@ __global__ __launch_bounds__(512) void k_state_output(const bf16* __restrict__ q
     typedef Vec<T>::v8 v8;
     typedef Vec<T>::v4 v4;
     typedef short s4 __attribute__((ext_vector_type(4)));
-    typedef int i4 __attribute__((ext_vector_type(4)));
-    typedef int i2 __attribute__((ext_vector_type(2)));
     typedef s4 __attribute__((address_space(3))) * lds_s4;
     constexpr int NKP = DK / 32, NDB = DK / 16;
     constexpr int TPW = (NDB + 3) / 4;          // state tiles owned per state wave
-    constexpr int KP = DK + 8;                  // LDS row pitch of the K and Q tiles (elements)
-    constexpr int NSEG = DK / 8;                // 16-byte segments per row
-    constexpr int LPT = kChunk * NSEG / 256;    // row segments fetched per output-wave thread
+    constexpr int FRAG = 512;                   // elements of one fragment block (64 lanes x 8)
     constexpr int TFRAG = kTPairs * 2 * 512;    // T elements per (chunk, head)
-    constexpr int TLD = TFRAG * 2 / 16 / 256;   // 16-byte T loads per output-wave thread
+    constexpr int NTCP = TFRAG * 2 / 1024;      // 1 KB copies of T per chunk
+    constexpr int MCP = 2 * NKP + 4;            // copies per output wave per chunk
     constexpr int RSRC = 0x00020000;            // buffer descriptor word 3 (raw 32-bit access)
-    __shared__ __attribute__((aligned(16))) T Ks[2][kChunk * KP];
-    __shared__ __attribute__((aligned(16))) T Qs[2][kChunk * KP];
-    __shared__ __attribute__((aligned(16))) T Tb[2][TFRAG];
-    __shared__ __attribute__((aligned(16))) T Vs[2][kChunk * 16];
-    __shared__ __attribute__((aligned(16))) f32x4 Rs[2][kChunk];
-    __shared__ float Gs[2][kChunk];
-    __shared__ __attribute__((aligned(16))) T Sb[NKP][2][512];
-    __shared__ __attribute__((aligned(16))) T Zb[2][2][512];
-    __shared__ __attribute__((aligned(16))) T Vb[2][2][512];
-    __shared__ __attribute__((aligned(16))) T Vtb[2][2][512];
+    static_assert(8 * NKP + NTCP + 4 == 4 * MCP, "copy schedule");
+    // chunk tiles, double-buffered; each half is its own array so that the
+    // compiler can tell reads of one half from copies into the other
+    __shared__ __attribute__((aligned(16))) T Ks0[4 * NKP * FRAG], Ks1[4 * NKP * FRAG];
+    __shared__ __attribute__((aligned(16))) T Qs0[4 * NKP * FRAG], Qs1[4 * NKP * FRAG];
+    __shared__ __attribute__((aligned(16))) T Tb0[TFRAG], Tb1[TFRAG];
+    __shared__ __attribute__((aligned(16))) T Vs0[kChunk * 16], Vs1[kChunk * 16];
+    __shared__ __attribute__((aligned(16))) f32x4 Rs0[kChunk], Rs1[kChunk];
+    __shared__ __attribute__((aligned(16))) float Gs0[kChunk], Gs1[kChunk];
+    __shared__ __attribute__((aligned(16))) T Sb[NKP][2][FRAG];
+    __shared__ __attribute__((aligned(16))) T Zb[2][2][FRAG];
+    __shared__ __attribute__((aligned(16))) T Vb[2][2][FRAG];
+    __shared__ __attribute__((aligned(16))) T Vtb[2][2][FRAG];
     __shared__ __attribute__((aligned(16))) f32x4 QSx[4][64];
 
     const int n = blockIdx.x, h = blockIdx.y, nb = blockIdx.z;
@@ -724,7 +731,12 @@ __global__ __launch_bounds__(512) void k_state_output(const bf16* __restrict__ q
         return __builtin_amdgcn_make_buffer_rsrc(
             const_cast<char*>(reinterpret_cast<const char*>(base)) + elem_off * elem_bytes, (short)0, (int)bytes, RSRC);
     };
-    auto store_split_half = [&](T (*buf)[2][512], int tp, int half, const f32x4& x) {
+    // slot of lane (row rr, quarter qq) inside a K/Q fragment block (XOR swizzle by quarter parity)
+    auto slot = [](int rr, int qq) { return 16 * qq + (rr ^ (4 * (qq & 1))); };
+    auto frag = [&](const T* tile, int tb, int kp) {
+        return *reinterpret_cast<const v8*>(&tile[(tb * NKP + kp) * FRAG + slot(r, qd) * 8]);
+    };
+    auto store_split_half = [&](T (*buf)[2][FRAG], int tp, int half, const f32x4& x) {
         float xx[8] = {x[0], x[1], x[2], x[3], 0.f, 0.f, 0.f, 0.f};
         const Split<T> sp = split8<T>(xx);
         v4 hi4 = {sp.hi[0], sp.hi[1], sp.hi[2], sp.hi[3]};
@@ -732,15 +744,11 @@ __global__ __launch_bounds__(512) void k_state_output(const bf16* __restrict__ q
         *reinterpret_cast<v4*>(&buf[tp][0][lane * 8 + 4 * half]) = hi4;
         *reinterpret_cast<v4*>(&buf[tp][1][lane * 8 + 4 * half]) = lo4;
     };
-    auto load_split = [&](T (*buf)[2][512], int tp) {
+    auto load_split = [&](T (*buf)[2][FRAG], int tp) {
         Split<T> sp;
         sp.hi = *reinterpret_cast<const v8*>(&buf[tp][0][lane * 8]);
         sp.lo = *reinterpret_cast<const v8*>(&buf[tp][1][lane * 8]);
         return sp;
-    };
-    // pair fragment of row `row` of a K or Q tile, contraction block kp (one 16-byte read)
-    auto tile_pair = [&](const T* tile, int row, int kp) {
-        return *reinterpret_cast<const v8*>(&tile[row * KP + kp * 32 + 8 * qd]);
     };
     const int64_t sbase = ((int64_t)n * Nv + h) * DK * DV;
 
@@ -757,29 +765,73 @@ __global__ __launch_bounds__(512) void k_state_output(const bf16* __restrict__ q
             for (int j = 0; j < 4; ++j)
                 S[t][j] = (db < NDB && S0) ? S0[sbase + (int64_t)(db * 16 + 4 * qd + j) * DV + nb * 16 + r] : 0.f;
         }
+        // S tile db (rows 16 db + 4 qd + j of this lane's column r) -> B fragments of
+        // contraction block db / 2 in the 8 qd + e order
         auto publish_state = [&]() {
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
                 const int db = w * TPW + t;
-                if (db < NDB) store_split_half(Sb, db >> 1, db & 1, S[t]);
+                if (db < NDB) {
+                    float xx[8] = {S[t][0], S[t][1], S[t][2], S[t][3], 0.f, 0.f, 0.f, 0.f};
+                    const Split<T> sp = split8<T>(xx);
+                    v4 hi4 = {sp.hi[0], sp.hi[1], sp.hi[2], sp.hi[3]};
+                    v4 lo4 = {sp.lo[0], sp.lo[1], sp.lo[2], sp.lo[3]};
+                    const int dst = (16 * (2 * (db & 1) + (qd >> 1)) + r) * 8 + 4 * (qd & 1);
+                    *reinterpret_cast<v4*>(&Sb[db >> 1][0][dst]) = hi4;
+                    *reinterpret_cast<v4*>(&Sb[db >> 1][1][dst]) = lo4;
+                }
             }
+        };
+        // transposed K operand: K^T rows 16 db.., positions of pair tp (stacked order)
+        auto kt_frag = [&](const T* Kb, int db, int tp) {
+            const int j = lane & 15;
+            const int qq = 2 * (db & 1) + ((j & 3) >> 1);
+            const int e0 = 4 * (j & 1);
+            v4 part[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int rr = 4 * qd + (j >> 2);             // row inside block 2 tp + hh
+                const T* p = &Kb[((2 * tp + hh) * NKP + (db >> 1)) * FRAG + slot(rr, qq) * 8 + e0];
+                part[hh] = __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)p));
+            }
+            return concat<T>(part[0], part[1]);
         };
         if (c0 < c1) {
             publish_state();
-            __syncthreads();
+            lds_barrier();
             for (int c = c0; c < c1; ++c) {
-                const int buf = (c - c0) & 1;
+                const bool odd = (c - c0) & 1;
                 const int L = chunk_L(c);
-                const T* Kb = Ks[buf];
-                const T* Qb = Qs[buf];
+                const T* Kb = odd ? Ks1 : Ks0;
+                const T* Qb = odd ? Qs1 : Qs0;
+                const T* Tbb = odd ? Tb1 : Tb0;
+                const T* Vsb = odd ? Vs1 : Vs0;
+                const f32x4* Rsb = odd ? Rs1 : Rs0;
 
                 // ---- A: Y = K S_in (hi and lo passes), Z = V - exp(G) Y -> LDS
                 Split<T> BS[NKP];
-                v8 ka[NKP];
+                v8 ka[NKP], qa[NKP];
 #pragma unroll
                 for (int kp = 0; kp < NKP; ++kp) {
                     BS[kp] = load_split(Sb, kp);
-                    ka[kp] = tile_pair(Kb, w * 16 + r, kp);
+                    ka[kp] = frag(Kb, w, kp);
+                }
+                f32x4 rrow[4];
+                float vrow[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    rrow[j] = Rsb[w * 16 + 4 * qd + j];
+                    vrow[j] = to_f(Vsb[(w * 16 + 4 * qd + j) * 16 + r]);
+                }
+                Split<T> tf[2];
+#pragma unroll
+                for (int kp = 0; kp < NKP; ++kp) qa[kp] = frag(Qb, w, kp);
+#pragma unroll
+                for (int tp = 0; tp < 2; ++tp) {
+                    if (tp < ntp) {
+                        tf[tp].hi = load_frag<T>(&Tbb[(pbase + tp) * 2 * FRAG], lane);
+                        tf[tp].lo = load_frag<T>(&Tbb[(pbase + tp) * 2 * FRAG + FRAG], lane);
+                    }
                 }
                 f32x4 Yh = {0.f, 0.f, 0.f, 0.f}, Yl = Yh;
 #pragma unroll
@@ -787,32 +839,24 @@ __global__ __launch_bounds__(512) void k_state_output(const bf16* __restrict__ q
                     Yh = mfma_pair(ka[kp], BS[kp].hi, Yh);
                     Yl = mfma_pair(ka[kp], BS[kp].lo, Yl);
                 }
-                f32x4 rrow[4];
-                float vrow[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    rrow[j] = Rs[buf][w * 16 + 4 * qd + j];
-                    vrow[j] = to_f(Vs[buf][(w * 16 + 4 * qd + j) * 16 + r]);
-                }
                 f32x4 Z;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) Z[j] = vrow[j] - rrow[j].x * (Yh[j] + Yl[j]);
                 store_split_half(Zb, w >> 1, w & 1, Z);
-                __syncthreads();                                                    // barrier 1
+                lds_barrier();                                                    // barrier 1
 
                 // ---- B: Q S_in for the output waves; V_new = T Z -> LDS
-                Split<T> tf[2], zf[2];
+                Split<T> zf[2];
 #pragma unroll
-                for (int tp = 0; tp < 2; ++tp) {
-                    if (tp < ntp) {
-                        tf[tp].hi = load_frag<T>(&Tb[buf][(pbase + tp) * 2 * 512], lane);
-                        tf[tp].lo = load_frag<T>(&Tb[buf][(pbase + tp) * 2 * 512 + 512], lane);
-                        zf[tp] = load_split(Zb, tp);
-                    }
+                for (int tp = 0; tp < 2; ++tp)
+                    if (tp < ntp) zf[tp] = load_split(Zb, tp);
+                v8 kt[TPW][2];
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) {
+                    const int db = min(w * TPW + t, NDB - 1);
+#pragma unroll
+                    for (int tp = 0; tp < 2; ++tp) kt[t][tp] = kt_frag(Kb, db, tp);
                 }
-                v8 qa[NKP];
-#pragma unroll
-                for (int kp = 0; kp < NKP; ++kp) qa[kp] = tile_pair(Qb, w * 16 + r, kp);
                 f32x4 Qh = {0.f, 0.f, 0.f, 0.f}, Ql = Qh;
 #pragma unroll
                 for (int kp = 0; kp < NKP; ++kp) {
@@ -837,24 +881,11 @@ __global__ __launch_bounds__(512) void k_state_output(const bf16* __restrict__ q
                 store_split_half(Vtb, w >> 1, w & 1, VD);
                 store_split_half(Vb, w >> 1, w & 1, VN);
                 QSx[w][lane] = Qh + Ql;
-                __syncthreads();                                                    // barrier 2
+                lds_barrier();                                                    // barrier 2
 
                 // ---- C: S_out = exp(G_last) S_in + K^T V_decayed for the dk tiles of this wave
                 const Split<T> vt[2] = {load_split(Vtb, 0), load_split(Vtb, 1)};
-                v8 kt[TPW][2];
-#pragma unroll
-                for (int t = 0; t < TPW; ++t) {
-                    const int db = min(w * TPW + t, NDB - 1);
-                    const int col = (db >> 1) * 32 + 4 * (2 * (lane & 3) + (db & 1));   // permuted column slot
-#pragma unroll
-                    for (int tp = 0; tp < 2; ++tp) {
-                        const int row = tp * 32 + 4 * qd + ((lane & 15) >> 2);
-                        s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&Kb[row * KP + col]));
-                        s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&Kb[(row + 16) * KP + col]));
-                        kt[t][tp] = concat<T>(__builtin_bit_cast(v4, lo), __builtin_bit_cast(v4, hi));
-                    }
-                }
-                const float a_last = Rs[buf][L - 1].x;
+                const float a_last = Rsb[L - 1].x;
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) {
                     const int db = w * TPW + t;
@@ -869,7 +900,7 @@ __global__ __launch_bounds__(512) void k_state_output(const bf16* __restrict__ q
                     }
                 }
                 publish_state();
-                __syncthreads();                                                    // barrier 3
+                lds_barrier();                                                    // barrier 3
             }
         }
         if (ST) {
@@ -886,138 +917,128 @@ __global__ __launch_bounds__(512) void k_state_output(const bf16* __restrict__ q
         return;
     }
 
-    // ============================================================ output waves
     if (c0 >= c1) return;
+    if (wv >= 8) {
+        // ======================================================== copy waves
+        // Wave 8+w issues copies u = w + 4 m (m < MCP) of a chunk's list (K blocks,
+        // Q blocks, T pieces, then the V halves, R and G) into one LDS half, all at
+        // the start of a step, and waits for them before the step's last barrier.
+        const int w = wv - 8;
+        const int kq_lane = (((lane & 15) ^ (4 * ((lane >> 4) & 1))) * Nk * DK + 8 * (lane >> 4)) * 2;
+        auto copy_chunk = [&](int c, bool odd) {
+            T* Kd = odd ? Ks1 : Ks0;
+            T* Qd = odd ? Qs1 : Qs0;
+            T* Td = odd ? Tb1 : Tb0;
+            T* Vd = odd ? Vs1 : Vs0;
+            f32x4* Rd = odd ? Rs1 : Rs0;
+            float* Gd = odd ? Gs1 : Gs0;
+            const int64_t s = chunk_s(c);
+            const int L = chunk_L(c);
+            const uint32_t kq_bytes = (uint32_t)((L - 1) * Nk * DK + DK) * 2u;
+            const auto rk = rsrc(k, (s * Nk + kh) * DK, 2, kq_bytes);
+            const auto rq = rsrc(q, (s * Nk + kh) * DK, 2, kq_bytes);
+            const auto rt = rsrc(Tf, ((int64_t)c * Nv + h) * TFRAG, 2, TFRAG * 2);
+#pragma unroll
+            for (int m = 0; m < MCP; ++m) {
+                const int u = w + 4 * m;
+                if (m < NKP) {                               // K block (tb, kp)
+                    const int tb = u / NKP, kp = u % NKP;
+                    buffer_to_lds16(rk, Kd + u * FRAG, kq_lane + (16 * tb * Nk * DK + 32 * kp) * 2);
+                } else if (m < 2 * NKP) {                    // Q block
+                    const int f = u - 4 * NKP, tb = f / NKP, kp = f % NKP;
+                    buffer_to_lds16(rq, Qd + f * FRAG, kq_lane + (16 * tb * Nk * DK + 32 * kp) * 2);
+                } else if (m < 2 * NKP + NTCP / 4) {         // T piece
+                    const int p = u - 8 * NKP;
+                    buffer_to_lds16(rt, Td + p * FRAG, (p * 64 + lane) * 16);
+                } else if (w < 2) {                          // V rows 32 w .. 32 w + 31 (16 columns)
+                    buffer_to_lds16(rsrc(v, (s * Nv + h) * DV + nb * 16, 2, (uint32_t)((L - 1) * Nv * DV + 16) * 2u),
+                                    Vd + w * 512, ((32 * w + (lane >> 1)) * Nv * DV + 8 * (lane & 1)) * 2);
+                } else if (w == 2) {                         // R
+                    buffer_to_lds16(rsrc(R, ((int64_t)c * Nv + h) * kChunk, 16, kChunk * 16), Rd, lane * 16);
+                } else {                                     // G
+                    buffer_to_lds4(rsrc(Gc, ((int64_t)c * Nv + h) * kChunk, 4, kChunk * 4), Gd, lane * 4);
+                }
+            }
+        };
+        copy_chunk(c0, false);
+        wait_vmem();
+        lds_barrier();
+        for (int c = c0; c < c1; ++c) {
+            if (c + 1 < c1) copy_chunk(c + 1, !((c - c0) & 1));
+            lds_barrier();                                                          // barrier 1
+            lds_barrier();                                                          // barrier 2
+            wait_vmem();                 // this wave's copies of chunk c+1 have landed
+            lds_barrier();                                                          // barrier 3
+        }
+        return;
+    }
+
+    // ============================================================ output waves
     const int w = wv - 4;
-    const int ot = tid - 256;                      // thread index within the output waves
     const int ntp = (w >> 1) + 1;
     const int ob = out_f32 ? 4 : 2;
-    int kq_off[LPT], kq_dst[LPT];
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-        const int idx = ot + 256 * i, row = idx / NSEG, seg = idx % NSEG;
-        kq_off[i] = (row * Nk * DK + seg * 8) * 2;
-        const int s4i = seg & 3;                   // 8 columns = two 4-column groups of a 32-block
-        kq_dst[i] = row * KP + (seg >> 2) * 32 + 4 * (s4i < 2 ? 4 * s4i : 4 * (s4i - 2) + 1);
-    }
-    const int v_off = ((ot >> 2) * Nv * DV + (ot & 3) * 4) * 2;
     int o_off[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) o_off[j] = ((w * 16 + 4 * qd + j) * Nv * DV + r) * ob;
-
-    struct Fetch {
-        i4 kr[LPT], qr[LPT], tr[TLD], rr;
-        i2 vr;
-        int g;
-    };
-    auto fetch = [&](int c, Fetch& F) {
-        const int64_t s = chunk_s(c);
-        const int L = chunk_L(c);
-        const uint32_t kq_bytes = (uint32_t)((L - 1) * Nk * DK + DK) * 2u;
-        const auto rk = rsrc(k, (s * Nk + kh) * DK, 2, kq_bytes);
-        const auto rq = rsrc(q, (s * Nk + kh) * DK, 2, kq_bytes);
+    // score block of positions 16 W.. (transposed tiles K_j Q_i^T, j-blocks <= W), decayed
+    Split<T> pa[2];
+    auto scores = [&](auto Wc, const T* Kb, const T* Qb, const float* Gsb, const f32x4* Rsb) {
+        constexpr int W = decltype(Wc)::value;
+        v8 qa[NKP], kb[W + 1][NKP];
 #pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            F.kr[i] = __builtin_bit_cast(i4, __builtin_amdgcn_raw_buffer_load_b128(rk, kq_off[i], 0, 0));
-            F.qr[i] = __builtin_bit_cast(i4, __builtin_amdgcn_raw_buffer_load_b128(rq, kq_off[i], 0, 0));
-        }
-        const auto rt = rsrc(Tf, ((int64_t)c * Nv + h) * TFRAG, 2, TFRAG * 2);
+        for (int kp = 0; kp < NKP; ++kp) qa[kp] = frag(Qb, W, kp);
 #pragma unroll
-        for (int i = 0; i < TLD; ++i)
-            F.tr[i] = __builtin_bit_cast(i4, __builtin_amdgcn_raw_buffer_load_b128(rt, (ot + 256 * i) * 16, 0, 0));
-        const auto rv = rsrc(v, (s * Nv + h) * DV + nb * 16, 2, (uint32_t)((L - 1) * Nv * DV + 16) * 2u);
-        F.vr = __builtin_bit_cast(i2, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, 0, 0));
-        if (w == 0) {
-            const auto rr = rsrc(R, ((int64_t)c * Nv + h) * kChunk, 16, kChunk * 16);
-            F.rr = __builtin_bit_cast(i4, __builtin_amdgcn_raw_buffer_load_b128(rr, lane * 16, 0, 0));
-        } else if (w == 1) {
-            const auto rg = rsrc(Gc, ((int64_t)c * Nv + h) * kChunk, 4, kChunk * 4);
-            F.g = __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(rg, lane * 4, 0, 0));
-        }
-    };
-    auto stage = [&](const Fetch& F, int buf) {
+        for (int tj = 0; tj <= W; ++tj)
 #pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            const i2 k0 = {F.kr[i].x, F.kr[i].y}, k1 = {F.kr[i].z, F.kr[i].w};
-            const i2 q0 = {F.qr[i].x, F.qr[i].y}, q1 = {F.qr[i].z, F.qr[i].w};
-            *reinterpret_cast<i2*>(&Ks[buf][kq_dst[i]]) = k0;
-            *reinterpret_cast<i2*>(&Ks[buf][kq_dst[i] + 8]) = k1;
-            *reinterpret_cast<i2*>(&Qs[buf][kq_dst[i]]) = q0;
-            *reinterpret_cast<i2*>(&Qs[buf][kq_dst[i] + 8]) = q1;
-        }
+            for (int kp = 0; kp < NKP; ++kp) kb[tj][kp] = frag(Kb, tj, kp);
+        f32x4 pt[W + 1];
 #pragma unroll
-        for (int i = 0; i < TLD; ++i) *reinterpret_cast<i4*>(&Tb[buf][(ot + 256 * i) * 8]) = F.tr[i];
-        *reinterpret_cast<i2*>(&Vs[buf][ot * 4]) = F.vr;
-        if (w == 0) Rs[buf][lane] = __builtin_bit_cast(f32x4, F.rr);
-        else if (w == 1) Gs[buf][lane] = __builtin_bit_cast(float, F.g);
-    };
-
-    Fetch F;
-    fetch(c0, F);
-    stage(F, 0);
-    if (c0 + 1 < c1) fetch(c0 + 1, F);
-    __syncthreads();
-    for (int c = c0; c < c1; ++c) {
-        const int buf = (c - c0) & 1;
-        const int64_t s = chunk_s(c);
-        const int L = chunk_L(c);
-        const T* Kb = Ks[buf];
-        const T* Qb = Qs[buf];
-
-        // ---- A: score block of positions 16w..16w+15 (transposed tiles K_j Q_i^T), decayed
-        v8 qa[NKP];
+        for (int tj = 0; tj <= W; ++tj) pt[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kp = 0; kp < NKP; ++kp) qa[kp] = tile_pair(Qb, w * 16 + r, kp);
-        f32x4 pd = {0.f, 0.f, 0.f, 0.f}, po[3];
+        for (int kp = 0; kp < NKP; ++kp)
 #pragma unroll
-        for (int tj = 0; tj < 3; ++tj) po[tj] = pd;
-#pragma unroll
-        for (int kp = 0; kp < NKP; ++kp) pd = mfma_pair(tile_pair(Kb, w * 16 + r, kp), qa[kp], pd);
-#pragma unroll
-        for (int tj = 0; tj < 3; ++tj) {
-            if (tj < w) {
-#pragma unroll
-                for (int kp = 0; kp < NKP; ++kp) po[tj] = mfma_pair(tile_pair(Kb, tj * 16 + r, kp), qa[kp], po[tj]);
-            }
-        }
-        const float gi = Gs[buf][w * 16 + r];
-        const float rzi = Rs[buf][w * 16 + r].z;
+            for (int tj = 0; tj <= W; ++tj) pt[tj] = mfma_pair(kb[tj][kp], qa[kp], pt[tj]);
+        const float gi = Gsb[W * 16 + r];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {                 // diagonal block: exp(G_i - G_j) for j <= i
-            const float d = __expf(gi - Gs[buf][w * 16 + 4 * qd + jj]);
-            pd[jj] = 4 * qd + jj <= r ? pd[jj] * d : 0.f;
+            const float d = __expf(gi - Gsb[W * 16 + 4 * qd + jj]);
+            pt[W][jj] = 4 * qd + jj <= r ? pt[W][jj] * d : 0.f;
         }
-        float gam = rzi;                                 // earlier blocks: R.z_i (block ends between) R.w_j
+        float gam = Rsb[W * 16 + r].z;                  // earlier blocks: R.z_i (block ends between) R.w_j
 #pragma unroll
-        for (int tj = 2; tj >= 0; --tj) {
-            if (tj < w) {
-                if (tj + 1 < w) gam *= Rs[buf][16 * (tj + 1) + 15].z;
+        for (int tj = W - 1; tj >= 0; --tj) {
+            if (tj + 1 < W) gam *= Rsb[16 * (tj + 1) + 15].z;
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) po[tj][jj] *= gam * Rs[buf][tj * 16 + 4 * qd + jj].w;
-            }
+            for (int jj = 0; jj < 4; ++jj) pt[tj][jj] *= gam * Rsb[tj * 16 + 4 * qd + jj].w;
         }
         const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-        Split<T> pa[2];
-        if (w == 0) pa[0] = split_acc_pair<T>(pd, zero4);
-        else if (w == 1) pa[0] = split_acc_pair<T>(po[0], pd);
-        else {
-            pa[0] = split_acc_pair<T>(po[0], po[1]);
-            pa[1] = w == 2 ? split_acc_pair<T>(pd, zero4) : split_acc_pair<T>(po[2], pd);
-        }
-        __syncthreads();                                                            // barrier 1
+        pa[0] = split_acc_pair<T>(pt[0], W >= 1 ? pt[W >= 1 ? 1 : 0] : zero4);
+        if constexpr (W >= 2) pa[1] = split_acc_pair<T>(pt[2], W >= 3 ? pt[W >= 3 ? 3 : 2] : zero4);
+    };
 
-        // ---- B: chunk c+1 into the other LDS half; fetch chunk c+2
-        if (c + 1 < c1) {
-            stage(F, buf ^ 1);
-            if (c + 2 < c1) fetch(c + 2, F);
+    lds_barrier();
+    for (int c = c0; c < c1; ++c) {
+        const bool odd = (c - c0) & 1;
+        const T* Kb = odd ? Ks1 : Ks0;
+        const T* Qb = odd ? Qs1 : Qs0;
+        const float* Gsb = odd ? Gs1 : Gs0;
+        const f32x4* Rsb = odd ? Rs1 : Rs0;
+
+        // ---- A: score block of positions 16w..16w+15
+        switch (w) {
+            case 0: scores(std::integral_constant<int, 0>{}, Kb, Qb, Gsb, Rsb); break;
+            case 1: scores(std::integral_constant<int, 1>{}, Kb, Qb, Gsb, Rsb); break;
+            case 2: scores(std::integral_constant<int, 2>{}, Kb, Qb, Gsb, Rsb); break;
+            default: scores(std::integral_constant<int, 3>{}, Kb, Qb, Gsb, Rsb); break;
         }
-        __syncthreads();                                                            // barrier 2
+        lds_barrier();                                                              // barrier 1
+        lds_barrier();                                                              // barrier 2
 
         // ---- C: O = scale [exp(G) Q S_in + P V_new] for positions 16w..16w+15
         const f32x4 qs = QSx[w][lane];
         f32x4 out, ol = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) out[j] = Rs[buf][w * 16 + 4 * qd + j].x * qs[j];
+        for (int j = 0; j < 4; ++j) out[j] = Rsb[w * 16 + 4 * qd + j].x * qs[j];
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp) {
             if (tp < ntp) {
@@ -1027,6 +1048,8 @@ __global__ __launch_bounds__(512) void k_state_output(const bf16* __restrict__ q
                 ol = mfma_pair(pa[tp].hi, vn.lo, ol);
             }
         }
+        const int64_t s = chunk_s(c);
+        const int L = chunk_L(c);
         const auto ro = rsrc(o, (s * Nv + h) * DV + nb * 16, ob, (uint32_t)(((L - 1) * Nv * DV + 16) * ob));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {                   // rows past the chunk end fall outside ro
@@ -1035,10 +1058,9 @@ __global__ __launch_bounds__(512) void k_state_output(const bf16* __restrict__ q
             else __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, to_t<T>(val)), ro,
                                                        o_off[j], 0, 0);
         }
-        __syncthreads();                                                            // barrier 3
+        lds_barrier();                                                              // barrier 3
     }
 }
-
 // ============================================================ launchers
 template <typename T, int DK, int DV>
 static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
@@ -1071,7 +1093,7 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
     if (a.N > 0) {
         if constexpr (kFused) {
             if (fused) {
-                k_state_output<DK, DV><<<dim3(a.N, a.Nv, DV / 16), 512, 0, st>>>(
+                k_state_output<DK, DV><<<dim3(a.N, a.Nv, DV / 16), 768, 0, st>>>(
                     (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const float*)a.Gc, (const f32x4*)a.R,
                     (const bf16*)a.Tf, a.S0,
                     a.chunk_start, a.chunk_len, a.seq_first, a.Nk, a.Nv, a.scale, a.out_f32, a.o, a.ST);
