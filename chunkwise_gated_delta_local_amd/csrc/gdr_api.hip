@@ -25,7 +25,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Plan {
     int64_t Ttot;
     int32_t nt_cap;
-    size_t off_seq, off_start, off_len, off_first, off_G, off_R, off_Gc, off_Tf, off_A, off_W, off_U, off_KT, off_H, off_VN;
+    size_t off_seq, off_start, off_len, off_first, off_G, off_R, off_Tf, off_Pf, off_A, off_W, off_U, off_KT, off_H, off_VN;
     size_t sz_Tf, sz_A, sz_W, sz_U, sz_KT, sz_H, sz_VN;   // per chunk except A (whole)
     size_t production;         // bytes gdr_chunk_fwd needs
     size_t reference;          // bytes gdr_chunk_fwd_debug needs (five separate kernels)
@@ -97,10 +97,10 @@ Plan make_plan(const gdr_problem_t* p) {
     pl.off_first = take(((size_t)p->num_seqs + 1) * 4);
     pl.off_G = take(T * Nv * 4);
     const bool bf = p->io_dtype == GDR_BF16;
-    pl.off_R = take(bf ? cap * Nv * 64 * 16 : 0);  // decay factors, chunk-major (float4)
-    pl.off_Gc = take(bf ? cap * Nv * 64 * 4 : 0);  // G, chunk-major
+    pl.off_R = take(bf ? cap * Nv * 64 * 8 : 0);   // decay factors, chunk-major (float2)
     pl.sz_Tf = bf ? Nv * 6 * 2 * 512 * es : 0;   // T = A diag(beta): 6 split pair fragments
     pl.off_Tf = take(cap * pl.sz_Tf);
+    pl.off_Pf = take(cap * pl.sz_Tf);             // score block: same six split pair fragments
     const size_t fused_end = off;
     pl.sz_A = T * Nv * 64 * 4;
     pl.off_A = take(pl.sz_A);
@@ -176,8 +176,8 @@ gdr_status_t run(const gdr_problem_t* p, const void* q, const void* k, const voi
     a.A = w + pl.off_A; a.W = w + pl.off_W; a.U = w + pl.off_U; a.KT = w + pl.off_KT;
     a.H = w + pl.off_H; a.VN = w + pl.off_VN;
     a.Tf = pl.sz_Tf ? w + pl.off_Tf : nullptr;
+    a.Pf = pl.sz_Tf ? w + pl.off_Pf : nullptr;
     a.R = pl.sz_Tf ? w + pl.off_R : nullptr;
-    a.Gc = pl.sz_Tf ? w + pl.off_Gc : nullptr;
     a.reference = reference;
     a.stream = static_cast<hipStream_t>(stream);
 

@@ -38,6 +38,7 @@ namespace gdr {
 
 typedef __bf16 bf16;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 template <typename T> struct Vec;
 template <> struct Vec<bf16> {
@@ -257,6 +258,13 @@ __device__ __forceinline__ void buffer_to_lds4(__amdgpu_buffer_rsrc_t rs, const 
 // vector-memory wait first (wait_vmem()).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector memory operations are outstanding
+// (they complete in issue order, so every older one has finished).
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 __device__ __forceinline__ float load_beta(const void* beta, int64_t idx, int beta_f32) {
     return beta_f32 ? reinterpret_cast<const float*>(beta)[idx]

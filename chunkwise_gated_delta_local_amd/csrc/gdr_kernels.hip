@@ -99,23 +99,18 @@ __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict_
 // GLA notes, forward step 1, chunk-local cumulative log gate). One thread per
 // (chunk, head); neighbouring threads take neighbouring heads so every row
 // access is coalesced. g == NULL writes zeros (ungated rule).
-// When R is given, the decay factors the fused state pass needs are written
-// per token too, all of the form exp(non-positive), so none can overflow
-// (with b = t / 16 the 16-row block of position t in its chunk):
+// When R is given, the two decay factors the fused state pass needs are
+// written per token too:
 //   R.x = exp(G_t)                      decay from the chunk start
 //   R.y = exp(G_last - G_t)             decay to the chunk end
-//   R.z = exp(G_t - G_{16b-1})          decay from the end of the previous block (G_{-1} = 0)
-//   R.w = exp(G_{16b+15} - G_t)         decay to the end of t's block (clamped to the chunk end)
-// so that exp(G_i - G_j) for j in an earlier block than i is a product of
-// R.z_i, R.z at the ends of the blocks in between, and R.w_j.
-// R and Gc are written chunk-major, [chunk][head][64 positions] (positions past
-// the chunk end: G_last for Gc, zeros for R), so the sequential pass reads the
-// factors of one (chunk, head) as one contiguous block.
+// chunk-major, [chunk][head][64 positions] with zeros past the chunk end, so
+// that the sequential pass reads the factors of one (chunk, head) as one
+// contiguous 512-byte block.
 __global__ __launch_bounds__(256) void k_gate_cumsum(const float* __restrict__ g,
                                                       const int32_t* __restrict__ chunk_start,
                                                       const int32_t* __restrict__ chunk_len,
                                                       int32_t NT, int32_t Nv, float* __restrict__ G,
-                                                      f32x4* __restrict__ R, float* __restrict__ Gc) {
+                                                      f32x2* __restrict__ R) {
     const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (p >= (int64_t)NT * Nv) return;
     const int32_t c = (int32_t)(p / Nv), h = (int32_t)(p % Nv);
@@ -133,17 +128,10 @@ __global__ __launch_bounds__(256) void k_gate_cumsum(const float* __restrict__ g
     }
     if (R) {
         const float g_last = L > 0 ? x[L - 1] : 0.f;
-        f32x4* Rc = R + ((int64_t)c * Nv + h) * kChunk;
-        float* Gcc = Gc + ((int64_t)c * Nv + h) * kChunk;
+        f32x2* Rc = R + ((int64_t)c * Nv + h) * kChunk;
 #pragma unroll
-        for (int32_t i = 0; i < kChunk; ++i) {
-            const int b = i >> 4;
-            const float g_prev = b > 0 ? x[16 * b - 1] : 0.f;
-            const int e = min(16 * b + 15, L > 0 ? L - 1 : 0);
-            Rc[i] = i < L ? f32x4{__expf(x[i]), __expf(g_last - x[i]), __expf(x[i] - g_prev), __expf(x[e] - x[i])}
-                          : f32x4{0.f, 0.f, 0.f, 0.f};
-            Gcc[i] = x[i];
-        }
+        for (int32_t i = 0; i < kChunk; ++i)
+            Rc[i] = i < L ? f32x2{__expf(x[i]), __expf(g_last - x[i])} : f32x2{0.f, 0.f};
     }
 }
 
@@ -168,15 +156,23 @@ __global__ __launch_bounds__(256) void k_gate_cumsum(const float* __restrict__ g
 //      section 2.3: T absorbs diag(beta)) as split (hi, lo) pair fragments of
 //      its lower-triangular 16 x 32 blocks for the fused state pass (when Tf
 //      is given).
+//   6. When Pf is given (fused pipeline): the intra-chunk score block
+//      P = (Q K^T) (.) D, D_ij = exp(G_i - G_j) for j <= i (ChunkGatedDeltaRule
+//      page, formula (5); FLA DeltaNet article, section 2.4), as split pair
+//      fragments in the same six-block layout as T, so that the state pass
+//      does not recompute it for every dv tile. Q K^T is formed once per key
+//      head; the decay is applied per value head.
 template <typename T, int DK>
-__global__ __launch_bounds__(256) void k_build_solve(const T* __restrict__ k, const void* __restrict__ beta,
-                                                      int beta_f32, const float* __restrict__ G,
+__global__ __launch_bounds__(256) void k_build_solve(const T* __restrict__ k, const T* __restrict__ q,
+                                                      const void* __restrict__ beta, int beta_f32,
+                                                      const float* __restrict__ G,
                                                       const int32_t* __restrict__ chunk_start,
                                                       const int32_t* __restrict__ chunk_len,
                                                       int32_t Nk, int32_t Nv, float* __restrict__ A_out,
-                                                      T* __restrict__ Tf) {
+                                                      T* __restrict__ Tf, T* __restrict__ Pf) {
     constexpr int KP = DK + 8;                 // padded LDS row (elements)
     __shared__ __attribute__((aligned(16))) T Ks[kChunk * KP];
+    __shared__ __attribute__((aligned(16))) T Qs[kChunk * KP];
     __shared__ float Lf[kChunk][kChunk + 1];
     __shared__ float Af[kChunk][kChunk + 1];
     __shared__ float bs[kChunk], gs[kChunk];
@@ -187,12 +183,14 @@ __global__ __launch_bounds__(256) void k_build_solve(const T* __restrict__ k, co
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, qd = lane >> 4;
     typedef typename Vec<T>::v8 v8;
 
-    // 1. K rows of the chunk (zero past the chunk end)
+    // 1. K (and Q) rows of the chunk (zero past the chunk end)
     for (int idx = tid; idx < kChunk * (DK / 8); idx += 256) {
         const int row = idx / (DK / 8), seg = idx % (DK / 8);
-        v8 val = zero_pair<T>();
+        v8 val = zero_pair<T>(), qv = zero_pair<T>();
         if (row < L) val = *reinterpret_cast<const v8*>(k + ((s + row) * Nk + kh) * DK + seg * 8);
+        if (Pf && row < L) qv = *reinterpret_cast<const v8*>(q + ((s + row) * Nk + kh) * DK + seg * 8);
         *reinterpret_cast<v8*>(&Ks[row * KP + seg * 8]) = val;
+        if (Pf) *reinterpret_cast<v8*>(&Qs[row * KP + seg * 8]) = qv;
     }
     __syncthreads();
 
@@ -207,6 +205,21 @@ __global__ __launch_bounds__(256) void k_build_solve(const T* __restrict__ k, co
                 v8 a = load_pair_row<T>(&Ks[(wave * 16 + r) * KP + kp * 32], qd);
                 v8 b = load_pair_row<T>(&Ks[(j * 16 + r) * KP + kp * 32], qd);
                 kk[j] = mfma_pair(a, b, kk[j]);
+            }
+        }
+    }
+
+    // transposed score tiles of block row `wave`: qk[j] holds k_{16j+4qd+jj} . q_{16*wave+r}
+    f32x4 qk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        qk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (Pf && j <= wave) {
+#pragma unroll
+            for (int kp = 0; kp < DK / 32; ++kp) {
+                v8 a = load_pair_row<T>(&Ks[(j * 16 + r) * KP + kp * 32], qd);
+                v8 b = load_pair_row<T>(&Qs[(wave * 16 + r) * KP + kp * 32], qd);
+                qk[j] = mfma_pair(a, b, qk[j]);
             }
         }
     }
@@ -330,6 +343,29 @@ __global__ __launch_bounds__(256) void k_build_solve(const T* __restrict__ k, co
                 T* dst = Tf + (((int64_t)c * Nv + h) * kTPairs + p) * 2 * 512;
                 store_frag<T>(dst, lane, sp.hi);
                 if constexpr (kSplitNeeded<T>) store_frag<T>(dst + 512, lane, sp.lo);
+            }
+        }
+        // 6. score pairs of block row `wave`: P_ij = (q_i . k_j) exp(G_i - G_j), j <= i < L
+        if (Pf) {
+            const int i = wave * 16 + r;
+            f32x4 pt[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int col = j * 16 + 4 * qd + jj;
+                    pt[j][jj] = (j <= wave && col <= i && i < L) ? qk[j][jj] * __expf(gs[i] - gs[col]) : 0.f;
+                }
+            }
+            const int pbase = (wave == 0) ? 0 : (wave == 1 ? 1 : (wave == 2 ? 2 : 4));
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp) {
+                if (2 * tp <= wave) {
+                    const Split<T> sp = split_acc_pair<T>(pt[2 * tp], pt[2 * tp + 1]);
+                    T* dst = Pf + (((int64_t)c * Nv + h) * kTPairs + pbase + tp) * 2 * 512;
+                    store_frag<T>(dst, lane, sp.hi);
+                    if constexpr (kSplitNeeded<T>) store_frag<T>(dst + 512, lane, sp.lo);
+                }
             }
         }
         __syncthreads();
@@ -680,9 +716,8 @@ __global__ __launch_bounds__(256) void k_output(const T* __restrict__ q, const T
 // written to LDS in the first order by the wave that updates it.
 template <int DK, int DV>
 __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                                       const bf16* __restrict__ v, const float* __restrict__ Gc,
-                                                       const f32x4* __restrict__ R, const bf16* __restrict__ Tf,
-                                                       const float* __restrict__ S0,
+                                                       const bf16* __restrict__ v, const f32x2* __restrict__ R, const bf16* __restrict__ Tf,
+                                                       const bf16* __restrict__ Pf, const float* __restrict__ S0,
                                                        const int32_t* __restrict__ chunk_start,
                                                        const int32_t* __restrict__ chunk_len,
                                                        const int32_t* __restrict__ seq_first, int32_t Nk, int32_t Nv,
@@ -698,17 +733,17 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
     constexpr int FRAG = 512;                   // elements of one fragment block (64 lanes x 8)
     constexpr int TFRAG = kTPairs * 2 * 512;    // T elements per (chunk, head)
     constexpr int NTCP = TFRAG * 2 / 1024;      // 1 KB copies of T per chunk
-    constexpr int MCP = 2 * NKP + 4;            // copies per output wave per chunk
+    constexpr int MCE = 2 * NKP + NTCP / 4;     // early-list copies per copy wave per chunk
     constexpr int RSRC = 0x00020000;            // buffer descriptor word 3 (raw 32-bit access)
-    static_assert(8 * NKP + NTCP + 4 == 4 * MCP, "copy schedule");
+    static_assert(NTCP % 4 == 0 && NTCP + 3 <= 16, "copy schedule");
     // chunk tiles, double-buffered; each half is its own array so that the
     // compiler can tell reads of one half from copies into the other
     __shared__ __attribute__((aligned(16))) T Ks0[4 * NKP * FRAG], Ks1[4 * NKP * FRAG];
     __shared__ __attribute__((aligned(16))) T Qs0[4 * NKP * FRAG], Qs1[4 * NKP * FRAG];
     __shared__ __attribute__((aligned(16))) T Tb0[TFRAG], Tb1[TFRAG];
+    __shared__ __attribute__((aligned(16))) T Pb0[TFRAG], Pb1[TFRAG];
     __shared__ __attribute__((aligned(16))) T Vs0[kChunk * 16], Vs1[kChunk * 16];
-    __shared__ __attribute__((aligned(16))) f32x4 Rs0[kChunk], Rs1[kChunk];
-    __shared__ __attribute__((aligned(16))) float Gs0[kChunk], Gs1[kChunk];
+    __shared__ __attribute__((aligned(16))) f32x2 Rs0[kChunk], Rs1[kChunk];
     __shared__ __attribute__((aligned(16))) T Sb[NKP][2][FRAG];
     __shared__ __attribute__((aligned(16))) T Zb[2][2][FRAG];
     __shared__ __attribute__((aligned(16))) T Vb[2][2][FRAG];
@@ -736,18 +771,23 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
     auto frag = [&](const T* tile, int tb, int kp) {
         return *reinterpret_cast<const v8*>(&tile[(tb * NKP + kp) * FRAG + slot(r, qd) * 8]);
     };
+    // Exchange buffers hold split pair fragments as two lane-linear half blocks
+    // (elements 0..3 of every lane, then elements 4..7), so that the wave that
+    // produces one half writes 8 contiguous bytes per lane.
     auto store_split_half = [&](T (*buf)[2][FRAG], int tp, int half, const f32x4& x) {
         float xx[8] = {x[0], x[1], x[2], x[3], 0.f, 0.f, 0.f, 0.f};
         const Split<T> sp = split8<T>(xx);
         v4 hi4 = {sp.hi[0], sp.hi[1], sp.hi[2], sp.hi[3]};
         v4 lo4 = {sp.lo[0], sp.lo[1], sp.lo[2], sp.lo[3]};
-        *reinterpret_cast<v4*>(&buf[tp][0][lane * 8 + 4 * half]) = hi4;
-        *reinterpret_cast<v4*>(&buf[tp][1][lane * 8 + 4 * half]) = lo4;
+        *reinterpret_cast<v4*>(&buf[tp][0][half * 256 + lane * 4]) = hi4;
+        *reinterpret_cast<v4*>(&buf[tp][1][half * 256 + lane * 4]) = lo4;
     };
     auto load_split = [&](T (*buf)[2][FRAG], int tp) {
         Split<T> sp;
-        sp.hi = *reinterpret_cast<const v8*>(&buf[tp][0][lane * 8]);
-        sp.lo = *reinterpret_cast<const v8*>(&buf[tp][1][lane * 8]);
+        sp.hi = concat<T>(*reinterpret_cast<const v4*>(&buf[tp][0][lane * 4]),
+                          *reinterpret_cast<const v4*>(&buf[tp][0][256 + lane * 4]));
+        sp.lo = concat<T>(*reinterpret_cast<const v4*>(&buf[tp][1][lane * 4]),
+                          *reinterpret_cast<const v4*>(&buf[tp][1][256 + lane * 4]));
         return sp;
     };
     const int64_t sbase = ((int64_t)n * Nv + h) * DK * DV;
@@ -776,7 +816,7 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
                     const Split<T> sp = split8<T>(xx);
                     v4 hi4 = {sp.hi[0], sp.hi[1], sp.hi[2], sp.hi[3]};
                     v4 lo4 = {sp.lo[0], sp.lo[1], sp.lo[2], sp.lo[3]};
-                    const int dst = (16 * (2 * (db & 1) + (qd >> 1)) + r) * 8 + 4 * (qd & 1);
+                    const int dst = (qd & 1) * 256 + (16 * (2 * (db & 1) + (qd >> 1)) + r) * 4;
                     *reinterpret_cast<v4*>(&Sb[db >> 1][0][dst]) = hi4;
                     *reinterpret_cast<v4*>(&Sb[db >> 1][1][dst]) = lo4;
                 }
@@ -806,7 +846,7 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
                 const T* Qb = odd ? Qs1 : Qs0;
                 const T* Tbb = odd ? Tb1 : Tb0;
                 const T* Vsb = odd ? Vs1 : Vs0;
-                const f32x4* Rsb = odd ? Rs1 : Rs0;
+                const f32x2* Rsb = odd ? Rs1 : Rs0;
 
                 // ---- A: Y = K S_in (hi and lo passes), Z = V - exp(G) Y -> LDS
                 Split<T> BS[NKP];
@@ -816,7 +856,7 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
                     BS[kp] = load_split(Sb, kp);
                     ka[kp] = frag(Kb, w, kp);
                 }
-                f32x4 rrow[4];
+                f32x2 rrow[4];
                 float vrow[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -832,6 +872,13 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
                         tf[tp].hi = load_frag<T>(&Tbb[(pbase + tp) * 2 * FRAG], lane);
                         tf[tp].lo = load_frag<T>(&Tbb[(pbase + tp) * 2 * FRAG + FRAG], lane);
                     }
+                }
+                v8 kt[TPW][2];                          // K^T operands of phase C
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) {
+                    const int db = min(w * TPW + t, NDB - 1);
+#pragma unroll
+                    for (int tp = 0; tp < 2; ++tp) kt[t][tp] = kt_frag(Kb, db, tp);
                 }
                 f32x4 Yh = {0.f, 0.f, 0.f, 0.f}, Yl = Yh;
 #pragma unroll
@@ -850,13 +897,6 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
 #pragma unroll
                 for (int tp = 0; tp < 2; ++tp)
                     if (tp < ntp) zf[tp] = load_split(Zb, tp);
-                v8 kt[TPW][2];
-#pragma unroll
-                for (int t = 0; t < TPW; ++t) {
-                    const int db = min(w * TPW + t, NDB - 1);
-#pragma unroll
-                    for (int tp = 0; tp < 2; ++tp) kt[t][tp] = kt_frag(Kb, db, tp);
-                }
                 f32x4 Qh = {0.f, 0.f, 0.f, 0.f}, Ql = Qh;
 #pragma unroll
                 for (int kp = 0; kp < NKP; ++kp) {
@@ -920,18 +960,20 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
     if (c0 >= c1) return;
     if (wv >= 8) {
         // ======================================================== copy waves
-        // Wave 8+w issues copies u = w + 4 m (m < MCP) of a chunk's list (K blocks,
-        // Q blocks, T pieces, then the V halves, R and G) into one LDS half, all at
-        // the start of a step, and waits for them before the step's last barrier.
+        // Wave 8+w moves its share of each chunk's tiles into LDS. A chunk's
+        // early list (K blocks, Q blocks, T pieces: read only in phase A) is
+        // issued during phases B and C two steps ahead, once the state waves
+        // have finished reading the half it overwrites; its late list (score
+        // pieces, V halves, R: read until phase C) during phase A one step
+        // ahead. Before the last barrier of step c the wave waits for everything
+        // but the early list of chunk c+2, which may still be in flight (vector
+        // memory operations complete in order).
         const int w = wv - 8;
         const int kq_lane = (((lane & 15) ^ (4 * ((lane >> 4) & 1))) * Nk * DK + 8 * (lane >> 4)) * 2;
-        auto copy_chunk = [&](int c, bool odd) {
+        auto copy_early = [&](int c, bool odd, int m0, int m1) {
             T* Kd = odd ? Ks1 : Ks0;
             T* Qd = odd ? Qs1 : Qs0;
             T* Td = odd ? Tb1 : Tb0;
-            T* Vd = odd ? Vs1 : Vs0;
-            f32x4* Rd = odd ? Rs1 : Rs0;
-            float* Gd = odd ? Gs1 : Gs0;
             const int64_t s = chunk_s(c);
             const int L = chunk_L(c);
             const uint32_t kq_bytes = (uint32_t)((L - 1) * Nk * DK + DK) * 2u;
@@ -939,35 +981,60 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
             const auto rq = rsrc(q, (s * Nk + kh) * DK, 2, kq_bytes);
             const auto rt = rsrc(Tf, ((int64_t)c * Nv + h) * TFRAG, 2, TFRAG * 2);
 #pragma unroll
-            for (int m = 0; m < MCP; ++m) {
+            for (int m = 0; m < MCE; ++m) {
                 const int u = w + 4 * m;
+                if (m < m0 || m >= m1) continue;
                 if (m < NKP) {                               // K block (tb, kp)
                     const int tb = u / NKP, kp = u % NKP;
                     buffer_to_lds16(rk, Kd + u * FRAG, kq_lane + (16 * tb * Nk * DK + 32 * kp) * 2);
                 } else if (m < 2 * NKP) {                    // Q block
                     const int f = u - 4 * NKP, tb = f / NKP, kp = f % NKP;
                     buffer_to_lds16(rq, Qd + f * FRAG, kq_lane + (16 * tb * Nk * DK + 32 * kp) * 2);
-                } else if (m < 2 * NKP + NTCP / 4) {         // T piece
+                } else {                                     // T piece
                     const int p = u - 8 * NKP;
                     buffer_to_lds16(rt, Td + p * FRAG, (p * 64 + lane) * 16);
-                } else if (w < 2) {                          // V rows 32 w .. 32 w + 31 (16 columns)
-                    buffer_to_lds16(rsrc(v, (s * Nv + h) * DV + nb * 16, 2, (uint32_t)((L - 1) * Nv * DV + 16) * 2u),
-                                    Vd + w * 512, ((32 * w + (lane >> 1)) * Nv * DV + 8 * (lane & 1)) * 2);
-                } else if (w == 2) {                         // R
-                    buffer_to_lds16(rsrc(R, ((int64_t)c * Nv + h) * kChunk, 16, kChunk * 16), Rd, lane * 16);
-                } else {                                     // G
-                    buffer_to_lds4(rsrc(Gc, ((int64_t)c * Nv + h) * kChunk, 4, kChunk * 4), Gd, lane * 4);
                 }
             }
         };
-        copy_chunk(c0, false);
+        auto copy_late = [&](int c, bool odd) {
+            T* Pd = odd ? Pb1 : Pb0;
+            T* Vd = odd ? Vs1 : Vs0;
+            f32x2* Rd = odd ? Rs1 : Rs0;
+            const int64_t s = chunk_s(c);
+            const int L = chunk_L(c);
+            const auto rp = rsrc(Pf, ((int64_t)c * Nv + h) * TFRAG, 2, TFRAG * 2);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int u = w + 4 * m;
+                if (u < NTCP) {                              // score piece
+                    buffer_to_lds16(rp, Pd + u * FRAG, (u * 64 + lane) * 16);
+                } else if (u < NTCP + 2) {                   // V rows 32 vh .. 32 vh + 31 (16 columns)
+                    const int vh = u - NTCP;
+                    buffer_to_lds16(rsrc(v, (s * Nv + h) * DV + nb * 16, 2, (uint32_t)((L - 1) * Nv * DV + 16) * 2u),
+                                    Vd + vh * 512, ((32 * vh + (lane >> 1)) * Nv * DV + 8 * (lane & 1)) * 2);
+                } else if (u == NTCP + 2 && lane < 32) {     // R (512 bytes: two positions per lane)
+                    buffer_to_lds16(rsrc(R, ((int64_t)c * Nv + h) * kChunk, 8, kChunk * 8), Rd, lane * 16);
+                }
+            }
+        };
+        constexpr int MEB = MCE / 2;                     // early copies issued in phase B (rest in C)
+        copy_early(c0, false, 0, MCE);
+        copy_late(c0, false);
         wait_vmem();
+        if (c0 + 1 < c1) copy_early(c0 + 1, true, 0, MCE);
         lds_barrier();
         for (int c = c0; c < c1; ++c) {
-            if (c + 1 < c1) copy_chunk(c + 1, !((c - c0) & 1));
+            const bool odd = (c - c0) & 1;
+            if (c + 1 < c1) copy_late(c + 1, !odd);
             lds_barrier();                                                          // barrier 1
+            if (c + 2 < c1) copy_early(c + 2, odd, 0, MEB);
             lds_barrier();                                                          // barrier 2
-            wait_vmem();                 // this wave's copies of chunk c+1 have landed
+            if (c + 2 < c1) {
+                copy_early(c + 2, odd, MEB, MCE);
+                wait_vmem_but<MCE>();    // chunk c+1 has landed; chunk c+2's early list may be in flight
+            } else {
+                wait_vmem();
+            }
             lds_barrier();                                                          // barrier 3
         }
         return;
@@ -980,61 +1047,25 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
     int o_off[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) o_off[j] = ((w * 16 + 4 * qd + j) * Nv * DV + r) * ob;
-    // score block of positions 16 W.. (transposed tiles K_j Q_i^T, j-blocks <= W), decayed
-    Split<T> pa[2];
-    auto scores = [&](auto Wc, const T* Kb, const T* Qb, const float* Gsb, const f32x4* Rsb) {
-        constexpr int W = decltype(Wc)::value;
-        v8 qa[NKP], kb[W + 1][NKP];
-#pragma unroll
-        for (int kp = 0; kp < NKP; ++kp) qa[kp] = frag(Qb, W, kp);
-#pragma unroll
-        for (int tj = 0; tj <= W; ++tj)
-#pragma unroll
-            for (int kp = 0; kp < NKP; ++kp) kb[tj][kp] = frag(Kb, tj, kp);
-        f32x4 pt[W + 1];
-#pragma unroll
-        for (int tj = 0; tj <= W; ++tj) pt[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kp = 0; kp < NKP; ++kp)
-#pragma unroll
-            for (int tj = 0; tj <= W; ++tj) pt[tj] = mfma_pair(kb[tj][kp], qa[kp], pt[tj]);
-        const float gi = Gsb[W * 16 + r];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {                 // diagonal block: exp(G_i - G_j) for j <= i
-            const float d = __expf(gi - Gsb[W * 16 + 4 * qd + jj]);
-            pt[W][jj] = 4 * qd + jj <= r ? pt[W][jj] * d : 0.f;
-        }
-        float gam = Rsb[W * 16 + r].z;                  // earlier blocks: R.z_i (block ends between) R.w_j
-#pragma unroll
-        for (int tj = W - 1; tj >= 0; --tj) {
-            if (tj + 1 < W) gam *= Rsb[16 * (tj + 1) + 15].z;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) pt[tj][jj] *= gam * Rsb[tj * 16 + 4 * qd + jj].w;
-        }
-        const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-        pa[0] = split_acc_pair<T>(pt[0], W >= 1 ? pt[W >= 1 ? 1 : 0] : zero4);
-        if constexpr (W >= 2) pa[1] = split_acc_pair<T>(pt[2], W >= 3 ? pt[W >= 3 ? 3 : 2] : zero4);
-    };
-
+    const int pbase = (w == 0) ? 0 : (w == 1 ? 1 : (w == 2 ? 2 : 4));
     lds_barrier();
     for (int c = c0; c < c1; ++c) {
         const bool odd = (c - c0) & 1;
-        const T* Kb = odd ? Ks1 : Ks0;
-        const T* Qb = odd ? Qs1 : Qs0;
-        const float* Gsb = odd ? Gs1 : Gs0;
-        const f32x4* Rsb = odd ? Rs1 : Rs0;
-
-        // ---- A: score block of positions 16w..16w+15
-        switch (w) {
-            case 0: scores(std::integral_constant<int, 0>{}, Kb, Qb, Gsb, Rsb); break;
-            case 1: scores(std::integral_constant<int, 1>{}, Kb, Qb, Gsb, Rsb); break;
-            case 2: scores(std::integral_constant<int, 2>{}, Kb, Qb, Gsb, Rsb); break;
-            default: scores(std::integral_constant<int, 3>{}, Kb, Qb, Gsb, Rsb); break;
-        }
+        const T* Pbb = odd ? Pb1 : Pb0;
+        const f32x2* Rsb = odd ? Rs1 : Rs0;
         lds_barrier();                                                              // barrier 1
         lds_barrier();                                                              // barrier 2
 
         // ---- C: O = scale [exp(G) Q S_in + P V_new] for positions 16w..16w+15
+        Split<T> pa[2], vn[2];
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+            if (tp < ntp) {
+                pa[tp].hi = load_frag<T>(&Pbb[(pbase + tp) * 2 * FRAG], lane);
+                pa[tp].lo = load_frag<T>(&Pbb[(pbase + tp) * 2 * FRAG + FRAG], lane);
+                vn[tp] = load_split(Vb, tp);
+            }
+        }
         const f32x4 qs = QSx[w][lane];
         f32x4 out, ol = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1042,10 +1073,9 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp) {
             if (tp < ntp) {
-                const Split<T> vn = load_split(Vb, tp);
-                out = mfma_pair(pa[tp].hi, vn.hi, out);
-                ol = mfma_pair(pa[tp].lo, vn.hi, ol);
-                ol = mfma_pair(pa[tp].hi, vn.lo, ol);
+                out = mfma_pair(pa[tp].hi, vn[tp].hi, out);
+                ol = mfma_pair(pa[tp].lo, vn[tp].hi, ol);
+                ol = mfma_pair(pa[tp].hi, vn[tp].lo, ol);
             }
         }
         const int64_t s = chunk_s(c);
@@ -1077,13 +1107,14 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
     if (NT > 0) {
         const int64_t units = (int64_t)NT * a.Nv;
         k_gate_cumsum<<<(unsigned)((units + 255) / 256), 256, 0, st>>>(a.g, a.chunk_start, a.chunk_len, NT, a.Nv, a.G,
-                                                                        fused ? (f32x4*)a.R : nullptr, (float*)a.Gc);
+                                                                        fused ? (f32x2*)a.R : nullptr);
     }
     mark(2);
     if (NT > 0)
-        k_build_solve<T, DK><<<dim3(NT, a.Nk), 256, 0, st>>>((const T*)a.k, a.beta, a.beta_f32, a.G, a.chunk_start,
-                                                            a.chunk_len, a.Nk, a.Nv, fused ? nullptr : (float*)a.A,
-                                                            (T*)a.Tf);
+        k_build_solve<T, DK><<<dim3(NT, a.Nk), 256, 0, st>>>((const T*)a.k, (const T*)a.q, a.beta, a.beta_f32, a.G,
+                                                            a.chunk_start, a.chunk_len, a.Nk, a.Nv,
+                                                            fused ? nullptr : (float*)a.A, (T*)a.Tf,
+                                                            fused ? (T*)a.Pf : nullptr);
     mark(3);
     if (NT > 0 && !fused)
         k_wu<T, DK, DV><<<dim3(NT, a.Nk), 256, 0, st>>>((const T*)a.k, (const T*)a.v, a.beta, a.beta_f32, a.G,
@@ -1094,8 +1125,8 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
         if constexpr (kFused) {
             if (fused) {
                 k_state_output<DK, DV><<<dim3(a.N, a.Nv, DV / 16), 768, 0, st>>>(
-                    (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const float*)a.Gc, (const f32x4*)a.R,
-                    (const bf16*)a.Tf, a.S0,
+                    (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const f32x2*)a.R,
+                    (const bf16*)a.Tf, (const bf16*)a.Pf, a.S0,
                     a.chunk_start, a.chunk_len, a.seq_first, a.Nk, a.Nv, a.scale, a.out_f32, a.o, a.ST);
             }
         }

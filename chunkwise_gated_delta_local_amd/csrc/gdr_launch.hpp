@@ -26,8 +26,8 @@ struct LaunchArgs {
     float* G;
     void *A, *W, *U, *KT, *H, *VN;   // reference-pipeline intermediates
     void* Tf;                        // T = A diag(beta) fragments (fused pipeline)
-    void* R;                         // decay factors, chunk-major (fused pipeline)
-    void* Gc;                        // G, chunk-major (fused pipeline)
+    void* Pf;                        // score block (Q K^T) (.) D fragments (fused pipeline)
+    void* R;                         // decay factors exp(G), exp(G_last - G), chunk-major (fused pipeline)
     bool reference;                  // run the five separate kernels even for bf16
     hipStream_t stream;
 };
