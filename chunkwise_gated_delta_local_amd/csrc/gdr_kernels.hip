@@ -163,19 +163,25 @@ __global__ __launch_bounds__(256) void k_gate_cumsum(const float* __restrict__ g
 //      does not recompute it for every dv tile. Q K^T is formed once per key
 //      head; the decay is applied per value head.
 template <typename T, int DK>
-__global__ __launch_bounds__(256) void k_build_solve(const T* __restrict__ k, const T* __restrict__ q,
-                                                      const void* __restrict__ beta, int beta_f32,
-                                                      const float* __restrict__ G,
-                                                      const int32_t* __restrict__ chunk_start,
-                                                      const int32_t* __restrict__ chunk_len,
-                                                      int32_t Nk, int32_t Nv, float* __restrict__ A_out,
-                                                      T* __restrict__ Tf, T* __restrict__ Pf) {
+__global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k, const T* __restrict__ q,
+                                                         const void* __restrict__ beta, int beta_f32,
+                                                         const float* __restrict__ G,
+                                                         const int32_t* __restrict__ chunk_start,
+                                                         const int32_t* __restrict__ chunk_len,
+                                                         int32_t Nk, int32_t Nv, float* __restrict__ A_out,
+                                                         T* __restrict__ Tf, T* __restrict__ Pf) {
     constexpr int KP = DK + 8;                 // padded LDS row (elements)
-    __shared__ __attribute__((aligned(16))) T Ks[kChunk * KP];
-    __shared__ __attribute__((aligned(16))) T Qs[kChunk * KP];
-    __shared__ float Lf[kChunk][kChunk + 1];
-    __shared__ float Af[kChunk][kChunk + 1];
+    constexpr int SEGS = kChunk * (DK / 8) / 256;   // 16-byte row segments per thread
+    // The K and Q tiles are only needed until the K K^T and Q K^T tiles are in
+    // registers; L and A reuse their LDS afterwards.
+    constexpr int TILE_BYTES = 2 * kChunk * KP * (int)sizeof(T);
+    constexpr int LA_BYTES = 2 * kChunk * (kChunk + 1) * 4;
+    __shared__ __attribute__((aligned(16))) char smem[TILE_BYTES > LA_BYTES ? TILE_BYTES : LA_BYTES];
     __shared__ float bs[kChunk], gs[kChunk];
+    T* Ks = reinterpret_cast<T*>(smem);
+    T* Qs = Ks + kChunk * KP;
+    float (*Lf)[kChunk + 1] = reinterpret_cast<float (*)[kChunk + 1]>(smem);
+    float (*Af)[kChunk + 1] = Lf + kChunk;
 
     const int c = blockIdx.x, kh = blockIdx.y;
     const int64_t s = chunk_start[c];
@@ -183,14 +189,25 @@ __global__ __launch_bounds__(256) void k_build_solve(const T* __restrict__ k, co
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, qd = lane >> 4;
     typedef typename Vec<T>::v8 v8;
 
-    // 1. K (and Q) rows of the chunk (zero past the chunk end)
-    for (int idx = tid; idx < kChunk * (DK / 8); idx += 256) {
-        const int row = idx / (DK / 8), seg = idx % (DK / 8);
-        v8 val = zero_pair<T>(), qv = zero_pair<T>();
-        if (row < L) val = *reinterpret_cast<const v8*>(k + ((s + row) * Nk + kh) * DK + seg * 8);
-        if (Pf && row < L) qv = *reinterpret_cast<const v8*>(q + ((s + row) * Nk + kh) * DK + seg * 8);
-        *reinterpret_cast<v8*>(&Ks[row * KP + seg * 8]) = val;
-        if (Pf) *reinterpret_cast<v8*>(&Qs[row * KP + seg * 8]) = qv;
+    // 1. K (and Q) rows of the chunk (zero past the chunk end): all loads first
+    {
+        v8 kv[SEGS], qv[SEGS];
+#pragma unroll
+        for (int i = 0; i < SEGS; ++i) {
+            const int idx = tid + 256 * i, row = idx / (DK / 8), seg = idx % (DK / 8);
+            kv[i] = zero_pair<T>();
+            qv[i] = zero_pair<T>();
+            if (row < L) {
+                kv[i] = *reinterpret_cast<const v8*>(k + ((s + row) * Nk + kh) * DK + seg * 8);
+                if (Pf) qv[i] = *reinterpret_cast<const v8*>(q + ((s + row) * Nk + kh) * DK + seg * 8);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < SEGS; ++i) {
+            const int idx = tid + 256 * i, row = idx / (DK / 8), seg = idx % (DK / 8);
+            *reinterpret_cast<v8*>(&Ks[row * KP + seg * 8]) = kv[i];
+            if (Pf) *reinterpret_cast<v8*>(&Qs[row * KP + seg * 8]) = qv[i];
+        }
     }
     __syncthreads();
 
@@ -208,7 +225,6 @@ __global__ __launch_bounds__(256) void k_build_solve(const T* __restrict__ k, co
             }
         }
     }
-
     // transposed score tiles of block row `wave`: qk[j] holds k_{16j+4qd+jj} . q_{16*wave+r}
     f32x4 qk[4];
 #pragma unroll
@@ -223,6 +239,12 @@ __global__ __launch_bounds__(256) void k_build_solve(const T* __restrict__ k, co
             }
         }
     }
+    __syncthreads();                           // tiles consumed: the LDS now holds L and A
+    // the two strictly-upper 16x16 blocks of A that the block merges read are zero
+    for (int idx = tid; idx < 2 * 256; idx += 256) {
+        const int blk = idx >> 8, e = idx & 255, row = blk * 32 + (e >> 4), col = blk * 32 + 16 + (e & 15);
+        Af[row][col] = 0.f;
+    }
 
     const int group = Nv / Nk;
     for (int hh = 0; hh < group; ++hh) {
@@ -231,13 +253,9 @@ __global__ __launch_bounds__(256) void k_build_solve(const T* __restrict__ k, co
             bs[tid] = tid < L ? load_beta(beta, (s + tid) * Nv + h, beta_f32) : 0.f;
             gs[tid] = tid < L ? G[(s + tid) * Nv + h] : 0.f;
         }
-        for (int idx = tid; idx < kChunk * kChunk; idx += 256) {
-            Lf[idx >> 6][idx & 63] = 0.f;
-            Af[idx >> 6][idx & 63] = 0.f;
-        }
         __syncthreads();
 
-        // 2. strictly lower L
+        // 2. strictly lower L (every entry of the blocks on and below the diagonal)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (j <= wave) {
