@@ -41,20 +41,25 @@ T_FRAG_BYTES = 6 * 2 * 512 * 2          # T = A diag(beta) split fragments per (
 def stage_algorithmic_bytes(w: synth.Workload, Ttot: int, N: int, NT: int, out_bytes: int,
                             s0: bool) -> dict:
     """Bytes each kernel must move by its own inputs and outputs: every tensor it
-    reads read once, every tensor it writes written once, in its stored type."""
+    reads read once, every tensor it writes written once, in its stored type
+    (intermediates of the pipeline included: T and the score block are 6 split
+    bf16 pair fragments per (chunk, value head), the decay factors 8 bytes per
+    position)."""
     es = 2 if w.dtype == "bf16" else 4
     Nv, Nk, dk, dv = w.Nv, w.Nk, w.dk, w.dv
     tv = Ttot * Nv                      # token-heads (value heads)
     tk = Ttot * Nk                      # token-heads (q/k heads)
     beta_b = es
     state = N * Nv * dk * dv * 4
+    frag = NT * Nv * T_FRAG_BYTES       # one six-pair split fragment set per (chunk, value head)
+    rfac = NT * Nv * 64 * 8             # decay factors, chunk-major
     if w.dtype == "bf16":               # fused path
         return {
             "k_chunk_table": 4 * (N + 1) + 16 * NT,
-            "k_gate_cumsum": tv * (4 + 4),
-            "k_build_solve": tk * dk * es + tv * (beta_b + 4) + NT * Nv * T_FRAG_BYTES,   # k, beta, G in; T out
-            "k_state_output": 2 * tk * dk * es + tv * dv * es + tv * 4 + NT * Nv * T_FRAG_BYTES  # q, k, v, G, T in
-                              + tv * dv * out_bytes + state * (2 if s0 else 1),                  # o, S_T out (S0 in)
+            "k_gate_cumsum": tv * (4 + 4) + rfac,                                        # g in; G, R out
+            "k_build_solve": 2 * tk * dk * es + tv * (beta_b + 4) + 2 * frag,           # k, q, beta, G in; T, P out
+            "k_state_output": 2 * tk * dk * es + tv * dv * es + rfac + 2 * frag         # q, k, v, R, T, P in
+                              + tv * dv * out_bytes + state * (2 if s0 else 1),          # o, S_T out (S0 in)
             "(fused)": 0,
         }
     return {
@@ -146,6 +151,73 @@ def copy_probe(mib: int) -> None:
     print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 3}), flush=True)
 
 
+def _counter_means(path: str, counter: str) -> dict:
+    """Mean counter value per dispatch, by kernel name, from a rocprofv3 counter_collection.csv."""
+    import csv
+    sums, counts = {}, {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            sums[name] = sums.get(name, 0.0) + float(row["Counter_Value"])
+            counts[name] = counts.get(name, 0) + 1
+    return {n: sums[n] / counts[n] for n in sums}
+
+
+def counter_summary(src: str, out_dir: str, workload: int) -> None:
+    """HBM bytes per launch of every gdr kernel from FETCH_SIZE / WRITE_SIZE runs,
+    each scaled by what the same counter reads for the copy probe of known size."""
+    def csv_of(sub):
+        for root, _, files in os.walk(os.path.join(src, sub)):
+            for fn in files:
+                if fn.endswith("counter_collection.csv"):
+                    return os.path.join(root, fn)
+        raise FileNotFoundError(os.path.join(src, sub))
+    fetch, write = _counter_means(csv_of("fetch"), "FETCH_SIZE"), _counter_means(csv_of("write"), "WRITE_SIZE")
+    cfetch, cwrite = _counter_means(csv_of("cfetch"), "FETCH_SIZE"), _counter_means(csv_of("cwrite"), "WRITE_SIZE")
+    probe = [n for n in cfetch if "neg_kernel" in n]
+    if not probe:
+        raise RuntimeError("copy-probe kernel not found in the calibration runs")
+    probe_kib = 1024 * 1024.0                            # --copy-probe-mib 1024: 1 GiB read and 1 GiB written
+    f_scale = probe_kib / cfetch[probe[0]]
+    w_scale = probe_kib / cwrite[probe[0]]
+    wl = "T65536_Nk16_Nv32_d128" if workload == 5 else "workload%d" % workload
+    os.makedirs(out_dir, exist_ok=True)
+    for name in sorted(fetch):
+        short = next((k for k in sorted(STAGE_KERNELS + ("k_state_output",), key=len, reverse=True) if k in name), None)
+        if short is None or name not in write:
+            continue
+        fb, wb = fetch[name] * f_scale * 1024.0, write[name] * w_scale * 1024.0
+        path = os.path.join(out_dir, "%s_%s_counters.txt" % (short, wl))
+        with open(path, "w") as f:
+            f.write("# HBM traffic of %s, workload %s (one forward per bench step)\n" % (short, wl))
+            f.write("# commands (run from the repository root):\n")
+            f.write("#   rocprofv3 --pmc FETCH_SIZE -d <dir>/fetch -o run --output-format csv -- "
+                    "python3 bench.py --steps 3 --warmup 1 --cpu-seconds 0\n")
+            f.write("#   rocprofv3 --pmc WRITE_SIZE -d <dir>/write -o run --output-format csv -- "
+                    "python3 bench.py --steps 3 --warmup 1 --cpu-seconds 0\n")
+            f.write("#   rocprofv3 --pmc FETCH_SIZE -d <dir>/cfetch -o run --output-format csv -- "
+                    "python3 bench.py --copy-probe-mib 1024\n")
+            f.write("#   rocprofv3 --pmc WRITE_SIZE -d <dir>/cwrite -o run --output-format csv -- "
+                    "python3 bench.py --copy-probe-mib 1024\n")
+            f.write("#   python3 bench.py --counter-summary <dir> --summary-out profiles\n")
+            f.write("# FETCH_SIZE / WRITE_SIZE are in KiB per dispatch; each is scaled by (known bytes of the\n")
+            f.write("# copy probe) / (counter reading for the copy probe).\n")
+            f.write("kernel: %s\n" % name)
+            f.write("source_digest: %s\n" % source_digest())
+            f.write("fetch_kib_per_dispatch_raw: %.1f\n" % fetch[name])
+            f.write("write_kib_per_dispatch_raw: %.1f\n" % write[name])
+            f.write("copy_probe_fetch_kib_raw: %.1f\n" % cfetch[probe[0]])
+            f.write("copy_probe_write_kib_raw: %.1f\n" % cwrite[probe[0]])
+            f.write("fetch_scale: %.4f\n" % f_scale)
+            f.write("write_scale: %.4f\n" % w_scale)
+            f.write("hbm_read_bytes_per_launch: %.0f\n" % fb)
+            f.write("hbm_write_bytes_per_launch: %.0f\n" % wb)
+            f.write("hbm_bytes_per_launch: %.0f\n" % (fb + wb))
+        print(path)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,7 +228,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget; 0 skips it")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB three times (calibrates HBM byte counters)")
+    ap.add_argument("--counter-summary", metavar="DIR",
+                    help="only summarise rocprofv3 counter runs found under DIR (fetch/, write/, cfetch/, cwrite/) "
+                         "into one text file per kernel, written to --summary-out")
+    ap.add_argument("--summary-out", metavar="DIR", default="profiles")
     args = ap.parse_args()
+    if args.counter_summary:
+        counter_summary(args.counter_summary, args.summary_out, args.workload)
+        return
     if args.gpus != 1:
         print("bench.py: this implementation runs on one GPU only; --gpus %d is not supported" % args.gpus,
               file=sys.stderr)
