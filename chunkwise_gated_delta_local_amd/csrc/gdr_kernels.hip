@@ -696,42 +696,43 @@ __global__ __launch_bounds__(256) void k_output(const T* __restrict__ q, const T
 }
 
 // ============================================================ K4 + K5 fused: state pass with output
-// Production path for bf16 inputs. One workgroup of eight wavefronts per
+// Production path for bf16 inputs. One workgroup of twelve wavefronts per
 // (sequence, value head, 16 columns of dv) walks the sequence's chunks in
 // order with the state slice S (dk x 16, fp32) on chip, and produces the output
 // of each chunk as it goes, so neither the per-chunk states nor V_new reach HBM.
 // Per chunk (ChunkGatedDeltaRule page, formulas (3)-(6); FLA DeltaNet article,
-// sections 2.3-2.4), with T = A diag(beta) from the A-build kernel:
+// sections 2.3-2.4), with T = A diag(beta) and the score block
+// P = (Q K^T) (.) D from the A-build kernel:
 //   Y     = K S_in,  Z = V - diag(exp(G)) Y      so that V_new = U - W S_in = T Z
 //   V_new = T Z                                  (T lower triangular)
 //   S_out = exp(G_last) S_in + K^T diag(exp(G_last - G)) V_new
-//   O     = scale [diag(exp(G)) Q S_in + (Q K^T (.) D) V_new]
-// The wavefronts split into two roles that run side by side, one of each on
+//   O     = scale [diag(exp(G)) Q S_in + P V_new]
+// The wavefronts split into three roles that run side by side, one of each on
 // every SIMD:
-//   state waves  (0..3): wave w owns positions 16w..16w+15 for Y, Z, Q S_in and
-//                        V_new, and dk tiles of S for the update. This is the
-//                        sequential chain.
-//   output waves (4..7): wave 4+w computes the score block of positions
-//                        16w..16w+15 and their output, and copies the next
-//                        chunk's tiles from global memory straight into LDS.
-// Each chunk step has three phases separated by workgroup barriers:
-//   A  state: S_in (split) from LDS, Y, Z -> LDS      output: scores + decay
-//   B  state: Q S_in, V_new = T Z -> LDS               output: -
-//   C  state: S update, S_out (split) -> LDS           output: O
-// and the output waves spread the copies of chunk c+1 over all three phases
-// (16-byte buffer loads to LDS, rows past the chunk end read as zero). K and Q
-// tiles are held fragment-major: one 1 KB block per (16 rows, 32 columns),
-// lane l's 16 bytes at a swizzled slot, so that every matrix-core operand is
-// one 16-byte LDS read; K^T operands come from the same blocks through
-// transposing LDS reads. The decay exp(G_i - G_j) of the score block is a
-// product of the precomputed factors R outside the diagonal 16x16 blocks,
-// where it is evaluated directly.
+//   state waves  (0..3):  wave w owns positions 16w..16w+15 for Y, Z, Q S_in and
+//                         V_new, and dk tiles of S for the update. This is the
+//                         sequential chain.
+//   output waves (4..7):  wave 4+w forms the output of positions 16w..16w+15.
+//   copy waves   (8..11): move the coming chunks' tiles from global memory
+//                         straight into LDS (16-byte buffer loads to LDS, rows
+//                         past the chunk end read as zero) and do nothing else,
+//                         so no wave that reads LDS ever waits for a copy.
+// Each chunk step has three phases separated by barriers that wait for LDS
+// traffic only (never for global loads or stores):
+//   A  state: S_in (split) from LDS, Y, Z -> LDS; every read of the chunk's
+//             K, Q and T tiles happens here
+//   B  state: Q S_in -> LDS, V_new = T Z -> LDS
+//   C  state: S update, S_out (split) -> LDS        output: O -> global
+// K and Q tiles sit in LDS fragment-major: one 1 KB block per (16 rows, 32
+// columns), lane l's 16 bytes at a swizzled slot, so that every matrix-core
+// operand is one 16-byte LDS read; K^T operands come from the same blocks
+// through transposing LDS reads.
 //
-// Contraction orders: products over dk (K S, Q S, K Q^T) take the 32 indices
-// of a block as 8 qd + e for lane quarter qd and element e (so that a fragment
-// is 16 contiguous bytes of a row); products over positions (T Z, K^T V,
-// P V_new) use the stacked-accumulator order of gdr_device.hpp. The state is
-// written to LDS in the first order by the wave that updates it.
+// Contraction orders: products over dk (K S, Q S) take the 32 indices of a
+// block as 8 qd + e for lane quarter qd and element e (so that a fragment is 16
+// contiguous bytes of a row); products over positions (T Z, K^T V, P V_new) use
+// the stacked-accumulator order of gdr_device.hpp. The state is written to LDS
+// in the first order by the wave that updates it.
 template <int DK, int DV>
 __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                        const bf16* __restrict__ v, const f32x2* __restrict__ R, const bf16* __restrict__ Tf,
