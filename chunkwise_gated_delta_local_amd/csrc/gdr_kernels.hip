@@ -713,15 +713,19 @@ __global__ __launch_bounds__(256) void k_output(const T* __restrict__ q, const T
 //                         V_new, and dk tiles of S for the update. This is the
 //                         sequential chain.
 //   output waves (4..7):  wave 4+w forms the output of positions 16w..16w+15.
-//   copy waves   (8..11): move the coming chunks' tiles from global memory
-//                         straight into LDS (16-byte buffer loads to LDS, rows
-//                         past the chunk end read as zero) and do nothing else,
-//                         so no wave that reads LDS ever waits for a copy.
+//   copy waves   (8..11): move the coming chunks' K, Q, score, V and R tiles
+//                         from global memory straight into LDS (16-byte buffer
+//                         loads to LDS, rows past the chunk end read as zero)
+//                         and do nothing else, so no wave that reads LDS ever
+//                         waits for a copy.
+// The state waves load their T fragments for the next chunk straight into
+// registers once T Z has used the current ones (they issue no global stores,
+// so waiting for those loads never waits for a store).
 // Each chunk step has three phases separated by barriers that wait for LDS
 // traffic only (never for global loads or stores):
 //   A  state: S_in (split) from LDS, Y, Z -> LDS; every read of the chunk's
-//             K, Q and T tiles happens here
-//   B  state: Q S_in -> LDS, V_new = T Z -> LDS
+//             K and Q tiles happens here
+//   B  state: Q S_in -> LDS, V_new = T Z -> LDS, next chunk's T -> registers
 //   C  state: S update, S_out (split) -> LDS        output: O -> global
 // K and Q tiles sit in LDS fragment-major: one 1 KB block per (16 rows, 32
 // columns), lane l's 16 bytes at a swizzled slot, so that every matrix-core
@@ -752,14 +756,13 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
     constexpr int FRAG = 512;                   // elements of one fragment block (64 lanes x 8)
     constexpr int TFRAG = kTPairs * 2 * 512;    // T elements per (chunk, head)
     constexpr int NTCP = TFRAG * 2 / 1024;      // 1 KB copies of T per chunk
-    constexpr int MCE = 2 * NKP + NTCP / 4;     // early-list copies per copy wave per chunk
+    constexpr int MCE = 2 * NKP;                // early-list copies per copy wave per chunk
     constexpr int RSRC = 0x00020000;            // buffer descriptor word 3 (raw 32-bit access)
-    static_assert(NTCP % 4 == 0 && NTCP + 3 <= 16, "copy schedule");
+    static_assert(NTCP % 4 == 0, "fragment count");
     // chunk tiles, double-buffered; each half is its own array so that the
     // compiler can tell reads of one half from copies into the other
     __shared__ __attribute__((aligned(16))) T Ks0[4 * NKP * FRAG], Ks1[4 * NKP * FRAG];
     __shared__ __attribute__((aligned(16))) T Qs0[4 * NKP * FRAG], Qs1[4 * NKP * FRAG];
-    __shared__ __attribute__((aligned(16))) T Tb0[TFRAG], Tb1[TFRAG];
     __shared__ __attribute__((aligned(16))) T Pb0[TFRAG], Pb1[TFRAG];
     __shared__ __attribute__((aligned(16))) T Vs0[kChunk * 16], Vs1[kChunk * 16];
     __shared__ __attribute__((aligned(16))) f32x2 Rs0[kChunk], Rs1[kChunk];
@@ -810,6 +813,17 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
         return sp;
     };
     const int64_t sbase = ((int64_t)n * Nv + h) * DK * DV;
+    // split pair fragment p (hi, lo) of a six-pair set (T or the score block) of
+    // chunk c, straight into registers (16 bytes per lane per half)
+    auto load_pair_set = [&](const T* base, int c, int p) {
+        typedef int i4 __attribute__((ext_vector_type(4)));
+        const auto rs = rsrc(base, ((int64_t)c * Nv + h) * TFRAG, 2, TFRAG * 2);
+        Split<T> sp;
+        sp.hi = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rs, (p * 2 * FRAG) * 2 + lane * 16, 0, 0));
+        sp.lo = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rs, (p * 2 * FRAG + FRAG) * 2 + lane * 16,
+                                                                             0, 0));
+        return sp;
+    };
 
     if (wv < 4) {
         // ======================================================== state waves
@@ -856,6 +870,12 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
             return concat<T>(part[0], part[1]);
         };
         if (c0 < c1) {
+            // T pairs of block w for the current chunk, in registers; the next
+            // chunk's are loaded once T Z has used them
+            Split<T> tf[2];
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp)
+                if (tp < ntp) tf[tp] = load_pair_set(Tf, c0, pbase + tp);
             publish_state();
             lds_barrier();
             for (int c = c0; c < c1; ++c) {
@@ -863,7 +883,6 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
                 const int L = chunk_L(c);
                 const T* Kb = odd ? Ks1 : Ks0;
                 const T* Qb = odd ? Qs1 : Qs0;
-                const T* Tbb = odd ? Tb1 : Tb0;
                 const T* Vsb = odd ? Vs1 : Vs0;
                 const f32x2* Rsb = odd ? Rs1 : Rs0;
 
@@ -882,16 +901,8 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
                     rrow[j] = Rsb[w * 16 + 4 * qd + j];
                     vrow[j] = to_f(Vsb[(w * 16 + 4 * qd + j) * 16 + r]);
                 }
-                Split<T> tf[2];
 #pragma unroll
                 for (int kp = 0; kp < NKP; ++kp) qa[kp] = frag(Qb, w, kp);
-#pragma unroll
-                for (int tp = 0; tp < 2; ++tp) {
-                    if (tp < ntp) {
-                        tf[tp].hi = load_frag<T>(&Tbb[(pbase + tp) * 2 * FRAG], lane);
-                        tf[tp].lo = load_frag<T>(&Tbb[(pbase + tp) * 2 * FRAG + FRAG], lane);
-                    }
-                }
                 v8 kt[TPW][2];                          // K^T operands of phase C
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) {
@@ -940,6 +951,11 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
                 store_split_half(Vtb, w >> 1, w & 1, VD);
                 store_split_half(Vb, w >> 1, w & 1, VN);
                 QSx[w][lane] = Qh + Ql;
+                if (c + 1 < c1) {
+#pragma unroll
+                    for (int tp = 0; tp < 2; ++tp)
+                        if (tp < ntp) tf[tp] = load_pair_set(Tf, c + 1, pbase + tp);
+                }
                 lds_barrier();                                                    // barrier 2
 
                 // ---- C: S_out = exp(G_last) S_in + K^T V_decayed for the dk tiles of this wave
@@ -980,11 +996,11 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
     if (wv >= 8) {
         // ======================================================== copy waves
         // Wave 8+w moves its share of each chunk's tiles into LDS. A chunk's
-        // early list (K blocks, Q blocks, T pieces: read only in phase A) is
-        // issued during phases B and C two steps ahead, once the state waves
-        // have finished reading the half it overwrites; its late list (score
-        // pieces, V halves, R: read until phase C) during phase A one step
-        // ahead. Before the last barrier of step c the wave waits for everything
+        // early list (K and Q blocks: read only in phase A) is issued during
+        // phases B and C two steps ahead, once the state waves have finished
+        // reading the half it overwrites; its late list (score pieces, V
+        // halves, R: read until phase C) during phase A one step ahead. (T goes
+        // straight into the state waves' registers.) Before the last barrier of step c the wave waits for everything
         // but the early list of chunk c+2, which may still be in flight (vector
         // memory operations complete in order).
         const int w = wv - 8;
@@ -992,13 +1008,11 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
         auto copy_early = [&](int c, bool odd, int m0, int m1) {
             T* Kd = odd ? Ks1 : Ks0;
             T* Qd = odd ? Qs1 : Qs0;
-            T* Td = odd ? Tb1 : Tb0;
             const int64_t s = chunk_s(c);
             const int L = chunk_L(c);
             const uint32_t kq_bytes = (uint32_t)((L - 1) * Nk * DK + DK) * 2u;
             const auto rk = rsrc(k, (s * Nk + kh) * DK, 2, kq_bytes);
             const auto rq = rsrc(q, (s * Nk + kh) * DK, 2, kq_bytes);
-            const auto rt = rsrc(Tf, ((int64_t)c * Nv + h) * TFRAG, 2, TFRAG * 2);
 #pragma unroll
             for (int m = 0; m < MCE; ++m) {
                 const int u = w + 4 * m;
@@ -1006,21 +1020,18 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
                 if (m < NKP) {                               // K block (tb, kp)
                     const int tb = u / NKP, kp = u % NKP;
                     buffer_to_lds16(rk, Kd + u * FRAG, kq_lane + (16 * tb * Nk * DK + 32 * kp) * 2);
-                } else if (m < 2 * NKP) {                    // Q block
+                } else {                                     // Q block
                     const int f = u - 4 * NKP, tb = f / NKP, kp = f % NKP;
                     buffer_to_lds16(rq, Qd + f * FRAG, kq_lane + (16 * tb * Nk * DK + 32 * kp) * 2);
-                } else {                                     // T piece
-                    const int p = u - 8 * NKP;
-                    buffer_to_lds16(rt, Td + p * FRAG, (p * 64 + lane) * 16);
                 }
             }
         };
         auto copy_late = [&](int c, bool odd) {
-            T* Pd = odd ? Pb1 : Pb0;
             T* Vd = odd ? Vs1 : Vs0;
             f32x2* Rd = odd ? Rs1 : Rs0;
             const int64_t s = chunk_s(c);
             const int L = chunk_L(c);
+            T* Pd = odd ? Pb1 : Pb0;
             const auto rp = rsrc(Pf, ((int64_t)c * Nv + h) * TFRAG, 2, TFRAG * 2);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
@@ -1070,12 +1081,12 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
     lds_barrier();
     for (int c = c0; c < c1; ++c) {
         const bool odd = (c - c0) & 1;
-        const T* Pbb = odd ? Pb1 : Pb0;
         const f32x2* Rsb = odd ? Rs1 : Rs0;
         lds_barrier();                                                              // barrier 1
         lds_barrier();                                                              // barrier 2
 
         // ---- C: O = scale [exp(G) Q S_in + P V_new] for positions 16w..16w+15
+        const T* Pbb = odd ? Pb1 : Pb0;
         Split<T> pa[2], vn[2];
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp) {
@@ -1097,6 +1108,7 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
                 ol = mfma_pair(pa[tp].hi, vn[tp].lo, ol);
             }
         }
+
         const int64_t s = chunk_s(c);
         const int L = chunk_L(c);
         const auto ro = rsrc(o, (s * Nv + h) * DV + nb * 16, ob, (uint32_t)(((L - 1) * Nv * DV + 16) * ob));
