@@ -22,8 +22,8 @@ STAGE_NAMES = ("chunk_table", "gate_cumsum", "build_solve", "wu", "state", "outp
 _DTYPES = {torch.float32: GDR_F32, torch.bfloat16: GDR_BF16}
 
 EXPORTED = ("gdr_validate", "gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd_debug_workspace_size",
-            "gdr_chunk_fwd", "gdr_chunk_fwd_debug", "gdr_chunk_fwd_timed", "gdr_status_string",
-            "gdr_last_error_message")
+            "gdr_chunk_fwd", "gdr_chunk_fwd_debug", "gdr_chunk_fwd_timed", "gdr_recurrent_fwd",
+            "gdr_status_string", "gdr_last_error_message")
 
 
 class Problem(ctypes.Structure):
@@ -67,8 +67,9 @@ def load_library():
     lib.gdr_chunk_fwd.argtypes = fwd_args
     lib.gdr_chunk_fwd_debug.argtypes = fwd_args + [ctypes.POINTER(Intermediates)]
     lib.gdr_chunk_fwd_timed.argtypes = fwd_args + [P]
+    lib.gdr_recurrent_fwd.argtypes = [PP, P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_int, P, P, P]
     for f in ("gdr_validate", "gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd_debug_workspace_size",
-              "gdr_chunk_fwd", "gdr_chunk_fwd_debug", "gdr_chunk_fwd_timed"):
+              "gdr_chunk_fwd", "gdr_chunk_fwd_debug", "gdr_chunk_fwd_timed", "gdr_recurrent_fwd"):
         getattr(lib, f).restype = ctypes.c_int
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_status_string.restype = ctypes.c_char_p
@@ -113,7 +114,7 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 def _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu, chunk_size,
-             output_final_state, out_dtype, debug=False):
+             output_final_state, out_dtype, debug=False, workspace=True):
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:2] != q.shape[:2]:
         raise ValueError("expected q, k [B,T,Nk,dk] and v [B,T,Nv,dv]")
     dev = q.device
@@ -150,6 +151,8 @@ def _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu,
                         _DTYPES[out_dtype])
     o = torch.empty(v.shape, dtype=out_dtype, device=dev)
     S_T = torch.empty((N, Nv, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
+    if not workspace:                         # token-by-token path: no workspace
+        return prob, o, S_T, cu_dev, cu_host, scale
     ws = torch.empty(workspace_size(prob, debug), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     args = [ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), ctypes.c_float(scale),
@@ -169,6 +172,25 @@ def chunk_fwd(q, k, v, beta, g=None, scale=None, initial_state=None, output_fina
                                         chunk_size, output_final_state, out_dtype)
     _check(lib.gdr_chunk_fwd(*args))
     del keep
+    return o, S_T
+
+
+def recurrent_fwd(q, k, v, beta, g=None, scale=None, initial_state=None, output_final_state=True,
+                  cu_seqlens=None, cu_seqlens_cpu=None, use_qk_l2norm_in_kernel=False, out_dtype=None):
+    """Token-by-token (fused recurrent) gated delta-rule forward: the same
+    result as chunk_fwd, for decoding and short inputs. Returns (o, final_state
+    or None). use_qk_l2norm_in_kernel: q and k are L2-normalised per token
+    inside the kernel."""
+    lib = load_library()
+    prob, o, S_T, cu_dev, cu_host, scale = _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens,
+                                                    cu_seqlens_cpu, 64, output_final_state, out_dtype,
+                                                    workspace=False)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib.gdr_recurrent_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 ctypes.c_float(scale), _ptr(initial_state), _ptr(cu_dev), _ptr(cu_host),
+                                 ctypes.c_int(1 if use_qk_l2norm_in_kernel else 0), _ptr(o), _ptr(S_T),
+                                 ctypes.c_void_p(stream)))
+    del cu_dev, cu_host
     return o, S_T
 
 

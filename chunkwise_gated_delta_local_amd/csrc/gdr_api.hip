@@ -287,4 +287,43 @@ const char* gdr_status_string(gdr_status_t s) {
 
 const char* gdr_last_error_message(void) { return g_err; }
 
+gdr_status_t gdr_recurrent_fwd(const gdr_problem_t* p, const void* q, const void* k, const void* v, const float* g,
+                               const void* beta, float scale, const float* initial_state, const int32_t* cu_dev,
+                               const int32_t* cu_host, int use_qk_l2norm, void* o, float* final_state,
+                               void* stream) {
+    if (!p) return fail(GDR_ERR_NULL, "problem is NULL");
+    gdr_problem_t pc = *p;
+    pc.chunk_size = 64;                        // not used by the token-by-token path
+    gdr_status_t st = check_problem(&pc);
+    if (st != GDR_OK) return st;
+    if ((cu_dev == nullptr) != (cu_host == nullptr))
+        return fail(GDR_ERR_NULL, "cu_seqlens_dev and cu_seqlens_host must both be given or both be NULL");
+    st = check_seqlens(&pc, cu_host, cu_host != nullptr);
+    if (st != GDR_OK) return st;
+    const int64_t Ttot = pc.batch * pc.seq_len;
+    if (Ttot > 0 && (!q || !k || !v || !beta || !o))
+        return fail(GDR_ERR_NULL, "q, k, v, beta and o are required");
+    gdr::RecurrentArgs a;
+    a.bf16 = pc.io_dtype == GDR_BF16;
+    a.dk = pc.head_dim_qk;
+    a.dv = pc.head_dim_v;
+    a.Nk = pc.num_qk_heads;
+    a.Nv = pc.num_v_heads;
+    a.N = pc.num_seqs;
+    a.T_row = pc.seq_len;
+    a.Ttot = Ttot;
+    a.q = q; a.k = k; a.v = v; a.beta = beta;
+    a.beta_f32 = pc.beta_dtype == GDR_F32;
+    a.out_f32 = pc.out_dtype == GDR_F32;
+    a.l2norm = use_qk_l2norm ? 1 : 0;
+    a.g = g; a.S0 = initial_state; a.scale = scale;
+    a.cu_dev = cu_dev;
+    a.o = o; a.ST = final_state;
+    a.stream = static_cast<hipStream_t>(stream);
+    hipError_t e = gdr::launch_recurrent(a);
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    g_err[0] = '\0';
+    return GDR_OK;
+}
+
 }  // extern "C"

@@ -159,8 +159,8 @@ __device__ __forceinline__ void store_pair_half(T* base, int lane, int half, con
 template <typename T> struct Split {
     typename Vec<T>::v8 hi, lo;
 };
-template <typename T> constexpr bool kSplitNeeded = false;
-template <> constexpr bool kSplitNeeded<bf16> = true;
+template <typename T> inline constexpr bool kSplitNeeded = false;
+template <> inline constexpr bool kSplitNeeded<bf16> = true;
 
 // fp32 values -> hi/lo pair fragment (lo unused for fp32)
 template <typename T>

@@ -38,4 +38,22 @@ struct LaunchArgs {
 // before the first and after every one of the six stages.
 hipError_t launch_forward(const LaunchArgs& a, hipEvent_t* events);
 
+// Token-by-token forward (gdr_recurrent.hip): no workspace.
+struct RecurrentArgs {
+    bool bf16;
+    int dk, dv;
+    int32_t Nk, Nv, N;
+    int64_t T_row, Ttot;
+    const void *q, *k, *v, *beta;
+    int beta_f32, out_f32, l2norm;
+    const float* g;
+    const float* S0;
+    float scale;
+    const int32_t* cu_dev;     // NULL: fixed length T_row per sequence
+    void* o;
+    float* ST;
+    hipStream_t stream;
+};
+hipError_t launch_recurrent(const RecurrentArgs& a);
+
 }  // namespace gdr

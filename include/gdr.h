@@ -114,6 +114,28 @@ gdr_status_t gdr_chunk_fwd_workspace_size(const gdr_problem_t* problem, size_t* 
 gdr_status_t gdr_chunk_fwd_debug_workspace_size(const gdr_problem_t* problem, size_t* bytes);
 
 /*
+ * Token-by-token (fused recurrent) gated delta-rule forward: the same result
+ * as gdr_chunk_fwd, computed one token at a time with the state on chip, for
+ * decoding and short inputs (FLA notes page, "fused recurrent fwd"; the model
+ * layer there takes this path for queries of at most 64 tokens).
+ *   Arguments as for gdr_chunk_fwd; problem->chunk_size is ignored and no
+ *   workspace is needed.
+ *   use_qk_l2norm  nonzero: q and k of every token are divided by
+ *                  sqrt(sum of squares + 1e-6) inside the kernel before use
+ *                  (the in-kernel L2 normalisation option of the FLA
+ *                  DeltaNet article, section 5); the caller's tensors are not
+ *                  modified.
+ * Errors as for gdr_chunk_fwd. Asynchronous on `stream`.
+ */
+gdr_status_t gdr_recurrent_fwd(const gdr_problem_t* problem,
+                               const void* q, const void* k, const void* v,
+                               const float* g, const void* beta, float scale,
+                               const float* initial_state,
+                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                               int use_qk_l2norm,
+                               void* o, float* final_state, void* stream);
+
+/*
  * Chunked gated delta-rule forward.
  *   q, k, v, beta  required inputs (layouts above).
  *   g              NULL for the ungated rule (identical to g == 0).

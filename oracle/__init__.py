@@ -13,9 +13,13 @@ Two independent forms of the method:
 * ``chunked_forward`` (NumPy, ``chunked.py``): the WY / UT chunk algorithm,
   step by step, emitting the per-step intermediates G, A, W, U, h, V_new.
 
-Both are pinned by the CPU tests in ``tests/test_oracle_*.py`` against closed
+``normalize.l2_normalize`` is the optional per-vector L2 normalisation of q
+and k that the token-by-token forward can apply first.
+
+All are pinned by the CPU tests in ``tests/test_oracle_*.py`` against closed
 forms, identities and brute-force products fixed by the pages and by algebra.
 Every function is pinned; none is "parity unpinned".
 """
 from .recurrence import recurrence, build  # noqa: F401
 from .chunked import chunked_forward  # noqa: F401
+from .normalize import l2_normalize  # noqa: F401

@@ -392,3 +392,23 @@ def test_intermediates_layout_and_consistency():
     assert np.allclose(A_tail[:, :, 36:], 0)
     for i in range(36):
         assert np.allclose(A_tail[i, :, i + 1:], 0) and np.allclose(A_tail[i, :, i], 1)
+
+
+# ---------------------------------------------------------------- L2 normalisation of q, k (token-by-token option)
+def test_l2_normalize_pins():
+    from oracle import l2_normalize
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((5, 3, 64))
+    # eps = 0: the textbook unit vector x / ||x|| (NumPy's norm as an independent routine)
+    ref = x / np.linalg.norm(x, axis=-1, keepdims=True)
+    assert np.max(np.abs(l2_normalize(x, eps=0.0) - ref)) < 1e-15
+    # unit length, and invariant to positive scaling
+    assert np.allclose(np.linalg.norm(l2_normalize(x, eps=0.0), axis=-1), 1.0, atol=1e-15)
+    assert np.max(np.abs(l2_normalize(7.5 * x, eps=0.0) - l2_normalize(x, eps=0.0))) < 1e-15
+    # default eps: the norm falls short of one by eps / (2 ||x||^2) to first order
+    n2 = np.sum(x * x, axis=-1)
+    got = np.linalg.norm(l2_normalize(x), axis=-1)
+    assert np.allclose(got, 1.0 - 1e-6 / (2 * n2), rtol=0, atol=1e-13)
+    # a zero vector stays zero (no division by zero)
+    z = l2_normalize(np.zeros((2, 8)))
+    assert np.all(z == 0.0)
