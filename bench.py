@@ -224,6 +224,48 @@ def counter_summary(src: str, out_dir: str, workload: int) -> None:
         print(path)
 
 
+def bench_recurrent(args) -> None:
+    """One decode step per bench step: --decode-seqs sequences of one token each,
+    16 q/k heads, 32 value heads, dk = dv = 128, bf16, from a random fp32 state,
+    with the final state written. The step moves the state in and out of HBM;
+    the roofline is the token-by-token kernel's bytes over its HIP-event time."""
+    Nseq = args.decode_seqs
+    w = synth.custom("decode-%dseq-Nk16-Nv32-d128" % Nseq, B=1, T=0, Nk=16, Nv=32, dk=128, dv=128, dtype="bf16",
+                     g_mean=6.0, s0="randn", lengths=tuple([1] * Nseq))
+    inp = synth.generate(w, seed=7)
+    dev = torch.device("cuda:0")
+    d = {k: (None if inp[k] is None else inp[k].to(dev)) for k in ("q", "k", "v", "beta", "g", "S0", "cu_seqlens")}
+    run = lambda: api.recurrent_fwd(d["q"], d["k"], d["v"], d["beta"], g=d["g"], scale=inp["scale"],
+                                    initial_state=d["S0"], output_final_state=True, cu_seqlens=d["cu_seqlens"],
+                                    cu_seqlens_cpu=inp["cu_seqlens"])
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    K = args.steps
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(K):
+        run()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / K
+    state = Nseq * w.Nv * w.dk * w.dv * 4
+    io = Nseq * (2 * w.Nk * w.dk * 2 + w.Nv * (w.dv * 2 + 2 + 4) + w.Nv * w.dv * 2)   # q, k, v, beta, g in; o out
+    alg = 2 * state + io
+    achieved = alg / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "decode tokens/s (token-by-token forward), %d sequences" % Nseq,
+        "value": Nseq / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "seqs": Nseq, "Nk": w.Nk, "Nv": w.Nv, "dk": w.dk, "dv": w.dv, "seed": 7},
+        "roofline": {"bound": "hbm", "kernel": "k_recurrent", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": alg,
+                     "avg_ms": ms},
+        "cpu_baseline": None,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,6 +276,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget; 0 skips it")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB three times (calibrates HBM byte counters)")
+    ap.add_argument("--mode", choices=("chunk", "recurrent"), default="chunk",
+                    help="chunk: the chunked forward on --workload (default); recurrent: one decode step "
+                         "(token-by-token kernel) for --decode-seqs sequences from a random state")
+    ap.add_argument("--decode-seqs", type=int, default=64)
     ap.add_argument("--counter-summary", metavar="DIR",
                     help="only summarise rocprofv3 counter runs found under DIR (fetch/, write/, cfetch/, cwrite/) "
                          "into one text file per kernel, written to --summary-out")
@@ -252,6 +298,9 @@ def main():
 
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib)
+        return
+    if args.mode == "recurrent":
+        bench_recurrent(args)
         return
 
     w = synth.WORKLOADS[args.workload]
