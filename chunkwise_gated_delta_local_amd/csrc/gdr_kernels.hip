@@ -1071,6 +1071,11 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
     }
 
     // ============================================================ output waves
+    // The output of chunk c is formed in phase A of step c+1 (after the loop for
+    // the last chunk): its operands V_new and Q S_in stay in the exchange buffers
+    // until phase B of step c+1, and the score pairs and exp(G) are taken into
+    // registers in phase B of step c, before the copy waves overwrite that LDS
+    // half with chunk c+2.
     const int w = wv - 4;
     const int ntp = (w >> 1) + 1;
     const int ob = out_f32 ? 4 : 2;
@@ -1078,28 +1083,17 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
 #pragma unroll
     for (int j = 0; j < 4; ++j) o_off[j] = ((w * 16 + 4 * qd + j) * Nv * DV + r) * ob;
     const int pbase = (w == 0) ? 0 : (w == 1 ? 1 : (w == 2 ? 2 : 4));
-    lds_barrier();
-    for (int c = c0; c < c1; ++c) {
-        const bool odd = (c - c0) & 1;
-        const f32x2* Rsb = odd ? Rs1 : Rs0;
-        lds_barrier();                                                              // barrier 1
-        lds_barrier();                                                              // barrier 2
-
-        // ---- C: O = scale [exp(G) Q S_in + P V_new] for positions 16w..16w+15
-        const T* Pbb = odd ? Pb1 : Pb0;
-        Split<T> pa[2], vn[2];
+    Split<T> pa[2];                                  // score pairs of the pending chunk
+    float ex[4];                                     // exp(G) of its rows
+    auto output = [&](int c) {                       // O = scale [exp(G) Q S_in + P V_new], positions 16w..
+        Split<T> vn[2];
 #pragma unroll
-        for (int tp = 0; tp < 2; ++tp) {
-            if (tp < ntp) {
-                pa[tp].hi = load_frag<T>(&Pbb[(pbase + tp) * 2 * FRAG], lane);
-                pa[tp].lo = load_frag<T>(&Pbb[(pbase + tp) * 2 * FRAG + FRAG], lane);
-                vn[tp] = load_split(Vb, tp);
-            }
-        }
+        for (int tp = 0; tp < 2; ++tp)
+            if (tp < ntp) vn[tp] = load_split(Vb, tp);
         const f32x4 qs = QSx[w][lane];
         f32x4 out, ol = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) out[j] = Rsb[w * 16 + 4 * qd + j].x * qs[j];
+        for (int j = 0; j < 4; ++j) out[j] = ex[j] * qs[j];
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp) {
             if (tp < ntp) {
@@ -1108,7 +1102,6 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
                 ol = mfma_pair(pa[tp].hi, vn[tp].lo, ol);
             }
         }
-
         const int64_t s = chunk_s(c);
         const int L = chunk_L(c);
         const auto ro = rsrc(o, (s * Nv + h) * DV + nb * 16, ob, (uint32_t)(((L - 1) * Nv * DV + 16) * ob));
@@ -1119,8 +1112,31 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
             else __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, to_t<T>(val)), ro,
                                                        o_off[j], 0, 0);
         }
+    };
+    lds_barrier();
+    for (int c = c0; c < c1; ++c) {
+        const bool odd = (c - c0) & 1;
+
+        // ---- A: output of the previous chunk
+        if (c > c0) output(c - 1);
+        lds_barrier();                                                              // barrier 1
+
+        // ---- B: this chunk's score pairs and exp(G) into registers
+        const T* Pbb = odd ? Pb1 : Pb0;
+        const f32x2* Rsb = odd ? Rs1 : Rs0;
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+            if (tp < ntp) {
+                pa[tp].hi = load_frag<T>(&Pbb[(pbase + tp) * 2 * FRAG], lane);
+                pa[tp].lo = load_frag<T>(&Pbb[(pbase + tp) * 2 * FRAG + FRAG], lane);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ex[j] = Rsb[w * 16 + 4 * qd + j].x;
+        lds_barrier();                                                              // barrier 2
         lds_barrier();                                                              // barrier 3
     }
+    output(c1 - 1);
 }
 // ============================================================ launchers
 template <typename T, int DK, int DV>

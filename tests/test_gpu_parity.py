@@ -93,6 +93,16 @@ EDGE = [
 ]
 
 
+@pytest.mark.parametrize("dk", [32, 64, 128])
+@pytest.mark.parametrize("dv", [32, 64, 128])
+def test_every_head_dim_pair_bf16(dk, dv):
+    """Every (dk, dv) instantiation of the fused path: several chunks, a tail,
+    GQA, an initial state."""
+    w = synth.custom("dims_%d_%d" % (dk, dv), B=2, T=150, Nk=1, Nv=2, dk=dk, dv=dv, dtype="bf16", s0="randn")
+    inp = synth.generate(w, seed=dk + dv)
+    check_run(inp, oracle_reference(inp), TOL["bf16"], "dims(%d,%d)" % (dk, dv))
+
+
 @pytest.mark.parametrize("name,kw", EDGE, ids=[e[0] for e in EDGE])
 def test_edge_cases(name, kw):
     w = synth.custom(name, **kw)
