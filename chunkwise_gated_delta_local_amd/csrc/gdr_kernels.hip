@@ -175,19 +175,35 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
     // The K and Q tiles are only needed until the K K^T and Q K^T tiles are in
     // registers; L and A reuse their LDS afterwards.
     constexpr int TILE_BYTES = 2 * kChunk * KP * (int)sizeof(T);
-    constexpr int LA_BYTES = 2 * kChunk * (kChunk + 1) * 4;
+    constexpr int LP = kChunk + 4;             // L and A row pitch (floats): 16-byte aligned rows
+    constexpr int LA_BYTES = 2 * kChunk * LP * 4;
     __shared__ __attribute__((aligned(16))) char smem[TILE_BYTES > LA_BYTES ? TILE_BYTES : LA_BYTES];
-    __shared__ float bs[kChunk], gs[kChunk];
+    __shared__ __attribute__((aligned(16))) float bs[kChunk], gs[kChunk];
     T* Ks = reinterpret_cast<T*>(smem);
     T* Qs = Ks + kChunk * KP;
-    float (*Lf)[kChunk + 1] = reinterpret_cast<float (*)[kChunk + 1]>(smem);
-    float (*Af)[kChunk + 1] = Lf + kChunk;
+    float (*Lf)[LP] = reinterpret_cast<float (*)[LP]>(smem);
+    float (*Af)[LP] = Lf + kChunk;
 
     const int c = blockIdx.x, kh = blockIdx.y;
     const int64_t s = chunk_start[c];
     const int L = chunk_len[c];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, qd = lane >> 4;
     typedef typename Vec<T>::v8 v8;
+
+    const int group = Nv / Nk;
+    // beta and G of a value head go through registers: head 0's are fetched with
+    // the tiles, each next head's while the current one is processed
+    float b_nx = 0.f, g_nx = 0.f;
+    auto fetch_gates = [&](int hh) {
+        const int h = kh * group + hh;
+        if (tid < kChunk && tid < L) {
+            b_nx = load_beta(beta, (s + tid) * Nv + h, beta_f32);
+            g_nx = G[(s + tid) * Nv + h];
+        } else {
+            b_nx = 0.f;
+            g_nx = 0.f;
+        }
+    };
 
     // 1. K (and Q) rows of the chunk (zero past the chunk end): all loads first
     {
@@ -202,6 +218,7 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
                 if (Pf) qv[i] = *reinterpret_cast<const v8*>(q + ((s + row) * Nk + kh) * DK + seg * 8);
             }
         }
+        fetch_gates(0);
 #pragma unroll
         for (int i = 0; i < SEGS; ++i) {
             const int idx = tid + 256 * i, row = idx / (DK / 8), seg = idx % (DK / 8);
@@ -246,14 +263,14 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
         Af[row][col] = 0.f;
     }
 
-    const int group = Nv / Nk;
     for (int hh = 0; hh < group; ++hh) {
         const int h = kh * group + hh;
         if (tid < kChunk) {
-            bs[tid] = tid < L ? load_beta(beta, (s + tid) * Nv + h, beta_f32) : 0.f;
-            gs[tid] = tid < L ? G[(s + tid) * Nv + h] : 0.f;
+            bs[tid] = b_nx;
+            gs[tid] = g_nx;
         }
         __syncthreads();
+        if (hh + 1 < group) fetch_gates(hh + 1);
 
         // 2. strictly lower L (every entry of the blocks on and below the diagonal)
 #pragma unroll
@@ -270,9 +287,15 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
         }
         __syncthreads();
 
-        // 3. diagonal block `wave`: lane r < 16 owns column r of the block.
-        if (lane < 16) {
+        // 3. diagonal block `wave`: lane r < 16 owns column r of the block. Lane i
+        //    holds row i of the block's L in registers; each substitution step
+        //    takes L[i][m] from lane i (a wave-uniform value), so the recursion
+        //    reads LDS only once per row.
+        {
             const int b0 = wave * 16;
+            float lrow[16];
+#pragma unroll
+            for (int m = 0; m < 16; ++m) lrow[m] = Lf[b0 + r][b0 + m];
             float x[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) x[i] = (i == lane) ? 1.f : 0.f;
@@ -280,11 +303,14 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
             for (int i = 1; i < 16; ++i) {
                 float acc = 0.f;
 #pragma unroll
-                for (int m = 0; m < i; ++m) acc += Lf[b0 + i][b0 + m] * x[m];
+                for (int m = 0; m < i; ++m)
+                    acc += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lrow[m]), i)) * x[m];
                 if (i > lane) x[i] = -acc;
             }
+            if (lane < 16) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) Af[b0 + i][b0 + lane] = x[i];
+                for (int i = 0; i < 16; ++i) Af[b0 + i][b0 + lane] = x[i];
+            }
         }
         __syncthreads();
 
@@ -351,11 +377,16 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
             for (int p = wave; p < kTPairs; p += 4) {
                 const int tb = kTPairTb[p], tp = kTPairTp[p];
                 const int row = tb * 16 + r;
+                const int m0 = tp * 32 + 4 * qd;           // positions m0..m0+3 and m0+16..m0+19
+                const f32x4 a0 = *reinterpret_cast<const f32x4*>(&Af[row][m0]);
+                const f32x4 a1 = *reinterpret_cast<const f32x4*>(&Af[row][m0 + 16]);
+                const f32x4 b0 = *reinterpret_cast<const f32x4*>(&bs[m0]);
+                const f32x4 b1 = *reinterpret_cast<const f32x4*>(&bs[m0 + 16]);
                 float x[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int m = tp * 32 + (e < 4 ? 4 * qd + e : 16 + 4 * qd + e - 4);
-                    x[e] = (row < L && m <= row) ? Af[row][m] * bs[m] : 0.f;
+                for (int e = 0; e < 4; ++e) {
+                    x[e] = (row < L && m0 + e <= row) ? a0[e] * b0[e] : 0.f;
+                    x[4 + e] = (row < L && m0 + 16 + e <= row) ? a1[e] * b1[e] : 0.f;
                 }
                 const Split<T> sp = split8<T>(x);
                 T* dst = Tf + (((int64_t)c * Nv + h) * kTPairs + p) * 2 * 512;
