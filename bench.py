@@ -32,6 +32,7 @@ from chunkwise_gated_delta_local_amd import api, synth  # noqa: E402
 METRIC = "fwd tokens/s at Hv=32,dk=dv=128,T=64k bf16; % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ("chunkwise_gated_delta_local_amd/csrc/gdr_kernels.hip",
+                  "chunkwise_gated_delta_local_amd/csrc/gdr_recurrent.hip",
                   "chunkwise_gated_delta_local_amd/csrc/gdr_device.hpp")
 STAGE_KERNELS = ("k_chunk_table", "k_gate_cumsum", "k_build_solve", "k_wu", "k_state", "k_output")
 FUSED_STAGE_KERNELS = ("k_chunk_table", "k_gate_cumsum", "k_build_solve", "(fused)", "k_state_output", "(fused)")
@@ -180,7 +181,17 @@ def counter_summary(src: str, out_dir: str, workload: int) -> None:
                 if fn.endswith("counter_collection.csv"):
                     return os.path.join(root, fn)
         raise FileNotFoundError(os.path.join(src, sub))
-    fetch, write = _counter_means(csv_of("fetch"), "FETCH_SIZE"), _counter_means(csv_of("write"), "WRITE_SIZE")
+    jobs = [("fetch", "write", "T65536_Nk16_Nv32_d128" if workload == 5 else "workload%d" % workload,
+             "python3 bench.py --steps 3 --warmup 1 --cpu-seconds 0")]
+    if os.path.isdir(os.path.join(src, "rfetch")) and os.path.isdir(os.path.join(src, "rwrite")):
+        jobs.append(("rfetch", "rwrite", "decode256_Nk16_Nv32_d128",
+                     "python3 bench.py --mode recurrent --decode-seqs 256 --steps 3 --warmup 1"))
+    for fdir, wdir, wl, cmd in jobs:
+        _counter_summary_one(src, out_dir, csv_of, fdir, wdir, wl, cmd)
+
+
+def _counter_summary_one(src, out_dir, csv_of, fdir, wdir, wl, cmd):
+    fetch, write = _counter_means(csv_of(fdir), "FETCH_SIZE"), _counter_means(csv_of(wdir), "WRITE_SIZE")
     cfetch, cwrite = _counter_means(csv_of("cfetch"), "FETCH_SIZE"), _counter_means(csv_of("cwrite"), "WRITE_SIZE")
     probe = [n for n in cfetch if "neg_kernel" in n]
     if not probe:
@@ -188,10 +199,10 @@ def counter_summary(src: str, out_dir: str, workload: int) -> None:
     probe_kib = 1024 * 1024.0                            # --copy-probe-mib 1024: 1 GiB read and 1 GiB written
     f_scale = probe_kib / cfetch[probe[0]]
     w_scale = probe_kib / cwrite[probe[0]]
-    wl = "T65536_Nk16_Nv32_d128" if workload == 5 else "workload%d" % workload
     os.makedirs(out_dir, exist_ok=True)
     for name in sorted(fetch):
-        short = next((k for k in sorted(STAGE_KERNELS + ("k_state_output",), key=len, reverse=True) if k in name), None)
+        short = next((k for k in sorted(STAGE_KERNELS + ("k_state_output", "k_recurrent"), key=len, reverse=True)
+                      if k in name), None)
         if short is None or name not in write:
             continue
         fb, wb = fetch[name] * f_scale * 1024.0, write[name] * w_scale * 1024.0
@@ -199,10 +210,8 @@ def counter_summary(src: str, out_dir: str, workload: int) -> None:
         with open(path, "w") as f:
             f.write("# HBM traffic of %s, workload %s (one forward per bench step)\n" % (short, wl))
             f.write("# commands (run from the repository root):\n")
-            f.write("#   rocprofv3 --pmc FETCH_SIZE -d <dir>/fetch -o run --output-format csv -- "
-                    "python3 bench.py --steps 3 --warmup 1 --cpu-seconds 0\n")
-            f.write("#   rocprofv3 --pmc WRITE_SIZE -d <dir>/write -o run --output-format csv -- "
-                    "python3 bench.py --steps 3 --warmup 1 --cpu-seconds 0\n")
+            f.write("#   rocprofv3 --pmc FETCH_SIZE -d <dir>/%s -o run --output-format csv -- %s\n" % (fdir, cmd))
+            f.write("#   rocprofv3 --pmc WRITE_SIZE -d <dir>/%s -o run --output-format csv -- %s\n" % (wdir, cmd))
             f.write("#   rocprofv3 --pmc FETCH_SIZE -d <dir>/cfetch -o run --output-format csv -- "
                     "python3 bench.py --copy-probe-mib 1024\n")
             f.write("#   rocprofv3 --pmc WRITE_SIZE -d <dir>/cwrite -o run --output-format csv -- "
@@ -260,7 +269,9 @@ def bench_recurrent(args) -> None:
         "data": "synthetic",
         "config": {"workload": w.name, "seqs": Nseq, "Nk": w.Nk, "Nv": w.Nv, "dk": w.dk, "dv": w.dv, "seed": 7},
         "roofline": {"bound": "hbm", "kernel": "k_recurrent", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": alg,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": counter_traffic("k_recurrent", "decode%d_Nk16_Nv32_d128" % Nseq),
+                     "algorithmic_bytes": alg,
                      "avg_ms": ms},
         "cpu_baseline": None,
     }), flush=True)
