@@ -277,6 +277,84 @@ def bench_recurrent(args) -> None:
     }), flush=True)
 
 
+def _time_forward(fwd, K, W):
+    """Mean ms per forward and per stage (HIP events) over K timed calls."""
+    for _ in range(W):
+        fwd()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(api.NUM_STAGES + 1)] for _ in range(K)]
+    for row in events:
+        for e in row:
+            e.record()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(K):
+        fwd.timed(events[s])
+    end.record()
+    torch.cuda.synchronize()
+    stage_ms = np.array([[events[s][i].elapsed_time(events[s][i + 1]) for i in range(api.NUM_STAGES)]
+                         for s in range(K)]).mean(axis=0)
+    return start.elapsed_time(end) / K, stage_ms
+
+
+def bench_segmented(args) -> None:
+    """Segment-parallel state passing against the serial pass on one long
+    sequence with few heads (64k tokens, 2 q/k heads, 4 value heads, dk = dv =
+    128, bf16): the serial state pass has 4 x 8 = 32 workgroups for 256 compute
+    units. Reports the segmented forward (--segment-chunks, 0 = the library's
+    choice), the serial forward, a sweep of segment lengths, and the largest
+    difference between the two outputs."""
+    w = synth.custom("long-1seq-Nk2-Nv4-T65536-d128", B=1, T=65536, Nk=2, Nv=4, dk=128, dv=128, dtype="bf16",
+                     g_mean=6.0, s0="zero")
+    inp = synth.generate(w, seed=8)
+    dev = torch.device("cuda:0")
+    d = {k: (None if inp[k] is None else inp[k].to(dev)) for k in ("q", "k", "v", "beta", "g", "S0")}
+    make = lambda sc: api.Forward(d["q"], d["k"], d["v"], d["beta"], g=d["g"], scale=inp["scale"],
+                                  initial_state=d["S0"], output_final_state=True, segment_chunks=sc)
+    K, W = args.steps, args.warmup
+    serial = make(None)
+    ms_serial, st_serial = _time_forward(serial, K, W)
+    seg = make(args.segment_chunks)
+    ms_seg, st_seg = _time_forward(seg, K, W)
+    torch.cuda.synchronize()
+    # the outputs are bf16: their difference is counted in bf16 steps (spacing at the larger value)
+    o_a, o_b = serial.o.float(), seg.o.float()
+    mag = torch.maximum(o_a.abs(), o_b.abs())
+    step = torch.where(mag > 0, torch.exp2(torch.floor(torch.log2(mag)) - 7), torch.ones_like(mag))
+    diff_o = float(((o_a - o_b).abs() / step).max())
+    diff_s = float((serial.final_state - seg.final_state).abs().max()) / float(
+        serial.final_state.pow(2).mean().sqrt())
+    sweep = {}
+    for sc in (16, 32, 64, 128, 256):
+        f = make(sc)
+        sweep[str(sc)] = _time_forward(f, max(5, K // 4), 2)[0]
+        del f
+    Ttot = w.T
+    NT = Ttot // 64
+    alg = stage_algorithmic_bytes(w, Ttot, 1, NT, 2, False)["k_state_output"]
+    achieved = alg / (st_seg[4] * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "fwd tokens/s, one 64k-token sequence with 4 value heads (segment-parallel state passing)",
+        "value": Ttot / (ms_seg * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": ms_seg, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": Ttot, "Nk": w.Nk, "Nv": w.Nv, "dk": w.dk, "dv": w.dv, "chunk": 64,
+                   "segment_chunks": args.segment_chunks, "seed": 8},
+        "serial": {"ms_per_step": ms_serial, "value": Ttot / (ms_serial * 1e-3),
+                   "state_stage_ms": float(st_serial[4])},
+        "speedup_vs_serial": ms_serial / ms_seg,
+        "state_stage_ms": float(st_seg[4]),
+        "stage_ms": {("%d:%s" % (i, api.STAGE_NAMES[i])): float(st_seg[i]) for i in range(api.NUM_STAGES)},
+        "sweep_ms_per_step": sweep,
+        "diff_vs_serial": {"o_max_bf16_steps": diff_o, "S_T_max_over_rms": diff_s},
+        "roofline": {"bound": "hbm", "kernel": "state stage (two side-by-side passes, scan, output pass)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes": alg, "avg_ms": float(st_seg[4])},
+        "cpu_baseline": None,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -287,9 +365,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget; 0 skips it")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB three times (calibrates HBM byte counters)")
-    ap.add_argument("--mode", choices=("chunk", "recurrent"), default="chunk",
+    ap.add_argument("--mode", choices=("chunk", "recurrent", "segmented"), default="chunk",
                     help="chunk: the chunked forward on --workload (default); recurrent: one decode step "
-                         "(token-by-token kernel) for --decode-seqs sequences from a random state")
+                         "(token-by-token kernel) for --decode-seqs sequences from a random state; segmented: "
+                         "segment-parallel against serial state passing on one long sequence with few heads")
+    ap.add_argument("--segment-chunks", type=int, default=0,
+                    help="chunks per segment in --mode segmented (0: the library's choice)")
     ap.add_argument("--decode-seqs", type=int, default=64)
     ap.add_argument("--counter-summary", metavar="DIR",
                     help="only summarise rocprofv3 counter runs found under DIR (fetch/, write/, cfetch/, cwrite/) "
@@ -312,6 +393,9 @@ def main():
         return
     if args.mode == "recurrent":
         bench_recurrent(args)
+        return
+    if args.mode == "segmented":
+        bench_segmented(args)
         return
 
     w = synth.WORKLOADS[args.workload]

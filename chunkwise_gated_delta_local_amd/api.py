@@ -23,6 +23,7 @@ _DTYPES = {torch.float32: GDR_F32, torch.bfloat16: GDR_BF16}
 
 EXPORTED = ("gdr_validate", "gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd_debug_workspace_size",
             "gdr_chunk_fwd", "gdr_chunk_fwd_debug", "gdr_chunk_fwd_timed", "gdr_recurrent_fwd",
+            "gdr_chunk_fwd_segmented_workspace_size", "gdr_chunk_fwd_segmented",
             "gdr_status_string", "gdr_last_error_message")
 
 
@@ -68,8 +69,11 @@ def load_library():
     lib.gdr_chunk_fwd_debug.argtypes = fwd_args + [ctypes.POINTER(Intermediates)]
     lib.gdr_chunk_fwd_timed.argtypes = fwd_args + [P]
     lib.gdr_recurrent_fwd.argtypes = [PP, P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_int, P, P, P]
+    lib.gdr_chunk_fwd_segmented_workspace_size.argtypes = [PP, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdr_chunk_fwd_segmented.argtypes = fwd_args[:12] + [ctypes.c_int32] + fwd_args[12:] + [P]
     for f in ("gdr_validate", "gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd_debug_workspace_size",
-              "gdr_chunk_fwd", "gdr_chunk_fwd_debug", "gdr_chunk_fwd_timed", "gdr_recurrent_fwd"):
+              "gdr_chunk_fwd", "gdr_chunk_fwd_debug", "gdr_chunk_fwd_timed", "gdr_recurrent_fwd",
+              "gdr_chunk_fwd_segmented_workspace_size", "gdr_chunk_fwd_segmented"):
         getattr(lib, f).restype = ctypes.c_int
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_status_string.restype = ctypes.c_char_p
@@ -101,9 +105,15 @@ def validate(problem: Problem, cu_seqlens_host=None) -> int:
     return lib.gdr_validate(ctypes.byref(problem), None if cu is None else ctypes.c_void_p(cu.data_ptr()))
 
 
-def workspace_size(problem: Problem, debug: bool = False) -> int:
+def workspace_size(problem: Problem, debug: bool = False, segment_chunks: Optional[int] = None) -> int:
+    """Workspace bytes of gdr_chunk_fwd, of gdr_chunk_fwd_debug (debug), or of
+    gdr_chunk_fwd_segmented with that segment_chunks (0: automatic)."""
     lib = load_library()
     n = ctypes.c_size_t(0)
+    if segment_chunks is not None:
+        _check(lib.gdr_chunk_fwd_segmented_workspace_size(ctypes.byref(problem), ctypes.c_int32(segment_chunks),
+                                                          ctypes.byref(n)))
+        return int(n.value)
     fn = lib.gdr_chunk_fwd_debug_workspace_size if debug else lib.gdr_chunk_fwd_workspace_size
     _check(fn(ctypes.byref(problem), ctypes.byref(n)))
     return int(n.value)
@@ -114,7 +124,7 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 def _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu, chunk_size,
-             output_final_state, out_dtype, debug=False, workspace=True):
+             output_final_state, out_dtype, debug=False, workspace=True, segment_chunks=None):
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:2] != q.shape[:2]:
         raise ValueError("expected q, k [B,T,Nk,dk] and v [B,T,Nv,dv]")
     dev = q.device
@@ -153,24 +163,32 @@ def _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu,
     S_T = torch.empty((N, Nv, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
     if not workspace:                         # token-by-token path: no workspace
         return prob, o, S_T, cu_dev, cu_host, scale
-    ws = torch.empty(workspace_size(prob, debug), dtype=torch.uint8, device=dev)
+    ws = torch.empty(workspace_size(prob, debug, segment_chunks), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     args = [ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), ctypes.c_float(scale),
             _ptr(initial_state), _ptr(cu_dev), _ptr(cu_host), _ptr(o), _ptr(S_T), _ptr(ws),
             ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream)]
+    if segment_chunks is not None:            # gdr_chunk_fwd_segmented: segment_chunks before the workspace
+        args = args[:12] + [ctypes.c_int32(segment_chunks)] + args[12:]
     keep = (cu_dev, cu_host, ws)
     return prob, args, o, S_T, keep
 
 
 def chunk_fwd(q, k, v, beta, g=None, scale=None, initial_state=None, output_final_state=True,
-              cu_seqlens=None, cu_seqlens_cpu=None, chunk_size=64, out_dtype=None):
+              cu_seqlens=None, cu_seqlens_cpu=None, chunk_size=64, out_dtype=None, segment_chunks=None):
     """Chunked gated delta-rule forward. Returns (o, final_state or None).
 
-    out_dtype: dtype of o, the io dtype (default) or torch.float32."""
+    out_dtype: dtype of o, the io dtype (default) or torch.float32.
+    segment_chunks: None runs gdr_chunk_fwd (one serial state pass per
+    sequence); an int runs gdr_chunk_fwd_segmented with segments of that many
+    chunks (0: the library chooses)."""
     lib = load_library()
     prob, args, o, S_T, keep = _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu,
-                                        chunk_size, output_final_state, out_dtype)
-    _check(lib.gdr_chunk_fwd(*args))
+                                        chunk_size, output_final_state, out_dtype, segment_chunks=segment_chunks)
+    if segment_chunks is None:
+        _check(lib.gdr_chunk_fwd(*args))
+    else:
+        _check(lib.gdr_chunk_fwd_segmented(*args, None))
     del keep
     return o, S_T
 
@@ -235,19 +253,26 @@ class Forward:
     the whole forward on the stream that was current at construction."""
 
     def __init__(self, q, k, v, beta, g=None, scale=None, initial_state=None, output_final_state=True,
-                 cu_seqlens=None, cu_seqlens_cpu=None, chunk_size=64, out_dtype=None):
+                 cu_seqlens=None, cu_seqlens_cpu=None, chunk_size=64, out_dtype=None, segment_chunks=None):
         self.lib = load_library()
+        self.segment_chunks = segment_chunks
         self.problem, self.args, self.o, self.final_state, self._keep = _prepare(
             q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu, chunk_size,
-            output_final_state, out_dtype)
+            output_final_state, out_dtype, segment_chunks=segment_chunks)
         self.inputs = (q, k, v, beta, g, initial_state)       # keep alive while prepared
 
     def __call__(self):
-        _check(self.lib.gdr_chunk_fwd(*self.args))
+        if self.segment_chunks is None:
+            _check(self.lib.gdr_chunk_fwd(*self.args))
+        else:
+            _check(self.lib.gdr_chunk_fwd_segmented(*self.args, None))
 
     def timed(self, events):
         """Enqueue one forward and record the NUM_STAGES + 1 torch.cuda.Event
         objects around its stages (they must have been recorded once, so that
         their HIP handles exist)."""
         handles = (ctypes.c_void_p * (NUM_STAGES + 1))(*[e.cuda_event for e in events])
-        _check(self.lib.gdr_chunk_fwd_timed(*self.args, handles))
+        if self.segment_chunks is None:
+            _check(self.lib.gdr_chunk_fwd_timed(*self.args, handles))
+        else:
+            _check(self.lib.gdr_chunk_fwd_segmented(*self.args, handles))

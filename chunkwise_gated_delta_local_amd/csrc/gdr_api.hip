@@ -121,10 +121,49 @@ Plan make_plan(const gdr_problem_t* p) {
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
+// Segment-parallel state passing. Automatic choice (segment_chunks == 0): when
+// the serial state pass has fewer than 64 workgroups (sequences x value heads x
+// 16-column dv tiles), each sequence is cut into up to 256 / that many
+// segments, so that the segmented passes fill the 256 compute units once;
+// otherwise the serial pass runs (fewer than four segments per sequence do not
+// repay the two extra passes).
+int32_t auto_segments_per_seq(const gdr_problem_t* p) {
+    const int64_t w0 = (int64_t)p->num_seqs * p->num_v_heads * (p->head_dim_v / 16);
+    if (w0 <= 0 || w0 >= 64) return 1;
+    return (int32_t)(256 / w0);
+}
+
+// Upper bound on the segment count for any cu_seqlens with this problem's
+// num_seqs and total length.
+int64_t segment_bound(const gdr_problem_t* p, int32_t seg_chunks) {
+    if (seg_chunks > 0) return make_plan(p).nt_cap / seg_chunks + p->num_seqs;
+    const int32_t per_seq = auto_segments_per_seq(p);
+    return per_seq > 1 ? (int64_t)p->num_seqs * per_seq : 0;   // 0: the serial pass runs
+}
+
+struct SegPlan {
+    size_t off_first, off_seqseg, off_Sloc, off_M, off_Sstart, end;
+};
+
+// Segment region, laid out after `base` bytes for `nseg` segments.
+SegPlan make_seg_plan(const gdr_problem_t* p, size_t base, int64_t nseg) {
+    SegPlan sp;
+    const size_t Nv = p->num_v_heads, dk = p->head_dim_qk, dv = p->head_dim_v;
+    size_t off = align256(base);
+    auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+    sp.off_first = take(((size_t)nseg + 1) * 4);
+    sp.off_seqseg = take(((size_t)p->num_seqs + 1) * 4);
+    sp.off_Sloc = take((size_t)nseg * Nv * dk * dv * 4);
+    sp.off_M = take((size_t)nseg * Nv * dk * dk * 4);
+    sp.off_Sstart = take((size_t)nseg * Nv * dk * dv * 4);
+    sp.end = off;
+    return sp;
+}
+
 gdr_status_t run(const gdr_problem_t* p, const void* q, const void* k, const void* v, const float* g,
                  const void* beta, float scale, const float* S0, const int32_t* cu_dev, const int32_t* cu_host,
                  void* o, float* ST, void* ws, size_t ws_bytes, void* stream, hipEvent_t* events,
-                 bool reference, Plan* plan_out, int32_t* nt_out) {
+                 bool reference, Plan* plan_out, int32_t* nt_out, int32_t seg_req = -1) {
     gdr_status_t st = check_problem(p);
     if (st != GDR_OK) return st;
     if ((cu_dev == nullptr) != (cu_host == nullptr))
@@ -140,15 +179,41 @@ gdr_status_t run(const gdr_problem_t* p, const void* q, const void* k, const voi
     Plan pl = make_plan(p);
     if (!ws) return fail(GDR_ERR_WORKSPACE, "workspace is NULL");
     if (((uintptr_t)ws & 255) != 0) return fail(GDR_ERR_WORKSPACE, "workspace not 256-byte aligned");
-    const size_t need = reference ? pl.reference : pl.production;
-    if (ws_bytes < need) return fail(GDR_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+    size_t need = reference ? pl.reference : pl.production;
 
-    int64_t nt = 0;
+    int64_t nt = 0, max_chunks = 0;
     for (int32_t n = 0; n < p->num_seqs; ++n) {
         const int64_t len = cu_host ? (int64_t)cu_host[n + 1] - cu_host[n] : p->seq_len;
         nt += (len + 63) / 64;
+        max_chunks = (len + 63) / 64 > max_chunks ? (len + 63) / 64 : max_chunks;
     }
     if (nt > pl.nt_cap) return fail(GDR_ERR_SEQLENS, "chunk count %lld exceeds capacity", (long long)nt);
+
+    // segments: seg_req < 0 none, 0 automatic, > 0 chunks per segment; only a
+    // split of some sequence into two or more segments takes the segmented passes
+    int64_t seg_chunks = 0, nseg = 0;
+    if (seg_req >= 0 && max_chunks > 1) {
+        if (seg_req > 0) {
+            seg_chunks = seg_req;
+        } else {
+            const int32_t per_seq = auto_segments_per_seq(p);
+            if (per_seq > 1) seg_chunks = (max_chunks + per_seq - 1) / per_seq;
+        }
+        if (seg_chunks > 0 && seg_chunks < max_chunks) {
+            for (int32_t n = 0; n < p->num_seqs; ++n) {
+                const int64_t len = cu_host ? (int64_t)cu_host[n + 1] - cu_host[n] : p->seq_len;
+                nseg += ((len + 63) / 64 + seg_chunks - 1) / seg_chunks;
+            }
+        } else {
+            seg_chunks = 0;
+        }
+    }
+    SegPlan sp{};
+    if (nseg > 0) {
+        sp = make_seg_plan(p, need, nseg);
+        need = sp.end;
+    }
+    if (ws_bytes < need) return fail(GDR_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
 
     char* w = static_cast<char*>(ws);
     gdr::LaunchArgs a;
@@ -179,6 +244,13 @@ gdr_status_t run(const gdr_problem_t* p, const void* q, const void* k, const voi
     a.Pf = pl.sz_Tf ? w + pl.off_Pf : nullptr;
     a.R = pl.sz_Tf ? w + pl.off_R : nullptr;
     a.reference = reference;
+    a.nseg = (int32_t)nseg;
+    a.seg_chunks = (int32_t)seg_chunks;
+    a.seg_first = nseg ? reinterpret_cast<int32_t*>(w + sp.off_first) : nullptr;
+    a.seq_seg = nseg ? reinterpret_cast<int32_t*>(w + sp.off_seqseg) : nullptr;
+    a.Sloc = nseg ? reinterpret_cast<float*>(w + sp.off_Sloc) : nullptr;
+    a.Mseg = nseg ? reinterpret_cast<float*>(w + sp.off_M) : nullptr;
+    a.Sstart = nseg ? reinterpret_cast<float*>(w + sp.off_Sstart) : nullptr;
     a.stream = static_cast<hipStream_t>(stream);
 
     hipError_t e = gdr::launch_forward(a, events);
@@ -255,6 +327,34 @@ gdr_status_t gdr_chunk_fwd_debug(const gdr_problem_t* p, const void* q, const vo
         if (e != hipSuccess) return fail(GDR_ERR_HIP, "intermediate copy failed: %s", hipGetErrorString(e));
     }
     return GDR_OK;
+}
+
+gdr_status_t gdr_chunk_fwd_segmented_workspace_size(const gdr_problem_t* problem, int32_t segment_chunks,
+                                                    size_t* bytes) {
+    if (!bytes) return fail(GDR_ERR_NULL, "bytes is NULL");
+    gdr_status_t st = check_problem(problem);
+    if (st != GDR_OK) return st;
+    if (segment_chunks < 0) return fail(GDR_ERR_SHAPE, "segment_chunks must be >= 0 (got %d)", segment_chunks);
+    const size_t base = make_plan(problem).production;
+    *bytes = make_seg_plan(problem, base, segment_bound(problem, segment_chunks)).end;
+    return GDR_OK;
+}
+
+gdr_status_t gdr_chunk_fwd_segmented(const gdr_problem_t* p, const void* q, const void* k, const void* v,
+                                     const float* g, const void* beta, float scale, const float* initial_state,
+                                     const int32_t* cu_dev, const int32_t* cu_host, void* o, float* final_state,
+                                     int32_t segment_chunks, void* workspace, size_t workspace_bytes, void* stream,
+                                     void* const* stage_events) {
+    if (segment_chunks < 0) return fail(GDR_ERR_SHAPE, "segment_chunks must be >= 0 (got %d)", segment_chunks);
+    hipEvent_t ev[GDR_NUM_STAGES + 1];
+    if (stage_events) {
+        for (int i = 0; i <= GDR_NUM_STAGES; ++i) {
+            if (!stage_events[i]) return fail(GDR_ERR_NULL, "stage_events[%d] is NULL", i);
+            ev[i] = static_cast<hipEvent_t>(stage_events[i]);
+        }
+    }
+    return run(p, q, k, v, g, beta, scale, initial_state, cu_dev, cu_host, o, final_state, workspace,
+               workspace_bytes, stream, stage_events ? ev : nullptr, false, nullptr, nullptr, segment_chunks);
 }
 
 gdr_status_t gdr_chunk_fwd_timed(const gdr_problem_t* p, const void* q, const void* k, const void* v,

@@ -543,10 +543,13 @@ __global__ __launch_bounds__(256) void k_wu(const T* __restrict__ k, const T* __
 //   S      = exp(G_last) S + K^T diag(exp(G_last - G)) V_new
 // S in accumulator layout is already the pair-fragment operand of W S, and
 // V_new in accumulator layout is already the operand of K^T V_new.
+// For segment-parallel state passing: the state may start as I
+// (init_identity; the grid then covers dk columns), U == NULL stands for
+// U = 0, and H and V_new are written only when their pointers are given.
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(64) void k_state(const float* __restrict__ Wf, const float* __restrict__ Uf,
                                                const T* __restrict__ KTf, const float* __restrict__ G,
-                                               const float* __restrict__ S0,
+                                               const float* __restrict__ S0, int init_identity,
                                                const int32_t* __restrict__ chunk_start,
                                                const int32_t* __restrict__ chunk_len,
                                                const int32_t* __restrict__ seq_first, int32_t Nk, int32_t Nv,
@@ -562,8 +565,10 @@ __global__ __launch_bounds__(64) void k_state(const float* __restrict__ Wf, cons
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            S[db][j] = S0 ? S0[sbase + (int64_t)(db * 16 + 4 * qd + j) * DV + nb * 16 + r] : 0.f;
+        for (int j = 0; j < 4; ++j) {
+            const int row = db * 16 + 4 * qd + j, col = nb * 16 + r;
+            S[db][j] = init_identity ? (row == col ? 1.f : 0.f) : S0 ? S0[sbase + (int64_t)row * DV + col] : 0.f;
+        }
 
     const int c0 = seq_first[n], c1 = seq_first[n + 1];
     for (int c = c0; c < c1; ++c) {
@@ -578,7 +583,7 @@ __global__ __launch_bounds__(64) void k_state(const float* __restrict__ Wf, cons
 #pragma unroll
         for (int kp = 0; kp < NKP; ++kp) {
             f8 raw = __builtin_shufflevector(S[2 * kp], S[2 * kp + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-            store_frag_f32(hdst + kp * 512, lane, raw);
+            if (Hf) store_frag_f32(hdst + kp * 512, lane, raw);
             sb[kp] = split_acc_pair<T>(S[2 * kp], S[2 * kp + 1]);
         }
 
@@ -592,11 +597,11 @@ __global__ __launch_bounds__(64) void k_state(const float* __restrict__ Wf, cons
 #pragma unroll
             for (int kp = 0; kp < NKP; ++kp)
                 x = mfma_dd<T>(split_v8<T>(load_frag_f32(wsrc + (tb * NKP + kp) * 512, lane)), sb[kp], x);
-            vn[tb] = load_tile_f32(usrc + (tb * NNB + nb) * 256, lane) - x;
+            vn[tb] = (Uf ? load_tile_f32(usrc + (tb * NNB + nb) * 256, lane) : f32x4{0.f, 0.f, 0.f, 0.f}) - x;
         }
         float* vdst = VNf + (((int64_t)c * Nv + h) * NNB + nb) * 2 * 512;
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) store_pair_half_f32(vdst + (tb >> 1) * 512, lane, tb & 1, vn[tb]);
+        for (int tb = 0; tb < 4 && VNf; ++tb) store_pair_half_f32(vdst + (tb >> 1) * 512, lane, tb & 1, vn[tb]);
 
         // decay each position to the chunk end; positions past the end contribute nothing
         f32x4 vd[4];
@@ -727,6 +732,11 @@ __global__ __launch_bounds__(256) void k_output(const T* __restrict__ q, const T
 }
 
 // ============================================================ K4 + K5 fused: state pass with output
+// Modes of the fused pass: kFull (state and output, from S0); kStateOnly (the
+// state alone: end states, no output work); kTransition (state alone from
+// S = I with V read as zero: the map a run of chunks applies to its entering
+// state). The last two serve segment-parallel state passing (below).
+constexpr int kFull = 0, kStateOnly = 1, kTransition = 2;
 // Production path for bf16 inputs. One workgroup of twelve wavefronts per
 // (sequence, value head, 16 columns of dv) walks the sequence's chunks in
 // order with the state slice S (dk x 16, fp32) on chip, and produces the output
@@ -768,7 +778,7 @@ __global__ __launch_bounds__(256) void k_output(const T* __restrict__ q, const T
 // contiguous bytes of a row); products over positions (T Z, K^T V, P V_new) use
 // the stacked-accumulator order of gdr_device.hpp. The state is written to LDS
 // in the first order by the wave that updates it.
-template <int DK, int DV>
+template <int DK, int DV, int MODE>
 __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                        const bf16* __restrict__ v, const f32x2* __restrict__ R, const bf16* __restrict__ Tf,
                                                        const bf16* __restrict__ Pf, const float* __restrict__ S0,
@@ -808,6 +818,7 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave index, uniform
     const int lane = tid & 63, r = lane & 15, qd = lane >> 4;
     const int kh = h / (Nv / Nk);
+    constexpr bool want_o = MODE == kFull;       // else state only: no Q, score or output work
     const int c0 = seq_first[n], c1 = seq_first[n + 1];
     // The chunks of a sequence are consecutive 64-token pieces of its token
     // range, so their start and length follow from the range.
@@ -866,8 +877,12 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
         for (int t = 0; t < TPW; ++t) {
             const int db = w * TPW + t;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                S[t][j] = (db < NDB && S0) ? S0[sbase + (int64_t)(db * 16 + 4 * qd + j) * DV + nb * 16 + r] : 0.f;
+            for (int j = 0; j < 4; ++j) {
+                const int row = db * 16 + 4 * qd + j, col = nb * 16 + r;
+                S[t][j] = db >= NDB ? 0.f
+                          : MODE == kTransition ? (row == col ? 1.f : 0.f)
+                          : S0 ? S0[sbase + (int64_t)row * DV + col] : 0.f;
+            }
         }
         // S tile db (rows 16 db + 4 qd + j of this lane's column r) -> B fragments of
         // contraction block db / 2 in the 8 qd + e order
@@ -933,7 +948,7 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
                     vrow[j] = to_f(Vsb[(w * 16 + 4 * qd + j) * 16 + r]);
                 }
 #pragma unroll
-                for (int kp = 0; kp < NKP; ++kp) qa[kp] = frag(Qb, w, kp);
+                for (int kp = 0; kp < NKP; ++kp) qa[kp] = want_o ? frag(Qb, w, kp) : v8{};
                 v8 kt[TPW][2];                          // K^T operands of phase C
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) {
@@ -959,10 +974,12 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
                 for (int tp = 0; tp < 2; ++tp)
                     if (tp < ntp) zf[tp] = load_split(Zb, tp);
                 f32x4 Qh = {0.f, 0.f, 0.f, 0.f}, Ql = Qh;
+                if constexpr (want_o) {
 #pragma unroll
-                for (int kp = 0; kp < NKP; ++kp) {
-                    Qh = mfma_pair(qa[kp], BS[kp].hi, Qh);
-                    Ql = mfma_pair(qa[kp], BS[kp].lo, Ql);
+                    for (int kp = 0; kp < NKP; ++kp) {
+                        Qh = mfma_pair(qa[kp], BS[kp].hi, Qh);
+                        Ql = mfma_pair(qa[kp], BS[kp].lo, Ql);
+                    }
                 }
                 f32x4 Va = {0.f, 0.f, 0.f, 0.f}, Vl = Va;
 #pragma unroll
@@ -981,7 +998,7 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
                 }
                 store_split_half(Vtb, w >> 1, w & 1, VD);
                 store_split_half(Vb, w >> 1, w & 1, VN);
-                QSx[w][lane] = Qh + Ql;
+                if constexpr (want_o) QSx[w][lane] = Qh + Ql;
                 if (c + 1 < c1) {
 #pragma unroll
                     for (int tp = 0; tp < 2; ++tp)
@@ -1047,7 +1064,7 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
 #pragma unroll
             for (int m = 0; m < MCE; ++m) {
                 const int u = w + 4 * m;
-                if (m < m0 || m >= m1) continue;
+                if (m < m0 || m >= m1 || (m >= NKP && !want_o)) continue;
                 if (m < NKP) {                               // K block (tb, kp)
                     const int tb = u / NKP, kp = u % NKP;
                     buffer_to_lds16(rk, Kd + u * FRAG, kq_lane + (16 * tb * Nk * DK + 32 * kp) * 2);
@@ -1068,10 +1085,13 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
             for (int m = 0; m < 4; ++m) {
                 const int u = w + 4 * m;
                 if (u < NTCP) {                              // score piece
-                    buffer_to_lds16(rp, Pd + u * FRAG, (u * 64 + lane) * 16);
+                    if constexpr (want_o) buffer_to_lds16(rp, Pd + u * FRAG, (u * 64 + lane) * 16);
                 } else if (u < NTCP + 2) {                   // V rows 32 vh .. 32 vh + 31 (16 columns)
+                    // transition pass: an empty range, so every row reads as zero
                     const int vh = u - NTCP;
-                    buffer_to_lds16(rsrc(v, (s * Nv + h) * DV + nb * 16, 2, (uint32_t)((L - 1) * Nv * DV + 16) * 2u),
+                    const uint32_t vbytes = MODE == kTransition ? 0u : (uint32_t)((L - 1) * Nv * DV + 16) * 2u;
+                    buffer_to_lds16(rsrc(MODE == kTransition ? k : v,
+                                         MODE == kTransition ? 0 : (s * Nv + h) * DV + nb * 16, 2, vbytes),
                                     Vd + vh * 512, ((32 * vh + (lane >> 1)) * Nv * DV + 8 * (lane & 1)) * 2);
                 } else if (u == NTCP + 2 && lane < 32) {     // R (512 bytes: two positions per lane)
                     buffer_to_lds16(rsrc(R, ((int64_t)c * Nv + h) * kChunk, 8, kChunk * 8), Rd, lane * 16);
@@ -1092,7 +1112,9 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
             lds_barrier();                                                          // barrier 2
             if (c + 2 < c1) {
                 copy_early(c + 2, odd, MEB, MCE);
-                wait_vmem_but<MCE>();    // chunk c+1 has landed; chunk c+2's early list may be in flight
+                // chunk c+1 has landed; chunk c+2's early list (its K blocks only, without o) may be in flight
+                if constexpr (want_o) wait_vmem_but<MCE>();
+                else wait_vmem_but<MEB>();
             } else {
                 wait_vmem();
             }
@@ -1107,6 +1129,15 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
     // until phase B of step c+1, and the score pairs and exp(G) are taken into
     // registers in phase B of step c, before the copy waves overwrite that LDS
     // half with chunk c+2.
+    if constexpr (!want_o) {                         // state only: keep step with the barriers
+        lds_barrier();
+        for (int c = c0; c < c1; ++c) {
+            lds_barrier();
+            lds_barrier();
+            lds_barrier();
+        }
+        return;
+    }
     const int w = wv - 4;
     const int ntp = (w >> 1) + 1;
     const int ob = out_f32 ? 4 : 2;
@@ -1169,6 +1200,121 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
     }
     output(c1 - 1);
 }
+// ============================================================ segment-parallel state passing
+// The state recursion is affine in the state: over any run of chunks,
+//   S_end = M S_start + S_loc,
+// where S_loc is the end state reached from a zero state and M (dk x dk) is the
+// end state reached from S_start = I with V = 0 (the per-chunk map
+// S -> exp(G_last) S + K^T diag(exp(G_last - G)) T (V - diag(exp(G)) K S),
+// ChunkGatedDeltaRule page formulas (3) and (6), composed over the run). So a
+// long sequence can be cut into segments of whole chunks whose local states and
+// transitions are formed side by side; one short scan over the segments then
+// gives each segment's true entering state, and a last pass from those states
+// writes the output (FLA DeltaNet article, section 2.4: the chunk states form
+// a linear recurrence, here composed segment by segment instead of chunk by
+// chunk).
+//
+// Segment table: segment j of the batch covers chunks seg_first[j] ..
+// seg_first[j + 1] - 1, at most `seg_chunks` consecutive chunks of one
+// sequence; seq_seg[n] is the first segment of sequence n (seq_seg[N] = the
+// segment count). Entries are clamped to the capacity `cap` sized on the host,
+// and entries no sequence reaches are empty, so a table built from offsets
+// that disagree with the host's copy still stays inside every buffer.
+__global__ __launch_bounds__(1024) void k_segment_table(const int32_t* __restrict__ seq_first, int32_t N,
+                                                         int32_t seg_chunks, int32_t cap,
+                                                         int32_t* __restrict__ seg_first,
+                                                         int32_t* __restrict__ seq_seg) {
+    __shared__ int32_t scan[1024];
+    const int tid = threadIdx.x;
+    const int32_t end = seq_first[N];
+    for (int32_t j = tid; j <= cap; j += 1024) seg_first[j] = end;
+    __syncthreads();
+    int32_t base = 0;
+    for (int32_t n0 = 0; n0 < N; n0 += 1024) {
+        const int32_t n = n0 + tid;
+        const int32_t f = n < N ? seq_first[n] : 0;
+        const int32_t nch = n < N ? seq_first[n + 1] - f : 0;
+        const int32_t nseg = (nch + seg_chunks - 1) / seg_chunks;
+        scan[tid] = nseg;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {         // inclusive Hillis-Steele scan
+            int32_t add = tid >= off ? scan[tid - off] : 0;
+            __syncthreads();
+            scan[tid] += add;
+            __syncthreads();
+        }
+        const int32_t first = base + scan[tid] - nseg;
+        if (n < N) {
+            seq_seg[n] = first < cap ? first : cap;
+            for (int32_t i = 0; i < nseg && first + i < cap; ++i) seg_first[first + i] = f + i * seg_chunks;
+        }
+        base += scan[1023];
+        __syncthreads();
+    }
+    if (tid == 0) seq_seg[N] = base < cap ? base : cap;
+}
+
+// Scan over the segments of each sequence, per (sequence, value head, 16
+// columns of dv): S = S0; for each segment j in order, S_start[j] = S, then
+// S = M_j S + S_loc[j]; the last S is the sequence's final state. fp32 FMA
+// throughout. Thread u < 2 dk owns row u / 2 and columns 8 (u % 2) .. + 7 of
+// the slice; the slice itself sits in LDS, so every step reads the rows of M_j
+// from memory once and the slice as LDS broadcasts.
+// Layouts: S_loc, S_start [segments][Nv][dk][dv], M [segments][Nv][dk][dk],
+// S0 and ST [N][Nv][dk][dv], all fp32.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void k_segment_scan(const int32_t* __restrict__ seq_seg,
+                                                       const float* __restrict__ S0, const float* __restrict__ Sloc,
+                                                       const float* __restrict__ M, int32_t Nv,
+                                                       float* __restrict__ Sstart, float* __restrict__ ST) {
+    static_assert(2 * DK <= 256, "one row half per thread");
+    __shared__ __attribute__((aligned(16))) float Ss[DK][16];
+    const int n = blockIdx.x, h = blockIdx.y, nb = blockIdx.z;
+    const int tid = threadIdx.x;
+    const bool own = tid < 2 * DK;
+    const int i = tid >> 1, c8 = 8 * (tid & 1);
+    const int64_t col = (int64_t)nb * 16 + c8;
+    f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
+    if (own && S0) {
+        const float* src = S0 + (((int64_t)n * Nv + h) * DK + i) * DV + col;
+        x0 = *reinterpret_cast<const f32x4*>(src);
+        x1 = *reinterpret_cast<const f32x4*>(src + 4);
+    }
+    const int32_t j0 = seq_seg[n], j1 = seq_seg[n + 1];
+    for (int32_t j = j0; j < j1; ++j) {
+        const int64_t sb = (((int64_t)j * Nv + h) * DK + i) * DV + col;
+        if (own) {
+            *reinterpret_cast<f32x4*>(&Ss[i][c8]) = x0;
+            *reinterpret_cast<f32x4*>(&Ss[i][c8 + 4]) = x1;
+            *reinterpret_cast<f32x4*>(Sstart + sb) = x0;
+            *reinterpret_cast<f32x4*>(Sstart + sb + 4) = x1;
+        }
+        __syncthreads();
+        if (own) {
+            x0 = *reinterpret_cast<const f32x4*>(Sloc + sb);
+            x1 = *reinterpret_cast<const f32x4*>(Sloc + sb + 4);
+            const float* mrow = M + (((int64_t)j * Nv + h) * DK + i) * DK;
+#pragma unroll 4
+            for (int m4 = 0; m4 < DK; m4 += 4) {
+                const f32x4 mv = *reinterpret_cast<const f32x4*>(mrow + m4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const f32x4 s0 = *reinterpret_cast<const f32x4*>(&Ss[m4 + e][c8]);
+                    const f32x4 s1 = *reinterpret_cast<const f32x4*>(&Ss[m4 + e][c8 + 4]);
+                    x0 += mv[e] * s0;
+                    x1 += mv[e] * s1;
+                }
+            }
+        }
+        __syncthreads();                         // the slice is read before it is overwritten
+    }
+    if (own && ST) {
+        float* dst = ST + (((int64_t)n * Nv + h) * DK + i) * DV + col;
+        *reinterpret_cast<f32x4*>(dst) = x0;
+        *reinterpret_cast<f32x4*>(dst + 4) = x1;
+    }
+}
+
 // ============================================================ launchers
 template <typename T, int DK, int DV>
 static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
@@ -1181,6 +1327,9 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
     mark(0);
     k_chunk_table<<<1, 1024, 0, st>>>(a.cu_dev, a.T_row, a.N, a.Ttot, cap, a.chunk_seq, a.chunk_start,
                                       a.chunk_len, a.seq_first);
+    const bool segmented = a.nseg > 0 && a.N > 0;
+    if (segmented)
+        k_segment_table<<<1, 1024, 0, st>>>(a.seq_first, a.N, a.seg_chunks, a.nseg, a.seg_first, a.seq_seg);
     mark(1);
     if (NT > 0) {
         const int64_t units = (int64_t)NT * a.Nv;
@@ -1199,10 +1348,42 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
                                                        (const float*)a.A, a.chunk_start, a.chunk_len, a.Nk, a.Nv,
                                                        (float*)a.W, (float*)a.U, (T*)a.KT);
     mark(4);
-    if (a.N > 0) {
+    if (segmented) {
+        // local end states from zero, transitions from I with V = 0, the scan,
+        // then the pass from the entering states that writes the output
+        const dim3 gs(a.nseg, a.Nv, DV / 16), gm(a.nseg, a.Nv, DK / 16), gn(a.N, a.Nv, DV / 16);
         if constexpr (kFused) {
             if (fused) {
-                k_state_output<DK, DV><<<dim3(a.N, a.Nv, DV / 16), 768, 0, st>>>(
+                const bf16 *q = (const bf16*)a.q, *k = (const bf16*)a.k, *v = (const bf16*)a.v;
+                const bf16 *Tf = (const bf16*)a.Tf, *Pf = (const bf16*)a.Pf;
+                const f32x2* R = (const f32x2*)a.R;
+                k_state_output<DK, DV, kStateOnly><<<gs, 768, 0, st>>>(
+                    q, k, v, R, Tf, Pf, nullptr, a.chunk_start, a.chunk_len, a.seg_first, a.Nk, a.Nv, a.scale,
+                    a.out_f32, nullptr, a.Sloc);
+                k_state_output<DK, DK, kTransition><<<gm, 768, 0, st>>>(
+                    q, k, nullptr, R, Tf, Pf, nullptr, a.chunk_start, a.chunk_len, a.seg_first, a.Nk, a.Nv, a.scale,
+                    a.out_f32, nullptr, a.Mseg);
+                k_segment_scan<DK, DV><<<gn, 256, 0, st>>>(a.seq_seg, a.S0, a.Sloc, a.Mseg, a.Nv, a.Sstart, a.ST);
+                k_state_output<DK, DV, kFull><<<gs, 768, 0, st>>>(
+                    q, k, v, R, Tf, Pf, a.Sstart, a.chunk_start, a.chunk_len, a.seg_first, a.Nk, a.Nv, a.scale,
+                    a.out_f32, a.o, nullptr);
+            }
+        }
+        if (!fused) {
+            const float *W = (const float*)a.W, *U = (const float*)a.U;
+            const T* KT = (const T*)a.KT;
+            k_state<T, DK, DV><<<gs, 64, 0, st>>>(W, U, KT, a.G, nullptr, 0, a.chunk_start, a.chunk_len, a.seg_first,
+                                                  a.Nk, a.Nv, nullptr, nullptr, a.Sloc);
+            k_state<T, DK, DK><<<gm, 64, 0, st>>>(W, nullptr, KT, a.G, nullptr, 1, a.chunk_start, a.chunk_len,
+                                                  a.seg_first, a.Nk, a.Nv, nullptr, nullptr, a.Mseg);
+            k_segment_scan<DK, DV><<<gn, 256, 0, st>>>(a.seq_seg, a.S0, a.Sloc, a.Mseg, a.Nv, a.Sstart, a.ST);
+            k_state<T, DK, DV><<<gs, 64, 0, st>>>(W, U, KT, a.G, a.Sstart, 0, a.chunk_start, a.chunk_len,
+                                                  a.seg_first, a.Nk, a.Nv, (float*)a.H, (float*)a.VN, nullptr);
+        }
+    } else if (a.N > 0) {
+        if constexpr (kFused) {
+            if (fused) {
+                k_state_output<DK, DV, kFull><<<dim3(a.N, a.Nv, DV / 16), 768, 0, st>>>(
                     (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const f32x2*)a.R,
                     (const bf16*)a.Tf, (const bf16*)a.Pf, a.S0,
                     a.chunk_start, a.chunk_len, a.seq_first, a.Nk, a.Nv, a.scale, a.out_f32, a.o, a.ST);
@@ -1210,7 +1391,7 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
         }
         if (!fused)
             k_state<T, DK, DV><<<dim3(a.N, a.Nv, DV / 16), 64, 0, st>>>((const float*)a.W, (const float*)a.U,
-                                                                       (const T*)a.KT, a.G, a.S0, a.chunk_start,
+                                                                       (const T*)a.KT, a.G, a.S0, 0, a.chunk_start,
                                                                        a.chunk_len, a.seq_first, a.Nk, a.Nv,
                                                                        (float*)a.H, (float*)a.VN, a.ST);
     }

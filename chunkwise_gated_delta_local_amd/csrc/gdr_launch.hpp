@@ -29,6 +29,11 @@ struct LaunchArgs {
     void* Pf;                        // score block (Q K^T) (.) D fragments (fused pipeline)
     void* R;                         // decay factors exp(G), exp(G_last - G), chunk-major (fused pipeline)
     bool reference;                  // run the five separate kernels even for bf16
+    // segment-parallel state passing (nseg == 0: one serial pass per sequence)
+    int32_t nseg;                    // segment-table capacity: the host's count of segments
+    int32_t seg_chunks;              // chunks per segment
+    int32_t *seg_first, *seq_seg;    // [nseg + 1], [N + 1]
+    float *Sloc, *Mseg, *Sstart;     // local end states, transitions, entering states (fp32)
     hipStream_t stream;
 };
 

@@ -160,6 +160,48 @@ gdr_status_t gdr_chunk_fwd(const gdr_problem_t* problem,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Segment-parallel state passing on one GPU: the same result as gdr_chunk_fwd
+ * (up to rounding order), for inputs whose serial state pass would leave most
+ * compute units idle: few sequences times value heads, and long sequences.
+ *
+ * The chunk-to-chunk state map S -> exp(G_last) S + K^T diag(exp(G_last - G))
+ * V_new, with V_new = T (V - diag(exp(G)) K S) (ChunkGatedDeltaRule page,
+ * section 3.2, formulas (3) and (6); FLA DeltaNet article, section 2.4), is
+ * affine in S. Each sequence is cut into segments of `segment_chunks` whole
+ * 64-token chunks (the last one shorter). For every segment, side by side:
+ * its end state from a zero state (S_loc) and its dk x dk transition M (the
+ * end state from S = I with V = 0). One scan per (sequence, value head) then
+ * forms the entering states S_start[j+1] = M_j S_start[j] + S_loc[j] from
+ * initial_state, and a last pass from those states writes o. final_state is
+ * the scan's last value. All of these are fp32.
+ *   segment_chunks  > 0: chunks per segment. 0: the library chooses. It cuts
+ *                   each sequence into up to 256 / W segments when the serial
+ *                   pass has W < 64 workgroups (W = num_seqs * num_v_heads *
+ *                   head_dim_v / 16); otherwise it runs the serial pass.
+ *                   When no sequence spans more than one segment, the serial
+ *                   pass runs too. Negative: GDR_ERR_SHAPE.
+ *   stage_events    NULL, or GDR_NUM_STAGES + 1 events recorded as for
+ *                   gdr_chunk_fwd_timed; stage [5] covers all four segment
+ *                   launches (the two side-by-side passes, the scan, the
+ *                   output pass).
+ *   workspace       at least gdr_chunk_fwd_segmented_workspace_size bytes for
+ *                   the same segment_chunks. That is the production workspace
+ *                   plus, per segment, 4 * num_v_heads * dk * (2 dv + dk)
+ *                   bytes.
+ * Other arguments and errors as for gdr_chunk_fwd. Asynchronous on `stream`.
+ */
+gdr_status_t gdr_chunk_fwd_segmented_workspace_size(const gdr_problem_t* problem, int32_t segment_chunks,
+                                                    size_t* bytes);
+gdr_status_t gdr_chunk_fwd_segmented(const gdr_problem_t* problem,
+                                     const void* q, const void* k, const void* v,
+                                     const float* g, const void* beta, float scale,
+                                     const float* initial_state,
+                                     const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                                     void* o, float* final_state, int32_t segment_chunks,
+                                     void* workspace, size_t workspace_bytes, void* stream,
+                                     void* const* stage_events);
+
+/*
  * Intermediates of the five kernels, for per-kernel parity checks. Each
  * pointer is a caller-owned device buffer (NULL to skip) that receives a copy
  * of the workspace region in the layout the kernels use; sizes follow from

@@ -133,3 +133,49 @@ def test_validate_out_dtype(lib):
     assert status(prob(out_dtype=api.GDR_F32)) == 0
     assert status(prob(io_dtype=api.GDR_F32, out_dtype=api.GDR_BF16)) == 3
     assert status(prob(out_dtype=9)) == 3
+
+
+def test_segmented_workspace_size(lib):
+    """The segmented workspace is the production one plus, per segment, the
+    local state, the transition and the entering state (fp32); shorter
+    segments need more of it, and a negative segment length is an error."""
+    from chunkwise_gated_delta_local_amd import api
+    p = prob(seq_len=64 * 64)
+    base = api.workspace_size(p)
+    per_seg = 4 * p.num_v_heads * p.head_dim_qk * (2 * p.head_dim_v + p.head_dim_qk)
+    s16 = api.workspace_size(p, segment_chunks=16)
+    s4 = api.workspace_size(p, segment_chunks=4)
+    assert base + per_seg * (64 // 16) <= s16 < s4
+    assert s4 >= base + per_seg * (64 // 4)
+    n = ctypes.c_size_t(0)
+    assert lib.gdr_chunk_fwd_segmented_workspace_size(ctypes.byref(p), ctypes.c_int32(-1), ctypes.byref(n)) == 2
+
+
+def test_segmented_automatic_choice_workspace(lib):
+    """Automatic segments: a problem with few workgroups (here 2 sequences x 4
+    value heads x 4 dv tiles = 32 < 64) gets room for up to 256 / 32 segments
+    per sequence; one with 64 or more runs the serial pass and needs no segment
+    states."""
+    from chunkwise_gated_delta_local_amd import api
+    small = prob(seq_len=64 * 256)
+    per_seg = 4 * small.num_v_heads * small.head_dim_qk * (2 * small.head_dim_v + small.head_dim_qk)
+    grid = small.num_seqs * small.num_v_heads * (small.head_dim_v // 16)
+    assert grid < 64
+    assert api.workspace_size(small, segment_chunks=0) >= (api.workspace_size(small)
+                                                          + per_seg * small.num_seqs * (256 // grid))
+    wide = prob(seq_len=64 * 256, Nk=32, Nv=32, dk=32, dv=32)
+    per_seg_w = 4 * 32 * 32 * (2 * 32 + 32)
+    assert api.workspace_size(wide, segment_chunks=0) < api.workspace_size(wide) + per_seg_w
+
+
+def test_segmented_rejects_before_launch(lib):
+    from chunkwise_gated_delta_local_amd import api
+    if torch.cuda.is_available():
+        pytest.skip("passes placeholder addresses; host-logic test for machines without a GPU")
+    p = prob(seq_len=64 * 8)
+    fake = ctypes.c_void_p(1 << 20)
+    args = [ctypes.byref(p), fake, fake, fake, None, fake, ctypes.c_float(1.0), None, None, None, fake, None]
+    assert lib.gdr_chunk_fwd_segmented(*args, ctypes.c_int32(-2), fake, ctypes.c_size_t(1 << 40), None, None) == 2
+    assert lib.gdr_chunk_fwd_segmented(*args, ctypes.c_int32(1), None, ctypes.c_size_t(0), None, None) == 6
+    serial_ws = api.workspace_size(p)           # enough for the serial pass, not for 1-chunk segments
+    assert lib.gdr_chunk_fwd_segmented(*args, ctypes.c_int32(1), fake, ctypes.c_size_t(serial_ws), None, None) == 6

@@ -1,0 +1,120 @@
+"""GPU parity of segment-parallel state passing (gdr_chunk_fwd_segmented)
+against the fp64 oracle, element by element, and against the serial pass.
+
+Cases: single long sequences cut into 1-, 3- and 7-chunk segments and the
+automatic choice; the fused bf16 path and the five-kernel fp32 path; varlen
+batches with empty, one-token, one-chunk and ragged sequences; GQA; the ungated
+rule; dk != dv (the transition pass then runs with dk columns); no final
+state; and a problem the automatic choice leaves serial (bitwise equal to
+gdr_chunk_fwd).
+"""
+import numpy as np
+import pytest
+import torch
+
+from chunkwise_gated_delta_local_amd import api, synth
+from gpu_common import TOL, bf16_rounding_excess, f64, oracle_inputs, rel_err, to_dev
+from oracle import recurrence
+
+pytestmark = pytest.mark.gpu
+
+
+def run(inp, segment_chunks, out_f32=True, output_final_state=True):
+    d = to_dev(inp)
+    o, S = api.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], g=d["g"], scale=inp["scale"], initial_state=d["S0"],
+                         output_final_state=output_final_state, cu_seqlens=d["cu_seqlens"],
+                         cu_seqlens_cpu=inp["cu_seqlens"], out_dtype=torch.float32 if out_f32 else None,
+                         segment_chunks=segment_chunks)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def oracle_ref(inp):
+    x = oracle_inputs(inp)
+    return recurrence(x["q"], x["k"], x["v"], x["beta"], x["g"], x["scale"], x["S0"], x["cu"])
+
+
+def long_seq(dtype, seed, T=64 * 20 + 13, Nk=1, Nv=2, dk=64, dv=64, gated=True, s0="randn", B=1):
+    w = synth.custom("long", B=B, T=T, Nk=Nk, Nv=Nv, dk=dk, dv=dv, dtype=dtype, gated=gated, s0=s0)
+    return synth.generate(w, seed=seed)
+
+
+CASES = {
+    "bf16_long_seg1": (lambda: long_seq("bf16", 31), 1),
+    "bf16_long_seg3": (lambda: long_seq("bf16", 32), 3),
+    "bf16_long_seg7": (lambda: long_seq("bf16", 33), 7),
+    "bf16_long_auto": (lambda: long_seq("bf16", 34), 0),
+    "f32_B2_seg2": (lambda: long_seq("f32", 35, T=700, B=2, Nk=2, Nv=2, dk=32, dv=64), 2),
+    "f32_long_auto": (lambda: long_seq("f32", 36, T=64 * 17 + 5, dk=32, dv=32), 0),
+    "bf16_ungated_seg3": (lambda: long_seq("bf16", 37, gated=False, s0="zero"), 3),
+    "bf16_dk128_dv32_seg4": (lambda: long_seq("bf16", 38, T=64 * 9 + 40, Nk=1, Nv=1, dk=128, dv=32), 4),
+    "bf16_varlen_gqa_seg2": (lambda: synth.generate(synth.custom(
+        "varlen", B=1, T=0, Nk=2, Nv=4, dk=128, dv=128, dtype="bf16", s0="randn",
+        lengths=(0, 1, 64, 65, 300, 1000)), seed=39), 2),
+    "f32_varlen_seg3": (lambda: synth.generate(synth.custom(
+        "varlen32", B=1, T=0, Nk=1, Nv=2, dk=64, dv=32, dtype="f32", s0="randn",
+        lengths=(200, 0, 17, 640)), seed=40), 3),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_segmented_parity(case):
+    make, sc = CASES[case]
+    inp = make()
+    w = inp["workload"]
+    tol = TOL[w.dtype]
+    o, S = run(inp, sc)
+    o_ref, S_ref = oracle_ref(inp)
+    eo = rel_err(f64(o).reshape(o_ref.shape), o_ref)
+    es = rel_err(f64(S), S_ref)
+    o_s, S_s = run_serial(inp)
+    ds_o, ds_s = rel_err(f64(o), f64(o_s)), rel_err(f64(S), f64(S_s))
+    msg = "%s (segment_chunks %d) err o %.3e S_T %.3e (tol %.0e) | vs serial o %.2e S_T %.2e" % (
+        case, sc, eo, es, tol, ds_o, ds_s)
+    if w.dtype == "bf16":
+        ob, _ = run(inp, sc, out_f32=False, output_final_state=False)
+        exc = bf16_rounding_excess(f64(ob).reshape(o_ref.shape), o_ref)
+        msg += " | bf16-out max error in bf16 steps %.3f" % exc
+        assert exc <= 1.0
+    print(msg, flush=True)
+    assert np.all(np.isfinite(f64(o))) and np.all(np.isfinite(f64(S)))
+    assert eo <= tol and es <= tol
+    # the two passes compute the same fp32-level result in a different order
+    assert ds_o <= 1e-4 and ds_s <= 1e-4
+
+
+def run_serial(inp):
+    d = to_dev(inp)
+    o, S = api.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], g=d["g"], scale=inp["scale"], initial_state=d["S0"],
+                         cu_seqlens=d["cu_seqlens"], cu_seqlens_cpu=inp["cu_seqlens"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def test_segmented_without_final_state():
+    inp = long_seq("bf16", 41)
+    o, S = run(inp, 2, output_final_state=False)
+    assert S is None
+    o_ref, _ = oracle_ref(inp)
+    assert rel_err(f64(o).reshape(o_ref.shape), o_ref) <= TOL["bf16"]
+
+
+def test_automatic_choice_keeps_wide_problems_serial():
+    """4 sequences x 16 value heads x 8 dv tiles = 512 workgroups: the library
+    runs the serial pass, bit for bit the result of gdr_chunk_fwd."""
+    inp = synth.generate(synth.WORKLOADS[3], seed=3)
+    o_a, S_a = run(inp, 0, out_f32=False)
+    d = to_dev(inp)
+    o_s, S_s = api.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], g=d["g"], scale=inp["scale"],
+                             initial_state=d["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_s) and torch.equal(S_a, S_s)
+
+
+def test_segments_longer_than_every_sequence_run_serial():
+    """segment_chunks at least the longest sequence's chunk count: no
+    sequence is split, the serial pass runs (same bits as gdr_chunk_fwd)."""
+    inp = long_seq("bf16", 42, T=64 * 5)
+    o_a, S_a = run(inp, 5)
+    o_s, S_s = run_serial(inp)
+    assert torch.equal(o_a, o_s) and torch.equal(S_a, S_s)
