@@ -278,10 +278,19 @@ def bench_recurrent(args) -> None:
 
 
 def _time_forward(fwd, K, W):
-    """Mean ms per forward and per stage (HIP events) over K timed calls."""
+    """Mean ms per forward and per stage (HIP events) over K timed calls
+    (stages: None for a call that records no stage events)."""
     for _ in range(W):
         fwd()
     torch.cuda.synchronize()
+    if not fwd.stage_events:
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(K):
+            fwd()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / K, None
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(api.NUM_STAGES + 1)] for _ in range(K)]
     for row in events:
         for e in row:
@@ -296,6 +305,44 @@ def _time_forward(fwd, K, W):
     stage_ms = np.array([[events[s][i].elapsed_time(events[s][i + 1]) for i in range(api.NUM_STAGES)]
                          for s in range(K)]).mean(axis=0)
     return start.elapsed_time(end) / K, stage_ms
+
+
+def bench_chunk_sizes(args) -> None:
+    """Chunk-size sensitivity on --workload: the five-kernel path at C = 16,
+    32 and 64 (serial depth T/C of the state pass against the C x C solve and
+    the C-wide intra-chunk products), each with its per-stage times, next to
+    the fused C = 64 path that gdr_chunk_fwd runs for bf16. The five-kernel
+    path at C = 64 is timed through gdr_chunk_fwd_debug with no intermediates
+    requested (it then copies nothing; no per-stage times)."""
+    w = synth.WORKLOADS[args.workload]
+    inp = synth.generate(w, seed=args.workload)
+    dev = torch.device("cuda:0")
+    d = {k: (None if inp[k] is None else inp[k].to(dev)) for k in ("q", "k", "v", "beta", "g", "S0", "cu_seqlens")}
+    K, W = args.steps, args.warmup
+    B, T = inp["q"].shape[:2]
+    Ttot = B * T
+    rows = {}
+    for C in (16, 32, 64):
+        fwd = api.Forward(d["q"], d["k"], d["v"], d["beta"], g=d["g"], scale=inp["scale"], initial_state=d["S0"],
+                          output_final_state=True, cu_seqlens=d["cu_seqlens"], cu_seqlens_cpu=inp["cu_seqlens"],
+                          chunk_size=C, five_kernel=(C == 64))   # C < 64: gdr_chunk_fwd runs the five kernels
+        ms, st = _time_forward(fwd, K, W)
+        rows["five-kernel C=%d" % C] = {"ms_per_step": ms, "tokens_per_s": Ttot / (ms * 1e-3),
+                                        "stage_ms": None if st is None else
+                                        {api.STAGE_NAMES[i]: float(st[i]) for i in range(api.NUM_STAGES)}}
+        del fwd
+        torch.cuda.empty_cache()
+    if w.dtype == "bf16":
+        fwd = api.Forward(d["q"], d["k"], d["v"], d["beta"], g=d["g"], scale=inp["scale"], initial_state=d["S0"],
+                          output_final_state=True, cu_seqlens=d["cu_seqlens"], cu_seqlens_cpu=inp["cu_seqlens"])
+        ms, st = _time_forward(fwd, K, W)
+        rows["fused C=64"] = {"ms_per_step": ms, "tokens_per_s": Ttot / (ms * 1e-3),
+                              "stage_ms": {api.STAGE_NAMES[i]: float(st[i]) for i in range(api.NUM_STAGES)}}
+    print(json.dumps({"metric": "fwd tokens/s by chunk size", "unit": "tokens/s", "n_gpus": 1, "steps": K,
+                      "warmup": W, "dtype": w.dtype, "data": "synthetic",
+                      "config": {"workload": w.name, "T": Ttot, "Nk": w.Nk, "Nv": w.Nv, "dk": w.dk, "dv": w.dv,
+                                 "seed": args.workload},
+                      "paths": rows}), flush=True)
 
 
 def bench_segmented(args) -> None:
@@ -365,10 +412,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget; 0 skips it")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB three times (calibrates HBM byte counters)")
-    ap.add_argument("--mode", choices=("chunk", "recurrent", "segmented"), default="chunk",
+    ap.add_argument("--mode", choices=("chunk", "recurrent", "segmented", "chunk-sizes"), default="chunk",
                     help="chunk: the chunked forward on --workload (default); recurrent: one decode step "
                          "(token-by-token kernel) for --decode-seqs sequences from a random state; segmented: "
-                         "segment-parallel against serial state passing on one long sequence with few heads")
+                         "segment-parallel against serial state passing on one long sequence with few heads; "
+                         "chunk-sizes: the five-kernel path at C = 16, 32, 64 and the fused path on --workload")
     ap.add_argument("--segment-chunks", type=int, default=0,
                     help="chunks per segment in --mode segmented (0: the library's choice)")
     ap.add_argument("--decode-seqs", type=int, default=64)
@@ -396,6 +444,9 @@ def main():
         return
     if args.mode == "segmented":
         bench_segmented(args)
+        return
+    if args.mode == "chunk-sizes":
+        bench_chunk_sizes(args)
         return
 
     w = synth.WORKLOADS[args.workload]

@@ -212,11 +212,12 @@ def recurrent_fwd(q, k, v, beta, g=None, scale=None, initial_state=None, output_
     return o, S_T
 
 
-def num_chunks(B, T, cu_host) -> int:
+def num_chunks(B, T, cu_host, chunk_size=64) -> int:
+    C = int(chunk_size)
     if cu_host is None:
-        return B * ((T + 63) // 64)
+        return B * ((T + C - 1) // C)
     lens = (cu_host[1:] - cu_host[:-1]).tolist()
-    return sum((n + 63) // 64 for n in lens)
+    return sum((n + C - 1) // C for n in lens)
 
 
 def chunk_fwd_debug(q, k, v, beta, g=None, scale=None, initial_state=None, output_final_state=True,
@@ -228,17 +229,19 @@ def chunk_fwd_debug(q, k, v, beta, g=None, scale=None, initial_state=None, outpu
                                         chunk_size, output_final_state, out_dtype, debug=True)
     B, T, Nk, dk = q.shape
     Nv, dv = v.shape[2], v.shape[3]
-    NT = num_chunks(B, T, keep[1])
+    C = int(chunk_size)
+    NT = num_chunks(B, T, keep[1], C)
+    ntb, ntp = C // 16, max(1, C // 32)
     dev, dt = q.device, q.dtype
     out = dict(
         G=torch.zeros((B * T, Nv), dtype=torch.float32, device=dev),
-        A=torch.zeros((B * T, Nv, 64), dtype=torch.float32, device=dev),
-        W=torch.zeros((NT, Nv, 4, dk // 32, 64, 8), dtype=torch.float32, device=dev),
-        U=torch.zeros((NT, Nv, 4, dv // 16, 64, 4), dtype=torch.float32, device=dev),
-        KT=torch.zeros((NT, Nk, dk // 16, 2, 64, 8), dtype=dt, device=dev),
+        A=torch.zeros((B * T, Nv, C), dtype=torch.float32, device=dev),
+        W=torch.zeros((NT, Nv, ntb, dk // 32, 64, 8), dtype=torch.float32, device=dev),
+        U=torch.zeros((NT, Nv, ntb, dv // 16, 64, 4), dtype=torch.float32, device=dev),
+        KT=torch.zeros((NT, Nk, dk // 16, ntp, 64, 8), dtype=dt, device=dev),
         H=torch.zeros((NT, Nv, dv // 16, dk // 32, 64, 8), dtype=torch.float32, device=dev),
-        VN=torch.zeros((NT, Nv, dv // 16, 2, 64, 8), dtype=torch.float32, device=dev),
-        T=torch.zeros((NT, Nv, 6, 2, 64, 8), dtype=dt, device=dev) if dt == torch.bfloat16 else None,
+        VN=torch.zeros((NT, Nv, dv // 16, ntp, 64, 8), dtype=torch.float32, device=dev),
+        T=torch.zeros((NT, Nv, 6, 2, 64, 8), dtype=dt, device=dev) if dt == torch.bfloat16 and C == 64 else None,
     )
     dbg = Intermediates(*(_ptr(out[n]) for n in ("G", "A", "W", "U", "KT", "H", "VN", "T")), 0)
     _check(lib.gdr_chunk_fwd_debug(*args, ctypes.byref(dbg)))
@@ -253,16 +256,28 @@ class Forward:
     the whole forward on the stream that was current at construction."""
 
     def __init__(self, q, k, v, beta, g=None, scale=None, initial_state=None, output_final_state=True,
-                 cu_seqlens=None, cu_seqlens_cpu=None, chunk_size=64, out_dtype=None, segment_chunks=None):
+                 cu_seqlens=None, cu_seqlens_cpu=None, chunk_size=64, out_dtype=None, segment_chunks=None,
+                 five_kernel=False):
+        """five_kernel: run the five kernels as separate launches (through
+        gdr_chunk_fwd_debug with no intermediates requested) even where
+        gdr_chunk_fwd would take the fused path; such calls record no stage
+        events."""
         self.lib = load_library()
         self.segment_chunks = segment_chunks
+        self.five_kernel = five_kernel
+        if five_kernel and segment_chunks is not None:
+            raise ValueError("five_kernel and segment_chunks do not combine")
         self.problem, self.args, self.o, self.final_state, self._keep = _prepare(
             q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu, chunk_size,
-            output_final_state, out_dtype, segment_chunks=segment_chunks)
+            output_final_state, out_dtype, debug=five_kernel, segment_chunks=segment_chunks)
+        self._no_intermediates = Intermediates()
+        self.stage_events = not five_kernel
         self.inputs = (q, k, v, beta, g, initial_state)       # keep alive while prepared
 
     def __call__(self):
-        if self.segment_chunks is None:
+        if self.five_kernel:
+            _check(self.lib.gdr_chunk_fwd_debug(*self.args, ctypes.byref(self._no_intermediates)))
+        elif self.segment_chunks is None:
             _check(self.lib.gdr_chunk_fwd(*self.args))
         else:
             _check(self.lib.gdr_chunk_fwd_segmented(*self.args, None))

@@ -53,8 +53,8 @@ gdr_status_t check_problem(const gdr_problem_t* p) {
         return fail(GDR_ERR_DTYPE, "out_dtype must equal io_dtype or be GDR_F32");
     if (!supported_dim(p->head_dim_qk) || !supported_dim(p->head_dim_v))
         return fail(GDR_ERR_UNSUPPORTED, "head dims (%d, %d) not in {32, 64, 128}", p->head_dim_qk, p->head_dim_v);
-    if (p->chunk_size != 64)
-        return fail(GDR_ERR_UNSUPPORTED, "chunk_size %d not supported (64 only)", p->chunk_size);
+    if (p->chunk_size != 16 && p->chunk_size != 32 && p->chunk_size != 64)
+        return fail(GDR_ERR_UNSUPPORTED, "chunk_size %d not supported (16, 32 or 64)", p->chunk_size);
     if (p->num_seqs < 0) return fail(GDR_ERR_SHAPE, "num_seqs must be >= 0");
     const int64_t Ttot = p->batch * p->seq_len;
     if (p->seq_len > ((int64_t)1 << 31) - 1 || Ttot > ((int64_t)1 << 31) - 1 - 64)
@@ -80,10 +80,16 @@ gdr_status_t check_seqlens(const gdr_problem_t* p, const int32_t* cu, bool varle
     return GDR_OK;
 }
 
+// The fused path runs for bf16 inputs with C = 64; everything else runs the
+// five kernels, whose production workspace holds their intermediates too.
+bool fused_path(const gdr_problem_t* p) { return p->io_dtype == GDR_BF16 && p->chunk_size == 64; }
+
 Plan make_plan(const gdr_problem_t* p) {
     Plan pl;
     pl.Ttot = p->batch * p->seq_len;
-    int64_t cap = pl.Ttot / 64 + p->num_seqs;
+    const size_t C = (size_t)p->chunk_size;
+    const size_t CP = C < 32 ? 32 : C;             // chunk positions padded to whole 32-position pairs
+    int64_t cap = pl.Ttot / (int64_t)C + p->num_seqs;
     if (cap < 1) cap = 1;
     pl.nt_cap = (int32_t)cap;
     const size_t es = p->io_dtype == GDR_BF16 ? 2 : 4;
@@ -96,26 +102,26 @@ Plan make_plan(const gdr_problem_t* p) {
     pl.off_len = take(cap * 4);
     pl.off_first = take(((size_t)p->num_seqs + 1) * 4);
     pl.off_G = take(T * Nv * 4);
-    const bool bf = p->io_dtype == GDR_BF16;
-    pl.off_R = take(bf ? cap * Nv * 64 * 8 : 0);   // decay factors, chunk-major (float2)
-    pl.sz_Tf = bf ? Nv * 6 * 2 * 512 * es : 0;   // T = A diag(beta): 6 split pair fragments
+    const bool fused = fused_path(p);
+    pl.off_R = take(fused ? cap * Nv * 64 * 8 : 0);   // decay factors, chunk-major (float2)
+    pl.sz_Tf = fused ? Nv * 6 * 2 * 512 * es : 0;   // T = A diag(beta): 6 split pair fragments
     pl.off_Tf = take(cap * pl.sz_Tf);
-    pl.off_Pf = take(cap * pl.sz_Tf);             // score block: same six split pair fragments
+    pl.off_Pf = take(cap * pl.sz_Tf);                // score block: same six split pair fragments
     const size_t fused_end = off;
-    pl.sz_A = T * Nv * 64 * 4;
+    pl.sz_A = T * Nv * C * 4;
     pl.off_A = take(pl.sz_A);
-    pl.sz_W = Nv * 64 * dk * 4;            // per chunk
+    pl.sz_W = Nv * C * dk * 4;             // per chunk
     pl.off_W = take(cap * pl.sz_W);
-    pl.sz_U = Nv * 64 * dv * 4;
+    pl.sz_U = Nv * C * dv * 4;
     pl.off_U = take(cap * pl.sz_U);
-    pl.sz_KT = Nk * 64 * dk * es;
+    pl.sz_KT = Nk * CP * dk * es;
     pl.off_KT = take(cap * pl.sz_KT);
     pl.sz_H = Nv * dk * dv * 4;
     pl.off_H = take(cap * pl.sz_H);
-    pl.sz_VN = Nv * 64 * dv * 4;
+    pl.sz_VN = Nv * CP * dv * 4;
     pl.off_VN = take(cap * pl.sz_VN);
     pl.reference = off;
-    pl.production = bf ? fused_end : off;
+    pl.production = fused ? fused_end : off;
     return pl;
 }
 
@@ -181,11 +187,12 @@ gdr_status_t run(const gdr_problem_t* p, const void* q, const void* k, const voi
     if (((uintptr_t)ws & 255) != 0) return fail(GDR_ERR_WORKSPACE, "workspace not 256-byte aligned");
     size_t need = reference ? pl.reference : pl.production;
 
+    const int64_t C = p->chunk_size;
     int64_t nt = 0, max_chunks = 0;
     for (int32_t n = 0; n < p->num_seqs; ++n) {
         const int64_t len = cu_host ? (int64_t)cu_host[n + 1] - cu_host[n] : p->seq_len;
-        nt += (len + 63) / 64;
-        max_chunks = (len + 63) / 64 > max_chunks ? (len + 63) / 64 : max_chunks;
+        nt += (len + C - 1) / C;
+        max_chunks = (len + C - 1) / C > max_chunks ? (len + C - 1) / C : max_chunks;
     }
     if (nt > pl.nt_cap) return fail(GDR_ERR_SEQLENS, "chunk count %lld exceeds capacity", (long long)nt);
 
@@ -202,7 +209,7 @@ gdr_status_t run(const gdr_problem_t* p, const void* q, const void* k, const voi
         if (seg_chunks > 0 && seg_chunks < max_chunks) {
             for (int32_t n = 0; n < p->num_seqs; ++n) {
                 const int64_t len = cu_host ? (int64_t)cu_host[n + 1] - cu_host[n] : p->seq_len;
-                nseg += ((len + 63) / 64 + seg_chunks - 1) / seg_chunks;
+                nseg += ((len + C - 1) / C + seg_chunks - 1) / seg_chunks;
             }
         } else {
             seg_chunks = 0;
@@ -220,6 +227,7 @@ gdr_status_t run(const gdr_problem_t* p, const void* q, const void* k, const voi
     a.bf16 = p->io_dtype == GDR_BF16;
     a.dk = p->head_dim_qk;
     a.dv = p->head_dim_v;
+    a.C = p->chunk_size;
     a.Nk = p->num_qk_heads;
     a.Nv = p->num_v_heads;
     a.N = p->num_seqs;

@@ -2,7 +2,9 @@
 //
 // Method (FLA DeltaNet article on pnsm.cn, sections 2.3-2.4 and 3.1-3.4;
 // ChunkGatedDeltaRule math page, section 3, formulas (1)-(6)). Per chunk of
-// C = 64 tokens and value head h (q/k head kh = h / (Nv/Nk)):
+// C tokens (C = 64; the five-kernel path also takes C = 16 and 32, the chunk
+// sizes the FLA article's tests sweep, section 6) and value head h (q/k head
+// kh = h / (Nv/Nk)):
 //   G     = chunk-local inclusive prefix sum of g                       (K1)
 //   L_ij  = beta_i (k_i . k_j) exp(G_i - G_j), i > j;  A = (I + L)^-1    (K2)
 //   W     = A diag(beta exp(G)) K,  U = A diag(beta) V                   (K3)
@@ -26,13 +28,13 @@ __constant__ int kTPairTb[kTPairs] = {0, 1, 2, 2, 3, 3};
 __constant__ int kTPairTp[kTPairs] = {0, 0, 0, 1, 0, 1};
 
 // ============================================================ chunk table
-// Builds, from the sequence offsets, the list of chunks (sequence id, first
-// token, length) numbered sequence by sequence, and the first chunk of each
-// sequence. One block; sequences are scanned 1024 at a time. Offsets are
+// Builds, from the sequence offsets, the list of chunks of C tokens (sequence
+// id, first token, length) numbered sequence by sequence, and the first chunk
+// of each sequence. One block; sequences are scanned 1024 at a time. Offsets are
 // clamped to [0, Ttot] and chunk indices to the table capacity, so inconsistent
 // offsets can never send a later kernel outside its buffers.
 __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict__ cu, int64_t T_row,
-                                                       int32_t N, int64_t Ttot, int32_t cap,
+                                                       int32_t N, int64_t Ttot, int32_t cap, int32_t C,
                                                        int32_t* __restrict__ chunk_seq,
                                                        int32_t* __restrict__ chunk_start,
                                                        int32_t* __restrict__ chunk_len,
@@ -55,7 +57,7 @@ __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict_
             s = s < 0 ? 0 : (s > Ttot ? Ttot : s);
             e = e < s ? s : (e > Ttot ? Ttot : e);
         }
-        const int32_t nch = (int32_t)((e - s + kChunk - 1) / kChunk);
+        const int32_t nch = (int32_t)((e - s + C - 1) / C);
         scan[tid] = nch;   // chunks of sequence n
         __syncthreads();
         for (int off = 1; off < 1024; off <<= 1) {         // inclusive Hillis-Steele scan
@@ -84,8 +86,8 @@ __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict_
         int64_t e = cu ? (int64_t)cu[n + 1] : (int64_t)(n + 1) * T_row;
         s = s < 0 ? 0 : (s > Ttot ? Ttot : s);
         e = e < s ? s : (e > Ttot ? Ttot : e);
-        const int64_t cs = s + (int64_t)(c - seq_first[n]) * kChunk;
-        const int64_t ce = cs + kChunk < e ? cs + kChunk : e;
+        const int64_t cs = s + (int64_t)(c - seq_first[n]) * C;
+        const int64_t ce = cs + C < e ? cs + C : e;
         const bool empty = !(ce > cs);
         chunk_seq[c] = n;
         chunk_start[c] = empty ? 0 : (int32_t)cs;          // empty entries point at token 0
@@ -106,6 +108,7 @@ __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict_
 // chunk-major, [chunk][head][64 positions] with zeros past the chunk end, so
 // that the sequential pass reads the factors of one (chunk, head) as one
 // contiguous 512-byte block.
+template <int C>
 __global__ __launch_bounds__(256) void k_gate_cumsum(const float* __restrict__ g,
                                                       const int32_t* __restrict__ chunk_start,
                                                       const int32_t* __restrict__ chunk_len,
@@ -116,37 +119,37 @@ __global__ __launch_bounds__(256) void k_gate_cumsum(const float* __restrict__ g
     const int32_t c = (int32_t)(p / Nv), h = (int32_t)(p % Nv);
     const int64_t s = chunk_start[c];
     const int32_t L = chunk_len[c];
-    float x[kChunk];
+    float x[C];
 #pragma unroll
-    for (int32_t i = 0; i < kChunk; ++i) x[i] = (g && i < L) ? g[(s + i) * Nv + h] : 0.f;   // independent loads
+    for (int32_t i = 0; i < C; ++i) x[i] = (g && i < L) ? g[(s + i) * Nv + h] : 0.f;   // independent loads
     float acc = 0.f;
 #pragma unroll
-    for (int32_t i = 0; i < kChunk; ++i) {
+    for (int32_t i = 0; i < C; ++i) {
         acc += x[i];
         x[i] = acc;                              // x now holds G (positions past the end repeat G_last)
         if (i < L) G[(s + i) * Nv + h] = acc;
     }
     if (R) {
         const float g_last = L > 0 ? x[L - 1] : 0.f;
-        f32x2* Rc = R + ((int64_t)c * Nv + h) * kChunk;
+        f32x2* Rc = R + ((int64_t)c * Nv + h) * C;
 #pragma unroll
-        for (int32_t i = 0; i < kChunk; ++i)
+        for (int32_t i = 0; i < C; ++i)
             Rc[i] = i < L ? f32x2{__expf(x[i]), __expf(g_last - x[i])} : f32x2{0.f, 0.f};
     }
 }
 
 // ============================================================ K2: A-build + solve
-// One workgroup (4 wavefronts) per (chunk, q/k head); it serves the Nv/Nk
+// One workgroup (C/16 wavefronts) per (chunk, q/k head); it serves the Nv/Nk
 // value heads that share the key head, computing K K^T once (FLA DeltaNet
 // article, section 3.1: beta-scaled K K^T, strictly lower part).
 //   1. K chunk -> LDS; wave w forms the K K^T tiles of block row w on MFMA.
 //   2. Per value head: L = tril(beta_i (k_i.k_j) exp(G_i - G_j), -1) -> LDS (fp32).
-//   3. The four 16x16 diagonal blocks of A = (I + L)^-1 by forward substitution
+//   3. The C/16 16x16 diagonal blocks of A = (I + L)^-1 by forward substitution
 //      in fp32, one column per lane (ChunkGatedDeltaRule page, section 3.1,
 //      row-recursive correction; FLA DeltaNet article, section 3.2, 16x16
 //      blocks).
 //   4. Off-diagonal blocks by block substitution on MFMA, merging
-//      16 -> 32 -> 64 (FLA DeltaNet article, section 3.2):
+//      16 -> 32 -> 64 as far as C reaches (FLA DeltaNet article, section 3.2):
 //        A_ij = -A_ii L_ij A_jj for the two 16-blocks below the diagonal of each
 //        32-block, then the lower-left 32x32 block = -A_bot L_bl A_top.
 //      Both operands are derived values, so each product takes the split
@@ -154,15 +157,15 @@ __global__ __launch_bounds__(256) void k_gate_cumsum(const float* __restrict__ g
 //   5. A rows (fp32) -> global, zero above the diagonal and past the chunk end
 //      (when A_out is given), and/or T = A diag(beta) (FLA DeltaNet article,
 //      section 2.3: T absorbs diag(beta)) as split (hi, lo) pair fragments of
-//      its lower-triangular 16 x 32 blocks for the fused state pass (when Tf
-//      is given).
-//   6. When Pf is given (fused pipeline): the intra-chunk score block
+//      its lower-triangular 16 x 32 blocks for the fused state pass (C = 64,
+//      when Tf is given).
+//   6. When Pf is given (fused pipeline, C = 64): the intra-chunk score block
 //      P = (Q K^T) (.) D, D_ij = exp(G_i - G_j) for j <= i (ChunkGatedDeltaRule
 //      page, formula (5); FLA DeltaNet article, section 2.4), as split pair
 //      fragments in the same six-block layout as T, so that the state pass
 //      does not recompute it for every dv tile. Q K^T is formed once per key
 //      head; the decay is applied per value head.
-template <typename T, int DK>
+template <typename T, int DK, int C>
 __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k, const T* __restrict__ q,
                                                          const void* __restrict__ beta, int beta_f32,
                                                          const float* __restrict__ G,
@@ -170,19 +173,22 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
                                                          const int32_t* __restrict__ chunk_len,
                                                          int32_t Nk, int32_t Nv, float* __restrict__ A_out,
                                                          T* __restrict__ Tf, T* __restrict__ Pf) {
+    static_assert(C == 16 || C == 32 || C == 64, "chunk size");
+    constexpr int NTB = C / 16;                // 16-row blocks of the chunk, one wavefront each
+    constexpr int NTHR = 64 * NTB;
     constexpr int KP = DK + 8;                 // padded LDS row (elements)
-    constexpr int SEGS = kChunk * (DK / 8) / 256;   // 16-byte row segments per thread
+    constexpr int SEGS = C * (DK / 8) / NTHR;  // 16-byte row segments per thread
     // The K and Q tiles are only needed until the K K^T and Q K^T tiles are in
     // registers; L and A reuse their LDS afterwards.
-    constexpr int TILE_BYTES = 2 * kChunk * KP * (int)sizeof(T);
-    constexpr int LP = kChunk + 4;             // L and A row pitch (floats): 16-byte aligned rows
-    constexpr int LA_BYTES = 2 * kChunk * LP * 4;
+    constexpr int TILE_BYTES = 2 * C * KP * (int)sizeof(T);
+    constexpr int LP = C + 4;                  // L and A row pitch (floats): 16-byte aligned rows
+    constexpr int LA_BYTES = 2 * C * LP * 4;
     __shared__ __attribute__((aligned(16))) char smem[TILE_BYTES > LA_BYTES ? TILE_BYTES : LA_BYTES];
-    __shared__ __attribute__((aligned(16))) float bs[kChunk], gs[kChunk];
+    __shared__ __attribute__((aligned(16))) float bs[C], gs[C];
     T* Ks = reinterpret_cast<T*>(smem);
-    T* Qs = Ks + kChunk * KP;
+    T* Qs = Ks + C * KP;
     float (*Lf)[LP] = reinterpret_cast<float (*)[LP]>(smem);
-    float (*Af)[LP] = Lf + kChunk;
+    float (*Af)[LP] = Lf + C;
 
     const int c = blockIdx.x, kh = blockIdx.y;
     const int64_t s = chunk_start[c];
@@ -196,7 +202,7 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
     float b_nx = 0.f, g_nx = 0.f;
     auto fetch_gates = [&](int hh) {
         const int h = kh * group + hh;
-        if (tid < kChunk && tid < L) {
+        if (tid < C && tid < L) {
             b_nx = load_beta(beta, (s + tid) * Nv + h, beta_f32);
             g_nx = G[(s + tid) * Nv + h];
         } else {
@@ -210,7 +216,7 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
         v8 kv[SEGS], qv[SEGS];
 #pragma unroll
         for (int i = 0; i < SEGS; ++i) {
-            const int idx = tid + 256 * i, row = idx / (DK / 8), seg = idx % (DK / 8);
+            const int idx = tid + NTHR * i, row = idx / (DK / 8), seg = idx % (DK / 8);
             kv[i] = zero_pair<T>();
             qv[i] = zero_pair<T>();
             if (row < L) {
@@ -221,7 +227,7 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
         fetch_gates(0);
 #pragma unroll
         for (int i = 0; i < SEGS; ++i) {
-            const int idx = tid + 256 * i, row = idx / (DK / 8), seg = idx % (DK / 8);
+            const int idx = tid + NTHR * i, row = idx / (DK / 8), seg = idx % (DK / 8);
             *reinterpret_cast<v8*>(&Ks[row * KP + seg * 8]) = kv[i];
             if (Pf) *reinterpret_cast<v8*>(&Qs[row * KP + seg * 8]) = qv[i];
         }
@@ -229,9 +235,9 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
     __syncthreads();
 
     // K K^T tiles of block row `wave`: kk[j] holds rows 16*wave + 4*qd + jj, column 16*j + r.
-    f32x4 kk[4];
+    f32x4 kk[NTB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NTB; ++j) {
         kk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (j <= wave) {
 #pragma unroll
@@ -243,9 +249,9 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
         }
     }
     // transposed score tiles of block row `wave`: qk[j] holds k_{16j+4qd+jj} . q_{16*wave+r}
-    f32x4 qk[4];
+    f32x4 qk[NTB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NTB; ++j) {
         qk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (Pf && j <= wave) {
 #pragma unroll
@@ -258,14 +264,14 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
     }
     __syncthreads();                           // tiles consumed: the LDS now holds L and A
     // the two strictly-upper 16x16 blocks of A that the block merges read are zero
-    for (int idx = tid; idx < 2 * 256; idx += 256) {
+    for (int idx = tid; idx < (NTB / 2) * 256; idx += NTHR) {
         const int blk = idx >> 8, e = idx & 255, row = blk * 32 + (e >> 4), col = blk * 32 + 16 + (e & 15);
         Af[row][col] = 0.f;
     }
 
     for (int hh = 0; hh < group; ++hh) {
         const int h = kh * group + hh;
-        if (tid < kChunk) {
+        if (tid < C) {
             bs[tid] = b_nx;
             gs[tid] = g_nx;
         }
@@ -274,7 +280,7 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
 
         // 2. strictly lower L (every entry of the blocks on and below the diagonal)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NTB; ++j) {
             if (j <= wave) {
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
@@ -316,7 +322,7 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
 
         // 4a. A_ij = -A_ii (L_ij A_jj) for (i, j) = (1, 0) [wave 0] and (3, 2) [wave 1];
         //     contraction depth 16: pair elements 4..7 are zero.
-        if (wave < 2) {
+        if (wave < NTB / 2) {
             const int bi = 2 * wave + 1, bj = 2 * wave;
             float la[8], db[8], ai[8];
 #pragma unroll
@@ -335,32 +341,34 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
         __syncthreads();
 
         // 4b. lower-left 32x32 block = -A_bot (L_bl A_top); wave w < 2 takes column block w.
-        if (wave < 2) {
-            const int ct = wave;
-            float bt[8];
+        if constexpr (C == 64) {
+            if (wave < 2) {
+                const int ct = wave;
+                float bt[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                bt[e] = Af[4 * qd + e][ct * 16 + r];
-                bt[4 + e] = Af[16 + 4 * qd + e][ct * 16 + r];
-            }
-            const Split<T> b = split8<T>(bt);
-            f32x4 t1[2];
+                for (int e = 0; e < 4; ++e) {
+                    bt[e] = Af[4 * qd + e][ct * 16 + r];
+                    bt[4 + e] = Af[16 + 4 * qd + e][ct * 16 + r];
+                }
+                const Split<T> b = split8<T>(bt);
+                f32x4 t1[2];
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-                t1[rb] = mfma_dd<T>(load_split_row<T>(&Lf[32 + 16 * rb + r][0], qd), b, f32x4{0.f, 0.f, 0.f, 0.f});
-            const Split<T> b2 = split_acc_pair<T>(t1[0], t1[1]);
+                for (int rb = 0; rb < 2; ++rb)
+                    t1[rb] = mfma_dd<T>(load_split_row<T>(&Lf[32 + 16 * rb + r][0], qd), b, f32x4{0.f, 0.f, 0.f, 0.f});
+                const Split<T> b2 = split_acc_pair<T>(t1[0], t1[1]);
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                f32x4 t2 = mfma_dd<T>(load_split_row<T>(&Af[32 + 16 * rb + r][32], qd), b2, f32x4{0.f, 0.f, 0.f, 0.f});
+                for (int rb = 0; rb < 2; ++rb) {
+                    f32x4 t2 = mfma_dd<T>(load_split_row<T>(&Af[32 + 16 * rb + r][32], qd), b2, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) Af[32 + 16 * rb + 4 * qd + jj][ct * 16 + r] = -t2[jj];
+                    for (int jj = 0; jj < 4; ++jj) Af[32 + 16 * rb + 4 * qd + jj][ct * 16 + r] = -t2[jj];
+                }
             }
         }
         __syncthreads();
 
         // 5. rows of A for the valid tokens (fp32)
-        for (int idx = tid; A_out && idx < kChunk * 16; idx += 256) {
-            const int row = idx >> 4, seg = idx & 15;
+        for (int idx = tid; A_out && idx < C * (C / 4); idx += NTHR) {
+            const int row = idx / (C / 4), seg = idx % (C / 4);
             if (row < L) {
                 f32x4 val;
 #pragma unroll
@@ -368,52 +376,56 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
                     const int col = seg * 4 + e;
                     val[e] = (col <= row) ? Af[row][col] : 0.f;
                 }
-                *reinterpret_cast<f32x4*>(A_out + ((s + row) * Nv + h) * kChunk + seg * 4) = val;
+                *reinterpret_cast<f32x4*>(A_out + ((s + row) * Nv + h) * C + seg * 4) = val;
             }
         }
         // T = A diag(beta) pair fragments: pair p covers rows 16*tb + r and positions 32*tp + m(qd, e)
         // for (tb, tp) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1); rows past the chunk end are zero.
-        if (Tf) {
-            for (int p = wave; p < kTPairs; p += 4) {
-                const int tb = kTPairTb[p], tp = kTPairTp[p];
-                const int row = tb * 16 + r;
-                const int m0 = tp * 32 + 4 * qd;           // positions m0..m0+3 and m0+16..m0+19
-                const f32x4 a0 = *reinterpret_cast<const f32x4*>(&Af[row][m0]);
-                const f32x4 a1 = *reinterpret_cast<const f32x4*>(&Af[row][m0 + 16]);
-                const f32x4 b0 = *reinterpret_cast<const f32x4*>(&bs[m0]);
-                const f32x4 b1 = *reinterpret_cast<const f32x4*>(&bs[m0 + 16]);
-                float x[8];
+        if constexpr (C == 64) {
+            if (Tf) {
+                for (int p = wave; p < kTPairs; p += 4) {
+                    const int tb = kTPairTb[p], tp = kTPairTp[p];
+                    const int row = tb * 16 + r;
+                    const int m0 = tp * 32 + 4 * qd;           // positions m0..m0+3 and m0+16..m0+19
+                    const f32x4 a0 = *reinterpret_cast<const f32x4*>(&Af[row][m0]);
+                    const f32x4 a1 = *reinterpret_cast<const f32x4*>(&Af[row][m0 + 16]);
+                    const f32x4 b0 = *reinterpret_cast<const f32x4*>(&bs[m0]);
+                    const f32x4 b1 = *reinterpret_cast<const f32x4*>(&bs[m0 + 16]);
+                    float x[8];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[e] = (row < L && m0 + e <= row) ? a0[e] * b0[e] : 0.f;
-                    x[4 + e] = (row < L && m0 + 16 + e <= row) ? a1[e] * b1[e] : 0.f;
+                    for (int e = 0; e < 4; ++e) {
+                        x[e] = (row < L && m0 + e <= row) ? a0[e] * b0[e] : 0.f;
+                        x[4 + e] = (row < L && m0 + 16 + e <= row) ? a1[e] * b1[e] : 0.f;
+                    }
+                    const Split<T> sp = split8<T>(x);
+                    T* dst = Tf + (((int64_t)c * Nv + h) * kTPairs + p) * 2 * 512;
+                    store_frag<T>(dst, lane, sp.hi);
+                    if constexpr (kSplitNeeded<T>) store_frag<T>(dst + 512, lane, sp.lo);
                 }
-                const Split<T> sp = split8<T>(x);
-                T* dst = Tf + (((int64_t)c * Nv + h) * kTPairs + p) * 2 * 512;
-                store_frag<T>(dst, lane, sp.hi);
-                if constexpr (kSplitNeeded<T>) store_frag<T>(dst + 512, lane, sp.lo);
             }
         }
         // 6. score pairs of block row `wave`: P_ij = (q_i . k_j) exp(G_i - G_j), j <= i < L
-        if (Pf) {
-            const int i = wave * 16 + r;
-            f32x4 pt[4];
+        if constexpr (C == 64) {
+            if (Pf) {
+                const int i = wave * 16 + r;
+                f32x4 pt[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < 4; ++j) {
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int col = j * 16 + 4 * qd + jj;
-                    pt[j][jj] = (j <= wave && col <= i && i < L) ? qk[j][jj] * __expf(gs[i] - gs[col]) : 0.f;
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int col = j * 16 + 4 * qd + jj;
+                        pt[j][jj] = (j <= wave && col <= i && i < L) ? qk[j][jj] * __expf(gs[i] - gs[col]) : 0.f;
+                    }
                 }
-            }
-            const int pbase = (wave == 0) ? 0 : (wave == 1 ? 1 : (wave == 2 ? 2 : 4));
+                const int pbase = (wave == 0) ? 0 : (wave == 1 ? 1 : (wave == 2 ? 2 : 4));
 #pragma unroll
-            for (int tp = 0; tp < 2; ++tp) {
-                if (2 * tp <= wave) {
-                    const Split<T> sp = split_acc_pair<T>(pt[2 * tp], pt[2 * tp + 1]);
-                    T* dst = Pf + (((int64_t)c * Nv + h) * kTPairs + pbase + tp) * 2 * 512;
-                    store_frag<T>(dst, lane, sp.hi);
-                    if constexpr (kSplitNeeded<T>) store_frag<T>(dst + 512, lane, sp.lo);
+                for (int tp = 0; tp < 2; ++tp) {
+                    if (2 * tp <= wave) {
+                        const Split<T> sp = split_acc_pair<T>(pt[2 * tp], pt[2 * tp + 1]);
+                        T* dst = Pf + (((int64_t)c * Nv + h) * kTPairs + pbase + tp) * 2 * 512;
+                        store_frag<T>(dst, lane, sp.hi);
+                        if constexpr (kSplitNeeded<T>) store_frag<T>(dst + 512, lane, sp.lo);
+                    }
                 }
             }
         }
@@ -422,7 +434,7 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
 }
 
 // ============================================================ K3: w/u products
-// One workgroup (4 wavefronts) per (chunk, q/k head). Formulas (1) and (2) of
+// One workgroup (C/16 wavefronts) per (chunk, q/k head). Formulas (1) and (2) of
 // the ChunkGatedDeltaRule page (FLA DeltaNet article, section 3.3, where
 // diag(beta) is absorbed into one operand):
 //   W = (A diag(beta exp(G))) K  -> stored as W^T tiles, which in accumulator
@@ -432,17 +444,23 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
 // K^T and V^T are staged in LDS so that the contraction over chunk positions
 // reads contiguous LDS rows; the key head's K^T is also written out once, as
 // pair fragments, for the state pass. W and U are stored in fp32.
-template <typename T, int DK, int DV>
+// Wavefront w owns chunk positions 16w..16w+15 (C / 16 wavefronts). Products
+// over positions take them in 32-position pairs; for C = 16 the second half
+// of the one pair is zero.
+template <typename T, int DK, int DV, int C>
 __global__ __launch_bounds__(256) void k_wu(const T* __restrict__ k, const T* __restrict__ v,
                                              const void* __restrict__ beta, int beta_f32,
                                              const float* __restrict__ G, const float* __restrict__ A,
                                              const int32_t* __restrict__ chunk_start,
                                              const int32_t* __restrict__ chunk_len, int32_t Nk, int32_t Nv,
                                              float* __restrict__ Wf, float* __restrict__ Uf, T* __restrict__ KTf) {
-    constexpr int MP = kChunk + 8;             // padded LDS row over chunk positions
+    constexpr int NTB = C / 16, NTHR = 64 * NTB;
+    constexpr int CP = C < 32 ? 32 : C;        // positions padded to whole pairs
+    constexpr int NTP = CP / 32;
+    constexpr int MP = CP + 8;                 // padded LDS row over chunk positions
     __shared__ __attribute__((aligned(16))) T KTs[DK * MP];
     __shared__ __attribute__((aligned(16))) T VTs[DV * MP];
-    __shared__ float bs[kChunk], sc[kChunk];
+    __shared__ float bs[CP], sc[CP];
 
     const int c = blockIdx.x, kh = blockIdx.y;
     const int64_t s = chunk_start[c];
@@ -451,8 +469,8 @@ __global__ __launch_bounds__(256) void k_wu(const T* __restrict__ k, const T* __
     typedef typename Vec<T>::v8 v8;
 
     // K^T of the chunk (zero past the chunk end); consecutive threads take consecutive positions.
-    for (int idx = tid; idx < kChunk * (DK / 8); idx += 256) {
-        const int m = idx & 63, seg = idx >> 6;
+    for (int idx = tid; idx < CP * (DK / 8); idx += NTHR) {
+        const int m = idx % CP, seg = idx / CP;
         v8 val = zero_pair<T>();
         if (m < L) val = *reinterpret_cast<const v8*>(k + ((s + m) * Nk + kh) * DK + seg * 8);
 #pragma unroll
@@ -461,10 +479,10 @@ __global__ __launch_bounds__(256) void k_wu(const T* __restrict__ k, const T* __
     __syncthreads();
 
     // K^T pair fragments for the state pass: [c][kh][db][tp]
-    for (int f = wave; f < (DK / 16) * 2; f += 4) {
-        const int db = f >> 1, tp = f & 1;
+    for (int f = wave; f < (DK / 16) * NTP; f += NTB) {
+        const int db = f / NTP, tp = f % NTP;
         v8 val = load_pair_row<T>(&KTs[(db * 16 + r) * MP + tp * 32], qd);
-        store_frag<T>(KTf + (((int64_t)c * Nk + kh) * (DK / 16) * 2 + f) * 512, lane, val);
+        store_frag<T>(KTf + (((int64_t)c * Nk + kh) * (DK / 16) * NTP + f) * 512, lane, val);
     }
 
     const int group = Nv / Nk;
@@ -473,13 +491,13 @@ __global__ __launch_bounds__(256) void k_wu(const T* __restrict__ k, const T* __
     for (int hh = 0; hh < group; ++hh) {
         const int h = kh * group + hh;
         __syncthreads();                       // previous head's readers are done with VTs / sc
-        if (tid < kChunk) {
+        if (tid < CP) {
             const float bm = tid < L ? load_beta(beta, (s + tid) * Nv + h, beta_f32) : 0.f;
             bs[tid] = bm;
             sc[tid] = tid < L ? bm * __expf(G[(s + tid) * Nv + h]) : 0.f;
         }
-        for (int idx = tid; idx < kChunk * (DV / 8); idx += 256) {
-            const int m = idx & 63, seg = idx >> 6;
+        for (int idx = tid; idx < CP * (DV / 8); idx += NTHR) {
+            const int m = idx % CP, seg = idx / CP;
             v8 val = zero_pair<T>();
             if (m < L) val = *reinterpret_cast<const v8*>(v + ((s + m) * Nv + h) * DV + seg * 8);
 #pragma unroll
@@ -488,18 +506,18 @@ __global__ __launch_bounds__(256) void k_wu(const T* __restrict__ k, const T* __
         __syncthreads();
 
         // Row i of A over positions m, scaled by beta_m (for U) and beta_m exp(G_m) (for W).
-        Split<T> aU[2], aW[2];
+        Split<T> aU[NTP], aW[NTP];
 #pragma unroll
-        for (int tp = 0; tp < 2; ++tp) {
+        for (int tp = 0; tp < NTP; ++tp) {
             float xa[8], xu[8], xw[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) xa[e] = 0.f;
             if (i < L) {
-                const float* row = A + ((s + i) * Nv + h) * kChunk + tp * 32;
+                const float* row = A + ((s + i) * Nv + h) * C + tp * 32;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     xa[e] = row[4 * qd + e];
-                    xa[4 + e] = row[16 + 4 * qd + e];
+                    if (C > 16) xa[4 + e] = row[16 + 4 * qd + e];
                 }
             }
 #pragma unroll
@@ -516,9 +534,9 @@ __global__ __launch_bounds__(256) void k_wu(const T* __restrict__ k, const T* __
         for (int db = 0; db < DK / 16; ++db) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int tp = 0; tp < 2; ++tp)
+            for (int tp = 0; tp < NTP; ++tp)
                 acc = mfma_xd<T>(load_pair_row<T>(&KTs[(db * 16 + r) * MP + tp * 32], qd), aW[tp], acc);
-            float* dst = Wf + ((((int64_t)c * Nv + h) * 4 + tb) * (DK / 32) + (db >> 1)) * 512;
+            float* dst = Wf + ((((int64_t)c * Nv + h) * NTB + tb) * (DK / 32) + (db >> 1)) * 512;
             store_pair_half_f32(dst, lane, db & 1, acc);
         }
         // U tiles (tb, nb): rows i, columns dv
@@ -526,9 +544,9 @@ __global__ __launch_bounds__(256) void k_wu(const T* __restrict__ k, const T* __
         for (int nb = 0; nb < DV / 16; ++nb) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int tp = 0; tp < 2; ++tp)
+            for (int tp = 0; tp < NTP; ++tp)
                 acc = mfma_dx<T>(aU[tp], load_pair_row<T>(&VTs[(nb * 16 + r) * MP + tp * 32], qd), acc);
-            store_tile_f32(Uf + ((((int64_t)c * Nv + h) * 4 + tb) * (DV / 16) + nb) * 256, lane, acc);
+            store_tile_f32(Uf + ((((int64_t)c * Nv + h) * NTB + tb) * (DV / 16) + nb) * 256, lane, acc);
         }
     }
 }
@@ -546,7 +564,7 @@ __global__ __launch_bounds__(256) void k_wu(const T* __restrict__ k, const T* __
 // For segment-parallel state passing: the state may start as I
 // (init_identity; the grid then covers dk columns), U == NULL stands for
 // U = 0, and H and V_new are written only when their pointers are given.
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, int C>
 __global__ __launch_bounds__(64) void k_state(const float* __restrict__ Wf, const float* __restrict__ Uf,
                                                const T* __restrict__ KTf, const float* __restrict__ G,
                                                const float* __restrict__ S0, int init_identity,
@@ -555,6 +573,7 @@ __global__ __launch_bounds__(64) void k_state(const float* __restrict__ Wf, cons
                                                const int32_t* __restrict__ seq_first, int32_t Nk, int32_t Nv,
                                                float* __restrict__ Hf, float* __restrict__ VNf, float* __restrict__ ST) {
     constexpr int NDB = DK / 16, NKP = DK / 32, NNB = DV / 16;
+    constexpr int NTB = C / 16, NTP = C < 32 ? 1 : C / 32;   // 16-row blocks, 32-position pairs
     const int n = blockIdx.x, h = blockIdx.y, nb = blockIdx.z;
     const int lane = threadIdx.x, r = lane & 15, qd = lane >> 4;
     const int kh = h / (Nv / Nk);
@@ -587,40 +606,46 @@ __global__ __launch_bounds__(64) void k_state(const float* __restrict__ Wf, cons
             sb[kp] = split_acc_pair<T>(S[2 * kp], S[2 * kp + 1]);
         }
 
-        // V_new = U - W S for the 4 blocks of 16 chunk positions
-        f32x4 vn[4];
-        const float* wsrc = Wf + ((int64_t)c * Nv + h) * 4 * NKP * 512;
-        const float* usrc = Uf + ((int64_t)c * Nv + h) * 4 * NNB * 256;
+        // V_new = U - W S for the blocks of 16 chunk positions (zero in the padding of C = 16)
+        f32x4 vn[2 * NTP];
+        const float* wsrc = Wf + ((int64_t)c * Nv + h) * NTB * NKP * 512;
+        const float* usrc = Uf + ((int64_t)c * Nv + h) * NTB * NNB * 256;
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
+        for (int tb = NTB; tb < 2 * NTP; ++tb) vn[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
             f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kp = 0; kp < NKP; ++kp)
                 x = mfma_dd<T>(split_v8<T>(load_frag_f32(wsrc + (tb * NKP + kp) * 512, lane)), sb[kp], x);
             vn[tb] = (Uf ? load_tile_f32(usrc + (tb * NNB + nb) * 256, lane) : f32x4{0.f, 0.f, 0.f, 0.f}) - x;
         }
-        float* vdst = VNf + (((int64_t)c * Nv + h) * NNB + nb) * 2 * 512;
+        float* vdst = VNf + (((int64_t)c * Nv + h) * NNB + nb) * NTP * 512;
 #pragma unroll
-        for (int tb = 0; tb < 4 && VNf; ++tb) store_pair_half_f32(vdst + (tb >> 1) * 512, lane, tb & 1, vn[tb]);
+        for (int tb = 0; tb < 2 * NTP && VNf; ++tb)
+            store_pair_half_f32(vdst + (tb >> 1) * 512, lane, tb & 1, vn[tb]);
 
         // decay each position to the chunk end; positions past the end contribute nothing
-        f32x4 vd[4];
+        f32x4 vd[2 * NTP];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+        for (int tb = 0; tb < 2 * NTP; ++tb)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = tb * 16 + 4 * qd + j;
                 vd[tb][j] = row < L ? vn[tb][j] * __expf(g_last - G[(s + row) * Nv + h]) : 0.f;
             }
-        const Split<T> vb[2] = {split_acc_pair<T>(vd[0], vd[1]), split_acc_pair<T>(vd[2], vd[3])};
+        Split<T> vb[NTP];
+#pragma unroll
+        for (int tp = 0; tp < NTP; ++tp) vb[tp] = split_acc_pair<T>(vd[2 * tp], vd[2 * tp + 1]);
 
         const float a_last = __expf(g_last);
-        const T* ksrc = KTf + ((int64_t)c * Nk + kh) * NDB * 2 * 512;
+        const T* ksrc = KTf + ((int64_t)c * Nk + kh) * NDB * NTP * 512;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             f32x4 acc = S[db] * a_last;
 #pragma unroll
-            for (int tp = 0; tp < 2; ++tp) acc = mfma_xd<T>(load_frag<T>(ksrc + (db * 2 + tp) * 512, lane), vb[tp], acc);
+            for (int tp = 0; tp < NTP; ++tp)
+                acc = mfma_xd<T>(load_frag<T>(ksrc + (db * NTP + tp) * 512, lane), vb[tp], acc);
             S[db] = acc;
         }
     }
@@ -633,20 +658,21 @@ __global__ __launch_bounds__(64) void k_state(const float* __restrict__ Wf, cons
 }
 
 // ============================================================ K5: output
-// One workgroup (4 wavefronts) per (chunk, value head); wave w produces the
+// One workgroup (C/16 wavefronts) per (chunk, value head); wave w produces the
 // output rows 16w..16w+15 for all dv (ChunkGatedDeltaRule page, formulas (4)
 // and (5); FLA DeltaNet article, section 3.4 "chunk_fwd_o"):
 //   O = scale [ diag(exp(G)) Q H + (Q K^T (.) D) V_new ],  D_ij = exp(G_i - G_j), j <= i.
 // The score block is formed transposed (K Q^T) so that its accumulator tiles
 // are the pair-fragment operand of the product with V_new; the upper
 // triangle and positions past the chunk end are masked explicitly.
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, int C>
 __global__ __launch_bounds__(256) void k_output(const T* __restrict__ q, const T* __restrict__ k,
                                                  const float* __restrict__ G, const float* __restrict__ Hf,
                                                  const float* __restrict__ VNf, const int32_t* __restrict__ chunk_start,
                                                  const int32_t* __restrict__ chunk_len, int32_t Nk, int32_t Nv,
                                                  float scale, int out_f32, void* __restrict__ o) {
     constexpr int NKP = DK / 32, NNB = DV / 16;
+    constexpr int NTB = C / 16, NTP = C < 32 ? 1 : C / 32;   // wavefronts (16-row blocks), 32-position pairs
     const int c = blockIdx.x, h = blockIdx.y;
     const int64_t s = chunk_start[c];
     const int L = chunk_len[c];
@@ -686,11 +712,11 @@ __global__ __launch_bounds__(256) void k_output(const T* __restrict__ q, const T
     }
 
     // scores, transposed: pt[tj] rows j = 16*tj + 4*qd + jj, column i
-    f32x4 pt[4];
+    f32x4 pt[2 * NTP];
 #pragma unroll
-    for (int tj = 0; tj < 4; ++tj) {
+    for (int tj = 0; tj < 2 * NTP; ++tj) {
         pt[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (tj <= tb) {
+        if (tj < NTB && tj <= tb) {
             const int jr = tj * 16 + r;
 #pragma unroll
             for (int kp = 0; kp < NKP; ++kp) {
@@ -706,16 +732,18 @@ __global__ __launch_bounds__(256) void k_output(const T* __restrict__ q, const T
             }
         }
     }
-    const Split<T> pa[2] = {split_acc_pair<T>(pt[0], pt[1]), split_acc_pair<T>(pt[2], pt[3])};
+    Split<T> pa[NTP];
+#pragma unroll
+    for (int tp = 0; tp < NTP; ++tp) pa[tp] = split_acc_pair<T>(pt[2 * tp], pt[2 * tp + 1]);
 
     // intra-chunk part: (Q K^T (.) D) V_new
-    const float* vsrc = VNf + ((int64_t)c * Nv + h) * NNB * 2 * 512;
+    const float* vsrc = VNf + ((int64_t)c * Nv + h) * NNB * NTP * 512;
 #pragma unroll
     for (int nb = 0; nb < NNB; ++nb) {
 #pragma unroll
-        for (int tp = 0; tp < 2; ++tp)
+        for (int tp = 0; tp < NTP; ++tp)
             if (2 * tp <= tb)
-                out[nb] = mfma_dd<T>(pa[tp], split_v8<T>(load_frag_f32(vsrc + (nb * 2 + tp) * 512, lane)), out[nb]);
+                out[nb] = mfma_dd<T>(pa[tp], split_v8<T>(load_frag_f32(vsrc + (nb * NTP + tp) * 512, lane)), out[nb]);
     }
 
 #pragma unroll
@@ -1316,16 +1344,17 @@ __global__ __launch_bounds__(256) void k_segment_scan(const int32_t* __restrict_
 }
 
 // ============================================================ launchers
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, int C>
 static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
     hipStream_t st = a.stream;
     auto mark = [&](int i) { if (ev) (void)hipEventRecord(ev[i], st); };
     const int32_t cap = a.nt_cap;
     const int32_t NT = a.nt;
-    constexpr bool kFused = std::is_same<T, bf16>::value;
+    constexpr bool kFused = std::is_same<T, bf16>::value && C == 64;
+    constexpr int NTHR = 64 * (C / 16);        // one wavefront per 16-row block of a chunk
     const bool fused = kFused && !a.reference;
     mark(0);
-    k_chunk_table<<<1, 1024, 0, st>>>(a.cu_dev, a.T_row, a.N, a.Ttot, cap, a.chunk_seq, a.chunk_start,
+    k_chunk_table<<<1, 1024, 0, st>>>(a.cu_dev, a.T_row, a.N, a.Ttot, cap, C, a.chunk_seq, a.chunk_start,
                                       a.chunk_len, a.seq_first);
     const bool segmented = a.nseg > 0 && a.N > 0;
     if (segmented)
@@ -1333,18 +1362,18 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
     mark(1);
     if (NT > 0) {
         const int64_t units = (int64_t)NT * a.Nv;
-        k_gate_cumsum<<<(unsigned)((units + 255) / 256), 256, 0, st>>>(a.g, a.chunk_start, a.chunk_len, NT, a.Nv, a.G,
-                                                                        fused ? (f32x2*)a.R : nullptr);
+        k_gate_cumsum<C><<<(unsigned)((units + 255) / 256), 256, 0, st>>>(a.g, a.chunk_start, a.chunk_len, NT, a.Nv,
+                                                                           a.G, fused ? (f32x2*)a.R : nullptr);
     }
     mark(2);
     if (NT > 0)
-        k_build_solve<T, DK><<<dim3(NT, a.Nk), 256, 0, st>>>((const T*)a.k, (const T*)a.q, a.beta, a.beta_f32, a.G,
+        k_build_solve<T, DK, C><<<dim3(NT, a.Nk), NTHR, 0, st>>>((const T*)a.k, (const T*)a.q, a.beta, a.beta_f32, a.G,
                                                             a.chunk_start, a.chunk_len, a.Nk, a.Nv,
                                                             fused ? nullptr : (float*)a.A, (T*)a.Tf,
                                                             fused ? (T*)a.Pf : nullptr);
     mark(3);
     if (NT > 0 && !fused)
-        k_wu<T, DK, DV><<<dim3(NT, a.Nk), 256, 0, st>>>((const T*)a.k, (const T*)a.v, a.beta, a.beta_f32, a.G,
+        k_wu<T, DK, DV, C><<<dim3(NT, a.Nk), NTHR, 0, st>>>((const T*)a.k, (const T*)a.v, a.beta, a.beta_f32, a.G,
                                                        (const float*)a.A, a.chunk_start, a.chunk_len, a.Nk, a.Nv,
                                                        (float*)a.W, (float*)a.U, (T*)a.KT);
     mark(4);
@@ -1372,12 +1401,12 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
         if (!fused) {
             const float *W = (const float*)a.W, *U = (const float*)a.U;
             const T* KT = (const T*)a.KT;
-            k_state<T, DK, DV><<<gs, 64, 0, st>>>(W, U, KT, a.G, nullptr, 0, a.chunk_start, a.chunk_len, a.seg_first,
+            k_state<T, DK, DV, C><<<gs, 64, 0, st>>>(W, U, KT, a.G, nullptr, 0, a.chunk_start, a.chunk_len, a.seg_first,
                                                   a.Nk, a.Nv, nullptr, nullptr, a.Sloc);
-            k_state<T, DK, DK><<<gm, 64, 0, st>>>(W, nullptr, KT, a.G, nullptr, 1, a.chunk_start, a.chunk_len,
+            k_state<T, DK, DK, C><<<gm, 64, 0, st>>>(W, nullptr, KT, a.G, nullptr, 1, a.chunk_start, a.chunk_len,
                                                   a.seg_first, a.Nk, a.Nv, nullptr, nullptr, a.Mseg);
             k_segment_scan<DK, DV><<<gn, 256, 0, st>>>(a.seq_seg, a.S0, a.Sloc, a.Mseg, a.Nv, a.Sstart, a.ST);
-            k_state<T, DK, DV><<<gs, 64, 0, st>>>(W, U, KT, a.G, a.Sstart, 0, a.chunk_start, a.chunk_len,
+            k_state<T, DK, DV, C><<<gs, 64, 0, st>>>(W, U, KT, a.G, a.Sstart, 0, a.chunk_start, a.chunk_len,
                                                   a.seg_first, a.Nk, a.Nv, (float*)a.H, (float*)a.VN, nullptr);
         }
     } else if (a.N > 0) {
@@ -1390,24 +1419,24 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
             }
         }
         if (!fused)
-            k_state<T, DK, DV><<<dim3(a.N, a.Nv, DV / 16), 64, 0, st>>>((const float*)a.W, (const float*)a.U,
+            k_state<T, DK, DV, C><<<dim3(a.N, a.Nv, DV / 16), 64, 0, st>>>((const float*)a.W, (const float*)a.U,
                                                                        (const T*)a.KT, a.G, a.S0, 0, a.chunk_start,
                                                                        a.chunk_len, a.seq_first, a.Nk, a.Nv,
                                                                        (float*)a.H, (float*)a.VN, a.ST);
     }
     mark(5);
     if (NT > 0 && !fused)
-        k_output<T, DK, DV><<<dim3(NT, a.Nv), 256, 0, st>>>((const T*)a.q, (const T*)a.k, a.G, (const float*)a.H,
+        k_output<T, DK, DV, C><<<dim3(NT, a.Nv), NTHR, 0, st>>>((const T*)a.q, (const T*)a.k, a.G, (const float*)a.H,
                                                            (const float*)a.VN, a.chunk_start, a.chunk_len, a.Nk, a.Nv,
                                                            a.scale, a.out_f32, a.o);
     mark(6);
     return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, int C>
 static hipError_t dispatch_dims(const LaunchArgs& a, hipEvent_t* ev) {
 #define GDR_CASE(DKv, DVv) \
-    if (a.dk == DKv && a.dv == DVv) return launch_pipeline<T, DKv, DVv>(a, ev);
+    if (a.dk == DKv && a.dv == DVv) return launch_pipeline<T, DKv, DVv, C>(a, ev);
     GDR_CASE(32, 32) GDR_CASE(32, 64) GDR_CASE(32, 128)
     GDR_CASE(64, 32) GDR_CASE(64, 64) GDR_CASE(64, 128)
     GDR_CASE(128, 32) GDR_CASE(128, 64) GDR_CASE(128, 128)
@@ -1415,9 +1444,17 @@ static hipError_t dispatch_dims(const LaunchArgs& a, hipEvent_t* ev) {
     return hipErrorInvalidValue;
 }
 
+template <typename T>
+static hipError_t dispatch_chunk(const LaunchArgs& a, hipEvent_t* ev) {
+    if (a.C == 64) return dispatch_dims<T, 64>(a, ev);
+    if (a.C == 32) return dispatch_dims<T, 32>(a, ev);
+    if (a.C == 16) return dispatch_dims<T, 16>(a, ev);
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_forward(const LaunchArgs& a, hipEvent_t* events) {
-    if (a.bf16) return dispatch_dims<bf16>(a, events);
-    return dispatch_dims<float>(a, events);
+    if (a.bf16) return dispatch_chunk<bf16>(a, events);
+    return dispatch_chunk<float>(a, events);
 }
 
 }  // namespace gdr

@@ -9,6 +9,7 @@ namespace gdr {
 struct LaunchArgs {
     bool bf16;                 // compute/io type: bf16 (true) or fp32
     int dk, dv;
+    int C;                     // chunk size: 64, or 16 / 32 (five-kernel path)
     int32_t Nk, Nv, N;         // q/k heads, v heads, sequences
     int64_t T_row, Ttot;       // tokens per batch row (fixed length), total tokens
     int32_t nt, nt_cap;        // chunks used, chunk-table capacity
@@ -37,9 +38,9 @@ struct LaunchArgs {
     hipStream_t stream;
 };
 
-// Enqueues the whole forward on a.stream. bf16 inputs take the fused path
-// (state pass and output in one kernel) unless a.reference is set; fp32
-// inputs always take the five-kernel path. events: NULL, or 7 events recorded
+// Enqueues the whole forward on a.stream. bf16 inputs with C = 64 take the
+// fused path (state pass and output in one kernel) unless a.reference is set;
+// fp32 inputs and C = 16 or 32 take the five-kernel path. events: NULL, or 7 events recorded
 // before the first and after every one of the six stages.
 hipError_t launch_forward(const LaunchArgs& a, hipEvent_t* events);
 

@@ -10,12 +10,16 @@
  *
  * starting from S_0 = initial_state[n, h] (zeros when absent); the state after
  * the last token is returned as final_state[n, h]. The library computes this
- * with the chunkwise WY/UT algorithm (chunk size C = 64) in five HIP kernels:
- * gate prefix sums, A-build + triangular solve, w/u products, the sequential
- * state pass, and the output. For bf16 inputs gdr_chunk_fwd fuses the w/u
- * products and the output into the state pass (the products W S and U are
- * formed there as T (V - diag(exp(G)) K S) with T = A diag(beta)); fp32 inputs
- * and gdr_chunk_fwd_debug run the five kernels as separate launches.
+ * with the chunkwise WY/UT algorithm (chunk size C = 64, 32 or 16) in five HIP
+ * kernels: gate prefix sums, A-build + triangular solve, w/u products, the
+ * sequential state pass, and the output. For bf16 inputs with C = 64,
+ * gdr_chunk_fwd fuses the w/u products and the output into the state pass (the
+ * products W S and U are formed there as T (V - diag(exp(G)) K S) with
+ * T = A diag(beta)); fp32 inputs, C = 16 or 32, and gdr_chunk_fwd_debug run the
+ * five kernels as separate launches. The chunk size changes only the rounding
+ * order of the result (FLA DeltaNet article, section 6, tests the chunked
+ * form at several chunk sizes against the recurrence); it trades the serial
+ * depth T / C of the state pass against the C x C work of the solve.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -86,7 +90,7 @@ typedef struct {
     int32_t num_v_heads;    /* Nv >= 1, Nv % Nk == 0; V-head h reads q/k head h/(Nv/Nk) */
     int32_t head_dim_qk;    /* dk: 32, 64 or 128 in this build                     */
     int32_t head_dim_v;     /* dv: 32, 64 or 128 in this build                     */
-    int32_t chunk_size;     /* C: 64 in this build                                 */
+    int32_t chunk_size;     /* C: 64, 32 or 16                                     */
     int32_t num_seqs;       /* N: batch, or len(cu_seqlens) - 1                    */
     int32_t io_dtype;       /* gdr_dtype_t of q, k and v                           */
     int32_t beta_dtype;     /* gdr_dtype_t of beta: io_dtype or GDR_F32            */
@@ -206,7 +210,7 @@ gdr_status_t gdr_chunk_fwd_segmented(const gdr_problem_t* problem,
  * pointer is a caller-owned device buffer (NULL to skip) that receives a copy
  * of the workspace region in the layout the kernels use; sizes follow from
  * the problem and NT, the number of chunks (sum over sequences of
- * ceil(len / 64), numbered sequence by sequence in token order). T below is
+ * ceil(len / C), numbered sequence by sequence in token order). T below is
  * the input type: bf16 when io_dtype is bf16, fp32 when it is fp32. Values
  * derived inside the method are kept in fp32.
  *
@@ -218,20 +222,22 @@ gdr_status_t gdr_chunk_fwd_segmented(const gdr_problem_t* problem,
  *   lane, element j of lane l equal to Y[4*qd + j][r].
  *
  * Layouts (Nv = num_v_heads, Nk = num_qk_heads, c = chunk, i/j = position in
- * the chunk, tb = i / 16, db/kp = 16/32-blocks of dk, nb = 16-block of dv,
- * tp = 32-block of chunk positions):
+ * the chunk, tb = i / 16 (C / 16 blocks), db/kp = 16/32-blocks of dk, nb =
+ * 16-block of dv, tp = 32-block of chunk positions (NTP = max(1, C / 32)
+ * blocks; with C = 16 the one block's positions 16..31 hold zeros)):
  *   G    [Ttot][Nv] fp32                  chunk-local inclusive prefix sum of g
- *   A    [Ttot][Nv][64] fp32              row i of (I + L)^-1 for the token's chunk;
+ *   A    [Ttot][Nv][C] fp32               row i of (I + L)^-1 for the token's chunk;
  *                                         zero above the diagonal and past the chunk end
- *   W    [NT][Nv][4 tb][dk/32 kp] fp32 pair fragments (rows i, m = dk index)
- *   U    [NT][Nv][4 tb][dv/16 nb] fp32 accumulator tiles (rows i, columns dv)
- *   KT   [NT][Nk][dk/16 db][2 tp] T pair fragments of K^T (rows dk, m = position)
+ *   W    [NT][Nv][C/16 tb][dk/32 kp] fp32 pair fragments (rows i, m = dk index)
+ *   U    [NT][Nv][C/16 tb][dv/16 nb] fp32 accumulator tiles (rows i, columns dv)
+ *   KT   [NT][Nk][dk/16 db][NTP tp] T pair fragments of K^T (rows dk, m = position)
  *   H    [NT][Nv][dv/16 nb][dk/32 kp] fp32 pair fragments of the chunk's
  *                                     entering state transposed (rows dv, m = dk)
- *   VN   [NT][Nv][dv/16 nb][2 tp] fp32 pair fragments of V_new^T (rows dv, m = position)
+ *   VN   [NT][Nv][dv/16 nb][NTP tp] fp32 pair fragments of V_new^T (rows dv, m = position)
  *   T    [NT][Nv][6 pairs][2 hi/lo] bf16 pair fragments of T = A diag(beta)
  *        (rows i, m = position) for the blocks (tb, tp) = (0,0) (1,0) (2,0)
- *        (2,1) (3,0) (3,1); T = hi + lo. bf16 inputs only (NULL otherwise).
+ *        (2,1) (3,0) (3,1); T = hi + lo. bf16 inputs with C = 64 only (NULL
+ *        otherwise).
  * Chunk positions past the end of a sequence hold zeros in W, U, KT and VN.
  */
 typedef struct {

@@ -31,24 +31,25 @@ def unpack_tile(tile):
 
 
 def W_natural(W):
-    """[NT, Nv, 4, dk/32, 64, 8] -> [NT, Nv, 64, dk] (rows = chunk position)."""
-    X = unpack_pair(W)                                    # [NT, Nv, 4, nkp, 16, 32]
-    NT, Nv, _, nkp = X.shape[:4]
-    return X.transpose(0, 1, 2, 4, 3, 5).reshape(NT, Nv, 64, nkp * 32)
+    """[NT, Nv, C/16, dk/32, 64, 8] -> [NT, Nv, C, dk] (rows = chunk position)."""
+    X = unpack_pair(W)                                    # [NT, Nv, ntb, nkp, 16, 32]
+    NT, Nv, ntb, nkp = X.shape[:4]
+    return X.transpose(0, 1, 2, 4, 3, 5).reshape(NT, Nv, ntb * 16, nkp * 32)
 
 
 def U_natural(U):
-    """[NT, Nv, 4, dv/16, 64, 4] -> [NT, Nv, 64, dv]."""
-    Y = unpack_tile(U)                                    # [NT, Nv, 4, nnb, 16, 16]
-    NT, Nv, _, nnb = Y.shape[:4]
-    return Y.transpose(0, 1, 2, 4, 3, 5).reshape(NT, Nv, 64, nnb * 16)
+    """[NT, Nv, C/16, dv/16, 64, 4] -> [NT, Nv, C, dv]."""
+    Y = unpack_tile(U)                                    # [NT, Nv, ntb, nnb, 16, 16]
+    NT, Nv, ntb, nnb = Y.shape[:4]
+    return Y.transpose(0, 1, 2, 4, 3, 5).reshape(NT, Nv, ntb * 16, nnb * 16)
 
 
 def KT_natural(KT):
-    """[NT, Nk, dk/16, 2, 64, 8] -> K [NT, Nk, 64, dk]."""
-    X = unpack_pair(KT)                                   # [NT, Nk, ndb, 2, 16(dk), 32(pos)]
-    NT, Nk, ndb = X.shape[:3]
-    KTn = X.transpose(0, 1, 2, 4, 3, 5).reshape(NT, Nk, ndb * 16, 64)
+    """[NT, Nk, dk/16, ntp, 64, 8] -> K [NT, Nk, 32 ntp, dk] (ntp = max(1, C/32);
+    with C = 16, positions 16..31 are the zero padding)."""
+    X = unpack_pair(KT)                                   # [NT, Nk, ndb, ntp, 16(dk), 32(pos)]
+    NT, Nk, ndb, ntp = X.shape[:4]
+    KTn = X.transpose(0, 1, 2, 4, 3, 5).reshape(NT, Nk, ndb * 16, ntp * 32)
     return KTn.transpose(0, 1, 3, 2)
 
 
@@ -61,15 +62,15 @@ def H_natural(H):
 
 
 def VN_natural(VN):
-    """[NT, Nv, dv/16, 2, 64, 8] -> V_new [NT, Nv, 64, dv]."""
-    X = unpack_pair(VN)                                   # [NT, Nv, nnb, 2, 16(dv), 32(pos)]
-    NT, Nv, nnb = X.shape[:3]
-    VT = X.transpose(0, 1, 2, 4, 3, 5).reshape(NT, Nv, nnb * 16, 64)
+    """[NT, Nv, dv/16, ntp, 64, 8] -> V_new [NT, Nv, 32 ntp, dv]."""
+    X = unpack_pair(VN)                                   # [NT, Nv, nnb, ntp, 16(dv), 32(pos)]
+    NT, Nv, nnb, ntp = X.shape[:4]
+    VT = X.transpose(0, 1, 2, 4, 3, 5).reshape(NT, Nv, nnb * 16, ntp * 32)
     return VT.transpose(0, 1, 3, 2)
 
 
 def chunk_rows_to_tokens(X, chunks, Ttot):
-    """[NT, H, 64, D] chunk-position rows -> [Ttot, H, D] token rows (valid rows only)."""
+    """[NT, H, C, D] chunk-position rows -> [Ttot, H, D] token rows (valid rows only)."""
     NT, H, _, D = X.shape
     out = np.zeros((Ttot, H, D))
     for c, (_, s, L) in enumerate(chunks):

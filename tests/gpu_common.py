@@ -27,12 +27,13 @@ def to_dev(inp, beta_f32=False):
     return d
 
 
-def run_gpu(inp, debug=False, beta_f32=False, output_final_state=True, out_f32=False):
+def run_gpu(inp, debug=False, beta_f32=False, output_final_state=True, out_f32=False, chunk_size=64):
     d = to_dev(inp, beta_f32)
     fn = api.chunk_fwd_debug if debug else api.chunk_fwd
     res = fn(d["q"], d["k"], d["v"], d["beta"], g=d["g"], scale=inp["scale"], initial_state=d["S0"],
              output_final_state=output_final_state, cu_seqlens=d["cu_seqlens"],
-             cu_seqlens_cpu=inp["cu_seqlens"], out_dtype=torch.float32 if out_f32 else None)
+             cu_seqlens_cpu=inp["cu_seqlens"], out_dtype=torch.float32 if out_f32 else None,
+             chunk_size=chunk_size)
     torch.cuda.synchronize()
     return res
 

@@ -56,12 +56,26 @@ def test_validate_accepts_good_problems(lib):
     assert status(prob(batch=1, seq_len=0, num_seqs=1), [0, 0]) == 0
     for d in (32, 64, 128):
         assert status(prob(dk=d, dv=128 if d == 32 else 32)) == 0
+    for C in (16, 32, 64):
+        assert status(prob(chunk_size=C)) == 0
+
+
+def test_workspace_scales_with_chunk_size(lib):
+    """Five-kernel intermediates scale with C (A rows of C entries, W and U of
+    C positions per chunk, more chunks for smaller C); bf16 with C = 64 takes
+    the fused path's smaller workspace."""
+    from chunkwise_gated_delta_local_amd import api
+    f32 = {C: api.workspace_size(prob(seq_len=4096, io_dtype=api.GDR_F32, beta_dtype=api.GDR_F32, chunk_size=C))
+           for C in (16, 32, 64)}
+    assert f32[16] > f32[64] and f32[32] > f32[64]
+    bf = {C: api.workspace_size(prob(seq_len=4096, chunk_size=C)) for C in (16, 32, 64)}
+    assert bf[64] < bf[32] and bf[64] < bf[16]
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=0), 2), (dict(seq_len=-1), 2), (dict(Nk=3, Nv=4), 2), (dict(Nk=0), 2),
     (dict(io_dtype=7), 3), (dict(beta_dtype=1, io_dtype=0), 3),
-    (dict(dk=48), 4), (dict(dv=256), 4), (dict(chunk_size=32), 4),
+    (dict(dk=48), 4), (dict(dv=256), 4), (dict(chunk_size=48), 4), (dict(chunk_size=128), 4),
     (dict(num_seqs=3), 2),
 ])
 def test_validate_rejects(lib, kw, code):

@@ -161,22 +161,29 @@ def test_empty_sequence_batch_returns_initial_state():
 
 # ------------------------------------------------------------ per-kernel parity
 KERNEL_CASES = [
-    ("cfg2", synth.WORKLOADS[2], 2),
+    ("cfg2", synth.WORKLOADS[2], 2, 64),
     ("gqa_varlen", synth.custom("gqa_varlen", B=1, T=0, Nk=2, Nv=4, dk=128, dv=128, dtype="bf16",
-                                lengths=(1, 63, 64, 65, 130)), 21),
-    ("f32", synth.custom("f32k", B=1, T=150, Nk=1, Nv=2, dk=32, dv=64, dtype="f32"), 22),
+                                lengths=(1, 63, 64, 65, 130)), 21, 64),
+    ("f32", synth.custom("f32k", B=1, T=150, Nk=1, Nv=2, dk=32, dv=64, dtype="f32"), 22, 64),
+    ("gqa_varlen_C32", synth.custom("gqa_varlen32", B=1, T=0, Nk=2, Nv=4, dk=128, dv=64, dtype="bf16",
+                                    lengths=(1, 31, 32, 33, 100)), 23, 32),
+    ("gqa_varlen_C16", synth.custom("gqa_varlen16", B=1, T=0, Nk=2, Nv=4, dk=64, dv=128, dtype="bf16",
+                                    lengths=(1, 15, 16, 17, 70)), 24, 16),
+    ("f32_C16", synth.custom("f32k16", B=1, T=75, Nk=1, Nv=2, dk=32, dv=64, dtype="f32"), 25, 16),
+    ("f32_C32", synth.custom("f32k32", B=2, T=70, Nk=1, Nv=1, dk=64, dv=32, dtype="f32"), 26, 32),
 ]
 
 
-@pytest.mark.parametrize("name,w,seed", KERNEL_CASES, ids=[c[0] for c in KERNEL_CASES])
-def test_intermediates_match_chunked_oracle(name, w, seed):
-    """Each of the five kernels against the chunked oracle's intermediate:
-    K1 -> G, K2 -> A, K3 -> W, U (and K^T), K4 -> H, V_new, S_T, K5 -> o."""
+@pytest.mark.parametrize("name,w,seed,C", KERNEL_CASES, ids=[c[0] for c in KERNEL_CASES])
+def test_intermediates_match_chunked_oracle(name, w, seed, C):
+    """Each of the five kernels against the chunked oracle's intermediate at
+    chunk size C: K1 -> G, K2 -> A, K3 -> W, U (and K^T), K4 -> H, V_new, S_T,
+    K5 -> o."""
     inp = synth.generate(w, seed=seed)
-    res = run_gpu(inp, debug=True, out_f32=True)
+    res = run_gpu(inp, debug=True, out_f32=True, chunk_size=C)
     x = oracle_inputs(inp)
     ref = chunked_forward(x["q"], x["k"], x["v"], x["beta"], x["g"], x["scale"], x["S0"], x["cu"],
-                          intermediates=True)
+                          chunk_size=C, intermediates=True)
     chunks = ref["chunks"]
     Ttot = x["q"].shape[0]
     tol = TOL[w.dtype]
@@ -211,8 +218,8 @@ def test_intermediates_match_chunked_oracle(name, w, seed):
         assert e <= tol, (name, key, e)
 
 
-@pytest.mark.parametrize("name,w,seed", KERNEL_CASES[:2], ids=[c[0] for c in KERNEL_CASES[:2]])
-def test_fused_path_matches_reference_path(name, w, seed):
+@pytest.mark.parametrize("name,w,seed,C", KERNEL_CASES[:2], ids=[c[0] for c in KERNEL_CASES[:2]])
+def test_fused_path_matches_reference_path(name, w, seed, C):
     """The production call (state pass and output fused) and the debug call
     (five separate kernels) compute the same result to fp32-level accuracy."""
     inp = synth.generate(w, seed=seed)
