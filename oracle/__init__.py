@@ -16,6 +16,10 @@ Two independent forms of the method:
 ``normalize.l2_normalize`` is the optional per-vector L2 normalisation of q
 and k that the token-by-token forward can apply first.
 
+``backward.recurrence_backward`` (NumPy) differentiates the token recurrence
+in reverse token order: dq, dk, dv, dbeta, dg and the initial state's
+gradient for given output and final-state gradients.
+
 All are pinned by the CPU tests in ``tests/test_oracle_*.py`` against closed
 forms, identities and brute-force products fixed by the pages and by algebra.
 Every function is pinned; none is "parity unpinned".
@@ -23,3 +27,4 @@ Every function is pinned; none is "parity unpinned".
 from .recurrence import recurrence, build  # noqa: F401
 from .chunked import chunked_forward  # noqa: F401
 from .normalize import l2_normalize  # noqa: F401
+from .backward import recurrence_backward  # noqa: F401
