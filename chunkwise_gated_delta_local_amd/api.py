@@ -24,6 +24,7 @@ _DTYPES = {torch.float32: GDR_F32, torch.bfloat16: GDR_BF16}
 EXPORTED = ("gdr_validate", "gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd_debug_workspace_size",
             "gdr_chunk_fwd", "gdr_chunk_fwd_debug", "gdr_chunk_fwd_timed", "gdr_recurrent_fwd",
             "gdr_chunk_fwd_segmented_workspace_size", "gdr_chunk_fwd_segmented",
+            "gdr_chunk_bwd_workspace_size", "gdr_chunk_bwd",
             "gdr_status_string", "gdr_last_error_message")
 
 
@@ -71,9 +72,12 @@ def load_library():
     lib.gdr_recurrent_fwd.argtypes = [PP, P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_int, P, P, P]
     lib.gdr_chunk_fwd_segmented_workspace_size.argtypes = [PP, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     lib.gdr_chunk_fwd_segmented.argtypes = fwd_args[:12] + [ctypes.c_int32] + fwd_args[12:] + [P]
+    lib.gdr_chunk_bwd_workspace_size.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdr_chunk_bwd.argtypes = fwd_args[:10] + [P] * 8 + [P, ctypes.c_size_t, P]
     for f in ("gdr_validate", "gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd_debug_workspace_size",
               "gdr_chunk_fwd", "gdr_chunk_fwd_debug", "gdr_chunk_fwd_timed", "gdr_recurrent_fwd",
-              "gdr_chunk_fwd_segmented_workspace_size", "gdr_chunk_fwd_segmented"):
+              "gdr_chunk_fwd_segmented_workspace_size", "gdr_chunk_fwd_segmented",
+              "gdr_chunk_bwd_workspace_size", "gdr_chunk_bwd"):
         getattr(lib, f).restype = ctypes.c_int
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_status_string.restype = ctypes.c_char_p
@@ -210,6 +214,66 @@ def recurrent_fwd(q, k, v, beta, g=None, scale=None, initial_state=None, output_
                                  ctypes.c_void_p(stream)))
     del cu_dev, cu_host
     return o, S_T
+
+
+class Backward:
+    """A prepared gdr_chunk_bwd call on fixed tensors, for repeated launches.
+    Gradient buffers (fp32) and the workspace are allocated once; each call
+    enqueues the whole backward (forward recompute included) on the stream
+    that was current at construction. d_o has o's dtype: the io dtype, or
+    float32 (out_dtype)."""
+
+    def __init__(self, q, k, v, beta, g=None, scale=None, initial_state=None, cu_seqlens=None,
+                 cu_seqlens_cpu=None, d_o=None, d_final_state=None, chunk_size=64, want_dg=True,
+                 want_dh0=True):
+        self.lib = load_library()
+        if d_o is None or d_o.shape != v.shape or d_o.dtype not in (q.dtype, torch.float32):
+            raise ValueError("d_o must be shaped like v, in the io dtype or float32")
+        prob, _o, _S, cu_dev, cu_host, scale = _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens,
+                                                        cu_seqlens_cpu, chunk_size, False, d_o.dtype,
+                                                        workspace=False)
+        N = prob.num_seqs
+        B, T, Nk, dk = q.shape
+        Nv, dv = v.shape[2], v.shape[3]
+        if d_final_state is not None and (d_final_state.shape != (N, Nv, dk, dv)
+                                          or d_final_state.dtype != torch.float32):
+            raise ValueError("d_final_state must be [N,Nv,dk,dv] float32")
+        for t in (d_o, d_final_state):
+            if t is not None and (t.device != q.device or not t.is_contiguous()):
+                raise ValueError("all tensors must be contiguous and on the same device")
+        dev = q.device
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.dq = torch.empty(q.shape, **f32)
+        self.dk = torch.empty(k.shape, **f32)
+        self.dv = torch.empty(v.shape, **f32)
+        self.dbeta = torch.empty(beta.shape, **f32)
+        self.dg = torch.empty(beta.shape, **f32) if want_dg else None
+        self.dh0 = torch.empty((N, Nv, dk, dv), **f32) if want_dh0 else None
+        n = ctypes.c_size_t(0)
+        self.problem = prob
+        _check(self.lib.gdr_chunk_bwd_workspace_size(ctypes.byref(prob), ctypes.byref(n)))
+        self.ws = torch.empty(int(n.value), dtype=torch.uint8, device=dev)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        self.args = [ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), ctypes.c_float(scale),
+                     _ptr(initial_state), _ptr(cu_dev), _ptr(cu_host), _ptr(d_o), _ptr(d_final_state),
+                     _ptr(self.dq), _ptr(self.dk), _ptr(self.dv), _ptr(self.dbeta), _ptr(self.dg),
+                     _ptr(self.dh0), _ptr(self.ws), ctypes.c_size_t(self.ws.numel()), ctypes.c_void_p(stream)]
+        self._keep = (q, k, v, beta, g, initial_state, d_o, d_final_state, cu_dev, cu_host)
+
+    def __call__(self):
+        _check(self.lib.gdr_chunk_bwd(*self.args))
+
+
+def chunk_bwd(q, k, v, beta, d_o, g=None, scale=None, initial_state=None, d_final_state=None,
+              cu_seqlens=None, cu_seqlens_cpu=None, chunk_size=64):
+    """Backward of chunk_fwd: returns dict dq, dk, dv, dbeta, dg, dh0 (fp32),
+    the gradients of a loss given dL/do (d_o) and dL/dS_T (d_final_state,
+    None = zeros). The forward is recomputed. With g None, dg is the
+    gradient at g = 0."""
+    bwd = Backward(q, k, v, beta, g=g, scale=scale, initial_state=initial_state, cu_seqlens=cu_seqlens,
+                   cu_seqlens_cpu=cu_seqlens_cpu, d_o=d_o, d_final_state=d_final_state, chunk_size=chunk_size)
+    bwd()
+    return dict(dq=bwd.dq, dk=bwd.dk, dv=bwd.dv, dbeta=bwd.dbeta, dg=bwd.dg, dh0=bwd.dh0)
 
 
 def num_chunks(B, T, cu_host, chunk_size=64) -> int:

@@ -166,10 +166,63 @@ SegPlan make_seg_plan(const gdr_problem_t* p, size_t base, int64_t nseg) {
     return sp;
 }
 
-gdr_status_t run(const gdr_problem_t* p, const void* q, const void* k, const void* v, const float* g,
-                 const void* beta, float scale, const float* S0, const int32_t* cu_dev, const int32_t* cu_host,
-                 void* o, float* ST, void* ws, size_t ws_bytes, void* stream, hipEvent_t* events,
-                 bool reference, Plan* plan_out, int32_t* nt_out, int32_t seg_req = -1) {
+// Chunks of every sequence (and the longest sequence's count) for this chunk size.
+void count_chunks(const gdr_problem_t* p, const int32_t* cu_host, int64_t* nt, int64_t* max_chunks) {
+    const int64_t C = p->chunk_size;
+    *nt = 0;
+    *max_chunks = 0;
+    for (int32_t n = 0; n < p->num_seqs; ++n) {
+        const int64_t len = cu_host ? (int64_t)cu_host[n + 1] - cu_host[n] : p->seq_len;
+        *nt += (len + C - 1) / C;
+        *max_chunks = (len + C - 1) / C > *max_chunks ? (len + C - 1) / C : *max_chunks;
+    }
+}
+
+// Launch arguments of the forward pipeline over the workspace regions of `pl`.
+gdr::LaunchArgs fill_args(const gdr_problem_t* p, const Plan& pl, int64_t nt, const void* q, const void* k,
+                          const void* v, const float* g, const void* beta, float scale, const float* S0,
+                          const int32_t* cu_dev, void* o, float* ST, char* w, bool reference, void* stream) {
+    gdr::LaunchArgs a;
+    a.bf16 = p->io_dtype == GDR_BF16;
+    a.dk = p->head_dim_qk;
+    a.dv = p->head_dim_v;
+    a.C = p->chunk_size;
+    a.Nk = p->num_qk_heads;
+    a.Nv = p->num_v_heads;
+    a.N = p->num_seqs;
+    a.T_row = p->seq_len;
+    a.Ttot = p->batch * p->seq_len;
+    a.nt = (int32_t)nt;
+    a.nt_cap = pl.nt_cap;
+    a.q = q; a.k = k; a.v = v; a.beta = beta;
+    a.beta_f32 = p->beta_dtype == GDR_F32;
+    a.out_f32 = p->out_dtype == GDR_F32;
+    a.g = g; a.S0 = S0; a.scale = scale;
+    a.cu_dev = cu_dev;
+    a.o = o; a.ST = ST;
+    a.chunk_seq = reinterpret_cast<int32_t*>(w + pl.off_seq);
+    a.chunk_start = reinterpret_cast<int32_t*>(w + pl.off_start);
+    a.chunk_len = reinterpret_cast<int32_t*>(w + pl.off_len);
+    a.seq_first = reinterpret_cast<int32_t*>(w + pl.off_first);
+    a.G = reinterpret_cast<float*>(w + pl.off_G);
+    a.A = w + pl.off_A; a.W = w + pl.off_W; a.U = w + pl.off_U; a.KT = w + pl.off_KT;
+    a.H = w + pl.off_H; a.VN = w + pl.off_VN;
+    a.Tf = pl.sz_Tf ? w + pl.off_Tf : nullptr;
+    a.Pf = pl.sz_Tf ? w + pl.off_Pf : nullptr;
+    a.R = pl.sz_Tf ? w + pl.off_R : nullptr;
+    a.reference = reference;
+    a.nseg = 0;
+    a.seg_chunks = 0;
+    a.seg_first = a.seq_seg = nullptr;
+    a.Sloc = a.Mseg = a.Sstart = nullptr;
+    a.stream = static_cast<hipStream_t>(stream);
+    return a;
+}
+
+// Checks shared by the chunked entry points: problem, offsets, required inputs, alignment.
+gdr_status_t check_inputs(const gdr_problem_t* p, const void* q, const void* k, const void* v, const float* g,
+                          const void* beta, const float* S0, const int32_t* cu_dev, const int32_t* cu_host,
+                          void* ws) {
     gdr_status_t st = check_problem(p);
     if (st != GDR_OK) return st;
     if ((cu_dev == nullptr) != (cu_host == nullptr))
@@ -177,23 +230,56 @@ gdr_status_t run(const gdr_problem_t* p, const void* q, const void* k, const voi
     st = check_seqlens(p, cu_host, cu_host != nullptr);
     if (st != GDR_OK) return st;
     const int64_t Ttot = p->batch * p->seq_len;
-    if (Ttot > 0 && (!q || !k || !v || !beta || !o))
-        return fail(GDR_ERR_NULL, "q, k, v, beta and o are required");
-    const void* ptrs[] = {q, k, v, beta, g, S0, o, ST};
+    if (Ttot > 0 && (!q || !k || !v || !beta))
+        return fail(GDR_ERR_NULL, "q, k, v and beta are required");
+    const void* ptrs[] = {q, k, v, beta, g, S0};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return fail(GDR_ERR_SHAPE, "tensor base address not 16-byte aligned");
-    Plan pl = make_plan(p);
     if (!ws) return fail(GDR_ERR_WORKSPACE, "workspace is NULL");
     if (((uintptr_t)ws & 255) != 0) return fail(GDR_ERR_WORKSPACE, "workspace not 256-byte aligned");
-    size_t need = reference ? pl.reference : pl.production;
+    return GDR_OK;
+}
 
+// Backward workspace: the five-kernel forward's regions, then the backward's own.
+struct BwdPlan {
+    size_t off_o, off_P, off_Hn, off_Vn, off_Wn, off_dSout, off_dVn, off_dWs, off_dqv, off_dkv, end;
+};
+
+BwdPlan make_bwd_plan(const gdr_problem_t* p, const Plan& pl) {
+    BwdPlan bp;
+    const size_t C = p->chunk_size, cap = (size_t)pl.nt_cap;
+    const size_t Nv = p->num_v_heads, dk = p->head_dim_qk, dv = p->head_dim_v;
+    const size_t T = (size_t)(pl.Ttot > 0 ? pl.Ttot : 1);
+    size_t off = align256(pl.reference);
+    auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+    bp.off_o = take(T * Nv * dv * 4);
+    bp.off_P = take(cap * Nv * C * C * 4);
+    bp.off_Hn = take(cap * Nv * dk * dv * 4);
+    bp.off_Vn = take(T * Nv * dv * 4);
+    bp.off_Wn = take(T * Nv * dk * 4);
+    bp.off_dSout = take(cap * Nv * dk * dv * 4);
+    bp.off_dVn = take(T * Nv * dv * 4);
+    bp.off_dWs = take(T * Nv * dk * 4);
+    bp.off_dqv = take(T * Nv * dk * 4);
+    bp.off_dkv = take(T * Nv * dk * 4);
+    bp.end = off;
+    return bp;
+}
+
+gdr_status_t run(const gdr_problem_t* p, const void* q, const void* k, const void* v, const float* g,
+                 const void* beta, float scale, const float* S0, const int32_t* cu_dev, const int32_t* cu_host,
+                 void* o, float* ST, void* ws, size_t ws_bytes, void* stream, hipEvent_t* events,
+                 bool reference, Plan* plan_out, int32_t* nt_out, int32_t seg_req = -1) {
+    if (p && p->batch * p->seq_len > 0 && !o) return fail(GDR_ERR_NULL, "o is required");
+    if ((o && !aligned16(o)) || (ST && !aligned16(ST)))
+        return fail(GDR_ERR_SHAPE, "tensor base address not 16-byte aligned");
+    gdr_status_t st = check_inputs(p, q, k, v, g, beta, S0, cu_dev, cu_host, ws);
+    if (st != GDR_OK) return st;
+    Plan pl = make_plan(p);
+    size_t need = reference ? pl.reference : pl.production;
     const int64_t C = p->chunk_size;
     int64_t nt = 0, max_chunks = 0;
-    for (int32_t n = 0; n < p->num_seqs; ++n) {
-        const int64_t len = cu_host ? (int64_t)cu_host[n + 1] - cu_host[n] : p->seq_len;
-        nt += (len + C - 1) / C;
-        max_chunks = (len + C - 1) / C > max_chunks ? (len + C - 1) / C : max_chunks;
-    }
+    count_chunks(p, cu_host, &nt, &max_chunks);
     if (nt > pl.nt_cap) return fail(GDR_ERR_SEQLENS, "chunk count %lld exceeds capacity", (long long)nt);
 
     // segments: seg_req < 0 none, 0 automatic, > 0 chunks per segment; only a
@@ -223,35 +309,7 @@ gdr_status_t run(const gdr_problem_t* p, const void* q, const void* k, const voi
     if (ws_bytes < need) return fail(GDR_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
 
     char* w = static_cast<char*>(ws);
-    gdr::LaunchArgs a;
-    a.bf16 = p->io_dtype == GDR_BF16;
-    a.dk = p->head_dim_qk;
-    a.dv = p->head_dim_v;
-    a.C = p->chunk_size;
-    a.Nk = p->num_qk_heads;
-    a.Nv = p->num_v_heads;
-    a.N = p->num_seqs;
-    a.T_row = p->seq_len;
-    a.Ttot = Ttot;
-    a.nt = (int32_t)nt;
-    a.nt_cap = pl.nt_cap;
-    a.q = q; a.k = k; a.v = v; a.beta = beta;
-    a.beta_f32 = p->beta_dtype == GDR_F32;
-    a.out_f32 = p->out_dtype == GDR_F32;
-    a.g = g; a.S0 = S0; a.scale = scale;
-    a.cu_dev = cu_dev;
-    a.o = o; a.ST = ST;
-    a.chunk_seq = reinterpret_cast<int32_t*>(w + pl.off_seq);
-    a.chunk_start = reinterpret_cast<int32_t*>(w + pl.off_start);
-    a.chunk_len = reinterpret_cast<int32_t*>(w + pl.off_len);
-    a.seq_first = reinterpret_cast<int32_t*>(w + pl.off_first);
-    a.G = reinterpret_cast<float*>(w + pl.off_G);
-    a.A = w + pl.off_A; a.W = w + pl.off_W; a.U = w + pl.off_U; a.KT = w + pl.off_KT;
-    a.H = w + pl.off_H; a.VN = w + pl.off_VN;
-    a.Tf = pl.sz_Tf ? w + pl.off_Tf : nullptr;
-    a.Pf = pl.sz_Tf ? w + pl.off_Pf : nullptr;
-    a.R = pl.sz_Tf ? w + pl.off_R : nullptr;
-    a.reference = reference;
+    gdr::LaunchArgs a = fill_args(p, pl, nt, q, k, v, g, beta, scale, S0, cu_dev, o, ST, w, reference, stream);
     a.nseg = (int32_t)nseg;
     a.seg_chunks = (int32_t)seg_chunks;
     a.seg_first = nseg ? reinterpret_cast<int32_t*>(w + sp.off_first) : nullptr;
@@ -259,7 +317,6 @@ gdr_status_t run(const gdr_problem_t* p, const void* q, const void* k, const voi
     a.Sloc = nseg ? reinterpret_cast<float*>(w + sp.off_Sloc) : nullptr;
     a.Mseg = nseg ? reinterpret_cast<float*>(w + sp.off_M) : nullptr;
     a.Sstart = nseg ? reinterpret_cast<float*>(w + sp.off_Sstart) : nullptr;
-    a.stream = static_cast<hipStream_t>(stream);
 
     hipError_t e = gdr::launch_forward(a, events);
     if (e != hipSuccess) return fail(GDR_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -363,6 +420,54 @@ gdr_status_t gdr_chunk_fwd_segmented(const gdr_problem_t* p, const void* q, cons
     }
     return run(p, q, k, v, g, beta, scale, initial_state, cu_dev, cu_host, o, final_state, workspace,
                workspace_bytes, stream, stage_events ? ev : nullptr, false, nullptr, nullptr, segment_chunks);
+}
+
+gdr_status_t gdr_chunk_bwd_workspace_size(const gdr_problem_t* problem, size_t* bytes) {
+    if (!bytes) return fail(GDR_ERR_NULL, "bytes is NULL");
+    gdr_status_t st = check_problem(problem);
+    if (st != GDR_OK) return st;
+    *bytes = make_bwd_plan(problem, make_plan(problem)).end;
+    return GDR_OK;
+}
+
+gdr_status_t gdr_chunk_bwd(const gdr_problem_t* p, const void* q, const void* k, const void* v, const float* g,
+                           const void* beta, float scale, const float* initial_state, const int32_t* cu_dev,
+                           const int32_t* cu_host, const void* d_o, const float* d_final_state, float* dq,
+                           float* dk, float* dv, float* dbeta, float* dg, float* d_initial_state, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    gdr_status_t st = check_inputs(p, q, k, v, g, beta, initial_state, cu_dev, cu_host, workspace);
+    if (st != GDR_OK) return st;
+    const int64_t Ttot = p->batch * p->seq_len;
+    if (Ttot > 0 && (!d_o || !dq || !dk || !dv || !dbeta))
+        return fail(GDR_ERR_NULL, "d_o, dq, dk, dv and dbeta are required");
+    const void* ptrs[] = {d_o, d_final_state, dq, dk, dv, dbeta, dg, d_initial_state};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return fail(GDR_ERR_SHAPE, "tensor base address not 16-byte aligned");
+    const Plan pl = make_plan(p);
+    const BwdPlan bp = make_bwd_plan(p, pl);
+    if (workspace_bytes < bp.end)
+        return fail(GDR_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, bp.end);
+    int64_t nt = 0, max_chunks = 0;
+    count_chunks(p, cu_host, &nt, &max_chunks);
+    if (nt > pl.nt_cap) return fail(GDR_ERR_SEQLENS, "chunk count %lld exceeds capacity", (long long)nt);
+
+    char* w = static_cast<char*>(workspace);
+    gdr::BackwardArgs b;
+    b.fwd = fill_args(p, pl, nt, q, k, v, g, beta, scale, initial_state, cu_dev, w + bp.off_o, nullptr, w,
+                      true, stream);
+    b.fwd.out_f32 = 1;                              // the recomputed output goes to an fp32 scratch
+    b.d_o = d_o;
+    b.do_f32 = p->out_dtype == GDR_F32;
+    b.dST = d_final_state;
+    b.dq = dq; b.dk = dk; b.dv = dv; b.dbeta = dbeta; b.dg = dg; b.dS0 = d_initial_state;
+    auto f = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
+    b.P = f(bp.off_P); b.Hn = f(bp.off_Hn); b.Vn = f(bp.off_Vn); b.Wn = f(bp.off_Wn);
+    b.dSout = f(bp.off_dSout); b.dVn = f(bp.off_dVn); b.dWs = f(bp.off_dWs);
+    b.dqv = f(bp.off_dqv); b.dkv = f(bp.off_dkv);
+    hipError_t e = gdr::launch_backward(b);
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    g_err[0] = '\0';
+    return GDR_OK;
 }
 
 gdr_status_t gdr_chunk_fwd_timed(const gdr_problem_t* p, const void* q, const void* k, const void* v,

@@ -1,0 +1,471 @@
+// Backward pass of the chunked gated delta rule for gfx950.
+//
+// Given dO (the loss gradient with respect to o) and dS_T (with respect to the
+// final state), computes dq, dk, dv, dbeta, dg and the initial state's
+// gradient. The structure follows the chunked backward of the pages (GLA
+// notes, backward steps 1-7: recompute the gate sums and the chunk states,
+// run the state gradient backwards over the chunks, then form the per-chunk
+// gradients of V, of the intra-chunk score block and of Q, K and the gate),
+// extended through the delta rule's WY products (ChunkGatedDeltaRule page,
+// formulas (1)-(6); FLA DeltaNet article, sections 2.3-2.4).
+//
+// Per chunk (positions i < L, chunk-local gate sums G, G_last = G_{L-1},
+// D_ij = exp(G_i - G_j) for j <= i, P = (Q K^T) (.) D, h = the entering state,
+// V_new = U - W h, dS = the gradient with respect to the state leaving the
+// chunk):
+//   reverse state pass:
+//     dV_new = scale P^T dO + diag(exp(G_last - G)) K dS
+//     dS_in  = exp(G_last) dS + scale Q^T diag(exp(G)) dO - W^T dV_new
+//   per chunk:
+//     dQ  = scale diag(exp(G)) dO h^T + dM K,   dP = scale dO V_new^T (j <= i), dM = dP (.) D
+//     dW  = -dV_new h^T,  dU = dV_new
+//     dV  = diag(beta) A^T dU
+//     dA  = dU (diag(beta) V)^T + dW (diag(beta exp(G)) K)^T,  dL = -A^T dA A^T (strictly lower part F)
+//     dK  = dM^T Q + diag(exp(G_last - G)) V_new dS^T + diag(beta exp(G)) A^T dW
+//           + diag(beta) (F (.) D) K + (F (.) D)^T diag(beta) K
+//     dbeta_i = v_i . (A^T dU)_i + exp(G_i) k_i . (A^T dW)_i + sum_j F_ij (k_i . k_j) D_ij
+//     dG_i from exp(G) in the inter-chunk output, D in P and L, exp(G_last - G)
+//     and exp(G_last) in the state update and exp(G) in W; dg = the reverse
+//     prefix sum of dG inside the chunk.
+// dq and dk are formed per value head and summed over the heads that share a
+// q/k head. All arithmetic is fp32 on the vector units; the forward values are
+// recomputed by the five-kernel forward path.
+#include "gdr_device.hpp"
+#include "gdr_launch.hpp"
+
+namespace gdr {
+
+namespace {
+
+// offset of element (row r < 16, contraction index m < 32) inside a pair fragment
+__device__ __forceinline__ int pair_off(int r, int m) {
+    const int mm = m & 15;
+    return (16 * (mm >> 2) + r) * 8 + (mm & 3) + (m >= 16 ? 4 : 0);
+}
+
+// out(i, j) = sum over kk < K of a(i, kk) b(kk, j) for i < M, j < N; each
+// thread takes 4 x 4 blocks of the output and keeps them in registers.
+template <int M, int N, typename FA, typename FB, typename FS>
+__device__ __forceinline__ void gemm44(int K, FA&& a, FB&& b, FS&& store) {
+    static_assert(M % 4 == 0 && N % 4 == 0, "4 x 4 blocks");
+    constexpr int BN = N / 4, NB = (M / 4) * BN;
+    for (int blk = threadIdx.x; blk < NB; blk += blockDim.x) {
+        const int i0 = (blk / BN) * 4, j0 = (blk % BN) * 4;
+        float acc[4][4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+        for (int kk = 0; kk < K; ++kk) {
+            float av[4], bv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) av[r] = a(i0 + r, kk);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) bv[c] = b(kk, j0 + c);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[r][c] += av[r] * bv[c];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) store(i0 + r, j0 + c, acc[r][c]);
+    }
+}
+
+__device__ __forceinline__ float load_any(const void* p, int64_t idx, int is_f32) {
+    return is_f32 ? reinterpret_cast<const float*>(p)[idx] : (float)reinterpret_cast<const bf16*>(p)[idx];
+}
+
+// ------------------------------------------------------------ preparation
+// One workgroup per (chunk, value head): the forward intermediates in natural
+// row-major layouts (the chunk's entering state h [dk][dv], V_new and W by
+// token row), and the score block P = (Q K^T) (.) D [C][C], zero above the
+// diagonal and past the chunk end.
+template <typename T, int DK, int DV, int C>
+__global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ q, const T* __restrict__ k,
+                                                   const float* __restrict__ G, const float* __restrict__ Hf,
+                                                   const float* __restrict__ VNf, const float* __restrict__ Wf,
+                                                   const int32_t* __restrict__ chunk_start,
+                                                   const int32_t* __restrict__ chunk_len, int32_t Nk, int32_t Nv,
+                                                   float* __restrict__ Hn, float* __restrict__ Vn,
+                                                   float* __restrict__ Wn, float* __restrict__ P) {
+    constexpr int NKP = DK / 32, NNB = DV / 16, NTB = C / 16, NTP = C < 32 ? 1 : C / 32;
+    const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    const int kh = h / (Nv / Nk);
+    const int64_t s = chunk_start[c];
+    const int L = chunk_len[c];
+    if (L <= 0) return;
+    __shared__ float gs[C];
+    if (tid < C) gs[tid] = tid < L ? G[(s + tid) * Nv + h] : 0.f;
+    const int64_t ch = (int64_t)c * Nv + h;
+    for (int idx = tid; idx < DK * DV; idx += 256) {
+        const int i = idx / DV, j = idx % DV;
+        Hn[ch * DK * DV + idx] = Hf[((ch * NNB + j / 16) * NKP + i / 32) * 512 + pair_off(j % 16, i % 32)];
+    }
+    for (int idx = tid; idx < L * DV; idx += 256) {
+        const int p = idx / DV, j = idx % DV;
+        Vn[((s + p) * Nv + h) * DV + j] = VNf[((ch * NNB + j / 16) * NTP + p / 32) * 512 + pair_off(j % 16, p % 32)];
+    }
+    for (int idx = tid; idx < L * DK; idx += 256) {
+        const int p = idx / DK, i = idx % DK;
+        Wn[((s + p) * Nv + h) * DK + i] = Wf[((ch * NTB + p / 16) * NKP + i / 32) * 512 + pair_off(p % 16, i % 32)];
+    }
+    __syncthreads();
+    float* Pc = P + ch * C * C;
+    gemm44<C, C>(DK,
+        [&](int i, int kk) { return i < L ? to_f(q[((s + i) * Nk + kh) * DK + kk]) : 0.f; },
+        [&](int kk, int j) { return j < L ? to_f(k[((s + j) * Nk + kh) * DK + kk]) : 0.f; },
+        [&](int i, int j, float x) { Pc[i * C + j] = (i < L && j <= i) ? x * __expf(gs[i] - gs[j]) : 0.f; });
+}
+
+// ------------------------------------------------------------ reverse state pass
+// One workgroup per (sequence, value head, 16 columns of dv) walks the chunks
+// backwards with the 16-column slice of the state gradient dS in LDS (fp32):
+// it stores dS (the gradient with respect to the chunk's outgoing state) and
+// dV_new for the chunk, then moves dS to the chunk's entering state. After the
+// first chunk, dS is the gradient with respect to the initial state.
+template <typename T, int DK, int DV, int C>
+__global__ __launch_bounds__(256) void k_bwd_state(const T* __restrict__ q, const T* __restrict__ k,
+                                                    const float* __restrict__ G, const float* __restrict__ P,
+                                                    const float* __restrict__ Wn, const void* __restrict__ d_o,
+                                                    int do_f32, const float* __restrict__ dST,
+                                                    const int32_t* __restrict__ chunk_start,
+                                                    const int32_t* __restrict__ chunk_len,
+                                                    const int32_t* __restrict__ seq_first, int32_t Nk, int32_t Nv,
+                                                    float scale, float* __restrict__ dSout,
+                                                    float* __restrict__ dVn, float* __restrict__ dS0) {
+    constexpr int CP = C + 1, KP = DK + 1;
+    constexpr int PER = DK * 16 / 256;          // dS elements per thread
+    __shared__ float dS[DK][16];
+    __shared__ float Ps[C][CP];
+    __shared__ float Ks[C][KP], Qe[C][KP], Ws[C][KP];
+    __shared__ float dOt[C][16], dVt[C][16];
+    __shared__ float gs[C];
+    const int n = blockIdx.x, h = blockIdx.y, nb = blockIdx.z, tid = threadIdx.x;
+    const int kh = h / (Nv / Nk);
+    for (int idx = tid; idx < DK * 16; idx += 256) {
+        const int m = idx / 16, j = idx % 16;
+        dS[m][j] = dST ? dST[(((int64_t)n * Nv + h) * DK + m) * DV + nb * 16 + j] : 0.f;
+    }
+    const int c0 = seq_first[n], c1 = seq_first[n + 1];
+    for (int c = c1 - 1; c >= c0; --c) {
+        const int64_t s = chunk_start[c];
+        const int L = chunk_len[c];
+        __syncthreads();                              // the previous chunk's readers are done
+        if (tid < C) gs[tid] = tid < L ? G[(s + tid) * Nv + h] : 0.f;
+        const float* Pc = P + ((int64_t)c * Nv + h) * C * C;
+        for (int idx = tid; idx < C * C; idx += 256) Ps[idx / C][idx % C] = Pc[idx];
+        for (int idx = tid; idx < C * DK; idx += 256) {
+            const int i = idx / DK, m = idx % DK;
+            const bool ok = i < L;
+            const int64_t row = (s + i) * Nk + kh;
+            Ks[i][m] = ok ? to_f(k[row * DK + m]) : 0.f;
+            Qe[i][m] = ok ? scale * __expf(G[(s + i) * Nv + h]) * to_f(q[row * DK + m]) : 0.f;
+            Ws[i][m] = ok ? Wn[((s + i) * Nv + h) * DK + m] : 0.f;
+        }
+        for (int idx = tid; idx < C * 16; idx += 256) {
+            const int i = idx / 16, j = idx % 16;
+            dOt[i][j] = i < L ? load_any(d_o, ((s + i) * Nv + h) * DV + nb * 16 + j, do_f32) : 0.f;
+        }
+        __syncthreads();
+        const float gL = gs[L - 1];
+        for (int idx = tid; idx < DK * 16; idx += 256) {
+            const int m = idx / 16, j = idx % 16;
+            dSout[(((int64_t)c * Nv + h) * DK + m) * DV + nb * 16 + j] = dS[m][j];
+        }
+        // dV_new = scale P^T dO + diag(exp(G_last - G)) K dS
+        for (int idx = tid; idx < C * 16; idx += 256) {
+            const int i = idx / 16, j = idx % 16;
+            float a1 = 0.f, a2 = 0.f;
+            for (int t = i; t < C; ++t) a1 += Ps[t][i] * dOt[t][j];
+#pragma unroll 8
+            for (int m = 0; m < DK; ++m) a2 += Ks[i][m] * dS[m][j];
+            const float val = i < L ? scale * a1 + __expf(gL - gs[i]) * a2 : 0.f;
+            dVt[i][j] = val;
+            if (i < L) dVn[((s + i) * Nv + h) * DV + nb * 16 + j] = val;
+        }
+        __syncthreads();
+        // dS_in = exp(G_last) dS + scale Q^T diag(exp(G)) dO - W^T dV_new
+        const float eL = __expf(gL);
+        float nw[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int idx = tid + 256 * e, m = idx / 16, j = idx % 16;
+            float acc = 0.f;
+            for (int i = 0; i < L; ++i) acc += Qe[i][m] * dOt[i][j] - Ws[i][m] * dVt[i][j];
+            nw[e] = eL * dS[m][j] + acc;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int idx = tid + 256 * e;
+            dS[idx / 16][idx % 16] = nw[e];
+        }
+    }
+    __syncthreads();
+    if (dS0) {
+        for (int idx = tid; idx < DK * 16; idx += 256) {
+            const int m = idx / 16, j = idx % 16;
+            dS0[(((int64_t)n * Nv + h) * DK + m) * DV + nb * 16 + j] = dS[m][j];
+        }
+    }
+}
+
+// ------------------------------------------------------------ per-chunk gradients
+// One workgroup per (chunk, value head). The C x C matrices (A, D, P, dP, dA /
+// F, A^T dA, K K^T) sit in LDS; the C x dk and C x dv operands are read from
+// memory. Writes dq and dk of this value head (summed over the group later),
+// dv, dbeta and dg, and uses a per-token scratch for dW.
+template <typename T, int DK, int DV, int C>
+__global__ __launch_bounds__(256) void k_bwd_chunk(const T* __restrict__ q, const T* __restrict__ k,
+                                                    const T* __restrict__ v, const void* __restrict__ beta,
+                                                    int beta_f32, const float* __restrict__ G,
+                                                    const float* __restrict__ A, const float* __restrict__ P,
+                                                    const float* __restrict__ Hn, const float* __restrict__ Vn,
+                                                    const float* __restrict__ dSout, const float* __restrict__ dVn,
+                                                    const void* __restrict__ d_o, int do_f32,
+                                                    const int32_t* __restrict__ chunk_start,
+                                                    const int32_t* __restrict__ chunk_len, int32_t Nk, int32_t Nv,
+                                                    float scale, float* __restrict__ dW, float* __restrict__ dqv,
+                                                    float* __restrict__ dkv, float* __restrict__ dv,
+                                                    float* __restrict__ dbeta, float* __restrict__ dg) {
+    constexpr int CP = C + 1;
+    __shared__ float Am[C][CP], Dm[C][CP], Pm[C][CP], dPm[C][CP], dAm[C][CP], Tm[C][CP], KKm[C][CP];
+    __shared__ float gs[C], eg[C], elg[C], bs[C], dGs[C], dBs[C], cv[C];
+    __shared__ float sum_sh;
+    const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    const int kh = h / (Nv / Nk);
+    const int64_t s = chunk_start[c];
+    const int L = chunk_len[c];
+    if (L <= 0) return;
+    const int64_t ch = (int64_t)c * Nv + h;
+    const float* Hc = Hn + ch * DK * DV;          // entering state [dk][dv]
+    const float* dSc = dSout + ch * DK * DV;      // gradient of the outgoing state [dk][dv]
+
+    auto Qg = [&](int i, int m) { return i < L ? to_f(q[((s + i) * Nk + kh) * DK + m]) : 0.f; };
+    auto Kg = [&](int i, int m) { return i < L ? to_f(k[((s + i) * Nk + kh) * DK + m]) : 0.f; };
+    auto Vg = [&](int i, int j) { return i < L ? to_f(v[((s + i) * Nv + h) * DV + j]) : 0.f; };
+    auto dOg = [&](int i, int j) { return i < L ? load_any(d_o, ((s + i) * Nv + h) * DV + j, do_f32) : 0.f; };
+    auto Vng = [&](int i, int j) { return i < L ? Vn[((s + i) * Nv + h) * DV + j] : 0.f; };
+    auto dVg = [&](int i, int j) { return i < L ? dVn[((s + i) * Nv + h) * DV + j] : 0.f; };
+    auto dWg = [&](int i, int m) { return i < L ? dW[((s + i) * Nv + h) * DK + m] : 0.f; };
+    auto row_dk = [&](int i) { return ((s + i) * Nv + h) * DK; };
+
+    if (tid < C) {
+        const bool ok = tid < L;
+        gs[tid] = ok ? G[(s + tid) * Nv + h] : 0.f;
+        bs[tid] = ok ? load_beta(beta, (s + tid) * Nv + h, beta_f32) : 0.f;
+        dGs[tid] = 0.f;
+        dBs[tid] = 0.f;
+        cv[tid] = 0.f;
+    }
+    if (tid == 0) sum_sh = 0.f;
+    for (int idx = tid; idx < C * C; idx += 256) {
+        const int i = idx / C, j = idx % C;
+        Am[i][j] = (i < L && j <= i) ? A[((s + i) * Nv + h) * C + j] : 0.f;
+        Pm[i][j] = P[ch * C * C + idx];
+    }
+    __syncthreads();
+    const float gL = gs[L - 1];
+    if (tid < C) {
+        eg[tid] = tid < L ? __expf(gs[tid]) : 0.f;
+        elg[tid] = tid < L ? __expf(gL - gs[tid]) : 0.f;
+    }
+    for (int idx = tid; idx < C * C; idx += 256) {
+        const int i = idx / C, j = idx % C;
+        Dm[i][j] = (i < L && j <= i) ? __expf(gs[i] - gs[j]) : 0.f;
+    }
+    __syncthreads();
+
+    // dP = scale dO V_new^T on and below the diagonal
+    gemm44<C, C>(DV, dOg, [&](int kk, int j) { return Vng(j, kk); },
+                 [&](int i, int j, float x) { dPm[i][j] = (i < L && j <= i) ? scale * x : 0.f; });
+    __syncthreads();
+    // gate gradient through D in P: E = dP (.) P, dG += row sums - column sums
+    if (tid < C) {
+        float acc = 0.f;
+        for (int j = 0; j < C; ++j) acc += dPm[tid][j] * Pm[tid][j] - dPm[j][tid] * Pm[j][tid];
+        dGs[tid] += acc;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < C * C; idx += 256) dPm[idx / C][idx % C] *= Dm[idx / C][idx % C];   // dM = dP (.) D
+    __syncthreads();
+
+    // dQ = scale diag(exp(G)) dO h^T + dM K
+    gemm44<C, DK>(DV + C,
+        [&](int i, int kk) { return kk < DV ? scale * eg[i] * dOg(i, kk) : dPm[i][kk - DV]; },
+        [&](int kk, int m) { return kk < DV ? Hc[m * DV + kk] : Kg(kk - DV, m); },
+        [&](int i, int m, float x) { if (i < L) dqv[row_dk(i) + m] = x; });
+    // dW = -dV_new h^T
+    gemm44<C, DK>(DV, dVg, [&](int kk, int m) { return Hc[m * DV + kk]; },
+                  [&](int i, int m, float x) { if (i < L) dW[row_dk(i) + m] = -x; });
+    __syncthreads();
+
+    // dV = diag(beta) A^T dU (dU = dV_new); dbeta += v . (A^T dU)
+    gemm44<C, DV>(C, [&](int i, int kk) { return Am[kk][i]; }, dVg,
+        [&](int i, int j, float x) {
+            if (i < L) {
+                dv[((s + i) * Nv + h) * DV + j] = bs[i] * x;
+                atomicAdd(&dBs[i], Vg(i, j) * x);
+            }
+        });
+    // A^T dW: dK = diag(beta exp(G)) A^T dW; dbeta, dG through exp(G) in W
+    gemm44<C, DK>(C, [&](int i, int kk) { return Am[kk][i]; }, dWg,
+        [&](int i, int m, float x) {
+            if (i < L) {
+                dkv[row_dk(i) + m] = bs[i] * eg[i] * x;
+                const float part = Kg(i, m) * x * eg[i];
+                atomicAdd(&dBs[i], part);
+                atomicAdd(&dGs[i], bs[i] * part);
+            }
+        });
+    // dA = dU (diag(beta) V)^T + dW (diag(beta exp(G)) K)^T
+    gemm44<C, C>(DV + DK,
+        [&](int i, int kk) { return kk < DV ? dVg(i, kk) : dWg(i, kk - DV); },
+        [&](int kk, int j) { return kk < DV ? bs[j] * Vg(j, kk) : bs[j] * eg[j] * Kg(j, kk - DV); },
+        [&](int i, int j, float x) { dAm[i][j] = x; });
+    // K K^T
+    gemm44<C, C>(DK, Kg, [&](int kk, int j) { return Kg(j, kk); }, [&](int i, int j, float x) { KKm[i][j] = x; });
+    __syncthreads();
+    // A^T dA
+    gemm44<C, C>(C, [&](int i, int kk) { return Am[kk][i]; }, [&](int kk, int j) { return dAm[kk][j]; },
+                 [&](int i, int j, float x) { Tm[i][j] = x; });
+    __syncthreads();
+    // F = strictly lower part of dL = -(A^T dA) A^T
+    gemm44<C, C>(C, [&](int i, int kk) { return Tm[i][kk]; }, [&](int kk, int j) { return Am[j][kk]; },
+                 [&](int i, int j, float x) { dAm[i][j] = (i < L && j < i) ? -x : 0.f; });
+    __syncthreads();
+    // dbeta and dG through L_ij = beta_i (k_i . k_j) D_ij
+    if (tid < C) {
+        float db = 0.f, dgr = 0.f;
+        for (int j = 0; j < C; ++j) {
+            db += dAm[tid][j] * KKm[tid][j] * Dm[tid][j];
+            dgr += dAm[tid][j] * bs[tid] * KKm[tid][j] * Dm[tid][j] - dAm[j][tid] * bs[j] * KKm[j][tid] * Dm[j][tid];
+        }
+        dBs[tid] += db;
+        dGs[tid] += dgr;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < C * C; idx += 256) dAm[idx / C][idx % C] *= Dm[idx / C][idx % C];   // F (.) D
+    __syncthreads();
+    // dK += diag(beta) (F (.) D) K + (F (.) D)^T diag(beta) K + dM^T Q
+    gemm44<C, DK>(3 * C,
+        [&](int i, int kk) {
+            return kk < C ? bs[i] * dAm[i][kk] : (kk < 2 * C ? dAm[kk - C][i] : dPm[kk - 2 * C][i]);
+        },
+        [&](int kk, int m) {
+            return kk < C ? Kg(kk, m) : (kk < 2 * C ? bs[kk - C] * Kg(kk - C, m) : Qg(kk - 2 * C, m));
+        },
+        [&](int i, int m, float x) { if (i < L) dkv[row_dk(i) + m] += x; });
+    // dK += diag(exp(G_last - G)) V_new dS^T; the same term's gate gradient
+    gemm44<C, DK>(DV, Vng, [&](int kk, int m) { return dSc[m * DV + kk]; },
+        [&](int i, int m, float x) {
+            if (i < L) {
+                const float y = elg[i] * x;
+                dkv[row_dk(i) + m] += y;
+                atomicAdd(&cv[i], Kg(i, m) * y);
+            }
+        });
+    // dG through exp(G) in the inter-chunk output: dG_i += dO_i . (scale exp(G_i) h^T q_i)
+    gemm44<C, DV>(DK, Qg, [&](int kk, int j) { return Hc[kk * DV + j]; },
+        [&](int i, int j, float x) { if (i < L) atomicAdd(&dGs[i], scale * eg[i] * dOg(i, j) * x); });
+    // exp(G_last) h in the state update: sum(dS (.) h)
+    {
+        float part = 0.f;
+        for (int idx = tid; idx < DK * DV; idx += 256) part += dSc[idx] * Hc[idx];
+        atomicAdd(&sum_sh, part);
+    }
+    __syncthreads();
+    if (tid < C) dGs[tid] -= cv[tid];
+    __syncthreads();
+    if (tid == 0) {
+        float tot = 0.f;
+        for (int i = 0; i < L; ++i) tot += cv[i];
+        dGs[L - 1] += tot + __expf(gL) * sum_sh;
+        float acc = 0.f;                             // dg = reverse prefix sum of dG in the chunk
+        for (int i = L - 1; i >= 0; --i) {
+            acc += dGs[i];
+            if (dg) dg[(s + i) * Nv + h] = acc;
+        }
+    }
+    if (tid < L) dbeta[(s + tid) * Nv + h] = dBs[tid];
+}
+
+// dq and dk of each q/k head: the sum over the value heads that share it.
+template <int DK>
+__global__ __launch_bounds__(256) void k_bwd_reduce_qk(const float* __restrict__ dqv, const float* __restrict__ dkv,
+                                                        int64_t Ttot, int32_t Nk, int32_t Nv,
+                                                        float* __restrict__ dq, float* __restrict__ dk) {
+    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (p >= Ttot * Nk * DK) return;
+    const int64_t t = p / ((int64_t)Nk * DK);
+    const int kh = (int)((p / DK) % Nk), m = (int)(p % DK);
+    const int group = Nv / Nk;
+    float aq = 0.f, ak = 0.f;
+    for (int hh = 0; hh < group; ++hh) {
+        const int64_t src = (t * Nv + kh * group + hh) * DK + m;
+        aq += dqv[src];
+        ak += dkv[src];
+    }
+    dq[p] = aq;
+    dk[p] = ak;
+}
+
+template <typename T, int DK, int DV, int C>
+hipError_t launch_bwd(const BackwardArgs& b) {
+    const LaunchArgs& a = b.fwd;
+    hipStream_t st = a.stream;
+    hipError_t e = launch_forward(a, nullptr);   // recompute: G, A, W, U, K^T, h, V_new
+    if (e != hipSuccess) return e;
+    const int32_t NT = a.nt;
+    if (NT > 0) {
+        k_bwd_prep<T, DK, DV, C><<<dim3(NT, a.Nv), 256, 0, st>>>(
+            (const T*)a.q, (const T*)a.k, a.G, (const float*)a.H, (const float*)a.VN, (const float*)a.W,
+            a.chunk_start, a.chunk_len, a.Nk, a.Nv, b.Hn, b.Vn, b.Wn, b.P);
+    }
+    if (a.N > 0) {
+        k_bwd_state<T, DK, DV, C><<<dim3(a.N, a.Nv, DV / 16), 256, 0, st>>>(
+            (const T*)a.q, (const T*)a.k, a.G, b.P, b.Wn, b.d_o, b.do_f32, b.dST, a.chunk_start, a.chunk_len,
+            a.seq_first, a.Nk, a.Nv, a.scale, b.dSout, b.dVn, b.dS0);
+    }
+    if (NT > 0) {
+        k_bwd_chunk<T, DK, DV, C><<<dim3(NT, a.Nv), 256, 0, st>>>(
+            (const T*)a.q, (const T*)a.k, (const T*)a.v, a.beta, a.beta_f32, a.G, (const float*)a.A, b.P, b.Hn,
+            b.Vn, b.dSout, b.dVn, b.d_o, b.do_f32, a.chunk_start, a.chunk_len, a.Nk, a.Nv, a.scale, b.dWs,
+            b.dqv, b.dkv, b.dv, b.dbeta, b.dg);
+    }
+    const int64_t nq = a.Ttot * a.Nk * DK;
+    if (nq > 0)
+        k_bwd_reduce_qk<DK><<<(unsigned)((nq + 255) / 256), 256, 0, st>>>(b.dqv, b.dkv, a.Ttot, a.Nk, a.Nv, b.dq,
+                                                                          b.dk);
+    return hipGetLastError();
+}
+
+template <typename T, int C>
+hipError_t bwd_dims(const BackwardArgs& b) {
+#define GDR_BCASE(DKv, DVv) \
+    if (b.fwd.dk == DKv && b.fwd.dv == DVv) return launch_bwd<T, DKv, DVv, C>(b);
+    GDR_BCASE(32, 32) GDR_BCASE(32, 64) GDR_BCASE(32, 128)
+    GDR_BCASE(64, 32) GDR_BCASE(64, 64) GDR_BCASE(64, 128)
+    GDR_BCASE(128, 32) GDR_BCASE(128, 64) GDR_BCASE(128, 128)
+#undef GDR_BCASE
+    return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t bwd_chunk(const BackwardArgs& b) {
+    if (b.fwd.C == 64) return bwd_dims<T, 64>(b);
+    if (b.fwd.C == 32) return bwd_dims<T, 32>(b);
+    if (b.fwd.C == 16) return bwd_dims<T, 16>(b);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BackwardArgs& b) {
+    return b.fwd.bf16 ? bwd_chunk<bf16>(b) : bwd_chunk<float>(b);
+}
+
+}  // namespace gdr

@@ -44,6 +44,28 @@ struct LaunchArgs {
 // before the first and after every one of the six stages.
 hipError_t launch_forward(const LaunchArgs& a, hipEvent_t* events);
 
+// Backward pass (gdr_backward.hip): recomputes the forward on the five-kernel
+// path (fwd.reference must be set; fwd.o is a scratch output), then the
+// reverse state pass and the per-chunk gradients.
+struct BackwardArgs {
+    LaunchArgs fwd;
+    const void* d_o;           // [Ttot][Nv][dv], fp32 (do_f32) or bf16
+    int do_f32;
+    const float* dST;          // [N][Nv][dk][dv] or NULL (zeros)
+    float *dq, *dk;            // [Ttot][Nk][dk]
+    float *dv;                 // [Ttot][Nv][dv]
+    float *dbeta, *dg;         // [Ttot][Nv]; dg may be NULL
+    float* dS0;                // [N][Nv][dk][dv] or NULL
+    // workspace (fp32, natural row-major layouts)
+    float *P;                  // [NT][Nv][C][C] score block (Q K^T) (.) D
+    float *Hn;                 // [NT][Nv][dk][dv] entering states
+    float *Vn, *dVn;           // [Ttot][Nv][dv] V_new and its gradient
+    float *Wn, *dWs;           // [Ttot][Nv][dk] W and its gradient
+    float *dSout;              // [NT][Nv][dk][dv] gradients of the outgoing states
+    float *dqv, *dkv;          // [Ttot][Nv][dk] dq, dk per value head
+};
+hipError_t launch_backward(const BackwardArgs& b);
+
 // Token-by-token forward (gdr_recurrent.hip): no workspace.
 struct RecurrentArgs {
     bool bf16;

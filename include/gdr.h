@@ -206,6 +206,41 @@ gdr_status_t gdr_chunk_fwd_segmented(const gdr_problem_t* problem,
                                      void* const* stage_events);
 
 /*
+ * Backward pass: the gradients of a loss L with respect to every input of
+ * gdr_chunk_fwd, given dL/do and dL/dS_T. The chunked backward of the pages
+ * (GLA notes, backward steps 1-7: recompute the gate sums and chunk states,
+ * run the state gradient backwards over the chunks, then the per-chunk
+ * gradients of V, the score block, Q, K and the gate), carried through the
+ * delta rule's WY products (ChunkGatedDeltaRule page, formulas (1)-(6); FLA
+ * DeltaNet article, sections 2.3-2.4). The pages' tests compare dq, dk, dv,
+ * dbeta and dh0 against the token recurrence (FLA DeltaNet article, section
+ * 6); dg completes the gated form.
+ *   Forward arguments (problem, q, k, v, g, beta, scale, initial_state,
+ *   cu_seqlens) exactly as given to gdr_chunk_fwd; the forward is recomputed.
+ *   d_o            [Ttot][Nv][dv] in problem->out_dtype: dL/do. Required.
+ *   d_final_state  [N][Nv][dk][dv] fp32, dL/dS_T; NULL means zeros.
+ *   dq, dk         [Ttot][Nk][dk] fp32 out (summed over the value heads that
+ *                  share a q/k head). Required.
+ *   dv             [Ttot][Nv][dv] fp32 out. Required.
+ *   dbeta          [Ttot][Nv] fp32 out. Required.
+ *   dg             [Ttot][Nv] fp32 out, or NULL to skip. With g == NULL it
+ *                  receives the gradient at g = 0.
+ *   d_initial_state [N][Nv][dk][dv] fp32 out, or NULL to skip.
+ *   workspace      at least gdr_chunk_bwd_workspace_size bytes, 256-byte aligned.
+ * All arithmetic is fp32. Errors as for gdr_chunk_fwd. Asynchronous on `stream`.
+ */
+gdr_status_t gdr_chunk_bwd_workspace_size(const gdr_problem_t* problem, size_t* bytes);
+gdr_status_t gdr_chunk_bwd(const gdr_problem_t* problem,
+                           const void* q, const void* k, const void* v,
+                           const float* g, const void* beta, float scale,
+                           const float* initial_state,
+                           const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                           const void* d_o, const float* d_final_state,
+                           float* dq, float* dk, float* dv, float* dbeta, float* dg,
+                           float* d_initial_state,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Intermediates of the five kernels, for per-kernel parity checks. Each
  * pointer is a caller-owned device buffer (NULL to skip) that receives a copy
  * of the workspace region in the layout the kernels use; sizes follow from
