@@ -345,6 +345,112 @@ def bench_chunk_sizes(args) -> None:
                       "paths": rows}), flush=True)
 
 
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+
+
+def backward_flops(w: synth.Workload, C: int, NT: int) -> dict:
+    """Algorithmic flops (2 per multiply-add) of the backward kernels for NT
+    chunks of C positions and Nv value heads: the matrix products each kernel
+    forms, at full chunk length (the per-chunk pass: 16 products, listed in
+    its source; the state pass: P^T dO over the lower triangle, K dS, Q^T dO
+    and W^T dV_new per dv column; the preparation: Q K^T)."""
+    dk, dv = w.dk, w.dv
+    macs_chunk = (C * C * dv + C * dk * (dv + C) + C * dk * dv + C * dv * C + C * dk * C + C * C * (dv + dk)
+                  + C * C * dk + 2 * C ** 3 + 3 * C * C * dk + C * dk * dv + C * dv * dk)
+    macs_state = dv * (C * (C // 2 + dk) + 2 * dk * C)
+    macs_prep = C * C * dk
+    u = NT * w.Nv
+    return {"k_bwd_chunk": 2 * macs_chunk * u, "k_bwd_state": 2 * macs_state * u, "k_bwd_prep": 2 * macs_prep * u}
+
+
+def bench_backward(args) -> None:
+    """The backward pass on --workload: dL/do and dL/dS_T are random, every
+    gradient is written (dq, dk, dv, dbeta, dg, dh0), and the forward is
+    recomputed inside the call (as a training step's backward would). Reports
+    tokens/s of the whole backward, per-stage HIP-event times, the dominant
+    kernel against the fp32 vector peak, and the oracle's backward on a bounded
+    sample of one value head."""
+    w = synth.WORKLOADS[args.workload]
+    inp = synth.generate(w, seed=args.workload)
+    dev = torch.device("cuda:0")
+    d = {k: (None if inp[k] is None else inp[k].to(dev)) for k in ("q", "k", "v", "beta", "g", "S0", "cu_seqlens")}
+    B, T = inp["q"].shape[:2]
+    Ttot, N = B * T, inp["N"]
+    rng = np.random.default_rng(11)
+    do = torch.from_numpy(rng.standard_normal((B, T, w.Nv, w.dv)).astype(np.float32)).to(inp["q"].dtype).to(dev)
+    dST = torch.from_numpy(rng.standard_normal((N, w.Nv, w.dk, w.dv)).astype(np.float32)).to(dev)
+    bwd = api.Backward(d["q"], d["k"], d["v"], d["beta"], g=d["g"], scale=inp["scale"], initial_state=d["S0"],
+                       cu_seqlens=d["cu_seqlens"], cu_seqlens_cpu=inp["cu_seqlens"], d_o=do, d_final_state=dST)
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        bwd()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(api.BWD_NUM_STAGES + 1)] for _ in range(K)]
+    for row in events:
+        for e in row:
+            e.record()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(K):
+        bwd.timed(events[s])
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / K
+    st = np.array([[events[s][i].elapsed_time(events[s][i + 1]) for i in range(api.BWD_NUM_STAGES)]
+                   for s in range(K)]).mean(axis=0)
+    NT = api.num_chunks(B, T, None if inp["cu_seqlens"] is None else inp["cu_seqlens"].to(torch.int32))
+    flops = backward_flops(w, 64, NT)
+    dom = int(np.argmax(st[1:])) + 1              # dominant backward kernel (the forward recompute aside)
+    kname = api.BWD_STAGE_NAMES[dom]
+    achieved = flops.get(kname, 0) / (st[dom] * 1e-3) / 1e12
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_backward_baseline(inp, args.cpu_seconds)
+    print(json.dumps({
+        "metric": "bwd tokens/s (gradients of q, k, v, beta, g, h0; forward recomputed)",
+        "value": Ttot / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": Ttot, "Nk": w.Nk, "Nv": w.Nv, "dk": w.dk, "dv": w.dv, "chunk": 64,
+                   "io_dtype": w.dtype, "seed": args.workload},
+        "stage_ms": {api.BWD_STAGE_NAMES[i]: float(st[i]) for i in range(api.BWD_NUM_STAGES)},
+        "roofline": {"bound": "alu", "kernel": kname, "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
+                     "algorithmic_flops": flops.get(kname, 0), "avg_ms": float(st[dom])},
+        "cpu_baseline": cpu,
+    }), flush=True)
+
+
+def cpu_backward_baseline(inp: dict, target_seconds: float) -> dict:
+    """The backward oracle (NumPy, fp64) on the first sequence of value head 0,
+    over as many tokens as fit in about target_seconds (timed on a growing
+    prefix), scaled to tokens/s of all value heads."""
+    from oracle import recurrence_backward
+
+    w = inp["workload"]
+    kh = 0
+    q = inp["q"].reshape(-1, w.Nk, w.dk)[:, kh:kh + 1].double().numpy()
+    k = inp["k"].reshape(-1, w.Nk, w.dk)[:, kh:kh + 1].double().numpy()
+    v = inp["v"].reshape(-1, w.Nv, w.dv)[:, :1].double().numpy()
+    beta = inp["beta"].reshape(-1, w.Nv)[:, :1].double().numpy()
+    g = None if inp["g"] is None else inp["g"].reshape(-1, w.Nv)[:, :1].double().numpy()
+    rng = np.random.default_rng(0)
+    n = 64
+    while True:
+        do = rng.standard_normal((n, 1, w.dv))
+        t0 = time.perf_counter()
+        recurrence_backward(q[:n], k[:n], v[:n], beta[:n], None if g is None else g[:n], inp["scale"], None,
+                            None, do, None)
+        dt = time.perf_counter() - t0
+        if dt > target_seconds / 4 or n * 2 > q.shape[0]:
+            break
+        n *= 2
+    rate = n / dt / w.Nv                          # tokens/s over all value heads
+    return {"value": rate, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%d tokens of one value head (NumPy fp64 backward), scaled by 1/%d heads" % (n, w.Nv)}
+
+
 def bench_segmented(args) -> None:
     """Segment-parallel state passing against the serial pass on one long
     sequence with few heads (64k tokens, 2 q/k heads, 4 value heads, dk = dv =
@@ -414,11 +520,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget; 0 skips it")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB three times (calibrates HBM byte counters)")
-    ap.add_argument("--mode", choices=("chunk", "recurrent", "segmented", "chunk-sizes"), default="chunk",
+    ap.add_argument("--mode", choices=("chunk", "recurrent", "segmented", "chunk-sizes", "backward"),
+                    default="chunk",
                     help="chunk: the chunked forward on --workload (default); recurrent: one decode step "
                          "(token-by-token kernel) for --decode-seqs sequences from a random state; segmented: "
                          "segment-parallel against serial state passing on one long sequence with few heads; "
-                         "chunk-sizes: the five-kernel path at C = 16, 32, 64 and the fused path on --workload")
+                         "chunk-sizes: the five-kernel path at C = 16, 32, 64 and the fused path on --workload; "
+                         "backward: the backward pass (forward recomputed) on --workload")
     ap.add_argument("--segment-chunks", type=int, default=0,
                     help="chunks per segment in --mode segmented (0: the library's choice)")
     ap.add_argument("--decode-seqs", type=int, default=64)
@@ -449,6 +557,9 @@ def main():
         return
     if args.mode == "chunk-sizes":
         bench_chunk_sizes(args)
+        return
+    if args.mode == "backward":
+        bench_backward(args)
         return
 
     w = synth.WORKLOADS[args.workload]

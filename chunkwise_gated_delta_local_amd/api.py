@@ -19,6 +19,8 @@ _lib = None
 GDR_F32, GDR_BF16 = 0, 1
 NUM_STAGES = 6
 STAGE_NAMES = ("chunk_table", "gate_cumsum", "build_solve", "wu", "state", "output")
+BWD_NUM_STAGES = 5
+BWD_STAGE_NAMES = ("forward_recompute", "k_bwd_prep", "k_bwd_state", "k_bwd_chunk", "k_bwd_reduce_qk")
 _DTYPES = {torch.float32: GDR_F32, torch.bfloat16: GDR_BF16}
 
 EXPORTED = ("gdr_validate", "gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd_debug_workspace_size",
@@ -73,7 +75,7 @@ def load_library():
     lib.gdr_chunk_fwd_segmented_workspace_size.argtypes = [PP, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     lib.gdr_chunk_fwd_segmented.argtypes = fwd_args[:12] + [ctypes.c_int32] + fwd_args[12:] + [P]
     lib.gdr_chunk_bwd_workspace_size.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
-    lib.gdr_chunk_bwd.argtypes = fwd_args[:10] + [P] * 8 + [P, ctypes.c_size_t, P]
+    lib.gdr_chunk_bwd.argtypes = fwd_args[:10] + [P] * 8 + [P, ctypes.c_size_t, P, P]
     for f in ("gdr_validate", "gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd_debug_workspace_size",
               "gdr_chunk_fwd", "gdr_chunk_fwd_debug", "gdr_chunk_fwd_timed", "gdr_recurrent_fwd",
               "gdr_chunk_fwd_segmented_workspace_size", "gdr_chunk_fwd_segmented",
@@ -261,7 +263,14 @@ class Backward:
         self._keep = (q, k, v, beta, g, initial_state, d_o, d_final_state, cu_dev, cu_host)
 
     def __call__(self):
-        _check(self.lib.gdr_chunk_bwd(*self.args))
+        _check(self.lib.gdr_chunk_bwd(*self.args, None))
+
+    def timed(self, events):
+        """Enqueue one backward and record the BWD_NUM_STAGES + 1
+        torch.cuda.Event objects around its stages (recorded once beforehand,
+        so that their HIP handles exist)."""
+        handles = (ctypes.c_void_p * (BWD_NUM_STAGES + 1))(*[e.cuda_event for e in events])
+        _check(self.lib.gdr_chunk_bwd(*self.args, handles))
 
 
 def chunk_bwd(q, k, v, beta, d_o, g=None, scale=None, initial_state=None, d_final_state=None,

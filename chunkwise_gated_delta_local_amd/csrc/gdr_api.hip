@@ -434,7 +434,14 @@ gdr_status_t gdr_chunk_bwd(const gdr_problem_t* p, const void* q, const void* k,
                            const void* beta, float scale, const float* initial_state, const int32_t* cu_dev,
                            const int32_t* cu_host, const void* d_o, const float* d_final_state, float* dq,
                            float* dk, float* dv, float* dbeta, float* dg, float* d_initial_state, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+                           size_t workspace_bytes, void* stream, void* const* stage_events) {
+    hipEvent_t ev[GDR_BWD_NUM_STAGES + 1];
+    if (stage_events) {
+        for (int i = 0; i <= GDR_BWD_NUM_STAGES; ++i) {
+            if (!stage_events[i]) return fail(GDR_ERR_NULL, "stage_events[%d] is NULL", i);
+            ev[i] = static_cast<hipEvent_t>(stage_events[i]);
+        }
+    }
     gdr_status_t st = check_inputs(p, q, k, v, g, beta, initial_state, cu_dev, cu_host, workspace);
     if (st != GDR_OK) return st;
     const int64_t Ttot = p->batch * p->seq_len;
@@ -464,6 +471,7 @@ gdr_status_t gdr_chunk_bwd(const gdr_problem_t* p, const void* q, const void* k,
     b.P = f(bp.off_P); b.Hn = f(bp.off_Hn); b.Vn = f(bp.off_Vn); b.Wn = f(bp.off_Wn);
     b.dSout = f(bp.off_dSout); b.dVn = f(bp.off_dVn); b.dWs = f(bp.off_dWs);
     b.dqv = f(bp.off_dqv); b.dkv = f(bp.off_dkv);
+    b.events = stage_events ? ev : nullptr;
     hipError_t e = gdr::launch_backward(b);
     if (e != hipSuccess) return fail(GDR_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     g_err[0] = '\0';

@@ -417,29 +417,36 @@ template <typename T, int DK, int DV, int C>
 hipError_t launch_bwd(const BackwardArgs& b) {
     const LaunchArgs& a = b.fwd;
     hipStream_t st = a.stream;
+    auto mark = [&](int i) { if (b.events) (void)hipEventRecord(b.events[i], st); };
+    mark(0);
     hipError_t e = launch_forward(a, nullptr);   // recompute: G, A, W, U, K^T, h, V_new
     if (e != hipSuccess) return e;
+    mark(1);
     const int32_t NT = a.nt;
     if (NT > 0) {
         k_bwd_prep<T, DK, DV, C><<<dim3(NT, a.Nv), 256, 0, st>>>(
             (const T*)a.q, (const T*)a.k, a.G, (const float*)a.H, (const float*)a.VN, (const float*)a.W,
             a.chunk_start, a.chunk_len, a.Nk, a.Nv, b.Hn, b.Vn, b.Wn, b.P);
     }
+    mark(2);
     if (a.N > 0) {
         k_bwd_state<T, DK, DV, C><<<dim3(a.N, a.Nv, DV / 16), 256, 0, st>>>(
             (const T*)a.q, (const T*)a.k, a.G, b.P, b.Wn, b.d_o, b.do_f32, b.dST, a.chunk_start, a.chunk_len,
             a.seq_first, a.Nk, a.Nv, a.scale, b.dSout, b.dVn, b.dS0);
     }
+    mark(3);
     if (NT > 0) {
         k_bwd_chunk<T, DK, DV, C><<<dim3(NT, a.Nv), 256, 0, st>>>(
             (const T*)a.q, (const T*)a.k, (const T*)a.v, a.beta, a.beta_f32, a.G, (const float*)a.A, b.P, b.Hn,
             b.Vn, b.dSout, b.dVn, b.d_o, b.do_f32, a.chunk_start, a.chunk_len, a.Nk, a.Nv, a.scale, b.dWs,
             b.dqv, b.dkv, b.dv, b.dbeta, b.dg);
     }
+    mark(4);
     const int64_t nq = a.Ttot * a.Nk * DK;
     if (nq > 0)
         k_bwd_reduce_qk<DK><<<(unsigned)((nq + 255) / 256), 256, 0, st>>>(b.dqv, b.dkv, a.Ttot, a.Nk, a.Nv, b.dq,
                                                                           b.dk);
+    mark(5);
     return hipGetLastError();
 }
 

@@ -63,6 +63,8 @@ struct BackwardArgs {
     float *Wn, *dWs;           // [Ttot][Nv][dk] W and its gradient
     float *dSout;              // [NT][Nv][dk][dv] gradients of the outgoing states
     float *dqv, *dkv;          // [Ttot][Nv][dk] dq, dk per value head
+    hipEvent_t* events;        // NULL, or 6 events: before the forward recompute and after
+                               // it, the preparation, the state pass, the per-chunk pass, the sum
 };
 hipError_t launch_backward(const BackwardArgs& b);
 

@@ -227,8 +227,15 @@ gdr_status_t gdr_chunk_fwd_segmented(const gdr_problem_t* problem,
  *                  receives the gradient at g = 0.
  *   d_initial_state [N][Nv][dk][dv] fp32 out, or NULL to skip.
  *   workspace      at least gdr_chunk_bwd_workspace_size bytes, 256-byte aligned.
+ *   stage_events   NULL, or GDR_BWD_NUM_STAGES + 1 caller-created events
+ *                  recorded on `stream`: [0] before the first kernel and [i]
+ *                  after stage i: [1] forward recompute (five kernels), [2]
+ *                  preparation (layouts, score block), [3] reverse state
+ *                  pass, [4] per-chunk gradients, [5] sum of dq and dk over
+ *                  the value heads of each q/k head.
  * All arithmetic is fp32. Errors as for gdr_chunk_fwd. Asynchronous on `stream`.
  */
+#define GDR_BWD_NUM_STAGES 5
 gdr_status_t gdr_chunk_bwd_workspace_size(const gdr_problem_t* problem, size_t* bytes);
 gdr_status_t gdr_chunk_bwd(const gdr_problem_t* problem,
                            const void* q, const void* k, const void* v,
@@ -238,7 +245,8 @@ gdr_status_t gdr_chunk_bwd(const gdr_problem_t* problem,
                            const void* d_o, const float* d_final_state,
                            float* dq, float* dk, float* dv, float* dbeta, float* dg,
                            float* d_initial_state,
-                           void* workspace, size_t workspace_bytes, void* stream);
+                           void* workspace, size_t workspace_bytes, void* stream,
+                           void* const* stage_events);
 
 /*
  * Intermediates of the five kernels, for per-kernel parity checks. Each
