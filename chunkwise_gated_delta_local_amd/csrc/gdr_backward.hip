@@ -214,12 +214,79 @@ __global__ __launch_bounds__(256) void k_bwd_state(const T* __restrict__ q, cons
 }
 
 // ------------------------------------------------------------ per-chunk gradients
-// One workgroup per (chunk, value head). The C x C matrices (A, D, P, dP, dA /
-// F, A^T dA, K K^T) sit in LDS; the C x dk and C x dv operands are read from
-// memory. Writes dq and dk of this value head (summed over the group later),
-// dv, dbeta and dg, and uses a per-token scratch for dW.
+constexpr int kStageK = 16;                     // K-tile of the staged products
+
+// Staged product: out(i, j) = sum over k < K of a(i, k) b(k, j) for i < M,
+// j < N (K a multiple of 16). Tiles of 16 columns of a and 16 rows of b are
+// first copied to LDS by all threads, consecutive threads taking consecutive
+// addresses of the operand (AK: a(i, k) is contiguous in k, else in i; BJ:
+// b(k, j) is contiguous in j, else in k). Each thread then accumulates its
+// 4 x 4 output blocks from LDS: the a values of a block row are shared by many
+// lanes (broadcast reads) and the b values of 4 consecutive columns are one
+// 16-byte read. As holds M x 17 floats, Bs 16 x (N + 4).
+template <int M, int N, bool AK, bool BJ, typename FA, typename FB, typename FS>
+__device__ __forceinline__ void gemm_lds(int K, float* As, float* Bs, FA&& a, FB&& b, FS&& store) {
+    constexpr int KT = kStageK, AP = KT + 1, BP = N + 4;
+    constexpr int BN = N / 4, NBLK = (M / 4) * BN, PER = (NBLK + 255) / 256;
+    static_assert(M % 4 == 0 && N % 4 == 0, "4 x 4 blocks");
+    const int tid = threadIdx.x;
+    float acc[PER][4][4];
+#pragma unroll
+    for (int p = 0; p < PER; ++p)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[p][r][c] = 0.f;
+    for (int k0 = 0; k0 < K; k0 += KT) {
+        __syncthreads();                               // the previous tile is consumed
+        for (int idx = tid; idx < M * KT; idx += 256) {
+            const int i = AK ? idx / KT : idx % M, kk = AK ? idx % KT : idx / M;
+            As[i * AP + kk] = a(i, k0 + kk);
+        }
+        for (int idx = tid; idx < KT * N; idx += 256) {
+            const int kk = BJ ? idx / N : idx % KT, j = BJ ? idx % N : idx / KT;
+            Bs[kk * BP + j] = b(k0 + kk, j);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int blk = tid + 256 * p;
+            if (NBLK % 256 == 0 || blk < NBLK) {
+                const int i0 = (blk / BN) * 4, j0 = (blk % BN) * 4;
+#pragma unroll
+                for (int kk = 0; kk < KT; ++kk) {
+                    const f32x4 bv = *reinterpret_cast<const f32x4*>(&Bs[kk * BP + j0]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float av = As[(i0 + r) * AP + kk];
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) acc[p][r][c] += av * bv[c];
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+        const int blk = tid + 256 * p;
+        if (NBLK % 256 == 0 || blk < NBLK) {
+            const int i0 = (blk / BN) * 4, j0 = (blk % BN) * 4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) store(i0 + r, j0 + c, acc[p][r][c]);
+        }
+    }
+}
+
+// One workgroup per (chunk, value head). Four C x C matrices sit in LDS (A;
+// dM = dP (.) D; dA, then F, then F (.) D; A^T dA, then K K^T) with the
+// staging tiles of the products, about 79 KB for C = 64, so that two
+// workgroups share a compute unit; D is recomputed from the gate sums where
+// it is needed. Writes dq and dk of this value head (summed over the group
+// later), dv, dbeta and dg, and uses a per-token scratch for dW.
 template <typename T, int DK, int DV, int C>
-__global__ __launch_bounds__(256) void k_bwd_chunk(const T* __restrict__ q, const T* __restrict__ k,
+__global__ __launch_bounds__(256, 2) void k_bwd_chunk(const T* __restrict__ q, const T* __restrict__ k,
                                                     const T* __restrict__ v, const void* __restrict__ beta,
                                                     int beta_f32, const float* __restrict__ G,
                                                     const float* __restrict__ A, const float* __restrict__ P,
@@ -231,8 +298,10 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(const T* __restrict__ q, cons
                                                     float scale, float* __restrict__ dW, float* __restrict__ dqv,
                                                     float* __restrict__ dkv, float* __restrict__ dv,
                                                     float* __restrict__ dbeta, float* __restrict__ dg) {
-    constexpr int CP = C + 1;
-    __shared__ float Am[C][CP], Dm[C][CP], Pm[C][CP], dPm[C][CP], dAm[C][CP], Tm[C][CP], KKm[C][CP];
+    constexpr int NMAX = (DK > DV ? DK : DV) > C ? (DK > DV ? DK : DV) : C;
+    __shared__ float Am[C * C], dMm[C * C], dAm[C * C], Xm[C * C];
+    __shared__ float As[C * (kStageK + 1)];
+    __shared__ __attribute__((aligned(16))) float Bs[kStageK * (NMAX + 4)];
     __shared__ float gs[C], eg[C], elg[C], bs[C], dGs[C], dBs[C], cv[C];
     __shared__ float sum_sh;
     const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
@@ -243,6 +312,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(const T* __restrict__ q, cons
     const int64_t ch = (int64_t)c * Nv + h;
     const float* Hc = Hn + ch * DK * DV;          // entering state [dk][dv]
     const float* dSc = dSout + ch * DK * DV;      // gradient of the outgoing state [dk][dv]
+    const float* Pc = P + ch * C * C;
 
     auto Qg = [&](int i, int m) { return i < L ? to_f(q[((s + i) * Nk + kh) * DK + m]) : 0.f; };
     auto Kg = [&](int i, int m) { return i < L ? to_f(k[((s + i) * Nk + kh) * DK + m]) : 0.f; };
@@ -252,6 +322,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(const T* __restrict__ q, cons
     auto dVg = [&](int i, int j) { return i < L ? dVn[((s + i) * Nv + h) * DV + j] : 0.f; };
     auto dWg = [&](int i, int m) { return i < L ? dW[((s + i) * Nv + h) * DK + m] : 0.f; };
     auto row_dk = [&](int i) { return ((s + i) * Nv + h) * DK; };
+    auto Dv = [&](int i, int j) { return (i < L && j <= i) ? __expf(gs[i] - gs[j]) : 0.f; };
 
     if (tid < C) {
         const bool ok = tid < L;
@@ -264,8 +335,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(const T* __restrict__ q, cons
     if (tid == 0) sum_sh = 0.f;
     for (int idx = tid; idx < C * C; idx += 256) {
         const int i = idx / C, j = idx % C;
-        Am[i][j] = (i < L && j <= i) ? A[((s + i) * Nv + h) * C + j] : 0.f;
-        Pm[i][j] = P[ch * C * C + idx];
+        Am[idx] = (i < L && j <= i) ? A[((s + i) * Nv + h) * C + j] : 0.f;
     }
     __syncthreads();
     const float gL = gs[L - 1];
@@ -273,38 +343,30 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(const T* __restrict__ q, cons
         eg[tid] = tid < L ? __expf(gs[tid]) : 0.f;
         elg[tid] = tid < L ? __expf(gL - gs[tid]) : 0.f;
     }
-    for (int idx = tid; idx < C * C; idx += 256) {
-        const int i = idx / C, j = idx % C;
-        Dm[i][j] = (i < L && j <= i) ? __expf(gs[i] - gs[j]) : 0.f;
-    }
-    __syncthreads();
 
-    // dP = scale dO V_new^T on and below the diagonal
-    gemm44<C, C>(DV, dOg, [&](int kk, int j) { return Vng(j, kk); },
-                 [&](int i, int j, float x) { dPm[i][j] = (i < L && j <= i) ? scale * x : 0.f; });
-    __syncthreads();
-    // gate gradient through D in P: E = dP (.) P, dG += row sums - column sums
-    if (tid < C) {
-        float acc = 0.f;
-        for (int j = 0; j < C; ++j) acc += dPm[tid][j] * Pm[tid][j] - dPm[j][tid] * Pm[j][tid];
-        dGs[tid] += acc;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < C * C; idx += 256) dPm[idx / C][idx % C] *= Dm[idx / C][idx % C];   // dM = dP (.) D
-    __syncthreads();
-
-    // dQ = scale diag(exp(G)) dO h^T + dM K
-    gemm44<C, DK>(DV + C,
-        [&](int i, int kk) { return kk < DV ? scale * eg[i] * dOg(i, kk) : dPm[i][kk - DV]; },
-        [&](int kk, int m) { return kk < DV ? Hc[m * DV + kk] : Kg(kk - DV, m); },
-        [&](int i, int m, float x) { if (i < L) dqv[row_dk(i) + m] = x; });
+    // dP = scale dO V_new^T on and below the diagonal; dM = dP (.) D, and the gate
+    // gradient through D in P: E = dP (.) P adds to dG_i and subtracts from dG_j
+    gemm_lds<C, C, true, false>(DV, As, Bs, dOg, [&](int kk, int j) { return Vng(j, kk); },
+        [&](int i, int j, float x) {
+            const float dp = (i < L && j <= i) ? scale * x : 0.f;
+            dMm[i * C + j] = dp * Dv(i, j);
+            const float e = dp * Pc[i * C + j];
+            if (e != 0.f) {
+                atomicAdd(&dGs[i], e);
+                atomicAdd(&dGs[j], -e);
+            }
+        });
+    // dQ = scale diag(exp(G)) dO h^T + dM K (the same thread owns each element in both products)
+    gemm_lds<C, DK, true, false>(DV, As, Bs, [&](int i, int kk) { return scale * eg[i] * dOg(i, kk); },
+                                 [&](int kk, int m) { return Hc[m * DV + kk]; },
+                                 [&](int i, int m, float x) { if (i < L) dqv[row_dk(i) + m] = x; });
+    gemm_lds<C, DK, true, true>(C, As, Bs, [&](int i, int kk) { return dMm[i * C + kk]; }, Kg,
+                                [&](int i, int m, float x) { if (i < L) dqv[row_dk(i) + m] += x; });
     // dW = -dV_new h^T
-    gemm44<C, DK>(DV, dVg, [&](int kk, int m) { return Hc[m * DV + kk]; },
-                  [&](int i, int m, float x) { if (i < L) dW[row_dk(i) + m] = -x; });
-    __syncthreads();
-
+    gemm_lds<C, DK, true, false>(DV, As, Bs, dVg, [&](int kk, int m) { return Hc[m * DV + kk]; },
+                                 [&](int i, int m, float x) { if (i < L) dW[row_dk(i) + m] = -x; });
     // dV = diag(beta) A^T dU (dU = dV_new); dbeta += v . (A^T dU)
-    gemm44<C, DV>(C, [&](int i, int kk) { return Am[kk][i]; }, dVg,
+    gemm_lds<C, DV, false, true>(C, As, Bs, [&](int i, int kk) { return Am[kk * C + i]; }, dVg,
         [&](int i, int j, float x) {
             if (i < L) {
                 dv[((s + i) * Nv + h) * DV + j] = bs[i] * x;
@@ -312,7 +374,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(const T* __restrict__ q, cons
             }
         });
     // A^T dW: dK = diag(beta exp(G)) A^T dW; dbeta, dG through exp(G) in W
-    gemm44<C, DK>(C, [&](int i, int kk) { return Am[kk][i]; }, dWg,
+    gemm_lds<C, DK, false, true>(C, As, Bs, [&](int i, int kk) { return Am[kk * C + i]; }, dWg,
         [&](int i, int m, float x) {
             if (i < L) {
                 dkv[row_dk(i) + m] = bs[i] * eg[i] * x;
@@ -322,45 +384,46 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(const T* __restrict__ q, cons
             }
         });
     // dA = dU (diag(beta) V)^T + dW (diag(beta exp(G)) K)^T
-    gemm44<C, C>(DV + DK,
-        [&](int i, int kk) { return kk < DV ? dVg(i, kk) : dWg(i, kk - DV); },
-        [&](int kk, int j) { return kk < DV ? bs[j] * Vg(j, kk) : bs[j] * eg[j] * Kg(j, kk - DV); },
-        [&](int i, int j, float x) { dAm[i][j] = x; });
+    gemm_lds<C, C, true, false>(DV, As, Bs, dVg, [&](int kk, int j) { return bs[j] * Vg(j, kk); },
+                                [&](int i, int j, float x) { dAm[i * C + j] = x; });
+    gemm_lds<C, C, true, false>(DK, As, Bs, dWg, [&](int kk, int j) { return bs[j] * eg[j] * Kg(j, kk); },
+                                [&](int i, int j, float x) { dAm[i * C + j] += x; });
+    // A^T dA, then F = strictly lower part of dL = -(A^T dA) A^T
+    gemm_lds<C, C, false, true>(C, As, Bs, [&](int i, int kk) { return Am[kk * C + i]; },
+                                [&](int kk, int j) { return dAm[kk * C + j]; },
+                                [&](int i, int j, float x) { Xm[i * C + j] = x; });
+    gemm_lds<C, C, true, false>(C, As, Bs, [&](int i, int kk) { return Xm[i * C + kk]; },
+                                [&](int kk, int j) { return Am[j * C + kk]; },
+                                [&](int i, int j, float x) { dAm[i * C + j] = (i < L && j < i) ? -x : 0.f; });
     // K K^T
-    gemm44<C, C>(DK, Kg, [&](int kk, int j) { return Kg(j, kk); }, [&](int i, int j, float x) { KKm[i][j] = x; });
-    __syncthreads();
-    // A^T dA
-    gemm44<C, C>(C, [&](int i, int kk) { return Am[kk][i]; }, [&](int kk, int j) { return dAm[kk][j]; },
-                 [&](int i, int j, float x) { Tm[i][j] = x; });
-    __syncthreads();
-    // F = strictly lower part of dL = -(A^T dA) A^T
-    gemm44<C, C>(C, [&](int i, int kk) { return Tm[i][kk]; }, [&](int kk, int j) { return Am[j][kk]; },
-                 [&](int i, int j, float x) { dAm[i][j] = (i < L && j < i) ? -x : 0.f; });
+    gemm_lds<C, C, true, false>(DK, As, Bs, Kg, [&](int kk, int j) { return Kg(j, kk); },
+                                [&](int i, int j, float x) { Xm[i * C + j] = x; });
     __syncthreads();
     // dbeta and dG through L_ij = beta_i (k_i . k_j) D_ij
     if (tid < C) {
         float db = 0.f, dgr = 0.f;
         for (int j = 0; j < C; ++j) {
-            db += dAm[tid][j] * KKm[tid][j] * Dm[tid][j];
-            dgr += dAm[tid][j] * bs[tid] * KKm[tid][j] * Dm[tid][j] - dAm[j][tid] * bs[j] * KKm[j][tid] * Dm[j][tid];
+            const float fd = dAm[tid * C + j] * Xm[tid * C + j] * Dv(tid, j);
+            db += fd;
+            dgr += fd * bs[tid] - dAm[j * C + tid] * bs[j] * Xm[j * C + tid] * Dv(j, tid);
         }
         dBs[tid] += db;
         dGs[tid] += dgr;
     }
     __syncthreads();
-    for (int idx = tid; idx < C * C; idx += 256) dAm[idx / C][idx % C] *= Dm[idx / C][idx % C];   // F (.) D
-    __syncthreads();
+    for (int idx = tid; idx < C * C; idx += 256) dAm[idx] *= Dv(idx / C, idx % C);   // F (.) D
     // dK += diag(beta) (F (.) D) K + (F (.) D)^T diag(beta) K + dM^T Q
-    gemm44<C, DK>(3 * C,
+    gemm_lds<C, DK, false, true>(3 * C, As, Bs,
         [&](int i, int kk) {
-            return kk < C ? bs[i] * dAm[i][kk] : (kk < 2 * C ? dAm[kk - C][i] : dPm[kk - 2 * C][i]);
+            return kk < C ? bs[i] * dAm[i * C + kk]
+                          : (kk < 2 * C ? dAm[(kk - C) * C + i] : dMm[(kk - 2 * C) * C + i]);
         },
         [&](int kk, int m) {
             return kk < C ? Kg(kk, m) : (kk < 2 * C ? bs[kk - C] * Kg(kk - C, m) : Qg(kk - 2 * C, m));
         },
         [&](int i, int m, float x) { if (i < L) dkv[row_dk(i) + m] += x; });
     // dK += diag(exp(G_last - G)) V_new dS^T; the same term's gate gradient
-    gemm44<C, DK>(DV, Vng, [&](int kk, int m) { return dSc[m * DV + kk]; },
+    gemm_lds<C, DK, true, false>(DV, As, Bs, Vng, [&](int kk, int m) { return dSc[m * DV + kk]; },
         [&](int i, int m, float x) {
             if (i < L) {
                 const float y = elg[i] * x;
@@ -369,7 +432,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(const T* __restrict__ q, cons
             }
         });
     // dG through exp(G) in the inter-chunk output: dG_i += dO_i . (scale exp(G_i) h^T q_i)
-    gemm44<C, DV>(DK, Qg, [&](int kk, int j) { return Hc[kk * DV + j]; },
+    gemm_lds<C, DV, true, true>(DK, As, Bs, Qg, [&](int kk, int j) { return Hc[kk * DV + j]; },
         [&](int i, int j, float x) { if (i < L) atomicAdd(&dGs[i], scale * eg[i] * dOg(i, j) * x); });
     // exp(G_last) h in the state update: sum(dS (.) h)
     {
