@@ -126,6 +126,9 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ q, const
 // it stores dS (the gradient with respect to the chunk's outgoing state) and
 // dV_new for the chunk, then moves dS to the chunk's entering state. After the
 // first chunk, dS is the gradient with respect to the initial state.
+// The next chunk's operands (K, Q, W rows, the score block, dO, G) are loaded
+// into registers with 16-byte loads while the current chunk is computed, and
+// the barriers wait for LDS traffic only, so the loads stay in flight.
 template <typename T, int DK, int DV, int C>
 __global__ __launch_bounds__(256) void k_bwd_state(const T* __restrict__ q, const T* __restrict__ k,
                                                     const float* __restrict__ G, const float* __restrict__ P,
@@ -136,12 +139,17 @@ __global__ __launch_bounds__(256) void k_bwd_state(const T* __restrict__ q, cons
                                                     const int32_t* __restrict__ seq_first, int32_t Nk, int32_t Nv,
                                                     float scale, float* __restrict__ dSout,
                                                     float* __restrict__ dVn, float* __restrict__ dS0) {
+    typedef typename Vec<T>::v8 v8;
     constexpr int CP = C + 1, KP = DK + 1;
     constexpr int PER = DK * 16 / 256;          // dS elements per thread
+    constexpr int NSEG = C * DK / 8;            // 8-element row pieces of K, Q and W
+    constexpr int NK8 = (NSEG + 255) / 256;
+    constexpr int NP4 = (C * C / 4 + 255) / 256;
+    constexpr int NO = (C * 16 + 255) / 256;
     __shared__ float dS[DK][16];
     __shared__ float Ps[C][CP];
-    __shared__ float Ks[C][KP], Qe[C][KP], Ws[C][KP];
-    __shared__ float dOt[C][16], dVt[C][16];
+    __shared__ float Ks[C][KP], Qs[C][KP], Ws[C][KP];
+    __shared__ float dOt[C][16], dOe[C][16], dVt[C][16];
     __shared__ float gs[C];
     const int n = blockIdx.x, h = blockIdx.y, nb = blockIdx.z, tid = threadIdx.x;
     const int kh = h / (Nv / Nk);
@@ -149,28 +157,78 @@ __global__ __launch_bounds__(256) void k_bwd_state(const T* __restrict__ q, cons
         const int m = idx / 16, j = idx % 16;
         dS[m][j] = dST ? dST[(((int64_t)n * Nv + h) * DK + m) * DV + nb * 16 + j] : 0.f;
     }
+    v8 kr[NK8], qr[NK8];
+    f32x4 wr[2 * NK8], pr[NP4];
+    float orr[NO], gr = 0.f;
+    auto fetch = [&](int c) {
+        const int64_t s = chunk_start[c];
+        const int L = chunk_len[c];
+#pragma unroll
+        for (int e = 0; e < NK8; ++e) {
+            const int idx = tid + 256 * e, i = idx / (DK / 8), seg = idx % (DK / 8);
+            const bool ok = idx < NSEG && i < L;
+            const int64_t row = ((s + i) * Nk + kh) * DK + seg * 8;
+            const float* wp = Wn + ((s + i) * Nv + h) * DK + seg * 8;
+            kr[e] = ok ? *reinterpret_cast<const v8*>(k + row) : zero_pair<T>();
+            qr[e] = ok ? *reinterpret_cast<const v8*>(q + row) : zero_pair<T>();
+            wr[2 * e] = ok ? *reinterpret_cast<const f32x4*>(wp) : f32x4{0.f, 0.f, 0.f, 0.f};
+            wr[2 * e + 1] = ok ? *reinterpret_cast<const f32x4*>(wp + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        const float* Pc = P + ((int64_t)c * Nv + h) * C * C;
+#pragma unroll
+        for (int e = 0; e < NP4; ++e) {
+            const int idx = tid + 256 * e;
+            pr[e] = idx < C * C / 4 ? *reinterpret_cast<const f32x4*>(Pc + 4 * idx) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int e = 0; e < NO; ++e) {
+            const int idx = tid + 256 * e, i = idx / 16, j = idx % 16;
+            orr[e] = (idx < C * 16 && i < L) ? load_any(d_o, ((s + i) * Nv + h) * DV + nb * 16 + j, do_f32) : 0.f;
+        }
+        gr = (tid < C && tid < L) ? G[(s + tid) * Nv + h] : 0.f;
+    };
+    auto commit = [&]() {                          // registers -> LDS
+#pragma unroll
+        for (int e = 0; e < NK8; ++e) {
+            const int idx = tid + 256 * e, i = idx / (DK / 8), seg = idx % (DK / 8);
+            if (idx < NSEG) {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    Ks[i][seg * 8 + t] = to_f(kr[e][t]);
+                    Qs[i][seg * 8 + t] = to_f(qr[e][t]);
+                    Ws[i][seg * 8 + t] = wr[2 * e + t / 4][t % 4];
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < NP4; ++e) {
+            const int idx = tid + 256 * e;
+            if (idx < C * C / 4) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) Ps[(4 * idx + t) / C][(4 * idx + t) % C] = pr[e][t];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < NO; ++e) {
+            const int idx = tid + 256 * e;
+            if (idx < C * 16) dOt[idx / 16][idx % 16] = orr[e];
+        }
+        if (tid < C) gs[tid] = gr;
+    };
     const int c0 = seq_first[n], c1 = seq_first[n + 1];
+    if (c1 > c0) fetch(c1 - 1);
     for (int c = c1 - 1; c >= c0; --c) {
         const int64_t s = chunk_start[c];
         const int L = chunk_len[c];
-        __syncthreads();                              // the previous chunk's readers are done
-        if (tid < C) gs[tid] = tid < L ? G[(s + tid) * Nv + h] : 0.f;
-        const float* Pc = P + ((int64_t)c * Nv + h) * C * C;
-        for (int idx = tid; idx < C * C; idx += 256) Ps[idx / C][idx % C] = Pc[idx];
-        for (int idx = tid; idx < C * DK; idx += 256) {
-            const int i = idx / DK, m = idx % DK;
-            const bool ok = i < L;
-            const int64_t row = (s + i) * Nk + kh;
-            Ks[i][m] = ok ? to_f(k[row * DK + m]) : 0.f;
-            Qe[i][m] = ok ? scale * __expf(G[(s + i) * Nv + h]) * to_f(q[row * DK + m]) : 0.f;
-            Ws[i][m] = ok ? Wn[((s + i) * Nv + h) * DK + m] : 0.f;
-        }
+        lds_barrier();                                // the previous chunk's readers are done
+        commit();
+        lds_barrier();
+        if (c > c0) fetch(c - 1);                     // in flight while this chunk is computed
+        const float gL = gs[L - 1];
         for (int idx = tid; idx < C * 16; idx += 256) {
             const int i = idx / 16, j = idx % 16;
-            dOt[i][j] = i < L ? load_any(d_o, ((s + i) * Nv + h) * DV + nb * 16 + j, do_f32) : 0.f;
+            dOe[i][j] = i < L ? scale * __expf(gs[i]) * dOt[i][j] : 0.f;
         }
-        __syncthreads();
-        const float gL = gs[L - 1];
         for (int idx = tid; idx < DK * 16; idx += 256) {
             const int m = idx / 16, j = idx % 16;
             dSout[(((int64_t)c * Nv + h) * DK + m) * DV + nb * 16 + j] = dS[m][j];
@@ -179,32 +237,32 @@ __global__ __launch_bounds__(256) void k_bwd_state(const T* __restrict__ q, cons
         for (int idx = tid; idx < C * 16; idx += 256) {
             const int i = idx / 16, j = idx % 16;
             float a1 = 0.f, a2 = 0.f;
-            for (int t = i; t < C; ++t) a1 += Ps[t][i] * dOt[t][j];
+            for (int t = i; t < L; ++t) a1 += Ps[t][i] * dOt[t][j];
 #pragma unroll 8
             for (int m = 0; m < DK; ++m) a2 += Ks[i][m] * dS[m][j];
             const float val = i < L ? scale * a1 + __expf(gL - gs[i]) * a2 : 0.f;
             dVt[i][j] = val;
             if (i < L) dVn[((s + i) * Nv + h) * DV + nb * 16 + j] = val;
         }
-        __syncthreads();
-        // dS_in = exp(G_last) dS + scale Q^T diag(exp(G)) dO - W^T dV_new
+        lds_barrier();
+        // dS_in = exp(G_last) dS + Q^T (scale diag(exp(G)) dO) - W^T dV_new
         const float eL = __expf(gL);
         float nw[PER];
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
             const int idx = tid + 256 * e, m = idx / 16, j = idx % 16;
             float acc = 0.f;
-            for (int i = 0; i < L; ++i) acc += Qe[i][m] * dOt[i][j] - Ws[i][m] * dVt[i][j];
+            for (int i = 0; i < L; ++i) acc += Qs[i][m] * dOe[i][j] - Ws[i][m] * dVt[i][j];
             nw[e] = eL * dS[m][j] + acc;
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
             const int idx = tid + 256 * e;
             dS[idx / 16][idx % 16] = nw[e];
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (dS0) {
         for (int idx = tid; idx < DK * 16; idx += 256) {
             const int m = idx / 16, j = idx % 16;
