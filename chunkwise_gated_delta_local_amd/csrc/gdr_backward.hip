@@ -78,200 +78,6 @@ __device__ __forceinline__ float load_any(const void* p, int64_t idx, int is_f32
     return is_f32 ? reinterpret_cast<const float*>(p)[idx] : (float)reinterpret_cast<const bf16*>(p)[idx];
 }
 
-// ------------------------------------------------------------ preparation
-// One workgroup per (chunk, value head): the forward intermediates in natural
-// row-major layouts (the chunk's entering state h [dk][dv], V_new and W by
-// token row), and the score block P = (Q K^T) (.) D [C][C], zero above the
-// diagonal and past the chunk end.
-template <typename T, int DK, int DV, int C>
-__global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ q, const T* __restrict__ k,
-                                                   const float* __restrict__ G, const float* __restrict__ Hf,
-                                                   const float* __restrict__ VNf, const float* __restrict__ Wf,
-                                                   const int32_t* __restrict__ chunk_start,
-                                                   const int32_t* __restrict__ chunk_len, int32_t Nk, int32_t Nv,
-                                                   float* __restrict__ Hn, float* __restrict__ Vn,
-                                                   float* __restrict__ Wn, float* __restrict__ P) {
-    constexpr int NKP = DK / 32, NNB = DV / 16, NTB = C / 16, NTP = C < 32 ? 1 : C / 32;
-    const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-    const int kh = h / (Nv / Nk);
-    const int64_t s = chunk_start[c];
-    const int L = chunk_len[c];
-    if (L <= 0) return;
-    __shared__ float gs[C];
-    if (tid < C) gs[tid] = tid < L ? G[(s + tid) * Nv + h] : 0.f;
-    const int64_t ch = (int64_t)c * Nv + h;
-    for (int idx = tid; idx < DK * DV; idx += 256) {
-        const int i = idx / DV, j = idx % DV;
-        Hn[ch * DK * DV + idx] = Hf[((ch * NNB + j / 16) * NKP + i / 32) * 512 + pair_off(j % 16, i % 32)];
-    }
-    for (int idx = tid; idx < L * DV; idx += 256) {
-        const int p = idx / DV, j = idx % DV;
-        Vn[((s + p) * Nv + h) * DV + j] = VNf[((ch * NNB + j / 16) * NTP + p / 32) * 512 + pair_off(j % 16, p % 32)];
-    }
-    for (int idx = tid; idx < L * DK; idx += 256) {
-        const int p = idx / DK, i = idx % DK;
-        Wn[((s + p) * Nv + h) * DK + i] = Wf[((ch * NTB + p / 16) * NKP + i / 32) * 512 + pair_off(p % 16, i % 32)];
-    }
-    __syncthreads();
-    float* Pc = P + ch * C * C;
-    gemm44<C, C>(DK,
-        [&](int i, int kk) { return i < L ? to_f(q[((s + i) * Nk + kh) * DK + kk]) : 0.f; },
-        [&](int kk, int j) { return j < L ? to_f(k[((s + j) * Nk + kh) * DK + kk]) : 0.f; },
-        [&](int i, int j, float x) { Pc[i * C + j] = (i < L && j <= i) ? x * __expf(gs[i] - gs[j]) : 0.f; });
-}
-
-// ------------------------------------------------------------ reverse state pass
-// One workgroup per (sequence, value head, 16 columns of dv) walks the chunks
-// backwards with the 16-column slice of the state gradient dS in LDS (fp32):
-// it stores dS (the gradient with respect to the chunk's outgoing state) and
-// dV_new for the chunk, then moves dS to the chunk's entering state. After the
-// first chunk, dS is the gradient with respect to the initial state.
-// The next chunk's operands (K, Q, W rows, the score block, dO, G) are loaded
-// into registers with 16-byte loads while the current chunk is computed, and
-// the barriers wait for LDS traffic only, so the loads stay in flight.
-template <typename T, int DK, int DV, int C>
-__global__ __launch_bounds__(256) void k_bwd_state(const T* __restrict__ q, const T* __restrict__ k,
-                                                    const float* __restrict__ G, const float* __restrict__ P,
-                                                    const float* __restrict__ Wn, const void* __restrict__ d_o,
-                                                    int do_f32, const float* __restrict__ dST,
-                                                    const int32_t* __restrict__ chunk_start,
-                                                    const int32_t* __restrict__ chunk_len,
-                                                    const int32_t* __restrict__ seq_first, int32_t Nk, int32_t Nv,
-                                                    float scale, float* __restrict__ dSout,
-                                                    float* __restrict__ dVn, float* __restrict__ dS0) {
-    typedef typename Vec<T>::v8 v8;
-    constexpr int CP = C + 1, KP = DK + 1;
-    constexpr int PER = DK * 16 / 256;          // dS elements per thread
-    constexpr int NSEG = C * DK / 8;            // 8-element row pieces of K, Q and W
-    constexpr int NK8 = (NSEG + 255) / 256;
-    constexpr int NP4 = (C * C / 4 + 255) / 256;
-    constexpr int NO = (C * 16 + 255) / 256;
-    __shared__ float dS[DK][16];
-    __shared__ float Ps[C][CP];
-    __shared__ float Ks[C][KP], Qs[C][KP], Ws[C][KP];
-    __shared__ float dOt[C][16], dOe[C][16], dVt[C][16];
-    __shared__ float gs[C];
-    const int n = blockIdx.x, h = blockIdx.y, nb = blockIdx.z, tid = threadIdx.x;
-    const int kh = h / (Nv / Nk);
-    for (int idx = tid; idx < DK * 16; idx += 256) {
-        const int m = idx / 16, j = idx % 16;
-        dS[m][j] = dST ? dST[(((int64_t)n * Nv + h) * DK + m) * DV + nb * 16 + j] : 0.f;
-    }
-    v8 kr[NK8], qr[NK8];
-    f32x4 wr[2 * NK8], pr[NP4];
-    float orr[NO], gr = 0.f;
-    auto fetch = [&](int c) {
-        const int64_t s = chunk_start[c];
-        const int L = chunk_len[c];
-#pragma unroll
-        for (int e = 0; e < NK8; ++e) {
-            const int idx = tid + 256 * e, i = idx / (DK / 8), seg = idx % (DK / 8);
-            const bool ok = idx < NSEG && i < L;
-            const int64_t row = ((s + i) * Nk + kh) * DK + seg * 8;
-            const float* wp = Wn + ((s + i) * Nv + h) * DK + seg * 8;
-            kr[e] = ok ? *reinterpret_cast<const v8*>(k + row) : zero_pair<T>();
-            qr[e] = ok ? *reinterpret_cast<const v8*>(q + row) : zero_pair<T>();
-            wr[2 * e] = ok ? *reinterpret_cast<const f32x4*>(wp) : f32x4{0.f, 0.f, 0.f, 0.f};
-            wr[2 * e + 1] = ok ? *reinterpret_cast<const f32x4*>(wp + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        const float* Pc = P + ((int64_t)c * Nv + h) * C * C;
-#pragma unroll
-        for (int e = 0; e < NP4; ++e) {
-            const int idx = tid + 256 * e;
-            pr[e] = idx < C * C / 4 ? *reinterpret_cast<const f32x4*>(Pc + 4 * idx) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int e = 0; e < NO; ++e) {
-            const int idx = tid + 256 * e, i = idx / 16, j = idx % 16;
-            orr[e] = (idx < C * 16 && i < L) ? load_any(d_o, ((s + i) * Nv + h) * DV + nb * 16 + j, do_f32) : 0.f;
-        }
-        gr = (tid < C && tid < L) ? G[(s + tid) * Nv + h] : 0.f;
-    };
-    auto commit = [&]() {                          // registers -> LDS
-#pragma unroll
-        for (int e = 0; e < NK8; ++e) {
-            const int idx = tid + 256 * e, i = idx / (DK / 8), seg = idx % (DK / 8);
-            if (idx < NSEG) {
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    Ks[i][seg * 8 + t] = to_f(kr[e][t]);
-                    Qs[i][seg * 8 + t] = to_f(qr[e][t]);
-                    Ws[i][seg * 8 + t] = wr[2 * e + t / 4][t % 4];
-                }
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < NP4; ++e) {
-            const int idx = tid + 256 * e;
-            if (idx < C * C / 4) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) Ps[(4 * idx + t) / C][(4 * idx + t) % C] = pr[e][t];
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < NO; ++e) {
-            const int idx = tid + 256 * e;
-            if (idx < C * 16) dOt[idx / 16][idx % 16] = orr[e];
-        }
-        if (tid < C) gs[tid] = gr;
-    };
-    const int c0 = seq_first[n], c1 = seq_first[n + 1];
-    if (c1 > c0) fetch(c1 - 1);
-    for (int c = c1 - 1; c >= c0; --c) {
-        const int64_t s = chunk_start[c];
-        const int L = chunk_len[c];
-        lds_barrier();                                // the previous chunk's readers are done
-        commit();
-        lds_barrier();
-        if (c > c0) fetch(c - 1);                     // in flight while this chunk is computed
-        const float gL = gs[L - 1];
-        for (int idx = tid; idx < C * 16; idx += 256) {
-            const int i = idx / 16, j = idx % 16;
-            dOe[i][j] = i < L ? scale * __expf(gs[i]) * dOt[i][j] : 0.f;
-        }
-        for (int idx = tid; idx < DK * 16; idx += 256) {
-            const int m = idx / 16, j = idx % 16;
-            dSout[(((int64_t)c * Nv + h) * DK + m) * DV + nb * 16 + j] = dS[m][j];
-        }
-        // dV_new = scale P^T dO + diag(exp(G_last - G)) K dS
-        for (int idx = tid; idx < C * 16; idx += 256) {
-            const int i = idx / 16, j = idx % 16;
-            float a1 = 0.f, a2 = 0.f;
-            for (int t = i; t < L; ++t) a1 += Ps[t][i] * dOt[t][j];
-#pragma unroll 8
-            for (int m = 0; m < DK; ++m) a2 += Ks[i][m] * dS[m][j];
-            const float val = i < L ? scale * a1 + __expf(gL - gs[i]) * a2 : 0.f;
-            dVt[i][j] = val;
-            if (i < L) dVn[((s + i) * Nv + h) * DV + nb * 16 + j] = val;
-        }
-        lds_barrier();
-        // dS_in = exp(G_last) dS + Q^T (scale diag(exp(G)) dO) - W^T dV_new
-        const float eL = __expf(gL);
-        float nw[PER];
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int idx = tid + 256 * e, m = idx / 16, j = idx % 16;
-            float acc = 0.f;
-            for (int i = 0; i < L; ++i) acc += Qs[i][m] * dOe[i][j] - Ws[i][m] * dVt[i][j];
-            nw[e] = eL * dS[m][j] + acc;
-        }
-        lds_barrier();
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int idx = tid + 256 * e;
-            dS[idx / 16][idx % 16] = nw[e];
-        }
-    }
-    lds_barrier();
-    if (dS0) {
-        for (int idx = tid; idx < DK * 16; idx += 256) {
-            const int m = idx / 16, j = idx % 16;
-            dS0[(((int64_t)n * Nv + h) * DK + m) * DV + nb * 16 + j] = dS[m][j];
-        }
-    }
-}
-
-// ------------------------------------------------------------ per-chunk gradients
 constexpr int kStageK = 16;                     // K-tile of the staged products
 
 // Staged product: out(i, j) = sum over k < K of a(i, k) b(k, j) for i < M,
@@ -337,6 +143,209 @@ __device__ __forceinline__ void gemm_lds(int K, float* As, float* Bs, FA&& a, FB
     }
 }
 
+// ------------------------------------------------------------ preparation
+// One workgroup per (chunk, value head): the forward intermediates in natural
+// row-major layouts (the chunk's entering state h [dk][dv], V_new and W by
+// token row), the score block P = (Q K^T) (.) D [C][C] (zero above the
+// diagonal and past the chunk end), and the two parts of the reverse state
+// pass that do not depend on the state gradient:
+//   X  = scale P^T dO                                   (into the dV_new buffer)
+//   Y' = Q^T diag(scale exp(G)) dO - W^T X  [dk][dv]    (into the dS buffer)
+// so that the serial pass only forms Z = diag(exp(G_last - G)) K dS,
+// dV_new = X + Z and dS <- exp(G_last) dS + Y' - W^T Z.
+template <typename T, int DK, int DV, int C>
+__global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ q, const T* __restrict__ k,
+                                                   const float* __restrict__ G, const float* __restrict__ Hf,
+                                                   const float* __restrict__ VNf, const float* __restrict__ Wf,
+                                                   const void* __restrict__ d_o, int do_f32, float scale,
+                                                   const int32_t* __restrict__ chunk_start,
+                                                   const int32_t* __restrict__ chunk_len, int32_t Nk, int32_t Nv,
+                                                   float* __restrict__ Hn, float* __restrict__ Vn,
+                                                   float* __restrict__ Wn, float* __restrict__ P,
+                                                   float* __restrict__ X, float* __restrict__ Yp) {
+    constexpr int NKP = DK / 32, NNB = DV / 16, NTB = C / 16, NTP = C < 32 ? 1 : C / 32;
+    constexpr int NMAX = (DK > DV ? DK : DV) > C ? (DK > DV ? DK : DV) : C;
+    __shared__ float Pm[C * C];
+    __shared__ float As[(DK > C ? DK : C) * (kStageK + 1)];
+    __shared__ __attribute__((aligned(16))) float Bs[kStageK * (NMAX + 4)];
+    __shared__ float gs[C], se[C];
+    const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    const int kh = h / (Nv / Nk);
+    const int64_t s = chunk_start[c];
+    const int L = chunk_len[c];
+    if (L <= 0) return;
+    if (tid < C) {
+        gs[tid] = tid < L ? G[(s + tid) * Nv + h] : 0.f;
+        se[tid] = tid < L ? scale * __expf(gs[tid]) : 0.f;
+    }
+    const int64_t ch = (int64_t)c * Nv + h;
+    for (int idx = tid; idx < DK * DV; idx += 256) {
+        const int i = idx / DV, j = idx % DV;
+        Hn[ch * DK * DV + idx] = Hf[((ch * NNB + j / 16) * NKP + i / 32) * 512 + pair_off(j % 16, i % 32)];
+    }
+    for (int idx = tid; idx < L * DV; idx += 256) {
+        const int p = idx / DV, j = idx % DV;
+        Vn[((s + p) * Nv + h) * DV + j] = VNf[((ch * NNB + j / 16) * NTP + p / 32) * 512 + pair_off(j % 16, p % 32)];
+    }
+    for (int idx = tid; idx < L * DK; idx += 256) {
+        const int p = idx / DK, i = idx % DK;
+        Wn[((s + p) * Nv + h) * DK + i] = Wf[((ch * NTB + p / 16) * NKP + i / 32) * 512 + pair_off(p % 16, i % 32)];
+    }
+    auto Qg = [&](int i, int m) { return i < L ? to_f(q[((s + i) * Nk + kh) * DK + m]) : 0.f; };
+    auto Kg = [&](int i, int m) { return i < L ? to_f(k[((s + i) * Nk + kh) * DK + m]) : 0.f; };
+    auto dOg = [&](int i, int j) { return i < L ? load_any(d_o, ((s + i) * Nv + h) * DV + j, do_f32) : 0.f; };
+    float* Pc = P + ch * C * C;
+    gemm_lds<C, C, true, false>(DK, As, Bs, Qg, [&](int kk, int j) { return Kg(j, kk); },
+        [&](int i, int j, float x) {
+            const float pv = (i < L && j <= i) ? x * __expf(gs[i] - gs[j]) : 0.f;
+            Pm[i * C + j] = pv;
+            Pc[i * C + j] = pv;
+        });
+    gemm_lds<C, DV, false, true>(C, As, Bs, [&](int i, int t) { return Pm[t * C + i]; }, dOg,
+                                 [&](int i, int j, float x) { if (i < L) X[((s + i) * Nv + h) * DV + j] = scale * x; });
+    gemm_lds<DK, DV, false, true>(2 * C, As, Bs,
+        [&](int m, int kk) {
+            return kk < C ? Qg(kk, m) : (kk - C < L ? -Wn[((s + kk - C) * Nv + h) * DK + m] : 0.f);
+        },
+        [&](int kk, int j) {
+            return kk < C ? se[kk] * dOg(kk, j) : (kk - C < L ? X[((s + kk - C) * Nv + h) * DV + j] : 0.f);
+        },
+        [&](int m, int j, float x) { Yp[(ch * DK + m) * DV + j] = x; });
+}
+
+// ------------------------------------------------------------ reverse state pass
+// One workgroup per (sequence, value head, 16 columns of dv) walks the chunks
+// backwards with the 16-column slice of the state gradient dS in LDS (fp32).
+// Per chunk, with X and Y' from the preparation kernel:
+//   Z = diag(exp(G_last - G)) K dS;  dV_new = X + Z   (overwrites X)
+//   the chunk's outgoing-state gradient dS is stored (over Y', after reading it)
+//   dS <- exp(G_last) dS + Y' - W^T Z
+// After the first chunk, dS is the gradient with respect to the initial state.
+// The next chunk's operands (K and W rows, X, Y', G) are loaded into registers
+// with 16-byte loads while the current chunk is computed, and the barriers
+// wait for LDS traffic only, so the loads stay in flight.
+template <typename T, int DK, int DV, int C>
+__global__ __launch_bounds__(256) void k_bwd_state(const T* __restrict__ k, const float* __restrict__ G,
+                                                    const float* __restrict__ Wn, const float* __restrict__ dST,
+                                                    const int32_t* __restrict__ chunk_start,
+                                                    const int32_t* __restrict__ chunk_len,
+                                                    const int32_t* __restrict__ seq_first, int32_t Nk, int32_t Nv,
+                                                    float* __restrict__ dSY, float* __restrict__ dVX,
+                                                    float* __restrict__ dS0) {
+    typedef typename Vec<T>::v8 v8;
+    constexpr int KP = DK + 1;
+    constexpr int PER = DK * 16 / 256;          // dS elements per thread
+    constexpr int NSEG = C * DK / 8;            // 8-element row pieces of K and W
+    constexpr int NK8 = (NSEG + 255) / 256;
+    constexpr int NZ = (C * 16 + 255) / 256;    // Z elements per thread
+    __shared__ float dS[DK][16];
+    __shared__ float Ks[C][KP], Ws[C][KP];
+    __shared__ float Zt[C][16];
+    __shared__ float gs[C];
+    const int n = blockIdx.x, h = blockIdx.y, nb = blockIdx.z, tid = threadIdx.x;
+    const int kh = h / (Nv / Nk);
+    for (int idx = tid; idx < DK * 16; idx += 256) {
+        const int m = idx / 16, j = idx % 16;
+        dS[m][j] = dST ? dST[(((int64_t)n * Nv + h) * DK + m) * DV + nb * 16 + j] : 0.f;
+    }
+    v8 kr[NK8];
+    f32x4 wr[2 * NK8];
+    float xr[NZ], yr[PER], gr = 0.f;
+    auto fetch = [&](int c) {
+        const int64_t s = chunk_start[c];
+        const int L = chunk_len[c];
+#pragma unroll
+        for (int e = 0; e < NK8; ++e) {
+            const int idx = tid + 256 * e, i = idx / (DK / 8), seg = idx % (DK / 8);
+            const bool ok = idx < NSEG && i < L;
+            const float* wp = Wn + ((s + i) * Nv + h) * DK + seg * 8;
+            kr[e] = ok ? *reinterpret_cast<const v8*>(k + ((s + i) * Nk + kh) * DK + seg * 8) : zero_pair<T>();
+            wr[2 * e] = ok ? *reinterpret_cast<const f32x4*>(wp) : f32x4{0.f, 0.f, 0.f, 0.f};
+            wr[2 * e + 1] = ok ? *reinterpret_cast<const f32x4*>(wp + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int e = 0; e < NZ; ++e) {
+            const int idx = tid + 256 * e, i = idx / 16, j = idx % 16;
+            xr[e] = (idx < C * 16 && i < L) ? dVX[((s + i) * Nv + h) * DV + nb * 16 + j] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int idx = tid + 256 * e, m = idx / 16, j = idx % 16;
+            yr[e] = dSY[(((int64_t)c * Nv + h) * DK + m) * DV + nb * 16 + j];
+        }
+        gr = (tid < C && tid < L) ? G[(s + tid) * Nv + h] : 0.f;
+    };
+    auto commit = [&]() {                          // K and W rows -> LDS
+#pragma unroll
+        for (int e = 0; e < NK8; ++e) {
+            const int idx = tid + 256 * e, i = idx / (DK / 8), seg = idx % (DK / 8);
+            if (idx < NSEG) {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    Ks[i][seg * 8 + t] = to_f(kr[e][t]);
+                    Ws[i][seg * 8 + t] = wr[2 * e + t / 4][t % 4];
+                }
+            }
+        }
+        if (tid < C) gs[tid] = gr;
+    };
+    const int c0 = seq_first[n], c1 = seq_first[n + 1];
+    if (c1 > c0) fetch(c1 - 1);
+    for (int c = c1 - 1; c >= c0; --c) {
+        const int64_t s = chunk_start[c];
+        const int L = chunk_len[c];
+        lds_barrier();                                // the previous chunk's readers are done
+        commit();
+        float x[NZ], y[PER];
+#pragma unroll
+        for (int e = 0; e < NZ; ++e) x[e] = xr[e];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) y[e] = yr[e];
+        lds_barrier();
+        if (c > c0) fetch(c - 1);                     // in flight while this chunk is computed
+        const float gL = gs[L - 1];
+        // Z = diag(exp(G_last - G)) K dS; dV_new = X + Z
+#pragma unroll
+        for (int e = 0; e < NZ; ++e) {
+            const int idx = tid + 256 * e, i = idx / 16, j = idx % 16;
+            if (idx < C * 16) {
+                float a = 0.f;
+#pragma unroll 8
+                for (int m = 0; m < DK; ++m) a += Ks[i][m] * dS[m][j];
+                const float z = i < L ? __expf(gL - gs[i]) * a : 0.f;
+                Zt[i][j] = z;
+                if (i < L) dVX[((s + i) * Nv + h) * DV + nb * 16 + j] = x[e] + z;
+            }
+        }
+        lds_barrier();
+        // the outgoing-state gradient of this chunk, then dS <- exp(G_last) dS + Y' - W^T Z
+        const float eL = __expf(gL);
+        float nw[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int idx = tid + 256 * e, m = idx / 16, j = idx % 16;
+            dSY[(((int64_t)c * Nv + h) * DK + m) * DV + nb * 16 + j] = dS[m][j];
+            float acc = 0.f;
+            for (int i = 0; i < L; ++i) acc += Ws[i][m] * Zt[i][j];
+            nw[e] = eL * dS[m][j] + y[e] - acc;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int idx = tid + 256 * e;
+            dS[idx / 16][idx % 16] = nw[e];
+        }
+    }
+    lds_barrier();
+    if (dS0) {
+        for (int idx = tid; idx < DK * 16; idx += 256) {
+            const int m = idx / 16, j = idx % 16;
+            dS0[(((int64_t)n * Nv + h) * DK + m) * DV + nb * 16 + j] = dS[m][j];
+        }
+    }
+}
+
+// ------------------------------------------------------------ per-chunk gradients
 // One workgroup per (chunk, value head). Four C x C matrices sit in LDS (A;
 // dM = dP (.) D; dA, then F, then F (.) D; A^T dA, then K K^T) with the
 // staging tiles of the products, about 79 KB for C = 64, so that two
@@ -546,14 +555,14 @@ hipError_t launch_bwd(const BackwardArgs& b) {
     const int32_t NT = a.nt;
     if (NT > 0) {
         k_bwd_prep<T, DK, DV, C><<<dim3(NT, a.Nv), 256, 0, st>>>(
-            (const T*)a.q, (const T*)a.k, a.G, (const float*)a.H, (const float*)a.VN, (const float*)a.W,
-            a.chunk_start, a.chunk_len, a.Nk, a.Nv, b.Hn, b.Vn, b.Wn, b.P);
+            (const T*)a.q, (const T*)a.k, a.G, (const float*)a.H, (const float*)a.VN, (const float*)a.W, b.d_o,
+            b.do_f32, a.scale, a.chunk_start, a.chunk_len, a.Nk, a.Nv, b.Hn, b.Vn, b.Wn, b.P, b.dVn, b.dSout);
     }
     mark(2);
     if (a.N > 0) {
         k_bwd_state<T, DK, DV, C><<<dim3(a.N, a.Nv, DV / 16), 256, 0, st>>>(
-            (const T*)a.q, (const T*)a.k, a.G, b.P, b.Wn, b.d_o, b.do_f32, b.dST, a.chunk_start, a.chunk_len,
-            a.seq_first, a.Nk, a.Nv, a.scale, b.dSout, b.dVn, b.dS0);
+            (const T*)a.k, a.G, b.Wn, b.dST, a.chunk_start, a.chunk_len, a.seq_first, a.Nk, a.Nv, b.dSout, b.dVn,
+            b.dS0);
     }
     mark(3);
     if (NT > 0) {
