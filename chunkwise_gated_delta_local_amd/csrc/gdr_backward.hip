@@ -81,17 +81,20 @@ __device__ __forceinline__ float load_any(const void* p, int64_t idx, int is_f32
 constexpr int kStageK = 16;                     // K-tile of the staged products
 
 // Staged product: out(i, j) = sum over k < K of a(i, k) b(k, j) for i < M,
-// j < N (K a multiple of 16). Tiles of 16 columns of a and 16 rows of b are
-// first copied to LDS by all threads, consecutive threads taking consecutive
+// j < N (K a multiple of 16). Tiles of 16 columns of a and 16 rows of b go
+// through LDS: each thread loads its share of the next tile into registers
+// while the current one is multiplied, consecutive threads taking consecutive
 // addresses of the operand (AK: a(i, k) is contiguous in k, else in i; BJ:
-// b(k, j) is contiguous in j, else in k). Each thread then accumulates its
-// 4 x 4 output blocks from LDS: the a values of a block row are shared by many
-// lanes (broadcast reads) and the b values of 4 consecutive columns are one
-// 16-byte read. As holds M x 17 floats, Bs 16 x (N + 4).
+// b(k, j) is contiguous in j, else in k). Each thread accumulates its 4 x 4
+// output blocks from LDS: the a values of a block row are shared by many lanes
+// (broadcast reads) and the b values of 4 consecutive columns are one 16-byte
+// read. As holds M x 17 floats, Bs 16 x (N + 4). The product starts with a
+// barrier, so its operands may be LDS or memory written by the phase before.
 template <int M, int N, bool AK, bool BJ, typename FA, typename FB, typename FS>
 __device__ __forceinline__ void gemm_lds(int K, float* As, float* Bs, FA&& a, FB&& b, FS&& store) {
     constexpr int KT = kStageK, AP = KT + 1, BP = N + 4;
     constexpr int BN = N / 4, NBLK = (M / 4) * BN, PER = (NBLK + 255) / 256;
+    constexpr int NA = (M * KT + 255) / 256, NB = (KT * N + 255) / 256;
     static_assert(M % 4 == 0 && N % 4 == 0, "4 x 4 blocks");
     const int tid = threadIdx.x;
     float acc[PER][4][4];
@@ -101,23 +104,45 @@ __device__ __forceinline__ void gemm_lds(int K, float* As, float* Bs, FA&& a, FB
         for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int c = 0; c < 4; ++c) acc[p][r][c] = 0.f;
+    float ra[NA], rb[NB];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int e = 0; e < NA; ++e) {
+            const int idx = tid + 256 * e;
+            const int i = AK ? idx / KT : idx % M, kk = AK ? idx % KT : idx / M;
+            ra[e] = (M * KT % 256 == 0 || idx < M * KT) ? a(i, k0 + kk) : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < NB; ++e) {
+            const int idx = tid + 256 * e;
+            const int kk = BJ ? idx / N : idx % KT, j = BJ ? idx % N : idx / KT;
+            rb[e] = (KT * N % 256 == 0 || idx < KT * N) ? b(k0 + kk, j) : 0.f;
+        }
+    };
+    __syncthreads();                                   // operands written by the previous phase are visible
+    fetch(0);
     for (int k0 = 0; k0 < K; k0 += KT) {
         __syncthreads();                               // the previous tile is consumed
-        for (int idx = tid; idx < M * KT; idx += 256) {
+#pragma unroll
+        for (int e = 0; e < NA; ++e) {
+            const int idx = tid + 256 * e;
             const int i = AK ? idx / KT : idx % M, kk = AK ? idx % KT : idx / M;
-            As[i * AP + kk] = a(i, k0 + kk);
+            if (M * KT % 256 == 0 || idx < M * KT) As[i * AP + kk] = ra[e];
         }
-        for (int idx = tid; idx < KT * N; idx += 256) {
+#pragma unroll
+        for (int e = 0; e < NB; ++e) {
+            const int idx = tid + 256 * e;
             const int kk = BJ ? idx / N : idx % KT, j = BJ ? idx % N : idx / KT;
-            Bs[kk * BP + j] = b(k0 + kk, j);
+            if (KT * N % 256 == 0 || idx < KT * N) Bs[kk * BP + j] = rb[e];
         }
         __syncthreads();
+        if (k0 + KT < K) fetch(k0 + KT);               // in flight during this tile's products
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int blk = tid + 256 * p;
             if (NBLK % 256 == 0 || blk < NBLK) {
                 const int i0 = (blk / BN) * 4, j0 = (blk % BN) * 4;
-#pragma unroll
+#pragma unroll 4
                 for (int kk = 0; kk < KT; ++kk) {
                     const f32x4 bv = *reinterpret_cast<const f32x4*>(&Bs[kk * BP + j0]);
 #pragma unroll
