@@ -240,9 +240,22 @@ gdr_status_t check_inputs(const gdr_problem_t* p, const void* q, const void* k, 
     return GDR_OK;
 }
 
-// Backward workspace: the five-kernel forward's regions, then the backward's own.
+// Segments of the backward's forward recompute: its state pass runs one
+// wavefront per (sequence, value head, 16 dv columns); the sequences are cut
+// into up to 2048 / (that many) segments (segment-parallel state passing), so
+// that the recompute's serial pass has about 2048 wavefronts.
+int32_t bwd_segments_per_seq(const gdr_problem_t* p) {
+    const int64_t w0 = (int64_t)p->num_seqs * p->num_v_heads * (p->head_dim_v / 16);
+    if (w0 <= 0 || w0 >= 1024) return 1;
+    return (int32_t)(2048 / w0);
+}
+
+// Backward workspace: the five-kernel forward's regions, then the backward's
+// own, then the recompute's segment region.
 struct BwdPlan {
-    size_t off_o, off_P, off_Hn, off_Vn, off_Wn, off_dSout, off_dVn, off_dWs, off_dqv, off_dkv, end;
+    size_t off_P, off_Hn, off_Vn, off_Wn, off_dSout, off_dVn, off_dWs, off_dqv, off_dkv, end;
+    SegPlan seg;
+    int64_t seg_bound;
 };
 
 BwdPlan make_bwd_plan(const gdr_problem_t* p, const Plan& pl) {
@@ -252,7 +265,6 @@ BwdPlan make_bwd_plan(const gdr_problem_t* p, const Plan& pl) {
     const size_t T = (size_t)(pl.Ttot > 0 ? pl.Ttot : 1);
     size_t off = align256(pl.reference);
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
-    bp.off_o = take(T * Nv * dv * 4);
     bp.off_P = take(cap * Nv * C * C * 4);
     bp.off_Hn = take(cap * Nv * dk * dv * 4);
     bp.off_Vn = take(T * Nv * dv * 4);
@@ -262,7 +274,10 @@ BwdPlan make_bwd_plan(const gdr_problem_t* p, const Plan& pl) {
     bp.off_dWs = take(T * Nv * dk * 4);
     bp.off_dqv = take(T * Nv * dk * 4);
     bp.off_dkv = take(T * Nv * dk * 4);
-    bp.end = off;
+    const int32_t per_seq = bwd_segments_per_seq(p);
+    bp.seg_bound = per_seq > 1 ? (int64_t)p->num_seqs * per_seq : 0;
+    bp.seg = make_seg_plan(p, off, bp.seg_bound);
+    bp.end = bp.seg_bound > 0 ? bp.seg.end : off;
     return bp;
 }
 
@@ -460,9 +475,29 @@ gdr_status_t gdr_chunk_bwd(const gdr_problem_t* p, const void* q, const void* k,
 
     char* w = static_cast<char*>(workspace);
     gdr::BackwardArgs b;
-    b.fwd = fill_args(p, pl, nt, q, k, v, g, beta, scale, initial_state, cu_dev, w + bp.off_o, nullptr, w,
-                      true, stream);
-    b.fwd.out_f32 = 1;                              // the recomputed output goes to an fp32 scratch
+    // the recompute needs the chunk states and V_new, not o
+    b.fwd = fill_args(p, pl, nt, q, k, v, g, beta, scale, initial_state, cu_dev, nullptr, nullptr, w, true,
+                      stream);
+    const int32_t per_seq = bwd_segments_per_seq(p);
+    if (per_seq > 1 && max_chunks > 1) {
+        const int64_t C = p->chunk_size;
+        const int64_t seg_chunks = (max_chunks + per_seq - 1) / per_seq;
+        int64_t nseg = 0;
+        for (int32_t n = 0; n < p->num_seqs; ++n) {
+            const int64_t len = cu_host ? (int64_t)cu_host[n + 1] - cu_host[n] : p->seq_len;
+            nseg += ((len + C - 1) / C + seg_chunks - 1) / seg_chunks;
+        }
+        if (nseg > p->num_seqs && nseg <= bp.seg_bound) {
+            const SegPlan sp = make_seg_plan(p, bp.seg.off_first, nseg);   // same start, nseg entries
+            b.fwd.nseg = (int32_t)nseg;
+            b.fwd.seg_chunks = (int32_t)seg_chunks;
+            b.fwd.seg_first = reinterpret_cast<int32_t*>(w + sp.off_first);
+            b.fwd.seq_seg = reinterpret_cast<int32_t*>(w + sp.off_seqseg);
+            b.fwd.Sloc = reinterpret_cast<float*>(w + sp.off_Sloc);
+            b.fwd.Mseg = reinterpret_cast<float*>(w + sp.off_M);
+            b.fwd.Sstart = reinterpret_cast<float*>(w + sp.off_Sstart);
+        }
+    }
     b.d_o = d_o;
     b.do_f32 = p->out_dtype == GDR_F32;
     b.dST = d_final_state;

@@ -1425,7 +1425,7 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
                                                                        (float*)a.H, (float*)a.VN, a.ST);
     }
     mark(5);
-    if (NT > 0 && !fused)
+    if (NT > 0 && !fused && a.o)
         k_output<T, DK, DV, C><<<dim3(NT, a.Nv), NTHR, 0, st>>>((const T*)a.q, (const T*)a.k, a.G, (const float*)a.H,
                                                            (const float*)a.VN, a.chunk_start, a.chunk_len, a.Nk, a.Nv,
                                                            a.scale, a.out_f32, a.o);

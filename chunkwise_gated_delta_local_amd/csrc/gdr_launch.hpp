@@ -20,7 +20,7 @@ struct LaunchArgs {
     const float* S0;           // NULL: zeros
     float scale;
     const int32_t* cu_dev;     // NULL: fixed length
-    void* o;
+    void* o;                   // NULL on the five-kernel path: no output kernel (the backward's recompute)
     float* ST;                 // NULL: not written
     // workspace regions
     int32_t *chunk_seq, *chunk_start, *chunk_len, *seq_first;
