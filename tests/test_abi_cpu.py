@@ -193,3 +193,30 @@ def test_segmented_rejects_before_launch(lib):
     assert lib.gdr_chunk_fwd_segmented(*args, ctypes.c_int32(1), None, ctypes.c_size_t(0), None, None) == 6
     serial_ws = api.workspace_size(p)           # enough for the serial pass, not for 1-chunk segments
     assert lib.gdr_chunk_fwd_segmented(*args, ctypes.c_int32(1), fake, ctypes.c_size_t(serial_ws), None, None) == 6
+
+
+def test_backward_rejects_before_launch(lib):
+    """gdr_chunk_bwd: missing gradient buffers, workspace or a misaligned
+    pointer come back as status codes, with no device work."""
+    from chunkwise_gated_delta_local_amd import api
+    if torch.cuda.is_available():
+        pytest.skip("passes placeholder addresses; host-logic test for machines without a GPU")
+    p = prob()
+    fake = ctypes.c_void_p(1 << 20)
+    base = [ctypes.byref(p), fake, fake, fake, None, fake, ctypes.c_float(1.0), None, None, None]
+    grads = [fake, None, fake, fake, fake, fake, None, None]       # d_o, dS_T, dq, dk, dv, dbeta, dg, dh0
+    big = ctypes.c_size_t(1 << 40)
+    assert lib.gdr_chunk_bwd(*base, *grads, None, ctypes.c_size_t(0), None, None) == 6
+    bad = list(grads)
+    bad[2] = None                                                   # dq missing
+    assert lib.gdr_chunk_bwd(*base, *bad, fake, big, None, None) == 1
+    bad = list(grads)
+    bad[0] = None                                                   # d_o missing
+    assert lib.gdr_chunk_bwd(*base, *bad, fake, big, None, None) == 1
+    bad = list(grads)
+    bad[4] = ctypes.c_void_p((1 << 20) + 4)                        # misaligned dv
+    assert lib.gdr_chunk_bwd(*base, *bad, fake, big, None, None) == 2
+    small = api.workspace_size(p)                                   # the forward's, not the backward's
+    n = ctypes.c_size_t(0)
+    assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0 and n.value > small
+    assert lib.gdr_chunk_bwd(*base, *grads, fake, ctypes.c_size_t(small), None, None) == 6

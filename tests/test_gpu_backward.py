@@ -108,3 +108,53 @@ def test_backward_without_final_state_gradient_and_fp32_do():
 def test_backward_every_head_dim_pair(dk, dv):
     w = synth.custom("bwd_dims", B=1, T=75, Nk=1, Nv=2, dk=dk, dv=dv, dtype="bf16", s0="randn")
     check("bwd_dims(%d,%d)" % (dk, dv), synth.generate(w, seed=440 + dk + dv), seed=6)
+
+
+def test_backward_long_sequence_d128():
+    """16 chunks of one sequence at dk = dv = 128 with GQA, against the oracle."""
+    w = synth.custom("bwd_long", B=1, T=1024, Nk=1, Nv=2, dk=128, dv=128, dtype="bf16", s0="randn", g_mean=6.0)
+    check("bwd_long_T1024", synth.generate(w, seed=450), seed=7)
+
+
+def test_backward_full_size_linearity():
+    """The long-context workload at full size (T = 65536, Nk = 16, Nv = 32,
+    dk = dv = 128, bf16) in the configuration the benchmark times. The oracle
+    cannot run at this size, so properties that hold at any size are checked:
+    every gradient is finite; the backward is linear in (dL/do, dL/dS_T), so
+    doubling both doubles dq, dk, dv and dh0 exactly (scaling by 2 is exact in
+    floating point and their sums run in a fixed order) and dbeta and dg to
+    fp32 rounding (their per-position sums are LDS atomics, whose order may
+    differ between runs); the gradients of a sum are the sum of the gradients
+    (to fp32 rounding)."""
+    w = synth.WORKLOADS[5]
+    inp = synth.generate(w, seed=5)
+    d = to_dev(inp)
+    rng = np.random.default_rng(12)
+    B, T = inp["q"].shape[:2]
+    do1 = torch.from_numpy(rng.standard_normal((B, T, w.Nv, w.dv)).astype(np.float32)).cuda()
+    do2 = torch.from_numpy(rng.standard_normal((B, T, w.Nv, w.dv)).astype(np.float32)).cuda()
+    dS1 = torch.from_numpy(rng.standard_normal((1, w.Nv, w.dk, w.dv)).astype(np.float32)).cuda()
+    dS2 = torch.from_numpy(rng.standard_normal((1, w.Nv, w.dk, w.dv)).astype(np.float32)).cuda()
+
+    def run(do, dS):
+        res = api.chunk_bwd(d["q"], d["k"], d["v"], d["beta"], do, g=d["g"], scale=inp["scale"],
+                            initial_state=d["S0"], d_final_state=dS)
+        torch.cuda.synchronize()
+        return res
+
+    r1 = run(do1, dS1)
+    r1x2 = run(2 * do1, 2 * dS1)
+    r2 = run(do2, dS2)
+    r12 = run(do1 + do2, dS1 + dS2)
+    for key in ("dq", "dk", "dv", "dbeta", "dg", "dh0"):
+        a = r1[key]
+        assert bool(torch.isfinite(a).all()), key
+        if key in ("dbeta", "dg"):
+            e2 = float((r1x2[key].double() - 2 * a.double()).abs().max() / (2 * a.double()).pow(2).mean().sqrt())
+            assert e2 < 1e-5, (key, e2)
+        else:
+            assert torch.equal(r1x2[key], 2 * a), key
+        ref = (a.double() + r2[key].double())
+        err = float((r12[key].double() - ref).abs().max() / ref.pow(2).mean().sqrt())
+        print("full-size %s: additivity max|d|/rms %.2e" % (key, err), flush=True)
+        assert err < 1e-4, (key, err)
