@@ -97,45 +97,40 @@ __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict_
 
 // ============================================================ K1: gate prefix sums
 // G[t, h] = sum of g over the tokens of t's chunk up to and including t, in
-// fp32 and in token order (ChunkGatedDeltaRule page, section 3, "G_i";
-// GLA notes, forward step 1, chunk-local cumulative log gate). One thread per
-// (chunk, head); neighbouring threads take neighbouring heads so every row
-// access is coalesced. g == NULL writes zeros (ungated rule).
+// fp32 (ChunkGatedDeltaRule page, section 3, "G_i"; GLA notes, forward step 1,
+// chunk-local cumulative log gate). One workgroup per (chunk, 256 / C heads):
+// lane i of each C-lane group takes position i of one head, and the prefix sum
+// runs across the group with shuffles (log2 C steps, always in the same
+// order). g == NULL writes zeros (ungated rule).
 // When R is given, the two decay factors the fused state pass needs are
 // written per token too:
 //   R.x = exp(G_t)                      decay from the chunk start
 //   R.y = exp(G_last - G_t)             decay to the chunk end
-// chunk-major, [chunk][head][64 positions] with zeros past the chunk end, so
+// chunk-major, [chunk][head][C positions] with zeros past the chunk end, so
 // that the sequential pass reads the factors of one (chunk, head) as one
-// contiguous 512-byte block.
+// contiguous block.
 template <int C>
 __global__ __launch_bounds__(256) void k_gate_cumsum(const float* __restrict__ g,
                                                       const int32_t* __restrict__ chunk_start,
                                                       const int32_t* __restrict__ chunk_len,
                                                       int32_t NT, int32_t Nv, float* __restrict__ G,
                                                       f32x2* __restrict__ R) {
-    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (p >= (int64_t)NT * Nv) return;
-    const int32_t c = (int32_t)(p / Nv), h = (int32_t)(p % Nv);
+    constexpr int HB = 256 / C;                   // heads per workgroup
+    const int c = blockIdx.x;
+    const int i = threadIdx.x % C, h = blockIdx.y * HB + threadIdx.x / C;
+    const bool on = h < Nv;
     const int64_t s = chunk_start[c];
-    const int32_t L = chunk_len[c];
-    float x[C];
+    const int L = chunk_len[c];
+    float x = (g && on && i < L) ? g[(s + i) * Nv + h] : 0.f;
 #pragma unroll
-    for (int32_t i = 0; i < C; ++i) x[i] = (g && i < L) ? g[(s + i) * Nv + h] : 0.f;   // independent loads
-    float acc = 0.f;
-#pragma unroll
-    for (int32_t i = 0; i < C; ++i) {
-        acc += x[i];
-        x[i] = acc;                              // x now holds G (positions past the end repeat G_last)
-        if (i < L) G[(s + i) * Nv + h] = acc;
+    for (int off = 1; off < C; off <<= 1) {       // inclusive scan over the group (every lane takes part)
+        const float y = __shfl_up(x, off, C);
+        if (i >= off) x += y;
     }
-    if (R) {
-        const float g_last = L > 0 ? x[L - 1] : 0.f;
-        f32x2* Rc = R + ((int64_t)c * Nv + h) * C;
-#pragma unroll
-        for (int32_t i = 0; i < C; ++i)
-            Rc[i] = i < L ? f32x2{__expf(x[i]), __expf(g_last - x[i])} : f32x2{0.f, 0.f};
-    }
+    const float g_last = __shfl(x, L > 0 ? L - 1 : 0, C);
+    if (on && i < L) G[(s + i) * Nv + h] = x;
+    if (R && on)
+        R[((int64_t)c * Nv + h) * C + i] = i < L ? f32x2{__expf(x), __expf(g_last - x)} : f32x2{0.f, 0.f};
 }
 
 // ============================================================ K2: A-build + solve
@@ -1361,9 +1356,8 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
         k_segment_table<<<1, 1024, 0, st>>>(a.seq_first, a.N, a.seg_chunks, a.nseg, a.seg_first, a.seq_seg);
     mark(1);
     if (NT > 0) {
-        const int64_t units = (int64_t)NT * a.Nv;
-        k_gate_cumsum<C><<<(unsigned)((units + 255) / 256), 256, 0, st>>>(a.g, a.chunk_start, a.chunk_len, NT, a.Nv,
-                                                                           a.G, fused ? (f32x2*)a.R : nullptr);
+        k_gate_cumsum<C><<<dim3(NT, (a.Nv + 256 / C - 1) / (256 / C)), 256, 0, st>>>(
+            a.g, a.chunk_start, a.chunk_len, NT, a.Nv, a.G, fused ? (f32x2*)a.R : nullptr);
     }
     mark(2);
     if (NT > 0)
