@@ -118,3 +118,18 @@ def test_segments_longer_than_every_sequence_run_serial():
     o_a, S_a = run(inp, 5)
     o_s, S_s = run_serial(inp)
     assert torch.equal(o_a, o_s) and torch.equal(S_a, S_s)
+
+
+def test_full_size_varlen_segmented_matches_serial():
+    """64 variable-length sequences (1 to 8192 tokens), Nk = 16, Nv = 32,
+    dk = dv = 128, bf16, from a random state, at full size: the automatic
+    choice keeps the serial pass (same bits); forced 16-chunk segments give
+    the serial result to fp32 rounding."""
+    inp = synth.generate(synth.WORKLOADS[4], seed=4)
+    o_s, S_s = run_serial(inp)
+    o_a, S_a = run(inp, 0)
+    assert torch.equal(o_a, o_s) and torch.equal(S_a, S_s)
+    o_f, S_f = run(inp, 16)
+    eo, es = rel_err(f64(o_f), f64(o_s)), rel_err(f64(S_f), f64(S_s))
+    print("cfg4 segmented (16 chunks) vs serial: o %.2e S_T %.2e" % (eo, es), flush=True)
+    assert eo <= 1e-4 and es <= 1e-4
