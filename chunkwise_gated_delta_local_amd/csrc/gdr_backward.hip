@@ -329,30 +329,50 @@ __global__ __launch_bounds__(256) void k_bwd_state(const T* __restrict__ k, cons
         lds_barrier();
         if (c > c0) fetch(c - 1);                     // in flight while this chunk is computed
         const float gL = gs[L - 1];
-        // Z = diag(exp(G_last - G)) K dS; dV_new = X + Z
+        // Z = diag(exp(G_last - G)) K dS; dV_new = X + Z. A thread's outputs share
+        // their column j (rows i0 + 16 e), so dS[m][j] is read once per m.
+        const int j0 = tid % 16, i0 = tid / 16;
+        {
+            float a[NZ];
 #pragma unroll
-        for (int e = 0; e < NZ; ++e) {
-            const int idx = tid + 256 * e, i = idx / 16, j = idx % 16;
-            if (idx < C * 16) {
-                float a = 0.f;
-#pragma unroll 8
-                for (int m = 0; m < DK; ++m) a += Ks[i][m] * dS[m][j];
-                const float z = i < L ? __expf(gL - gs[i]) * a : 0.f;
-                Zt[i][j] = z;
-                if (i < L) dVX[((s + i) * Nv + h) * DV + nb * 16 + j] = x[e] + z;
+            for (int e = 0; e < NZ; ++e) a[e] = 0.f;
+#pragma unroll 4
+            for (int m = 0; m < DK; ++m) {
+                const float d = dS[m][j0];
+#pragma unroll
+                for (int e = 0; e < NZ; ++e)
+                    if (NZ * 256 == C * 16 || i0 + 16 * e < C) a[e] += Ks[i0 + 16 * e][m] * d;
+            }
+#pragma unroll
+            for (int e = 0; e < NZ; ++e) {
+                const int i = i0 + 16 * e;
+                if (i < C) {
+                    const float z = i < L ? __expf(gL - gs[i]) * a[e] : 0.f;
+                    Zt[i][j0] = z;
+                    if (i < L) dVX[((s + i) * Nv + h) * DV + nb * 16 + j0] = x[e] + z;
+                }
             }
         }
         lds_barrier();
-        // the outgoing-state gradient of this chunk, then dS <- exp(G_last) dS + Y' - W^T Z
+        // the outgoing-state gradient of this chunk, then dS <- exp(G_last) dS + Y' - W^T Z;
+        // a thread's outputs share their column j (rows i0 + 16 e), so Z[i][j] is read once per i
         const float eL = __expf(gL);
-        float nw[PER];
+        float nw[PER], acc[PER];
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-            const int idx = tid + 256 * e, m = idx / 16, j = idx % 16;
-            dSY[(((int64_t)c * Nv + h) * DK + m) * DV + nb * 16 + j] = dS[m][j];
-            float acc = 0.f;
-            for (int i = 0; i < L; ++i) acc += Ws[i][m] * Zt[i][j];
-            nw[e] = eL * dS[m][j] + y[e] - acc;
+            const int m = i0 + 16 * e;
+            dSY[(((int64_t)c * Nv + h) * DK + m) * DV + nb * 16 + j0] = dS[m][j0];
+            acc[e] = 0.f;
+        }
+        for (int i = 0; i < L; ++i) {
+            const float z = Zt[i][j0];
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] += Ws[i][i0 + 16 * e] * z;
+        }
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int m = i0 + 16 * e;
+            nw[e] = eL * dS[m][j0] + y[e] - acc[e];
         }
         lds_barrier();
 #pragma unroll
