@@ -81,18 +81,18 @@ __device__ __forceinline__ float load_any(const void* p, int64_t idx, int is_f32
 constexpr int kStageK = 16;                     // K-tile of the staged products
 
 // Staged product: out(i, j) = sum over k < K of a(i, k) b(k, j) for i < M,
-// j < N (K a multiple of 16). Tiles of 16 columns of a and 16 rows of b go
+// j < N (K a multiple of KT, 16 or 32). Tiles of KT columns of a and KT rows of b go
 // through LDS: each thread loads its share of the next tile into registers
 // while the current one is multiplied, consecutive threads taking consecutive
 // addresses of the operand (AK: a(i, k) is contiguous in k, else in i; BJ:
 // b(k, j) is contiguous in j, else in k). Each thread accumulates its 4 x 4
 // output blocks from LDS: the a values of a block row are shared by many lanes
 // (broadcast reads) and the b values of 4 consecutive columns are one 16-byte
-// read. As holds M x 17 floats, Bs 16 x (N + 4). The product starts with a
-// barrier, so its operands may be LDS or memory written by the phase before.
-template <int M, int N, bool AK, bool BJ, typename FA, typename FB, typename FS>
+// read. As holds M x (KT + 1) floats, Bs KT x (N + 4). The product starts with
+// a barrier, so its operands may be LDS or memory written by the phase before.
+template <int M, int N, bool AK, bool BJ, int KT = kStageK, typename FA, typename FB, typename FS>
 __device__ __forceinline__ void gemm_lds(int K, float* As, float* Bs, FA&& a, FB&& b, FS&& store) {
-    constexpr int KT = kStageK, AP = KT + 1, BP = N + 4;
+    constexpr int AP = KT + 1, BP = N + 4;
     constexpr int BN = N / 4, NBLK = (M / 4) * BN, PER = (NBLK + 255) / 256;
     constexpr int NA = (M * KT + 255) / 256, NB = (KT * N + 255) / 256;
     static_assert(M % 4 == 0 && N % 4 == 0, "4 x 4 blocks");
@@ -190,9 +190,10 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ q, const
                                                    float* __restrict__ X, float* __restrict__ Yp) {
     constexpr int NKP = DK / 32, NNB = DV / 16, NTB = C / 16, NTP = C < 32 ? 1 : C / 32;
     constexpr int NMAX = (DK > DV ? DK : DV) > C ? (DK > DV ? DK : DV) : C;
+    constexpr int KT = 32;                       // deeper tiles: this kernel's LDS has room
     __shared__ float Pm[C * C];
-    __shared__ float As[(DK > C ? DK : C) * (kStageK + 1)];
-    __shared__ __attribute__((aligned(16))) float Bs[kStageK * (NMAX + 4)];
+    __shared__ float As[(DK > C ? DK : C) * (KT + 1)];
+    __shared__ __attribute__((aligned(16))) float Bs[KT * (NMAX + 4)];
     __shared__ float gs[C], se[C];
     const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     const int kh = h / (Nv / Nk);
@@ -220,15 +221,15 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ q, const
     auto Kg = [&](int i, int m) { return i < L ? to_f(k[((s + i) * Nk + kh) * DK + m]) : 0.f; };
     auto dOg = [&](int i, int j) { return i < L ? load_any(d_o, ((s + i) * Nv + h) * DV + j, do_f32) : 0.f; };
     float* Pc = P + ch * C * C;
-    gemm_lds<C, C, true, false>(DK, As, Bs, Qg, [&](int kk, int j) { return Kg(j, kk); },
+    gemm_lds<C, C, true, false, KT>(DK, As, Bs, Qg, [&](int kk, int j) { return Kg(j, kk); },
         [&](int i, int j, float x) {
             const float pv = (i < L && j <= i) ? x * __expf(gs[i] - gs[j]) : 0.f;
             Pm[i * C + j] = pv;
             Pc[i * C + j] = pv;
         });
-    gemm_lds<C, DV, false, true>(C, As, Bs, [&](int i, int t) { return Pm[t * C + i]; }, dOg,
+    gemm_lds<C, DV, false, true, (C % 32 == 0 ? KT : 16)>(C, As, Bs, [&](int i, int t) { return Pm[t * C + i]; }, dOg,
                                  [&](int i, int j, float x) { if (i < L) X[((s + i) * Nv + h) * DV + j] = scale * x; });
-    gemm_lds<DK, DV, false, true>(2 * C, As, Bs,
+    gemm_lds<DK, DV, false, true, KT>(2 * C, As, Bs,
         [&](int m, int kk) {
             return kk < C ? Qg(kk, m) : (kk - C < L ? -Wn[((s + kk - C) * Nv + h) * DK + m] : 0.f);
         },
