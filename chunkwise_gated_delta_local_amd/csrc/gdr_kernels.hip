@@ -755,11 +755,15 @@ __global__ __launch_bounds__(256) void k_output(const T* __restrict__ q, const T
 }
 
 // ============================================================ K4 + K5 fused: state pass with output
-// Modes of the fused pass: kFull (state and output, from S0); kStateOnly (the
-// state alone: end states, no output work); kTransition (state alone from
-// S = I with V read as zero: the map a run of chunks applies to its entering
-// state). The last two serve segment-parallel state passing (below).
-constexpr int kFull = 0, kStateOnly = 1, kTransition = 2;
+// Modes of the fused pass: kFull (state and output, from S0; twelve
+// wavefronts) and kSegment (eight wavefronts: state and copy roles only, no
+// output work). A kSegment workgroup with blockIdx.z < dv/16 forms the end
+// state of its run of chunks from a zero state; one with a larger blockIdx.z
+// forms the map a run of chunks applies to its entering state: the end state
+// from S = I (dk columns, written to ST2) with V read as zero. Both serve
+// segment-parallel state passing (below) and run in one launch, two
+// workgroups to a compute unit.
+constexpr int kFull = 0, kSegment = 1;
 // Production path for bf16 inputs. One workgroup of twelve wavefronts per
 // (sequence, value head, 16 columns of dv) walks the sequence's chunks in
 // order with the state slice S (dk x 16, fp32) on chip, and produces the output
@@ -802,14 +806,14 @@ constexpr int kFull = 0, kStateOnly = 1, kTransition = 2;
 // the stacked-accumulator order of gdr_device.hpp. The state is written to LDS
 // in the first order by the wave that updates it.
 template <int DK, int DV, int MODE>
-__global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q, const bf16* __restrict__ k,
+__global__ __launch_bounds__(MODE == kFull ? 768 : 512) void k_state_output(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                        const bf16* __restrict__ v, const f32x2* __restrict__ R, const bf16* __restrict__ Tf,
                                                        const bf16* __restrict__ Pf, const float* __restrict__ S0,
                                                        const int32_t* __restrict__ chunk_start,
                                                        const int32_t* __restrict__ chunk_len,
                                                        const int32_t* __restrict__ seq_first, int32_t Nk, int32_t Nv,
                                                        float scale, int out_f32, void* __restrict__ o,
-                                                       float* __restrict__ ST) {
+                                                       float* __restrict__ ST, float* __restrict__ ST2) {
     typedef bf16 T;
     typedef Vec<T>::v8 v8;
     typedef Vec<T>::v4 v4;
@@ -836,12 +840,17 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
     __shared__ __attribute__((aligned(16))) T Vtb[2][2][FRAG];
     __shared__ __attribute__((aligned(16))) f32x4 QSx[4][64];
 
-    const int n = blockIdx.x, h = blockIdx.y, nb = blockIdx.z;
+    const int n = blockIdx.x, h = blockIdx.y;
     const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave index, uniform
     const int lane = tid & 63, r = lane & 15, qd = lane >> 4;
     const int kh = h / (Nv / Nk);
     constexpr bool want_o = MODE == kFull;       // else state only: no Q, score or output work
+    constexpr int kCopy0 = want_o ? 8 : 4;       // first copy wave
+    const bool trans = MODE != kFull && (int)blockIdx.z >= DV / 16;   // transition workgroup
+    const int nb = trans ? (int)blockIdx.z - DV / 16 : (int)blockIdx.z;
+    const int NC = trans ? DK : DV;              // columns of the state written
+    float* const STo = trans ? ST2 : ST;
     const int c0 = seq_first[n], c1 = seq_first[n + 1];
     // The chunks of a sequence are consecutive 64-token pieces of its token
     // range, so their start and length follow from the range.
@@ -877,7 +886,7 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
                           *reinterpret_cast<const v4*>(&buf[tp][1][256 + lane * 4]));
         return sp;
     };
-    const int64_t sbase = ((int64_t)n * Nv + h) * DK * DV;
+    const int64_t sbase = ((int64_t)n * Nv + h) * DK * NC;
     // split pair fragment p (hi, lo) of a six-pair set (T or the score block) of
     // chunk c, straight into registers (16 bytes per lane per half)
     auto load_pair_set = [&](const T* base, int c, int p) {
@@ -903,8 +912,8 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
             for (int j = 0; j < 4; ++j) {
                 const int row = db * 16 + 4 * qd + j, col = nb * 16 + r;
                 S[t][j] = db >= NDB ? 0.f
-                          : MODE == kTransition ? (row == col ? 1.f : 0.f)
-                          : S0 ? S0[sbase + (int64_t)row * DV + col] : 0.f;
+                          : trans ? (row == col ? 1.f : 0.f)
+                          : S0 ? S0[sbase + (int64_t)row * NC + col] : 0.f;
             }
         }
         // S tile db (rows 16 db + 4 qd + j of this lane's column r) -> B fragments of
@@ -1049,14 +1058,14 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
                 lds_barrier();                                                    // barrier 3
             }
         }
-        if (ST) {
+        if (STo) {
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
                 const int db = w * TPW + t;
                 if (db < NDB) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        ST[sbase + (int64_t)(db * 16 + 4 * qd + j) * DV + nb * 16 + r] = S[t][j];
+                        STo[sbase + (int64_t)(db * 16 + 4 * qd + j) * NC + nb * 16 + r] = S[t][j];
                 }
             }
         }
@@ -1064,7 +1073,7 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
     }
 
     if (c0 >= c1) return;
-    if (wv >= 8) {
+    if (wv >= kCopy0) {
         // ======================================================== copy waves
         // Wave 8+w moves its share of each chunk's tiles into LDS. A chunk's
         // early list (K and Q blocks: read only in phase A) is issued during
@@ -1074,7 +1083,7 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
         // straight into the state waves' registers.) Before the last barrier of step c the wave waits for everything
         // but the early list of chunk c+2, which may still be in flight (vector
         // memory operations complete in order).
-        const int w = wv - 8;
+        const int w = wv - kCopy0;
         const int kq_lane = (((lane & 15) ^ (4 * ((lane >> 4) & 1))) * Nk * DK + 8 * (lane >> 4)) * 2;
         auto copy_early = [&](int c, bool odd, int m0, int m1) {
             T* Kd = odd ? Ks1 : Ks0;
@@ -1112,9 +1121,8 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
                 } else if (u < NTCP + 2) {                   // V rows 32 vh .. 32 vh + 31 (16 columns)
                     // transition pass: an empty range, so every row reads as zero
                     const int vh = u - NTCP;
-                    const uint32_t vbytes = MODE == kTransition ? 0u : (uint32_t)((L - 1) * Nv * DV + 16) * 2u;
-                    buffer_to_lds16(rsrc(MODE == kTransition ? k : v,
-                                         MODE == kTransition ? 0 : (s * Nv + h) * DV + nb * 16, 2, vbytes),
+                    const uint32_t vbytes = trans ? 0u : (uint32_t)((L - 1) * Nv * DV + 16) * 2u;
+                    buffer_to_lds16(rsrc(trans ? k : v, trans ? 0 : (s * Nv + h) * DV + nb * 16, 2, vbytes),
                                     Vd + vh * 512, ((32 * vh + (lane >> 1)) * Nv * DV + 8 * (lane & 1)) * 2);
                 } else if (u == NTCP + 2 && lane < 32) {     // R (512 bytes: two positions per lane)
                     buffer_to_lds16(rsrc(R, ((int64_t)c * Nv + h) * kChunk, 8, kChunk * 8), Rd, lane * 16);
@@ -1152,15 +1160,7 @@ __global__ __launch_bounds__(768) void k_state_output(const bf16* __restrict__ q
     // until phase B of step c+1, and the score pairs and exp(G) are taken into
     // registers in phase B of step c, before the copy waves overwrite that LDS
     // half with chunk c+2.
-    if constexpr (!want_o) {                         // state only: keep step with the barriers
-        lds_barrier();
-        for (int c = c0; c < c1; ++c) {
-            lds_barrier();
-            lds_barrier();
-            lds_barrier();
-        }
-        return;
-    }
+    if constexpr (!want_o) return;                   // (no output waves in this mode)
     const int w = wv - 4;
     const int ntp = (w >> 1) + 1;
     const int ob = out_f32 ? 4 : 2;
@@ -1380,16 +1380,13 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
                 const bf16 *q = (const bf16*)a.q, *k = (const bf16*)a.k, *v = (const bf16*)a.v;
                 const bf16 *Tf = (const bf16*)a.Tf, *Pf = (const bf16*)a.Pf;
                 const f32x2* R = (const f32x2*)a.R;
-                k_state_output<DK, DV, kStateOnly><<<gs, 768, 0, st>>>(
+                k_state_output<DK, DV, kSegment><<<dim3(a.nseg, a.Nv, DV / 16 + DK / 16), 512, 0, st>>>(
                     q, k, v, R, Tf, Pf, nullptr, a.chunk_start, a.chunk_len, a.seg_first, a.Nk, a.Nv, a.scale,
-                    a.out_f32, nullptr, a.Sloc);
-                k_state_output<DK, DK, kTransition><<<gm, 768, 0, st>>>(
-                    q, k, nullptr, R, Tf, Pf, nullptr, a.chunk_start, a.chunk_len, a.seg_first, a.Nk, a.Nv, a.scale,
-                    a.out_f32, nullptr, a.Mseg);
+                    a.out_f32, nullptr, a.Sloc, a.Mseg);
                 k_segment_scan<DK, DV><<<gn, 256, 0, st>>>(a.seq_seg, a.S0, a.Sloc, a.Mseg, a.Nv, a.Sstart, a.ST);
                 k_state_output<DK, DV, kFull><<<gs, 768, 0, st>>>(
                     q, k, v, R, Tf, Pf, a.Sstart, a.chunk_start, a.chunk_len, a.seg_first, a.Nk, a.Nv, a.scale,
-                    a.out_f32, a.o, nullptr);
+                    a.out_f32, a.o, nullptr, nullptr);
             }
         }
         if (!fused) {
@@ -1409,7 +1406,7 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
                 k_state_output<DK, DV, kFull><<<dim3(a.N, a.Nv, DV / 16), 768, 0, st>>>(
                     (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const f32x2*)a.R,
                     (const bf16*)a.Tf, (const bf16*)a.Pf, a.S0,
-                    a.chunk_start, a.chunk_len, a.seq_first, a.Nk, a.Nv, a.scale, a.out_f32, a.o, a.ST);
+                    a.chunk_start, a.chunk_len, a.seq_first, a.Nk, a.Nv, a.scale, a.out_f32, a.o, a.ST, nullptr);
             }
         }
         if (!fused)
