@@ -503,7 +503,7 @@ def bench_segmented(args) -> None:
         "stage_ms": {("%d:%s" % (i, api.STAGE_NAMES[i])): float(st_seg[i]) for i in range(api.NUM_STAGES)},
         "sweep_ms_per_step": sweep,
         "diff_vs_serial": {"o_max_bf16_steps": diff_o, "S_T_max_over_rms": diff_s},
-        "roofline": {"bound": "hbm", "kernel": "state stage (two side-by-side passes, scan, output pass)",
+        "roofline": {"bound": "hbm", "kernel": "state stage (segment pass, scan, output pass)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None, "algorithmic_bytes": alg, "avg_ms": float(st_seg[4])},
         "cpu_baseline": None,
