@@ -33,6 +33,8 @@
 #include "gdr_device.hpp"
 #include "gdr_launch.hpp"
 
+#include <type_traits>
+
 namespace gdr {
 
 namespace {
@@ -43,128 +45,173 @@ __device__ __forceinline__ int pair_off(int r, int m) {
     return (16 * (mm >> 2) + r) * 8 + (mm & 3) + (m >= 16 ? 4 : 0);
 }
 
-// out(i, j) = sum over kk < K of a(i, kk) b(kk, j) for i < M, j < N; each
-// thread takes 4 x 4 blocks of the output and keeps them in registers.
-template <int M, int N, typename FA, typename FB, typename FS>
-__device__ __forceinline__ void gemm44(int K, FA&& a, FB&& b, FS&& store) {
-    static_assert(M % 4 == 0 && N % 4 == 0, "4 x 4 blocks");
-    constexpr int BN = N / 4, NB = (M / 4) * BN;
-    for (int blk = threadIdx.x; blk < NB; blk += blockDim.x) {
-        const int i0 = (blk / BN) * 4, j0 = (blk % BN) * 4;
-        float acc[4][4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
-        for (int kk = 0; kk < K; ++kk) {
-            float av[4], bv[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) av[r] = a(i0 + r, kk);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) bv[c] = b(kk, j0 + c);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) acc[r][c] += av[r] * bv[c];
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) store(i0 + r, j0 + c, acc[r][c]);
-    }
-}
-
 __device__ __forceinline__ float load_any(const void* p, int64_t idx, int is_f32) {
     return is_f32 ? reinterpret_cast<const float*>(p)[idx] : (float)reinterpret_cast<const bf16*>(p)[idx];
 }
 
 constexpr int kStageK = 16;                     // K-tile of the staged products
 
-// Staged product: out(i, j) = sum over k < K of a(i, k) b(k, j) for i < M,
-// j < N (K a multiple of KT, 16 or 32). Tiles of KT columns of a and KT rows of b go
-// through LDS: each thread loads its share of the next tile into registers
-// while the current one is multiplied, consecutive threads taking consecutive
-// addresses of the operand (AK: a(i, k) is contiguous in k, else in i; BJ:
-// b(k, j) is contiguous in j, else in k). Each thread accumulates its 4 x 4
-// output blocks from LDS: the a values of a block row are shared by many lanes
-// (broadcast reads) and the b values of 4 consecutive columns are one 16-byte
-// read. As holds M x (KT + 1) floats, Bs KT x (N + 4). The product starts with
-// a barrier, so its operands may be LDS or memory written by the phase before.
-template <int M, int N, bool AK, bool BJ, int KT = kStageK, typename FA, typename FB, typename FS>
-__device__ __forceinline__ void gemm_lds(int K, float* As, float* Bs, FA&& a, FB&& b, FS&& store) {
-    constexpr int AP = KT + 1, BP = N + 4;
-    constexpr int BN = N / 4, NBLK = (M / 4) * BN, PER = (NBLK + 255) / 256;
-    constexpr int NA = (M * KT + 255) / 256, NB = (KT * N + 255) / 256;
-    static_assert(M % 4 == 0 && N % 4 == 0, "4 x 4 blocks");
-    const int tid = threadIdx.x;
-    float acc[PER][4][4];
+// LDS pitches of a staged operand tile (rows x KT contraction indices). An
+// operand read from memory along k is kept row by row with a pitch of 17
+// (mod 32) words; one read along its rows is kept k by k with a pitch of 16
+// (mod 32) words. Either way the stores of consecutive threads and the
+// matrix-core fragment reads (16 rows x 4 k per instruction) spread over the
+// LDS banks.
+constexpr int stage_kpitch(int KT) { return KT == 16 ? 17 : KT + 17; }
+constexpr int stage_rpitch(int R) { return R % 32 == 0 ? R + 16 : R + 32; }
+constexpr int stage_floats(int R, int KT) {
+    return R * stage_kpitch(KT) > KT * stage_rpitch(R) ? R * stage_kpitch(KT) : KT * stage_rpitch(R);
+}
+
+// One operand of a staged product: R rows by KT contraction indices, element
+// x(row, k). KC: consecutive k are adjacent in memory (else consecutive rows).
+// Each thread moves groups of 4 elements that are adjacent in memory.
+template <int R, int KT, bool KC>
+struct StageOp {
+    static constexpr int NG4 = R * KT / 4, NE = (NG4 + 255) / 256;
+    static __device__ __forceinline__ int off(int row, int k) {
+        return KC ? row * stage_kpitch(KT) + k : k * stage_rpitch(R) + row;
+    }
+    static __device__ __forceinline__ bool coords(int e, int& row, int& k) {
+        const int g4 = 4 * ((int)threadIdx.x + 256 * e);
+        row = KC ? g4 / KT : g4 % R;
+        k = KC ? g4 % KT : g4 / R;
+        return NG4 % 256 == 0 || g4 < 4 * NG4;
+    }
+    template <typename F>
+    static __device__ __forceinline__ void fetch(f32x4 (&r)[NE], F&& x, int k0) {
 #pragma unroll
-    for (int p = 0; p < PER; ++p)
+        for (int e = 0; e < NE; ++e) {
+            int row, k;
+            const bool ok = coords(e, row, k);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[p][r][c] = 0.f;
-    float ra[NA], rb[NB];
-    auto fetch = [&](int k0) {
-#pragma unroll
-        for (int e = 0; e < NA; ++e) {
-            const int idx = tid + 256 * e;
-            const int i = AK ? idx / KT : idx % M, kk = AK ? idx % KT : idx / M;
-            ra[e] = (M * KT % 256 == 0 || idx < M * KT) ? a(i, k0 + kk) : 0.f;
+            for (int u = 0; u < 4; ++u) r[e][u] = ok ? (KC ? x(row, k0 + k + u) : x(row + u, k0 + k)) : 0.f;
         }
+    }
+    static __device__ __forceinline__ void commit(float* S, const f32x4 (&r)[NE]) {
 #pragma unroll
-        for (int e = 0; e < NB; ++e) {
-            const int idx = tid + 256 * e;
-            const int kk = BJ ? idx / N : idx % KT, j = BJ ? idx % N : idx / KT;
-            rb[e] = (KT * N % 256 == 0 || idx < KT * N) ? b(k0 + kk, j) : 0.f;
-        }
-    };
-    __syncthreads();                                   // operands written by the previous phase are visible
-    fetch(0);
-    for (int k0 = 0; k0 < K; k0 += KT) {
-        __syncthreads();                               // the previous tile is consumed
+        for (int e = 0; e < NE; ++e) {
+            int row, k;
+            if (coords(e, row, k)) {
+                if (KC) {
 #pragma unroll
-        for (int e = 0; e < NA; ++e) {
-            const int idx = tid + 256 * e;
-            const int i = AK ? idx / KT : idx % M, kk = AK ? idx % KT : idx / M;
-            if (M * KT % 256 == 0 || idx < M * KT) As[i * AP + kk] = ra[e];
-        }
-#pragma unroll
-        for (int e = 0; e < NB; ++e) {
-            const int idx = tid + 256 * e;
-            const int kk = BJ ? idx / N : idx % KT, j = BJ ? idx % N : idx / KT;
-            if (KT * N % 256 == 0 || idx < KT * N) Bs[kk * BP + j] = rb[e];
-        }
-        __syncthreads();
-        if (k0 + KT < K) fetch(k0 + KT);               // in flight during this tile's products
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int blk = tid + 256 * p;
-            if (NBLK % 256 == 0 || blk < NBLK) {
-                const int i0 = (blk / BN) * 4, j0 = (blk % BN) * 4;
-#pragma unroll 4
-                for (int kk = 0; kk < KT; ++kk) {
-                    const f32x4 bv = *reinterpret_cast<const f32x4*>(&Bs[kk * BP + j0]);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float av = As[(i0 + r) * AP + kk];
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) acc[p][r][c] += av * bv[c];
-                    }
+                    for (int u = 0; u < 4; ++u) S[off(row, k + u)] = r[e][u];
+                } else {
+                    *reinterpret_cast<f32x4*>(&S[off(row, k)]) = r[e];
                 }
             }
         }
     }
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-        const int blk = tid + 256 * p;
-        if (NBLK % 256 == 0 || blk < NBLK) {
-            const int i0 = (blk / BN) * 4, j0 = (blk % BN) * 4;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) store(i0 + r, j0 + c, acc[p][r][c]);
+};
+
+// Wave layout of a staged product with TM x TN output tiles of 16 x 16 over
+// four wavefronts: WM x WN waves, each owning a block of (TM/WM) x (TN/WN)
+// tiles, the split with the fewest fragment reads per step (with fewer than
+// four tiles, some waves only stage operands).
+constexpr int stage_wm(int TM, int TN) {
+    if (TM * TN < 4) return TM;
+    int best = 0, cost = 1 << 30;
+    for (int wm = 1; wm <= 4; wm *= 2) {
+        const int wn = 4 / wm;
+        if (TM % wm == 0 && TN % wn == 0 && TM / wm + TN / wn < cost) {
+            cost = TM / wm + TN / wn;
+            best = wm;
         }
+    }
+    return best;
+}
+
+template <int M, int N>
+struct StageGrid {
+    static constexpr int TM = M / 16, TN = N / 16;
+    static constexpr int WM = stage_wm(TM, TN), WN = TM * TN < 4 ? TN : 4 / WM;
+    static constexpr int RM = TM / WM, RN = TN / WN;
+};
+
+// Staged product: out(i, j) = sum over k < K of a(i, k) b(k, j) for i < M,
+// j < N (M, N multiples of 16; K a multiple of KT, 16 or 32), on the fp32
+// matrix cores (v_mfma_f32_16x16x4_f32: products and sums in fp32). Tiles of
+// KT columns of a and KT rows of b go through LDS: each thread loads its
+// share of the next tile into registers while the current one is multiplied,
+// consecutive threads taking consecutive addresses of the operand (AK: a(i, k)
+// is contiguous in k, else in i; BJ: b(k, j) is contiguous in j, else in k).
+// Each wave accumulates its block of 16 x 16 tiles; lane 16 qd + r holds rows
+// 4 qd + 0..3 of column r of each tile. As and Bs hold stage_floats(M, KT)
+// and stage_floats(N, KT) floats. The product starts with a barrier, so its
+// operands may be LDS or memory written by the phase before; store(i, j, x)
+// is called once per output element, and for a given (M, N) always by the
+// same thread.
+// Row sums: when store returns a float (a contribution of element (i, j) to a
+// sum over j), the sums of each row are formed in a fixed order (per lane over
+// its tiles, then a butterfly over the 16 lanes of a row) and wave column wn
+// writes its part to Red[wn * M + i]; the caller adds the StageGrid<M, N>::WN
+// parts after a barrier. No atomics: the result is the same on every run.
+template <int M, int N, bool AK, bool BJ, int KT = kStageK, typename FA, typename FB, typename FS>
+__device__ __forceinline__ void gemm_lds(int K, float* As, float* Bs, FA&& a, FB&& b, FS&& store,
+                                         float* Red = nullptr) {
+    static_assert(M % 16 == 0 && N % 16 == 0 && KT % 4 == 0, "16 x 16 tiles");
+    using OA = StageOp<M, KT, AK>;
+    using OB = StageOp<N, KT, !BJ>;
+    using SG = StageGrid<M, N>;
+    constexpr int WM = SG::WM, WN = SG::WN, RM = SG::RM, RN = SG::RN;
+    constexpr bool kRowSum = !std::is_void<decltype(store(0, 0, 0.f))>::value;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const bool active = w < WM * WN;
+    const int tm0 = (w / WN) * RM, tn0 = (w % WN) * RN;
+    const int r = lane & 15, qd = lane >> 4;
+    auto bx = [&](int j, int k) { return b(k, j); };
+    f32x4 acc[RM][RN];
+#pragma unroll
+    for (int x = 0; x < RM; ++x)
+#pragma unroll
+        for (int y = 0; y < RN; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 ra[OA::NE], rb[OB::NE];
+    __syncthreads();                                   // operands written by the previous phase are visible
+    OA::fetch(ra, a, 0);
+    OB::fetch(rb, bx, 0);
+    for (int k0 = 0; k0 < K; k0 += KT) {
+        __syncthreads();                               // the previous tile is consumed
+        OA::commit(As, ra);
+        OB::commit(Bs, rb);
+        __syncthreads();
+        if (k0 + KT < K) {                             // in flight during this tile's products
+            OA::fetch(ra, a, k0 + KT);
+            OB::fetch(rb, bx, k0 + KT);
+        }
+        if (active) {
+#pragma unroll
+            for (int k4 = 0; k4 < KT; k4 += 4) {
+                float af[RM], bf[RN];
+#pragma unroll
+                for (int x = 0; x < RM; ++x) af[x] = As[OA::off(16 * (tm0 + x) + r, k4 + qd)];
+#pragma unroll
+                for (int y = 0; y < RN; ++y) bf[y] = Bs[OB::off(16 * (tn0 + y) + r, k4 + qd)];
+#pragma unroll
+                for (int x = 0; x < RM; ++x)
+#pragma unroll
+                    for (int y = 0; y < RN; ++y)
+                        acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[x], bf[y], acc[x][y], 0, 0, 0);
+            }
+        }
+    }
+    if (active) {
+#pragma unroll
+        for (int x = 0; x < RM; ++x)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int i = 16 * (tm0 + x) + 4 * qd + jj;
+                if constexpr (kRowSum) {
+                    float part = 0.f;
+#pragma unroll
+                    for (int y = 0; y < RN; ++y) part += store(i, 16 * (tn0 + y) + r, acc[x][y][jj]);
+#pragma unroll
+                    for (int o = 8; o > 0; o >>= 1) part += __shfl_xor(part, o);
+                    if (r == 0) Red[(w % WN) * M + i] = part;
+                } else {
+#pragma unroll
+                    for (int y = 0; y < RN; ++y) store(i, 16 * (tn0 + y) + r, acc[x][y][jj]);
+                }
+            }
     }
 }
 
@@ -192,8 +239,8 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ q, const
     constexpr int NMAX = (DK > DV ? DK : DV) > C ? (DK > DV ? DK : DV) : C;
     constexpr int KT = 32;                       // deeper tiles: this kernel's LDS has room
     __shared__ float Pm[C * C];
-    __shared__ float As[(DK > C ? DK : C) * (KT + 1)];
-    __shared__ __attribute__((aligned(16))) float Bs[KT * (NMAX + 4)];
+    __shared__ __attribute__((aligned(16))) float As[stage_floats(DK > C ? DK : C, KT)];
+    __shared__ __attribute__((aligned(16))) float Bs[stage_floats(NMAX, KT)];
     __shared__ float gs[C], se[C];
     const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     const int kh = h / (Nv / Nk);
@@ -413,10 +460,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(const T* __restrict__ q, c
                                                     float* __restrict__ dbeta, float* __restrict__ dg) {
     constexpr int NMAX = (DK > DV ? DK : DV) > C ? (DK > DV ? DK : DV) : C;
     __shared__ float Am[C * C], dMm[C * C], dAm[C * C], Xm[C * C];
-    __shared__ float As[C * (kStageK + 1)];
-    __shared__ __attribute__((aligned(16))) float Bs[kStageK * (NMAX + 4)];
+    __shared__ __attribute__((aligned(16))) float As[stage_floats(C, kStageK)];
+    __shared__ __attribute__((aligned(16))) float Bs[stage_floats(NMAX, kStageK)];
     __shared__ float gs[C], eg[C], elg[C], bs[C], dGs[C], dBs[C], cv[C];
-    __shared__ float sum_sh;
+    __shared__ float wsum[4];
     const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     const int kh = h / (Nv / Nk);
     const int64_t s = chunk_start[c];
@@ -443,9 +490,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(const T* __restrict__ q, c
         bs[tid] = ok ? load_beta(beta, (s + tid) * Nv + h, beta_f32) : 0.f;
         dGs[tid] = 0.f;
         dBs[tid] = 0.f;
-        cv[tid] = 0.f;
     }
-    if (tid == 0) sum_sh = 0.f;
     for (int idx = tid; idx < C * C; idx += 256) {
         const int i = idx / C, j = idx % C;
         Am[idx] = (i < L && j <= i) ? A[((s + i) * Nv + h) * C + j] : 0.f;
@@ -458,44 +503,64 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(const T* __restrict__ q, c
     }
 
     // dP = scale dO V_new^T on and below the diagonal; dM = dP (.) D, and the gate
-    // gradient through D in P: E = dP (.) P adds to dG_i and subtracts from dG_j
+    // gradient through D in P: E = dP (.) P (kept in Xm) adds its row sums to dG
+    // and subtracts its column sums
     gemm_lds<C, C, true, false>(DV, As, Bs, dOg, [&](int kk, int j) { return Vng(j, kk); },
         [&](int i, int j, float x) {
             const float dp = (i < L && j <= i) ? scale * x : 0.f;
             dMm[i * C + j] = dp * Dv(i, j);
-            const float e = dp * Pc[i * C + j];
-            if (e != 0.f) {
-                atomicAdd(&dGs[i], e);
-                atomicAdd(&dGs[j], -e);
-            }
+            Xm[i * C + j] = dp * Pc[i * C + j];
         });
     // dQ = scale diag(exp(G)) dO h^T + dM K (the same thread owns each element in both products)
     gemm_lds<C, DK, true, false>(DV, As, Bs, [&](int i, int kk) { return scale * eg[i] * dOg(i, kk); },
                                  [&](int kk, int m) { return Hc[m * DV + kk]; },
                                  [&](int i, int m, float x) { if (i < L) dqv[row_dk(i) + m] = x; });
+    {   // row and column sums of E, 256 / C threads per position, in a fixed order
+        constexpr int TPR = 256 / C;
+        const int i = tid / TPR, part = tid % TPR;
+        float rs = 0.f, cs = 0.f;
+        for (int j = part; j < C; j += TPR) {
+            rs += Xm[i * C + j];
+            cs += Xm[j * C + i];
+        }
+#pragma unroll
+        for (int o = TPR / 2; o > 0; o >>= 1) {
+            rs += __shfl_xor(rs, o);
+            cs += __shfl_xor(cs, o);
+        }
+        if (part == 0) dGs[i] += rs - cs;
+    }
     gemm_lds<C, DK, true, true>(C, As, Bs, [&](int i, int kk) { return dMm[i * C + kk]; }, Kg,
                                 [&](int i, int m, float x) { if (i < L) dqv[row_dk(i) + m] += x; });
     // dW = -dV_new h^T
     gemm_lds<C, DK, true, false>(DV, As, Bs, dVg, [&](int kk, int m) { return Hc[m * DV + kk]; },
                                  [&](int i, int m, float x) { if (i < L) dW[row_dk(i) + m] = -x; });
-    // dV = diag(beta) A^T dU (dU = dV_new); dbeta += v . (A^T dU)
+    // dV = diag(beta) A^T dU (dU = dV_new); dbeta += v . (A^T dU)  (row sums in dAm, free until dA)
+    float* const red1 = dAm;
+    float* const red2 = dAm + 4 * C;
     gemm_lds<C, DV, false, true>(C, As, Bs, [&](int i, int kk) { return Am[kk * C + i]; }, dVg,
         [&](int i, int j, float x) {
-            if (i < L) {
-                dv[((s + i) * Nv + h) * DV + j] = bs[i] * x;
-                atomicAdd(&dBs[i], Vg(i, j) * x);
-            }
-        });
+            if (i >= L) return 0.f;
+            dv[((s + i) * Nv + h) * DV + j] = bs[i] * x;
+            return Vg(i, j) * x;
+        }, red1);
     // A^T dW: dK = diag(beta exp(G)) A^T dW; dbeta, dG through exp(G) in W
     gemm_lds<C, DK, false, true>(C, As, Bs, [&](int i, int kk) { return Am[kk * C + i]; }, dWg,
         [&](int i, int m, float x) {
-            if (i < L) {
-                dkv[row_dk(i) + m] = bs[i] * eg[i] * x;
-                const float part = Kg(i, m) * x * eg[i];
-                atomicAdd(&dBs[i], part);
-                atomicAdd(&dGs[i], bs[i] * part);
-            }
-        });
+            if (i >= L) return 0.f;
+            dkv[row_dk(i) + m] = bs[i] * eg[i] * x;
+            return Kg(i, m) * x * eg[i];
+        }, red2);
+    __syncthreads();
+    if (tid < C) {
+        float r1 = 0.f, r2 = 0.f;
+#pragma unroll
+        for (int wn = 0; wn < StageGrid<C, DV>::WN; ++wn) r1 += red1[wn * C + tid];
+#pragma unroll
+        for (int wn = 0; wn < StageGrid<C, DK>::WN; ++wn) r2 += red2[wn * C + tid];
+        dBs[tid] += r1 + r2;
+        dGs[tid] += bs[tid] * r2;
+    }
     // dA = dU (diag(beta) V)^T + dW (diag(beta exp(G)) K)^T
     gemm_lds<C, C, true, false>(DV, As, Bs, dVg, [&](int kk, int j) { return bs[j] * Vg(j, kk); },
                                 [&](int i, int j, float x) { dAm[i * C + j] = x; });
@@ -535,30 +600,43 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(const T* __restrict__ q, c
             return kk < C ? Kg(kk, m) : (kk < 2 * C ? bs[kk - C] * Kg(kk - C, m) : Qg(kk - 2 * C, m));
         },
         [&](int i, int m, float x) { if (i < L) dkv[row_dk(i) + m] += x; });
-    // dK += diag(exp(G_last - G)) V_new dS^T; the same term's gate gradient
+    // dK += diag(exp(G_last - G)) V_new dS^T; the same term's gate gradient (row sums
+    // in Xm, free after the dK product above)
+    float* const red3 = Xm;
+    float* const red4 = Xm + 4 * C;
     gemm_lds<C, DK, true, false>(DV, As, Bs, Vng, [&](int kk, int m) { return dSc[m * DV + kk]; },
         [&](int i, int m, float x) {
-            if (i < L) {
-                const float y = elg[i] * x;
-                dkv[row_dk(i) + m] += y;
-                atomicAdd(&cv[i], Kg(i, m) * y);
-            }
-        });
+            if (i >= L) return 0.f;
+            const float y = elg[i] * x;
+            dkv[row_dk(i) + m] += y;
+            return Kg(i, m) * y;
+        }, red3);
     // dG through exp(G) in the inter-chunk output: dG_i += dO_i . (scale exp(G_i) h^T q_i)
     gemm_lds<C, DV, true, true>(DK, As, Bs, Qg, [&](int kk, int j) { return Hc[kk * DV + j]; },
-        [&](int i, int j, float x) { if (i < L) atomicAdd(&dGs[i], scale * eg[i] * dOg(i, j) * x); });
-    // exp(G_last) h in the state update: sum(dS (.) h)
+        [&](int i, int j, float x) { return i < L ? scale * eg[i] * dOg(i, j) * x : 0.f; }, red4);
+    // exp(G_last) h in the state update: sum(dS (.) h), per wave then over the waves
     {
         float part = 0.f;
         for (int idx = tid; idx < DK * DV; idx += 256) part += dSc[idx] * Hc[idx];
-        atomicAdd(&sum_sh, part);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
+        if ((tid & 63) == 0) wsum[tid >> 6] = part;
     }
     __syncthreads();
-    if (tid < C) dGs[tid] -= cv[tid];
+    if (tid < C) {
+        float c3 = 0.f, r4 = 0.f;
+#pragma unroll
+        for (int wn = 0; wn < StageGrid<C, DK>::WN; ++wn) c3 += red3[wn * C + tid];
+#pragma unroll
+        for (int wn = 0; wn < StageGrid<C, DV>::WN; ++wn) r4 += red4[wn * C + tid];
+        cv[tid] = c3;
+        dGs[tid] += r4 - c3;
+    }
     __syncthreads();
     if (tid == 0) {
         float tot = 0.f;
         for (int i = 0; i < L; ++i) tot += cv[i];
+        const float sum_sh = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
         dGs[L - 1] += tot + __expf(gL) * sum_sh;
         float acc = 0.f;                             // dg = reverse prefix sum of dG in the chunk
         for (int i = L - 1; i >= 0; --i) {

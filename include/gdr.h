@@ -233,9 +233,9 @@ gdr_status_t gdr_chunk_fwd_segmented(const gdr_problem_t* problem,
  *                  preparation (layouts, score block), [3] reverse state
  *                  pass, [4] per-chunk gradients, [5] sum of dq and dk over
  *                  the value heads of each q/k head.
- * All arithmetic is fp32. dq, dk, dv and d_initial_state are deterministic;
- * dbeta and dg sum per-position terms with atomic adds and may differ between
- * runs in their last bits. Errors as for gdr_chunk_fwd. Asynchronous on `stream`.
+ * All arithmetic is fp32 (products on the fp32 matrix cores), and every sum
+ * runs in a fixed order: the same inputs give the same bits on every run.
+ * Errors as for gdr_chunk_fwd. Asynchronous on `stream`.
  */
 #define GDR_BWD_NUM_STAGES 5
 gdr_status_t gdr_chunk_bwd_workspace_size(const gdr_problem_t* problem, size_t* bytes);
