@@ -832,6 +832,11 @@ __global__ __launch_bounds__(MODE == kFull ? 768 : 512) void k_state_output(cons
     __shared__ __attribute__((aligned(16))) T Ks0[4 * NKP * FRAG], Ks1[4 * NKP * FRAG];
     __shared__ __attribute__((aligned(16))) T Qs0[4 * NKP * FRAG], Qs1[4 * NKP * FRAG];
     __shared__ __attribute__((aligned(16))) T Pb0[TFRAG], Pb1[TFRAG];
+    // with output (twelve waves) the T pairs also come through LDS, so that the
+    // state waves issue no global loads: a load of theirs would queue behind
+    // the copy waves' tile loads in the compute unit's memory pipeline
+    constexpr int TLDS = MODE == kFull ? TFRAG : 1;
+    __shared__ __attribute__((aligned(16))) T Tb0[TLDS], Tb1[TLDS];
     __shared__ __attribute__((aligned(16))) T Vs0[kChunk * 16], Vs1[kChunk * 16];
     __shared__ __attribute__((aligned(16))) f32x2 Rs0[kChunk], Rs1[kChunk];
     __shared__ __attribute__((aligned(16))) T Sb[NKP][2][FRAG];
@@ -950,10 +955,13 @@ __global__ __launch_bounds__(MODE == kFull ? 768 : 512) void k_state_output(cons
         if (c0 < c1) {
             // T pairs of block w for the current chunk, in registers; the next
             // chunk's are loaded once T Z has used them
+            constexpr bool t_lds = MODE == kFull;
             Split<T> tf[2];
+            if constexpr (!t_lds) {
 #pragma unroll
-            for (int tp = 0; tp < 2; ++tp)
-                if (tp < ntp) tf[tp] = load_pair_set(Tf, c0, pbase + tp);
+                for (int tp = 0; tp < 2; ++tp)
+                    if (tp < ntp) tf[tp] = load_pair_set(Tf, c0, pbase + tp);
+            }
             publish_state();
             lds_barrier();
             for (int c = c0; c < c1; ++c) {
@@ -1005,6 +1013,16 @@ __global__ __launch_bounds__(MODE == kFull ? 768 : 512) void k_state_output(cons
 #pragma unroll
                 for (int tp = 0; tp < 2; ++tp)
                     if (tp < ntp) zf[tp] = load_split(Zb, tp);
+                if constexpr (t_lds) {
+                    const T* Tbb = odd ? Tb1 : Tb0;
+#pragma unroll
+                    for (int tp = 0; tp < 2; ++tp) {
+                        if (tp < ntp) {
+                            tf[tp].hi = load_frag<T>(&Tbb[(pbase + tp) * 2 * FRAG], lane);
+                            tf[tp].lo = load_frag<T>(&Tbb[(pbase + tp) * 2 * FRAG + FRAG], lane);
+                        }
+                    }
+                }
                 f32x4 Qh = {0.f, 0.f, 0.f, 0.f}, Ql = Qh;
                 if constexpr (want_o) {
 #pragma unroll
@@ -1031,7 +1049,7 @@ __global__ __launch_bounds__(MODE == kFull ? 768 : 512) void k_state_output(cons
                 store_split_half(Vtb, w >> 1, w & 1, VD);
                 store_split_half(Vb, w >> 1, w & 1, VN);
                 if constexpr (want_o) QSx[w][lane] = Qh + Ql;
-                if (c + 1 < c1) {
+                if (!t_lds && c + 1 < c1) {
 #pragma unroll
                     for (int tp = 0; tp < 2; ++tp)
                         if (tp < ntp) tf[tp] = load_pair_set(Tf, c + 1, pbase + tp);
@@ -1112,19 +1130,24 @@ __global__ __launch_bounds__(MODE == kFull ? 768 : 512) void k_state_output(cons
             const int64_t s = chunk_s(c);
             const int L = chunk_L(c);
             T* Pd = odd ? Pb1 : Pb0;
+            T* Td = odd ? Tb1 : Tb0;
             const auto rp = rsrc(Pf, ((int64_t)c * Nv + h) * TFRAG, 2, TFRAG * 2);
+            const auto rt = rsrc(Tf, ((int64_t)c * Nv + h) * TFRAG, 2, TFRAG * 2);
+            constexpr int NTP = MODE == kFull ? NTCP : 0;    // T pieces through LDS
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
+            for (int m = 0; m < (NTCP + NTP + 3 + 3) / 4; ++m) {
                 const int u = w + 4 * m;
                 if (u < NTCP) {                              // score piece
                     if constexpr (want_o) buffer_to_lds16(rp, Pd + u * FRAG, (u * 64 + lane) * 16);
-                } else if (u < NTCP + 2) {                   // V rows 32 vh .. 32 vh + 31 (16 columns)
+                } else if (u < NTCP + NTP) {                 // T piece
+                    buffer_to_lds16(rt, Td + (u - NTCP) * FRAG, ((u - NTCP) * 64 + lane) * 16);
+                } else if (u < NTCP + NTP + 2) {             // V rows 32 vh .. 32 vh + 31 (16 columns)
                     // transition pass: an empty range, so every row reads as zero
-                    const int vh = u - NTCP;
+                    const int vh = u - NTCP - NTP;
                     const uint32_t vbytes = trans ? 0u : (uint32_t)((L - 1) * Nv * DV + 16) * 2u;
                     buffer_to_lds16(rsrc(trans ? k : v, trans ? 0 : (s * Nv + h) * DV + nb * 16, 2, vbytes),
                                     Vd + vh * 512, ((32 * vh + (lane >> 1)) * Nv * DV + 8 * (lane & 1)) * 2);
-                } else if (u == NTCP + 2 && lane < 32) {     // R (512 bytes: two positions per lane)
+                } else if (u == NTCP + NTP + 2 && lane < 32) {   // R (512 bytes: two positions per lane)
                     buffer_to_lds16(rsrc(R, ((int64_t)c * Nv + h) * kChunk, 8, kChunk * 8), Rd, lane * 16);
                 }
             }
