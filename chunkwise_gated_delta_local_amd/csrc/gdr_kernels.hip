@@ -793,12 +793,13 @@ constexpr int kFull = 0, kSegment = 1;
 // traffic only (never for global loads or stores):
 //   A  state: S_in (split) from LDS, Y, Z -> LDS; every read of the chunk's
 //             K and Q tiles happens here
-//   B  state: Q S_in -> LDS, V_new = T Z -> LDS, next chunk's T -> registers
+//   B  state: Q S_in -> LDS, V_new = T Z -> LDS (T pairs from LDS)
 //   C  state: S update, S_out (split) -> LDS        output: O -> global
-// K and Q tiles sit in LDS fragment-major: one 1 KB block per (16 rows, 32
-// columns), lane l's 16 bytes at a swizzled slot, so that every matrix-core
-// operand is one 16-byte LDS read; K^T operands come from the same blocks
-// through transposing LDS reads.
+// K and Q tiles sit in LDS row-major with the 16-byte units of each row
+// XOR-permuted by the row (swz): every matrix-core operand is one 16-byte LDS
+// read, K^T operands come from the same tile through transposing LDS reads,
+// both without bank conflicts, and each 1 KB copy moves whole rows (strided
+// half-line copies of 16 rows each ran the state pass about 15 % slower).
 //
 // Contraction orders: products over dk (K S, Q S) take the 32 indices of a
 // block as 8 qd + e for lane quarter qd and element e (so that a fragment is 16
@@ -867,10 +868,15 @@ __global__ __launch_bounds__(MODE == kFull ? 768 : 512) void k_state_output(cons
         return __builtin_amdgcn_make_buffer_rsrc(
             const_cast<char*>(reinterpret_cast<const char*>(base)) + elem_off * elem_bytes, (short)0, (int)bytes, RSRC);
     };
-    // slot of lane (row rr, quarter qq) inside a K/Q fragment block (XOR swizzle by quarter parity)
-    auto slot = [](int rr, int qq) { return 16 * qq + (rr ^ (4 * (qq & 1))); };
+    // K and Q chunk tiles sit in LDS row-major (64 rows of dk values), the
+    // 16-byte units of each row permuted by an XOR with swz(row): the MFMA
+    // operand reads (rows 16 tb + r, unit 4 kp + qd) and the transposing K^T
+    // reads then hit distinct banks, and each tile copy moves whole rows.
+    constexpr int UPR = DK / 8;                  // 16-byte units per row
+    auto swz = [](int row) { return ((((row & 3) << 1) | ((row >> 2) & 1) | (row & 8))) & (UPR - 1); };
     auto frag = [&](const T* tile, int tb, int kp) {
-        return *reinterpret_cast<const v8*>(&tile[(tb * NKP + kp) * FRAG + slot(r, qd) * 8]);
+        const int row = 16 * tb + r;
+        return *reinterpret_cast<const v8*>(&tile[row * DK + ((4 * kp + qd) ^ swz(row)) * 8]);
     };
     // Exchange buffers hold split pair fragments as two lane-linear half blocks
     // (elements 0..3 of every lane, then elements 4..7), so that the wave that
@@ -939,15 +945,18 @@ __global__ __launch_bounds__(MODE == kFull ? 768 : 512) void k_state_output(cons
             }
         };
         // transposed K operand: K^T rows 16 db.., positions of pair tp (stacked order)
+        // (the transposing read gives lane (qd, r') element e = element (r' & 3)
+        // of lane (qd, 4 e + (r' >> 2)), so lane (qd, j) fetches the four dk
+        // values 16 db + 4 (j & 3) .. of position 16 (2 tp + hh) + 4 qd + (j >> 2))
         auto kt_frag = [&](const T* Kb, int db, int tp) {
             const int j = lane & 15;
-            const int qq = 2 * (db & 1) + ((j & 3) >> 1);
+            const int unit = 2 * db + ((j & 3) >> 1);
             const int e0 = 4 * (j & 1);
             v4 part[2];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                const int rr = 4 * qd + (j >> 2);             // row inside block 2 tp + hh
-                const T* p = &Kb[((2 * tp + hh) * NKP + (db >> 1)) * FRAG + slot(rr, qq) * 8 + e0];
+                const int row = 16 * (2 * tp + hh) + 4 * qd + (j >> 2);
+                const T* p = &Kb[row * DK + (unit ^ swz(row)) * 8 + e0];
                 part[hh] = __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)p));
             }
             return concat<T>(part[0], part[1]);
@@ -1102,7 +1111,12 @@ __global__ __launch_bounds__(MODE == kFull ? 768 : 512) void k_state_output(cons
         // but the early list of chunk c+2, which may still be in flight (vector
         // memory operations complete in order).
         const int w = wv - kCopy0;
-        const int kq_lane = (((lane & 15) ^ (4 * ((lane >> 4) & 1))) * Nk * DK + 8 * (lane >> 4)) * 2;
+        // copy u of a tile moves rows 512/DK * u .. (a whole number of rows per 1 KB)
+        constexpr int RPI = 512 / DK;
+        auto kq_off = [&](int u) {
+            const int row = RPI * u + lane / UPR;
+            return (row * Nk * DK + 8 * ((lane % UPR) ^ swz(row))) * 2;
+        };
         auto copy_early = [&](int c, bool odd, int m0, int m1) {
             T* Kd = odd ? Ks1 : Ks0;
             T* Qd = odd ? Qs1 : Qs0;
@@ -1115,12 +1129,11 @@ __global__ __launch_bounds__(MODE == kFull ? 768 : 512) void k_state_output(cons
             for (int m = 0; m < MCE; ++m) {
                 const int u = w + 4 * m;
                 if (m < m0 || m >= m1 || (m >= NKP && !want_o)) continue;
-                if (m < NKP) {                               // K block (tb, kp)
-                    const int tb = u / NKP, kp = u % NKP;
-                    buffer_to_lds16(rk, Kd + u * FRAG, kq_lane + (16 * tb * Nk * DK + 32 * kp) * 2);
-                } else {                                     // Q block
-                    const int f = u - 4 * NKP, tb = f / NKP, kp = f % NKP;
-                    buffer_to_lds16(rq, Qd + f * FRAG, kq_lane + (16 * tb * Nk * DK + 32 * kp) * 2);
+                if (m < NKP) {                               // K rows
+                    buffer_to_lds16(rk, Kd + u * FRAG, kq_off(u));
+                } else {                                     // Q rows
+                    const int f = u - 4 * NKP;
+                    buffer_to_lds16(rq, Qd + f * FRAG, kq_off(f));
                 }
             }
         };
