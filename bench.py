@@ -172,6 +172,55 @@ def _counter_means(path: str, counter: str) -> dict:
     return {n: sums[n] / counts[n] for n in sums}
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_BUSY_CU_CYCLES")
+
+
+def mfma_summary(src: str, out_dir: str) -> None:
+    """Matrix-core utilisation of every gdr kernel from one rocprofv3 counter run
+    (MFMA_COUNTERS, per dispatch): SQ_VALU_MFMA_BUSY_CYCLES (SIMD-cycles, summed
+    over all SIMDs) over the kernel's SIMD-cycles, GRBM_GUI_ACTIVE / 8 (the
+    counter is summed over the 8 XCDs) x 256 compute units x 4 SIMDs; and the
+    issue-rate estimate SQ_INSTS_MFMA x 16 cycles (one v_mfma_f32_16x16x32_bf16
+    on gfx950) over the same SIMD-cycles."""
+    path = None
+    for root, _, files in os.walk(src):
+        for fn in files:
+            if fn.endswith("counter_collection.csv"):
+                path = os.path.join(root, fn)
+    if path is None:
+        raise FileNotFoundError(src)
+    vals = {c: _counter_means(path, c) for c in MFMA_COUNTERS}
+    cmd = ("rocprofv3 --pmc " + " ".join(MFMA_COUNTERS) +
+           " -d <dir>/mfma -o run --output-format csv -- python3 bench.py --steps 3 --warmup 1 --cpu-seconds 0")
+    lines = ["# Matrix-core utilisation per kernel, workload T65536_Nk16_Nv32_d128 (one forward per bench step)",
+             "# command (run from the repository root):", "#   " + cmd,
+             "#   python3 bench.py --mfma-summary <dir> --summary-out profiles",
+             "# kernel cycles = GRBM_GUI_ACTIVE / 8 (the counter sums the 8 XCDs)",
+             "# mfma_busy_frac = SQ_VALU_MFMA_BUSY_CYCLES / (kernel cycles * 256 CUs * 4 SIMDs)",
+             "# mfma_issue_frac = SQ_INSTS_MFMA * 16 cycles / (kernel cycles * 256 * 4)",
+             "# (counter values are means per dispatch)"]
+    for name in sorted(vals["GRBM_GUI_ACTIVE"]):
+        if "gdr" not in name:
+            continue
+        act = vals["GRBM_GUI_ACTIVE"][name]
+        busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"].get(name, float("nan"))
+        insts = vals["SQ_INSTS_MFMA"].get(name, float("nan"))
+        lines += ["", "kernel: %s" % name,
+                  "grbm_gui_active: %.0f" % act,
+                  "sq_valu_mfma_busy_cycles: %.0f" % busy,
+                  "sq_insts_mfma: %.0f" % insts,
+                  "sq_insts_valu: %.0f" % vals["SQ_INSTS_VALU"].get(name, float("nan")),
+                  "sq_busy_cu_cycles: %.0f" % vals["SQ_BUSY_CU_CYCLES"].get(name, float("nan")),
+                  "kernel_cycles: %.0f" % (act / 8),
+                  "mfma_busy_frac: %.4f" % (busy / (act / 8 * 256 * 4)),
+                  "mfma_issue_frac: %.4f" % (insts * 16 / (act / 8 * 256 * 4))]
+    os.makedirs(out_dir, exist_ok=True)
+    out = os.path.join(out_dir, "mfma_util_T65536_Nk16_Nv32_d128_counters.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
 def counter_summary(src: str, out_dir: str, workload: int) -> None:
     """HBM bytes per launch of every gdr kernel from FETCH_SIZE / WRITE_SIZE runs,
     each scaled by what the same counter reads for the copy probe of known size."""
@@ -533,10 +582,15 @@ def main():
     ap.add_argument("--counter-summary", metavar="DIR",
                     help="only summarise rocprofv3 counter runs found under DIR (fetch/, write/, cfetch/, cwrite/) "
                          "into one text file per kernel, written to --summary-out")
+    ap.add_argument("--mfma-summary", metavar="DIR",
+                    help="only summarise a rocprofv3 run of MFMA_COUNTERS found under DIR into profiles/")
     ap.add_argument("--summary-out", metavar="DIR", default="profiles")
     args = ap.parse_args()
     if args.counter_summary:
         counter_summary(args.counter_summary, args.summary_out, args.workload)
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary, args.summary_out)
         return
     if args.gpus != 1:
         print("bench.py: this implementation runs on one GPU only; --gpus %d is not supported" % args.gpus,
