@@ -846,15 +846,31 @@ __global__ __launch_bounds__(MODE == kFull ? 768 : 512) void k_state_output(cons
     __shared__ __attribute__((aligned(16))) T Vtb[2][2][FRAG];
     __shared__ __attribute__((aligned(16))) f32x4 QSx[4][64];
 
-    const int n = blockIdx.x, h = blockIdx.y;
+    // XCD-aware placement: workgroups are dealt to the 8 XCDs round-robin by
+    // linear id, so the grid is renumbered for every XCD to take a contiguous
+    // run of (unit, head, column tile) triples, column tile fastest: the
+    // workgroups that read the same K and Q tiles (all column tiles of the
+    // value heads of one key head) then share one XCD's L2.
+    int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+    {
+        const int64_t W = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+        if (W % 8 == 0) {
+            const int64_t lin = bx + (int64_t)gridDim.x * (by + (int64_t)gridDim.y * bz);
+            const int64_t work = (lin % 8) * (W / 8) + lin / 8;
+            bz = (int)(work % gridDim.z);
+            by = (int)((work / gridDim.z) % gridDim.y);
+            bx = (int)(work / ((int64_t)gridDim.z * gridDim.y));
+        }
+    }
+    const int n = bx, h = by;
     const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave index, uniform
     const int lane = tid & 63, r = lane & 15, qd = lane >> 4;
     const int kh = h / (Nv / Nk);
     constexpr bool want_o = MODE == kFull;       // else state only: no Q, score or output work
     constexpr int kCopy0 = want_o ? 8 : 4;       // first copy wave
-    const bool trans = MODE != kFull && (int)blockIdx.z >= DV / 16;   // transition workgroup
-    const int nb = trans ? (int)blockIdx.z - DV / 16 : (int)blockIdx.z;
+    const bool trans = MODE != kFull && bz >= DV / 16;   // transition workgroup
+    const int nb = trans ? bz - DV / 16 : bz;
     const int NC = trans ? DK : DV;              // columns of the state written
     float* const STo = trans ? ST2 : ST;
     const int c0 = seq_first[n], c1 = seq_first[n + 1];
