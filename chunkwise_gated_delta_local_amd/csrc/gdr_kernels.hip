@@ -791,10 +791,13 @@ constexpr int kFull = 0, kSegment = 1;
 // so waiting for those loads never waits for a store).
 // Each chunk step has three phases separated by barriers that wait for LDS
 // traffic only (never for global loads or stores):
-//   A  state: S_in (split) from LDS, Y, Z -> LDS; every read of the chunk's
-//             K and Q tiles happens here
-//   B  state: Q S_in -> LDS, V_new = T Z -> LDS (T pairs from LDS)
-//   C  state: S update, S_out (split) -> LDS        output: O -> global
+//   A  state:  S_in (split) from LDS, Y, Z -> LDS; every read of the chunk's
+//              K and Q tiles happens here
+//      output: O of the previous chunk, in registers
+//   B  state:  Q S_in -> LDS, V_new = T Z -> LDS (T pairs from LDS)
+//      output: this chunk's score pairs and exp(G) from LDS
+//   C  state:  S update, S_out (split) -> LDS
+//      output: the previous chunk's O -> global
 // K and Q tiles sit in LDS row-major with the 16-byte units of each row
 // XOR-permuted by the row (swz): every matrix-core operand is one 16-byte LDS
 // read, K^T operands come from the same tile through transposing LDS reads,
@@ -1222,6 +1225,7 @@ __global__ __launch_bounds__(MODE == kFull ? 768 : 512) void k_state_output(cons
     const int pbase = (w == 0) ? 0 : (w == 1 ? 1 : (w == 2 ? 2 : 4));
     Split<T> pa[2];                                  // score pairs of the pending chunk
     float ex[4];                                     // exp(G) of its rows
+    f32x4 ofin;                                      // finished output rows, held until phase C
     auto output = [&](int c) {                       // O = scale [exp(G) Q S_in + P V_new], positions 16w..
         Split<T> vn[2];
 #pragma unroll
@@ -1239,12 +1243,16 @@ __global__ __launch_bounds__(MODE == kFull ? 768 : 512) void k_state_output(cons
                 ol = mfma_pair(pa[tp].hi, vn[tp].lo, ol);
             }
         }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ofin[j] = scale * (out[j] + ol[j]);
+    };
+    auto store_out = [&](int c) {
         const int64_t s = chunk_s(c);
         const int L = chunk_L(c);
         const auto ro = rsrc(o, (s * Nv + h) * DV + nb * 16, ob, (uint32_t)(((L - 1) * Nv * DV + 16) * ob));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {                   // rows past the chunk end fall outside ro
-            const float val = scale * (out[j] + ol[j]);
+            const float val = ofin[j];
             if (out_f32) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), ro, o_off[j], 0, 0);
             else __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, to_t<T>(val)), ro,
                                                        o_off[j], 0, 0);
@@ -1271,9 +1279,15 @@ __global__ __launch_bounds__(MODE == kFull ? 768 : 512) void k_state_output(cons
 #pragma unroll
         for (int j = 0; j < 4; ++j) ex[j] = Rsb[w * 16 + 4 * qd + j].x;
         lds_barrier();                                                              // barrier 2
+
+        // ---- C: store the previous chunk's output. Phase C is the output waves'
+        // idlest phase; issued in phase A the stores queue behind the copy
+        // waves' tile loads and lengthen that phase.
+        if (c > c0) store_out(c - 1);
         lds_barrier();                                                              // barrier 3
     }
     output(c1 - 1);
+    store_out(c1 - 1);
 }
 // ============================================================ segment-parallel state passing
 // The state recursion is affine in the state: over any run of chunks,
