@@ -288,24 +288,21 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
         }
         __syncthreads();
 
-        // 3. diagonal block `wave`: lane r < 16 owns column r of the block. Lane i
-        //    holds row i of the block's L in registers; each substitution step
-        //    takes L[i][m] from lane i (a wave-uniform value), so the recursion
-        //    reads LDS only once per row.
+        // 3. diagonal block `wave`: lane r < 16 owns column r of the block. Each
+        //    substitution step reads row i of the block's L with LDS reads whose
+        //    address is the same in every lane (broadcast, no bank conflicts),
+        //    so the recursion spends its vector instructions on the FMAs only.
         {
             const int b0 = wave * 16;
-            float lrow[16];
-#pragma unroll
-            for (int m = 0; m < 16; ++m) lrow[m] = Lf[b0 + r][b0 + m];
             float x[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) x[i] = (i == lane) ? 1.f : 0.f;
 #pragma unroll
             for (int i = 1; i < 16; ++i) {
+                const float* lr = &Lf[b0 + i][b0];     // the same address in every lane: broadcast reads
                 float acc = 0.f;
 #pragma unroll
-                for (int m = 0; m < i; ++m)
-                    acc += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lrow[m]), i)) * x[m];
+                for (int m = 0; m < i; ++m) acc += lr[m] * x[m];
                 if (i > lane) x[i] = -acc;
             }
             if (lane < 16) {
