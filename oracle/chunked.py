@@ -13,10 +13,12 @@ and notation of the pages, one (sequence, V-head, chunk) at a time:
   L      strictly lower part of beta_i (k_i . k_j) D_ij
          (FLA DeltaNet article, section 2.3 and 3.1; ChunkGatedDeltaRule
          page, section 3.1 "direct term")
-  A      (I + L)^-1, built row by row: start from -L and add to each row the
-         already-finished earlier rows weighted by that row's entries, then set
-         the unit diagonal (ChunkGatedDeltaRule page, section 3.1 "recursive
-         correction"; FLA DeltaNet article, section 4)
+  A      (I + L)^-1, the inverse of the unit lower-triangular matrix the
+         pages define (FLA DeltaNet article, section 2.3, the matrix T =
+         (I + tril(diag(beta) K K^T, -1))^-1 diag(beta) with the decay of the
+         gated form; ChunkGatedDeltaRule page, section 3.1 and formulas (1)-(2),
+         where A multiplies the beta-scaled rows). Solved here from its
+         definition (I + L) A = I, one column at a time by forward substitution
   W      A diag(beta * exp(G)) K        formula (1), "k_cumdecay"
   U      A diag(beta) V                 formula (2), "value_new"
   h      S_in, the state entering the chunk
@@ -78,21 +80,22 @@ def strict_lower_attn(Kc: np.ndarray, beta: np.ndarray, D: np.ndarray) -> np.nda
 
 
 def unit_lower_inverse(Lmat: np.ndarray) -> np.ndarray:
-    """A = (I + L)^-1 for strictly lower L, by row-wise forward substitution.
+    """A = (I + L)^-1 for strictly lower-triangular L.
 
-    X starts as -L. Row i is corrected by the finished rows m < i:
-    X[i, :] += sum_m X0[i, m] X[m, :], with X0 the uncorrected -L; then the
-    unit diagonal is added.
+    A is defined by (I + L) A = I. Column j of A solves (I + L) x = e_j; since
+    I + L is unit lower-triangular, row i of that system reads
+    x_i + sum_{m < i} L_im x_m = [i == j], so the entries follow in increasing
+    i by forward substitution (entries above the diagonal come out zero).
     """
     n = Lmat.shape[0]
-    X0 = -Lmat
-    X = X0.copy()
-    for i in range(1, n):
-        corr = np.zeros(n)
-        for m in range(i):
-            corr += X0[i, m] * X[m, :]
-        X[i, :] = X0[i, :] + corr
-    return X + np.eye(n)
+    A = np.zeros((n, n))
+    for j in range(n):
+        x = np.zeros(n)
+        for i in range(n):
+            rhs = 1.0 if i == j else 0.0
+            x[i] = rhs - float(np.dot(Lmat[i, :i], x[:i]))
+        A[:, j] = x
+    return A
 
 
 def wy_products(A, Kc, Vc, beta, G):
