@@ -879,7 +879,10 @@ __global__ __launch_bounds__(MODE == kFull ? 768 : 512) void k_state_output(cons
     const int64_t seq_s = c0 < c1 ? (int64_t)chunk_start[c0] : 0;
     const int64_t seq_e = c0 < c1 ? (int64_t)chunk_start[c1 - 1] + chunk_len[c1 - 1] : 0;
     auto chunk_s = [&](int c) { return seq_s + (int64_t)(c - c0) * kChunk; };
-    auto chunk_L = [&](int c) { return (int)min((int64_t)kChunk, seq_e - chunk_s(c)); };
+    // (clamped to [0, C]: a segment table built from offsets that disagree with
+    // the host's copy can never produce a negative length or a range past the
+    // chunk; an empty chunk copies nothing, leaves the state and writes no rows)
+    auto chunk_L = [&](int c) { return (int)max((int64_t)0, min((int64_t)kChunk, seq_e - chunk_s(c))); };
     auto rsrc = [&](const void* base, int64_t elem_off, int elem_bytes, uint32_t bytes) {
         return __builtin_amdgcn_make_buffer_rsrc(
             const_cast<char*>(reinterpret_cast<const char*>(base)) + elem_off * elem_bytes, (short)0, (int)bytes, RSRC);
@@ -1083,7 +1086,7 @@ __global__ __launch_bounds__(MODE == kFull ? 768 : 512) void k_state_output(cons
 
                 // ---- C: S_out = exp(G_last) S_in + K^T V_decayed for the dk tiles of this wave
                 const Split<T> vt[2] = {load_split(Vtb, 0), load_split(Vtb, 1)};
-                const float a_last = Rsb[L - 1].x;
+                const float a_last = L > 0 ? Rsb[L - 1].x : 1.f;
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) {
                     const int db = w * TPW + t;
@@ -1138,7 +1141,7 @@ __global__ __launch_bounds__(MODE == kFull ? 768 : 512) void k_state_output(cons
             T* Qd = odd ? Qs1 : Qs0;
             const int64_t s = chunk_s(c);
             const int L = chunk_L(c);
-            const uint32_t kq_bytes = (uint32_t)((L - 1) * Nk * DK + DK) * 2u;
+            const uint32_t kq_bytes = L > 0 ? (uint32_t)((L - 1) * Nk * DK + DK) * 2u : 0u;
             const auto rk = rsrc(k, (s * Nk + kh) * DK, 2, kq_bytes);
             const auto rq = rsrc(q, (s * Nk + kh) * DK, 2, kq_bytes);
 #pragma unroll
@@ -1173,7 +1176,7 @@ __global__ __launch_bounds__(MODE == kFull ? 768 : 512) void k_state_output(cons
                 } else if (u < NTCP + NTP + 2) {             // V rows 32 vh .. 32 vh + 31 (16 columns)
                     // transition pass: an empty range, so every row reads as zero
                     const int vh = u - NTCP - NTP;
-                    const uint32_t vbytes = trans ? 0u : (uint32_t)((L - 1) * Nv * DV + 16) * 2u;
+                    const uint32_t vbytes = (trans || L <= 0) ? 0u : (uint32_t)((L - 1) * Nv * DV + 16) * 2u;
                     buffer_to_lds16(rsrc(trans ? k : v, trans ? 0 : (s * Nv + h) * DV + nb * 16, 2, vbytes),
                                     Vd + vh * 512, ((32 * vh + (lane >> 1)) * Nv * DV + 8 * (lane & 1)) * 2);
                 } else if (u == NTCP + NTP + 2 && lane < 32) {   // R (512 bytes: two positions per lane)
@@ -1246,7 +1249,7 @@ __global__ __launch_bounds__(MODE == kFull ? 768 : 512) void k_state_output(cons
     auto store_out = [&](int c) {
         const int64_t s = chunk_s(c);
         const int L = chunk_L(c);
-        const auto ro = rsrc(o, (s * Nv + h) * DV + nb * 16, ob, (uint32_t)(((L - 1) * Nv * DV + 16) * ob));
+        const auto ro = rsrc(o, (s * Nv + h) * DV + nb * 16, ob, L > 0 ? (uint32_t)(((L - 1) * Nv * DV + 16) * ob) : 0u);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {                   // rows past the chunk end fall outside ro
             const float val = ofin[j];
@@ -1333,6 +1336,10 @@ __global__ __launch_bounds__(1024) void k_segment_table(const int32_t* __restric
         if (n < N) {
             seq_seg[n] = first < cap ? first : cap;
             for (int32_t i = 0; i < nseg && first + i < cap; ++i) seg_first[first + i] = f + i * seg_chunks;
+            // the sequence that holds the last kept segment ends it: when the
+            // offsets give more segments than the capacity, that segment takes
+            // the rest of its own sequence and never runs into the next one
+            if (first < cap && first + nseg >= cap) seg_first[cap] = f + nch;
         }
         base += scan[1023];
         __syncthreads();
