@@ -559,6 +559,9 @@ gdr_status_t gdr_recurrent_fwd(const gdr_problem_t* p, const void* q, const void
     const int64_t Ttot = pc.batch * pc.seq_len;
     if (Ttot > 0 && (!q || !k || !v || !beta || !o))
         return fail(GDR_ERR_NULL, "q, k, v, beta and o are required");
+    const void* ptrs[] = {q, k, v, beta, g, initial_state, o, final_state};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return fail(GDR_ERR_SHAPE, "tensor base address not 16-byte aligned");
     gdr::RecurrentArgs a;
     a.bf16 = pc.io_dtype == GDR_BF16;
     a.dk = pc.head_dim_qk;

@@ -220,3 +220,24 @@ def test_backward_rejects_before_launch(lib):
     n = ctypes.c_size_t(0)
     assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0 and n.value > small
     assert lib.gdr_chunk_bwd(*base, *grads, fake, ctypes.c_size_t(small), None, None) == 6
+
+
+def test_recurrent_rejects_before_launch(lib):
+    """gdr_recurrent_fwd checks what every entry point checks: required
+    pointers, and 16-byte alignment of every tensor it is given (outputs
+    included), with no device work."""
+    if torch.cuda.is_available():
+        pytest.skip("passes placeholder addresses; host-logic test for machines without a GPU")
+    p = prob()
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 4)
+    # problem, q, k, v, g, beta, scale, S0, cu_dev, cu_host, l2norm, o, final_state, stream
+    args = [ctypes.byref(p), fake, fake, fake, fake, fake, ctypes.c_float(1.0), fake, None, None, 0, fake, fake,
+            None]
+    for i in (1, 2, 3, 4, 5, 7, 11, 12):          # every tensor argument in turn
+        bad = list(args)
+        bad[i] = odd
+        assert lib.gdr_recurrent_fwd(*bad) == 2, i
+    bad = list(args)
+    bad[11] = None                                 # o missing
+    assert lib.gdr_recurrent_fwd(*bad) == 1
