@@ -54,17 +54,21 @@ def oracle_inputs(inp):
                 scale=inp["scale"])
 
 
-def bf16_ulp(x):
-    """Spacing of bf16 numbers at |x| (8 significant bits)."""
-    ax = np.abs(np.asarray(x, dtype=np.float64))
-    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
-    return np.where(ax > 0, np.ldexp(1.0, (e - 7).astype(np.int64)), 0.0)
+def bf16_round(x):
+    """Round fp64 values to the nearest bf16 (ties to even), through fp32."""
+    x32 = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    b = x32.view(np.uint32).astype(np.uint64)
+    r = (((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16).astype(np.uint32)
+    return r.view(np.float32).astype(np.float64)
 
 
 def bf16_rounding_excess(o_bf16, o_ref):
-    """max over elements of |o - ref| / (ulp(ref) + 1e-4 rms(ref)); <= 1 means every
-    bf16 output is within one bf16 step of the exact value (plus fp32-level noise)."""
+    """max over elements of (|o - ref| - |rne_bf16(ref) - ref|) / rms(ref): how
+    far the bf16 output lies beyond the error of the correctly rounded exact
+    value. A bf16 output is rne(y) of an internal fp32 value y, and
+    |rne(y) - ref| <= |rne(ref) - ref| + 2 |y - ref|, so this is at most twice
+    the fp32-output error; the tests hold it to the same bound."""
     o = np.asarray(o_bf16, dtype=np.float64)
     ref = np.asarray(o_ref, dtype=np.float64)
     rms = np.sqrt(np.mean(ref ** 2))
-    return float(np.max(np.abs(o - ref) / (bf16_ulp(ref) + 1e-4 * rms)))
+    return float(np.max(np.abs(o - ref) - np.abs(bf16_round(ref) - ref)) / (rms if rms > 0 else 1.0))

@@ -42,7 +42,8 @@ def to_np(t, heads, shape):
 
 def check_run(inp, ref, tol, label, beta_f32=False):
     """fp32 output: the max|d|/rms bound. bf16 inputs also run with bf16
-    output, which must sit within one bf16 step of the exact value."""
+    output, whose excess over the correctly rounded exact value's own error
+    (bf16_rounding_excess) must stay within the same bound."""
     o_ref, S_ref, heads = ref
     o32, S = run_gpu(inp, beta_f32=beta_f32, out_f32=True)
     o = to_np(o32[:, :, heads] if heads is not None else o32, None, o_ref.shape)
@@ -55,8 +56,8 @@ def check_run(inp, ref, tol, label, beta_f32=False):
         assert torch.equal(S16, S), (label, "final state depends on the output dtype")
         ob = to_np(o16[:, :, heads] if heads is not None else o16, None, o_ref.shape)
         excess = bf16_rounding_excess(ob, o_ref)
-        msg += " | bf16-out err o %.3e, max error in bf16 steps %.3f" % (rel_err(ob, o_ref), excess)
-        assert excess <= 1.0, (label, "bf16 output", excess)
+        msg += " | bf16-out err o %.3e, excess over rne(exact) %.3e" % (rel_err(ob, o_ref), excess)
+        assert excess <= tol, (label, "bf16 output", excess)
     print(msg, flush=True)
     assert eo <= tol, (label, "o", eo)
     assert es <= tol, (label, "S_T", es)
@@ -69,13 +70,36 @@ def test_config_full_parity(cfg):
     check_run(inp, oracle_reference(inp), TOL[w.dtype], "cfg%d" % cfg)
 
 
-@pytest.mark.parametrize("cfg,heads", [(4, (0, 17)), (5, (0, 9, 31))])
-def test_config_full_size_sampled_heads(cfg, heads):
-    """Full-size workloads as the bench runs them; the oracle computes a sample
-    of value heads (every sequence) one by one."""
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_config_full_size_all_heads(cfg):
+    """Full-size workloads in the bench's launch configuration, every value
+    head compared with the token recurrence. The GPU runs once over all heads;
+    the oracle runs per group of eight value heads (with their q/k heads) so
+    that its fp64 copies stay a few GB."""
     w = synth.WORKLOADS[cfg]
     inp = synth.generate(w, seed=cfg)
-    check_run(inp, oracle_reference(inp, heads), TOL[w.dtype], "cfg%d" % cfg)
+    tol = TOL[w.dtype]
+    o32, S = run_gpu(inp, out_f32=True)
+    o16, S16 = run_gpu(inp)
+    assert torch.equal(S16, S), ("cfg%d" % cfg, "final state depends on the output dtype")
+    Ttot = o32.shape[0] * o32.shape[1]
+    o32 = o32.reshape(Ttot, w.Nv, w.dv)
+    o16 = o16.reshape(Ttot, w.Nv, w.dv)
+    eo = es = ex = 0.0
+    group = 8
+    for h0 in range(0, w.Nv, group):
+        heads = list(range(h0, min(w.Nv, h0 + group)))
+        o_ref, S_ref, _ = oracle_reference(inp, heads)
+        o_ref = o_ref.reshape(Ttot, len(heads), w.dv)
+        o = o32[:, h0:h0 + len(heads)].double().cpu().numpy()
+        ob = o16[:, h0:h0 + len(heads)].double().cpu().numpy()
+        Sn = S[:, h0:h0 + len(heads)].double().cpu().numpy().reshape(S_ref.shape)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(Sn))
+        eo, es = max(eo, rel_err(o, o_ref)), max(es, rel_err(Sn, S_ref))
+        ex = max(ex, bf16_rounding_excess(ob, o_ref))
+        print("cfg%d heads %d..%d: o %.3e S_T %.3e bf16 excess %.3e" % (cfg, heads[0], heads[-1], eo, es, ex),
+              flush=True)
+    assert eo <= tol and es <= tol and ex <= tol, (cfg, eo, es, ex)
 
 
 EDGE = [

@@ -41,8 +41,9 @@ def check(name, inp, l2norm=False):
     ob, _ = run_rec(inp, l2norm=l2norm, out_f32=False, output_final_state=False)
     exc = bf16_rounding_excess(f64(ob).reshape(o_ref.shape), o_ref) if w.dtype == "bf16" else None
     print("%s recurrent fp32-out err o %.3e  S_T %.3e (tol %.0e)%s" % (
-        name, eo, es, tol, "" if exc is None else " | io-dtype out: max error in bf16 steps %.3f" % exc))
+        name, eo, es, tol, "" if exc is None else " | io-dtype out: excess over rne(exact) %.3e" % exc))
     assert eo <= tol and es <= tol
+    assert exc is None or exc <= tol
     if exc is not None:
         assert exc <= 1.0
     return o, S
