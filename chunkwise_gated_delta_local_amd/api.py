@@ -42,7 +42,8 @@ class Problem(ctypes.Structure):
 class Intermediates(ctypes.Structure):
     _fields_ = [("G", ctypes.c_void_p), ("A", ctypes.c_void_p), ("W", ctypes.c_void_p),
                 ("U", ctypes.c_void_p), ("KT", ctypes.c_void_p), ("H", ctypes.c_void_p),
-                ("VN", ctypes.c_void_p), ("T", ctypes.c_void_p), ("num_chunks", ctypes.c_int64)]
+                ("VN", ctypes.c_void_p), ("T", ctypes.c_void_p), ("P", ctypes.c_void_p),
+                ("R", ctypes.c_void_p), ("num_chunks", ctypes.c_int64)]
 
 
 class GdrError(RuntimeError):
@@ -129,6 +130,15 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _aligned16(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    """The library takes tensors whose base address is 16-byte aligned; a
+    contiguous view that starts elsewhere (a one-token slice of a decode
+    batch, say) is passed as an aligned copy."""
+    if t is None or t.data_ptr() % 16 == 0:
+        return t
+    return t.clone(memory_format=torch.contiguous_format)
+
+
 def _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu, chunk_size,
              output_final_state, out_dtype, debug=False, workspace=True, segment_chunks=None):
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:2] != q.shape[:2]:
@@ -158,6 +168,7 @@ def _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu,
     for t in tensors:
         if t is not None and (t.device != dev or not t.is_contiguous()):
             raise ValueError("all tensors must be contiguous and on the same device")
+    q, k, v, beta, g, initial_state = (_aligned16(t) for t in tensors)
     if scale is None:
         scale = dk ** -0.5
     out_dtype = q.dtype if out_dtype is None else out_dtype
@@ -168,7 +179,7 @@ def _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu,
     o = torch.empty(v.shape, dtype=out_dtype, device=dev)
     S_T = torch.empty((N, Nv, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
     if not workspace:                         # token-by-token path: no workspace
-        return prob, o, S_T, cu_dev, cu_host, scale
+        return prob, o, S_T, cu_dev, cu_host, scale, (q, k, v, beta, g, initial_state)
     ws = torch.empty(workspace_size(prob, debug, segment_chunks), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     args = [ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), ctypes.c_float(scale),
@@ -176,7 +187,7 @@ def _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu,
             ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream)]
     if segment_chunks is not None:            # gdr_chunk_fwd_segmented: segment_chunks before the workspace
         args = args[:12] + [ctypes.c_int32(segment_chunks)] + args[12:]
-    keep = (cu_dev, cu_host, ws)
+    keep = (cu_dev, cu_host, ws, q, k, v, beta, g, initial_state)
     return prob, args, o, S_T, keep
 
 
@@ -206,9 +217,10 @@ def recurrent_fwd(q, k, v, beta, g=None, scale=None, initial_state=None, output_
     or None). use_qk_l2norm_in_kernel: q and k are L2-normalised per token
     inside the kernel."""
     lib = load_library()
-    prob, o, S_T, cu_dev, cu_host, scale = _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens,
-                                                    cu_seqlens_cpu, 64, output_final_state, out_dtype,
-                                                    workspace=False)
+    prob, o, S_T, cu_dev, cu_host, scale, ins = _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens,
+                                                         cu_seqlens_cpu, 64, output_final_state, out_dtype,
+                                                         workspace=False)
+    q, k, v, beta, g, initial_state = ins
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(lib.gdr_recurrent_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                  ctypes.c_float(scale), _ptr(initial_state), _ptr(cu_dev), _ptr(cu_host),
@@ -231,9 +243,10 @@ class Backward:
         self.lib = load_library()
         if d_o is None or d_o.shape != v.shape or d_o.dtype not in (q.dtype, torch.float32):
             raise ValueError("d_o must be shaped like v, in the io dtype or float32")
-        prob, _o, _S, cu_dev, cu_host, scale = _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens,
-                                                        cu_seqlens_cpu, chunk_size, False, d_o.dtype,
-                                                        workspace=False)
+        prob, _o, _S, cu_dev, cu_host, scale, ins = _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens,
+                                                             cu_seqlens_cpu, chunk_size, False, d_o.dtype,
+                                                             workspace=False)
+        q, k, v, beta, g, initial_state = ins
         N = prob.num_seqs
         B, T, Nk, dk = q.shape
         Nv, dv = v.shape[2], v.shape[3]
@@ -243,6 +256,7 @@ class Backward:
         for t in (d_o, d_final_state):
             if t is not None and (t.device != q.device or not t.is_contiguous()):
                 raise ValueError("all tensors must be contiguous and on the same device")
+        d_o, d_final_state = _aligned16(d_o), _aligned16(d_final_state)
         dev = q.device
         f32 = dict(dtype=torch.float32, device=dev)
         self.dq = torch.empty(q.shape, **f32)
@@ -314,9 +328,14 @@ def chunk_fwd_debug(q, k, v, beta, g=None, scale=None, initial_state=None, outpu
         KT=torch.zeros((NT, Nk, dk // 16, ntp, 64, 8), dtype=dt, device=dev),
         H=torch.zeros((NT, Nv, dv // 16, dk // 32, 64, 8), dtype=torch.float32, device=dev),
         VN=torch.zeros((NT, Nv, dv // 16, ntp, 64, 8), dtype=torch.float32, device=dev),
-        T=torch.zeros((NT, Nv, 6, 2, 64, 8), dtype=dt, device=dev) if dt == torch.bfloat16 and C == 64 else None,
     )
-    dbg = Intermediates(*(_ptr(out[n]) for n in ("G", "A", "W", "U", "KT", "H", "VN", "T")), 0)
+    fp16_path = dt == torch.bfloat16 and C == 64
+    out.update(
+        T=torch.zeros((NT, Nv, 6, 64, 8), dtype=torch.float16, device=dev) if fp16_path else None,
+        P=torch.zeros((NT, Nv, 6, 64, 8), dtype=torch.float16, device=dev) if fp16_path else None,
+        R=torch.zeros((NT, Nv, 2, 64), dtype=torch.float32, device=dev) if fp16_path else None,
+    )
+    dbg = Intermediates(*(_ptr(out[n]) for n in ("G", "A", "W", "U", "KT", "H", "VN", "T", "P", "R")), 0)
     _check(lib.gdr_chunk_fwd_debug(*args, ctypes.byref(dbg)))
     out.update(o=o, S_T=S_T, num_chunks=int(dbg.num_chunks))
     del keep

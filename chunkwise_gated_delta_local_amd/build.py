@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(BUILD_DIR, "libgdr.so")
-SOURCES = ["gdr_api.hip", "gdr_kernels.hip", "gdr_recurrent.hip", "gdr_backward.hip"]
+SOURCES = ["gdr_api.hip", "gdr_kernels.hip", "gdr_fp16.hip", "gdr_recurrent.hip", "gdr_backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",

@@ -25,8 +25,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Plan {
     int64_t Ttot;
     int32_t nt_cap;
-    size_t off_seq, off_start, off_len, off_first, off_G, off_R, off_Tf, off_Pf, off_A, off_W, off_U, off_KT, off_H, off_VN;
-    size_t sz_Tf, sz_A, sz_W, sz_U, sz_KT, sz_H, sz_VN;   // per chunk except A (whole)
+    size_t off_seq, off_start, off_len, off_first, off_R16, off_T16, off_P16, off_G, off_A, off_W, off_U, off_KT,
+        off_H, off_VN;
+    size_t sz_T16, sz_R16, sz_A, sz_W, sz_U, sz_KT, sz_H, sz_VN;   // per chunk except A (whole)
     size_t production;         // bytes gdr_chunk_fwd needs
     size_t reference;          // bytes gdr_chunk_fwd_debug needs (five separate kernels)
 };
@@ -80,10 +81,14 @@ gdr_status_t check_seqlens(const gdr_problem_t* p, const int32_t* cu, bool varle
     return GDR_OK;
 }
 
-// The fused path runs for bf16 inputs with C = 64; everything else runs the
+// The fp16 path runs for bf16 inputs with C = 64; everything else runs the
 // five kernels, whose production workspace holds their intermediates too.
 bool fused_path(const gdr_problem_t* p) { return p->io_dtype == GDR_BF16 && p->chunk_size == 64; }
 
+// Workspace regions, 256-byte aligned, in this order: the chunk table; on the
+// fp16 path its decay rows, T and score fragments (the production workspace
+// ends there); then the five-kernel path's gate sums and intermediates (its
+// production workspace, and the debug entry point's for every problem).
 Plan make_plan(const gdr_problem_t* p) {
     Plan pl;
     pl.Ttot = p->batch * p->seq_len;
@@ -101,13 +106,14 @@ Plan make_plan(const gdr_problem_t* p) {
     pl.off_start = take(cap * 4);
     pl.off_len = take(cap * 4);
     pl.off_first = take(((size_t)p->num_seqs + 1) * 4);
-    pl.off_G = take(T * Nv * 4);
     const bool fused = fused_path(p);
-    pl.off_R = take(fused ? cap * Nv * 64 * 8 : 0);   // decay factors, chunk-major (float2)
-    pl.sz_Tf = fused ? Nv * 6 * 2 * 512 * es : 0;   // T = A diag(beta): 6 split pair fragments
-    pl.off_Tf = take(cap * pl.sz_Tf);
-    pl.off_Pf = take(cap * pl.sz_Tf);                // score block: same six split pair fragments
+    pl.sz_R16 = fused ? Nv * 2 * 64 * 4 : 0;      // exp(G), exp(G_last - G) per position
+    pl.sz_T16 = fused ? Nv * 6 * 512 * 2 : 0;     // six fp16 pair fragments
+    pl.off_R16 = take(cap * pl.sz_R16);
+    pl.off_T16 = take(cap * pl.sz_T16);
+    pl.off_P16 = take(cap * pl.sz_T16);
     const size_t fused_end = off;
+    pl.off_G = take(T * Nv * 4);
     pl.sz_A = T * Nv * C * 4;
     pl.off_A = take(pl.sz_A);
     pl.sz_W = Nv * C * dk * 4;             // per chunk
@@ -207,10 +213,11 @@ gdr::LaunchArgs fill_args(const gdr_problem_t* p, const Plan& pl, int64_t nt, co
     a.G = reinterpret_cast<float*>(w + pl.off_G);
     a.A = w + pl.off_A; a.W = w + pl.off_W; a.U = w + pl.off_U; a.KT = w + pl.off_KT;
     a.H = w + pl.off_H; a.VN = w + pl.off_VN;
-    a.Tf = pl.sz_Tf ? w + pl.off_Tf : nullptr;
-    a.Pf = pl.sz_Tf ? w + pl.off_Pf : nullptr;
-    a.R = pl.sz_Tf ? w + pl.off_R : nullptr;
+    a.T16 = pl.sz_T16 ? w + pl.off_T16 : nullptr;
+    a.P16 = pl.sz_T16 ? w + pl.off_P16 : nullptr;
+    a.R16 = pl.sz_R16 ? reinterpret_cast<float*>(w + pl.off_R16) : nullptr;
     a.reference = reference;
+    a.prep_only = false;
     a.nseg = 0;
     a.seg_chunks = 0;
     a.seg_first = a.seq_seg = nullptr;
@@ -399,7 +406,9 @@ gdr_status_t gdr_chunk_fwd_debug(const gdr_problem_t* p, const void* q, const vo
         {dbg->KT, pl.off_KT, (size_t)nt * pl.sz_KT},
         {dbg->H, pl.off_H, (size_t)nt * pl.sz_H},
         {dbg->VN, pl.off_VN, (size_t)nt * pl.sz_VN},
-        {dbg->T, pl.off_Tf, (size_t)nt * pl.sz_Tf},
+        {dbg->T, pl.off_T16, (size_t)nt * pl.sz_T16},
+        {dbg->P, pl.off_P16, (size_t)nt * pl.sz_T16},
+        {dbg->R, pl.off_R16, (size_t)nt * pl.sz_R16},
     };
     for (auto& c : copies) {
         if (!c.dst || c.bytes == 0) continue;

@@ -1,0 +1,778 @@
+// Production path of the chunked gated delta-rule forward for bf16 inputs
+// with C = 64, on the fp16 matrix cores of gfx950.
+//
+// Method (FLA DeltaNet article on pnsm.cn, sections 2.3-2.4 and 3.1-3.4;
+// ChunkGatedDeltaRule math page, section 3, formulas (1)-(6)); per chunk of
+// 64 tokens and value head h (q/k head kh = h / (Nv/Nk)):
+//   G      chunk-local inclusive prefix sum of g
+//   L      strictly lower beta_i (k_i . k_j) exp(G_i - G_j);   A = (I + L)^-1
+//   T      A diag(beta)                        (the article's T, section 2.3)
+//   P      (Q K^T) (.) D,  D_ij = exp(G_i - G_j) for j <= i    (formula (5))
+//   Y      K S_in,   Z = V - diag(exp(G)) Y,   V_new = T Z     (= U - W S_in, formula (3))
+//   S_out  exp(G_last) S_in + K^T diag(exp(G_last - G)) V_new (formula (6))
+//   O      scale [diag(exp(G)) Q S_in + P V_new]               (formulas (4), (5))
+//
+// Two kernels:
+//   k_prep     one workgroup per (chunk, q/k head), fully parallel over chunks:
+//              gate sums and decay rows, K K^T and Q K^T on exact bf16
+//              products, the triangular solve in fp32, then T and P rounded
+//              once to fp16 matrix-core fragments.
+//   k_chunk16  one workgroup per (sequence, value head, 16 columns of dv): the
+//              chunk-serial pass. One "chain" wavefront keeps the dk x 16 state
+//              slice in registers and runs the whole per-chunk dependency
+//              Y -> Z -> V_new -> S on the matrix cores without touching LDS
+//              for it: every product's result is, lane for lane, an operand of
+//              the next (two stacked accumulator tiles are a pair fragment of
+//              the transposed block). Two output wavefronts form O from Q and P
+//              (loaded straight into registers) and from the state and V_new
+//              the chain publishes; copy wavefronts stage K (converted to fp16)
+//              and the V and decay tiles in LDS.
+//
+// Number formats: q, k, v are exact in bf16 and exact in fp16 (an fp16 has
+// more significant bits; values below 2^-14 become fp16 subnormals, absolute
+// error below 2^-25). Every value derived inside the method (T, P, the state
+// operand, Z, V_new) is rounded once to fp16 (11 significant bits) where it
+// enters a product; every product accumulates in fp32 and the state itself is
+// carried in fp32. fp16 range: derived values must stay below 65504 in
+// magnitude, which holds for L2-normalised keys and gates g <= 0.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdr_device.hpp"
+#include "gdr_fp16.hpp"
+#include "gdr_launch.hpp"
+
+namespace gdr {
+
+typedef _Float16 f16;
+typedef f16 h8 __attribute__((ext_vector_type(8)));
+typedef f16 h4 __attribute__((ext_vector_type(4)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef s4 __attribute__((address_space(3))) * lds_s4;
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+namespace {
+
+constexpr int kPairs = 6;      // lower-triangular (16-row block, 32-position block) pairs of a 64 x 64 block
+__constant__ int kPairTb[kPairs] = {0, 1, 2, 2, 3, 3};
+__constant__ int kPairTp[kPairs] = {0, 0, 0, 1, 0, 1};
+constexpr int kFrag = 512;     // elements of one pair fragment (64 lanes x 8)
+constexpr int kRsrc = 0x00020000;   // buffer descriptor word 3: raw 32-bit access
+
+__device__ __forceinline__ f32x4 mfma16(const h8& a, const h8& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// two fp32 values -> packed fp16 pair, round to nearest even (v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pk16(float x, float y) {
+    typedef f16 h2 __attribute__((ext_vector_type(2)));
+    h2 v;
+    v[0] = (f16)x;
+    v[1] = (f16)y;
+    return __builtin_bit_cast(uint32_t, v);
+}
+// two accumulator tiles (contraction rows 0..15 and 16..31) -> fp16 pair fragment
+__device__ __forceinline__ h8 pack_pair(const f32x4& a0, const f32x4& a1) {
+    u4 w = {pk16(a0[0], a0[1]), pk16(a0[2], a0[3]), pk16(a1[0], a1[1]), pk16(a1[2], a1[3])};
+    return __builtin_bit_cast(h8, w);
+}
+__device__ __forceinline__ u2 pack4(const f32x4& a) { return u2{pk16(a[0], a[1]), pk16(a[2], a[3])}; }
+// eight bf16 (one 16-byte load) -> eight fp16; exact for normal values (bf16 has 8 significant bits)
+__device__ __forceinline__ h8 bf16x8_to_f16(const u4& w) {
+    u4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = __builtin_bit_cast(float, w[i] << 16);
+        const float hi = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+        r[i] = pk16(lo, hi);
+    }
+    return __builtin_bit_cast(h8, r);
+}
+__device__ __forceinline__ f32x4 bf16x4_to_f32(const s4& v) {
+    f32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = __builtin_bit_cast(float, ((uint32_t)(uint16_t)v[j]) << 16);
+    return r;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int64_t byte_off, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(reinterpret_cast<const char*>(base)) + byte_off,
+                                             (short)0, (int)bytes, kRsrc);
+}
+__device__ __forceinline__ u4 buf_load16(__amdgpu_buffer_rsrc_t rs, int voff) {
+    return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+}
+
+}  // namespace
+
+// ============================================================ k_prep
+// One workgroup (four wavefronts) per (chunk, q/k head); it serves the value
+// heads that share the key head (ChunkGatedDeltaRule page, section 1: GQA).
+//   1. K and Q rows of the chunk -> LDS (zero past the chunk end).
+//   2. K K^T and the transposed score tiles K Q^T of block row `wave` on bf16
+//      matrix cores: exact products of the inputs, fp32 sums (FLA DeltaNet
+//      article, section 3.1).
+//   3. Per value head:
+//      a. G = inclusive prefix sum of g over the chunk (one lane per position,
+//         a shuffle scan in fp32); the decay rows R = (exp(G), exp(G_last - G))
+//         (zero past the chunk end) for the state pass.
+//      b. L = tril(beta_i (k_i . k_j) exp(G_i - G_j), -1) in fp32 (LDS).
+//      c. The four 16 x 16 diagonal blocks of A = (I + L)^-1 by forward
+//         substitution in fp32, then the off-diagonal blocks by block
+//         substitution, 16 -> 32 -> 64, on split-bf16 matrix cores (three
+//         passes, fp32-level accuracy) (ChunkGatedDeltaRule page, section 3.1;
+//         FLA DeltaNet article, section 3.2).
+//      d. T = A diag(beta) and P_ij = (q_i . k_j) exp(G_i - G_j) (j <= i < L)
+//         rounded to fp16 pair fragments of the six lower blocks.
+template <int DK>
+__global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, const bf16* __restrict__ q,
+                                                  const void* __restrict__ beta, int beta_f32,
+                                                  const float* __restrict__ g,
+                                                  const int32_t* __restrict__ chunk_start,
+                                                  const int32_t* __restrict__ chunk_len, int32_t Nk, int32_t Nv,
+                                                  f16* __restrict__ Tf, f16* __restrict__ Pf,
+                                                  float* __restrict__ R) {
+    constexpr int C = 64, NTHR = 256;
+    constexpr int KP = DK + 8;                 // padded LDS row (elements)
+    constexpr int SEGS = C * (DK / 8) / NTHR;  // 16-byte row segments per thread (>= 1 for DK >= 32)
+    constexpr int TILE_BYTES = 2 * C * KP * 2;
+    constexpr int LP = C + 4;                  // L and A row pitch (floats)
+    constexpr int LA_BYTES = 2 * C * LP * 4;
+    static_assert(SEGS >= 1, "dk");
+    __shared__ __attribute__((aligned(16))) char smem[TILE_BYTES > LA_BYTES ? TILE_BYTES : LA_BYTES];
+    __shared__ __attribute__((aligned(16))) float bs[C], gs[C];
+    bf16* Ks = reinterpret_cast<bf16*>(smem);
+    bf16* Qs = Ks + C * KP;
+    float (*Lf)[LP] = reinterpret_cast<float (*)[LP]>(smem);
+    float (*Af)[LP] = Lf + C;
+    typedef Vec<bf16>::v8 v8;
+
+    const int c = blockIdx.x, kh = blockIdx.y;
+    const int64_t s = chunk_start[c];
+    const int L = chunk_len[c];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, qd = lane >> 4;
+    const int group = Nv / Nk;
+
+    // beta and g of a value head go through registers of wave 0: head 0's are
+    // fetched with the tiles, each next head's while the current one is processed
+    float b_nx = 0.f, g_nx = 0.f;
+    auto fetch_gates = [&](int hh) {
+        const int h = kh * group + hh;
+        const bool on = tid < L;
+        b_nx = on ? load_beta(beta, (s + tid) * Nv + h, beta_f32) : 0.f;
+        g_nx = (on && g) ? g[(s + tid) * Nv + h] : 0.f;
+    };
+
+    // 1. K and Q rows (all loads first)
+    {
+        v8 kv[SEGS], qv[SEGS];
+#pragma unroll
+        for (int i = 0; i < SEGS; ++i) {
+            const int idx = tid + NTHR * i, row = idx / (DK / 8), seg = idx % (DK / 8);
+            kv[i] = zero_pair<bf16>();
+            qv[i] = zero_pair<bf16>();
+            if (row < L) {
+                kv[i] = *reinterpret_cast<const v8*>(k + ((s + row) * Nk + kh) * DK + seg * 8);
+                qv[i] = *reinterpret_cast<const v8*>(q + ((s + row) * Nk + kh) * DK + seg * 8);
+            }
+        }
+        if (wave == 0) fetch_gates(0);
+#pragma unroll
+        for (int i = 0; i < SEGS; ++i) {
+            const int idx = tid + NTHR * i, row = idx / (DK / 8), seg = idx % (DK / 8);
+            *reinterpret_cast<v8*>(&Ks[row * KP + seg * 8]) = kv[i];
+            *reinterpret_cast<v8*>(&Qs[row * KP + seg * 8]) = qv[i];
+        }
+    }
+    __syncthreads();
+
+    // 2. kk[j]: K K^T rows 16 wave + 4 qd + jj, column 16 j + r.
+    //    qk[j]: k_{16 j + 4 qd + jj} . q_{16 wave + r} (the score block transposed).
+    f32x4 kk[4], qk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        kk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        qk[j] = kk[j];
+        if (j <= wave) {
+#pragma unroll
+            for (int kp = 0; kp < DK / 32; ++kp) {
+                const v8 kw = load_pair_row<bf16>(&Ks[(wave * 16 + r) * KP + kp * 32], qd);
+                const v8 kj = load_pair_row<bf16>(&Ks[(j * 16 + r) * KP + kp * 32], qd);
+                const v8 qw = load_pair_row<bf16>(&Qs[(wave * 16 + r) * KP + kp * 32], qd);
+                kk[j] = mfma_pair(kw, kj, kk[j]);
+                qk[j] = mfma_pair(kj, qw, qk[j]);
+            }
+        }
+    }
+    __syncthreads();                           // tiles consumed: the LDS now holds L and A
+    for (int idx = tid; idx < 2 * 256; idx += NTHR) {   // the two strictly-upper blocks the merges read
+        const int blk = idx >> 8, e = idx & 255, row = blk * 32 + (e >> 4), col = blk * 32 + 16 + (e & 15);
+        Af[row][col] = 0.f;
+    }
+
+    for (int hh = 0; hh < group; ++hh) {
+        const int h = kh * group + hh;
+        // 3a. prefix sum over the 64 positions (wave 0, one lane per position)
+        if (wave == 0) {
+            float x = g_nx;
+#pragma unroll
+            for (int off = 1; off < C; off <<= 1) {
+                const float y = __shfl_up(x, off, C);
+                if (lane >= off) x += y;
+            }
+            const float g_last = __shfl(x, L > 0 ? L - 1 : 0, C);
+            const bool on = lane < L;
+            gs[lane] = on ? x : 0.f;
+            bs[lane] = b_nx;
+            float* Rh = R + ((int64_t)c * Nv + h) * 2 * C;
+            Rh[lane] = on ? __expf(x) : 0.f;
+            Rh[C + lane] = on ? __expf(g_last - x) : 0.f;
+            if (hh + 1 < group) fetch_gates(hh + 1);
+        }
+        __syncthreads();
+
+        // 3b. strictly lower L
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j <= wave) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int i = wave * 16 + 4 * qd + jj, col = j * 16 + r;
+                    float val = 0.f;
+                    if (i > col && i < L) val = bs[i] * kk[j][jj] * __expf(gs[i] - gs[col]);
+                    Lf[i][col] = val;
+                }
+            }
+        }
+        __syncthreads();
+
+        // 3c. diagonal block `wave`: lane r < 16 owns column r of the block's
+        //     inverse; each substitution step reads row i of L with broadcast reads
+        {
+            const int b0 = wave * 16;
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[i] = (i == lane) ? 1.f : 0.f;
+#pragma unroll
+            for (int i = 1; i < 16; ++i) {
+                const float* lr = &Lf[b0 + i][b0];
+                float acc = 0.f;
+#pragma unroll
+                for (int m = 0; m < i; ++m) acc += lr[m] * x[m];
+                if (i > lane) x[i] = -acc;
+            }
+            if (lane < 16) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) Af[b0 + i][b0 + lane] = x[i];
+            }
+        }
+        __syncthreads();
+        // A_ij = -A_ii (L_ij A_jj) for (i, j) = (1, 0) [wave 0] and (3, 2) [wave 1]
+        if (wave < 2) {
+            const int bi = 2 * wave + 1, bj = 2 * wave;
+            float la[8], db[8], ai[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                la[e] = Lf[bi * 16 + r][bj * 16 + 4 * qd + e];
+                db[e] = Af[bj * 16 + 4 * qd + e][bj * 16 + r];
+                ai[e] = Af[bi * 16 + r][bi * 16 + 4 * qd + e];
+                la[4 + e] = db[4 + e] = ai[4 + e] = 0.f;
+            }
+            const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 t1 = mfma_dd<bf16>(split8<bf16>(la), split8<bf16>(db), zero4);
+            const f32x4 t2 = mfma_dd<bf16>(split8<bf16>(ai), split_acc_pair<bf16>(t1, zero4), zero4);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) Af[bi * 16 + 4 * qd + jj][bj * 16 + r] = -t2[jj];
+        }
+        __syncthreads();
+        // lower-left 32 x 32 block = -A_bot (L_bl A_top); wave w < 2 takes column block w
+        if (wave < 2) {
+            const int ct = wave;
+            float bt[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bt[e] = Af[4 * qd + e][ct * 16 + r];
+                bt[4 + e] = Af[16 + 4 * qd + e][ct * 16 + r];
+            }
+            const Split<bf16> b = split8<bf16>(bt);
+            f32x4 t1[2];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+                t1[rb] = mfma_dd<bf16>(load_split_row<bf16>(&Lf[32 + 16 * rb + r][0], qd), b,
+                                       f32x4{0.f, 0.f, 0.f, 0.f});
+            const Split<bf16> b2 = split_acc_pair<bf16>(t1[0], t1[1]);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const f32x4 t2 = mfma_dd<bf16>(load_split_row<bf16>(&Af[32 + 16 * rb + r][32], qd), b2,
+                                               f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) Af[32 + 16 * rb + 4 * qd + jj][ct * 16 + r] = -t2[jj];
+            }
+        }
+        __syncthreads();
+
+        // 3d. T = A diag(beta): pair p covers rows 16 tb + r and positions
+        //     32 tp + m(qd, e) (m = 4 qd + e, or 16 + 4 qd + e - 4); rows past the end are zero
+        for (int p = wave; p < kPairs; p += 4) {
+            const int tb = kPairTb[p], tp = kPairTp[p];
+            const int row = tb * 16 + r;
+            const int m0 = tp * 32 + 4 * qd;
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(&Af[row][m0]);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(&Af[row][m0 + 16]);
+            const f32x4 b0 = *reinterpret_cast<const f32x4*>(&bs[m0]);
+            const f32x4 b1 = *reinterpret_cast<const f32x4*>(&bs[m0 + 16]);
+            f32x4 x0, x1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x0[e] = (row < L && m0 + e <= row) ? a0[e] * b0[e] : 0.f;
+                x1[e] = (row < L && m0 + 16 + e <= row) ? a1[e] * b1[e] : 0.f;
+            }
+            *reinterpret_cast<h8*>(Tf + (((int64_t)c * Nv + h) * kPairs + p) * kFrag + lane * 8) = pack_pair(x0, x1);
+        }
+        //     P pairs of block row `wave` (rows i = 16 wave + r): the transposed
+        //     tiles qk[j] are, stacked two at a time, the pair fragments of P
+        {
+            const int i = wave * 16 + r;
+            f32x4 pt[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int col = j * 16 + 4 * qd + jj;
+                    pt[j][jj] = (j <= wave && col <= i && i < L) ? qk[j][jj] * __expf(gs[i] - gs[col]) : 0.f;
+                }
+            }
+            const int pbase = (wave == 0) ? 0 : (wave == 1 ? 1 : (wave == 2 ? 2 : 4));
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp) {
+                if (2 * tp <= wave)
+                    *reinterpret_cast<h8*>(Pf + (((int64_t)c * Nv + h) * kPairs + pbase + tp) * kFrag + lane * 8) =
+                        pack_pair(pt[2 * tp], pt[2 * tp + 1]);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ============================================================ k_chunk16
+// Modes: kFull16 (state and output from S0, or from the segment entering
+// states) and kSegment16 (state only: a workgroup with blockIdx.z < dv/16
+// forms the end state of its run of chunks from a zero state; one with a
+// larger blockIdx.z forms the map the run applies to its entering state, the
+// end state from S = I over dk columns with V read as zero). Both serve
+// segment-parallel state passing; the full mode also serves the serial pass.
+//
+// Wavefront roles (eight per workgroup, two per SIMD):
+//   0        chain: the state slice S (dk x 16, fp32) in registers; per chunk
+//              Y = K S (K from LDS in the stacked contraction order, S pairs
+//              from its own accumulators), Z = V - exp(G) Y, V_new = T Z
+//              (T pairs loaded from global memory one chunk ahead),
+//              S = exp(G_last) S + K^T (exp(G_last - G) V_new) with K^T from
+//              transposing LDS reads; publishes V_new and the next entering
+//              state (fp16) for the output waves.
+//   1, 2     output (full mode): chunk c's Q S_in part in step c and its
+//              P V_new part in step c + 1, for the row blocks {0, 3} and {1, 2};
+//              Q (bf16, converted) and P pairs come straight from global memory
+//              into registers one chunk ahead.
+//   3        copies the V slice and the decay rows of chunk c + 2 into LDS
+//              (16-byte buffer-to-LDS loads; rows past a chunk's end read zero).
+//   4 .. 7   K rows of chunk c + 2: loaded in step c - 1, converted to fp16
+//              and written to LDS in step c.
+// One LDS-only barrier per chunk step; K, V and R tiles are triple-buffered.
+//
+// LDS layout of a K tile: row-major, 64 rows of dk fp16 values, the 16-byte
+// units of row `row` permuted by an XOR with swz(row), so that the transposing
+// K^T reads of the chain hit distinct banks.
+template <int DK, int DV, int MODE>
+__global__ __launch_bounds__(512) void k_chunk16(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                 const bf16* __restrict__ v, const float* __restrict__ R,
+                                                 const f16* __restrict__ Tf, const f16* __restrict__ Pf,
+                                                 const float* __restrict__ S0,
+                                                 const int32_t* __restrict__ chunk_start,
+                                                 const int32_t* __restrict__ chunk_len,
+                                                 const int32_t* __restrict__ first, int32_t Nk, int32_t Nv,
+                                                 float scale, int out_f32, void* __restrict__ o,
+                                                 float* __restrict__ ST, float* __restrict__ ST2) {
+    constexpr int C = 64;
+    constexpr int NKP = DK / 32, NDB = DK / 16;
+    constexpr int UPR = DK / 8;                 // 16-byte units per K row
+    constexpr int KLD = UPR / 4;                // 16-byte K loads per lane per convert wave per chunk
+    constexpr bool want_o = MODE == kFull16;
+    static_assert(KLD >= 1, "dk");
+    __shared__ __attribute__((aligned(16))) f16 Ks[3][C * DK];
+    __shared__ __attribute__((aligned(16))) bf16 Vs[3][C * 16];
+    __shared__ __attribute__((aligned(16))) float Rs[3][2 * C];
+    __shared__ __attribute__((aligned(16))) f16 Sx[2][NKP][kFrag];     // entering state, natural dk order
+    __shared__ __attribute__((aligned(16))) f16 VNx[2][2][kFrag];      // V_new pairs (stacked positions)
+
+    // XCD-aware placement (as in the bf16 pass): each XCD takes a contiguous run
+    // of (unit, head, column tile) triples, so the workgroups that read the same
+    // K and Q tiles share one L2.
+    int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+    {
+        const int64_t W = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+        if (W % 8 == 0) {
+            const int64_t lin = bx + (int64_t)gridDim.x * (by + (int64_t)gridDim.y * bz);
+            const int64_t work = (lin % 8) * (W / 8) + lin / 8;
+            bz = (int)(work % gridDim.z);
+            by = (int)((work / gridDim.z) % gridDim.y);
+            bx = (int)(work / ((int64_t)gridDim.z * gridDim.y));
+        }
+    }
+    const int n = bx, h = by;
+    const int tid = threadIdx.x;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, r = lane & 15, qd = lane >> 4;
+    const int kh = h / (Nv / Nk);
+    const bool trans = MODE != kFull16 && bz >= DV / 16;   // transition workgroup
+    const int nb = trans ? bz - DV / 16 : bz;
+    const int NC = trans ? DK : DV;
+    float* const STo = trans ? ST2 : ST;
+    const int c0 = __builtin_amdgcn_readfirstlane(first[n]), c1 = __builtin_amdgcn_readfirstlane(first[n + 1]);
+    auto slot3 = [&](int c) { return (c - c0) % 3; };
+    // chunk start and length are the same in every lane: taken into scalar
+    // registers, so that the buffer descriptors built from them are uniform
+    // (a descriptor in vector registers makes the compiler wrap every buffer
+    // access in a loop over the distinct lane values)
+    auto chunk_s = [&](int c) { return (int64_t)__builtin_amdgcn_readfirstlane(chunk_start[c]); };
+    auto chunk_L = [&](int c) { return max(0, min(C, (int)__builtin_amdgcn_readfirstlane(chunk_len[c]))); };
+    auto swz = [](int row) { return ((((row & 3) << 1) | ((row >> 2) & 1) | (row & 8))) & (UPR - 1); };
+    const int64_t sbase = ((int64_t)n * Nv + h) * DK * NC;
+
+    if (wv == 0) {
+        // ======================================================== chain
+        f32x4 S[NDB];
+#pragma unroll
+        for (int t = 0; t < NDB; ++t) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = t * 16 + 4 * qd + j, col = nb * 16 + r;
+                S[t][j] = trans ? (row == col ? 1.f : 0.f) : (S0 ? S0[sbase + (int64_t)row * NC + col] : 0.f);
+            }
+        }
+        h8 Sp[NKP];
+        // state pairs (stacked dk order) for Y; the output waves' copy in natural
+        // order (lane (qd', r) element e = S[32 kp + 8 qd' + e][r])
+        auto make_pairs = [&](int c_next) {
+#pragma unroll
+            for (int kp = 0; kp < NKP; ++kp) {
+                Sp[kp] = pack_pair(S[2 * kp], S[2 * kp + 1]);
+                if constexpr (want_o) {
+                    const u4 w = __builtin_bit_cast(u4, Sp[kp]);
+                    f16* dst = Sx[(c_next - c0) & 1][kp];
+                    *reinterpret_cast<u2*>(&dst[(16 * (qd >> 1) + r) * 8 + 4 * (qd & 1)]) = u2{w[0], w[1]};
+                    *reinterpret_cast<u2*>(&dst[(16 * (2 + (qd >> 1)) + r) * 8 + 4 * (qd & 1)]) = u2{w[2], w[3]};
+                }
+            }
+        };
+        h8 tf[kPairs];
+        auto load_T = [&](int c) {
+            const auto rs = rsrc_of(Tf, ((int64_t)c * Nv + h) * kPairs * kFrag * 2, kPairs * kFrag * 2);
+#pragma unroll
+            for (int p = 0; p < kPairs; ++p) tf[p] = __builtin_bit_cast(h8, buf_load16(rs, p * kFrag * 2 + lane * 16));
+        };
+        make_pairs(c0);
+        if (c0 < c1) load_T(c0);
+        lds_barrier();                                                            // prologue barrier
+        for (int c = c0; c < c1; ++c) {
+            const int sl = slot3(c);
+            const int L = chunk_L(c);
+            const f16* Kb = Ks[sl];
+            // K operand of Y in the stacked dk order: elements 0..3 = dk 32 kp + 4 qd ..,
+            // 4..7 = dk 32 kp + 16 + 4 qd .., row 16 b + r (two 8-byte reads)
+            h8 ka[4][NKP];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int row = 16 * b + r;
+#pragma unroll
+                for (int kp = 0; kp < NKP; ++kp) {
+                    const int u1 = 4 * kp + (qd >> 1), u2_ = 4 * kp + 2 + (qd >> 1);
+                    const u2 lo = *reinterpret_cast<const u2*>(&Kb[row * DK + ((u1 ^ swz(row)) * 8) + 4 * (qd & 1)]);
+                    const u2 hi = *reinterpret_cast<const u2*>(&Kb[row * DK + ((u2_ ^ swz(row)) * 8) + 4 * (qd & 1)]);
+                    ka[b][kp] = __builtin_bit_cast(h8, u4{lo[0], lo[1], hi[0], hi[1]});
+                }
+            }
+            // V rows 16 b + 4 qd + j of column r (transposing reads of the bf16 tile)
+            f32x4 vrow[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int row = 16 * b + 4 * qd + (r >> 2);
+                const bf16* p = &Vs[sl][row * 16 + 4 * (r & 3)];
+                vrow[b] = bf16x4_to_f32(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)p));
+            }
+            f32x4 eg[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) eg[b] = *reinterpret_cast<const f32x4*>(&Rs[sl][16 * b + 4 * qd]);
+            // ---- Y = K S_in
+            f32x4 Y[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kp = 0; kp < NKP; ++kp) Y[b] = mfma16(ka[b][kp], Sp[kp], Y[b]);
+            }
+            // K^T operands for the update: lane (qd, j) fetches dk 16 db + 4 (j & 3) .. of
+            // position 16 (2 tp + hh) + 4 qd + (j >> 2); the transposing read hands lane
+            // (qd, r') the values of dk 16 db + r' at positions 32 tp + m(qd, e)
+            h8 kt[NDB][2];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                for (int tp = 0; tp < 2; ++tp) {
+                    s4 part[2];
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int row = 16 * (2 * tp + hh) + 4 * qd + (r >> 2);
+                        const int unit = 2 * db + ((r & 3) >> 1);
+                        const f16* p = &Kb[row * DK + (unit ^ swz(row)) * 8 + 4 * (r & 1)];
+                        part[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)p);
+                    }
+                    kt[db][tp] = __builtin_bit_cast(h8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+            }
+            f32x4 ed[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) ed[b] = *reinterpret_cast<const f32x4*>(&Rs[sl][C + 16 * b + 4 * qd]);
+            const float a_last = L > 0 ? Rs[sl][L - 1] : 1.f;
+            // ---- Z = V - exp(G) Y, V_new = T Z
+            f32x4 Z[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Z[b][j] = vrow[b][j] - eg[b][j] * Y[b][j];
+            }
+            const h8 zp0 = pack_pair(Z[0], Z[1]), zp1 = pack_pair(Z[2], Z[3]);
+            const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+            f32x4 VN[4];
+            VN[0] = mfma16(tf[0], zp0, zero4);
+            VN[1] = mfma16(tf[1], zp0, zero4);
+            VN[2] = mfma16(tf[3], zp1, mfma16(tf[2], zp0, zero4));
+            VN[3] = mfma16(tf[5], zp1, mfma16(tf[4], zp0, zero4));
+            if (c + 1 < c1) load_T(c + 1);
+            if constexpr (want_o) {
+                *reinterpret_cast<h8*>(&VNx[(c - c0) & 1][0][lane * 8]) = pack_pair(VN[0], VN[1]);
+                *reinterpret_cast<h8*>(&VNx[(c - c0) & 1][1][lane * 8]) = pack_pair(VN[2], VN[3]);
+            }
+            f32x4 VD[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) VD[b] = VN[b] * ed[b];
+            const h8 vd0 = pack_pair(VD[0], VD[1]), vd1 = pack_pair(VD[2], VD[3]);
+            // ---- S_out = exp(G_last) S_in + K^T VD
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                f32x4 acc = S[db] * a_last;
+                acc = mfma16(kt[db][0], vd0, acc);
+                S[db] = mfma16(kt[db][1], vd1, acc);
+            }
+            make_pairs(c + 1);
+            lds_barrier();                                                        // end of step c
+        }
+        if (STo) {
+#pragma unroll
+            for (int t = 0; t < NDB; ++t) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    STo[sbase + (int64_t)(t * 16 + 4 * qd + j) * NC + nb * 16 + r] = S[t][j];
+            }
+        }
+        return;
+    }
+
+    if (wv == 1 || wv == 2) {
+        // ======================================================== output
+        if constexpr (!want_o) return;
+        if (c0 >= c1) return;
+        const int ow = wv - 1;
+        const int blk[2] = {ow == 0 ? 0 : 1, ow == 0 ? 3 : 2};
+        const int ob = out_f32 ? 4 : 2;
+        u4 qraw[2][NKP];                        // Q rows (bf16) of the coming chunk
+        h8 pf[2][2], pnx[2][2];                 // P pairs of the pending and the coming chunk
+        f32x4 part[2];                          // exp(G) Q S_in of the pending chunk
+        auto load_qp = [&](int c) {
+            const int64_t s = chunk_s(c);
+            const int L = chunk_L(c);
+            const auto rq = rsrc_of(q, (s * Nk + kh) * DK * 2, L > 0 ? (uint32_t)((L - 1) * Nk * DK + DK) * 2u : 0u);
+            const auto rp = rsrc_of(Pf, ((int64_t)c * Nv + h) * kPairs * kFrag * 2, kPairs * kFrag * 2);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int I = blk[i];
+#pragma unroll
+                for (int kp = 0; kp < NKP; ++kp)
+                    qraw[i][kp] = buf_load16(rq, ((16 * I + r) * Nk * DK + 32 * kp + 8 * qd) * 2);
+                const int pb = I == 0 ? 0 : (I == 1 ? 1 : (I == 2 ? 2 : 4));
+#pragma unroll
+                for (int tp = 0; tp < 2; ++tp)
+                    if (2 * tp <= I) pnx[i][tp] = __builtin_bit_cast(h8, buf_load16(rp, (pb + tp) * kFrag * 2 + lane * 16));
+            }
+        };
+        auto finish = [&](int c) {                // O of chunk c += P V_new, then stored
+            const h8 vn0 = *reinterpret_cast<const h8*>(&VNx[(c - c0) & 1][0][lane * 8]);
+            const h8 vn1 = *reinterpret_cast<const h8*>(&VNx[(c - c0) & 1][1][lane * 8]);
+            const int64_t s = chunk_s(c);
+            const int L = chunk_L(c);
+            const auto ro = rsrc_of(o, ((s * Nv + h) * DV + nb * 16) * ob, L > 0 ? (uint32_t)(((L - 1) * Nv * DV + 16) * ob) : 0u);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int I = blk[i];
+                f32x4 acc = mfma16(pf[i][0], vn0, part[i]);
+                if (I >= 2) acc = mfma16(pf[i][1], vn1, acc);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {           // rows past the chunk end fall outside ro
+                    const float val = scale * acc[j];
+                    const int off = ((16 * I + 4 * qd + j) * Nv * DV + r) * ob;
+                    if (out_f32) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), ro, off, 0, 0);
+                    else __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)val), ro, off, 0, 0);
+                }
+            }
+        };
+        load_qp(c0);
+        lds_barrier();                                                            // prologue barrier
+        for (int c = c0; c < c1; ++c) {
+            const int sl = slot3(c);
+            if (c > c0) finish(c - 1);
+            // this chunk's operands, loaded one step ahead
+            h8 qf[2][NKP];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+#pragma unroll
+                for (int kp = 0; kp < NKP; ++kp) qf[i][kp] = bf16x8_to_f16(qraw[i][kp]);
+#pragma unroll
+                for (int tp = 0; tp < 2; ++tp) pf[i][tp] = pnx[i][tp];
+            }
+            if (c + 1 < c1) load_qp(c + 1);
+            h8 sx[NKP];
+#pragma unroll
+            for (int kp = 0; kp < NKP; ++kp) sx[kp] = *reinterpret_cast<const h8*>(&Sx[(c - c0) & 1][kp][lane * 8]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int I = blk[i];
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kp = 0; kp < NKP; ++kp) acc = mfma16(qf[i][kp], sx[kp], acc);
+                const f32x4 egv = *reinterpret_cast<const f32x4*>(&Rs[sl][16 * I + 4 * qd]);
+                part[i] = egv * acc;
+            }
+            lds_barrier();                                                        // end of step c
+        }
+        finish(c1 - 1);
+        return;
+    }
+
+    if (wv == 3) {
+        // ======================================================== V slice and decay rows
+        auto copy_vr = [&](int c) {
+            const int sl = slot3(c);
+            const int64_t s = chunk_s(c);
+            const int L = chunk_L(c);
+            const uint32_t vbytes = (trans || L <= 0) ? 0u : (uint32_t)((L - 1) * Nv * DV + 16) * 2u;
+            const auto rv = rsrc_of(v, ((s * Nv + h) * DV + nb * 16) * 2, vbytes);
+#pragma unroll
+            for (int vh = 0; vh < 2; ++vh)                // rows 32 vh .. 32 vh + 31, 16 columns
+                buffer_to_lds16(rv, &Vs[sl][vh * 512], ((32 * vh + (lane >> 1)) * Nv * DV + 8 * (lane & 1)) * 2);
+            if (lane < 32)                                // decay rows: 512 bytes
+                buffer_to_lds16(rsrc_of(R, ((int64_t)c * Nv + h) * 2 * C * 4, 2 * C * 4), &Rs[sl][0], lane * 16);
+        };
+        if (c0 < c1) copy_vr(c0);
+        if (c0 + 1 < c1) copy_vr(c0 + 1);
+        wait_vmem();
+        lds_barrier();                                                            // prologue barrier
+        for (int c = c0; c < c1; ++c) {
+            if (c + 2 < c1) {
+                copy_vr(c + 2);
+                wait_vmem_but<3>();           // chunk c + 1's copies (issued a step ago) have landed
+            } else {
+                wait_vmem();
+            }
+            lds_barrier();                                                        // end of step c
+        }
+        return;
+    }
+
+    // ============================================================ K rows -> fp16 (waves 4 .. 7)
+    {
+        const int w = wv - 4;
+        u4 kraw[KLD];
+        auto load_k = [&](int c) {
+            const int64_t s = chunk_s(c);
+            const int L = chunk_L(c);
+            const auto rk = rsrc_of(k, (s * Nk + kh) * DK * 2, L > 0 ? (uint32_t)((L - 1) * Nk * DK + DK) * 2u : 0u);
+#pragma unroll
+            for (int i = 0; i < KLD; ++i) {
+                const int f = (w * KLD + i) * 64 + lane;            // 16-byte unit of the tile
+                const int row = f / UPR, u = f % UPR;
+                kraw[i] = buf_load16(rk, (row * Nk * DK + 8 * u) * 2);
+            }
+        };
+        auto store_k = [&](int c) {
+            f16* dst = Ks[slot3(c)];
+#pragma unroll
+            for (int i = 0; i < KLD; ++i) {
+                const int f = (w * KLD + i) * 64 + lane;
+                const int row = f / UPR, u = f % UPR;
+                *reinterpret_cast<h8*>(&dst[row * DK + (u ^ swz(row)) * 8]) = bf16x8_to_f16(kraw[i]);
+            }
+        };
+        if (c0 < c1) { load_k(c0); wait_vmem(); store_k(c0); }
+        if (c0 + 1 < c1) { load_k(c0 + 1); wait_vmem(); store_k(c0 + 1); }
+        if (c0 + 2 < c1) load_k(c0 + 2);
+        lds_barrier();                                                            // prologue barrier
+        for (int c = c0; c < c1; ++c) {
+            if (c + 2 < c1) {
+                wait_vmem();
+                store_k(c + 2);
+                if (c + 3 < c1) load_k(c + 3);
+            }
+            lds_barrier();                                                        // end of step c
+        }
+    }
+}
+
+// ============================================================ launch
+template <int DK, int DV>
+static hipError_t launch_dims(const LaunchArgs& a, hipEvent_t* ev) {
+    hipStream_t st = a.stream;
+    auto mark = [&](int i) { if (ev) (void)hipEventRecord(ev[i], st); };
+    const int32_t NT = a.nt;
+    const bf16 *q = (const bf16*)a.q, *k = (const bf16*)a.k, *v = (const bf16*)a.v;
+    f16* Tf = (f16*)a.T16;
+    f16* Pf = (f16*)a.P16;
+    float* R = a.R16;
+    mark(2);
+    if (NT > 0)
+        k_prep<DK><<<dim3(NT, a.Nk), 256, 0, st>>>(k, q, a.beta, a.beta_f32, a.g, a.chunk_start, a.chunk_len, a.Nk,
+                                                     a.Nv, Tf, Pf, R);
+    mark(3);
+    mark(4);
+    if (a.N > 0 && !a.prep_only) {
+        if (a.nseg > 0) {
+            k_chunk16<DK, DV, kSegment16><<<dim3(a.nseg, a.Nv, DV / 16 + DK / 16), 512, 0, st>>>(
+                q, k, v, R, Tf, Pf, nullptr, a.chunk_start, a.chunk_len, a.seg_first, a.Nk, a.Nv, a.scale,
+                a.out_f32, nullptr, a.Sloc, a.Mseg);
+            const hipError_t e = launch_segment_scan(a);
+            if (e != hipSuccess) return e;
+            k_chunk16<DK, DV, kFull16><<<dim3(a.nseg, a.Nv, DV / 16), 512, 0, st>>>(
+                q, k, v, R, Tf, Pf, a.Sstart, a.chunk_start, a.chunk_len, a.seg_first, a.Nk, a.Nv, a.scale,
+                a.out_f32, a.o, nullptr, nullptr);
+        } else {
+            k_chunk16<DK, DV, kFull16><<<dim3(a.N, a.Nv, DV / 16), 512, 0, st>>>(
+                q, k, v, R, Tf, Pf, a.S0, a.chunk_start, a.chunk_len, a.seq_first, a.Nk, a.Nv, a.scale, a.out_f32,
+                a.o, a.ST, nullptr);
+        }
+    }
+    mark(5);
+    mark(6);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp16_path(const LaunchArgs& a, hipEvent_t* ev) {
+#define GDR_CASE(DKv, DVv) \
+    if (a.dk == DKv && a.dv == DVv) return launch_dims<DKv, DVv>(a, ev);
+    GDR_CASE(32, 32) GDR_CASE(32, 64) GDR_CASE(32, 128)
+    GDR_CASE(64, 32) GDR_CASE(64, 64) GDR_CASE(64, 128)
+    GDR_CASE(128, 32) GDR_CASE(128, 64) GDR_CASE(128, 128)
+#undef GDR_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

@@ -1,0 +1,25 @@
+// Internal interface of the fp16 production path (gdr_fp16.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gdr_launch.hpp"
+
+namespace gdr {
+
+// Modes of the fp16 chunk pass: state and output (serial pass, or the last
+// pass of segment-parallel state passing), or state only (segment passes).
+constexpr int kFull16 = 0, kSegment16 = 1;
+
+// Enqueues stages 2..6 of the forward for bf16 inputs with C = 64 (the chunk
+// and segment tables are built by the caller): k_prep, then the chunk pass (or
+// the two segment passes, the scan and the output pass). Records events
+// [2] .. [6] when `ev` is given. With a.prep_only set, only k_prep runs (the
+// debug entry point's copy of T, P and the decay rows).
+hipError_t launch_fp16_path(const LaunchArgs& a, hipEvent_t* ev);
+
+// Segment scan over the segments of every (sequence, value head, 16 columns)
+// (gdr_kernels.hip): S_start[j] and the final state from S0, M and S_loc.
+hipError_t launch_segment_scan(const LaunchArgs& a);
+
+}  // namespace gdr

@@ -18,14 +18,10 @@
 #include <type_traits>
 
 #include "gdr_device.hpp"
+#include "gdr_fp16.hpp"
 #include "gdr_launch.hpp"
 
 namespace gdr {
-
-// Lower-triangular pair fragments of T (16-row block tb, 32-position block tp).
-constexpr int kTPairs = 6;
-__constant__ int kTPairTb[kTPairs] = {0, 1, 2, 2, 3, 3};
-__constant__ int kTPairTp[kTPairs] = {0, 0, 0, 1, 0, 1};
 
 // ============================================================ chunk table
 // Builds, from the sequence offsets, the list of chunks of C tokens (sequence
@@ -102,19 +98,11 @@ __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict_
 // lane i of each C-lane group takes position i of one head, and the prefix sum
 // runs across the group with shuffles (log2 C steps, always in the same
 // order). g == NULL writes zeros (ungated rule).
-// When R is given, the two decay factors the fused state pass needs are
-// written per token too:
-//   R.x = exp(G_t)                      decay from the chunk start
-//   R.y = exp(G_last - G_t)             decay to the chunk end
-// chunk-major, [chunk][head][C positions] with zeros past the chunk end, so
-// that the sequential pass reads the factors of one (chunk, head) as one
-// contiguous block.
 template <int C>
 __global__ __launch_bounds__(256) void k_gate_cumsum(const float* __restrict__ g,
                                                       const int32_t* __restrict__ chunk_start,
                                                       const int32_t* __restrict__ chunk_len,
-                                                      int32_t NT, int32_t Nv, float* __restrict__ G,
-                                                      f32x2* __restrict__ R) {
+                                                      int32_t NT, int32_t Nv, float* __restrict__ G) {
     constexpr int HB = 256 / C;                   // heads per workgroup
     const int c = blockIdx.x;
     const int i = threadIdx.x % C, h = blockIdx.y * HB + threadIdx.x / C;
@@ -127,10 +115,7 @@ __global__ __launch_bounds__(256) void k_gate_cumsum(const float* __restrict__ g
         const float y = __shfl_up(x, off, C);
         if (i >= off) x += y;
     }
-    const float g_last = __shfl(x, L > 0 ? L - 1 : 0, C);
     if (on && i < L) G[(s + i) * Nv + h] = x;
-    if (R && on)
-        R[((int64_t)c * Nv + h) * C + i] = i < L ? f32x2{__expf(x), __expf(g_last - x)} : f32x2{0.f, 0.f};
 }
 
 // ============================================================ K2: A-build + solve
@@ -149,39 +134,27 @@ __global__ __launch_bounds__(256) void k_gate_cumsum(const float* __restrict__ g
 //        32-block, then the lower-left 32x32 block = -A_bot L_bl A_top.
 //      Both operands are derived values, so each product takes the split
 //      (three-pass) form.
-//   5. A rows (fp32) -> global, zero above the diagonal and past the chunk end
-//      (when A_out is given), and/or T = A diag(beta) (FLA DeltaNet article,
-//      section 2.3: T absorbs diag(beta)) as split (hi, lo) pair fragments of
-//      its lower-triangular 16 x 32 blocks for the fused state pass (C = 64,
-//      when Tf is given).
-//   6. When Pf is given (fused pipeline, C = 64): the intra-chunk score block
-//      P = (Q K^T) (.) D, D_ij = exp(G_i - G_j) for j <= i (ChunkGatedDeltaRule
-//      page, formula (5); FLA DeltaNet article, section 2.4), as split pair
-//      fragments in the same six-block layout as T, so that the state pass
-//      does not recompute it for every dv tile. Q K^T is formed once per key
-//      head; the decay is applied per value head.
+//   5. A rows (fp32) -> global, zero above the diagonal and past the chunk end.
 template <typename T, int DK, int C>
-__global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k, const T* __restrict__ q,
+__global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
                                                          const void* __restrict__ beta, int beta_f32,
                                                          const float* __restrict__ G,
                                                          const int32_t* __restrict__ chunk_start,
                                                          const int32_t* __restrict__ chunk_len,
-                                                         int32_t Nk, int32_t Nv, float* __restrict__ A_out,
-                                                         T* __restrict__ Tf, T* __restrict__ Pf) {
+                                                         int32_t Nk, int32_t Nv, float* __restrict__ A_out) {
     static_assert(C == 16 || C == 32 || C == 64, "chunk size");
     constexpr int NTB = C / 16;                // 16-row blocks of the chunk, one wavefront each
     constexpr int NTHR = 64 * NTB;
     constexpr int KP = DK + 8;                 // padded LDS row (elements)
     constexpr int SEGS = C * (DK / 8) / NTHR;  // 16-byte row segments per thread
-    // The K and Q tiles are only needed until the K K^T and Q K^T tiles are in
-    // registers; L and A reuse their LDS afterwards.
-    constexpr int TILE_BYTES = 2 * C * KP * (int)sizeof(T);
+    // The K tile is only needed until the K K^T tiles are in registers; L and A
+    // reuse its LDS afterwards.
+    constexpr int TILE_BYTES = C * KP * (int)sizeof(T);
     constexpr int LP = C + 4;                  // L and A row pitch (floats): 16-byte aligned rows
     constexpr int LA_BYTES = 2 * C * LP * 4;
     __shared__ __attribute__((aligned(16))) char smem[TILE_BYTES > LA_BYTES ? TILE_BYTES : LA_BYTES];
     __shared__ __attribute__((aligned(16))) float bs[C], gs[C];
     T* Ks = reinterpret_cast<T*>(smem);
-    T* Qs = Ks + C * KP;
     float (*Lf)[LP] = reinterpret_cast<float (*)[LP]>(smem);
     float (*Af)[LP] = Lf + C;
 
@@ -206,25 +179,20 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
         }
     };
 
-    // 1. K (and Q) rows of the chunk (zero past the chunk end): all loads first
+    // 1. K rows of the chunk (zero past the chunk end): all loads first
     {
-        v8 kv[SEGS], qv[SEGS];
+        v8 kv[SEGS];
 #pragma unroll
         for (int i = 0; i < SEGS; ++i) {
             const int idx = tid + NTHR * i, row = idx / (DK / 8), seg = idx % (DK / 8);
             kv[i] = zero_pair<T>();
-            qv[i] = zero_pair<T>();
-            if (row < L) {
-                kv[i] = *reinterpret_cast<const v8*>(k + ((s + row) * Nk + kh) * DK + seg * 8);
-                if (Pf) qv[i] = *reinterpret_cast<const v8*>(q + ((s + row) * Nk + kh) * DK + seg * 8);
-            }
+            if (row < L) kv[i] = *reinterpret_cast<const v8*>(k + ((s + row) * Nk + kh) * DK + seg * 8);
         }
         fetch_gates(0);
 #pragma unroll
         for (int i = 0; i < SEGS; ++i) {
             const int idx = tid + NTHR * i, row = idx / (DK / 8), seg = idx % (DK / 8);
             *reinterpret_cast<v8*>(&Ks[row * KP + seg * 8]) = kv[i];
-            if (Pf) *reinterpret_cast<v8*>(&Qs[row * KP + seg * 8]) = qv[i];
         }
     }
     __syncthreads();
@@ -240,20 +208,6 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
                 v8 a = load_pair_row<T>(&Ks[(wave * 16 + r) * KP + kp * 32], qd);
                 v8 b = load_pair_row<T>(&Ks[(j * 16 + r) * KP + kp * 32], qd);
                 kk[j] = mfma_pair(a, b, kk[j]);
-            }
-        }
-    }
-    // transposed score tiles of block row `wave`: qk[j] holds k_{16j+4qd+jj} . q_{16*wave+r}
-    f32x4 qk[NTB];
-#pragma unroll
-    for (int j = 0; j < NTB; ++j) {
-        qk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (Pf && j <= wave) {
-#pragma unroll
-            for (int kp = 0; kp < DK / 32; ++kp) {
-                v8 a = load_pair_row<T>(&Ks[(j * 16 + r) * KP + kp * 32], qd);
-                v8 b = load_pair_row<T>(&Qs[(wave * 16 + r) * KP + kp * 32], qd);
-                qk[j] = mfma_pair(a, b, qk[j]);
             }
         }
     }
@@ -369,56 +323,6 @@ __global__ __launch_bounds__(256, 4) void k_build_solve(const T* __restrict__ k,
                     val[e] = (col <= row) ? Af[row][col] : 0.f;
                 }
                 *reinterpret_cast<f32x4*>(A_out + ((s + row) * Nv + h) * C + seg * 4) = val;
-            }
-        }
-        // T = A diag(beta) pair fragments: pair p covers rows 16*tb + r and positions 32*tp + m(qd, e)
-        // for (tb, tp) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1); rows past the chunk end are zero.
-        if constexpr (C == 64) {
-            if (Tf) {
-                for (int p = wave; p < kTPairs; p += 4) {
-                    const int tb = kTPairTb[p], tp = kTPairTp[p];
-                    const int row = tb * 16 + r;
-                    const int m0 = tp * 32 + 4 * qd;           // positions m0..m0+3 and m0+16..m0+19
-                    const f32x4 a0 = *reinterpret_cast<const f32x4*>(&Af[row][m0]);
-                    const f32x4 a1 = *reinterpret_cast<const f32x4*>(&Af[row][m0 + 16]);
-                    const f32x4 b0 = *reinterpret_cast<const f32x4*>(&bs[m0]);
-                    const f32x4 b1 = *reinterpret_cast<const f32x4*>(&bs[m0 + 16]);
-                    float x[8];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        x[e] = (row < L && m0 + e <= row) ? a0[e] * b0[e] : 0.f;
-                        x[4 + e] = (row < L && m0 + 16 + e <= row) ? a1[e] * b1[e] : 0.f;
-                    }
-                    const Split<T> sp = split8<T>(x);
-                    T* dst = Tf + (((int64_t)c * Nv + h) * kTPairs + p) * 2 * 512;
-                    store_frag<T>(dst, lane, sp.hi);
-                    if constexpr (kSplitNeeded<T>) store_frag<T>(dst + 512, lane, sp.lo);
-                }
-            }
-        }
-        // 6. score pairs of block row `wave`: P_ij = (q_i . k_j) exp(G_i - G_j), j <= i < L
-        if constexpr (C == 64) {
-            if (Pf) {
-                const int i = wave * 16 + r;
-                f32x4 pt[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const int col = j * 16 + 4 * qd + jj;
-                        pt[j][jj] = (j <= wave && col <= i && i < L) ? qk[j][jj] * __expf(gs[i] - gs[col]) : 0.f;
-                    }
-                }
-                const int pbase = (wave == 0) ? 0 : (wave == 1 ? 1 : (wave == 2 ? 2 : 4));
-#pragma unroll
-                for (int tp = 0; tp < 2; ++tp) {
-                    if (2 * tp <= wave) {
-                        const Split<T> sp = split_acc_pair<T>(pt[2 * tp], pt[2 * tp + 1]);
-                        T* dst = Pf + (((int64_t)c * Nv + h) * kTPairs + pbase + tp) * 2 * 512;
-                        store_frag<T>(dst, lane, sp.hi);
-                        if constexpr (kSplitNeeded<T>) store_frag<T>(dst + 512, lane, sp.lo);
-                    }
-                }
             }
         }
         __syncthreads();
@@ -752,543 +656,6 @@ __global__ __launch_bounds__(256) void k_output(const T* __restrict__ q, const T
 }
 
 // ============================================================ K4 + K5 fused: state pass with output
-// Modes of the fused pass: kFull (state and output, from S0; twelve
-// wavefronts) and kSegment (eight wavefronts: state and copy roles only, no
-// output work). A kSegment workgroup with blockIdx.z < dv/16 forms the end
-// state of its run of chunks from a zero state; one with a larger blockIdx.z
-// forms the map a run of chunks applies to its entering state: the end state
-// from S = I (dk columns, written to ST2) with V read as zero. Both serve
-// segment-parallel state passing (below) and run in one launch, two
-// workgroups to a compute unit.
-constexpr int kFull = 0, kSegment = 1;
-// Production path for bf16 inputs. One workgroup of twelve wavefronts per
-// (sequence, value head, 16 columns of dv) walks the sequence's chunks in
-// order with the state slice S (dk x 16, fp32) on chip, and produces the output
-// of each chunk as it goes, so neither the per-chunk states nor V_new reach HBM.
-// Per chunk (ChunkGatedDeltaRule page, formulas (3)-(6); FLA DeltaNet article,
-// sections 2.3-2.4), with T = A diag(beta) and the score block
-// P = (Q K^T) (.) D from the A-build kernel:
-//   Y     = K S_in,  Z = V - diag(exp(G)) Y      so that V_new = U - W S_in = T Z
-//   V_new = T Z                                  (T lower triangular)
-//   S_out = exp(G_last) S_in + K^T diag(exp(G_last - G)) V_new
-//   O     = scale [diag(exp(G)) Q S_in + P V_new]
-// The wavefronts split into three roles that run side by side, one of each on
-// every SIMD:
-//   state waves  (0..3):  wave w owns positions 16w..16w+15 for Y, Z, Q S_in and
-//                         V_new, and dk tiles of S for the update. This is the
-//                         sequential chain.
-//   output waves (4..7):  wave 4+w forms the output of positions 16w..16w+15.
-//   copy waves   (8..11): move the coming chunks' K, Q, score, V and R tiles
-//                         from global memory straight into LDS (16-byte buffer
-//                         loads to LDS, rows past the chunk end read as zero)
-//                         and do nothing else, so no wave that reads LDS ever
-//                         waits for a copy.
-// The state waves load their T fragments for the next chunk straight into
-// registers once T Z has used the current ones (they issue no global stores,
-// so waiting for those loads never waits for a store).
-// Each chunk step has three phases separated by barriers that wait for LDS
-// traffic only (never for global loads or stores):
-//   A  state:  S_in (split) from LDS, Y, Z -> LDS; every read of the chunk's
-//              K and Q tiles happens here
-//      output: O of the previous chunk, in registers
-//   B  state:  Q S_in -> LDS, V_new = T Z -> LDS (T pairs from LDS)
-//      output: this chunk's score pairs and exp(G) from LDS
-//   C  state:  S update, S_out (split) -> LDS
-//      output: the previous chunk's O -> global
-// K and Q tiles sit in LDS row-major with the 16-byte units of each row
-// XOR-permuted by the row (swz): every matrix-core operand is one 16-byte LDS
-// read, K^T operands come from the same tile through transposing LDS reads,
-// both without bank conflicts, and each 1 KB copy moves whole rows (strided
-// half-line copies of 16 rows each ran the state pass about 15 % slower).
-//
-// Contraction orders: products over dk (K S, Q S) take the 32 indices of a
-// block as 8 qd + e for lane quarter qd and element e (so that a fragment is 16
-// contiguous bytes of a row); products over positions (T Z, K^T V, P V_new) use
-// the stacked-accumulator order of gdr_device.hpp. The state is written to LDS
-// in the first order by the wave that updates it.
-template <int DK, int DV, int MODE>
-__global__ __launch_bounds__(MODE == kFull ? 768 : 512) void k_state_output(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                                       const bf16* __restrict__ v, const f32x2* __restrict__ R, const bf16* __restrict__ Tf,
-                                                       const bf16* __restrict__ Pf, const float* __restrict__ S0,
-                                                       const int32_t* __restrict__ chunk_start,
-                                                       const int32_t* __restrict__ chunk_len,
-                                                       const int32_t* __restrict__ seq_first, int32_t Nk, int32_t Nv,
-                                                       float scale, int out_f32, void* __restrict__ o,
-                                                       float* __restrict__ ST, float* __restrict__ ST2) {
-    typedef bf16 T;
-    typedef Vec<T>::v8 v8;
-    typedef Vec<T>::v4 v4;
-    typedef short s4 __attribute__((ext_vector_type(4)));
-    typedef s4 __attribute__((address_space(3))) * lds_s4;
-    constexpr int NKP = DK / 32, NDB = DK / 16;
-    constexpr int TPW = (NDB + 3) / 4;          // state tiles owned per state wave
-    constexpr int FRAG = 512;                   // elements of one fragment block (64 lanes x 8)
-    constexpr int TFRAG = kTPairs * 2 * 512;    // T elements per (chunk, head)
-    constexpr int NTCP = TFRAG * 2 / 1024;      // 1 KB copies of T per chunk
-    constexpr int MCE = 2 * NKP;                // early-list copies per copy wave per chunk
-    constexpr int RSRC = 0x00020000;            // buffer descriptor word 3 (raw 32-bit access)
-    static_assert(NTCP % 4 == 0, "fragment count");
-    // chunk tiles, double-buffered; each half is its own array so that the
-    // compiler can tell reads of one half from copies into the other
-    __shared__ __attribute__((aligned(16))) T Ks0[4 * NKP * FRAG], Ks1[4 * NKP * FRAG];
-    __shared__ __attribute__((aligned(16))) T Qs0[4 * NKP * FRAG], Qs1[4 * NKP * FRAG];
-    __shared__ __attribute__((aligned(16))) T Pb0[TFRAG], Pb1[TFRAG];
-    // with output (twelve waves) the T pairs also come through LDS, so that the
-    // state waves issue no global loads: a load of theirs would queue behind
-    // the copy waves' tile loads in the compute unit's memory pipeline
-    constexpr int TLDS = MODE == kFull ? TFRAG : 1;
-    __shared__ __attribute__((aligned(16))) T Tb0[TLDS], Tb1[TLDS];
-    __shared__ __attribute__((aligned(16))) T Vs0[kChunk * 16], Vs1[kChunk * 16];
-    __shared__ __attribute__((aligned(16))) f32x2 Rs0[kChunk], Rs1[kChunk];
-    __shared__ __attribute__((aligned(16))) T Sb[NKP][2][FRAG];
-    __shared__ __attribute__((aligned(16))) T Zb[2][2][FRAG];
-    __shared__ __attribute__((aligned(16))) T Vb[2][2][FRAG];
-    __shared__ __attribute__((aligned(16))) T Vtb[2][2][FRAG];
-    __shared__ __attribute__((aligned(16))) f32x4 QSx[4][64];
-
-    // XCD-aware placement: workgroups are dealt to the 8 XCDs round-robin by
-    // linear id, so the grid is renumbered for every XCD to take a contiguous
-    // run of (unit, head, column tile) triples, column tile fastest: the
-    // workgroups that read the same K and Q tiles (all column tiles of the
-    // value heads of one key head) then share one XCD's L2.
-    int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
-    {
-        const int64_t W = (int64_t)gridDim.x * gridDim.y * gridDim.z;
-        if (W % 8 == 0) {
-            const int64_t lin = bx + (int64_t)gridDim.x * (by + (int64_t)gridDim.y * bz);
-            const int64_t work = (lin % 8) * (W / 8) + lin / 8;
-            bz = (int)(work % gridDim.z);
-            by = (int)((work / gridDim.z) % gridDim.y);
-            bx = (int)(work / ((int64_t)gridDim.z * gridDim.y));
-        }
-    }
-    const int n = bx, h = by;
-    const int tid = threadIdx.x;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave index, uniform
-    const int lane = tid & 63, r = lane & 15, qd = lane >> 4;
-    const int kh = h / (Nv / Nk);
-    constexpr bool want_o = MODE == kFull;       // else state only: no Q, score or output work
-    constexpr int kCopy0 = want_o ? 8 : 4;       // first copy wave
-    const bool trans = MODE != kFull && bz >= DV / 16;   // transition workgroup
-    const int nb = trans ? bz - DV / 16 : bz;
-    const int NC = trans ? DK : DV;              // columns of the state written
-    float* const STo = trans ? ST2 : ST;
-    const int c0 = seq_first[n], c1 = seq_first[n + 1];
-    // The chunks of a sequence are consecutive 64-token pieces of its token
-    // range, so their start and length follow from the range.
-    const int64_t seq_s = c0 < c1 ? (int64_t)chunk_start[c0] : 0;
-    const int64_t seq_e = c0 < c1 ? (int64_t)chunk_start[c1 - 1] + chunk_len[c1 - 1] : 0;
-    auto chunk_s = [&](int c) { return seq_s + (int64_t)(c - c0) * kChunk; };
-    // (clamped to [0, C]: a segment table built from offsets that disagree with
-    // the host's copy can never produce a negative length or a range past the
-    // chunk; an empty chunk copies nothing, leaves the state and writes no rows)
-    auto chunk_L = [&](int c) { return (int)max((int64_t)0, min((int64_t)kChunk, seq_e - chunk_s(c))); };
-    auto rsrc = [&](const void* base, int64_t elem_off, int elem_bytes, uint32_t bytes) {
-        return __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<char*>(reinterpret_cast<const char*>(base)) + elem_off * elem_bytes, (short)0, (int)bytes, RSRC);
-    };
-    // K and Q chunk tiles sit in LDS row-major (64 rows of dk values), the
-    // 16-byte units of each row permuted by an XOR with swz(row): the MFMA
-    // operand reads (rows 16 tb + r, unit 4 kp + qd) and the transposing K^T
-    // reads then hit distinct banks, and each tile copy moves whole rows.
-    constexpr int UPR = DK / 8;                  // 16-byte units per row
-    auto swz = [](int row) { return ((((row & 3) << 1) | ((row >> 2) & 1) | (row & 8))) & (UPR - 1); };
-    auto frag = [&](const T* tile, int tb, int kp) {
-        const int row = 16 * tb + r;
-        return *reinterpret_cast<const v8*>(&tile[row * DK + ((4 * kp + qd) ^ swz(row)) * 8]);
-    };
-    // Exchange buffers hold split pair fragments as two lane-linear half blocks
-    // (elements 0..3 of every lane, then elements 4..7), so that the wave that
-    // produces one half writes 8 contiguous bytes per lane.
-    auto store_split_half = [&](T (*buf)[2][FRAG], int tp, int half, const f32x4& x) {
-        float xx[8] = {x[0], x[1], x[2], x[3], 0.f, 0.f, 0.f, 0.f};
-        const Split<T> sp = split8<T>(xx);
-        v4 hi4 = {sp.hi[0], sp.hi[1], sp.hi[2], sp.hi[3]};
-        v4 lo4 = {sp.lo[0], sp.lo[1], sp.lo[2], sp.lo[3]};
-        *reinterpret_cast<v4*>(&buf[tp][0][half * 256 + lane * 4]) = hi4;
-        *reinterpret_cast<v4*>(&buf[tp][1][half * 256 + lane * 4]) = lo4;
-    };
-    auto load_split = [&](T (*buf)[2][FRAG], int tp) {
-        Split<T> sp;
-        sp.hi = concat<T>(*reinterpret_cast<const v4*>(&buf[tp][0][lane * 4]),
-                          *reinterpret_cast<const v4*>(&buf[tp][0][256 + lane * 4]));
-        sp.lo = concat<T>(*reinterpret_cast<const v4*>(&buf[tp][1][lane * 4]),
-                          *reinterpret_cast<const v4*>(&buf[tp][1][256 + lane * 4]));
-        return sp;
-    };
-    const int64_t sbase = ((int64_t)n * Nv + h) * DK * NC;
-    // split pair fragment p (hi, lo) of a six-pair set (T or the score block) of
-    // chunk c, straight into registers (16 bytes per lane per half)
-    auto load_pair_set = [&](const T* base, int c, int p) {
-        typedef int i4 __attribute__((ext_vector_type(4)));
-        const auto rs = rsrc(base, ((int64_t)c * Nv + h) * TFRAG, 2, TFRAG * 2);
-        Split<T> sp;
-        sp.hi = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rs, (p * 2 * FRAG) * 2 + lane * 16, 0, 0));
-        sp.lo = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rs, (p * 2 * FRAG + FRAG) * 2 + lane * 16,
-                                                                             0, 0));
-        return sp;
-    };
-
-    if (wv < 4) {
-        // ======================================================== state waves
-        const int w = wv;
-        const int ntp = (w >> 1) + 1;                       // T pairs of block w: positions < 32 * ntp
-        const int pbase = (w == 0) ? 0 : (w == 1 ? 1 : (w == 2 ? 2 : 4));
-        f32x4 S[TPW];
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            const int db = w * TPW + t;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = db * 16 + 4 * qd + j, col = nb * 16 + r;
-                S[t][j] = db >= NDB ? 0.f
-                          : trans ? (row == col ? 1.f : 0.f)
-                          : S0 ? S0[sbase + (int64_t)row * NC + col] : 0.f;
-            }
-        }
-        // S tile db (rows 16 db + 4 qd + j of this lane's column r) -> B fragments of
-        // contraction block db / 2 in the 8 qd + e order
-        auto publish_state = [&]() {
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                const int db = w * TPW + t;
-                if (db < NDB) {
-                    float xx[8] = {S[t][0], S[t][1], S[t][2], S[t][3], 0.f, 0.f, 0.f, 0.f};
-                    const Split<T> sp = split8<T>(xx);
-                    v4 hi4 = {sp.hi[0], sp.hi[1], sp.hi[2], sp.hi[3]};
-                    v4 lo4 = {sp.lo[0], sp.lo[1], sp.lo[2], sp.lo[3]};
-                    const int dst = (qd & 1) * 256 + (16 * (2 * (db & 1) + (qd >> 1)) + r) * 4;
-                    *reinterpret_cast<v4*>(&Sb[db >> 1][0][dst]) = hi4;
-                    *reinterpret_cast<v4*>(&Sb[db >> 1][1][dst]) = lo4;
-                }
-            }
-        };
-        // transposed K operand: K^T rows 16 db.., positions of pair tp (stacked order)
-        // (the transposing read gives lane (qd, r') element e = element (r' & 3)
-        // of lane (qd, 4 e + (r' >> 2)), so lane (qd, j) fetches the four dk
-        // values 16 db + 4 (j & 3) .. of position 16 (2 tp + hh) + 4 qd + (j >> 2))
-        auto kt_frag = [&](const T* Kb, int db, int tp) {
-            const int j = lane & 15;
-            const int unit = 2 * db + ((j & 3) >> 1);
-            const int e0 = 4 * (j & 1);
-            v4 part[2];
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int row = 16 * (2 * tp + hh) + 4 * qd + (j >> 2);
-                const T* p = &Kb[row * DK + (unit ^ swz(row)) * 8 + e0];
-                part[hh] = __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)p));
-            }
-            return concat<T>(part[0], part[1]);
-        };
-        if (c0 < c1) {
-            // T pairs of block w for the current chunk, in registers; the next
-            // chunk's are loaded once T Z has used them
-            constexpr bool t_lds = MODE == kFull;
-            Split<T> tf[2];
-            if constexpr (!t_lds) {
-#pragma unroll
-                for (int tp = 0; tp < 2; ++tp)
-                    if (tp < ntp) tf[tp] = load_pair_set(Tf, c0, pbase + tp);
-            }
-            publish_state();
-            lds_barrier();
-            for (int c = c0; c < c1; ++c) {
-                const bool odd = (c - c0) & 1;
-                const int L = chunk_L(c);
-                const T* Kb = odd ? Ks1 : Ks0;
-                const T* Qb = odd ? Qs1 : Qs0;
-                const T* Vsb = odd ? Vs1 : Vs0;
-                const f32x2* Rsb = odd ? Rs1 : Rs0;
-
-                // ---- A: Y = K S_in (hi and lo passes), Z = V - exp(G) Y -> LDS
-                Split<T> BS[NKP];
-                v8 ka[NKP], qa[NKP];
-#pragma unroll
-                for (int kp = 0; kp < NKP; ++kp) {
-                    BS[kp] = load_split(Sb, kp);
-                    ka[kp] = frag(Kb, w, kp);
-                }
-                f32x2 rrow[4];
-                float vrow[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    rrow[j] = Rsb[w * 16 + 4 * qd + j];
-                    vrow[j] = to_f(Vsb[(w * 16 + 4 * qd + j) * 16 + r]);
-                }
-#pragma unroll
-                for (int kp = 0; kp < NKP; ++kp) qa[kp] = want_o ? frag(Qb, w, kp) : v8{};
-                v8 kt[TPW][2];                          // K^T operands of phase C
-#pragma unroll
-                for (int t = 0; t < TPW; ++t) {
-                    const int db = min(w * TPW + t, NDB - 1);
-#pragma unroll
-                    for (int tp = 0; tp < 2; ++tp) kt[t][tp] = kt_frag(Kb, db, tp);
-                }
-                f32x4 Yh = {0.f, 0.f, 0.f, 0.f}, Yl = Yh;
-#pragma unroll
-                for (int kp = 0; kp < NKP; ++kp) {
-                    Yh = mfma_pair(ka[kp], BS[kp].hi, Yh);
-                    Yl = mfma_pair(ka[kp], BS[kp].lo, Yl);
-                }
-                f32x4 Z;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) Z[j] = vrow[j] - rrow[j].x * (Yh[j] + Yl[j]);
-                store_split_half(Zb, w >> 1, w & 1, Z);
-                lds_barrier();                                                    // barrier 1
-
-                // ---- B: Q S_in for the output waves; V_new = T Z -> LDS
-                Split<T> zf[2];
-#pragma unroll
-                for (int tp = 0; tp < 2; ++tp)
-                    if (tp < ntp) zf[tp] = load_split(Zb, tp);
-                if constexpr (t_lds) {
-                    const T* Tbb = odd ? Tb1 : Tb0;
-#pragma unroll
-                    for (int tp = 0; tp < 2; ++tp) {
-                        if (tp < ntp) {
-                            tf[tp].hi = load_frag<T>(&Tbb[(pbase + tp) * 2 * FRAG], lane);
-                            tf[tp].lo = load_frag<T>(&Tbb[(pbase + tp) * 2 * FRAG + FRAG], lane);
-                        }
-                    }
-                }
-                f32x4 Qh = {0.f, 0.f, 0.f, 0.f}, Ql = Qh;
-                if constexpr (want_o) {
-#pragma unroll
-                    for (int kp = 0; kp < NKP; ++kp) {
-                        Qh = mfma_pair(qa[kp], BS[kp].hi, Qh);
-                        Ql = mfma_pair(qa[kp], BS[kp].lo, Ql);
-                    }
-                }
-                f32x4 Va = {0.f, 0.f, 0.f, 0.f}, Vl = Va;
-#pragma unroll
-                for (int tp = 0; tp < 2; ++tp) {
-                    if (tp < ntp) {
-                        Va = mfma_pair(tf[tp].hi, zf[tp].hi, Va);
-                        Vl = mfma_pair(tf[tp].lo, zf[tp].hi, Vl);
-                        Vl = mfma_pair(tf[tp].hi, zf[tp].lo, Vl);
-                    }
-                }
-                f32x4 VN, VD;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    VN[j] = Va[j] + Vl[j];
-                    VD[j] = VN[j] * rrow[j].y;
-                }
-                store_split_half(Vtb, w >> 1, w & 1, VD);
-                store_split_half(Vb, w >> 1, w & 1, VN);
-                if constexpr (want_o) QSx[w][lane] = Qh + Ql;
-                if (!t_lds && c + 1 < c1) {
-#pragma unroll
-                    for (int tp = 0; tp < 2; ++tp)
-                        if (tp < ntp) tf[tp] = load_pair_set(Tf, c + 1, pbase + tp);
-                }
-                lds_barrier();                                                    // barrier 2
-
-                // ---- C: S_out = exp(G_last) S_in + K^T V_decayed for the dk tiles of this wave
-                const Split<T> vt[2] = {load_split(Vtb, 0), load_split(Vtb, 1)};
-                const float a_last = L > 0 ? Rsb[L - 1].x : 1.f;
-#pragma unroll
-                for (int t = 0; t < TPW; ++t) {
-                    const int db = w * TPW + t;
-                    if (db < NDB) {
-                        f32x4 acc = S[t] * a_last, lo = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int tp = 0; tp < 2; ++tp) {
-                            acc = mfma_pair(kt[t][tp], vt[tp].hi, acc);
-                            lo = mfma_pair(kt[t][tp], vt[tp].lo, lo);
-                        }
-                        S[t] = acc + lo;
-                    }
-                }
-                publish_state();
-                lds_barrier();                                                    // barrier 3
-            }
-        }
-        if (STo) {
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                const int db = w * TPW + t;
-                if (db < NDB) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        STo[sbase + (int64_t)(db * 16 + 4 * qd + j) * NC + nb * 16 + r] = S[t][j];
-                }
-            }
-        }
-        return;
-    }
-
-    if (c0 >= c1) return;
-    if (wv >= kCopy0) {
-        // ======================================================== copy waves
-        // Wave 8+w moves its share of each chunk's tiles into LDS. A chunk's
-        // early list (K and Q blocks: read only in phase A) is issued during
-        // phases B and C two steps ahead, once the state waves have finished
-        // reading the half it overwrites; its late list (score pieces, V
-        // halves, R: read until phase C) during phase A one step ahead. (T goes
-        // straight into the state waves' registers.) Before the last barrier of step c the wave waits for everything
-        // but the early list of chunk c+2, which may still be in flight (vector
-        // memory operations complete in order).
-        const int w = wv - kCopy0;
-        // copy u of a tile moves rows 512/DK * u .. (a whole number of rows per 1 KB)
-        constexpr int RPI = 512 / DK;
-        auto kq_off = [&](int u) {
-            const int row = RPI * u + lane / UPR;
-            return (row * Nk * DK + 8 * ((lane % UPR) ^ swz(row))) * 2;
-        };
-        auto copy_early = [&](int c, bool odd, int m0, int m1) {
-            T* Kd = odd ? Ks1 : Ks0;
-            T* Qd = odd ? Qs1 : Qs0;
-            const int64_t s = chunk_s(c);
-            const int L = chunk_L(c);
-            const uint32_t kq_bytes = L > 0 ? (uint32_t)((L - 1) * Nk * DK + DK) * 2u : 0u;
-            const auto rk = rsrc(k, (s * Nk + kh) * DK, 2, kq_bytes);
-            const auto rq = rsrc(q, (s * Nk + kh) * DK, 2, kq_bytes);
-#pragma unroll
-            for (int m = 0; m < MCE; ++m) {
-                const int u = w + 4 * m;
-                if (m < m0 || m >= m1 || (m >= NKP && !want_o)) continue;
-                if (m < NKP) {                               // K rows
-                    buffer_to_lds16(rk, Kd + u * FRAG, kq_off(u));
-                } else {                                     // Q rows
-                    const int f = u - 4 * NKP;
-                    buffer_to_lds16(rq, Qd + f * FRAG, kq_off(f));
-                }
-            }
-        };
-        auto copy_late = [&](int c, bool odd) {
-            T* Vd = odd ? Vs1 : Vs0;
-            f32x2* Rd = odd ? Rs1 : Rs0;
-            const int64_t s = chunk_s(c);
-            const int L = chunk_L(c);
-            T* Pd = odd ? Pb1 : Pb0;
-            T* Td = odd ? Tb1 : Tb0;
-            const auto rp = rsrc(Pf, ((int64_t)c * Nv + h) * TFRAG, 2, TFRAG * 2);
-            const auto rt = rsrc(Tf, ((int64_t)c * Nv + h) * TFRAG, 2, TFRAG * 2);
-            constexpr int NTP = MODE == kFull ? NTCP : 0;    // T pieces through LDS
-#pragma unroll
-            for (int m = 0; m < (NTCP + NTP + 3 + 3) / 4; ++m) {
-                const int u = w + 4 * m;
-                if (u < NTCP) {                              // score piece
-                    if constexpr (want_o) buffer_to_lds16(rp, Pd + u * FRAG, (u * 64 + lane) * 16);
-                } else if (u < NTCP + NTP) {                 // T piece
-                    buffer_to_lds16(rt, Td + (u - NTCP) * FRAG, ((u - NTCP) * 64 + lane) * 16);
-                } else if (u < NTCP + NTP + 2) {             // V rows 32 vh .. 32 vh + 31 (16 columns)
-                    // transition pass: an empty range, so every row reads as zero
-                    const int vh = u - NTCP - NTP;
-                    const uint32_t vbytes = (trans || L <= 0) ? 0u : (uint32_t)((L - 1) * Nv * DV + 16) * 2u;
-                    buffer_to_lds16(rsrc(trans ? k : v, trans ? 0 : (s * Nv + h) * DV + nb * 16, 2, vbytes),
-                                    Vd + vh * 512, ((32 * vh + (lane >> 1)) * Nv * DV + 8 * (lane & 1)) * 2);
-                } else if (u == NTCP + NTP + 2 && lane < 32) {   // R (512 bytes: two positions per lane)
-                    buffer_to_lds16(rsrc(R, ((int64_t)c * Nv + h) * kChunk, 8, kChunk * 8), Rd, lane * 16);
-                }
-            }
-        };
-        constexpr int MEB = MCE / 2;                     // early copies issued in phase B (rest in C)
-        copy_early(c0, false, 0, MCE);
-        copy_late(c0, false);
-        wait_vmem();
-        if (c0 + 1 < c1) copy_early(c0 + 1, true, 0, MCE);
-        lds_barrier();
-        for (int c = c0; c < c1; ++c) {
-            const bool odd = (c - c0) & 1;
-            if (c + 1 < c1) copy_late(c + 1, !odd);
-            lds_barrier();                                                          // barrier 1
-            if (c + 2 < c1) copy_early(c + 2, odd, 0, MEB);
-            lds_barrier();                                                          // barrier 2
-            if (c + 2 < c1) {
-                copy_early(c + 2, odd, MEB, MCE);
-                // chunk c+1 has landed; chunk c+2's early list (its K blocks only, without o) may be in flight
-                if constexpr (want_o) wait_vmem_but<MCE>();
-                else wait_vmem_but<MEB>();
-            } else {
-                wait_vmem();
-            }
-            lds_barrier();                                                          // barrier 3
-        }
-        return;
-    }
-
-    // ============================================================ output waves
-    // The output of chunk c is formed in phase A of step c+1 (after the loop for
-    // the last chunk): its operands V_new and Q S_in stay in the exchange buffers
-    // until phase B of step c+1, and the score pairs and exp(G) are taken into
-    // registers in phase B of step c, before the copy waves overwrite that LDS
-    // half with chunk c+2.
-    if constexpr (!want_o) return;                   // (no output waves in this mode)
-    const int w = wv - 4;
-    const int ntp = (w >> 1) + 1;
-    const int ob = out_f32 ? 4 : 2;
-    int o_off[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o_off[j] = ((w * 16 + 4 * qd + j) * Nv * DV + r) * ob;
-    const int pbase = (w == 0) ? 0 : (w == 1 ? 1 : (w == 2 ? 2 : 4));
-    Split<T> pa[2];                                  // score pairs of the pending chunk
-    float ex[4];                                     // exp(G) of its rows
-    f32x4 ofin;                                      // finished output rows, held until phase C
-    auto output = [&](int c) {                       // O = scale [exp(G) Q S_in + P V_new], positions 16w..
-        Split<T> vn[2];
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp)
-            if (tp < ntp) vn[tp] = load_split(Vb, tp);
-        const f32x4 qs = QSx[w][lane];
-        f32x4 out, ol = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) out[j] = ex[j] * qs[j];
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp) {
-            if (tp < ntp) {
-                out = mfma_pair(pa[tp].hi, vn[tp].hi, out);
-                ol = mfma_pair(pa[tp].lo, vn[tp].hi, ol);
-                ol = mfma_pair(pa[tp].hi, vn[tp].lo, ol);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ofin[j] = scale * (out[j] + ol[j]);
-    };
-    auto store_out = [&](int c) {
-        const int64_t s = chunk_s(c);
-        const int L = chunk_L(c);
-        const auto ro = rsrc(o, (s * Nv + h) * DV + nb * 16, ob, L > 0 ? (uint32_t)(((L - 1) * Nv * DV + 16) * ob) : 0u);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {                   // rows past the chunk end fall outside ro
-            const float val = ofin[j];
-            if (out_f32) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), ro, o_off[j], 0, 0);
-            else __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, to_t<T>(val)), ro,
-                                                       o_off[j], 0, 0);
-        }
-    };
-    lds_barrier();
-    for (int c = c0; c < c1; ++c) {
-        const bool odd = (c - c0) & 1;
-
-        // ---- A: output of the previous chunk
-        if (c > c0) output(c - 1);
-        lds_barrier();                                                              // barrier 1
-
-        // ---- B: this chunk's score pairs and exp(G) into registers
-        const T* Pbb = odd ? Pb1 : Pb0;
-        const f32x2* Rsb = odd ? Rs1 : Rs0;
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp) {
-            if (tp < ntp) {
-                pa[tp].hi = load_frag<T>(&Pbb[(pbase + tp) * 2 * FRAG], lane);
-                pa[tp].lo = load_frag<T>(&Pbb[(pbase + tp) * 2 * FRAG + FRAG], lane);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ex[j] = Rsb[w * 16 + 4 * qd + j].x;
-        lds_barrier();                                                              // barrier 2
-
-        // ---- C: store the previous chunk's output. Phase C is the output waves'
-        // idlest phase; issued in phase A the stores queue behind the copy
-        // waves' tile loads and lengthen that phase.
-        if (c > c0) store_out(c - 1);
-        lds_barrier();                                                              // barrier 3
-    }
-    output(c1 - 1);
-    store_out(c1 - 1);
-}
 // ============================================================ segment-parallel state passing
 // The state recursion is affine in the state: over any run of chunks,
 //   S_end = M S_start + S_loc,
@@ -1409,15 +776,35 @@ __global__ __launch_bounds__(256) void k_segment_scan(const int32_t* __restrict_
 }
 
 // ============================================================ launchers
+template <int DK, int DV>
+static hipError_t scan_dims(const LaunchArgs& a) {
+    k_segment_scan<DK, DV><<<dim3(a.N, a.Nv, DV / 16), 256, 0, a.stream>>>(a.seq_seg, a.S0, a.Sloc, a.Mseg, a.Nv,
+                                                                       a.Sstart, a.ST);
+    return hipGetLastError();
+}
+
+hipError_t launch_segment_scan(const LaunchArgs& a) {
+#define GDR_CASE(DKv, DVv) \
+    if (a.dk == DKv && a.dv == DVv) return scan_dims<DKv, DVv>(a);
+    GDR_CASE(32, 32) GDR_CASE(32, 64) GDR_CASE(32, 128)
+    GDR_CASE(64, 32) GDR_CASE(64, 64) GDR_CASE(64, 128)
+    GDR_CASE(128, 32) GDR_CASE(128, 64) GDR_CASE(128, 128)
+#undef GDR_CASE
+    return hipErrorInvalidValue;
+}
+
+// bf16 inputs with C = 64 take the fp16 path (gdr_fp16.hip) after the chunk
+// and segment tables; everything else, and the debug entry point, runs the
+// five kernels. For the debug entry point on a bf16 C = 64 problem, k_prep
+// runs as well, so that its T, score block and decay rows can be copied out.
 template <typename T, int DK, int DV, int C>
 static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
     hipStream_t st = a.stream;
     auto mark = [&](int i) { if (ev) (void)hipEventRecord(ev[i], st); };
     const int32_t cap = a.nt_cap;
     const int32_t NT = a.nt;
-    constexpr bool kFused = std::is_same<T, bf16>::value && C == 64;
+    constexpr bool kFp16 = std::is_same<T, bf16>::value && C == 64;
     constexpr int NTHR = 64 * (C / 16);        // one wavefront per 16-row block of a chunk
-    const bool fused = kFused && !a.reference;
     mark(0);
     k_chunk_table<<<1, 1024, 0, st>>>(a.cu_dev, a.T_row, a.N, a.Ttot, cap, C, a.chunk_seq, a.chunk_start,
                                       a.chunk_len, a.seq_first);
@@ -1425,68 +812,53 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
     if (segmented)
         k_segment_table<<<1, 1024, 0, st>>>(a.seq_first, a.N, a.seg_chunks, a.nseg, a.seg_first, a.seq_seg);
     mark(1);
+    if constexpr (kFp16) {
+        if (!a.reference) return launch_fp16_path(a, ev);
+        if (a.T16) {
+            LaunchArgs b = a;
+            b.prep_only = true;
+            b.nseg = 0;
+            const hipError_t e = launch_fp16_path(b, nullptr);
+            if (e != hipSuccess) return e;
+        }
+    }
     if (NT > 0) {
-        k_gate_cumsum<C><<<dim3(NT, (a.Nv + 256 / C - 1) / (256 / C)), 256, 0, st>>>(
-            a.g, a.chunk_start, a.chunk_len, NT, a.Nv, a.G, fused ? (f32x2*)a.R : nullptr);
+        k_gate_cumsum<C><<<dim3(NT, (a.Nv + 256 / C - 1) / (256 / C)), 256, 0, st>>>(a.g, a.chunk_start, a.chunk_len,
+                                                                                   NT, a.Nv, a.G);
     }
     mark(2);
     if (NT > 0)
-        k_build_solve<T, DK, C><<<dim3(NT, a.Nk), NTHR, 0, st>>>((const T*)a.k, (const T*)a.q, a.beta, a.beta_f32, a.G,
-                                                            a.chunk_start, a.chunk_len, a.Nk, a.Nv,
-                                                            fused ? nullptr : (float*)a.A, (T*)a.Tf,
-                                                            fused ? (T*)a.Pf : nullptr);
+        k_build_solve<T, DK, C><<<dim3(NT, a.Nk), NTHR, 0, st>>>((const T*)a.k, a.beta, a.beta_f32, a.G,
+                                                                  a.chunk_start, a.chunk_len, a.Nk, a.Nv,
+                                                                  (float*)a.A);
     mark(3);
-    if (NT > 0 && !fused)
+    if (NT > 0)
         k_wu<T, DK, DV, C><<<dim3(NT, a.Nk), NTHR, 0, st>>>((const T*)a.k, (const T*)a.v, a.beta, a.beta_f32, a.G,
                                                        (const float*)a.A, a.chunk_start, a.chunk_len, a.Nk, a.Nv,
                                                        (float*)a.W, (float*)a.U, (T*)a.KT);
     mark(4);
     if (segmented) {
         // local end states from zero, transitions from I with V = 0, the scan,
-        // then the pass from the entering states that writes the output
-        const dim3 gs(a.nseg, a.Nv, DV / 16), gm(a.nseg, a.Nv, DK / 16), gn(a.N, a.Nv, DV / 16);
-        if constexpr (kFused) {
-            if (fused) {
-                const bf16 *q = (const bf16*)a.q, *k = (const bf16*)a.k, *v = (const bf16*)a.v;
-                const bf16 *Tf = (const bf16*)a.Tf, *Pf = (const bf16*)a.Pf;
-                const f32x2* R = (const f32x2*)a.R;
-                k_state_output<DK, DV, kSegment><<<dim3(a.nseg, a.Nv, DV / 16 + DK / 16), 512, 0, st>>>(
-                    q, k, v, R, Tf, Pf, nullptr, a.chunk_start, a.chunk_len, a.seg_first, a.Nk, a.Nv, a.scale,
-                    a.out_f32, nullptr, a.Sloc, a.Mseg);
-                k_segment_scan<DK, DV><<<gn, 256, 0, st>>>(a.seq_seg, a.S0, a.Sloc, a.Mseg, a.Nv, a.Sstart, a.ST);
-                k_state_output<DK, DV, kFull><<<gs, 768, 0, st>>>(
-                    q, k, v, R, Tf, Pf, a.Sstart, a.chunk_start, a.chunk_len, a.seg_first, a.Nk, a.Nv, a.scale,
-                    a.out_f32, a.o, nullptr, nullptr);
-            }
-        }
-        if (!fused) {
-            const float *W = (const float*)a.W, *U = (const float*)a.U;
-            const T* KT = (const T*)a.KT;
-            k_state<T, DK, DV, C><<<gs, 64, 0, st>>>(W, U, KT, a.G, nullptr, 0, a.chunk_start, a.chunk_len, a.seg_first,
-                                                  a.Nk, a.Nv, nullptr, nullptr, a.Sloc);
-            k_state<T, DK, DK, C><<<gm, 64, 0, st>>>(W, nullptr, KT, a.G, nullptr, 1, a.chunk_start, a.chunk_len,
-                                                  a.seg_first, a.Nk, a.Nv, nullptr, nullptr, a.Mseg);
-            k_segment_scan<DK, DV><<<gn, 256, 0, st>>>(a.seq_seg, a.S0, a.Sloc, a.Mseg, a.Nv, a.Sstart, a.ST);
-            k_state<T, DK, DV, C><<<gs, 64, 0, st>>>(W, U, KT, a.G, a.Sstart, 0, a.chunk_start, a.chunk_len,
-                                                  a.seg_first, a.Nk, a.Nv, (float*)a.H, (float*)a.VN, nullptr);
-        }
+        // then the pass from the entering states that writes H and V_new
+        const dim3 gs(a.nseg, a.Nv, DV / 16), gm(a.nseg, a.Nv, DK / 16);
+        const float *W = (const float*)a.W, *U = (const float*)a.U;
+        const T* KT = (const T*)a.KT;
+        k_state<T, DK, DV, C><<<gs, 64, 0, st>>>(W, U, KT, a.G, nullptr, 0, a.chunk_start, a.chunk_len, a.seg_first,
+                                              a.Nk, a.Nv, nullptr, nullptr, a.Sloc);
+        k_state<T, DK, DK, C><<<gm, 64, 0, st>>>(W, nullptr, KT, a.G, nullptr, 1, a.chunk_start, a.chunk_len,
+                                              a.seg_first, a.Nk, a.Nv, nullptr, nullptr, a.Mseg);
+        const hipError_t e = launch_segment_scan(a);
+        if (e != hipSuccess) return e;
+        k_state<T, DK, DV, C><<<gs, 64, 0, st>>>(W, U, KT, a.G, a.Sstart, 0, a.chunk_start, a.chunk_len,
+                                              a.seg_first, a.Nk, a.Nv, (float*)a.H, (float*)a.VN, nullptr);
     } else if (a.N > 0) {
-        if constexpr (kFused) {
-            if (fused) {
-                k_state_output<DK, DV, kFull><<<dim3(a.N, a.Nv, DV / 16), 768, 0, st>>>(
-                    (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const f32x2*)a.R,
-                    (const bf16*)a.Tf, (const bf16*)a.Pf, a.S0,
-                    a.chunk_start, a.chunk_len, a.seq_first, a.Nk, a.Nv, a.scale, a.out_f32, a.o, a.ST, nullptr);
-            }
-        }
-        if (!fused)
-            k_state<T, DK, DV, C><<<dim3(a.N, a.Nv, DV / 16), 64, 0, st>>>((const float*)a.W, (const float*)a.U,
-                                                                       (const T*)a.KT, a.G, a.S0, 0, a.chunk_start,
-                                                                       a.chunk_len, a.seq_first, a.Nk, a.Nv,
-                                                                       (float*)a.H, (float*)a.VN, a.ST);
+        k_state<T, DK, DV, C><<<dim3(a.N, a.Nv, DV / 16), 64, 0, st>>>((const float*)a.W, (const float*)a.U,
+                                                                   (const T*)a.KT, a.G, a.S0, 0, a.chunk_start,
+                                                                   a.chunk_len, a.seq_first, a.Nk, a.Nv,
+                                                                   (float*)a.H, (float*)a.VN, a.ST);
     }
     mark(5);
-    if (NT > 0 && !fused && a.o)
+    if (NT > 0 && a.o)
         k_output<T, DK, DV, C><<<dim3(NT, a.Nv), NTHR, 0, st>>>((const T*)a.q, (const T*)a.k, a.G, (const float*)a.H,
                                                            (const float*)a.VN, a.chunk_start, a.chunk_len, a.Nk, a.Nv,
                                                            a.scale, a.out_f32, a.o);

@@ -26,10 +26,11 @@ struct LaunchArgs {
     int32_t *chunk_seq, *chunk_start, *chunk_len, *seq_first;
     float* G;
     void *A, *W, *U, *KT, *H, *VN;   // reference-pipeline intermediates
-    void* Tf;                        // T = A diag(beta) fragments (fused pipeline)
-    void* Pf;                        // score block (Q K^T) (.) D fragments (fused pipeline)
-    void* R;                         // decay factors exp(G), exp(G_last - G), chunk-major (fused pipeline)
+    void* T16;                       // T = A diag(beta), fp16 pair fragments [cap][Nv][6][64][8] (fp16 path)
+    void* P16;                       // score block (Q K^T) (.) D, same layout (fp16 path)
+    float* R16;                      // decay rows exp(G), exp(G_last - G): [cap][Nv][2][64] (fp16 path)
     bool reference;                  // run the five separate kernels even for bf16
+    bool prep_only;                  // fp16 path: run k_prep only (debug copies of T, P, R)
     // segment-parallel state passing (nseg == 0: one serial pass per sequence)
     int32_t nseg;                    // segment-table capacity: the host's count of segments
     int32_t seg_chunks;              // chunks per segment

@@ -279,11 +279,18 @@ gdr_status_t gdr_chunk_bwd(const gdr_problem_t* problem,
  *   H    [NT][Nv][dv/16 nb][dk/32 kp] fp32 pair fragments of the chunk's
  *                                     entering state transposed (rows dv, m = dk)
  *   VN   [NT][Nv][dv/16 nb][NTP tp] fp32 pair fragments of V_new^T (rows dv, m = position)
- *   T    [NT][Nv][6 pairs][2 hi/lo] bf16 pair fragments of T = A diag(beta)
- *        (rows i, m = position) for the blocks (tb, tp) = (0,0) (1,0) (2,0)
- *        (2,1) (3,0) (3,1); T = hi + lo. bf16 inputs with C = 64 only (NULL
- *        otherwise).
- * Chunk positions past the end of a sequence hold zeros in W, U, KT and VN.
+ *   T    [NT][Nv][6 pairs] fp16 pair fragments of T = A diag(beta) (rows i,
+ *        m = position) for the blocks (tb, tp) = (0,0) (1,0) (2,0) (2,1)
+ *        (3,0) (3,1), each value rounded once from fp32 (the operand of the
+ *        production pass). bf16 inputs with C = 64 only (NULL otherwise).
+ *   P    [NT][Nv][6 pairs] fp16 pair fragments of the score block
+ *        P = (Q K^T) (.) D, D_ij = exp(G_i - G_j) for j <= i (rows i, m = j),
+ *        same blocks and conditions as T.
+ *   R    [NT][Nv][2][C] fp32: exp(G_i) and exp(G_last - G_i) per chunk
+ *        position (zero past the chunk end); same conditions as T.
+ * Chunk positions past the end of a sequence hold zeros in W, U, KT, VN, T,
+ * P and R. The decay matrix D itself is not copied out: it is a function of
+ * G alone (ChunkGatedDeltaRule page, formula (5)), so a test forms it from G.
  */
 typedef struct {
     float* G;
@@ -294,6 +301,8 @@ typedef struct {
     void* H;
     void* VN;
     void* T;
+    void* P;
+    float* R;
     int64_t num_chunks;     /* out: NT */
 } gdr_intermediates_t;
 

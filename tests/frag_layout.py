@@ -90,9 +90,10 @@ T_PAIRS = ((0, 0), (1, 0), (2, 0), (2, 1), (3, 0), (3, 1))
 
 
 def T_natural(Tf):
-    """[NT, Nv, 6, 2 (hi, lo), 64, 8] -> T = hi + lo as [NT, Nv, 64, 64]
-    (rows and columns = chunk positions; blocks not stored are zero)."""
-    X = unpack_pair(np.asarray(Tf, dtype=np.float64).sum(axis=3))   # [NT, Nv, 6, 16, 32]
+    """[NT, Nv, 6, 64, 8] fp16 pair fragments -> [NT, Nv, 64, 64] (rows and
+    columns = chunk positions; blocks not stored are zero). Used for T = A
+    diag(beta) and for the score block P, which share the layout."""
+    X = unpack_pair(np.asarray(Tf, dtype=np.float64))                # [NT, Nv, 6, 16, 32]
     NT, Nv = X.shape[:2]
     out = np.zeros((NT, Nv, 64, 64))
     for p, (tb, tp) in enumerate(T_PAIRS):

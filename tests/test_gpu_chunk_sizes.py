@@ -69,14 +69,20 @@ def test_every_head_dim_pair_C32_bf16(dk, dv):
 
 
 def test_chunk_sizes_agree():
-    """C = 16, 32 and 64 give the same result up to fp32 rounding (config 2)."""
+    """C = 16, 32 and 64 give the same result (config 2): C = 16 and 32 run the
+    five kernels at fp32-level accuracy and agree to fp32 rounding; C = 64 runs
+    the production path with fp16 operands and agrees to a few 1e-3 of rms."""
     inp = synth.generate(synth.WORKLOADS[2], seed=2)
     outs = {C: run_gpu(inp, out_f32=True, chunk_size=C) for C in (16, 32, 64)}
+    eo = rel_err(f64(outs[16][0]), f64(outs[32][0]))
+    es = rel_err(f64(outs[16][1]), f64(outs[32][1]))
+    print("C=16 vs C=32: o %.2e S_T %.2e" % (eo, es), flush=True)
+    assert eo < 1e-4 and es < 1e-4
     for C in (16, 32):
         eo = rel_err(f64(outs[C][0]), f64(outs[64][0]))
         es = rel_err(f64(outs[C][1]), f64(outs[64][1]))
         print("C=%d vs C=64: o %.2e S_T %.2e" % (C, eo, es), flush=True)
-        assert eo < 1e-4 and es < 1e-4
+        assert eo < 1e-2 and es < 1e-2
 
 
 def test_segmented_at_chunk_size_32():

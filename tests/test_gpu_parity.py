@@ -230,13 +230,28 @@ def test_intermediates_match_chunked_oracle(name, w, seed, C):
     errs["S_T"] = rel_err(cpu(res["S_T"]), ref["S_T"])
     errs["o"] = rel_err(cpu(res["o"]).reshape(ref["o"].shape), ref["o"])
     if res["T"] is not None:
-        # T = A diag(beta) fragments (input of the fused state pass), natural per chunk
+        # k_prep's outputs (inputs of the production pass), natural per chunk:
+        # T = A diag(beta), the score block P = (Q K^T) (.) D, the decay rows
         Tn = fl.T_natural(res["T"].detach().cpu().float().numpy())
-        T_ref = np.zeros_like(Tn)
+        Pn = fl.T_natural(res["P"].detach().cpu().float().numpy())
+        Rn = res["R"].detach().cpu().double().numpy()
+        T_ref, P_ref, R_ref = np.zeros_like(Tn), np.zeros_like(Pn), np.zeros_like(Rn)
+        G = ref["G"]
         for c, (_, s0, Lc) in enumerate(chunks):
             A_c = ref["A"][s0:s0 + Lc, :, :Lc].transpose(1, 0, 2)          # [Nv, i, m]
             T_ref[c, :, :Lc, :Lc] = A_c * x["beta"][s0:s0 + Lc].T[:, None, :]
+            Gc = G[s0:s0 + Lc].T                                             # [Nv, Lc]
+            D = np.tril(np.exp(Gc[:, :, None] - Gc[:, None, :]))
+            grp = x["v"].shape[1] // x["q"].shape[1]
+            Qc = x["q"][s0:s0 + Lc][:, np.arange(Gc.shape[0]) // grp]        # [Lc, Nv, dk]
+            Kc = x["k"][s0:s0 + Lc][:, np.arange(Gc.shape[0]) // grp]
+            P_ref[c, :, :Lc, :Lc] = np.einsum("inq,jnq->nij", Qc, Kc) * D
+            R_ref[c, :, 0, :Lc] = np.exp(Gc)
+            R_ref[c, :, 1, :Lc] = np.exp(Gc[:, -1:] - Gc)
+        # fp16 fragments: one rounding of each value (relative 2^-11)
         errs["T"] = rel_err(Tn, T_ref)
+        errs["P"] = rel_err(Pn, P_ref)
+        errs["R"] = rel_err(Rn, R_ref)
     print(name, {k: "%.2e" % v for k, v in errs.items()}, flush=True)
     for key, e in errs.items():
         assert e <= tol, (name, key, e)
@@ -244,12 +259,14 @@ def test_intermediates_match_chunked_oracle(name, w, seed, C):
 
 @pytest.mark.parametrize("name,w,seed,C", KERNEL_CASES[:2], ids=[c[0] for c in KERNEL_CASES[:2]])
 def test_fused_path_matches_reference_path(name, w, seed, C):
-    """The production call (state pass and output fused) and the debug call
-    (five separate kernels) compute the same result to fp32-level accuracy."""
+    """The production call (fp16 matrix-core operands) and the debug call (five
+    separate kernels, fp32-level operands) compute the same result; they differ
+    by the production path's operand roundings (a few 1e-3 of rms), well inside
+    the 2e-2 bound each meets against the oracle."""
     inp = synth.generate(w, seed=seed)
     o1, S1 = run_gpu(inp, out_f32=True)
     res = run_gpu(inp, debug=True, out_f32=True)
     eo = rel_err(o1.cpu().double().numpy(), res["o"].cpu().double().numpy())
     es = rel_err(S1.cpu().double().numpy(), res["S_T"].cpu().double().numpy())
     print(name, "fused vs reference: o %.2e S_T %.2e" % (eo, es), flush=True)
-    assert eo < 1e-3 and es < 1e-3
+    assert eo < 1e-2 and es < 1e-2

@@ -79,8 +79,11 @@ def test_segmented_parity(case):
     print(msg, flush=True)
     assert np.all(np.isfinite(f64(o))) and np.all(np.isfinite(f64(S)))
     assert eo <= tol and es <= tol
-    # the two passes compute the same fp32-level result in a different order
-    assert ds_o <= 1e-4 and ds_s <= 1e-4
+    # the two passes compute the same result in a different order: fp32-level
+    # for fp32 inputs; for bf16 both round their derived operands to fp16 (the
+    # segment transitions included), so they agree to a few 1e-3 of rms
+    agree = 1e-4 if w.dtype == "f32" else 1e-2
+    assert ds_o <= agree and ds_s <= agree
 
 
 def run_serial(inp):
@@ -124,7 +127,7 @@ def test_full_size_varlen_segmented_matches_serial():
     """64 variable-length sequences (1 to 8192 tokens), Nk = 16, Nv = 32,
     dk = dv = 128, bf16, from a random state, at full size: the automatic
     choice keeps the serial pass (same bits); forced 16-chunk segments give
-    the serial result to fp32 rounding."""
+    the serial result up to the fp16 operand roundings of both passes."""
     inp = synth.generate(synth.WORKLOADS[4], seed=4)
     o_s, S_s = run_serial(inp)
     o_a, S_a = run(inp, 0)
@@ -132,4 +135,4 @@ def test_full_size_varlen_segmented_matches_serial():
     o_f, S_f = run(inp, 16)
     eo, es = rel_err(f64(o_f), f64(o_s)), rel_err(f64(S_f), f64(S_s))
     print("cfg4 segmented (16 chunks) vs serial: o %.2e S_T %.2e" % (eo, es), flush=True)
-    assert eo <= 1e-4 and es <= 1e-4
+    assert eo <= 1e-2 and es <= 1e-2
