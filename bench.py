@@ -15,6 +15,7 @@ bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -30,38 +31,57 @@ sys.path.insert(0, ROOT)
 from chunkwise_gated_delta_local_amd import api, synth  # noqa: E402
 
 METRIC = "fwd tokens/s at Hv=32,dk=dv=128,T=64k bf16; % of MFMA/HBM roofline"
-HBM_PEAK_GBS = 8000.0
+HBM_PEAK_GBS = 8000.0                   # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0          # MI355X dense bf16 / fp16 matrix cores, published
+FP32_MFMA_PEAK_TFLOPS = 157.3
 KERNEL_SOURCES = ("chunkwise_gated_delta_local_amd/csrc/gdr_kernels.hip",
+                  "chunkwise_gated_delta_local_amd/csrc/gdr_fp16.hip",
                   "chunkwise_gated_delta_local_amd/csrc/gdr_recurrent.hip",
                   "chunkwise_gated_delta_local_amd/csrc/gdr_device.hpp")
 STAGE_KERNELS = ("k_chunk_table", "k_gate_cumsum", "k_build_solve", "k_wu", "k_state", "k_output")
-FUSED_STAGE_KERNELS = ("k_chunk_table", "k_gate_cumsum", "k_build_solve", "(fused)", "k_state_output", "(fused)")
-T_FRAG_BYTES = 6 * 2 * 512 * 2          # T = A diag(beta) split fragments per (chunk, value head)
+FP16_STAGE_KERNELS = ("k_chunk_table", "(none)", "k_prep", "(none)", "k_chunk16", "(none)")
+FRAG16_BYTES = 6 * 512 * 2              # six fp16 pair fragments per (chunk, value head): T or the score block
+DECAY_ROW_BYTES = 2 * 64 * 4            # exp(G), exp(G_last - G) per (chunk, value head)
 
 
-def stage_algorithmic_bytes(w: synth.Workload, Ttot: int, N: int, NT: int, out_bytes: int,
-                            s0: bool) -> dict:
-    """Bytes each kernel must move by its own inputs and outputs: every tensor it
-    reads read once, every tensor it writes written once, in its stored type
-    (intermediates of the pipeline included: T and the score block are 6 split
-    bf16 pair fragments per (chunk, value head), the decay factors 8 bytes per
-    position)."""
+def method_bytes_per_token(w: synth.Workload, out_bytes: int) -> int:
+    """Bytes the method itself must move per token (all heads): q, k, v, g and
+    beta read once, o written once, in their stored types. The initial and
+    final states are counted apart (per sequence, not per token)."""
+    es = 2 if w.dtype == "bf16" else 4
+    g_bytes = w.Nv * 4 if w.gated else 0
+    return 2 * w.Nk * w.dk * es + w.Nv * w.dv * es + g_bytes + w.Nv * es + w.Nv * w.dv * out_bytes
+
+
+def method_flops_per_token(w: synth.Workload, C: int = 64) -> float:
+    """Floating-point operations of the chunk algorithm per token (all value
+    heads, 2 per multiply-add, full chunks): 6 dk dv for the state products
+    (W S, K^T V_new, Q S), 2C(3dk + 2dv) for the intra-chunk products (K K^T,
+    Q K^T, W, and U, the score block times V_new) and (2/3) C^2 for the
+    triangular solve."""
+    return w.Nv * (6.0 * w.dk * w.dv + 2.0 * C * (3 * w.dk + 2 * w.dv) + (2.0 / 3.0) * C * C)
+
+
+def stage_io_bytes(w: synth.Workload, Ttot: int, N: int, NT: int, out_bytes: int, s0: bool) -> dict:
+    """Bytes each kernel moves by its own inputs and outputs (every tensor it
+    reads read once, every tensor it writes written once, in its stored type),
+    the pipeline's intermediates included (T and the score block as fp16
+    fragments, the decay rows). Reported beside the method's bytes."""
     es = 2 if w.dtype == "bf16" else 4
     Nv, Nk, dk, dv = w.Nv, w.Nk, w.dk, w.dv
     tv = Ttot * Nv                      # token-heads (value heads)
     tk = Ttot * Nk                      # token-heads (q/k heads)
     beta_b = es
     state = N * Nv * dk * dv * 4
-    frag = NT * Nv * T_FRAG_BYTES       # one six-pair split fragment set per (chunk, value head)
-    rfac = NT * Nv * 64 * 8             # decay factors, chunk-major
-    if w.dtype == "bf16":               # fused path
+    if w.dtype == "bf16":               # fp16 path
+        frag = NT * Nv * FRAG16_BYTES
+        rows = NT * Nv * DECAY_ROW_BYTES
         return {
             "k_chunk_table": 4 * (N + 1) + 16 * NT,
-            "k_gate_cumsum": tv * (4 + 4) + rfac,                                        # g in; G, R out
-            "k_build_solve": 2 * tk * dk * es + tv * (beta_b + 4) + 2 * frag,           # k, q, beta, G in; T, P out
-            "k_state_output": 2 * tk * dk * es + tv * dv * es + rfac + 2 * frag         # q, k, v, R, T, P in
-                              + tv * dv * out_bytes + state * (2 if s0 else 1),          # o, S_T out (S0 in)
-            "(fused)": 0,
+            "k_prep": 2 * tk * dk * es + tv * (beta_b + 4) + 2 * frag + rows,        # k, q, beta, g in; T, P, R out
+            "k_chunk16": 2 * tk * dk * es + tv * dv * es + rows + 2 * frag             # q, k, v, R, T, P in
+                         + tv * dv * out_bytes + state * (2 if s0 else 1),             # o, S_T out (S0 in)
+            "(none)": 0,
         }
     return {
         "k_chunk_table": 4 * (N + 1) + 16 * NT,
@@ -74,6 +94,54 @@ def stage_algorithmic_bytes(w: synth.Workload, Ttot: int, N: int, NT: int, out_b
         "k_output": 2 * tk * dk * es + tv * 4 + NT * Nv * dk * dv * 4 + tv * dv * 4  # q, k, G, H, V_new in
                     + tv * dv * out_bytes,                                    # o out
     }
+
+
+def measure_peaks(repeats: int = 5) -> dict:
+    """The two roofline ceilings measured on this GPU with the library's probe
+    kernels (include/gdr_peaks.h): a 1 GiB streaming copy (bytes read +
+    written over time) and a loop of independent bf16 16x16x32 matrix-core
+    products on every SIMD. Best of `repeats` timed launches after a warm-up."""
+    lib = api.load_library()
+    stream = torch.cuda.current_stream()
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def best(launch):
+        launch()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(repeats):
+            ev[0].record()
+            launch()
+            ev[1].record()
+            torch.cuda.synchronize()
+            times.append(ev[0].elapsed_time(ev[1]))
+        return min(times)
+
+    copy_blocks = 256 * 8
+
+    def copy():
+        assert lib.gdr_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                 ctypes.c_size_t(nbytes), copy_blocks, ctypes.c_void_p(stream.cuda_stream)) == 0
+    t_copy = best(copy)
+    if not torch.equal(dst[:1024], src[:1024]):
+        raise RuntimeError("copy probe wrote wrong values")
+    del src, dst
+    mfma_blocks, iters = 256 * 4, 4096
+    out = torch.empty(mfma_blocks * 256, dtype=torch.float32, device="cuda:0")
+
+    def mfma():
+        assert lib.gdr_peak_mfma(ctypes.c_void_p(out.data_ptr()), mfma_blocks, iters,
+                                 ctypes.c_void_p(stream.cuda_stream)) == 0
+    t_mfma = best(mfma)
+    flops = lib.gdr_peak_mfma_flops(mfma_blocks, iters)
+    return {"hbm_GBps": 2 * nbytes / (t_copy * 1e-3) / 1e9,
+            "mfma_bf16_TFLOPs": flops / (t_mfma * 1e-3) / 1e12,
+            "how": "gdr_peak_copy: 1 GiB read + 1 GiB written by %d workgroups (16-byte non-temporal accesses); "
+                   "gdr_peak_mfma: %d workgroups x 4 wavefronts x %d x 8 independent "
+                   "v_mfma_f32_16x16x32_bf16; best of %d" % (copy_blocks, mfma_blocks, iters, repeats)}
 
 
 def source_digest() -> str:
@@ -110,37 +178,49 @@ def counter_traffic(kernel: str, workload: str):
         return None
 
 
-def cpu_baseline(inp: dict, target_seconds: float) -> dict:
-    """The fp64 token-recurrence oracle on the host cores, on the first Ts tokens
-    (all heads) of the same workload; Ts is calibrated to about target_seconds."""
+def cpu_baseline(inp: dict, target_seconds: float, threads: int = 0) -> dict:
+    """The fp64 token-recurrence oracle on the host cores over a bounded sample
+    of the same workload: the first Ts tokens of every sequence (all heads),
+    with Ts calibrated to about target_seconds (the whole workload when it
+    fits). threads = 0: every core this process may run on."""
     from oracle import recurrence
 
     w = inp["workload"]
-    T = inp["q"].shape[1]
-    threads = len(os.sched_getaffinity(0))
-
-    def sample(ts):
-        f = lambda t: None if t is None else t[0, :ts].double().numpy()
-        return (f(inp["q"]), f(inp["k"]), f(inp["v"]), f(inp["beta"]), f(inp["g"]))
+    threads = threads or len(os.sched_getaffinity(0))
+    B, T = inp["q"].shape[:2]
+    flat = lambda t: None if t is None else t.reshape((B * T,) + tuple(t.shape[2:]))
+    q, k, v, beta, g = (flat(inp[n]) for n in ("q", "k", "v", "beta", "g"))
+    if inp["cu_seqlens"] is not None:
+        cu = inp["cu_seqlens"].numpy().astype(np.int64)
+    else:
+        cu = np.arange(B + 1, dtype=np.int64) * T
+    lens = np.diff(cu)
+    S0 = None if inp["S0"] is None else inp["S0"].double().numpy()
 
     def run(ts):
-        q, k, v, b, g = sample(ts)
+        take = np.minimum(lens, ts)
+        idx = np.concatenate([np.arange(cu[n], cu[n] + take[n]) for n in range(len(lens))])
+        sub = lambda t: None if t is None else t[torch.from_numpy(idx)].double().numpy()
+        cs = np.concatenate([[0], np.cumsum(take)])
+        args = (sub(q), sub(k), sub(v), sub(beta), sub(g))
         t0 = time.perf_counter()
-        recurrence(q, k, v, b, g, inp["scale"], None, np.array([0, ts]), threads=threads)
-        return time.perf_counter() - t0
+        recurrence(*args, inp["scale"], S0, cs, threads=threads)
+        return time.perf_counter() - t0, int(take.sum())
 
-    probe = min(256, T)
-    dt = run(probe)
-    ts = int(min(T, max(probe, probe * target_seconds / max(dt, 1e-6))))
-    ts = max(64, (ts // 64) * 64) if ts < T else T
-    dt = run(ts)
+    longest = int(lens.max()) if len(lens) else 0
+    probe = min(256, longest)
+    dt, _ = run(probe)
+    ts = int(min(longest, max(probe, probe * target_seconds / max(dt, 1e-6))))
+    ts = max(64, (ts // 64) * 64) if ts < longest else longest
+    dt, tokens = run(ts)
     return {
-        "value": ts / dt,
+        "value": tokens / dt,
         "unit": "tokens/s",
         "cores": int(getattr(recurrence, "last_threads", threads)),
         "kind": "oracle",
-        "sample": "tokens [0, %d) of the %d-token sequence, all %d value heads; fp64 C token "
-                  "recurrence, OpenMP over heads; %.1f s" % (ts, T, w.Nv, dt),
+        "sample": "the first %d tokens of each of the %d sequences (%d of %d tokens), all %d value heads; "
+                  "fp64 C token recurrence, OpenMP over (sequence, head); %.1f s"
+                  % (ts, len(lens), tokens, int(lens.sum()), w.Nv, dt),
     }
 
 
@@ -536,7 +616,7 @@ def bench_segmented(args) -> None:
         del f
     Ttot = w.T
     NT = Ttot // 64
-    alg = stage_algorithmic_bytes(w, Ttot, 1, NT, 2, False)["k_state_output"]
+    alg = method_bytes_per_token(w, 2) * Ttot
     achieved = alg / (st_seg[4] * 1e-3) / 1e9
     print(json.dumps({
         "metric": "fwd tokens/s, one 64k-token sequence with 4 value heads (segment-parallel state passing)",
@@ -569,13 +649,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget; 0 skips it")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB three times (calibrates HBM byte counters)")
-    ap.add_argument("--mode", choices=("chunk", "recurrent", "segmented", "chunk-sizes", "backward"),
+    ap.add_argument("--mode", choices=("chunk", "recurrent", "segmented", "chunk-sizes", "backward", "configs"),
                     default="chunk",
                     help="chunk: the chunked forward on --workload (default); recurrent: one decode step "
                          "(token-by-token kernel) for --decode-seqs sequences from a random state; segmented: "
                          "segment-parallel against serial state passing on one long sequence with few heads; "
                          "chunk-sizes: the five-kernel path at C = 16, 32, 64 and the fused path on --workload; "
-                         "backward: the backward pass (forward recomputed) on --workload")
+                         "backward: the backward pass (forward recomputed) on --workload; "
+                         "configs: every synthetic workload 1-5 with the oracle beside it")
     ap.add_argument("--segment-chunks", type=int, default=0,
                     help="chunks per segment in --mode segmented (0: the library's choice)")
     ap.add_argument("--decode-seqs", type=int, default=64)
@@ -585,6 +666,9 @@ def main():
     ap.add_argument("--mfma-summary", metavar="DIR",
                     help="only summarise a rocprofv3 run of MFMA_COUNTERS found under DIR into profiles/")
     ap.add_argument("--summary-out", metavar="DIR", default="profiles")
+    ap.add_argument("--summary-file", metavar="FILE", help="--mode configs: also write a markdown table here")
+    ap.add_argument("--no-peaks", dest="peaks", action="store_false",
+                    help="skip measuring the HBM-copy and matrix-core peaks")
     args = ap.parse_args()
     if args.counter_summary:
         counter_summary(args.counter_summary, args.summary_out, args.workload)
@@ -614,6 +698,9 @@ def main():
         return
     if args.mode == "backward":
         bench_backward(args)
+        return
+    if args.mode == "configs":
+        bench_configs(args)
         return
 
     w = synth.WORKLOADS[args.workload]
@@ -651,17 +738,34 @@ def main():
                          for s in range(K)]).mean(axis=0)
 
     out_bytes = 4 if (args.out_dtype == "f32" or w.dtype == "f32") else 2
-    alg = stage_algorithmic_bytes(w, Ttot, N, NT, out_bytes, inp["S0"] is not None)
-    names = FUSED_STAGE_KERNELS if w.dtype == "bf16" else STAGE_KERNELS
+    io = stage_io_bytes(w, Ttot, N, NT, out_bytes, inp["S0"] is not None)
+    names = FP16_STAGE_KERNELS if w.dtype == "bf16" else STAGE_KERNELS
     dom = int(np.argmax(stage_ms))
     kname = names[dom]
-    achieved = alg[kname] / (stage_ms[dom] * 1e-3) / 1e9
+    bpt = method_bytes_per_token(w, out_bytes)
+    fpt = method_flops_per_token(w)
+    alg_bytes = bpt * Ttot
+    alg_flops = fpt * Ttot
+    achieved = alg_bytes / (stage_ms[dom] * 1e-3) / 1e9
     traffic = counter_traffic(kname, "T65536_Nk16_Nv32_d128" if args.workload == 5 else "workload%d" % args.workload)
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+    peaks = measure_peaks() if args.peaks else None
 
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(inp, args.cpu_seconds)
 
+    step_s = ms_per_step * 1e-3
+    e2e = {
+        "bytes_per_token": bpt, "flop_per_token": fpt,
+        "hbm_GBps": alg_bytes / step_s / 1e9, "hbm_frac": alg_bytes / step_s / 1e9 / HBM_PEAK_GBS,
+        "mfma_TFLOPs": alg_flops / step_s / 1e12, "mfma_frac": alg_flops / step_s / 1e12 / mfma_peak,
+        "mfma_peak": mfma_peak,
+    }
+    if peaks is not None:
+        e2e["hbm_frac_measured_peak"] = e2e["hbm_GBps"] / peaks["hbm_GBps"]
+        if w.dtype == "bf16":
+            e2e["mfma_frac_measured_peak"] = e2e["mfma_TFLOPs"] / peaks["mfma_bf16_TFLOPs"]
     line = {
         "metric": METRIC,
         "value": Ttot * K / (total_ms * 1e-3),
@@ -678,15 +782,96 @@ def main():
         "config": {"workload": w.name, "T": Ttot, "Nk": w.Nk, "Nv": w.Nv, "dk": w.dk, "dv": w.dv, "chunk": 64,
                    "gated": w.gated, "g": "logsigmoid(N(%g,1))" % w.g_mean, "S0": w.s0,
                    "out_dtype": "f32" if out_bytes == 4 else w.dtype, "seed": args.workload},
+        # dominant kernel: the method's algorithmic bytes over its average launch time
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes": alg[kname], "avg_ms": float(stage_ms[dom])},
+                     "algorithmic_bytes": alg_bytes, "bytes_per_token": bpt, "avg_ms": float(stage_ms[dom]),
+                     "kernel_io_bytes": io[kname],
+                     "mfma_frac": alg_flops / (stage_ms[dom] * 1e-3) / 1e12 / mfma_peak},
+        "end_to_end": e2e,
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
         "stage_ms": {("%d:%s" % (i, names[i])): float(stage_ms[i]) for i in range(api.NUM_STAGES)},
-        "end_to_end_hbm_frac": (24768.0 * Ttot / (ms_per_step * 1e-3) / 1e9) / HBM_PEAK_GBS
-        if args.workload == 5 and out_bytes == 2 else None,
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_configs(args) -> None:
+    """Every synthetic workload (1-5): median and p90 of per-call HIP-event
+    times over --steps calls after --warmup, tokens/s, and the end-to-end
+    algorithmic fractions of HBM and matrix-core peaks; the oracle's token
+    recurrence timed beside it on all host threads (bounded sample) and, for
+    workloads 1-3, on one thread. One JSON line per workload; with
+    --summary-file, also a markdown table there."""
+    peaks = measure_peaks() if args.peaks else None
+    rows = []
+    for cfg in range(1, 6):
+        w = synth.WORKLOADS[cfg]
+        inp = synth.generate(w, seed=cfg)
+        dev = torch.device("cuda:0")
+        d = {k: (None if inp[k] is None else inp[k].to(dev)) for k in ("q", "k", "v", "beta", "g", "S0",
+                                                                          "cu_seqlens")}
+        fwd = api.Forward(d["q"], d["k"], d["v"], d["beta"], g=d["g"], scale=inp["scale"], initial_state=d["S0"],
+                          output_final_state=True, cu_seqlens=d["cu_seqlens"], cu_seqlens_cpu=inp["cu_seqlens"])
+        B, T = inp["q"].shape[:2]
+        Ttot = B * T
+        for _ in range(args.warmup):
+            fwd()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for a, b in ev:
+            a.record()
+            fwd()
+            b.record()
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in ev])
+        med, p90 = float(np.median(t)), float(np.percentile(t, 90))
+        out_bytes = 2 if w.dtype == "bf16" else 4
+        bpt, fpt = method_bytes_per_token(w, out_bytes), method_flops_per_token(w)
+        mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+        hbm = bpt * Ttot / (med * 1e-3) / 1e9
+        tf = fpt * Ttot / (med * 1e-3) / 1e12
+        row = {"workload": w.name, "cfg": cfg, "tokens": Ttot, "median_ms": med, "p90_ms": p90,
+               "tokens_per_s": Ttot / (med * 1e-3), "hbm_GBps": hbm, "hbm_frac": hbm / HBM_PEAK_GBS,
+               "mfma_TFLOPs": tf, "mfma_frac": tf / mfma_peak, "mfma_peak": mfma_peak}
+        if peaks is not None:
+            row["hbm_frac_measured_peak"] = hbm / peaks["hbm_GBps"]
+            if w.dtype == "bf16":
+                row["mfma_frac_measured_peak"] = tf / peaks["mfma_bf16_TFLOPs"]
+        if args.cpu_seconds > 0:
+            row["oracle"] = cpu_baseline(inp, args.cpu_seconds)
+            if cfg <= 3:
+                row["oracle_1thread"] = cpu_baseline(inp, args.cpu_seconds, threads=1)
+        del fwd, d
+        torch.cuda.empty_cache()
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+    if args.summary_file:
+        lines = ["# Forward throughput on every synthetic workload", "",
+                 "command: `python3 bench.py --mode configs --steps %d --warmup %d --cpu-seconds %g --summary-file "
+                 "<file>`" % (args.steps, args.warmup, args.cpu_seconds), ""]
+        if peaks is not None:
+            lines += ["Measured peaks: HBM copy %.0f GB/s, bf16 matrix cores %.0f TFLOP/s (%s)." % (
+                peaks["hbm_GBps"], peaks["mfma_bf16_TFLOPs"], peaks["how"]), ""]
+        lines += ["| cfg | workload | tokens | median ms | p90 ms | tokens/s | HBM frac (spec / measured) "
+                  "| MFMA frac (spec / measured) | oracle tokens/s (threads) | oracle 1 thread |",
+                  "|---|---|---|---|---|---|---|---|---|---|"]
+        for r in rows:
+            o = r.get("oracle")
+            o1 = r.get("oracle_1thread")
+            lines.append("| %d | %s | %d | %.4f | %.4f | %.3g | %.4f / %s | %.4f / %s | %s | %s |" % (
+                r["cfg"], r["workload"], r["tokens"], r["median_ms"], r["p90_ms"], r["tokens_per_s"],
+                r["hbm_frac"], "%.4f" % r["hbm_frac_measured_peak"] if "hbm_frac_measured_peak" in r else "-",
+                r["mfma_frac"], "%.4f" % r["mfma_frac_measured_peak"] if "mfma_frac_measured_peak" in r else "-",
+                "%.3g (%d)" % (o["value"], o["cores"]) if o else "-",
+                "%.3g" % o1["value"] if o1 else "-"))
+        lines += ["", "Fractions are the method's algorithmic bytes (q, k, v, g, beta read once, o written once) "
+                  "and flops (6 dk dv + 2C(3dk + 2dv) + (2/3)C^2 per token-head) over the median call time, "
+                  "against the published peaks (HBM 8 TB/s; bf16 2.5 PFLOP/s, fp32 157.3 TFLOP/s for "
+                  "workload 1) and the measured ones."]
+        with open(args.summary_file, "w") as f:
+            f.write("\n".join(lines) + "\n")
 
 
 if __name__ == "__main__":

@@ -27,7 +27,8 @@ EXPORTED = ("gdr_validate", "gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd_debug
             "gdr_chunk_fwd", "gdr_chunk_fwd_debug", "gdr_chunk_fwd_timed", "gdr_recurrent_fwd",
             "gdr_chunk_fwd_segmented_workspace_size", "gdr_chunk_fwd_segmented",
             "gdr_chunk_bwd_workspace_size", "gdr_chunk_bwd",
-            "gdr_status_string", "gdr_last_error_message")
+            "gdr_status_string", "gdr_last_error_message",
+            "gdr_peak_copy", "gdr_peak_mfma", "gdr_peak_mfma_flops")
 
 
 class Problem(ctypes.Structure):
@@ -86,6 +87,12 @@ def load_library():
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_last_error_message.argtypes = []
     lib.gdr_last_error_message.restype = ctypes.c_char_p
+    lib.gdr_peak_copy.argtypes = [P, P, ctypes.c_size_t, ctypes.c_int32, P]
+    lib.gdr_peak_copy.restype = ctypes.c_int
+    lib.gdr_peak_mfma.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P]
+    lib.gdr_peak_mfma.restype = ctypes.c_int
+    lib.gdr_peak_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.gdr_peak_mfma_flops.restype = ctypes.c_double
     _lib = lib
     return lib
 

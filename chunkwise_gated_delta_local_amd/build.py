@@ -14,7 +14,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(BUILD_DIR, "libgdr.so")
-SOURCES = ["gdr_api.hip", "gdr_kernels.hip", "gdr_fp16.hip", "gdr_recurrent.hip", "gdr_backward.hip"]
+SOURCES = ["gdr_api.hip", "gdr_kernels.hip", "gdr_fp16.hip", "gdr_recurrent.hip", "gdr_backward.hip",
+           "gdr_peaks.hip"]
+# per-file options: the matrix-core loops of these files keep their accumulators
+# in VGPRs (without it the compiler moves loop-carried accumulators between
+# AGPRs and VGPRs on every iteration)
+EXTRA_FLAGS = {"gdr_peaks.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
@@ -27,7 +32,7 @@ def build(verbose: bool = False) -> str:
     objs, procs = [], []
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(HERE, "csrc", src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(HERE, "csrc", src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
