@@ -19,7 +19,8 @@ SOURCES = ["gdr_api.hip", "gdr_kernels.hip", "gdr_fp16.hip", "gdr_recurrent.hip"
 # per-file options: the matrix-core loops of these files keep their accumulators
 # in VGPRs (without it the compiler moves loop-carried accumulators between
 # AGPRs and VGPRs on every iteration)
-EXTRA_FLAGS = {"gdr_peaks.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA_FLAGS = {"gdr_peaks.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "gdr_fp16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",

@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gdr_device.hpp"
 #include "gdr_fp16.hpp"
 #include "gdr_launch.hpp"
@@ -363,29 +365,31 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
 // end state from S = I over dk columns with V read as zero). Both serve
 // segment-parallel state passing; the full mode also serves the serial pass.
 //
-// Wavefront roles (eight per workgroup, two per SIMD):
-//   0        chain: the state slice S (dk x 16, fp32) in registers; per chunk
-//              Y = K S (K from LDS in the stacked contraction order, S pairs
-//              from its own accumulators), Z = V - exp(G) Y, V_new = T Z
-//              (T pairs loaded from global memory one chunk ahead),
-//              S = exp(G_last) S + K^T (exp(G_last - G) V_new) with K^T from
-//              transposing LDS reads; publishes V_new and the next entering
-//              state (fp16) for the output waves.
-//   1, 2     output (full mode): chunk c's Q S_in part in step c and its
-//              P V_new part in step c + 1, for the row blocks {0, 3} and {1, 2};
-//              Q (bf16, converted) and P pairs come straight from global memory
-//              into registers one chunk ahead.
-//   3        copies the V slice and the decay rows of chunk c + 2 into LDS
-//              (16-byte buffer-to-LDS loads; rows past a chunk's end read zero).
-//   4 .. 7   K rows of chunk c + 2: loaded in step c - 1, converted to fp16
-//              and written to LDS in step c.
-// One LDS-only barrier per chunk step; K, V and R tiles are triple-buffered.
+// One workgroup of four wavefronts (one per SIMD, up to 512 registers each)
+// per (sequence, value head, 16 columns of dv). Per chunk c the chain
+// wavefront runs the serial dependency
+//     Y = K S,  Z = V - exp(G) Y,  V_new = T Z,  S = exp(G_last) S + K^T (exp(G_last - G) V_new)
+// on the matrix cores with the dk x 16 state slice in registers: every
+// product's accumulators are, lane for lane, an operand of the next (two
+// stacked accumulator tiles are a pair fragment of the transposed block).
+// All of its operands are in registers when the step starts: the K operand
+// of Y and the V and decay rows of chunk c + 1 are read from LDS during step
+// c, T two chunks ahead from global memory. The other three wavefronts form
+// the output, transposed (O^T = S^T Q^T + V_new^T P^T, so that each lane holds
+// four adjacent columns of one row), for the row blocks {0, 1}, {2} and {3}:
+// chunk c's S part in step c, its V_new part and the store in step c + 1.
+// Their global loads (Q rows, score pairs, K rows) are issued two steps
+// before use. Wavefront 1 also copies the V slice and decay rows of chunk
+// c + 3 into LDS (16-byte buffer-to-LDS loads); wavefronts 2 and 3 convert
+// the K rows of chunk c + 2 (rows 0..31 and 32..63) to fp16 in LDS.
+// One LDS-only barrier per chunk step. K tiles are triple-buffered, V and
+// decay rows quadruple-buffered, the published state and V_new double-buffered.
 //
 // LDS layout of a K tile: row-major, 64 rows of dk fp16 values, the 16-byte
-// units of row `row` permuted by an XOR with swz(row), so that the transposing
-// K^T reads of the chain hit distinct banks.
+// units of row `row` permuted by an XOR with swz(row), so that the chain's
+// operand reads and its transposing K^T reads hit distinct banks.
 template <int DK, int DV, int MODE>
-__global__ __launch_bounds__(512) void k_chunk16(const bf16* __restrict__ q, const bf16* __restrict__ k,
+__global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                  const bf16* __restrict__ v, const float* __restrict__ R,
                                                  const f16* __restrict__ Tf, const f16* __restrict__ Pf,
                                                  const float* __restrict__ S0,
@@ -397,18 +401,18 @@ __global__ __launch_bounds__(512) void k_chunk16(const bf16* __restrict__ q, con
     constexpr int C = 64;
     constexpr int NKP = DK / 32, NDB = DK / 16;
     constexpr int UPR = DK / 8;                 // 16-byte units per K row
-    constexpr int KLD = UPR / 4;                // 16-byte K loads per lane per convert wave per chunk
+    constexpr int KLD = DK / 16;                // 16-byte K loads per lane per converting wave per chunk
     constexpr bool want_o = MODE == kFull16;
-    static_assert(KLD >= 1, "dk");
     __shared__ __attribute__((aligned(16))) f16 Ks[3][C * DK];
-    __shared__ __attribute__((aligned(16))) bf16 Vs[3][C * 16];
-    __shared__ __attribute__((aligned(16))) float Rs[3][2 * C];
+    __shared__ __attribute__((aligned(16))) bf16 Vs[4][C * 16];
+    __shared__ __attribute__((aligned(16))) float Rs[4][2 * C];
+    __shared__ __attribute__((aligned(16))) f16 Ts[4][kPairs * kFrag];  // T pair fragments
     __shared__ __attribute__((aligned(16))) f16 Sx[2][NKP][kFrag];     // entering state, natural dk order
     __shared__ __attribute__((aligned(16))) f16 VNx[2][2][kFrag];      // V_new pairs (stacked positions)
 
-    // XCD-aware placement (as in the bf16 pass): each XCD takes a contiguous run
-    // of (unit, head, column tile) triples, so the workgroups that read the same
-    // K and Q tiles share one L2.
+    // XCD-aware placement: each XCD takes a contiguous run of (unit, head,
+    // column tile) triples, so the workgroups that read the same K and Q
+    // tiles share one L2.
     int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
     {
         const int64_t W = (int64_t)gridDim.x * gridDim.y * gridDim.z;
@@ -431,116 +435,141 @@ __global__ __launch_bounds__(512) void k_chunk16(const bf16* __restrict__ q, con
     float* const STo = trans ? ST2 : ST;
     const int c0 = __builtin_amdgcn_readfirstlane(first[n]), c1 = __builtin_amdgcn_readfirstlane(first[n + 1]);
     auto slot3 = [&](int c) { return (c - c0) % 3; };
-    // chunk start and length are the same in every lane: taken into scalar
-    // registers, so that the buffer descriptors built from them are uniform
-    // (a descriptor in vector registers makes the compiler wrap every buffer
-    // access in a loop over the distinct lane values)
-    auto chunk_s = [&](int c) { return (int64_t)__builtin_amdgcn_readfirstlane(chunk_start[c]); };
-    auto chunk_L = [&](int c) { return max(0, min(C, (int)__builtin_amdgcn_readfirstlane(chunk_len[c]))); };
+    auto slot4 = [&](int c) { return (c - c0) & 3; };
+    // chunk start and length in scalar registers (uniform buffer descriptors);
+    // a chunk past the sequence's last reads as empty
+    auto chunk_s = [&](int c) { return c < c1 ? (int64_t)__builtin_amdgcn_readfirstlane(chunk_start[c]) : (int64_t)0; };
+    auto chunk_L = [&](int c) {
+        return c < c1 ? max(0, min(C, (int)__builtin_amdgcn_readfirstlane(chunk_len[c]))) : 0;
+    };
     auto swz = [](int row) { return ((((row & 3) << 1) | ((row >> 2) & 1) | (row & 8))) & (UPR - 1); };
     const int64_t sbase = ((int64_t)n * Nv + h) * DK * NC;
+    typedef std::integral_constant<int, 0> P0;
+    typedef std::integral_constant<int, 1> P1;
 
     if (wv == 0) {
         // ======================================================== chain
+        // State tile t, accumulator row 4 qd + j holds dk row srow(t, 4 qd + j) =
+        // 32 (t / 2) + 8 qd + 4 (t % 2) + j: then the two tiles 2 kp, 2 kp + 1,
+        // stacked, are the state's operand for dk 32 kp .. 32 kp + 31 in the
+        // natural order (lane (qd, r) element e = dk 32 kp + 8 qd + e), the order
+        // in which a 16-byte read of a K row is that row's operand.
+        auto srow = [&](int t, int j) { return 32 * (t >> 1) + 8 * qd + 4 * (t & 1) + j; };
         f32x4 S[NDB];
 #pragma unroll
         for (int t = 0; t < NDB; ++t) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int row = t * 16 + 4 * qd + j, col = nb * 16 + r;
+                const int row = srow(t, j), col = nb * 16 + r;
                 S[t][j] = trans ? (row == col ? 1.f : 0.f) : (S0 ? S0[sbase + (int64_t)row * NC + col] : 0.f);
             }
         }
         h8 Sp[NKP];
-        // state pairs (stacked dk order) for Y; the output waves' copy in natural
-        // order (lane (qd', r) element e = S[32 kp + 8 qd' + e][r])
+        // state pairs for Y; the output waves take the same fragments
         auto make_pairs = [&](int c_next) {
 #pragma unroll
             for (int kp = 0; kp < NKP; ++kp) {
                 Sp[kp] = pack_pair(S[2 * kp], S[2 * kp + 1]);
-                if constexpr (want_o) {
-                    const u4 w = __builtin_bit_cast(u4, Sp[kp]);
-                    f16* dst = Sx[(c_next - c0) & 1][kp];
-                    *reinterpret_cast<u2*>(&dst[(16 * (qd >> 1) + r) * 8 + 4 * (qd & 1)]) = u2{w[0], w[1]};
-                    *reinterpret_cast<u2*>(&dst[(16 * (2 + (qd >> 1)) + r) * 8 + 4 * (qd & 1)]) = u2{w[2], w[3]};
-                }
+                if constexpr (want_o) *reinterpret_cast<h8*>(&Sx[(c_next - c0) & 1][kp][lane * 8]) = Sp[kp];
             }
         };
-        h8 tf[kPairs];
-        auto load_T = [&](int c) {
-            const auto rs = rsrc_of(Tf, ((int64_t)c * Nv + h) * kPairs * kFrag * 2, kPairs * kFrag * 2);
-#pragma unroll
-            for (int p = 0; p < kPairs; ++p) tf[p] = __builtin_bit_cast(h8, buf_load16(rs, p * kFrag * 2 + lane * 16));
-        };
-        make_pairs(c0);
-        if (c0 < c1) load_T(c0);
-        lds_barrier();                                                            // prologue barrier
-        for (int c = c0; c < c1; ++c) {
-            const int sl = slot3(c);
-            const int L = chunk_L(c);
-            const f16* Kb = Ks[sl];
-            // K operand of Y in the stacked dk order: elements 0..3 = dk 32 kp + 4 qd ..,
-            // 4..7 = dk 32 kp + 16 + 4 qd .., row 16 b + r (two 8-byte reads)
-            h8 ka[4][NKP];
+        // K operand of Y: row 16 b + r, dk 32 kp + 8 qd .. + 7 (one 16-byte read)
+        h8 ka[4][NKP];
+        auto read_ka = [&](int c) {
+            const f16* Kb = Ks[slot3(c)];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 const int row = 16 * b + r;
 #pragma unroll
-                for (int kp = 0; kp < NKP; ++kp) {
-                    const int u1 = 4 * kp + (qd >> 1), u2_ = 4 * kp + 2 + (qd >> 1);
-                    const u2 lo = *reinterpret_cast<const u2*>(&Kb[row * DK + ((u1 ^ swz(row)) * 8) + 4 * (qd & 1)]);
-                    const u2 hi = *reinterpret_cast<const u2*>(&Kb[row * DK + ((u2_ ^ swz(row)) * 8) + 4 * (qd & 1)]);
-                    ka[b][kp] = __builtin_bit_cast(h8, u4{lo[0], lo[1], hi[0], hi[1]});
-                }
+                for (int kp = 0; kp < NKP; ++kp)
+                    ka[b][kp] = *reinterpret_cast<const h8*>(&Kb[row * DK + ((4 * kp + qd) ^ swz(row)) * 8]);
             }
-            // V rows 16 b + 4 qd + j of column r (transposing reads of the bf16 tile)
-            f32x4 vrow[4];
+        };
+        // V rows 16 b + 4 qd + j of column r (transposing reads of the bf16 tile),
+        // exp(G) of those rows and exp(G_last) of the chunk
+        struct VR {
+            s4 v[4];
+            f32x4 eg[4];
+            float a0, a1;                         // exp(G_last) = a0 a1
+        };
+        auto read_vr = [&](int c) {
+            VR x;
+            const int sl = slot4(c);
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 const int row = 16 * b + 4 * qd + (r >> 2);
-                const bf16* p = &Vs[sl][row * 16 + 4 * (r & 3)];
-                vrow[b] = bf16x4_to_f32(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)p));
+                x.v[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)&Vs[sl][row * 16 + 4 * (r & 3)]);
+                x.eg[b] = *reinterpret_cast<const f32x4*>(&Rs[sl][16 * b + 4 * qd]);
             }
-            f32x4 eg[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) eg[b] = *reinterpret_cast<const f32x4*>(&Rs[sl][16 * b + 4 * qd]);
-            // ---- Y = K S_in
+            // exp(G_last) = exp(G_0) exp(G_last - G_0), from the rows themselves (no
+            // scalar load of the chunk length inside the chain: its wait would also
+            // wait for every LDS read in flight)
+            x.a0 = Rs[sl][0];
+            x.a1 = Rs[sl][C];
+            return x;
+        };
+        VR vr;
+        make_pairs(c0);
+        lds_barrier();                                                            // prologue barrier
+        if (c0 < c1) {
+            read_ka(c0);
+            vr = read_vr(c0);
+        }
+        auto step = [&](int c) {
+            const int sl = slot3(c), s4l = slot4(c);
+            const f16* Kb = Ks[sl];
+            // ---- Y = K S_in (operands read in the previous step)
             f32x4 Y[4];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int b = 0; b < 4; ++b) Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kp = 0; kp < NKP; ++kp) Y[b] = mfma16(ka[b][kp], Sp[kp], Y[b]);
+            for (int kp = 0; kp < NKP; ++kp)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) Y[b] = mfma16(ka[b][kp], Sp[kp], Y[b]);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) S[db] = S[db] * (vr.a0 * vr.a1);
+            // the next chunk's K operand (Y has taken this chunk's), V and decay rows
+            VR vr_next = vr;
+            if (c + 1 < c1) {
+                read_ka(c + 1);
+                vr_next = read_vr(c + 1);
             }
-            // K^T operands for the update: lane (qd, j) fetches dk 16 db + 4 (j & 3) .. of
-            // position 16 (2 tp + hh) + 4 qd + (j >> 2); the transposing read hands lane
-            // (qd, r') the values of dk 16 db + r' at positions 32 tp + m(qd, e)
+            __builtin_amdgcn_sched_barrier(0);
+            // T of this chunk, the K^T operands of the update and the decay rows.
+            // K^T for state tile t: lane (qd, j) fetches the 4 dk values from
+            // 32 (t / 2) + 8 (j & 3) + 4 (t % 2) of position 16 (2 tp + hh) + 4 qd + (j >> 2);
+            // the transposing read hands lane (qd, r') the values of dk row
+            // srow(t, r') at positions 32 tp + m(qd, e)
+            h8 tf[kPairs];
+#pragma unroll
+            for (int p = 0; p < kPairs; ++p) tf[p] = *reinterpret_cast<const h8*>(&Ts[s4l][p * kFrag + lane * 8]);
             h8 kt[NDB][2];
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
+            for (int t = 0; t < NDB; ++t) {
 #pragma unroll
                 for (int tp = 0; tp < 2; ++tp) {
                     s4 part[2];
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh) {
                         const int row = 16 * (2 * tp + hh) + 4 * qd + (r >> 2);
-                        const int unit = 2 * db + ((r & 3) >> 1);
-                        const f16* p = &Kb[row * DK + (unit ^ swz(row)) * 8 + 4 * (r & 1)];
+                        const int unit = 4 * (t >> 1) + (r & 3);
+                        const f16* p = &Kb[row * DK + (unit ^ swz(row)) * 8 + 4 * (t & 1)];
                         part[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)p);
                     }
-                    kt[db][tp] = __builtin_bit_cast(h8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                    kt[t][tp] = __builtin_bit_cast(h8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
                 }
             }
             f32x4 ed[4];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) ed[b] = *reinterpret_cast<const f32x4*>(&Rs[sl][C + 16 * b + 4 * qd]);
-            const float a_last = L > 0 ? Rs[sl][L - 1] : 1.f;
+            for (int b = 0; b < 4; ++b) ed[b] = *reinterpret_cast<const f32x4*>(&Rs[s4l][C + 16 * b + 4 * qd]);
+            __builtin_amdgcn_sched_barrier(0);                // every read above is issued before Z
             // ---- Z = V - exp(G) Y, V_new = T Z
             f32x4 Z[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
+                const f32x4 vv = bf16x4_to_f32(vr.v[b]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) Z[b][j] = vrow[b][j] - eg[b][j] * Y[b][j];
+                for (int j = 0; j < 4; ++j) Z[b][j] = vv[j] - vr.eg[b][j] * Y[b][j];
             }
             const h8 zp0 = pack_pair(Z[0], Z[1]), zp1 = pack_pair(Z[2], Z[3]);
             const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -549,7 +578,6 @@ __global__ __launch_bounds__(512) void k_chunk16(const bf16* __restrict__ q, con
             VN[1] = mfma16(tf[1], zp0, zero4);
             VN[2] = mfma16(tf[3], zp1, mfma16(tf[2], zp0, zero4));
             VN[3] = mfma16(tf[5], zp1, mfma16(tf[4], zp0, zero4));
-            if (c + 1 < c1) load_T(c + 1);
             if constexpr (want_o) {
                 *reinterpret_cast<h8*>(&VNx[(c - c0) & 1][0][lane * 8]) = pack_pair(VN[0], VN[1]);
                 *reinterpret_cast<h8*>(&VNx[(c - c0) & 1][1][lane * 8]) = pack_pair(VN[2], VN[3]);
@@ -560,109 +588,65 @@ __global__ __launch_bounds__(512) void k_chunk16(const bf16* __restrict__ q, con
             const h8 vd0 = pack_pair(VD[0], VD[1]), vd1 = pack_pair(VD[2], VD[3]);
             // ---- S_out = exp(G_last) S_in + K^T VD
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                f32x4 acc = S[db] * a_last;
-                acc = mfma16(kt[db][0], vd0, acc);
-                S[db] = mfma16(kt[db][1], vd1, acc);
-            }
+            for (int t = 0; t < NDB; ++t) S[t] = mfma16(kt[t][1], vd1, mfma16(kt[t][0], vd0, S[t]));
+            __builtin_amdgcn_sched_barrier(0);
+            vr = vr_next;
             make_pairs(c + 1);
             lds_barrier();                                                        // end of step c
-        }
+        };
+        for (int c = c0; c < c1; ++c) step(c);
         if (STo) {
 #pragma unroll
             for (int t = 0; t < NDB; ++t) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    STo[sbase + (int64_t)(t * 16 + 4 * qd + j) * NC + nb * 16 + r] = S[t][j];
+                    STo[sbase + (int64_t)srow(t, j) * NC + nb * 16 + r] = S[t][j];
             }
         }
         return;
     }
 
-    if (wv == 1 || wv == 2) {
-        // ======================================================== output
-        if constexpr (!want_o) return;
-        if (c0 >= c1) return;
-        const int ow = wv - 1;
-        const int blk[2] = {ow == 0 ? 0 : 1, ow == 0 ? 3 : 2};
+    // ============================================================ helper waves
+    // wavefront 1: output rows 0..31 (blocks 0, 1) and the V / decay-row copies;
+    // wavefronts 2, 3: output block 2 / 3 and the K rows 0..31 / 32..63.
+    auto helper = [&](auto nblk_t, auto convert_t) {
+        constexpr int NBL = decltype(nblk_t)::value;       // output row blocks of this wave
+        constexpr bool CONV = decltype(convert_t)::value;   // converts K rows (else copies V and decay rows)
+        int blk[NBL];
+        if constexpr (NBL == 2) {
+            blk[0] = 0;
+            blk[1] = 1;
+        } else {
+            blk[0] = wv;
+        }
+        const int rbase = (wv - 2) * 32;                    // K rows of a converting wave
         const int ob = out_f32 ? 4 : 2;
-        u4 qraw[2][NKP];                        // Q rows (bf16) of the coming chunk
-        h8 pf[2][2], pnx[2][2];                 // P pairs of the pending and the coming chunk
-        f32x4 part[2];                          // exp(G) Q S_in of the pending chunk
-        auto load_qp = [&](int c) {
+        // ---- K rows: raw bf16 of the chunks of each parity, loaded four steps
+        //      before their chunk is read (two before they are converted)
+        u4 kraw[2][KLD];
+        auto load_k = [&](int c, u4* dst) {
             const int64_t s = chunk_s(c);
             const int L = chunk_L(c);
-            const auto rq = rsrc_of(q, (s * Nk + kh) * DK * 2, L > 0 ? (uint32_t)((L - 1) * Nk * DK + DK) * 2u : 0u);
-            const auto rp = rsrc_of(Pf, ((int64_t)c * Nv + h) * kPairs * kFrag * 2, kPairs * kFrag * 2);
+            const auto rk = rsrc_of(k, (s * Nk + kh) * DK * 2, L > 0 ? (uint32_t)((L - 1) * Nk * DK + DK) * 2u : 0u);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int I = blk[i];
-#pragma unroll
-                for (int kp = 0; kp < NKP; ++kp)
-                    qraw[i][kp] = buf_load16(rq, ((16 * I + r) * Nk * DK + 32 * kp + 8 * qd) * 2);
-                const int pb = I == 0 ? 0 : (I == 1 ? 1 : (I == 2 ? 2 : 4));
-#pragma unroll
-                for (int tp = 0; tp < 2; ++tp)
-                    if (2 * tp <= I) pnx[i][tp] = __builtin_bit_cast(h8, buf_load16(rp, (pb + tp) * kFrag * 2 + lane * 16));
+            for (int i = 0; i < KLD; ++i) {
+                const int f = i * 64 + lane;
+                const int row = rbase + f / UPR, u = f % UPR;
+                dst[i] = buf_load16(rk, (row * Nk * DK + 8 * u) * 2);
             }
         };
-        auto finish = [&](int c) {                // O of chunk c += P V_new, then stored
-            const h8 vn0 = *reinterpret_cast<const h8*>(&VNx[(c - c0) & 1][0][lane * 8]);
-            const h8 vn1 = *reinterpret_cast<const h8*>(&VNx[(c - c0) & 1][1][lane * 8]);
-            const int64_t s = chunk_s(c);
-            const int L = chunk_L(c);
-            const auto ro = rsrc_of(o, ((s * Nv + h) * DV + nb * 16) * ob, L > 0 ? (uint32_t)(((L - 1) * Nv * DV + 16) * ob) : 0u);
+        auto store_k = [&](int c, const u4* src) {
+            f16* dst = Ks[slot3(c)];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int I = blk[i];
-                f32x4 acc = mfma16(pf[i][0], vn0, part[i]);
-                if (I >= 2) acc = mfma16(pf[i][1], vn1, acc);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {           // rows past the chunk end fall outside ro
-                    const float val = scale * acc[j];
-                    const int off = ((16 * I + 4 * qd + j) * Nv * DV + r) * ob;
-                    if (out_f32) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), ro, off, 0, 0);
-                    else __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)val), ro, off, 0, 0);
-                }
+            for (int i = 0; i < KLD; ++i) {
+                const int f = i * 64 + lane;
+                const int row = rbase + f / UPR, u = f % UPR;
+                *reinterpret_cast<h8*>(&dst[row * DK + (u ^ swz(row)) * 8]) = bf16x8_to_f16(src[i]);
             }
         };
-        load_qp(c0);
-        lds_barrier();                                                            // prologue barrier
-        for (int c = c0; c < c1; ++c) {
-            const int sl = slot3(c);
-            if (c > c0) finish(c - 1);
-            // this chunk's operands, loaded one step ahead
-            h8 qf[2][NKP];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-#pragma unroll
-                for (int kp = 0; kp < NKP; ++kp) qf[i][kp] = bf16x8_to_f16(qraw[i][kp]);
-#pragma unroll
-                for (int tp = 0; tp < 2; ++tp) pf[i][tp] = pnx[i][tp];
-            }
-            if (c + 1 < c1) load_qp(c + 1);
-            h8 sx[NKP];
-#pragma unroll
-            for (int kp = 0; kp < NKP; ++kp) sx[kp] = *reinterpret_cast<const h8*>(&Sx[(c - c0) & 1][kp][lane * 8]);
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int I = blk[i];
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kp = 0; kp < NKP; ++kp) acc = mfma16(qf[i][kp], sx[kp], acc);
-                const f32x4 egv = *reinterpret_cast<const f32x4*>(&Rs[sl][16 * I + 4 * qd]);
-                part[i] = egv * acc;
-            }
-            lds_barrier();                                                        // end of step c
-        }
-        finish(c1 - 1);
-        return;
-    }
-
-    if (wv == 3) {
-        // ======================================================== V slice and decay rows
+        // ---- V slice, decay rows and T of a chunk -> LDS (9 buffer-to-LDS loads)
         auto copy_vr = [&](int c) {
-            const int sl = slot3(c);
+            const int sl = slot4(c);
             const int64_t s = chunk_s(c);
             const int L = chunk_L(c);
             const uint32_t vbytes = (trans || L <= 0) ? 0u : (uint32_t)((L - 1) * Nv * DV + 16) * 2u;
@@ -670,62 +654,139 @@ __global__ __launch_bounds__(512) void k_chunk16(const bf16* __restrict__ q, con
 #pragma unroll
             for (int vh = 0; vh < 2; ++vh)                // rows 32 vh .. 32 vh + 31, 16 columns
                 buffer_to_lds16(rv, &Vs[sl][vh * 512], ((32 * vh + (lane >> 1)) * Nv * DV + 8 * (lane & 1)) * 2);
+            const uint32_t rbytes = c < c1 ? 2 * C * 4 : 0u;
             if (lane < 32)                                // decay rows: 512 bytes
-                buffer_to_lds16(rsrc_of(R, ((int64_t)c * Nv + h) * 2 * C * 4, 2 * C * 4), &Rs[sl][0], lane * 16);
+                buffer_to_lds16(rsrc_of(R, (c < c1 ? (int64_t)c * Nv + h : 0) * 2 * C * 4, rbytes), &Rs[sl][0],
+                                lane * 16);
+            const auto rt = rsrc_of(Tf, (c < c1 ? (int64_t)c * Nv + h : 0) * kPairs * kFrag * 2,
+                                    c < c1 ? kPairs * kFrag * 2 : 0u);
+#pragma unroll
+            for (int p = 0; p < kPairs; ++p) buffer_to_lds16(rt, &Ts[sl][p * kFrag], p * kFrag * 2 + lane * 16);
         };
-        if (c0 < c1) copy_vr(c0);
-        if (c0 + 1 < c1) copy_vr(c0 + 1);
-        wait_vmem();
-        lds_barrier();                                                            // prologue barrier
-        for (int c = c0; c < c1; ++c) {
-            if (c + 2 < c1) {
-                copy_vr(c + 2);
-                wait_vmem_but<3>();           // chunk c + 1's copies (issued a step ago) have landed
-            } else {
-                wait_vmem();
-            }
-            lds_barrier();                                                        // end of step c
-        }
-        return;
-    }
-
-    // ============================================================ K rows -> fp16 (waves 4 .. 7)
-    {
-        const int w = wv - 4;
-        u4 kraw[KLD];
-        auto load_k = [&](int c) {
+        // ---- output operands: Q rows (bf16) of chunk c loaded in step c - 2; the
+        //      score pairs of chunk c loaded in step c - 1 and used in step c + 1
+        u4 qraw[2][NBL][NKP];
+        h8 praw[2][2];
+        f32x4 part[NBL];                                    // exp(G) (Q S_in)^T of the pending chunk
+        auto load_q = [&](int c, u4 (*dst)[NKP]) {
             const int64_t s = chunk_s(c);
             const int L = chunk_L(c);
-            const auto rk = rsrc_of(k, (s * Nk + kh) * DK * 2, L > 0 ? (uint32_t)((L - 1) * Nk * DK + DK) * 2u : 0u);
+            const auto rq = rsrc_of(q, (s * Nk + kh) * DK * 2, L > 0 ? (uint32_t)((L - 1) * Nk * DK + DK) * 2u : 0u);
 #pragma unroll
-            for (int i = 0; i < KLD; ++i) {
-                const int f = (w * KLD + i) * 64 + lane;            // 16-byte unit of the tile
-                const int row = f / UPR, u = f % UPR;
-                kraw[i] = buf_load16(rk, (row * Nk * DK + 8 * u) * 2);
+            for (int i = 0; i < NBL; ++i)
+#pragma unroll
+                for (int kp = 0; kp < NKP; ++kp)
+                    dst[i][kp] = buf_load16(rq, ((16 * blk[i] + r) * Nk * DK + 32 * kp + 8 * qd) * 2);
+        };
+        // the two score pairs this wave needs: blocks 0 and 1 (pairs 0, 1) or
+        // block b >= 2 (pairs 2 b - 2, 2 b - 1)
+        const int pbase = NBL == 2 ? 0 : 2 * wv - 2;
+        auto load_p = [&](int c, h8* dst) {
+            const auto rp = rsrc_of(Pf, (c < c1 ? (int64_t)c * Nv + h : 0) * kPairs * kFrag * 2,
+                                    c < c1 ? kPairs * kFrag * 2 : 0u);
+#pragma unroll
+            for (int p = 0; p < 2; ++p) dst[p] = __builtin_bit_cast(h8, buf_load16(rp, (pbase + p) * kFrag * 2 + lane * 16));
+        };
+        // O of chunk cc (stored only when cc is one of this sequence's chunks):
+        // its S part plus the score block times V_new, transposed, scaled
+        auto finish = [&](int cc, auto parc) {
+            constexpr int PC = decltype(parc)::value;       // parity of chunk cc
+            const bool valid = cc >= c0 && cc < c1;
+            const int64_t s = valid ? chunk_s(cc) : 0;
+            const int L = valid ? chunk_L(cc) : 0;
+            const auto ro = rsrc_of(o, ((s * Nv + h) * DV + nb * 16) * ob,
+                                    L > 0 ? (uint32_t)(((L - 1) * Nv * DV + 16) * ob) : 0u);
+            const h8 vn0 = *reinterpret_cast<const h8*>(&VNx[PC][0][lane * 8]);
+            const h8 vn1 = *reinterpret_cast<const h8*>(&VNx[PC][1][lane * 8]);
+#pragma unroll
+            for (int i = 0; i < NBL; ++i) {
+                f32x4 acc;
+                if constexpr (NBL == 2) {
+                    acc = mfma16(vn0, praw[PC][i], part[i]);
+                } else {
+                    acc = mfma16(vn1, praw[PC][1], mfma16(vn0, praw[PC][0], part[i]));
+                }
+                const f32x4 x = acc * scale;
+                const int off = ((16 * blk[i] + r) * Nv * DV + 4 * qd) * ob;   // rows past the end fall outside ro
+                if (out_f32) {
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, x), ro, off, 0, 0);
+                } else {
+                    typedef bf16 b4 __attribute__((ext_vector_type(4)));
+                    const b4 y = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, y), ro, off, 0, 0);
+                }
             }
         };
-        auto store_k = [&](int c) {
-            f16* dst = Ks[slot3(c)];
 #pragma unroll
-            for (int i = 0; i < KLD; ++i) {
-                const int f = (w * KLD + i) * 64 + lane;
-                const int row = f / UPR, u = f % UPR;
-                *reinterpret_cast<h8*>(&dst[row * DK + (u ^ swz(row)) * 8]) = bf16x8_to_f16(kraw[i]);
-            }
-        };
-        if (c0 < c1) { load_k(c0); wait_vmem(); store_k(c0); }
-        if (c0 + 1 < c1) { load_k(c0 + 1); wait_vmem(); store_k(c0 + 1); }
-        if (c0 + 2 < c1) load_k(c0 + 2);
+        for (int i = 0; i < NBL; ++i) part[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        praw[1][0] = praw[1][1] = h8{};
+        // prologue: K rows of the first two chunks converted, of the next two in
+        // flight; V and decay rows of the first three chunks copied
+        if constexpr (CONV) {
+            load_k(c0, kraw[0]);
+            load_k(c0 + 1, kraw[1]);
+            store_k(c0, kraw[0]);
+            store_k(c0 + 1, kraw[1]);
+            load_k(c0 + 2, kraw[0]);
+            load_k(c0 + 3, kraw[1]);
+        } else {
+            copy_vr(c0);
+            copy_vr(c0 + 1);
+            wait_vmem();
+            copy_vr(c0 + 2);
+        }
+        if constexpr (want_o) {
+            load_q(c0, qraw[0]);
+            load_q(c0 + 1, qraw[1]);
+            load_p(c0, praw[0]);
+        }
         lds_barrier();                                                            // prologue barrier
-        for (int c = c0; c < c1; ++c) {
-            if (c + 2 < c1) {
-                wait_vmem();
-                store_k(c + 2);
-                if (c + 3 < c1) load_k(c + 3);
+        auto step = [&](int c, auto par) {
+            constexpr int PAR = decltype(par)::value;
+            if constexpr (!CONV) copy_vr(c + 3);
+            if constexpr (CONV) {
+                store_k(c + 2, kraw[PAR]);                  // K rows of chunk c + 2 (loaded in step c - 2)
+                load_k(c + 4, kraw[PAR]);
+            }
+            if constexpr (want_o) {
+                finish(c - 1, std::integral_constant<int, PAR ^ 1>{});
+                load_p(c + 1, praw[PAR ^ 1]);
+                // (Q S_in)^T of chunk c
+                h8 sx[NKP];
+#pragma unroll
+                for (int kp = 0; kp < NKP; ++kp) sx[kp] = *reinterpret_cast<const h8*>(&Sx[PAR][kp][lane * 8]);
+#pragma unroll
+                for (int i = 0; i < NBL; ++i) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kp = 0; kp < NKP; ++kp) acc = mfma16(sx[kp], bf16x8_to_f16(qraw[PAR][i][kp]), acc);
+                    part[i] = acc * Rs[slot4(c)][16 * blk[i] + r];
+                }
+                load_q(c + 2, qraw[PAR]);
+            }
+            // V, decay rows and T of chunk c + 2 (copied in step c - 1) have landed:
+            // every vector memory operation of this wave issued after them (the
+            // rest of step c - 1 and all of step c) may still be in flight
+            if constexpr (!CONV) {
+                if constexpr (want_o) wait_vmem_but<2 * (NBL * NKP + 2 + NBL) + 9>();
+                else wait_vmem_but<9>();
             }
             lds_barrier();                                                        // end of step c
+        };
+        for (int c = c0; c < c1; c += 2) {
+            step(c, P0{});
+            if (c + 1 < c1) step(c + 1, P1{});
         }
-    }
+        if constexpr (want_o) {                             // the last chunk's output
+            if (c1 > c0) {
+                if ((c1 - 1 - c0) & 1) finish(c1 - 1, P1{});
+                else finish(c1 - 1, P0{});
+            }
+        }
+        wait_vmem();
+    };
+    if (wv == 1) helper(std::integral_constant<int, 2>{}, std::false_type{});
+    else helper(std::integral_constant<int, 1>{}, std::true_type{});
 }
 
 // ============================================================ launch
@@ -746,16 +807,16 @@ static hipError_t launch_dims(const LaunchArgs& a, hipEvent_t* ev) {
     mark(4);
     if (a.N > 0 && !a.prep_only) {
         if (a.nseg > 0) {
-            k_chunk16<DK, DV, kSegment16><<<dim3(a.nseg, a.Nv, DV / 16 + DK / 16), 512, 0, st>>>(
+            k_chunk16<DK, DV, kSegment16><<<dim3(a.nseg, a.Nv, DV / 16 + DK / 16), 256, 0, st>>>(
                 q, k, v, R, Tf, Pf, nullptr, a.chunk_start, a.chunk_len, a.seg_first, a.Nk, a.Nv, a.scale,
                 a.out_f32, nullptr, a.Sloc, a.Mseg);
             const hipError_t e = launch_segment_scan(a);
             if (e != hipSuccess) return e;
-            k_chunk16<DK, DV, kFull16><<<dim3(a.nseg, a.Nv, DV / 16), 512, 0, st>>>(
+            k_chunk16<DK, DV, kFull16><<<dim3(a.nseg, a.Nv, DV / 16), 256, 0, st>>>(
                 q, k, v, R, Tf, Pf, a.Sstart, a.chunk_start, a.chunk_len, a.seg_first, a.Nk, a.Nv, a.scale,
                 a.out_f32, a.o, nullptr, nullptr);
         } else {
-            k_chunk16<DK, DV, kFull16><<<dim3(a.N, a.Nv, DV / 16), 512, 0, st>>>(
+            k_chunk16<DK, DV, kFull16><<<dim3(a.N, a.Nv, DV / 16), 256, 0, st>>>(
                 q, k, v, R, Tf, Pf, a.S0, a.chunk_start, a.chunk_len, a.seq_first, a.Nk, a.Nv, a.scale, a.out_f32,
                 a.o, a.ST, nullptr);
         }
