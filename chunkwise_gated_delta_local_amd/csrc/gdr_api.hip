@@ -25,9 +25,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Plan {
     int64_t Ttot;
     int32_t nt_cap;
-    size_t off_seq, off_start, off_len, off_first, off_R16, off_T16, off_P16, off_G, off_A, off_W, off_U, off_KT,
-        off_H, off_VN;
-    size_t sz_T16, sz_R16, sz_A, sz_W, sz_U, sz_KT, sz_H, sz_VN;   // per chunk except A (whole)
+    size_t off_seq, off_start, off_len, off_first, off_R16, off_T16, off_P16, off_K16, off_Q16, off_G, off_A, off_W,
+        off_U, off_KT, off_H, off_VN;
+    size_t sz_T16, sz_R16, sz_K16, sz_A, sz_W, sz_U, sz_KT, sz_H, sz_VN;   // per chunk except A (whole)
     size_t production;         // bytes gdr_chunk_fwd needs
     size_t reference;          // bytes gdr_chunk_fwd_debug needs (five separate kernels)
 };
@@ -86,8 +86,8 @@ gdr_status_t check_seqlens(const gdr_problem_t* p, const int32_t* cu, bool varle
 bool fused_path(const gdr_problem_t* p) { return p->io_dtype == GDR_BF16 && p->chunk_size == 64; }
 
 // Workspace regions, 256-byte aligned, in this order: the chunk table; on the
-// fp16 path its decay rows, T and score fragments (the production workspace
-// ends there); then the five-kernel path's gate sums and intermediates (its
+// fp16 path its decay rows, T and score fragments and the fp16 K and Q tiles
+// (the production workspace ends there); then the five-kernel path's gate sums and intermediates (its
 // production workspace, and the debug entry point's for every problem).
 Plan make_plan(const gdr_problem_t* p) {
     Plan pl;
@@ -112,6 +112,9 @@ Plan make_plan(const gdr_problem_t* p) {
     pl.off_R16 = take(cap * pl.sz_R16);
     pl.off_T16 = take(cap * pl.sz_T16);
     pl.off_P16 = take(cap * pl.sz_T16);
+    pl.sz_K16 = fused ? Nk * 64 * dk * 2 : 0;     // fp16 K (and Q) tiles
+    pl.off_K16 = take(cap * pl.sz_K16);
+    pl.off_Q16 = take(cap * pl.sz_K16);
     const size_t fused_end = off;
     pl.off_G = take(T * Nv * 4);
     pl.sz_A = T * Nv * C * 4;
@@ -216,6 +219,8 @@ gdr::LaunchArgs fill_args(const gdr_problem_t* p, const Plan& pl, int64_t nt, co
     a.T16 = pl.sz_T16 ? w + pl.off_T16 : nullptr;
     a.P16 = pl.sz_T16 ? w + pl.off_P16 : nullptr;
     a.R16 = pl.sz_R16 ? reinterpret_cast<float*>(w + pl.off_R16) : nullptr;
+    a.K16 = pl.sz_K16 ? w + pl.off_K16 : nullptr;
+    a.Q16 = pl.sz_K16 ? w + pl.off_Q16 : nullptr;
     a.reference = reference;
     a.prep_only = false;
     a.nseg = 0;

@@ -106,12 +106,22 @@ __device__ __forceinline__ u4 buf_load16(__amdgpu_buffer_rsrc_t rs, int voff) {
     return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
 }
 
+// fp16 K and Q tiles (64 rows of DK values per chunk and q/k head): the 16-byte
+// unit u of row `row` sits at unit u ^ tile_swz(row), in global memory as in
+// LDS, so that a tile is copied verbatim and the chunk pass's operand reads
+// (16-byte row reads and transposing K^T reads) spread over the LDS banks.
+template <int DK>
+__device__ __forceinline__ int tile_swz(int row) {
+    return ((((row & 3) << 1) | ((row >> 2) & 1) | (row & 8))) & (DK / 8 - 1);
+}
+
 }  // namespace
 
 // ============================================================ k_prep
 // One workgroup (four wavefronts) per (chunk, q/k head); it serves the value
 // heads that share the key head (ChunkGatedDeltaRule page, section 1: GQA).
-//   1. K and Q rows of the chunk -> LDS (zero past the chunk end).
+//   1. K and Q rows of the chunk -> LDS (zero past the chunk end), and as fp16
+//      tiles for the chunk pass.
 //   2. K K^T and the transposed score tiles K Q^T of block row `wave` on bf16
 //      matrix cores: exact products of the inputs, fp32 sums (FLA DeltaNet
 //      article, section 3.1).
@@ -134,7 +144,8 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
                                                   const int32_t* __restrict__ chunk_start,
                                                   const int32_t* __restrict__ chunk_len, int32_t Nk, int32_t Nv,
                                                   f16* __restrict__ Tf, f16* __restrict__ Pf,
-                                                  float* __restrict__ R) {
+                                                  float* __restrict__ R, f16* __restrict__ K16,
+                                                  f16* __restrict__ Q16) {
     constexpr int C = 64, NTHR = 256;
     constexpr int KP = DK + 8;                 // padded LDS row (elements)
     constexpr int SEGS = C * (DK / 8) / NTHR;  // 16-byte row segments per thread (>= 1 for DK >= 32)
@@ -180,11 +191,18 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
             }
         }
         if (wave == 0) fetch_gates(0);
+        f16* kt16 = K16 + ((int64_t)c * Nk + kh) * C * DK;
+        f16* qt16 = Q16 + ((int64_t)c * Nk + kh) * C * DK;
 #pragma unroll
         for (int i = 0; i < SEGS; ++i) {
             const int idx = tid + NTHR * i, row = idx / (DK / 8), seg = idx % (DK / 8);
             *reinterpret_cast<v8*>(&Ks[row * KP + seg * 8]) = kv[i];
             *reinterpret_cast<v8*>(&Qs[row * KP + seg * 8]) = qv[i];
+            // the fp16 tiles of the chunk pass (exact: bf16 values are fp16 values
+            // down to fp16's subnormal range)
+            const int u = (seg ^ tile_swz<DK>(row)) * 8;
+            *reinterpret_cast<h8*>(&kt16[row * DK + u]) = bf16x8_to_f16(__builtin_bit_cast(u4, kv[i]));
+            *reinterpret_cast<h8*>(&qt16[row * DK + u]) = bf16x8_to_f16(__builtin_bit_cast(u4, qv[i]));
         }
     }
     __syncthreads();
@@ -392,6 +410,7 @@ template <int DK, int DV, int MODE>
 __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                  const bf16* __restrict__ v, const float* __restrict__ R,
                                                  const f16* __restrict__ Tf, const f16* __restrict__ Pf,
+                                                 const f16* __restrict__ K16, const f16* __restrict__ Q16,
                                                  const float* __restrict__ S0,
                                                  const int32_t* __restrict__ chunk_start,
                                                  const int32_t* __restrict__ chunk_len,
@@ -400,12 +419,10 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
                                                  float* __restrict__ ST, float* __restrict__ ST2) {
     constexpr int C = 64;
     constexpr int NKP = DK / 32, NDB = DK / 16;
-    constexpr int UPR = DK / 8;                 // 16-byte units per K row
-    constexpr int KLD = DK / 16;                // 16-byte K loads per lane per converting wave per chunk
     constexpr bool want_o = MODE == kFull16;
-    __shared__ __attribute__((aligned(16))) f16 Ks[3][C * DK];
+    __shared__ __attribute__((aligned(16))) f16 Ks[4][C * DK];
     __shared__ __attribute__((aligned(16))) bf16 Vs[4][C * 16];
-    __shared__ __attribute__((aligned(16))) float Rs[4][2 * C];
+    __shared__ __attribute__((aligned(16))) float Rs[4][4 * C];        // decay rows in the first half
     __shared__ __attribute__((aligned(16))) f16 Ts[4][kPairs * kFrag];  // T pair fragments
     __shared__ __attribute__((aligned(16))) f16 Sx[2][NKP][kFrag];     // entering state, natural dk order
     __shared__ __attribute__((aligned(16))) f16 VNx[2][2][kFrag];      // V_new pairs (stacked positions)
@@ -434,18 +451,37 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
     const int NC = trans ? DK : DV;
     float* const STo = trans ? ST2 : ST;
     const int c0 = __builtin_amdgcn_readfirstlane(first[n]), c1 = __builtin_amdgcn_readfirstlane(first[n + 1]);
-    auto slot3 = [&](int c) { return (c - c0) % 3; };
-    auto slot4 = [&](int c) { return (c - c0) & 3; };
+    auto slot4 = [&](int c) { return (c - c0) & 3; };      // K tiles; V, decay rows and T
     // chunk start and length in scalar registers (uniform buffer descriptors);
     // a chunk past the sequence's last reads as empty
     auto chunk_s = [&](int c) { return c < c1 ? (int64_t)__builtin_amdgcn_readfirstlane(chunk_start[c]) : (int64_t)0; };
     auto chunk_L = [&](int c) {
         return c < c1 ? max(0, min(C, (int)__builtin_amdgcn_readfirstlane(chunk_len[c]))) : 0;
     };
-    auto swz = [](int row) { return ((((row & 3) << 1) | ((row >> 2) & 1) | (row & 8))) & (UPR - 1); };
+    auto swz = [](int row) { return tile_swz<DK>(row); };
     const int64_t sbase = ((int64_t)n * Nv + h) * DK * NC;
     typedef std::integral_constant<int, 0> P0;
     typedef std::integral_constant<int, 1> P1;
+    // V slice, decay rows and T of a chunk -> LDS: 9 buffer-to-LDS loads of 16
+    // bytes per lane (a chunk past the sequence's last reads as zero)
+    auto copy_vrt = [&](int c) {
+        const int sl = slot4(c);
+        const int64_t s = chunk_s(c);
+        const int L = chunk_L(c);
+        const uint32_t vbytes = (trans || L <= 0) ? 0u : (uint32_t)((L - 1) * Nv * DV + 16) * 2u;
+        const auto rv = rsrc_of(v, ((s * Nv + h) * DV + nb * 16) * 2, vbytes);
+#pragma unroll
+        for (int vh = 0; vh < 2; ++vh)                    // rows 32 vh .. 32 vh + 31, 16 columns
+            buffer_to_lds16(rv, &Vs[sl][vh * 512], ((32 * vh + (lane >> 1)) * Nv * DV + 8 * (lane & 1)) * 2);
+        const uint32_t rbytes = c < c1 ? 2 * C * 4 : 0u;
+        // decay rows: 512 bytes; lanes 32..63 repeat them into the slot's unused half
+        buffer_to_lds16(rsrc_of(R, (c < c1 ? (int64_t)c * Nv + h : 0) * 2 * C * 4, rbytes), &Rs[sl][0],
+                        (lane & 31) * 16);
+        const auto rt = rsrc_of(Tf, (c < c1 ? (int64_t)c * Nv + h : 0) * kPairs * kFrag * 2,
+                                c < c1 ? kPairs * kFrag * 2 : 0u);
+#pragma unroll
+        for (int p = 0; p < kPairs; ++p) buffer_to_lds16(rt, &Ts[sl][p * kFrag], p * kFrag * 2 + lane * 16);
+    };
 
     if (wv == 0) {
         // ======================================================== chain
@@ -465,18 +501,16 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
             }
         }
         h8 Sp[NKP];
-        // state pairs for Y; the output waves take the same fragments
-        auto make_pairs = [&](int c_next) {
+        // state pairs for Y; the output waves take the same fragments (published
+        // at the start of the chunk's step, read in the next step)
+        auto make_pairs = [&]() {
 #pragma unroll
-            for (int kp = 0; kp < NKP; ++kp) {
-                Sp[kp] = pack_pair(S[2 * kp], S[2 * kp + 1]);
-                if constexpr (want_o) *reinterpret_cast<h8*>(&Sx[(c_next - c0) & 1][kp][lane * 8]) = Sp[kp];
-            }
+            for (int kp = 0; kp < NKP; ++kp) Sp[kp] = pack_pair(S[2 * kp], S[2 * kp + 1]);
         };
         // K operand of Y: row 16 b + r, dk 32 kp + 8 qd .. + 7 (one 16-byte read)
         h8 ka[4][NKP];
         auto read_ka = [&](int c) {
-            const f16* Kb = Ks[slot3(c)];
+            const f16* Kb = Ks[slot4(c)];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 const int row = 16 * b + r;
@@ -509,16 +543,22 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
             return x;
         };
         VR vr;
-        make_pairs(c0);
+        make_pairs();
         lds_barrier();                                                            // prologue barrier
         if (c0 < c1) {
             read_ka(c0);
             vr = read_vr(c0);
         }
         auto step = [&](int c) {
-            const int sl = slot3(c), s4l = slot4(c);
-            const f16* Kb = Ks[sl];
-            // ---- Y = K S_in (operands read in the previous step)
+            const int s4l = slot4(c), s5l = slot4(c);
+            const f16* Kb = Ks[s4l];
+            // ---- region 1: S_in's pairs published; Y = K S_in (operands read in the
+            //      previous step) with the reads of this chunk's T pairs, decay rows
+            //      and K^T operands and the scaling of S by exp(G_last) interleaved
+            if constexpr (want_o) {
+#pragma unroll
+                for (int kp = 0; kp < NKP; ++kp) *reinterpret_cast<h8*>(&Sx[(c - c0) & 1][kp][lane * 8]) = Sp[kp];
+            }
             f32x4 Y[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b) Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -526,23 +566,16 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
             for (int kp = 0; kp < NKP; ++kp)
 #pragma unroll
                 for (int b = 0; b < 4; ++b) Y[b] = mfma16(ka[b][kp], Sp[kp], Y[b]);
+            h8 tf[kPairs];
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) S[db] = S[db] * (vr.a0 * vr.a1);
-            // the next chunk's K operand (Y has taken this chunk's), V and decay rows
-            VR vr_next = vr;
-            if (c + 1 < c1) {
-                read_ka(c + 1);
-                vr_next = read_vr(c + 1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // T of this chunk, the K^T operands of the update and the decay rows.
+            for (int p = 0; p < kPairs; ++p) tf[p] = *reinterpret_cast<const h8*>(&Ts[s5l][p * kFrag + lane * 8]);
+            f32x4 ed[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) ed[b] = *reinterpret_cast<const f32x4*>(&Rs[s5l][C + 16 * b + 4 * qd]);
             // K^T for state tile t: lane (qd, j) fetches the 4 dk values from
             // 32 (t / 2) + 8 (j & 3) + 4 (t % 2) of position 16 (2 tp + hh) + 4 qd + (j >> 2);
             // the transposing read hands lane (qd, r') the values of dk row
             // srow(t, r') at positions 32 tp + m(qd, e)
-            h8 tf[kPairs];
-#pragma unroll
-            for (int p = 0; p < kPairs; ++p) tf[p] = *reinterpret_cast<const h8*>(&Ts[s4l][p * kFrag + lane * 8]);
             h8 kt[NDB][2];
 #pragma unroll
             for (int t = 0; t < NDB; ++t) {
@@ -559,11 +592,19 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
                     kt[t][tp] = __builtin_bit_cast(h8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
                 }
             }
-            f32x4 ed[4];
+            const float al = vr.a0 * vr.a1;
 #pragma unroll
-            for (int b = 0; b < 4; ++b) ed[b] = *reinterpret_cast<const f32x4*>(&Rs[s4l][C + 16 * b + 4 * qd]);
-            __builtin_amdgcn_sched_barrier(0);                // every read above is issued before Z
-            // ---- Z = V - exp(G) Y, V_new = T Z
+            for (int db = 0; db < NDB; ++db) S[db] = S[db] * al;
+#pragma unroll
+            for (int i = 0; i < 4 * NKP; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one product
+                __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);       // three LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);       // two vector ops
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- region 2: Z = V - exp(G) Y, V_new = T Z, VD = exp(G_last - G) V_new,
+            //      with the next chunk's K operand read (past the sequence's last
+            //      chunk it reads a stale slot and is not used)
             f32x4 Z[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
@@ -578,6 +619,7 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
             VN[1] = mfma16(tf[1], zp0, zero4);
             VN[2] = mfma16(tf[3], zp1, mfma16(tf[2], zp0, zero4));
             VN[3] = mfma16(tf[5], zp1, mfma16(tf[4], zp0, zero4));
+            read_ka(c + 1);
             if constexpr (want_o) {
                 *reinterpret_cast<h8*>(&VNx[(c - c0) & 1][0][lane * 8]) = pack_pair(VN[0], VN[1]);
                 *reinterpret_cast<h8*>(&VNx[(c - c0) & 1][1][lane * 8]) = pack_pair(VN[2], VN[3]);
@@ -586,12 +628,14 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
 #pragma unroll
             for (int b = 0; b < 4; ++b) VD[b] = VN[b] * ed[b];
             const h8 vd0 = pack_pair(VD[0], VD[1]), vd1 = pack_pair(VD[2], VD[3]);
-            // ---- S_out = exp(G_last) S_in + K^T VD
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- region 3: S_out = exp(G_last) S_in + K^T VD, with the next chunk's
+            //      V and decay rows read
 #pragma unroll
             for (int t = 0; t < NDB; ++t) S[t] = mfma16(kt[t][1], vd1, mfma16(kt[t][0], vd0, S[t]));
+            vr = read_vr(c + 1);
             __builtin_amdgcn_sched_barrier(0);
-            vr = vr_next;
-            make_pairs(c + 1);
+            make_pairs();
             lds_barrier();                                                        // end of step c
         };
         for (int c = c0; c < c1; ++c) step(c);
@@ -607,11 +651,17 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
     }
 
     // ============================================================ helper waves
-    // wavefront 1: output rows 0..31 (blocks 0, 1) and the V / decay-row copies;
-    // wavefronts 2, 3: output block 2 / 3 and the K rows 0..31 / 32..63.
-    auto helper = [&](auto nblk_t, auto convert_t) {
+    // wavefront 1: output rows 0..31 (blocks 0, 1) and the copies of the V slice,
+    // decay rows and T; wavefront 2: output block 2 and the copies of K rows
+    // 0..31; wavefront 3: output block 3 and the copies of K rows 32..63. A
+    // helper reads no LDS array it copies into (the compiler would otherwise wait
+    // for the copies before each such read). Every copy is a 16-byte buffer-to-LDS load
+    // of chunk c + 3 issued at the start of step c; the wave waits for the
+    // previous step's copies (all of its vector memory operations issued after
+    // them may still be in flight) before the step's closing barrier.
+    auto helper = [&](auto nblk_t, auto role_t) {
         constexpr int NBL = decltype(nblk_t)::value;       // output row blocks of this wave
-        constexpr bool CONV = decltype(convert_t)::value;   // converts K rows (else copies V and decay rows)
+        constexpr int ROLE = decltype(role_t)::value;       // 1: V, decay rows, T; 2: K rows 0..31; 3: K rows 32..63
         int blk[NBL];
         if constexpr (NBL == 2) {
             blk[0] = 0;
@@ -619,64 +669,39 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
         } else {
             blk[0] = wv;
         }
-        const int rbase = (wv - 2) * 32;                    // K rows of a converting wave
         const int ob = out_f32 ? 4 : 2;
-        // ---- K rows: raw bf16 of the chunks of each parity, loaded four steps
-        //      before their chunk is read (two before they are converted)
-        u4 kraw[2][KLD];
-        auto load_k = [&](int c, u4* dst) {
-            const int64_t s = chunk_s(c);
-            const int L = chunk_L(c);
-            const auto rk = rsrc_of(k, (s * Nk + kh) * DK * 2, L > 0 ? (uint32_t)((L - 1) * Nk * DK + DK) * 2u : 0u);
+        // ---- K rows of a chunk (half of the fp16 tile: DK / 16 loads) -> LDS
+        auto copy_k = [&](int c) {
+            const int half = wv - 2;
+            const auto rk = rsrc_of(K16, (c < c1 ? (int64_t)c * Nk + kh : 0) * C * DK * 2, c < c1 ? C * DK * 2 : 0u);
 #pragma unroll
-            for (int i = 0; i < KLD; ++i) {
-                const int f = i * 64 + lane;
-                const int row = rbase + f / UPR, u = f % UPR;
-                dst[i] = buf_load16(rk, (row * Nk * DK + 8 * u) * 2);
+            for (int i = 0; i < DK / 16; ++i) {
+                const int off = (half * (DK / 16) + i) * 1024;
+                buffer_to_lds16(rk, reinterpret_cast<const char*>(Ks[slot4(c)]) + off, off + lane * 16);
             }
         };
-        auto store_k = [&](int c, const u4* src) {
-            f16* dst = Ks[slot3(c)];
-#pragma unroll
-            for (int i = 0; i < KLD; ++i) {
-                const int f = i * 64 + lane;
-                const int row = rbase + f / UPR, u = f % UPR;
-                *reinterpret_cast<h8*>(&dst[row * DK + (u ^ swz(row)) * 8]) = bf16x8_to_f16(src[i]);
-            }
-        };
-        // ---- V slice, decay rows and T of a chunk -> LDS (9 buffer-to-LDS loads)
-        auto copy_vr = [&](int c) {
-            const int sl = slot4(c);
-            const int64_t s = chunk_s(c);
-            const int L = chunk_L(c);
-            const uint32_t vbytes = (trans || L <= 0) ? 0u : (uint32_t)((L - 1) * Nv * DV + 16) * 2u;
-            const auto rv = rsrc_of(v, ((s * Nv + h) * DV + nb * 16) * 2, vbytes);
-#pragma unroll
-            for (int vh = 0; vh < 2; ++vh)                // rows 32 vh .. 32 vh + 31, 16 columns
-                buffer_to_lds16(rv, &Vs[sl][vh * 512], ((32 * vh + (lane >> 1)) * Nv * DV + 8 * (lane & 1)) * 2);
-            const uint32_t rbytes = c < c1 ? 2 * C * 4 : 0u;
-            if (lane < 32)                                // decay rows: 512 bytes
-                buffer_to_lds16(rsrc_of(R, (c < c1 ? (int64_t)c * Nv + h : 0) * 2 * C * 4, rbytes), &Rs[sl][0],
-                                lane * 16);
-            const auto rt = rsrc_of(Tf, (c < c1 ? (int64_t)c * Nv + h : 0) * kPairs * kFrag * 2,
-                                    c < c1 ? kPairs * kFrag * 2 : 0u);
-#pragma unroll
-            for (int p = 0; p < kPairs; ++p) buffer_to_lds16(rt, &Ts[sl][p * kFrag], p * kFrag * 2 + lane * 16);
-        };
-        // ---- output operands: Q rows (bf16) of chunk c loaded in step c - 2; the
-        //      score pairs of chunk c loaded in step c - 1 and used in step c + 1
-        u4 qraw[2][NBL][NKP];
+        constexpr int NDMA = ROLE == 1 ? 3 + kPairs : DK / 16;    // copies per step
+        // ---- output operands: the Q rows (fp16 tile) and score pairs of chunk c,
+        //      loaded in step c - 1 and used in step c + 1, when the chunk's
+        //      entering state and V_new (published in step c) are in LDS
+        h8 qraw[2][NBL][NKP];
         h8 praw[2][2];
-        f32x4 part[NBL];                                    // exp(G) (Q S_in)^T of the pending chunk
-        auto load_q = [&](int c, u4 (*dst)[NKP]) {
-            const int64_t s = chunk_s(c);
-            const int L = chunk_L(c);
-            const auto rq = rsrc_of(q, (s * Nk + kh) * DK * 2, L > 0 ? (uint32_t)((L - 1) * Nk * DK + DK) * 2u : 0u);
+        float egraw[2][NBL];                                // exp(G) of this lane's output row
+        auto load_eg = [&](int c, float* dst) {
+            const auto rr = rsrc_of(R, (c < c1 ? (int64_t)c * Nv + h : 0) * 2 * C * 4, c < c1 ? C * 4 : 0u);
 #pragma unroll
             for (int i = 0; i < NBL; ++i)
+                dst[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, (16 * blk[i] + r) * 4, 0, 0));
+        };
+        auto load_q = [&](int c, h8 (*dst)[NKP]) {
+            const auto rq = rsrc_of(Q16, (c < c1 ? (int64_t)c * Nk + kh : 0) * C * DK * 2, c < c1 ? C * DK * 2 : 0u);
+#pragma unroll
+            for (int i = 0; i < NBL; ++i) {
+                const int row = 16 * blk[i] + r;
 #pragma unroll
                 for (int kp = 0; kp < NKP; ++kp)
-                    dst[i][kp] = buf_load16(rq, ((16 * blk[i] + r) * Nk * DK + 32 * kp + 8 * qd) * 2);
+                    dst[i][kp] = __builtin_bit_cast(h8, buf_load16(rq, (row * DK + ((4 * kp + qd) ^ tile_swz<DK>(row)) * 8) * 2));
+            }
         };
         // the two score pairs this wave needs: blocks 0 and 1 (pairs 0, 1) or
         // block b >= 2 (pairs 2 b - 2, 2 b - 1)
@@ -687,8 +712,8 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
 #pragma unroll
             for (int p = 0; p < 2; ++p) dst[p] = __builtin_bit_cast(h8, buf_load16(rp, (pbase + p) * kFrag * 2 + lane * 16));
         };
-        // O of chunk cc (stored only when cc is one of this sequence's chunks):
-        // its S part plus the score block times V_new, transposed, scaled
+        // O of chunk cc = scale [exp(G) (Q S_in) + P V_new], formed transposed
+        // (stored only when cc is one of this sequence's chunks)
         auto finish = [&](int cc, auto parc) {
             constexpr int PC = decltype(parc)::value;       // parity of chunk cc
             const bool valid = cc >= c0 && cc < c1;
@@ -696,15 +721,21 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
             const int L = valid ? chunk_L(cc) : 0;
             const auto ro = rsrc_of(o, ((s * Nv + h) * DV + nb * 16) * ob,
                                     L > 0 ? (uint32_t)(((L - 1) * Nv * DV + 16) * ob) : 0u);
+            h8 sx[NKP];
+#pragma unroll
+            for (int kp = 0; kp < NKP; ++kp) sx[kp] = *reinterpret_cast<const h8*>(&Sx[PC][kp][lane * 8]);
             const h8 vn0 = *reinterpret_cast<const h8*>(&VNx[PC][0][lane * 8]);
             const h8 vn1 = *reinterpret_cast<const h8*>(&VNx[PC][1][lane * 8]);
 #pragma unroll
             for (int i = 0; i < NBL; ++i) {
-                f32x4 acc;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kp = 0; kp < NKP; ++kp) acc = mfma16(sx[kp], qraw[PC][i][kp], acc);
+                acc = acc * egraw[PC][i];
                 if constexpr (NBL == 2) {
-                    acc = mfma16(vn0, praw[PC][i], part[i]);
+                    acc = mfma16(vn0, praw[PC][i], acc);
                 } else {
-                    acc = mfma16(vn1, praw[PC][1], mfma16(vn0, praw[PC][0], part[i]));
+                    acc = mfma16(vn1, praw[PC][1], mfma16(vn0, praw[PC][0], acc));
                 }
                 const f32x4 x = acc * scale;
                 const int off = ((16 * blk[i] + r) * Nv * DV + 4 * qd) * ob;   // rows past the end fall outside ro
@@ -718,65 +749,49 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
             }
         };
 #pragma unroll
-        for (int i = 0; i < NBL; ++i) part[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < NBL; ++i)
+#pragma unroll
+            for (int kp = 0; kp < NKP; ++kp) qraw[1][i][kp] = h8{};
         praw[1][0] = praw[1][1] = h8{};
-        // prologue: K rows of the first two chunks converted, of the next two in
-        // flight; V and decay rows of the first three chunks copied
-        if constexpr (CONV) {
-            load_k(c0, kraw[0]);
-            load_k(c0 + 1, kraw[1]);
-            store_k(c0, kraw[0]);
-            store_k(c0 + 1, kraw[1]);
-            load_k(c0 + 2, kraw[0]);
-            load_k(c0 + 3, kraw[1]);
-        } else {
-            copy_vr(c0);
-            copy_vr(c0 + 1);
-            wait_vmem();
-            copy_vr(c0 + 2);
-        }
+#pragma unroll
+        for (int i = 0; i < NBL; ++i) egraw[1][i] = 0.f;
+        // prologue: the copies of the first three chunks landed
+        auto copy = [&](int c) {
+            if constexpr (ROLE == 1) copy_vrt(c);
+            else copy_k(c);
+        };
+        copy(c0);
+        copy(c0 + 1);
+        copy(c0 + 2);
+        wait_vmem();
         if constexpr (want_o) {
             load_q(c0, qraw[0]);
-            load_q(c0 + 1, qraw[1]);
             load_p(c0, praw[0]);
+            load_eg(c0, egraw[0]);
         }
         lds_barrier();                                                            // prologue barrier
         auto step = [&](int c, auto par) {
             constexpr int PAR = decltype(par)::value;
-            if constexpr (!CONV) copy_vr(c + 3);
-            if constexpr (CONV) {
-                store_k(c + 2, kraw[PAR]);                  // K rows of chunk c + 2 (loaded in step c - 2)
-                load_k(c + 4, kraw[PAR]);
-            }
+            copy(c + 3);
             if constexpr (want_o) {
                 finish(c - 1, std::integral_constant<int, PAR ^ 1>{});
                 load_p(c + 1, praw[PAR ^ 1]);
-                // (Q S_in)^T of chunk c
-                h8 sx[NKP];
-#pragma unroll
-                for (int kp = 0; kp < NKP; ++kp) sx[kp] = *reinterpret_cast<const h8*>(&Sx[PAR][kp][lane * 8]);
-#pragma unroll
-                for (int i = 0; i < NBL; ++i) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kp = 0; kp < NKP; ++kp) acc = mfma16(sx[kp], bf16x8_to_f16(qraw[PAR][i][kp]), acc);
-                    part[i] = acc * Rs[slot4(c)][16 * blk[i] + r];
-                }
-                load_q(c + 2, qraw[PAR]);
+                load_q(c + 1, qraw[PAR ^ 1]);
+                load_eg(c + 1, egraw[PAR ^ 1]);
             }
-            // V, decay rows and T of chunk c + 2 (copied in step c - 1) have landed:
-            // every vector memory operation of this wave issued after them (the
-            // rest of step c - 1 and all of step c) may still be in flight
-            if constexpr (!CONV) {
-                if constexpr (want_o) wait_vmem_but<2 * (NBL * NKP + 2 + NBL) + 9>();
-                else wait_vmem_but<9>();
-            }
+            // the copies of chunk c + 2 (issued in step c - 1) have landed
+            constexpr int after = want_o ? NBL + 2 + NBL * NKP + NBL : 0;   // operations per step after the copies
+            if constexpr (NDMA > 0) wait_vmem_but<2 * after + NDMA>();
             lds_barrier();                                                        // end of step c
         };
-        for (int c = c0; c < c1; c += 2) {
+        // both steps of a pair in the loop body on every path, so that the
+        // compiler's waits for loads issued two steps earlier count both steps
+        int c = c0;
+        for (; c + 1 < c1; c += 2) {
             step(c, P0{});
-            if (c + 1 < c1) step(c + 1, P1{});
+            step(c + 1, P1{});
         }
+        if (c < c1) step(c, P0{});
         if constexpr (want_o) {                             // the last chunk's output
             if (c1 > c0) {
                 if ((c1 - 1 - c0) & 1) finish(c1 - 1, P1{});
@@ -785,8 +800,9 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
         }
         wait_vmem();
     };
-    if (wv == 1) helper(std::integral_constant<int, 2>{}, std::false_type{});
-    else helper(std::integral_constant<int, 1>{}, std::true_type{});
+    if (wv == 1) helper(std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});
+    else if (wv == 2) helper(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
+    else helper(std::integral_constant<int, 1>{}, std::integral_constant<int, 3>{});
 }
 
 // ============================================================ launch
@@ -802,23 +818,23 @@ static hipError_t launch_dims(const LaunchArgs& a, hipEvent_t* ev) {
     mark(2);
     if (NT > 0)
         k_prep<DK><<<dim3(NT, a.Nk), 256, 0, st>>>(k, q, a.beta, a.beta_f32, a.g, a.chunk_start, a.chunk_len, a.Nk,
-                                                     a.Nv, Tf, Pf, R);
+                                                     a.Nv, Tf, Pf, R, (f16*)a.K16, (f16*)a.Q16);
     mark(3);
     mark(4);
     if (a.N > 0 && !a.prep_only) {
         if (a.nseg > 0) {
             k_chunk16<DK, DV, kSegment16><<<dim3(a.nseg, a.Nv, DV / 16 + DK / 16), 256, 0, st>>>(
-                q, k, v, R, Tf, Pf, nullptr, a.chunk_start, a.chunk_len, a.seg_first, a.Nk, a.Nv, a.scale,
-                a.out_f32, nullptr, a.Sloc, a.Mseg);
+                q, k, v, R, Tf, Pf, (const f16*)a.K16, (const f16*)a.Q16, nullptr, a.chunk_start, a.chunk_len,
+                a.seg_first, a.Nk, a.Nv, a.scale, a.out_f32, nullptr, a.Sloc, a.Mseg);
             const hipError_t e = launch_segment_scan(a);
             if (e != hipSuccess) return e;
             k_chunk16<DK, DV, kFull16><<<dim3(a.nseg, a.Nv, DV / 16), 256, 0, st>>>(
-                q, k, v, R, Tf, Pf, a.Sstart, a.chunk_start, a.chunk_len, a.seg_first, a.Nk, a.Nv, a.scale,
-                a.out_f32, a.o, nullptr, nullptr);
+                q, k, v, R, Tf, Pf, (const f16*)a.K16, (const f16*)a.Q16, a.Sstart, a.chunk_start, a.chunk_len,
+                a.seg_first, a.Nk, a.Nv, a.scale, a.out_f32, a.o, nullptr, nullptr);
         } else {
             k_chunk16<DK, DV, kFull16><<<dim3(a.N, a.Nv, DV / 16), 256, 0, st>>>(
-                q, k, v, R, Tf, Pf, a.S0, a.chunk_start, a.chunk_len, a.seq_first, a.Nk, a.Nv, a.scale, a.out_f32,
-                a.o, a.ST, nullptr);
+                q, k, v, R, Tf, Pf, (const f16*)a.K16, (const f16*)a.Q16, a.S0, a.chunk_start, a.chunk_len,
+                a.seq_first, a.Nk, a.Nv, a.scale, a.out_f32, a.o, a.ST, nullptr);
         }
     }
     mark(5);

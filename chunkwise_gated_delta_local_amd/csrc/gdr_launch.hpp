@@ -29,6 +29,8 @@ struct LaunchArgs {
     void* T16;                       // T = A diag(beta), fp16 pair fragments [cap][Nv][6][64][8] (fp16 path)
     void* P16;                       // score block (Q K^T) (.) D, same layout (fp16 path)
     float* R16;                      // decay rows exp(G), exp(G_last - G): [cap][Nv][2][64] (fp16 path)
+    void* K16;                       // K rows in fp16, [cap][Nk][64][dk], 16-byte units swizzled (fp16 path)
+    void* Q16;                       // Q rows, same layout (fp16 path)
     bool reference;                  // run the five separate kernels even for bf16
     bool prep_only;                  // fp16 path: run k_prep only (debug copies of T, P, R)
     // segment-parallel state passing (nseg == 0: one serial pass per sequence)
