@@ -422,8 +422,6 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
     constexpr bool want_o = MODE == kFull16;
     __shared__ __attribute__((aligned(16))) f16 Ks[4][C * DK];
     __shared__ __attribute__((aligned(16))) bf16 Vs[4][C * 16];
-    __shared__ __attribute__((aligned(16))) float Rs[4][4 * C];        // decay rows in the first half
-    __shared__ __attribute__((aligned(16))) f16 Ts[4][kPairs * kFrag];  // T pair fragments
     __shared__ __attribute__((aligned(16))) f16 Sx[2][NKP][kFrag];     // entering state, natural dk order
     __shared__ __attribute__((aligned(16))) f16 VNx[2][2][kFrag];      // V_new pairs (stacked positions)
 
@@ -462,9 +460,9 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
     const int64_t sbase = ((int64_t)n * Nv + h) * DK * NC;
     typedef std::integral_constant<int, 0> P0;
     typedef std::integral_constant<int, 1> P1;
-    // V slice, decay rows and T of a chunk -> LDS: 9 buffer-to-LDS loads of 16
-    // bytes per lane (a chunk past the sequence's last reads as zero)
-    auto copy_vrt = [&](int c) {
+    // V slice of a chunk -> LDS: 2 buffer-to-LDS loads of 16 bytes per lane
+    // (a chunk past the sequence's last reads as zero)
+    auto copy_v = [&](int c) {
         const int sl = slot4(c);
         const int64_t s = chunk_s(c);
         const int L = chunk_L(c);
@@ -473,14 +471,6 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
 #pragma unroll
         for (int vh = 0; vh < 2; ++vh)                    // rows 32 vh .. 32 vh + 31, 16 columns
             buffer_to_lds16(rv, &Vs[sl][vh * 512], ((32 * vh + (lane >> 1)) * Nv * DV + 8 * (lane & 1)) * 2);
-        const uint32_t rbytes = c < c1 ? 2 * C * 4 : 0u;
-        // decay rows: 512 bytes; lanes 32..63 repeat them into the slot's unused half
-        buffer_to_lds16(rsrc_of(R, (c < c1 ? (int64_t)c * Nv + h : 0) * 2 * C * 4, rbytes), &Rs[sl][0],
-                        (lane & 31) * 16);
-        const auto rt = rsrc_of(Tf, (c < c1 ? (int64_t)c * Nv + h : 0) * kPairs * kFrag * 2,
-                                c < c1 ? kPairs * kFrag * 2 : 0u);
-#pragma unroll
-        for (int p = 0; p < kPairs; ++p) buffer_to_lds16(rt, &Ts[sl][p * kFrag], p * kFrag * 2 + lane * 16);
     };
 
     if (wv == 0) {
@@ -519,12 +509,9 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
                     ka[b][kp] = *reinterpret_cast<const h8*>(&Kb[row * DK + ((4 * kp + qd) ^ swz(row)) * 8]);
             }
         };
-        // V rows 16 b + 4 qd + j of column r (transposing reads of the bf16 tile),
-        // exp(G) of those rows and exp(G_last) of the chunk
+        // V rows 16 b + 4 qd + j of column r (transposing reads of the bf16 tile)
         struct VR {
             s4 v[4];
-            f32x4 eg[4];
-            float a0, a1;                         // exp(G_last) = a0 a1
         };
         auto read_vr = [&](int c) {
             VR x;
@@ -533,16 +520,36 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
             for (int b = 0; b < 4; ++b) {
                 const int row = 16 * b + 4 * qd + (r >> 2);
                 x.v[b] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)&Vs[sl][row * 16 + 4 * (r & 3)]);
-                x.eg[b] = *reinterpret_cast<const f32x4*>(&Rs[sl][16 * b + 4 * qd]);
             }
-            // exp(G_last) = exp(G_0) exp(G_last - G_0), from the rows themselves (no
-            // scalar load of the chunk length inside the chain: its wait would also
-            // wait for every LDS read in flight)
-            x.a0 = Rs[sl][0];
-            x.a1 = Rs[sl][C];
+            return x;
+        };
+        // T pairs and decay rows of a chunk, loaded from global memory a step
+        // ahead (the chain's only vector memory operations): exp(G) and
+        // exp(G_last - G) of rows 16 b + 4 qd + j, and exp(G_last) =
+        // exp(G_0) exp(G_last - G_0) from the rows themselves
+        struct TR {
+            h8 tf[kPairs];
+            f32x4 eg[4], ed[4];
+            float a0, a1;
+        };
+        auto load_tr = [&](int c) {
+            TR x;
+            const bool ok = c < c1;
+            const auto rt = rsrc_of(Tf, (ok ? (int64_t)c * Nv + h : 0) * kPairs * kFrag * 2, ok ? kPairs * kFrag * 2 : 0u);
+            const auto rr = rsrc_of(R, (ok ? (int64_t)c * Nv + h : 0) * 2 * C * 4, ok ? 2 * C * 4 : 0u);
+#pragma unroll
+            for (int p = 0; p < kPairs; ++p) x.tf[p] = __builtin_bit_cast(h8, buf_load16(rt, p * kFrag * 2 + lane * 16));
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                x.eg[b] = __builtin_bit_cast(f32x4, buf_load16(rr, (16 * b + 4 * qd) * 4));
+                x.ed[b] = __builtin_bit_cast(f32x4, buf_load16(rr, (C + 16 * b + 4 * qd) * 4));
+            }
+            x.a0 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, 0, 0, 0));
+            x.a1 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, C * 4, 0, 0));
             return x;
         };
         VR vr;
+        TR tr = load_tr(c0);
         make_pairs();
         lds_barrier();                                                            // prologue barrier
         if (c0 < c1) {
@@ -550,11 +557,12 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
             vr = read_vr(c0);
         }
         auto step = [&](int c) {
-            const int s4l = slot4(c), s5l = slot4(c);
+            const int s4l = slot4(c);
             const f16* Kb = Ks[s4l];
+            const TR tr_next = load_tr(c + 1);
             // ---- region 1: S_in's pairs published; Y = K S_in (operands read in the
-            //      previous step) with the reads of this chunk's T pairs, decay rows
-            //      and K^T operands and the scaling of S by exp(G_last) interleaved
+            //      previous step) with the reads of this chunk's K^T operands and the
+            //      scaling of S by exp(G_last) interleaved
             if constexpr (want_o) {
 #pragma unroll
                 for (int kp = 0; kp < NKP; ++kp) *reinterpret_cast<h8*>(&Sx[(c - c0) & 1][kp][lane * 8]) = Sp[kp];
@@ -566,12 +574,8 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
             for (int kp = 0; kp < NKP; ++kp)
 #pragma unroll
                 for (int b = 0; b < 4; ++b) Y[b] = mfma16(ka[b][kp], Sp[kp], Y[b]);
-            h8 tf[kPairs];
-#pragma unroll
-            for (int p = 0; p < kPairs; ++p) tf[p] = *reinterpret_cast<const h8*>(&Ts[s5l][p * kFrag + lane * 8]);
-            f32x4 ed[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) ed[b] = *reinterpret_cast<const f32x4*>(&Rs[s5l][C + 16 * b + 4 * qd]);
+            const h8* tf = tr.tf;
+            const f32x4* ed = tr.ed;
             // K^T for state tile t: lane (qd, j) fetches the 4 dk values from
             // 32 (t / 2) + 8 (j & 3) + 4 (t % 2) of position 16 (2 tp + hh) + 4 qd + (j >> 2);
             // the transposing read hands lane (qd, r') the values of dk row
@@ -592,7 +596,7 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
                     kt[t][tp] = __builtin_bit_cast(h8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
                 }
             }
-            const float al = vr.a0 * vr.a1;
+            const float al = tr.a0 * tr.a1;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) S[db] = S[db] * al;
 #pragma unroll
@@ -610,7 +614,7 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
             for (int b = 0; b < 4; ++b) {
                 const f32x4 vv = bf16x4_to_f32(vr.v[b]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) Z[b][j] = vv[j] - vr.eg[b][j] * Y[b][j];
+                for (int j = 0; j < 4; ++j) Z[b][j] = vv[j] - tr.eg[b][j] * Y[b][j];
             }
             const h8 zp0 = pack_pair(Z[0], Z[1]), zp1 = pack_pair(Z[2], Z[3]);
             const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -636,6 +640,7 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
             vr = read_vr(c + 1);
             __builtin_amdgcn_sched_barrier(0);
             make_pairs();
+            tr = tr_next;
             lds_barrier();                                                        // end of step c
         };
         for (int c = c0; c < c1; ++c) step(c);
@@ -651,8 +656,8 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
     }
 
     // ============================================================ helper waves
-    // wavefront 1: output rows 0..31 (blocks 0, 1) and the copies of the V slice,
-    // decay rows and T; wavefront 2: output block 2 and the copies of K rows
+    // wavefront 1: output rows 0..31 (blocks 0, 1) and the copies of the V slice;
+    // wavefront 2: output block 2 and the copies of K rows
     // 0..31; wavefront 3: output block 3 and the copies of K rows 32..63. A
     // helper reads no LDS array it copies into (the compiler would otherwise wait
     // for the copies before each such read). Every copy is a 16-byte buffer-to-LDS load
@@ -661,7 +666,7 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
     // them may still be in flight) before the step's closing barrier.
     auto helper = [&](auto nblk_t, auto role_t) {
         constexpr int NBL = decltype(nblk_t)::value;       // output row blocks of this wave
-        constexpr int ROLE = decltype(role_t)::value;       // 1: V, decay rows, T; 2: K rows 0..31; 3: K rows 32..63
+        constexpr int ROLE = decltype(role_t)::value;       // 1: V; 2: K rows 0..31; 3: K rows 32..63
         int blk[NBL];
         if constexpr (NBL == 2) {
             blk[0] = 0;
@@ -680,7 +685,7 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
                 buffer_to_lds16(rk, reinterpret_cast<const char*>(Ks[slot4(c)]) + off, off + lane * 16);
             }
         };
-        constexpr int NDMA = ROLE == 1 ? 3 + kPairs : DK / 16;    // copies per step
+        constexpr int NDMA = ROLE == 1 ? 2 : DK / 16;    // copies per step
         // ---- output operands: the Q rows (fp16 tile) and score pairs of chunk c,
         //      loaded in step c - 1 and used in step c + 1, when the chunk's
         //      entering state and V_new (published in step c) are in LDS
@@ -757,7 +762,7 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
         for (int i = 0; i < NBL; ++i) egraw[1][i] = 0.f;
         // prologue: the copies of the first three chunks landed
         auto copy = [&](int c) {
-            if constexpr (ROLE == 1) copy_vrt(c);
+            if constexpr (ROLE == 1) copy_v(c);
             else copy_k(c);
         };
         copy(c0);
