@@ -28,7 +28,8 @@ EXPORTED = ("gdr_validate", "gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd_debug
             "gdr_chunk_fwd_segmented_workspace_size", "gdr_chunk_fwd_segmented",
             "gdr_chunk_bwd_workspace_size", "gdr_chunk_bwd",
             "gdr_status_string", "gdr_last_error_message",
-            "gdr_peak_copy", "gdr_peak_mfma", "gdr_peak_mfma_flops")
+            "gdr_peak_copy", "gdr_peak_mfma", "gdr_peak_mfma_flops",
+            "gdr_chunk_fwd_noalloc", "gdr_chunk_fwd_noalloc_max_workspace")
 
 
 class Problem(ctypes.Structure):
@@ -87,6 +88,10 @@ def load_library():
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_last_error_message.argtypes = []
     lib.gdr_last_error_message.restype = ctypes.c_char_p
+    lib.gdr_chunk_fwd_noalloc.argtypes = fwd_args[:12] + [P]
+    lib.gdr_chunk_fwd_noalloc.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_noalloc_max_workspace.argtypes = []
+    lib.gdr_chunk_fwd_noalloc_max_workspace.restype = ctypes.c_size_t
     lib.gdr_peak_copy.argtypes = [P, P, ctypes.c_size_t, ctypes.c_int32, P]
     lib.gdr_peak_copy.restype = ctypes.c_int
     lib.gdr_peak_mfma.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P]
@@ -214,6 +219,23 @@ def chunk_fwd(q, k, v, beta, g=None, scale=None, initial_state=None, output_fina
     else:
         _check(lib.gdr_chunk_fwd_segmented(*args, None))
     del keep
+    return o, S_T
+
+
+def chunk_fwd_noalloc(q, k, v, beta, g=None, scale=None, initial_state=None, output_final_state=True,
+                      cu_seqlens=None, cu_seqlens_cpu=None, chunk_size=64, out_dtype=None):
+    """As chunk_fwd, through gdr_chunk_fwd_noalloc: the library's per-GPU
+    scratch array serves as the workspace (o and the final state are still
+    allocated here, by torch). Calls on one GPU must not overlap."""
+    lib = load_library()
+    prob, o, S_T, cu_dev, cu_host, scale, ins = _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens,
+                                                         cu_seqlens_cpu, chunk_size, output_final_state,
+                                                         out_dtype, workspace=False)
+    q, k, v, beta, g, initial_state = ins
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib.gdr_chunk_fwd_noalloc(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     ctypes.c_float(scale), _ptr(initial_state), _ptr(cu_dev), _ptr(cu_host),
+                                     _ptr(o), _ptr(S_T), ctypes.c_void_p(stream)))
     return o, S_T
 
 

@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "gdr.h"
 #include "gdr_launch.hpp"
 
@@ -353,6 +355,37 @@ gdr_status_t run(const gdr_problem_t* p, const void* q, const void* k, const voi
     return GDR_OK;
 }
 
+// ---------------------------------------------------------------- no-allocation scratch
+// gdr_chunk_fwd_noalloc's workspace: a file-scope device array, one copy per GPU
+// (the loader places it with the code object on every device the library runs
+// on; it lives until the process ends). Host code never passes `scratch` itself
+// to a kernel or a copy (on the host it is only a stand-in for the symbol): the
+// device address of each GPU's copy comes from hipGetSymbolAddress, taken once
+// per device with that device current.
+constexpr size_t kNoAllocScratchBytes = (size_t)256 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+gdr_status_t scratch_of_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(GDR_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(GDR_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return GDR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -388,6 +421,26 @@ gdr_status_t gdr_chunk_fwd(const gdr_problem_t* p, const void* q, const void* k,
     return run(p, q, k, v, g, beta, scale, initial_state, cu_dev, cu_host, o, final_state, workspace,
                workspace_bytes, stream, nullptr, false, nullptr, nullptr);
 }
+
+gdr_status_t gdr_chunk_fwd_noalloc(const gdr_problem_t* p, const void* q, const void* k, const void* v,
+                                   const float* g, const void* beta, float scale, const float* initial_state,
+                                   const int32_t* cu_dev, const int32_t* cu_host, void* o, float* final_state,
+                                   void* stream) {
+    gdr_status_t st = check_problem(p);
+    if (st != GDR_OK) return st;
+    const size_t need = make_plan(p).production;
+    if (need > kNoAllocScratchBytes)
+        return fail(GDR_ERR_WORKSPACE,
+                    "problem needs %zu bytes of scratch; gdr_chunk_fwd_noalloc holds %zu per GPU "
+                    "(use gdr_chunk_fwd with a caller workspace)", need, kNoAllocScratchBytes);
+    void* ws = nullptr;
+    st = scratch_of_current_device(&ws);
+    if (st != GDR_OK) return st;
+    return run(p, q, k, v, g, beta, scale, initial_state, cu_dev, cu_host, o, final_state, ws,
+               kNoAllocScratchBytes, stream, nullptr, false, nullptr, nullptr);
+}
+
+size_t gdr_chunk_fwd_noalloc_max_workspace(void) { return kNoAllocScratchBytes; }
 
 gdr_status_t gdr_chunk_fwd_debug(const gdr_problem_t* p, const void* q, const void* k, const void* v,
                                  const float* g, const void* beta, float scale, const float* initial_state,

@@ -164,6 +164,33 @@ gdr_status_t gdr_chunk_fwd(const gdr_problem_t* problem,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdr_chunk_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and results as gdr_chunk_fwd, with the workspace taken
+ * from a scratch array the library holds on every GPU it runs on (256 MiB per
+ * GPU, kept until the process ends). The caller passes inputs and outputs only.
+ *   Arguments and layouts as for gdr_chunk_fwd; the buffers and `stream`
+ *   belong to the current device.
+ *   Returns GDR_ERR_WORKSPACE (nothing enqueued) when the problem needs more
+ *   than gdr_chunk_fwd_noalloc_max_workspace() bytes of workspace (what
+ *   gdr_chunk_fwd_workspace_size reports); GDR_ERR_HIP when the scratch
+ *   array's address cannot be obtained. Allocates nothing (no hipMalloc or
+ *   hipFree, on the first call either).
+ *   Every call on one GPU uses the same scratch: calls that overlap on one GPU
+ *   (on different streams, or from different threads without ordering) race,
+ *   and the caller must order them. Nothing in the scratch has to start at zero.
+ */
+gdr_status_t gdr_chunk_fwd_noalloc(const gdr_problem_t* problem,
+                                   const void* q, const void* k, const void* v,
+                                   const float* g, const void* beta, float scale,
+                                   const float* initial_state,
+                                   const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                                   void* o, float* final_state, void* stream);
+
+/* Bytes of scratch gdr_chunk_fwd_noalloc holds per GPU (its largest workspace). */
+size_t gdr_chunk_fwd_noalloc_max_workspace(void);
+
+/*
  * Segment-parallel state passing on one GPU: the same result as gdr_chunk_fwd
  * (up to rounding order), for inputs whose serial state pass would leave most
  * compute units idle: few sequences times value heads, and long sequences.

@@ -246,3 +246,21 @@ def test_recurrent_rejects_before_launch(lib):
     bad = list(args)
     bad[11] = None                                 # o missing
     assert lib.gdr_recurrent_fwd(*bad) == 1
+
+
+def test_noalloc_rejects_oversized_problem_before_any_device_call(lib):
+    """gdr_chunk_fwd_noalloc refuses a problem whose workspace exceeds its
+    per-GPU scratch with GDR_ERR_WORKSPACE, before touching a device."""
+    from chunkwise_gated_delta_local_amd import api
+    cap = lib.gdr_chunk_fwd_noalloc_max_workspace()
+    assert cap == 256 << 20
+    p = prob(batch=1, seq_len=65536, Nk=16, Nv=32, dk=128, dv=128, num_seqs=1)
+    assert api.workspace_size(p) > cap
+    fake = ctypes.c_void_p(1 << 20)          # never dereferenced: rejected first
+    st = lib.gdr_chunk_fwd_noalloc(ctypes.byref(p), fake, fake, fake, None, fake, ctypes.c_float(1.0), None, None,
+                                   None, fake, None, None)
+    assert st == 6
+    assert b"gdr_chunk_fwd_noalloc" in lib.gdr_last_error_message()
+    # a problem that fits passes the size check (it then needs a device)
+    small = prob(batch=2, seq_len=1000, Nk=4, Nv=4, dk=64, dv=64, num_seqs=2)
+    assert api.workspace_size(small) <= cap
