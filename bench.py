@@ -271,7 +271,8 @@ def mfma_summary(src: str, out_dir: str) -> None:
         raise FileNotFoundError(src)
     vals = {c: _counter_means(path, c) for c in MFMA_COUNTERS}
     cmd = ("rocprofv3 --pmc " + " ".join(MFMA_COUNTERS) +
-           " -d <dir>/mfma -o run --output-format csv -- python3 bench.py --steps 3 --warmup 1 --cpu-seconds 0")
+           " -d <dir>/mfma -o run --output-format csv -- python3 bench.py --steps 3 --warmup 1 --cpu-seconds 0"
+           " --no-peaks")
     lines = ["# Matrix-core utilisation per kernel, workload T65536_Nk16_Nv32_d128 (one forward per bench step)",
              "# command (run from the repository root):", "#   " + cmd,
              "#   python3 bench.py --mfma-summary <dir> --summary-out profiles",
@@ -311,7 +312,7 @@ def counter_summary(src: str, out_dir: str, workload: int) -> None:
                     return os.path.join(root, fn)
         raise FileNotFoundError(os.path.join(src, sub))
     jobs = [("fetch", "write", "T65536_Nk16_Nv32_d128" if workload == 5 else "workload%d" % workload,
-             "python3 bench.py --steps 3 --warmup 1 --cpu-seconds 0")]
+             "python3 bench.py --steps 3 --warmup 1 --cpu-seconds 0 --no-peaks")]
     if os.path.isdir(os.path.join(src, "rfetch")) and os.path.isdir(os.path.join(src, "rwrite")):
         jobs.append(("rfetch", "rwrite", "decode256_Nk16_Nv32_d128",
                      "python3 bench.py --mode recurrent --decode-seqs 256 --steps 3 --warmup 1"))
@@ -330,8 +331,8 @@ def _counter_summary_one(src, out_dir, csv_of, fdir, wdir, wl, cmd):
     w_scale = probe_kib / cwrite[probe[0]]
     os.makedirs(out_dir, exist_ok=True)
     for name in sorted(fetch):
-        short = next((k for k in sorted(STAGE_KERNELS + ("k_state_output", "k_recurrent"), key=len, reverse=True)
-                      if k in name), None)
+        short = next((k for k in sorted(STAGE_KERNELS + FP16_STAGE_KERNELS[:1] + ("k_prep", "k_chunk16", "k_recurrent"),
+                                        key=len, reverse=True) if k in name), None)
         if short is None or name not in write:
             continue
         fb, wb = fetch[name] * f_scale * 1024.0, write[name] * w_scale * 1024.0
@@ -360,6 +361,39 @@ def _counter_summary_one(src, out_dir, csv_of, fdir, wdir, wl, cmd):
             f.write("hbm_write_bytes_per_launch: %.0f\n" % wb)
             f.write("hbm_bytes_per_launch: %.0f\n" % (fb + wb))
         print(path)
+
+
+def trace_summary(src: str, out_file: str, title: str, cmd: str) -> None:
+    """Markdown table of a rocprofv3 --kernel-trace --stats run (run_kernel_stats.csv under src)."""
+    import csv
+    import re
+    path = None
+    for root, _, files in os.walk(src):
+        for fn in files:
+            if fn.endswith("kernel_stats.csv"):
+                path = os.path.join(root, fn)
+    if path is None:
+        raise FileNotFoundError(src)
+    rows = list(csv.DictReader(open(path)))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+
+    def short(name):
+        m = re.search(r"(k_[a-z0-9_]+)(?:I|E|<|\()", name)
+        base = m.group(1) if m else name[:60]
+        t = re.search(r"I(Li\d+E)+", name)
+        if t:
+            base += "<" + ", ".join(re.findall(r"Li(\d+)E", t.group(0))) + ">"
+        return base
+    lines = ["# Kernel trace: " + title, "", "Command (repository root):", "", "    " + cmd, "",
+             "From `run_kernel_stats.csv` (durations in microseconds):", "",
+             "| kernel | calls | average | min | max | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append("| %s | %s | %.1f | %.1f | %.1f | %.1f%% |" % (
+            short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, 100 * float(r["TotalDurationNs"]) / total))
+    with open(out_file, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out_file)
 
 
 def bench_recurrent(args) -> None:
@@ -666,6 +700,8 @@ def main():
     ap.add_argument("--mfma-summary", metavar="DIR",
                     help="only summarise a rocprofv3 run of MFMA_COUNTERS found under DIR into profiles/")
     ap.add_argument("--summary-out", metavar="DIR", default="profiles")
+    ap.add_argument("--trace-summary", nargs=4, metavar=("DIR", "OUT_FILE", "TITLE", "COMMAND"),
+                    help="only write a markdown summary of a rocprofv3 --kernel-trace --stats run")
     ap.add_argument("--summary-file", metavar="FILE", help="--mode configs: also write a markdown table here")
     ap.add_argument("--no-peaks", dest="peaks", action="store_false",
                     help="skip measuring the HBM-copy and matrix-core peaks")
@@ -675,6 +711,9 @@ def main():
         return
     if args.mfma_summary:
         mfma_summary(args.mfma_summary, args.summary_out)
+        return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
         return
     if args.gpus != 1:
         print("bench.py: this implementation runs on one GPU only; --gpus %d is not supported" % args.gpus,
