@@ -23,10 +23,11 @@
 //              Y -> Z -> V_new -> S on the matrix cores without touching LDS
 //              for it: every product's result is, lane for lane, an operand of
 //              the next (two stacked accumulator tiles are a pair fragment of
-//              the transposed block). Two output wavefronts form O from Q and P
-//              (loaded straight into registers) and from the state and V_new
-//              the chain publishes; copy wavefronts stage K (converted to fp16)
-//              and the V and decay tiles in LDS.
+//              the transposed block). Three helper wavefronts form O from the
+//              fp16 Q rows, the P pairs and exp(G) (loaded straight into
+//              registers) and from the state and V_new the chain publishes in
+//              LDS; they also copy the fp16 K tiles and the V slices of later
+//              chunks into LDS with buffer-to-LDS loads.
 //
 // Number formats: q, k, v are exact in bf16 and exact in fp16 (an fp16 has
 // more significant bits; values below 2^-14 become fp16 subnormals, absolute
@@ -391,17 +392,17 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
 // product's accumulators are, lane for lane, an operand of the next (two
 // stacked accumulator tiles are a pair fragment of the transposed block).
 // All of its operands are in registers when the step starts: the K operand
-// of Y and the V and decay rows of chunk c + 1 are read from LDS during step
-// c, T two chunks ahead from global memory. The other three wavefronts form
-// the output, transposed (O^T = S^T Q^T + V_new^T P^T, so that each lane holds
-// four adjacent columns of one row), for the row blocks {0, 1}, {2} and {3}:
-// chunk c's S part in step c, its V_new part and the store in step c + 1.
-// Their global loads (Q rows, score pairs, K rows) are issued two steps
-// before use. Wavefront 1 also copies the V slice and decay rows of chunk
-// c + 3 into LDS (16-byte buffer-to-LDS loads); wavefronts 2 and 3 convert
-// the K rows of chunk c + 2 (rows 0..31 and 32..63) to fp16 in LDS.
-// One LDS-only barrier per chunk step. K tiles are triple-buffered, V and
-// decay rows quadruple-buffered, the published state and V_new double-buffered.
+// of Y and the V rows of chunk c + 1 are read from LDS during step c, the T
+// pairs and decay rows of chunk c + 1 from global memory. The other three
+// wavefronts form the output, transposed (O^T = S^T Q^T + V_new^T P^T, so that
+// each lane holds four adjacent columns of one row), for the row blocks
+// {0, 1}, {2} and {3}: chunk c's output in step c + 1, from the entering state
+// and V_new the chain published in step c and from the Q rows, score pairs and
+// exp(G) they loaded from global memory in step c - 1. Wavefront 1 also copies
+// the V slice of chunk c + 3 into LDS (16-byte buffer-to-LDS loads);
+// wavefronts 2 and 3 copy the two halves (rows 0..31 and 32..63) of chunk
+// c + 3's fp16 K tile. One LDS-only barrier per chunk step. K tiles and V
+// slices are quadruple-buffered, the published state and V_new double-buffered.
 //
 // LDS layout of a K tile: row-major, 64 rows of dk fp16 values, the 16-byte
 // units of row `row` permuted by an XOR with swz(row), so that the chain's

@@ -10,13 +10,17 @@
  *
  * starting from S_0 = initial_state[n, h] (zeros when absent); the state after
  * the last token is returned as final_state[n, h]. The library computes this
- * with the chunkwise WY/UT algorithm (chunk size C = 64, 32 or 16) in five HIP
- * kernels: gate prefix sums, A-build + triangular solve, w/u products, the
- * sequential state pass, and the output. For bf16 inputs with C = 64,
- * gdr_chunk_fwd fuses the w/u products and the output into the state pass (the
- * products W S and U are formed there as T (V - diag(exp(G)) K S) with
- * T = A diag(beta)); fp32 inputs, C = 16 or 32, and gdr_chunk_fwd_debug run the
- * five kernels as separate launches. The chunk size changes only the rounding
+ * with the chunkwise WY/UT algorithm (chunk size C = 64, 32 or 16). For bf16
+ * inputs with C = 64, gdr_chunk_fwd runs two kernels after the chunk table: a
+ * chunk-parallel preparation (gate prefix sums, decay rows, the triangular
+ * solve, T = A diag(beta) and the score block (Q K^T) (.) D) and the
+ * chunk-serial pass, which forms U - W S as T (V - diag(exp(G)) K S) and the
+ * output in the same kernel; every derived operand of its matrix-core
+ * products is rounded once to fp16 and every product accumulates in fp32.
+ * fp32 inputs, C = 16 or 32, and gdr_chunk_fwd_debug run five kernels as
+ * separate launches (gate prefix sums, A-build + solve, w/u products, the
+ * state pass, the output) with every derived value in fp32. The chunk size
+ * changes only the rounding
  * order of the result (FLA DeltaNet article, section 6, tests the chunked
  * form at several chunk sizes against the recurrence); it trades the serial
  * depth T / C of the state pass against the C x C work of the solve.
@@ -80,8 +84,10 @@ typedef enum {
  * cu[num_seqs] = seq_len) marks sequence n as tokens [cu[n], cu[n+1]).
  * Zero-length sequences are allowed (their final state equals the initial).
  * Without cu_seqlens each batch row is one sequence and num_seqs = batch.
- * Values derived inside the method are carried at fp32 accuracy whatever the
- * input type; out_dtype = GDR_F32 returns o without a final bf16 rounding.
+ * The state and every sum are fp32 whatever the input type; the bf16 C = 64
+ * path rounds the derived operands of its products (T, the score block, the
+ * state, V - diag(exp(G)) K S, V_new) once to fp16, the other paths keep them
+ * in fp32. out_dtype = GDR_F32 returns o without a final bf16 rounding.
  */
 typedef struct {
     int64_t batch;          /* B >= 1; must be 1 when cu_seqlens is given          */
@@ -99,21 +105,38 @@ typedef struct {
 
 /*
  * Host-only check of a problem description (and of cu_seqlens_host when not
- * NULL). Touches no device memory. Returns the first error found.
+ * NULL). Touches no device memory. Returns the first error found. The checks
+ * are those the chunked API states for its arguments (FLA DeltaNet article,
+ * section 5, parameter table): q, k, v of one dtype with the stated shapes,
+ * beta [B, T, H], the state [N, H, dk, dv] with N = batch or
+ * len(cu_seqlens) - 1, batch 1 when cu_seqlens is given, and a chunk size of
+ * 16, 32 or 64. Two differences from that table: fp32 q, k, v are accepted,
+ * and Nv may be a multiple of Nk (grouped value heads, ChunkGatedDeltaRule
+ * page, section 1). Sizes outside this build (head dims other than 32, 64 or
+ * 128) are GDR_ERR_UNSUPPORTED.
  */
 gdr_status_t gdr_validate(const gdr_problem_t* problem, const int32_t* cu_seqlens_host);
 
 /*
  * Workspace bytes needed by gdr_chunk_fwd (and gdr_chunk_fwd_timed) for this
  * problem: an upper bound that holds for every cu_seqlens with the same
- * num_seqs and total length. The workspace must be 256-byte aligned.
+ * num_seqs and total length. The workspace must be 256-byte aligned. It holds
+ * the per-chunk values that do not depend on the state (FLA DeltaNet article,
+ * section 3.1-3.3: the products and the solve that precede the state pass):
+ * the chunk table and, for bf16 inputs with C = 64, the decay rows, T and the
+ * score block (12.5 KB per chunk and value head) and the fp16 K and Q tiles
+ * (256 dk bytes per chunk and q/k head); the five-kernel path (fp32 inputs,
+ * C = 16 or 32) keeps all of its intermediates there. Validation errors as
+ * for gdr_validate.
  */
 gdr_status_t gdr_chunk_fwd_workspace_size(const gdr_problem_t* problem, size_t* bytes);
 
 /*
  * Workspace bytes needed by gdr_chunk_fwd_debug, which runs the five kernels
- * as separate launches and keeps every intermediate (much larger than the
- * production workspace).
+ * as separate launches and keeps every intermediate: G, A, W, U, K^T, the
+ * chunk-entering states and V_new (FLA DeltaNet article, section 3.4: the
+ * three-stage pipeline whose intermediates these are), much larger than the
+ * production workspace. Validation errors as for gdr_validate.
  */
 gdr_status_t gdr_chunk_fwd_debug_workspace_size(const gdr_problem_t* problem, size_t* bytes);
 
@@ -333,10 +356,14 @@ typedef struct {
     int64_t num_chunks;     /* out: NT */
 } gdr_intermediates_t;
 
-/* Same result as gdr_chunk_fwd, computed by the five kernels as separate
- * launches; then copies the intermediates (asynchronously, on the same
- * stream) into the buffers of `dbg`. The workspace must hold
- * gdr_chunk_fwd_debug_workspace_size bytes. */
+/* Same result as gdr_chunk_fwd up to rounding, computed by the five kernels as
+ * separate launches with every derived value in fp32 (the stages of the FLA
+ * DeltaNet article, sections 3.1-3.4: K K^T, the solve, W and U, the state
+ * pass, the output); then copies the intermediates (asynchronously, on the
+ * same stream) into the buffers of `dbg`. For bf16 inputs with C = 64 it also
+ * runs the production preparation kernel and copies its T, P and R. The
+ * workspace must hold gdr_chunk_fwd_debug_workspace_size bytes; errors as for
+ * gdr_chunk_fwd (GDR_ERR_WORKSPACE when it is smaller). */
 gdr_status_t gdr_chunk_fwd_debug(const gdr_problem_t* problem,
                                  const void* q, const void* k, const void* v,
                                  const float* g, const void* beta, float scale,
@@ -354,8 +381,9 @@ gdr_status_t gdr_chunk_fwd_debug(const gdr_problem_t* problem,
  * stage_events[0 .. GDR_NUM_STAGES] (hipEvent_t handles) on `stream`: [0]
  * before the first kernel and [i] after stage i, the stages being [1] chunk
  * table, [2] gate prefix sums, [3] A-build + solve, [4] w/u, [5] state pass,
- * [6] output. On the fused bf16 path stages [4] and [6] launch nothing (their
- * work runs inside [5]). Nothing is synchronised; the caller reads the elapsed
+ * [6] output. On the bf16 C = 64 path stages [2], [4] and [6] launch nothing:
+ * [3] is the preparation kernel (gate sums included) and [5] the chunk-serial
+ * pass with the w/u products and the output. Nothing is synchronised; the caller reads the elapsed
  * times once the stream has passed the last event. Used to time each kernel
  * inside a benchmark's timed region.
  */
