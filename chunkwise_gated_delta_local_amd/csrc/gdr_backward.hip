@@ -28,8 +28,10 @@
 //     and exp(G_last) in the state update and exp(G) in W; dg = the reverse
 //     prefix sum of dG inside the chunk.
 // dq and dk are formed per value head and summed over the heads that share a
-// q/k head. All arithmetic is fp32 on the vector units; the forward values are
-// recomputed by the five-kernel forward path.
+// q/k head. All arithmetic is fp32: the products run on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32) with operands staged through LDS, the rest on the
+// vector units. The forward values are recomputed by the five-kernel forward
+// path.
 #include "gdr_device.hpp"
 #include "gdr_launch.hpp"
 
@@ -673,7 +675,9 @@ hipError_t launch_bwd(const BackwardArgs& b) {
     hipStream_t st = a.stream;
     auto mark = [&](int i) { if (b.events) (void)hipEventRecord(b.events[i], st); };
     mark(0);
-    hipError_t e = launch_forward(a, nullptr);   // recompute: G, A, W, U, K^T, h, V_new
+    LaunchArgs f = a;
+    f.T16 = nullptr;                             // the fp16 path's T, score block and decay rows are not needed
+    hipError_t e = launch_forward(f, nullptr);   // recompute: G, A, W, U, K^T, h, V_new
     if (e != hipSuccess) return e;
     mark(1);
     const int32_t NT = a.nt;

@@ -15,12 +15,15 @@
 // 1e-6) inside the kernel (FLA DeltaNet article, section 5, the in-kernel L2
 // normalisation option).
 //
-// Mapping: one wavefront per (sequence, value head, 64 columns of dv). Lane j
-// owns column j of the state slice with all dk rows in registers, so neither
-// S^T k nor S^T q needs a reduction across lanes. Blocks of 16 tokens of q and
-// k (normalised if asked, in fp32) are staged in LDS and read back as
-// broadcasts; beta and g are wave-uniform scalar loads. The arithmetic is fp32
-// throughout; o is rounded once, at the store.
+// Mapping: one wavefront per (sequence, value head, 256 / RQ columns of dv),
+// RQ = dk / 16. Lane l = RQ cg + rq owns columns 4 cg .. 4 cg + 3 of the state
+// slice over rows 16 rq .. 16 rq + 15: 64 state values in registers, so that
+// four wavefronts fit on a SIMD. S^T k and S^T q are sums over the lane's rows
+// followed by a butterfly over the RQ lanes of a group. Each lane reads its 16
+// elements of q_t and k_t straight from global memory (the lanes of one row
+// range read the same bytes); beta and g are wave-uniform scalar loads. The
+// state moves in and out with 16-byte non-temporal accesses (it is read and
+// written once), four columns of one row per access. The arithmetic is fp32 throughout; o is rounded once, at the store.
 #include "gdr_device.hpp"
 #include "gdr_launch.hpp"
 
@@ -28,7 +31,39 @@ namespace gdr {
 
 namespace {
 
-constexpr int kTokBlock = 16;   // tokens of q and k staged per LDS block
+constexpr int kRowsPerLane = 16;
+
+// 16 consecutive elements of a q/k row -> fp32 (16-byte loads; the offset is a
+// multiple of 16 elements)
+__device__ __forceinline__ void load_part(const bf16* p, float* x) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const uint4 w = *reinterpret_cast<const uint4*>(p + 8 * c);
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[8 * c + 2 * e] = __uint_as_float(u[e] << 16);
+            x[8 * c + 2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+        }
+    }
+}
+__device__ __forceinline__ void load_part(const float* p, float* x) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float4 w = *reinterpret_cast<const float4*>(p + 4 * c);
+        x[4 * c] = w.x;
+        x[4 * c + 1] = w.y;
+        x[4 * c + 2] = w.z;
+        x[4 * c + 3] = w.w;
+    }
+}
+// sum over the RQ adjacent lanes of a group
+template <int RQ>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int m = 1; m < RQ; m <<= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
 
 template <typename T, int DK>
 __global__ __launch_bounds__(64) void k_recurrent(const T* __restrict__ q, const T* __restrict__ k,
@@ -38,14 +73,15 @@ __global__ __launch_bounds__(64) void k_recurrent(const T* __restrict__ q, const
                                                    int64_t T_row, int64_t Ttot, int32_t Nk, int32_t Nv, int32_t DV,
                                                    float scale, int l2norm, int out_f32, void* __restrict__ o,
                                                    float* __restrict__ ST) {
-    static_assert(DK <= 128 && DK % 32 == 0, "dk");
-    constexpr int EPL = (DK + 63) / 64;          // q/k elements staged per lane per token
-    __shared__ __attribute__((aligned(16))) float kq[2][kTokBlock][DK];
-
+    constexpr int RPL = kRowsPerLane;
+    constexpr int RQ = DK / RPL;                 // lanes per column group (2, 4 or 8)
+    constexpr int COLS = 4 * 64 / RQ;            // state columns per wavefront
+    static_assert(DK % RPL == 0 && RQ >= 2 && RQ <= 8, "dk");
     const int n = blockIdx.x, h = blockIdx.y;
-    const int lane = threadIdx.x;
-    const int j = blockIdx.z * 64 + lane;        // this lane's state column
-    const bool active = j < DV;
+    const int lane = threadIdx.x, rq = lane % RQ, cg = lane / RQ;
+    const int j0 = blockIdx.z * COLS + 4 * cg;   // this lane's first state column
+    const bool active = j0 < DV;                 // DV is a multiple of 32: all four columns or none
+    const int r0 = rq * RPL;                     // this lane's first state row
     const int kh = h / (Nv / Nk);
     int64_t s = cu ? (int64_t)cu[n] : (int64_t)n * T_row;
     int64_t e = cu ? (int64_t)cu[n + 1] : (int64_t)(n + 1) * T_row;
@@ -53,80 +89,71 @@ __global__ __launch_bounds__(64) void k_recurrent(const T* __restrict__ q, const
     e = e < s ? s : (e > Ttot ? Ttot : e);
 
     const int64_t sbase = ((int64_t)n * Nv + h) * DK * DV;
-    float S[DK];
+    f32x4 S[RPL];                                // S[i][c]: row r0 + i, column j0 + c
 #pragma unroll
-    for (int i = 0; i < DK; ++i) S[i] = (S0 && active) ? S0[sbase + (int64_t)i * DV + j] : 0.f;
+    for (int i = 0; i < RPL; ++i)
+        S[i] = (S0 && active)
+                   ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(&S0[sbase + (int64_t)(r0 + i) * DV + j0]))
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t t0 = s; t0 < e; t0 += kTokBlock) {
-        const int nt = (int)min((int64_t)kTokBlock, e - t0);
-        // stage q and k of tokens t0 .. t0+nt-1 (lane holds elements lane, lane + 64)
-        for (int tt = 0; tt < nt; ++tt) {
-            const int64_t row = (t0 + tt) * Nk + kh;
+    for (int64_t t = s; t < e; ++t) {
+        const int64_t row = t * Nk + kh, th = t * Nv + h;
+        float kx[RPL], qx[RPL];
+        load_part(k + row * DK + r0, kx);
+        load_part(q + row * DK + r0, qx);
+        const float b = load_beta(beta, th, beta_f32);
+        const float a = g ? __expf(g[th]) : 1.f;
+        f32x4 vv = {0.f, 0.f, 0.f, 0.f};
+        if (active) {
 #pragma unroll
-            for (int w = 0; w < 2; ++w) {
-                const T* src = (w == 0 ? k : q) + row * DK;
-                float x[EPL];
-                float ss = 0.f;
+            for (int c = 0; c < 4; ++c) vv[c] = to_f(v[th * DV + j0 + c]);
+        }
+        float rk = 1.f, rqn = 1.f;
+        if (l2norm) {                            // 1 / |x| of the whole vector: sums over the group's rows
+            float sk = 0.f, sq = 0.f;
 #pragma unroll
-                for (int c = 0; c < EPL; ++c) {
-                    const int i = lane + 64 * c;
-                    x[c] = i < DK ? to_f(src[i]) : 0.f;
-                    ss += x[c] * x[c];
-                }
-                if (l2norm) {
+            for (int i = 0; i < RPL; ++i) {
+                sk += kx[i] * kx[i];
+                sq += qx[i] * qx[i];
+            }
+            rk = 1.f / sqrtf(group_sum<RQ>(sk) + 1e-6f);
+            rqn = 1.f / sqrtf(group_sum<RQ>(sq) + 1e-6f);
+        }
+        // u = beta (v - exp(g) S_old^T k); S = exp(g) S_old + k u, with k = kx rk
+        f32x4 ks = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-                    const float rn = 1.f / sqrtf(ss + 1e-6f);
+        for (int i = 0; i < RPL; ++i) ks += kx[i] * S[i];
+        f32x4 u;
 #pragma unroll
-                    for (int c = 0; c < EPL; ++c) x[c] *= rn;
-                }
+        for (int c = 0; c < 4; ++c) u[c] = b * (vv[c] - a * (rk * group_sum<RQ>(ks[c])));
+        u = u * rk;
 #pragma unroll
-                for (int c = 0; c < EPL; ++c) {
-                    const int i = lane + 64 * c;
-                    if (i < DK) kq[w][tt][i] = x[c];
-                }
+        for (int i = 0; i < RPL; ++i) S[i] = S[i] * a + kx[i] * u;
+        f32x4 os = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) os += qx[i] * S[i];
+        // every lane of the group holds the four sums; lane rq stores the
+        // columns c with c % RQ == rq
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float x = scale * rqn * group_sum<RQ>(os[c]);
+            if (active && c % RQ == rq) {
+                if (out_f32) reinterpret_cast<float*>(o)[th * DV + j0 + c] = x;
+                else reinterpret_cast<T*>(o)[th * DV + j0 + c] = to_t<T>(x);
             }
         }
-        __syncthreads();
-        for (int tt = 0; tt < nt; ++tt) {
-            const int64_t t = t0 + tt;
-            const int64_t th = t * Nv + h;
-            const float b = load_beta(beta, th, beta_f32);
-            const float a = g ? __expf(g[th]) : 1.f;
-            const float vj = active ? to_f(v[th * DV + j]) : 0.f;
-            // u = beta (v - exp(g) S_old^T k); S = exp(g) S_old + k u
-            float ks0 = 0.f, ks1 = 0.f;
-#pragma unroll
-            for (int i = 0; i < DK; i += 2) {
-                ks0 += kq[0][tt][i] * S[i];
-                ks1 += kq[0][tt][i + 1] * S[i + 1];
-            }
-            const float u = b * (vj - a * (ks0 + ks1));
-#pragma unroll
-            for (int i = 0; i < DK; ++i) S[i] = S[i] * a + kq[0][tt][i] * u;
-            float o0 = 0.f, o1 = 0.f;
-#pragma unroll
-            for (int i = 0; i < DK; i += 2) {
-                o0 += kq[1][tt][i] * S[i];
-                o1 += kq[1][tt][i + 1] * S[i + 1];
-            }
-            const float val = scale * (o0 + o1);
-            if (active) {
-                if (out_f32) reinterpret_cast<float*>(o)[th * DV + j] = val;
-                else reinterpret_cast<T*>(o)[th * DV + j] = to_t<T>(val);
-            }
-        }
-        __syncthreads();                          // the block is consumed before it is overwritten
     }
     if (ST && active) {
 #pragma unroll
-        for (int i = 0; i < DK; ++i) ST[sbase + (int64_t)i * DV + j] = S[i];
+        for (int i = 0; i < RPL; ++i)
+            __builtin_nontemporal_store(S[i], reinterpret_cast<f32x4*>(&ST[sbase + (int64_t)(r0 + i) * DV + j0]));
     }
 }
 
 template <typename T>
 hipError_t dispatch(const RecurrentArgs& a) {
-    const dim3 grid(a.N, a.Nv, (a.dv + 63) / 64);
+    const int cols = 4 * 64 * kRowsPerLane / a.dk;     // state columns per wavefront
+    const dim3 grid(a.N, a.Nv, (a.dv + cols - 1) / cols);
 #define GDR_REC(DKv)                                                                                              \
     if (a.dk == DKv) {                                                                                            \
         k_recurrent<T, DKv><<<grid, 64, 0, a.stream>>>((const T*)a.q, (const T*)a.k, (const T*)a.v, a.beta,      \
