@@ -392,17 +392,18 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
 // product's accumulators are, lane for lane, an operand of the next (two
 // stacked accumulator tiles are a pair fragment of the transposed block).
 // All of its operands are in registers when the step starts: the K operand
-// of Y and the V rows of chunk c + 1 are read from LDS during step c, the T
-// pairs and decay rows of chunk c + 1 from global memory. The other three
+// of Y, the V rows, the T pairs and the decay rows of chunk c + 1 are read
+// from LDS during step c; the chain issues no vector-memory operation. The other three
 // wavefronts form the output, transposed (O^T = S^T Q^T + V_new^T P^T, so that
 // each lane holds four adjacent columns of one row), for the row blocks
 // {0, 1}, {2} and {3}: chunk c's output in step c + 1, from the entering state
 // and V_new the chain published in step c and from the Q rows, score pairs and
 // exp(G) they loaded from global memory in step c - 1. Wavefront 1 also copies
-// the V slice of chunk c + 3 into LDS (16-byte buffer-to-LDS loads);
-// wavefronts 2 and 3 copy the two halves (rows 0..31 and 32..63) of chunk
-// c + 3's fp16 K tile. One LDS-only barrier per chunk step. K tiles and V
-// slices are quadruple-buffered, the published state and V_new double-buffered.
+// the V slice and the decay rows of chunk c + 3 into LDS (16-byte
+// buffer-to-LDS loads); wavefronts 2 and 3 copy the two halves (rows 0..31
+// and 32..63) of chunk c + 3's fp16 K tile and half of its T pairs each. One
+// LDS-only barrier per chunk step. K tiles, V slices, T pairs and decay rows
+// are quadruple-buffered, the published state and V_new double-buffered.
 //
 // LDS layout of a K tile: row-major, 64 rows of dk fp16 values, the 16-byte
 // units of row `row` permuted by an XOR with swz(row), so that the chain's
@@ -423,6 +424,8 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
     constexpr bool want_o = MODE == kFull16;
     __shared__ __attribute__((aligned(16))) f16 Ks[4][C * DK];
     __shared__ __attribute__((aligned(16))) bf16 Vs[4][C * 16];
+    __shared__ __attribute__((aligned(16))) f16 Ts[4][kPairs * kFrag];  // T pairs of a chunk
+    __shared__ __attribute__((aligned(16))) float Rs[4][256];           // decay rows (128 used)
     __shared__ __attribute__((aligned(16))) f16 Sx[2][NKP][kFrag];     // entering state, natural dk order
     __shared__ __attribute__((aligned(16))) f16 VNx[2][2][kFrag];      // V_new pairs (stacked positions)
 
@@ -524,43 +527,40 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
             }
             return x;
         };
-        // T pairs and decay rows of a chunk, loaded from global memory a step
-        // ahead (the chain's only vector memory operations): exp(G) and
-        // exp(G_last - G) of rows 16 b + 4 qd + j, and exp(G_last) =
+        // T pairs and decay rows of a chunk, read from LDS a step ahead:
+        // exp(G) and exp(G_last - G) of rows 16 b + 4 qd + j, and exp(G_last) =
         // exp(G_0) exp(G_last - G_0) from the rows themselves
         struct TR {
             h8 tf[kPairs];
             f32x4 eg[4], ed[4];
             float a0, a1;
         };
-        auto load_tr = [&](int c) {
+        auto read_tr = [&](int c) {
             TR x;
-            const bool ok = c < c1;
-            const auto rt = rsrc_of(Tf, (ok ? (int64_t)c * Nv + h : 0) * kPairs * kFrag * 2, ok ? kPairs * kFrag * 2 : 0u);
-            const auto rr = rsrc_of(R, (ok ? (int64_t)c * Nv + h : 0) * 2 * C * 4, ok ? 2 * C * 4 : 0u);
+            const int sl = slot4(c);
 #pragma unroll
-            for (int p = 0; p < kPairs; ++p) x.tf[p] = __builtin_bit_cast(h8, buf_load16(rt, p * kFrag * 2 + lane * 16));
+            for (int p = 0; p < kPairs; ++p) x.tf[p] = *reinterpret_cast<const h8*>(&Ts[sl][p * kFrag + lane * 8]);
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                x.eg[b] = __builtin_bit_cast(f32x4, buf_load16(rr, (16 * b + 4 * qd) * 4));
-                x.ed[b] = __builtin_bit_cast(f32x4, buf_load16(rr, (C + 16 * b + 4 * qd) * 4));
+                x.eg[b] = *reinterpret_cast<const f32x4*>(&Rs[sl][16 * b + 4 * qd]);
+                x.ed[b] = *reinterpret_cast<const f32x4*>(&Rs[sl][C + 16 * b + 4 * qd]);
             }
-            x.a0 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, 0, 0, 0));
-            x.a1 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, C * 4, 0, 0));
+            x.a0 = Rs[sl][0];
+            x.a1 = Rs[sl][C];
             return x;
         };
         VR vr;
-        TR tr = load_tr(c0);
+        TR tr;
         make_pairs();
         lds_barrier();                                                            // prologue barrier
         if (c0 < c1) {
             read_ka(c0);
             vr = read_vr(c0);
+            tr = read_tr(c0);
         }
         auto step = [&](int c) {
             const int s4l = slot4(c);
             const f16* Kb = Ks[s4l];
-            const TR tr_next = load_tr(c + 1);
             // ---- region 1: S_in's pairs published; Y = K S_in (operands read in the
             //      previous step) with the reads of this chunk's K^T operands and the
             //      scaling of S by exp(G_last) interleaved
@@ -639,6 +639,7 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
 #pragma unroll
             for (int t = 0; t < NDB; ++t) S[t] = mfma16(kt[t][1], vd1, mfma16(kt[t][0], vd0, S[t]));
             vr = read_vr(c + 1);
+            const TR tr_next = read_tr(c + 1);
             __builtin_amdgcn_sched_barrier(0);
             make_pairs();
             tr = tr_next;
@@ -657,9 +658,10 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
     }
 
     // ============================================================ helper waves
-    // wavefront 1: output rows 0..31 (blocks 0, 1) and the copies of the V slice;
-    // wavefront 2: output block 2 and the copies of K rows
-    // 0..31; wavefront 3: output block 3 and the copies of K rows 32..63. A
+    // wavefront 1: output rows 0..31 (blocks 0, 1) and the copies of the V slice
+    // and the decay rows; wavefront 2: output block 2 and the copies of K rows
+    // 0..31 and T pairs 0..2; wavefront 3: output block 3 and the copies of K
+    // rows 32..63 and T pairs 3..5. A
     // helper reads no LDS array it copies into (the compiler would otherwise wait
     // for the copies before each such read). Every copy is a 16-byte buffer-to-LDS load
     // of chunk c + 3 issued at the start of step c; the wave waits for the
@@ -686,7 +688,23 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
                 buffer_to_lds16(rk, reinterpret_cast<const char*>(Ks[slot4(c)]) + off, off + lane * 16);
             }
         };
-        constexpr int NDMA = ROLE == 1 ? 2 : DK / 16;    // copies per step
+        // ---- decay rows of a chunk -> LDS (wavefront 1): one load (the rows are
+        //      512 bytes; lanes 32..63 read past them and write zeros)
+        auto copy_r = [&](int c) {
+            const bool ok = c < c1;
+            const auto rr = rsrc_of(R, (ok ? (int64_t)c * Nv + h : 0) * 2 * C * 4, ok ? 2 * C * 4 : 0u);
+            buffer_to_lds16(rr, &Rs[slot4(c)][0], lane * 16);
+        };
+        // ---- T pairs of a chunk -> LDS: pairs 0..2 (wavefront 2) or 3..5 (wavefront 3)
+        auto copy_t = [&](int c) {
+            const bool ok = c < c1;
+            const auto rt = rsrc_of(Tf, (ok ? (int64_t)c * Nv + h : 0) * kPairs * kFrag * 2, ok ? kPairs * kFrag * 2 : 0u);
+            const int p0 = (wv - 2) * (kPairs / 2);
+#pragma unroll
+            for (int p = p0; p < p0 + kPairs / 2; ++p)
+                buffer_to_lds16(rt, &Ts[slot4(c)][p * kFrag], p * kFrag * 2 + lane * 16);
+        };
+        constexpr int NDMA = ROLE == 1 ? 2 + 1 : DK / 16 + kPairs / 2;    // copies per step
         // ---- output operands: the Q rows (fp16 tile) and score pairs of chunk c,
         //      loaded in step c - 1 and used in step c + 1, when the chunk's
         //      entering state and V_new (published in step c) are in LDS
@@ -763,8 +781,13 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
         for (int i = 0; i < NBL; ++i) egraw[1][i] = 0.f;
         // prologue: the copies of the first three chunks landed
         auto copy = [&](int c) {
-            if constexpr (ROLE == 1) copy_v(c);
-            else copy_k(c);
+            if constexpr (ROLE == 1) {
+                copy_v(c);
+                copy_r(c);
+            } else {
+                copy_k(c);
+                copy_t(c);
+            }
         };
         copy(c0);
         copy(c0 + 1);
