@@ -267,7 +267,7 @@ int32_t bwd_segments_per_seq(const gdr_problem_t* p) {
 // Backward workspace: the five-kernel forward's regions, then the backward's
 // own, then the recompute's segment region.
 struct BwdPlan {
-    size_t off_P, off_Hn, off_Vn, off_Wn, off_dSout, off_dVn, off_dWs, off_dqv, off_dkv, end;
+    size_t off_P, off_Hn, off_Vn, off_WT, off_dSout, off_dVn, off_dWs, off_dqv, off_dkv, end;
     SegPlan seg;
     int64_t seg_bound;
 };
@@ -282,7 +282,7 @@ BwdPlan make_bwd_plan(const gdr_problem_t* p, const Plan& pl) {
     bp.off_P = take(cap * Nv * C * C * 4);
     bp.off_Hn = take(cap * Nv * dk * dv * 4);
     bp.off_Vn = take(T * Nv * dv * 4);
-    bp.off_Wn = take(T * Nv * dk * 4);
+    bp.off_WT = take(cap * Nv * dk * C * 4);
     bp.off_dSout = take(cap * Nv * dk * dv * 4);
     bp.off_dVn = take(T * Nv * dv * 4);
     bp.off_dWs = take(T * Nv * dk * 4);
@@ -570,7 +570,7 @@ gdr_status_t gdr_chunk_bwd(const gdr_problem_t* p, const void* q, const void* k,
     b.dST = d_final_state;
     b.dq = dq; b.dk = dk; b.dv = dv; b.dbeta = dbeta; b.dg = dg; b.dS0 = d_initial_state;
     auto f = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
-    b.P = f(bp.off_P); b.Hn = f(bp.off_Hn); b.Vn = f(bp.off_Vn); b.Wn = f(bp.off_Wn);
+    b.P = f(bp.off_P); b.Hn = f(bp.off_Hn); b.Vn = f(bp.off_Vn); b.WT = f(bp.off_WT);
     b.dSout = f(bp.off_dSout); b.dVn = f(bp.off_dVn); b.dWs = f(bp.off_dWs);
     b.dqv = f(bp.off_dqv); b.dkv = f(bp.off_dkv);
     b.events = stage_events ? ev : nullptr;

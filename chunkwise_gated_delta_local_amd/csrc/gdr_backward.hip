@@ -218,9 +218,9 @@ __device__ __forceinline__ void gemm_lds(int K, float* As, float* Bs, FA&& a, FB
 }
 
 // ------------------------------------------------------------ preparation
-// One workgroup per (chunk, value head): the forward intermediates in natural
-// row-major layouts (the chunk's entering state h [dk][dv], V_new and W by
-// token row), the score block P = (Q K^T) (.) D [C][C] (zero above the
+// One workgroup per (chunk, value head): the forward intermediates in plain
+// row-major layouts (the chunk's entering state h [dk][dv], V_new by token
+// row, W^T [dk][C] per chunk), the score block P = (Q K^T) (.) D [C][C] (zero above the
 // diagonal and past the chunk end), and the two parts of the reverse state
 // pass that do not depend on the state gradient:
 //   X  = scale P^T dO                                   (into the dV_new buffer)
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ q, const
                                                    const int32_t* __restrict__ chunk_start,
                                                    const int32_t* __restrict__ chunk_len, int32_t Nk, int32_t Nv,
                                                    float* __restrict__ Hn, float* __restrict__ Vn,
-                                                   float* __restrict__ Wn, float* __restrict__ P,
+                                                   float* __restrict__ WT, float* __restrict__ P,
                                                    float* __restrict__ X, float* __restrict__ Yp) {
     constexpr int NKP = DK / 32, NNB = DV / 16, NTB = C / 16, NTP = C < 32 ? 1 : C / 32;
     constexpr int NMAX = (DK > DV ? DK : DV) > C ? (DK > DV ? DK : DV) : C;
@@ -262,9 +262,10 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ q, const
         const int p = idx / DV, j = idx % DV;
         Vn[((s + p) * Nv + h) * DV + j] = VNf[((ch * NNB + j / 16) * NTP + p / 32) * 512 + pair_off(j % 16, p % 32)];
     }
-    for (int idx = tid; idx < L * DK; idx += 256) {
-        const int p = idx / DK, i = idx % DK;
-        Wn[((s + p) * Nv + h) * DK + i] = Wf[((ch * NTB + p / 16) * NKP + i / 32) * 512 + pair_off(p % 16, i % 32)];
+    for (int idx = tid; idx < DK * C; idx += 256) {      // W^T of the chunk, zero past its end
+        const int i = idx / C, p = idx % C;
+        WT[(ch * DK + i) * C + p] =
+            p < L ? Wf[((ch * NTB + p / 16) * NKP + i / 32) * 512 + pair_off(p % 16, i % 32)] : 0.f;
     }
     auto Qg = [&](int i, int m) { return i < L ? to_f(q[((s + i) * Nk + kh) * DK + m]) : 0.f; };
     auto Kg = [&](int i, int m) { return i < L ? to_f(k[((s + i) * Nk + kh) * DK + m]) : 0.f; };
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ q, const
                                  [&](int i, int j, float x) { if (i < L) X[((s + i) * Nv + h) * DV + j] = scale * x; });
     gemm_lds<DK, DV, false, true, KT>(2 * C, As, Bs,
         [&](int m, int kk) {
-            return kk < C ? Qg(kk, m) : (kk - C < L ? -Wn[((s + kk - C) * Nv + h) * DK + m] : 0.f);
+            return kk < C ? Qg(kk, m) : -WT[(ch * DK + m) * C + kk - C];
         },
         [&](int kk, int j) {
             return kk < C ? se[kk] * dOg(kk, j) : (kk - C < L ? X[((s + kk - C) * Nv + h) * DV + j] : 0.f);
@@ -289,153 +290,225 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ q, const
 }
 
 // ------------------------------------------------------------ reverse state pass
-// One workgroup per (sequence, value head, 16 columns of dv) walks the chunks
-// backwards with the 16-column slice of the state gradient dS in LDS (fp32).
-// Per chunk, with X and Y' from the preparation kernel:
+// One workgroup of four wavefronts per (sequence, value head, 16 columns of
+// dv) walks the chunks backwards with the 16-column slice of the state
+// gradient dS in fp32 accumulators. Per chunk, with X and Y' from the
+// preparation kernel:
 //   Z = diag(exp(G_last - G)) K dS;  dV_new = X + Z   (overwrites X)
 //   the chunk's outgoing-state gradient dS is stored (over Y', after reading it)
 //   dS <- exp(G_last) dS + Y' - W^T Z
-// After the first chunk, dS is the gradient with respect to the initial state.
-// The next chunk's operands (K and W rows, X, Y', G) are loaded into registers
-// with 16-byte loads while the current chunk is computed, and the barriers
-// wait for LDS traffic only, so the loads stay in flight.
+// Both products run on the fp32 matrix cores (v_mfma_f32_16x16x4_f32):
+// wavefront w forms rows 16 w .. 16 w + 15 of Z (contraction over dk) and the
+// dk row blocks w, w + 4, ... of W^T Z (contraction over the chunk's
+// positions). K (as fp32), W^T, Z^T and dS^T go through LDS; in each group of
+// four products lane (qd, r) takes the contraction indices 16 t + 4 qd + u,
+// u = 0..3, so that each operand of a group is one 16-byte read. The next
+// chunk's K rows, W^T, X, Y' and gate sums are loaded into registers while the
+// current chunk is computed.
 template <typename T, int DK, int DV, int C>
 __global__ __launch_bounds__(256) void k_bwd_state(const T* __restrict__ k, const float* __restrict__ G,
-                                                    const float* __restrict__ Wn, const float* __restrict__ dST,
+                                                    const float* __restrict__ WT, const float* __restrict__ dST,
                                                     const int32_t* __restrict__ chunk_start,
                                                     const int32_t* __restrict__ chunk_len,
                                                     const int32_t* __restrict__ seq_first, int32_t Nk, int32_t Nv,
                                                     float* __restrict__ dSY, float* __restrict__ dVX,
                                                     float* __restrict__ dS0) {
     typedef typename Vec<T>::v8 v8;
-    constexpr int KP = DK + 1;
-    constexpr int PER = DK * 16 / 256;          // dS elements per thread
-    constexpr int NSEG = C * DK / 8;            // 8-element row pieces of K and W
+    constexpr int NB = DK / 16;                 // dk row blocks of dS
+    constexpr int NBW = (NB + 3) / 4;           // row blocks per wavefront
+    constexpr int KP = DK + 4, CP = C + 4;      // LDS pitches (floats)
+    constexpr int NSEG = C * DK / 8;            // 8-element pieces of the K rows
     constexpr int NK8 = (NSEG + 255) / 256;
-    constexpr int NZ = (C * 16 + 255) / 256;    // Z elements per thread
-    __shared__ float dS[DK][16];
-    __shared__ float Ks[C][KP], Ws[C][KP];
-    __shared__ float Zt[C][16];
-    __shared__ float gs[C];
+    constexpr int NW4 = DK * C / 4;             // 4-float pieces of W^T
+    constexpr int NWT = (NW4 + 255) / 256;
+    __shared__ __attribute__((aligned(16))) float Ks[C][KP];
+    __shared__ __attribute__((aligned(16))) float Wt[DK][CP];
+    __shared__ __attribute__((aligned(16))) float dSt[16][KP];
+    __shared__ __attribute__((aligned(16))) float Zt[16][CP];
+    __shared__ float gs[256];                   // gate sums (one per thread; C used)
     const int n = blockIdx.x, h = blockIdx.y, nb = blockIdx.z, tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63, r = lane & 15, qd = lane >> 4;
     const int kh = h / (Nv / Nk);
-    for (int idx = tid; idx < DK * 16; idx += 256) {
-        const int m = idx / 16, j = idx % 16;
-        dS[m][j] = dST ? dST[(((int64_t)n * Nv + h) * DK + m) * DV + nb * 16 + j] : 0.f;
+    const int64_t hb = (int64_t)n * Nv + h;
+    // dS rows 16 m + 4 qd + v, column r, for the blocks m = w + 4 i
+    f32x4 dS[NBW];
+#pragma unroll
+    for (int i = 0; i < NBW; ++i) {
+        const int m = w + 4 * i;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            dS[i][v] = (m < NB && dST) ? dST[(hb * DK + 16 * m + 4 * qd + v) * DV + nb * 16 + r] : 0.f;
     }
-    v8 kr[NK8];
-    f32x4 wr[2 * NK8];
-    float xr[NZ], yr[PER], gr = 0.f;
-    auto fetch = [&](int c) {
+    // K rows and W^T of a chunk, loaded two chunks ahead into one of two
+    // register sets; X, Y' and the gate sums one chunk ahead
+    v8 kr[2][NK8];
+    f32x4 wr[2][NWT], xr, yr[NBW];
+    float gr = 0.f;
+    auto fetch_tiles = [&](int c, auto set_t) {
+        constexpr int SET = decltype(set_t)::value;
         const int64_t s = chunk_start[c];
         const int L = chunk_len[c];
+        // rows past the chunk's end fall outside the buffer and read as zero
+        const auto rk = buf_rsrc(k + (s * Nk + kh) * DK, L > 0 ? (uint32_t)(((L - 1) * Nk + 1) * DK * sizeof(T)) : 0u);
 #pragma unroll
         for (int e = 0; e < NK8; ++e) {
             const int idx = tid + 256 * e, i = idx / (DK / 8), seg = idx % (DK / 8);
-            const bool ok = idx < NSEG && i < L;
-            const float* wp = Wn + ((s + i) * Nv + h) * DK + seg * 8;
-            kr[e] = ok ? *reinterpret_cast<const v8*>(k + ((s + i) * Nk + kh) * DK + seg * 8) : zero_pair<T>();
-            wr[2 * e] = ok ? *reinterpret_cast<const f32x4*>(wp) : f32x4{0.f, 0.f, 0.f, 0.f};
-            wr[2 * e + 1] = ok ? *reinterpret_cast<const f32x4*>(wp + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int e = 0; e < NZ; ++e) {
-            const int idx = tid + 256 * e, i = idx / 16, j = idx % 16;
-            xr[e] = (idx < C * 16 && i < L) ? dVX[((s + i) * Nv + h) * DV + nb * 16 + j] : 0.f;
-        }
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int idx = tid + 256 * e, m = idx / 16, j = idx % 16;
-            yr[e] = dSY[(((int64_t)c * Nv + h) * DK + m) * DV + nb * 16 + j];
-        }
-        gr = (tid < C && tid < L) ? G[(s + tid) * Nv + h] : 0.f;
-    };
-    auto commit = [&]() {                          // K and W rows -> LDS
-#pragma unroll
-        for (int e = 0; e < NK8; ++e) {
-            const int idx = tid + 256 * e, i = idx / (DK / 8), seg = idx % (DK / 8);
-            if (idx < NSEG) {
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    Ks[i][seg * 8 + t] = to_f(kr[e][t]);
-                    Ws[i][seg * 8 + t] = wr[2 * e + t / 4][t % 4];
-                }
+            const int off = idx < NSEG ? (int)((i * Nk * DK + seg * 8) * sizeof(T)) : 0x7fffffff;
+            if constexpr (sizeof(T) == 2) {
+                kr[SET][e] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+            } else {
+                const f32x4 lo = buf_ld_f32x4(rk, off), hi = buf_ld_f32x4(rk, off + 16);
+                kr[SET][e] = __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             }
         }
-        if (tid < C) gs[tid] = gr;
+        const auto rw = buf_rsrc(WT + ((int64_t)c * Nv + h) * DK * C, DK * C * 4);
+#pragma unroll
+        for (int e = 0; e < NWT; ++e) wr[SET][e] = buf_ld_f32x4(rw, 16 * (tid + 256 * e));
     };
+    auto fetch_small = [&](int c) {
+        const int64_t s = chunk_start[c];
+        const int L = chunk_len[c];
+        const auto rx = buf_rsrc(dVX + (s * Nv + h) * DV + nb * 16, L > 0 ? (uint32_t)(((L - 1) * Nv * DV + 16) * 4) : 0u);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = 16 * w + 4 * qd + v;    // rows past the end (or past C) read as zero
+            xr[v] = buf_ld_f32(rx, (i * Nv * DV + r) * 4);
+        }
+        const auto ry = buf_rsrc(dSY + ((int64_t)c * Nv + h) * DK * DV + nb * 16, (uint32_t)((DK - 1) * DV + 16) * 4);
+#pragma unroll
+        for (int i = 0; i < NBW; ++i) {
+            const int m = w + 4 * i;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) yr[i][v] = buf_ld_f32(ry, ((16 * m + 4 * qd + v) * DV + r) * 4);
+        }
+        const auto rg = buf_rsrc(G + s * Nv + h, L > 0 ? (uint32_t)(((L - 1) * Nv + 1) * 4) : 0u);
+        gr = buf_ld_f32(rg, tid * Nv * 4);
+    };
+    auto put_dS = [&]() {                          // dS^T -> LDS
+#pragma unroll
+        for (int i = 0; i < NBW; ++i) {
+            const int m = w + 4 * i;
+            if (m < NB) *reinterpret_cast<f32x4*>(&dSt[r][16 * m + 4 * qd]) = dS[i];
+        }
+    };
+    typedef std::integral_constant<int, 0> S0_t;
+    typedef std::integral_constant<int, 1> S1_t;
+    put_dS();
     const int c0 = seq_first[n], c1 = seq_first[n + 1];
-    if (c1 > c0) fetch(c1 - 1);
-    for (int c = c1 - 1; c >= c0; --c) {
-        const int64_t s = chunk_start[c];
-        const int L = chunk_len[c];
-        lds_barrier();                                // the previous chunk's readers are done
-        commit();
-        float x[NZ], y[PER];
+    if (c1 <= c0) {
+        if (dS0) {                                  // no chunks: the gradient passes through
 #pragma unroll
-        for (int e = 0; e < NZ; ++e) x[e] = xr[e];
+            for (int i = 0; i < NBW; ++i) {
+                const int m = w + 4 * i;
+                if (m < NB) {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) y[e] = yr[e];
-        lds_barrier();
-        if (c > c0) fetch(c - 1);                     // in flight while this chunk is computed
-        const float gL = gs[L - 1];
-        // Z = diag(exp(G_last - G)) K dS; dV_new = X + Z. A thread's outputs share
-        // their column j (rows i0 + 16 e), so dS[m][j] is read once per m.
-        const int j0 = tid % 16, i0 = tid / 16;
-        {
-            float a[NZ];
-#pragma unroll
-            for (int e = 0; e < NZ; ++e) a[e] = 0.f;
-#pragma unroll 4
-            for (int m = 0; m < DK; ++m) {
-                const float d = dS[m][j0];
-#pragma unroll
-                for (int e = 0; e < NZ; ++e)
-                    if (NZ * 256 == C * 16 || i0 + 16 * e < C) a[e] += Ks[i0 + 16 * e][m] * d;
-            }
-#pragma unroll
-            for (int e = 0; e < NZ; ++e) {
-                const int i = i0 + 16 * e;
-                if (i < C) {
-                    const float z = i < L ? __expf(gL - gs[i]) * a[e] : 0.f;
-                    Zt[i][j0] = z;
-                    if (i < L) dVX[((s + i) * Nv + h) * DV + nb * 16 + j0] = x[e] + z;
+                    for (int v = 0; v < 4; ++v) dS0[(hb * DK + 16 * m + 4 * qd + v) * DV + nb * 16 + r] = dS[i][v];
                 }
             }
         }
-        lds_barrier();
-        // the outgoing-state gradient of this chunk, then dS <- exp(G_last) dS + Y' - W^T Z;
-        // a thread's outputs share their column j (rows i0 + 16 e), so Z[i][j] is read once per i
-        const float eL = __expf(gL);
-        float nw[PER], acc[PER];
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int m = i0 + 16 * e;
-            dSY[(((int64_t)c * Nv + h) * DK + m) * DV + nb * 16 + j0] = dS[m][j0];
-            acc[e] = 0.f;
-        }
-        for (int i = 0; i < L; ++i) {
-            const float z = Zt[i][j0];
-#pragma unroll
-            for (int e = 0; e < PER; ++e) acc[e] += Ws[i][i0 + 16 * e] * z;
-        }
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int m = i0 + 16 * e;
-            nw[e] = eL * dS[m][j0] + y[e] - acc[e];
-        }
-        lds_barrier();
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int idx = tid + 256 * e;
-            dS[idx / 16][idx % 16] = nw[e];
-        }
+        return;
     }
-    lds_barrier();
+    // every step issues its loads unconditionally (chunks before the first
+    // re-read chunk c0, unused), so that the compiler's waits count the same
+    // loads on every path
+    fetch_small(c1 - 1);
+    fetch_tiles(c1 - 1, S0_t{});
+    fetch_tiles(max(c1 - 2, c0), S1_t{});
+    auto step = [&](int c, auto set_t) {
+        constexpr int SET = decltype(set_t)::value;
+        const int64_t s = chunk_start[c];
+        const int L = chunk_len[c];
+        lds_barrier();                                // the previous chunk's reads are done
+#pragma unroll
+        for (int e = 0; e < NK8; ++e) {               // K rows and W^T -> LDS
+            const int idx = tid + 256 * e, i = idx / (DK / 8), seg = idx % (DK / 8);
+            if (NSEG % 256 == 0 || idx < NSEG) {
+                f32x4 a, b;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    a[t] = to_f(kr[SET][e][t]);
+                    b[t] = to_f(kr[SET][e][4 + t]);
+                }
+                *reinterpret_cast<f32x4*>(&Ks[i][seg * 8]) = a;
+                *reinterpret_cast<f32x4*>(&Ks[i][seg * 8 + 4]) = b;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < NWT; ++e) {
+            const int idx = tid + 256 * e;
+            if (NW4 % 256 == 0 || idx < NW4) *reinterpret_cast<f32x4*>(&Wt[idx / (C / 4)][4 * (idx % (C / 4))]) = wr[SET][e];
+        }
+        gs[tid] = gr;
+        const f32x4 x = xr;
+        f32x4 y[NBW];
+#pragma unroll
+        for (int i = 0; i < NBW; ++i) y[i] = yr[i];
+        lds_barrier();
+        // the small loads first: they are waited for at the next step's start,
+        // and loads complete in issue order
+        fetch_small(max(c - 1, c0));
+        fetch_tiles(max(c - 2, c0), set_t);          // in flight during this chunk and the next
+        const float gL = gs[L - 1];
+        // Z rows 16 w + 4 qd + v, column r; dV_new = X + Z
+        if (16 * w < C) {
+            f32x4 zu[4];                              // four independent sums (u), added at the end
+#pragma unroll
+            for (int u = 0; u < 4; ++u) zu[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < DK / 16; ++t) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(&Ks[16 * w + r][16 * t + 4 * qd]);
+                const f32x4 b = *reinterpret_cast<const f32x4*>(&dSt[r][16 * t + 4 * qd]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) zu[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], b[u], zu[u], 0, 0, 0);
+            }
+            f32x4 z = (zu[0] + zu[1]) + (zu[2] + zu[3]);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int i = 16 * w + 4 * qd + v;
+                z[v] = i < L ? __expf(gL - gs[i]) * z[v] : 0.f;
+                if (i < L) dVX[((s + i) * Nv + h) * DV + nb * 16 + r] = x[v] + z[v];
+            }
+            *reinterpret_cast<f32x4*>(&Zt[r][16 * w + 4 * qd]) = z;
+        }
+        lds_barrier();
+        // the outgoing-state gradient of this chunk, then dS <- exp(G_last) dS + Y' - W^T Z
+        const float eL = __expf(gL);
+#pragma unroll
+        for (int i = 0; i < NBW; ++i) {
+            const int m = w + 4 * i;
+            if (m < NB) {
+                f32x4 au[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};   // two independent sums
+#pragma unroll
+                for (int t = 0; t < C / 16; ++t) {
+                    const f32x4 a = *reinterpret_cast<const f32x4*>(&Wt[16 * m + r][16 * t + 4 * qd]);
+                    const f32x4 b = *reinterpret_cast<const f32x4*>(&Zt[r][16 * t + 4 * qd]);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        au[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], b[u], au[u & 1], 0, 0, 0);
+                }
+                const f32x4 acc = au[0] + au[1];
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    dSY[(((int64_t)c * Nv + h) * DK + 16 * m + 4 * qd + v) * DV + nb * 16 + r] = dS[i][v];
+                dS[i] = eL * dS[i] + y[i] - acc;
+            }
+        }
+        put_dS();
+    };
+    int c = c1 - 1;
+    for (; c - 1 >= c0; c -= 2) {
+        step(c, S0_t{});
+        step(c - 1, S1_t{});
+    }
+    if (c >= c0) step(c, S0_t{});
     if (dS0) {
-        for (int idx = tid; idx < DK * 16; idx += 256) {
-            const int m = idx / 16, j = idx % 16;
-            dS0[(((int64_t)n * Nv + h) * DK + m) * DV + nb * 16 + j] = dS[m][j];
+#pragma unroll
+        for (int i = 0; i < NBW; ++i) {
+            const int m = w + 4 * i;
+            if (m < NB) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) dS0[(hb * DK + 16 * m + 4 * qd + v) * DV + nb * 16 + r] = dS[i][v];
+            }
         }
     }
 }
@@ -684,12 +757,12 @@ hipError_t launch_bwd(const BackwardArgs& b) {
     if (NT > 0) {
         k_bwd_prep<T, DK, DV, C><<<dim3(NT, a.Nv), 256, 0, st>>>(
             (const T*)a.q, (const T*)a.k, a.G, (const float*)a.H, (const float*)a.VN, (const float*)a.W, b.d_o,
-            b.do_f32, a.scale, a.chunk_start, a.chunk_len, a.Nk, a.Nv, b.Hn, b.Vn, b.Wn, b.P, b.dVn, b.dSout);
+            b.do_f32, a.scale, a.chunk_start, a.chunk_len, a.Nk, a.Nv, b.Hn, b.Vn, b.WT, b.P, b.dVn, b.dSout);
     }
     mark(2);
     if (a.N > 0) {
         k_bwd_state<T, DK, DV, C><<<dim3(a.N, a.Nv, DV / 16), 256, 0, st>>>(
-            (const T*)a.k, a.G, b.Wn, b.dST, a.chunk_start, a.chunk_len, a.seq_first, a.Nk, a.Nv, b.dSout, b.dVn,
+            (const T*)a.k, a.G, b.WT, b.dST, a.chunk_start, a.chunk_len, a.seq_first, a.Nk, a.Nv, b.dSout, b.dVn,
             b.dS0);
     }
     mark(3);

@@ -251,6 +251,20 @@ __device__ __forceinline__ void buffer_to_lds4(__amdgpu_buffer_rsrc_t rs, const 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_dst, 4, voffset, 0, 0, 0);
 }
 
+// Range-checked loads: a buffer of `bytes` bytes at `base`; an access at or past
+// its end reads zero. A load whose invalid lanes fall outside the range needs
+// no select on the loaded value, so the wave does not wait for the load until
+// the value is used.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ f32x4 buf_ld_f32x4(__amdgpu_buffer_rsrc_t rs, int voffset) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voffset, 0, 0));
+}
+__device__ __forceinline__ float buf_ld_f32(__amdgpu_buffer_rsrc_t rs, int voffset) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voffset, 0, 0));
+}
+
 // Workgroup barrier for LDS traffic: this wave's LDS operations complete, then
 // all waves of the workgroup meet. Unlike __syncthreads() it does not wait for
 // the wave's outstanding global loads, stores or global-to-LDS copies; a copy

@@ -63,7 +63,8 @@ struct BackwardArgs {
     float *P;                  // [NT][Nv][C][C] score block (Q K^T) (.) D
     float *Hn;                 // [NT][Nv][dk][dv] entering states
     float *Vn, *dVn;           // [Ttot][Nv][dv] V_new and its gradient
-    float *Wn, *dWs;           // [Ttot][Nv][dk] W and its gradient
+    float *WT;                 // [NT][Nv][dk][C] W^T per chunk (zero past the chunk end)
+    float *dWs;                // [Ttot][Nv][dk] the gradient of W
     float *dSout;              // [NT][Nv][dk][dv] gradients of the outgoing states
     float *dqv, *dkv;          // [Ttot][Nv][dk] dq, dk per value head
     hipEvent_t* events;        // NULL, or 6 events: before the forward recompute and after
