@@ -65,12 +65,113 @@ constexpr int stage_floats(int R, int KT) {
     return R * stage_kpitch(KT) > KT * stage_rpitch(R) ? R * stage_kpitch(KT) : KT * stage_rpitch(R);
 }
 
+// Operands of a staged product. A global operand (kGlobal) loads raw 32-bit
+// words with range-checked buffer loads when a tile is fetched (an element
+// outside its matrix reads zero, so no select touches the loaded value) and
+// converts and scales them when the tile is committed to LDS: its loads stay
+// in flight while the previous tile's products run. Any other operand is a
+// function of (row, k) evaluated at commit (values in LDS).
+//
+// Matrix in global memory: element (row, col) at row * rstride + col
+// elements from the base; ES = 2 (bf16) or 4 (fp32) bytes, 0 when the
+// element size is the wave-uniform `es` (a tensor whose type is a runtime
+// argument: then every load reads the aligned 32-bit word that holds the
+// element, and the conversion picks its half). Rows at or past `rows` read as
+// zero.
+template <int ES>
+struct GMat {
+    __amdgpu_buffer_rsrc_t rs;
+    int rstride;
+    int es;
+    __device__ __forceinline__ static GMat make(const void* base, int64_t rstride, int rows, int cols, int es_rt = ES) {
+        GMat m;
+        const uint32_t bytes = rows > 0 ? (uint32_t)(((int64_t)(rows - 1) * rstride + cols) * es_rt) : 0u;
+        m.rs = buf_rsrc(base, bytes);
+        m.rstride = (int)rstride;
+        m.es = es_rt;
+        return m;
+    }
+    __device__ __forceinline__ uint32_t load(int row, int col, bool ok) const {
+        if constexpr (ES == 2) {
+            const int off = ok ? (row * rstride + col) * 2 : 0x7ffffff0;
+            return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
+        } else {
+            const int off = ok ? ((row * rstride + col) * (ES ? ES : es)) & ~3 : 0x7ffffff0;
+            return __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+        }
+    }
+    __device__ __forceinline__ float conv(uint32_t raw, int row, int col) const {
+        if constexpr (ES == 2) return __uint_as_float(raw << 16);
+        if constexpr (ES == 4) return __uint_as_float(raw);
+        if (es == 4) return __uint_as_float(raw);
+        return __uint_as_float(((row * rstride + col) & 1) ? (raw & 0xffff0000u) : (raw << 16));
+    }
+};
+template <typename T>
+constexpr int es_of() { return (int)sizeof(T); }
+
+// The operands below take the contraction index as k0 + kk, k0 being the
+// tile's first index (wave-uniform).
+// global operand x(row, k) = fin(row, k, M(row, k)), or M(k, row) when TR
+template <bool TR, int ES, typename Fin>
+struct GOp {
+    static constexpr bool kGlobal = true;
+    typedef uint32_t raw_t;
+    GMat<ES> m;
+    Fin fin;
+    __device__ __forceinline__ uint32_t load(int row, int k0, int kk, bool ok) const {
+        return TR ? m.load(k0 + kk, row, ok) : m.load(row, k0 + kk, ok);
+    }
+    __device__ __forceinline__ float value(uint32_t raw, int row, int k0, int kk) const {
+        return fin(row, k0 + kk, TR ? m.conv(raw, k0 + kk, row) : m.conv(raw, row, k0 + kk));
+    }
+};
+struct Ident {
+    __device__ __forceinline__ float operator()(int, int, float x) const { return x; }
+};
+template <bool TR, int ES, typename Fin = Ident>
+__device__ __forceinline__ GOp<TR, ES, Fin> gop(const GMat<ES>& m, Fin fin = Fin{}) {
+    return GOp<TR, ES, Fin>{m, fin};
+}
+// two global operands along k: x(row, k) = x0(row, k) for k < kc, else
+// x1(row, k - kc); kc is a multiple of the tile depth, so each tile reads one
+// of them (a wave-uniform branch with one load on either side)
+template <typename X0, typename X1>
+struct GCat {
+    static constexpr bool kGlobal = true;
+    X0 x0;
+    X1 x1;
+    int kc;
+    __device__ __forceinline__ uint32_t load(int row, int k0, int kk, bool ok) const {
+        if (k0 < kc) return x0.load(row, k0, kk, ok);
+        return x1.load(row, k0 - kc, kk, ok);
+    }
+    __device__ __forceinline__ float value(uint32_t raw, int row, int k0, int kk) const {
+        if (k0 < kc) return x0.value(raw, row, k0, kk);
+        return x1.value(raw, row, k0 - kc, kk);
+    }
+};
+template <typename X0, typename X1>
+__device__ __forceinline__ GCat<X0, X1> gcat(const X0& x0, const X1& x1, int kc) {
+    return GCat<X0, X1>{x0, x1, kc};
+}
+// operand evaluated at commit
+template <typename F>
+struct LOp {
+    static constexpr bool kGlobal = false;
+    F f;
+    __device__ __forceinline__ uint32_t load(int, int, int, bool) const { return 0u; }
+    __device__ __forceinline__ float value(uint32_t, int row, int k0, int kk) const { return f(row, k0 + kk); }
+};
+template <typename F>
+__device__ __forceinline__ LOp<F> lop(F f) { return LOp<F>{f}; }
 // One operand of a staged product: R rows by KT contraction indices, element
-// x(row, k). KC: consecutive k are adjacent in memory (else consecutive rows).
-// Each thread moves groups of 4 elements that are adjacent in memory.
+// x(row, k). KC: consecutive k are adjacent in LDS (else consecutive rows).
+// Each thread moves groups of 4 elements.
 template <int R, int KT, bool KC>
 struct StageOp {
     static constexpr int NG4 = R * KT / 4, NE = (NG4 + 255) / 256;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     static __device__ __forceinline__ int off(int row, int k) {
         return KC ? row * stage_kpitch(KT) + k : k * stage_rpitch(R) + row;
     }
@@ -80,26 +181,33 @@ struct StageOp {
         k = KC ? g4 % KT : g4 / R;
         return NG4 % 256 == 0 || g4 < 4 * NG4;
     }
-    template <typename F>
-    static __device__ __forceinline__ void fetch(f32x4 (&r)[NE], F&& x, int k0) {
+    template <typename X>
+    static __device__ __forceinline__ void fetch(u32x4 (&r)[NE], const X& x, int k0) {
+        if constexpr (X::kGlobal) {
 #pragma unroll
-        for (int e = 0; e < NE; ++e) {
-            int row, k;
-            const bool ok = coords(e, row, k);
+            for (int e = 0; e < NE; ++e) {
+                int row, k;
+                const bool ok = coords(e, row, k);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) r[e][u] = ok ? (KC ? x(row, k0 + k + u) : x(row + u, k0 + k)) : 0.f;
+                for (int u = 0; u < 4; ++u) r[e][u] = KC ? x.load(row, k0, k + u, ok) : x.load(row + u, k0, k, ok);
+            }
         }
     }
-    static __device__ __forceinline__ void commit(float* S, const f32x4 (&r)[NE]) {
+    template <typename X>
+    static __device__ __forceinline__ void commit(float* S, const u32x4 (&r)[NE], const X& x, int k0) {
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
             int row, k;
             if (coords(e, row, k)) {
+                f32x4 v;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    v[u] = KC ? x.value(r[e][u], row, k0, k + u) : x.value(r[e][u], row + u, k0, k);
                 if (KC) {
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) S[off(row, k + u)] = r[e][u];
+                    for (int u = 0; u < 4; ++u) S[off(row, k + u)] = v[u];
                 } else {
-                    *reinterpret_cast<f32x4*>(&S[off(row, k)]) = r[e];
+                    *reinterpret_cast<f32x4*>(&S[off(row, k)]) = v;
                 }
             }
         }
@@ -130,55 +238,96 @@ struct StageGrid {
     static constexpr int RM = TM / WM, RN = TN / WN;
 };
 
-// Staged product: out(i, j) = sum over k < K of a(i, k) b(k, j) for i < M,
-// j < N (M, N multiples of 16; K a multiple of KT, 16 or 32), on the fp32
-// matrix cores (v_mfma_f32_16x16x4_f32: products and sums in fp32). Tiles of
-// KT columns of a and KT rows of b go through LDS: each thread loads its
-// share of the next tile into registers while the current one is multiplied,
-// consecutive threads taking consecutive addresses of the operand (AK: a(i, k)
-// is contiguous in k, else in i; BJ: b(k, j) is contiguous in j, else in k).
-// Each wave accumulates its block of 16 x 16 tiles; lane 16 qd + r holds rows
-// 4 qd + 0..3 of column r of each tile. As and Bs hold stage_floats(M, KT)
-// and stage_floats(N, KT) floats. The product starts with a barrier, so its
-// operands may be LDS or memory written by the phase before; store(i, j, x)
-// is called once per output element, and for a given (M, N) always by the
-// same thread.
+// Staged product: out(i, j) = sum over k < K of a(i, k) b(j, k) for i < M,
+// j < N (b is given transposed; M, N multiples of 16; K a multiple of KT, 16
+// or 32), on the fp32 matrix cores (v_mfma_f32_16x16x4_f32: products and sums
+// in fp32). a and b are operands as above. Tiles of KT contraction indices of
+// both go through LDS: the raw words of a global operand's next tile are
+// loaded while the current one is multiplied, and converted when it is
+// committed; consecutive threads take consecutive addresses of the operand
+// (AK: a(i, k) is contiguous in k, else in i; BJ: b(j, k) is contiguous in j,
+// else in k). Each wave accumulates its block of 16 x 16 tiles; lane 16 qd + r
+// holds rows 4 qd + 0..3 of column r of each tile. As and Bs hold
+// stage_floats(M, KT) and stage_floats(N, KT) floats. The product starts with
+// a barrier, so its operands may be LDS or memory written by the phase
+// before; store(i, j, x) is called once per output element, and for a given
+// (M, N) always by the same thread.
 // Row sums: when store returns a float (a contribution of element (i, j) to a
 // sum over j), the sums of each row are formed in a fixed order (per lane over
 // its tiles, then a butterfly over the 16 lanes of a row) and wave column wn
 // writes its part to Red[wn * M + i]; the caller adds the StageGrid<M, N>::WN
 // parts after a barrier. No atomics: the result is the same on every run.
+// no epilogue operand
+struct NoEp {
+    static constexpr bool kGlobal = false;
+    typedef uint32_t raw_t;
+};
+// two epilogue operands: store receives a float2 (x0(i, j), x1(i, j))
+template <typename X0, typename X1>
+struct EpPair {
+    static constexpr bool kGlobal = true;
+    typedef uint32_t raw_t __attribute__((ext_vector_type(2)));
+    X0 x0;
+    X1 x1;
+    __device__ __forceinline__ raw_t load(int i, int k0, int j, bool ok) const {
+        return raw_t{x0.load(i, k0, j, ok), x1.load(i, k0, j, ok)};
+    }
+    __device__ __forceinline__ float2 value(raw_t raw, int i, int k0, int j) const {
+        return make_float2(x0.value(raw[0], i, k0, j), x1.value(raw[1], i, k0, j));
+    }
+};
+template <typename X0, typename X1>
+__device__ __forceinline__ EpPair<X0, X1> ep_pair(const X0& x0, const X1& x1) {
+    return EpPair<X0, X1>{x0, x1};
+}
+// gemm_lds_e: as gemm_lds, with an epilogue operand ep (a global operand of
+// the output's shape): its elements are loaded together once the products are
+// issued and passed to store(i, j, x, ep(i, j)).
+template <int M, int N, bool AK, bool BJ, int KT, typename FA, typename FB, typename EP, typename FS>
+__device__ __forceinline__ void gemm_lds_e(int K, float* As, float* Bs, const FA& a, const FB& b, const EP& ep,
+                                           FS&& store, float* Red);
 template <int M, int N, bool AK, bool BJ, int KT = kStageK, typename FA, typename FB, typename FS>
-__device__ __forceinline__ void gemm_lds(int K, float* As, float* Bs, FA&& a, FB&& b, FS&& store,
+__device__ __forceinline__ void gemm_lds(int K, float* As, float* Bs, const FA& a, const FB& b, FS&& store,
                                          float* Red = nullptr) {
+    gemm_lds_e<M, N, AK, BJ, KT>(K, As, Bs, a, b, NoEp{}, store, Red);
+}
+template <int M, int N, bool AK, bool BJ, int KT, typename FA, typename FB, typename EP, typename FS>
+__device__ __forceinline__ void gemm_lds_e(int K, float* As, float* Bs, const FA& a, const FB& b, const EP& ep,
+                                           FS&& store, float* Red) {
     static_assert(M % 16 == 0 && N % 16 == 0 && KT % 4 == 0, "16 x 16 tiles");
     using OA = StageOp<M, KT, AK>;
     using OB = StageOp<N, KT, !BJ>;
     using SG = StageGrid<M, N>;
     constexpr int WM = SG::WM, WN = SG::WN, RM = SG::RM, RN = SG::RN;
-    constexpr bool kRowSum = !std::is_void<decltype(store(0, 0, 0.f))>::value;
+    constexpr bool kEp = !std::is_same<EP, NoEp>::value;
+    typedef typename EP::raw_t raw_t;
+    auto st = [&](int i, int j, float x, raw_t e) {
+        if constexpr (kEp) return store(i, j, x, ep.value(e, i, 0, j));
+        else return store(i, j, x);
+    };
+    constexpr bool kRowSum = !std::is_void<decltype(st(0, 0, 0.f, raw_t{}))>::value;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const bool active = w < WM * WN;
     const int tm0 = (w / WN) * RM, tn0 = (w % WN) * RN;
     const int r = lane & 15, qd = lane >> 4;
-    auto bx = [&](int j, int k) { return b(k, j); };
     f32x4 acc[RM][RN];
 #pragma unroll
     for (int x = 0; x < RM; ++x)
 #pragma unroll
         for (int y = 0; y < RN; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 ra[OA::NE], rb[OB::NE];
+    typename OA::u32x4 ra[OA::NE];
+    typename OB::u32x4 rb[OB::NE];
     __syncthreads();                                   // operands written by the previous phase are visible
     OA::fetch(ra, a, 0);
-    OB::fetch(rb, bx, 0);
+    OB::fetch(rb, b, 0);
     for (int k0 = 0; k0 < K; k0 += KT) {
-        __syncthreads();                               // the previous tile is consumed
-        OA::commit(As, ra);
-        OB::commit(Bs, rb);
-        __syncthreads();
+        lds_barrier();                                 // the previous tile is consumed (LDS only:
+        OA::commit(As, ra, a, k0);                     // the prefetched loads stay in flight)
+        OB::commit(Bs, rb, b, k0);
+        lds_barrier();
         if (k0 + KT < K) {                             // in flight during this tile's products
             OA::fetch(ra, a, k0 + KT);
-            OB::fetch(rb, bx, k0 + KT);
+            OB::fetch(rb, b, k0 + KT);
         }
         if (active) {
 #pragma unroll
@@ -197,6 +346,16 @@ __device__ __forceinline__ void gemm_lds(int K, float* As, float* Bs, FA&& a, FB
         }
     }
     if (active) {
+        raw_t ev[RM][4][RN];
+#pragma unroll
+        for (int x = 0; x < RM; ++x)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                for (int y = 0; y < RN; ++y) {
+                    if constexpr (kEp) ev[x][jj][y] = ep.load(16 * (tm0 + x) + 4 * qd + jj, 0, 16 * (tn0 + y) + r, true);
+                    else ev[x][jj][y] = raw_t{};
+                }
 #pragma unroll
         for (int x = 0; x < RM; ++x)
 #pragma unroll
@@ -205,13 +364,13 @@ __device__ __forceinline__ void gemm_lds(int K, float* As, float* Bs, FA&& a, FB
                 if constexpr (kRowSum) {
                     float part = 0.f;
 #pragma unroll
-                    for (int y = 0; y < RN; ++y) part += store(i, 16 * (tn0 + y) + r, acc[x][y][jj]);
+                    for (int y = 0; y < RN; ++y) part += st(i, 16 * (tn0 + y) + r, acc[x][y][jj], ev[x][jj][y]);
 #pragma unroll
                     for (int o = 8; o > 0; o >>= 1) part += __shfl_xor(part, o);
                     if (r == 0) Red[(w % WN) * M + i] = part;
                 } else {
 #pragma unroll
-                    for (int y = 0; y < RN; ++y) store(i, 16 * (tn0 + y) + r, acc[x][y][jj]);
+                    for (int y = 0; y < RN; ++y) st(i, 16 * (tn0 + y) + r, acc[x][y][jj], ev[x][jj][y]);
                 }
             }
     }
@@ -254,38 +413,62 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ q, const
         se[tid] = tid < L ? scale * __expf(gs[tid]) : 0.f;
     }
     const int64_t ch = (int64_t)c * Nv + h;
-    for (int idx = tid; idx < DK * DV; idx += 256) {
-        const int i = idx / DV, j = idx % DV;
-        Hn[ch * DK * DV + idx] = Hf[((ch * NNB + j / 16) * NKP + i / 32) * 512 + pair_off(j % 16, i % 32)];
-    }
-    for (int idx = tid; idx < L * DV; idx += 256) {
-        const int p = idx / DV, j = idx % DV;
-        Vn[((s + p) * Nv + h) * DV + j] = VNf[((ch * NNB + j / 16) * NTP + p / 32) * 512 + pair_off(j % 16, p % 32)];
-    }
-    for (int idx = tid; idx < DK * C; idx += 256) {      // W^T of the chunk, zero past its end
-        const int i = idx / C, p = idx % C;
-        WT[(ch * DK + i) * C + p] =
-            p < L ? Wf[((ch * NTB + p / 16) * NKP + i / 32) * 512 + pair_off(p % 16, i % 32)] : 0.f;
-    }
-    auto Qg = [&](int i, int m) { return i < L ? to_f(q[((s + i) * Nk + kh) * DK + m]) : 0.f; };
-    auto Kg = [&](int i, int m) { return i < L ? to_f(k[((s + i) * Nk + kh) * DK + m]) : 0.f; };
-    auto dOg = [&](int i, int j) { return i < L ? load_any(d_o, ((s + i) * Nv + h) * DV + j, do_f32) : 0.f; };
+    // element-wise copies in batches: 16 loads per thread in flight, then their stores
+    auto batched = [&](auto n_t, auto&& ld, auto&& st) {
+        constexpr int N = decltype(n_t)::value, PER = (N + 255) / 256, B = PER < 16 ? PER : 16;
+        static_assert(PER % B == 0, "batch");
+#pragma unroll
+        for (int b0 = 0; b0 < PER; b0 += B) {
+            float x[B];
+#pragma unroll
+            for (int e = 0; e < B; ++e) {
+                const int idx = tid + 256 * (b0 + e);
+                x[e] = (N % 256 == 0 || idx < N) ? ld(idx) : 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < B; ++e) {
+                const int idx = tid + 256 * (b0 + e);
+                if (N % 256 == 0 || idx < N) st(idx, x[e]);
+            }
+        }
+    };
+    batched(std::integral_constant<int, DK * DV>{},
+            [&](int idx) { const int i = idx / DV, j = idx % DV;
+                           return Hf[((ch * NNB + j / 16) * NKP + i / 32) * 512 + pair_off(j % 16, i % 32)]; },
+            [&](int idx, float x) { Hn[ch * DK * DV + idx] = x; });
+    batched(std::integral_constant<int, C * DV>{},
+            [&](int idx) { const int p = idx / DV, j = idx % DV;
+                           return VNf[((ch * NNB + j / 16) * NTP + p / 32) * 512 + pair_off(j % 16, p % 32)]; },
+            [&](int idx, float x) { const int p = idx / DV, j = idx % DV;
+                                    if (p < L) Vn[((s + p) * Nv + h) * DV + j] = x; });
+    batched(std::integral_constant<int, DK * C>{},              // W^T of the chunk, zero past its end
+            [&](int idx) { const int i = idx / C, p = idx % C;
+                           return Wf[((ch * NTB + p / 16) * NKP + i / 32) * 512 + pair_off(p % 16, i % 32)]; },
+            [&](int idx, float x) { const int i = idx / C, p = idx % C; WT[(ch * DK + i) * C + p] = p < L ? x : 0.f; });
+    constexpr int EI = es_of<T>();
+    const int esd = do_f32 ? 4 : 2;
+    const auto Qm = GMat<EI>::make(q + (s * Nk + kh) * DK, (int64_t)Nk * DK, L, DK);
+    const auto Km = GMat<EI>::make(k + (s * Nk + kh) * DK, (int64_t)Nk * DK, L, DK);
+    const auto dOm = GMat<0>::make(static_cast<const char*>(d_o) + (s * Nv + h) * DV * esd, (int64_t)Nv * DV, L, DV, esd);
+    const auto Xm = GMat<4>::make(X + (s * Nv + h) * DV, (int64_t)Nv * DV, L, DV);
+    const auto WTm = GMat<4>::make(WT + ch * DK * C, C, DK, C);
     float* Pc = P + ch * C * C;
-    gemm_lds<C, C, true, false, KT>(DK, As, Bs, Qg, [&](int kk, int j) { return Kg(j, kk); },
+    // P = (Q K^T) (.) D
+    gemm_lds<C, C, true, false, KT>(DK, As, Bs, gop<false>(Qm), gop<false>(Km),
         [&](int i, int j, float x) {
             const float pv = (i < L && j <= i) ? x * __expf(gs[i] - gs[j]) : 0.f;
             Pm[i * C + j] = pv;
             Pc[i * C + j] = pv;
         });
-    gemm_lds<C, DV, false, true, (C % 32 == 0 ? KT : 16)>(C, As, Bs, [&](int i, int t) { return Pm[t * C + i]; }, dOg,
+    // X = scale P^T dO
+    gemm_lds<C, DV, false, true, (C % 32 == 0 ? KT : 16)>(C, As, Bs, lop([&](int i, int t) { return Pm[t * C + i]; }),
+                                 gop<true>(dOm),
                                  [&](int i, int j, float x) { if (i < L) X[((s + i) * Nv + h) * DV + j] = scale * x; });
-    gemm_lds<DK, DV, false, true, KT>(2 * C, As, Bs,
-        [&](int m, int kk) {
-            return kk < C ? Qg(kk, m) : -WT[(ch * DK + m) * C + kk - C];
-        },
-        [&](int kk, int j) {
-            return kk < C ? se[kk] * dOg(kk, j) : (kk - C < L ? X[((s + kk - C) * Nv + h) * DV + j] : 0.f);
-        },
+    // Y' = Q^T diag(scale exp(G)) dO - W^T X (contraction over [Q rows | W^T columns])
+    // (tiles of 16 when C = 16: a tile must not straddle the two parts)
+    gemm_lds<DK, DV, false, true, (C % 32 == 0 ? KT : 16)>(2 * C, As, Bs,
+        gcat(gop<true>(Qm), gop<false>(WTm, [](int, int, float x) { return -x; }), C),
+        gcat(gop<true>(dOm, [&](int, int t, float x) { return se[t] * x; }), gop<true>(Xm), C),
         [&](int m, int j, float x) { Yp[(ch * DK + m) * DV + j] = x; });
 }
 
@@ -549,15 +732,22 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(const T* __restrict__ q, c
     const float* dSc = dSout + ch * DK * DV;      // gradient of the outgoing state [dk][dv]
     const float* Pc = P + ch * C * C;
 
-    auto Qg = [&](int i, int m) { return i < L ? to_f(q[((s + i) * Nk + kh) * DK + m]) : 0.f; };
-    auto Kg = [&](int i, int m) { return i < L ? to_f(k[((s + i) * Nk + kh) * DK + m]) : 0.f; };
-    auto Vg = [&](int i, int j) { return i < L ? to_f(v[((s + i) * Nv + h) * DV + j]) : 0.f; };
-    auto dOg = [&](int i, int j) { return i < L ? load_any(d_o, ((s + i) * Nv + h) * DV + j, do_f32) : 0.f; };
-    auto Vng = [&](int i, int j) { return i < L ? Vn[((s + i) * Nv + h) * DV + j] : 0.f; };
-    auto dVg = [&](int i, int j) { return i < L ? dVn[((s + i) * Nv + h) * DV + j] : 0.f; };
-    auto dWg = [&](int i, int m) { return i < L ? dW[((s + i) * Nv + h) * DK + m] : 0.f; };
     auto row_dk = [&](int i) { return ((s + i) * Nv + h) * DK; };
     auto Dv = [&](int i, int j) { return (i < L && j <= i) ? __expf(gs[i] - gs[j]) : 0.f; };
+    // the same matrices as operands of the staged products (rows past the chunk end read zero)
+    constexpr int EI = es_of<T>();
+    const int esd = do_f32 ? 4 : 2;
+    const auto Qm = GMat<EI>::make(q + (s * Nk + kh) * DK, (int64_t)Nk * DK, L, DK);
+    const auto Km = GMat<EI>::make(k + (s * Nk + kh) * DK, (int64_t)Nk * DK, L, DK);
+    const auto Vm = GMat<EI>::make(v + (s * Nv + h) * DV, (int64_t)Nv * DV, L, DV);
+    const auto dOm = GMat<0>::make(static_cast<const char*>(d_o) + (s * Nv + h) * DV * esd, (int64_t)Nv * DV, L, DV, esd);
+    const auto Vnm = GMat<4>::make(Vn + (s * Nv + h) * DV, (int64_t)Nv * DV, L, DV);
+    const auto dVnm = GMat<4>::make(dVn + (s * Nv + h) * DV, (int64_t)Nv * DV, L, DV);
+    const auto dWm = GMat<4>::make(dW + (s * Nv + h) * DK, (int64_t)Nv * DK, L, DK);
+    const auto Hm = GMat<4>::make(Hc, DV, DK, DV);
+    const auto dSm = GMat<4>::make(dSc, DV, DK, DV);
+    const auto dqvm = GMat<4>::make(dqv + (s * Nv + h) * DK, (int64_t)Nv * DK, L, DK);
+    const auto dkvm = GMat<4>::make(dkv + (s * Nv + h) * DK, (int64_t)Nv * DK, L, DK);
 
     if (tid < C) {
         const bool ok = tid < L;
@@ -566,9 +756,20 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(const T* __restrict__ q, c
         dGs[tid] = 0.f;
         dBs[tid] = 0.f;
     }
-    for (int idx = tid; idx < C * C; idx += 256) {
-        const int i = idx / C, j = idx % C;
-        Am[idx] = (i < L && j <= i) ? A[((s + i) * Nv + h) * C + j] : 0.f;
+    {   // A of the chunk: all loads first (rows past the end read zero), then the mask
+        constexpr int NA = (C * C + 255) / 256;
+        const auto rA = buf_rsrc(A + (s * Nv + h) * C, (uint32_t)(((L - 1) * Nv + 1) * C * 4));
+        float av[NA];
+#pragma unroll
+        for (int e = 0; e < NA; ++e) {
+            const int idx = tid + 256 * e;
+            av[e] = buf_ld_f32(rA, idx < C * C ? ((idx / C) * Nv * C + idx % C) * 4 : 0x7ffffff0);
+        }
+#pragma unroll
+        for (int e = 0; e < NA; ++e) {
+            const int idx = tid + 256 * e, i = idx / C, j = idx % C;
+            if (idx < C * C) Am[idx] = j <= i ? av[e] : 0.f;
+        }
     }
     __syncthreads();
     const float gL = gs[L - 1];
@@ -580,15 +781,16 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(const T* __restrict__ q, c
     // dP = scale dO V_new^T on and below the diagonal; dM = dP (.) D, and the gate
     // gradient through D in P: E = dP (.) P (kept in Xm) adds its row sums to dG
     // and subtracts its column sums
-    gemm_lds<C, C, true, false>(DV, As, Bs, dOg, [&](int kk, int j) { return Vng(j, kk); },
-        [&](int i, int j, float x) {
+    gemm_lds_e<C, C, true, false, kStageK>(DV, As, Bs, gop<false>(dOm), gop<false>(Vnm),
+        gop<false>(GMat<4>::make(Pc, C, C, C)),
+        [&](int i, int j, float x, float p) {
             const float dp = (i < L && j <= i) ? scale * x : 0.f;
             dMm[i * C + j] = dp * Dv(i, j);
-            Xm[i * C + j] = dp * Pc[i * C + j];
-        });
+            Xm[i * C + j] = dp * p;
+        }, nullptr);
     // dQ = scale diag(exp(G)) dO h^T + dM K (the same thread owns each element in both products)
-    gemm_lds<C, DK, true, false>(DV, As, Bs, [&](int i, int kk) { return scale * eg[i] * dOg(i, kk); },
-                                 [&](int kk, int m) { return Hc[m * DV + kk]; },
+    gemm_lds<C, DK, true, false>(DV, As, Bs, gop<false>(dOm, [&](int i, int, float x) { return scale * eg[i] * x; }),
+                                 gop<false>(Hm),
                                  [&](int i, int m, float x) { if (i < L) dqv[row_dk(i) + m] = x; });
     {   // row and column sums of E, 256 / C threads per position, in a fixed order
         constexpr int TPR = 256 / C;
@@ -605,26 +807,30 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(const T* __restrict__ q, c
         }
         if (part == 0) dGs[i] += rs - cs;
     }
-    gemm_lds<C, DK, true, true>(C, As, Bs, [&](int i, int kk) { return dMm[i * C + kk]; }, Kg,
-                                [&](int i, int m, float x) { if (i < L) dqv[row_dk(i) + m] += x; });
+    gemm_lds_e<C, DK, true, true, kStageK>(C, As, Bs, lop([&](int i, int kk) { return dMm[i * C + kk]; }), gop<true>(Km),
+                                           gop<false>(dqvm),
+                                           [&](int i, int m, float x, float old) { if (i < L) dqv[row_dk(i) + m] = old + x; },
+                                           nullptr);
     // dW = -dV_new h^T
-    gemm_lds<C, DK, true, false>(DV, As, Bs, dVg, [&](int kk, int m) { return Hc[m * DV + kk]; },
+    gemm_lds<C, DK, true, false>(DV, As, Bs, gop<false>(dVnm), gop<false>(Hm),
                                  [&](int i, int m, float x) { if (i < L) dW[row_dk(i) + m] = -x; });
     // dV = diag(beta) A^T dU (dU = dV_new); dbeta += v . (A^T dU)  (row sums in dAm, free until dA)
     float* const red1 = dAm;
     float* const red2 = dAm + 4 * C;
-    gemm_lds<C, DV, false, true>(C, As, Bs, [&](int i, int kk) { return Am[kk * C + i]; }, dVg,
-        [&](int i, int j, float x) {
+    gemm_lds_e<C, DV, false, true, kStageK>(C, As, Bs, lop([&](int i, int kk) { return Am[kk * C + i]; }), gop<true>(dVnm),
+        gop<false>(Vm),
+        [&](int i, int j, float x, float vij) {
             if (i >= L) return 0.f;
             dv[((s + i) * Nv + h) * DV + j] = bs[i] * x;
-            return Vg(i, j) * x;
+            return vij * x;
         }, red1);
     // A^T dW: dK = diag(beta exp(G)) A^T dW; dbeta, dG through exp(G) in W
-    gemm_lds<C, DK, false, true>(C, As, Bs, [&](int i, int kk) { return Am[kk * C + i]; }, dWg,
-        [&](int i, int m, float x) {
+    gemm_lds_e<C, DK, false, true, kStageK>(C, As, Bs, lop([&](int i, int kk) { return Am[kk * C + i]; }), gop<true>(dWm),
+        gop<false>(Km),
+        [&](int i, int m, float x, float kim) {
             if (i >= L) return 0.f;
             dkv[row_dk(i) + m] = bs[i] * eg[i] * x;
-            return Kg(i, m) * x * eg[i];
+            return kim * x * eg[i];
         }, red2);
     __syncthreads();
     if (tid < C) {
@@ -637,19 +843,20 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(const T* __restrict__ q, c
         dGs[tid] += bs[tid] * r2;
     }
     // dA = dU (diag(beta) V)^T + dW (diag(beta exp(G)) K)^T
-    gemm_lds<C, C, true, false>(DV, As, Bs, dVg, [&](int kk, int j) { return bs[j] * Vg(j, kk); },
+    gemm_lds<C, C, true, false>(DV, As, Bs, gop<false>(dVnm), gop<false>(Vm, [&](int j, int, float x) { return bs[j] * x; }),
                                 [&](int i, int j, float x) { dAm[i * C + j] = x; });
-    gemm_lds<C, C, true, false>(DK, As, Bs, dWg, [&](int kk, int j) { return bs[j] * eg[j] * Kg(j, kk); },
+    gemm_lds<C, C, true, false>(DK, As, Bs, gop<false>(dWm),
+                                gop<false>(Km, [&](int j, int, float x) { return bs[j] * eg[j] * x; }),
                                 [&](int i, int j, float x) { dAm[i * C + j] += x; });
     // A^T dA, then F = strictly lower part of dL = -(A^T dA) A^T
-    gemm_lds<C, C, false, true>(C, As, Bs, [&](int i, int kk) { return Am[kk * C + i]; },
-                                [&](int kk, int j) { return dAm[kk * C + j]; },
+    gemm_lds<C, C, false, true>(C, As, Bs, lop([&](int i, int kk) { return Am[kk * C + i]; }),
+                                lop([&](int j, int kk) { return dAm[kk * C + j]; }),
                                 [&](int i, int j, float x) { Xm[i * C + j] = x; });
-    gemm_lds<C, C, true, false>(C, As, Bs, [&](int i, int kk) { return Xm[i * C + kk]; },
-                                [&](int kk, int j) { return Am[j * C + kk]; },
+    gemm_lds<C, C, true, false>(C, As, Bs, lop([&](int i, int kk) { return Xm[i * C + kk]; }),
+                                lop([&](int j, int kk) { return Am[j * C + kk]; }),
                                 [&](int i, int j, float x) { dAm[i * C + j] = (i < L && j < i) ? -x : 0.f; });
     // K K^T
-    gemm_lds<C, C, true, false>(DK, As, Bs, Kg, [&](int kk, int j) { return Kg(j, kk); },
+    gemm_lds<C, C, true, false>(DK, As, Bs, gop<false>(Km), gop<false>(Km),
                                 [&](int i, int j, float x) { Xm[i * C + j] = x; });
     __syncthreads();
     // dbeta and dG through L_ij = beta_i (k_i . k_j) D_ij
@@ -666,33 +873,43 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(const T* __restrict__ q, c
     __syncthreads();
     for (int idx = tid; idx < C * C; idx += 256) dAm[idx] *= Dv(idx / C, idx % C);   // F (.) D
     // dK += diag(beta) (F (.) D) K + (F (.) D)^T diag(beta) K + dM^T Q
-    gemm_lds<C, DK, false, true>(3 * C, As, Bs,
-        [&](int i, int kk) {
+    gemm_lds_e<C, DK, false, true, kStageK>(3 * C, As, Bs,
+        lop([&](int i, int kk) {
             return kk < C ? bs[i] * dAm[i * C + kk]
-                          : (kk < 2 * C ? dAm[(kk - C) * C + i] : dMm[(kk - 2 * C) * C + i]);
-        },
-        [&](int kk, int m) {
-            return kk < C ? Kg(kk, m) : (kk < 2 * C ? bs[kk - C] * Kg(kk - C, m) : Qg(kk - 2 * C, m));
-        },
-        [&](int i, int m, float x) { if (i < L) dkv[row_dk(i) + m] += x; });
+                          : (kk < 2 * C ? bs[kk - C] * dAm[(kk - C) * C + i] : dMm[(kk - 2 * C) * C + i]);
+        }),
+        gcat(gop<true>(Km), gcat(gop<true>(Km), gop<true>(Qm), C), C), gop<false>(dkvm),
+        [&](int i, int m, float x, float old) { if (i < L) dkv[row_dk(i) + m] = old + x; }, nullptr);
     // dK += diag(exp(G_last - G)) V_new dS^T; the same term's gate gradient (row sums
     // in Xm, free after the dK product above)
     float* const red3 = Xm;
     float* const red4 = Xm + 4 * C;
-    gemm_lds<C, DK, true, false>(DV, As, Bs, Vng, [&](int kk, int m) { return dSc[m * DV + kk]; },
-        [&](int i, int m, float x) {
+    gemm_lds_e<C, DK, true, false, kStageK>(DV, As, Bs, gop<false>(Vnm), gop<false>(dSm), ep_pair(gop<false>(dkvm), gop<false>(Km)),
+        [&](int i, int m, float x, float2 e) {
             if (i >= L) return 0.f;
             const float y = elg[i] * x;
-            dkv[row_dk(i) + m] += y;
-            return Kg(i, m) * y;
+            dkv[row_dk(i) + m] = e.x + y;
+            return e.y * y;
         }, red3);
     // dG through exp(G) in the inter-chunk output: dG_i += dO_i . (scale exp(G_i) h^T q_i)
-    gemm_lds<C, DV, true, true>(DK, As, Bs, Qg, [&](int kk, int j) { return Hc[kk * DV + j]; },
-        [&](int i, int j, float x) { return i < L ? scale * eg[i] * dOg(i, j) * x : 0.f; }, red4);
+    gemm_lds_e<C, DV, true, true, kStageK>(DK, As, Bs, gop<false>(Qm), gop<true>(Hm), gop<false>(dOm),
+        [&](int i, int j, float x, float d) { return i < L ? scale * eg[i] * d * x : 0.f; }, red4);
     // exp(G_last) h in the state update: sum(dS (.) h), per wave then over the waves
     {
         float part = 0.f;
-        for (int idx = tid; idx < DK * DV; idx += 256) part += dSc[idx] * Hc[idx];
+        constexpr int N4 = DK * DV / 4 / 256, NBATCH = N4 < 8 ? N4 : 8;   // 16-byte pieces per thread
+        static_assert(N4 % NBATCH == 0, "dk dv");
+#pragma unroll
+        for (int b0 = 0; b0 < N4; b0 += NBATCH) {      // a batch of loads, then their products
+            f32x4 xs[NBATCH], xh[NBATCH];
+#pragma unroll
+            for (int e = 0; e < NBATCH; ++e) {
+                xs[e] = *reinterpret_cast<const f32x4*>(dSc + 4 * (tid + 256 * (b0 + e)));
+                xh[e] = *reinterpret_cast<const f32x4*>(Hc + 4 * (tid + 256 * (b0 + e)));
+            }
+#pragma unroll
+            for (int e = 0; e < NBATCH; ++e) part += (xs[e][0] * xh[e][0] + xs[e][1] * xh[e][1]) + (xs[e][2] * xh[e][2] + xs[e][3] * xh[e][3]);
+        }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
         if ((tid & 63) == 0) wsum[tid >> 6] = part;
