@@ -13,7 +13,10 @@ from typing import Optional
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_build", "libgdr.so")
+# GDR_LIBRARY names another build of the same library (the host-sanitizer
+# build that tests/sanitize_cpu.py makes); the default is the in-tree build
+_LIB_PATH = os.environ.get("GDR_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "_build",
+                                                          "libgdr.so")
 _lib = None
 
 GDR_F32, GDR_BF16 = 0, 1
@@ -151,8 +154,31 @@ def _aligned16(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
     return t.clone(memory_format=torch.contiguous_format)
 
 
+_GUARD_BYTE = 0xA5
+
+
+def _guarded(nbytes, guard, dev):
+    """A uint8 buffer of nbytes with `guard` canary bytes (0xA5) before and
+    after it: returns (whole buffer, the inner part)."""
+    whole = torch.empty(nbytes + 2 * guard, dtype=torch.uint8, device=dev)
+    whole[:guard].fill_(_GUARD_BYTE)
+    whole[guard + nbytes:].fill_(_GUARD_BYTE)
+    return whole, whole[guard:guard + nbytes]
+
+
+def _check_guards(guards, guard):
+    """Raise if a kernel wrote into the canary bytes around a buffer."""
+    for name, whole in guards:
+        n = whole.numel() - 2 * guard
+        for part, band in (("before", whole[:guard]), ("after", whole[guard + n:])):
+            bad = (band != _GUARD_BYTE).nonzero()
+            if bad.numel():
+                raise RuntimeError("write %s the %s buffer: %d canary bytes changed, first at offset %d"
+                                   % (part, name, bad.numel(), int(bad[0])))
+
+
 def _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu, chunk_size,
-             output_final_state, out_dtype, debug=False, workspace=True, segment_chunks=None):
+             output_final_state, out_dtype, debug=False, workspace=True, segment_chunks=None, guard=0):
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:2] != q.shape[:2]:
         raise ValueError("expected q, k [B,T,Nk,dk] and v [B,T,Nv,dv]")
     dev = q.device
@@ -188,36 +214,63 @@ def _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu,
         raise ValueError("out_dtype must be the io dtype or float32")
     prob = make_problem(B, T, Nk, Nv, dk, dv, N, _DTYPES[q.dtype], _DTYPES[beta.dtype], chunk_size,
                         _DTYPES[out_dtype])
-    o = torch.empty(v.shape, dtype=out_dtype, device=dev)
-    S_T = torch.empty((N, Nv, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
+    guards = []
+    if guard:                                 # debug canaries around every buffer the call writes
+        if guard % 256:
+            raise ValueError("guard must be a multiple of 256 bytes")
+        ob = torch.empty((), dtype=out_dtype).element_size() * v.numel()
+        whole, inner = _guarded(ob, guard, dev)
+        o = inner.view(out_dtype).view(v.shape)
+        guards.append(("o", whole))
+        S_T = None
+        if output_final_state:
+            whole, inner = _guarded(4 * N * Nv * dk * dv, guard, dev)
+            S_T = inner.view(torch.float32).view((N, Nv, dk, dv))
+            guards.append(("final state", whole))
+    else:
+        o = torch.empty(v.shape, dtype=out_dtype, device=dev)
+        S_T = torch.empty((N, Nv, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
     if not workspace:                         # token-by-token path: no workspace
         return prob, o, S_T, cu_dev, cu_host, scale, (q, k, v, beta, g, initial_state)
-    ws = torch.empty(workspace_size(prob, debug, segment_chunks), dtype=torch.uint8, device=dev)
+    if guard:
+        whole, ws = _guarded(workspace_size(prob, debug, segment_chunks), guard, dev)
+        guards.append(("workspace", whole))
+    else:
+        ws = torch.empty(workspace_size(prob, debug, segment_chunks), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     args = [ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), ctypes.c_float(scale),
             _ptr(initial_state), _ptr(cu_dev), _ptr(cu_host), _ptr(o), _ptr(S_T), _ptr(ws),
             ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream)]
     if segment_chunks is not None:            # gdr_chunk_fwd_segmented: segment_chunks before the workspace
         args = args[:12] + [ctypes.c_int32(segment_chunks)] + args[12:]
-    keep = (cu_dev, cu_host, ws, q, k, v, beta, g, initial_state)
+    keep = (cu_dev, cu_host, ws, q, k, v, beta, g, initial_state, guards)
     return prob, args, o, S_T, keep
 
 
 def chunk_fwd(q, k, v, beta, g=None, scale=None, initial_state=None, output_final_state=True,
-              cu_seqlens=None, cu_seqlens_cpu=None, chunk_size=64, out_dtype=None, segment_chunks=None):
+              cu_seqlens=None, cu_seqlens_cpu=None, chunk_size=64, out_dtype=None, segment_chunks=None,
+              guard=0):
     """Chunked gated delta-rule forward. Returns (o, final_state or None).
 
     out_dtype: dtype of o, the io dtype (default) or torch.float32.
     segment_chunks: None runs gdr_chunk_fwd (one serial state pass per
     sequence); an int runs gdr_chunk_fwd_segmented with segments of that many
-    chunks (0: the library chooses)."""
+    chunks (0: the library chooses).
+    guard: debugging aid, off by default. With guard > 0 (a multiple of 256)
+    the workspace, o and the final state are placed between `guard` canary
+    bytes on either side; after the call (which then synchronises) a changed
+    canary byte raises RuntimeError naming the buffer."""
     lib = load_library()
     prob, args, o, S_T, keep = _prepare(q, k, v, beta, g, scale, initial_state, cu_seqlens, cu_seqlens_cpu,
-                                        chunk_size, output_final_state, out_dtype, segment_chunks=segment_chunks)
+                                        chunk_size, output_final_state, out_dtype, segment_chunks=segment_chunks,
+                                        guard=guard)
     if segment_chunks is None:
         _check(lib.gdr_chunk_fwd(*args))
     else:
         _check(lib.gdr_chunk_fwd_segmented(*args, None))
+    if guard:
+        torch.cuda.synchronize(q.device)
+        _check_guards(keep[-1], guard)
     del keep
     return o, S_T
 

@@ -28,12 +28,22 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
          "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+# host-sanitizer build (tests/sanitize_cpu.py): the host code under AddressSanitizer
+# and UndefinedBehaviorSanitizer, the device code as in the normal build
+SAN_BUILD_DIR = os.path.join(HERE, "_build_san")
+SAN_FLAGS = ["-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    out_dir = SAN_BUILD_DIR if sanitize else BUILD_DIR
+    lib_path = os.path.join(out_dir, "libgdr.so")
+    os.makedirs(out_dir, exist_ok=True)
     objs, procs = [], []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(HERE, "csrc", src), "-o", obj]
+        obj = os.path.join(out_dir, src.replace(".hip", ".o"))
+        cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), *(SAN_FLAGS if sanitize else []),
+               "-c", os.path.join(HERE, "csrc", src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
@@ -48,16 +58,20 @@ def build(verbose: bool = False) -> str:
             print("\n".join(msgs))
     if failed:
         raise RuntimeError("hipcc failed:\n" + "\n".join("%s:\n%s" % f for f in failed))
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    subprocess.check_call([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
-    try:                                   # every symbol must resolve (a missing kernel stub shows here)
-        ctypes.CDLL(tmp, mode=os.RTLD_NOW)
-    except OSError as e:
-        os.unlink(tmp)
-        raise RuntimeError("built library does not load: %s" % e)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    tmp = lib_path + ".tmp%d" % os.getpid()
+    link = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
+    if sanitize:
+        link[4:4] = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"]
+    subprocess.check_call(link)
+    if not sanitize:                       # (the sanitizer build needs its runtime preloaded to load)
+        try:                               # every symbol must resolve (a missing kernel stub shows here)
+            ctypes.CDLL(tmp, mode=os.RTLD_NOW)
+        except OSError as e:
+            os.unlink(tmp)
+            raise RuntimeError("built library does not load: %s" % e)
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -18,24 +18,34 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "recurrence.c")
-_LIB = os.path.join(_HERE, "_build", "liboracle_recurrence.so")
+# GDR_ORACLE_LIBRARY names another build (the sanitizer build below)
+_LIB = os.environ.get("GDR_ORACLE_LIBRARY") or os.path.join(_HERE, "_build", "liboracle_recurrence.so")
+_SAN_LIB = os.path.join(_HERE, "_build_san", "liboracle_recurrence.so")
 _libs = {}
 
 
-def compile_source(src: str, out: str) -> str:
-    """Compile a recurrence source file into a shared library at ``out``."""
+def compile_source(src: str, out: str, sanitize: bool = False) -> str:
+    """Compile a recurrence source file into a shared library at ``out``; with
+    ``sanitize``, single-threaded under AddressSanitizer and
+    UndefinedBehaviorSanitizer with the compiler of libgdr.so's sanitizer
+    build (one sanitizer runtime serves both in a process)."""
     os.makedirs(os.path.dirname(out), exist_ok=True)
     tmp = out + ".tmp%d" % os.getpid()
-    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fopenmp", "-shared", "-fPIC",
-                           src, "-o", tmp, "-lm"])
+    if sanitize:
+        cmd = ["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-std=c99", "-fsanitize=address,undefined",
+               "-fno-omit-frame-pointer", "-shared", "-fPIC", src, "-o", tmp, "-lm"]
+    else:
+        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-shared", "-fPIC", src, "-o", tmp, "-lm"]
+    subprocess.check_call(cmd)
     os.replace(tmp, out)
     return out
 
 
-def build(force: bool = True) -> str:
-    if force or not os.path.exists(_LIB):
-        compile_source(_SRC, _LIB)
-    return _LIB
+def build(force: bool = True, sanitize: bool = False) -> str:
+    out = _SAN_LIB if sanitize else _LIB
+    if force or not os.path.exists(out):
+        compile_source(_SRC, out, sanitize)
+    return out
 
 
 def _load(path: Optional[str] = None):
