@@ -225,6 +225,7 @@ gdr::LaunchArgs fill_args(const gdr_problem_t* p, const Plan& pl, int64_t nt, co
     a.Q16 = pl.sz_K16 ? w + pl.off_Q16 : nullptr;
     a.reference = reference;
     a.prep_only = false;
+    a.states16 = false;
     a.nseg = 0;
     a.seg_chunks = 0;
     a.seg_first = a.seq_seg = nullptr;
@@ -545,7 +546,11 @@ gdr_status_t gdr_chunk_bwd(const gdr_problem_t* p, const void* q, const void* k,
     // the recompute needs the chunk states and V_new, not o
     b.fwd = fill_args(p, pl, nt, q, k, v, g, beta, scale, initial_state, cu_dev, nullptr, nullptr, w, true,
                       stream);
-    const int32_t per_seq = bwd_segments_per_seq(p);
+    // bf16 with C = 64 and enough (sequence, head, column tile) units to fill
+    // the GPU: the chunk states come from the fp16 chunk pass; otherwise from
+    // the five-kernel state pass, segment-parallel when there are few units
+    b.fwd.states16 = fused_path(p) && (int64_t)p->num_seqs * p->num_v_heads * (p->head_dim_v / 16) >= 128;
+    const int32_t per_seq = b.fwd.states16 ? 1 : bwd_segments_per_seq(p);
     if (per_seq > 1 && max_chunks > 1) {
         const int64_t C = p->chunk_size;
         const int64_t seg_chunks = (max_chunks + per_seq - 1) / per_seq;

@@ -41,6 +41,10 @@ namespace gdr {
 
 namespace {
 
+// offset of element (row r < 16, contraction index m < 32) inside a pair
+// fragment whose lane 16 qd + r holds m = 8 qd + e (natural order: the fp16
+// chunk pass writes its states so)
+__device__ __forceinline__ int pair_off_nat(int r, int m) { return (16 * (m >> 3) + r) * 8 + (m & 7); }
 // offset of element (row r < 16, contraction index m < 32) inside a pair fragment
 __device__ __forceinline__ int pair_off(int r, int m) {
     const int mm = m & 15;
@@ -386,6 +390,8 @@ __device__ __forceinline__ void gemm_lds_e(int K, float* As, float* Bs, const FA
 //   Y' = Q^T diag(scale exp(G)) dO - W^T X  [dk][dv]    (into the dS buffer)
 // so that the serial pass only forms Z = diag(exp(G_last - G)) K dS,
 // dV_new = X + Z and dS <- exp(G_last) dS + Y' - W^T Z.
+// h_nat: the entering states' fragments hold their contraction index in the
+// natural order (written so by the fp16 chunk pass), else in the pair order.
 template <typename T, int DK, int DV, int C>
 __global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ q, const T* __restrict__ k,
                                                    const float* __restrict__ G, const float* __restrict__ Hf,
@@ -395,7 +401,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ q, const
                                                    const int32_t* __restrict__ chunk_len, int32_t Nk, int32_t Nv,
                                                    float* __restrict__ Hn, float* __restrict__ Vn,
                                                    float* __restrict__ WT, float* __restrict__ P,
-                                                   float* __restrict__ X, float* __restrict__ Yp) {
+                                                   float* __restrict__ X, float* __restrict__ Yp, int h_nat) {
     constexpr int NKP = DK / 32, NNB = DV / 16, NTB = C / 16, NTP = C < 32 ? 1 : C / 32;
     constexpr int NMAX = (DK > DV ? DK : DV) > C ? (DK > DV ? DK : DV) : C;
     constexpr int KT = 32;                       // deeper tiles: this kernel's LDS has room
@@ -434,7 +440,8 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ q, const
     };
     batched(std::integral_constant<int, DK * DV>{},
             [&](int idx) { const int i = idx / DV, j = idx % DV;
-                           return Hf[((ch * NNB + j / 16) * NKP + i / 32) * 512 + pair_off(j % 16, i % 32)]; },
+                           return Hf[((ch * NNB + j / 16) * NKP + i / 32) * 512 +
+                                     (h_nat ? pair_off_nat(j % 16, i % 32) : pair_off(j % 16, i % 32))]; },
             [&](int idx, float x) { Hn[ch * DK * DV + idx] = x; });
     batched(std::integral_constant<int, C * DV>{},
             [&](int idx) { const int p = idx / DV, j = idx % DV;
@@ -966,7 +973,7 @@ hipError_t launch_bwd(const BackwardArgs& b) {
     auto mark = [&](int i) { if (b.events) (void)hipEventRecord(b.events[i], st); };
     mark(0);
     LaunchArgs f = a;
-    f.T16 = nullptr;                             // the fp16 path's T, score block and decay rows are not needed
+    if (!f.states16) f.T16 = nullptr;            // the fp16 path's T, score block and decay rows are not needed
     hipError_t e = launch_forward(f, nullptr);   // recompute: G, A, W, U, K^T, h, V_new
     if (e != hipSuccess) return e;
     mark(1);
@@ -974,7 +981,8 @@ hipError_t launch_bwd(const BackwardArgs& b) {
     if (NT > 0) {
         k_bwd_prep<T, DK, DV, C><<<dim3(NT, a.Nv), 256, 0, st>>>(
             (const T*)a.q, (const T*)a.k, a.G, (const float*)a.H, (const float*)a.VN, (const float*)a.W, b.d_o,
-            b.do_f32, a.scale, a.chunk_start, a.chunk_len, a.Nk, a.Nv, b.Hn, b.Vn, b.WT, b.P, b.dVn, b.dSout);
+            b.do_f32, a.scale, a.chunk_start, a.chunk_len, a.Nk, a.Nv, b.Hn, b.Vn, b.WT, b.P, b.dVn, b.dSout,
+            (int)a.states16);
     }
     mark(2);
     if (a.N > 0) {

@@ -418,16 +418,21 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
                                                  const int32_t* __restrict__ chunk_len,
                                                  const int32_t* __restrict__ first, int32_t Nk, int32_t Nv,
                                                  float scale, int out_f32, void* __restrict__ o,
-                                                 float* __restrict__ ST, float* __restrict__ ST2) {
+                                                 float* __restrict__ ST, float* __restrict__ ST2,
+                                                 float* __restrict__ Hout, float* __restrict__ VNout) {
     constexpr int C = 64;
     constexpr int NKP = DK / 32, NDB = DK / 16;
     constexpr bool want_o = MODE == kFull16;
+    constexpr bool want_h = MODE == kStates16;   // entering states and V_new out (fp32)
     __shared__ __attribute__((aligned(16))) f16 Ks[4][C * DK];
     __shared__ __attribute__((aligned(16))) bf16 Vs[4][C * 16];
     __shared__ __attribute__((aligned(16))) f16 Ts[4][kPairs * kFrag];  // T pairs of a chunk
     __shared__ __attribute__((aligned(16))) float Rs[4][256];           // decay rows (128 used)
     __shared__ __attribute__((aligned(16))) f16 Sx[2][NKP][kFrag];     // entering state, natural dk order
     __shared__ __attribute__((aligned(16))) f16 VNx[2][2][kFrag];      // V_new pairs (stacked positions)
+    // kStates16: the entering state's and V_new's fp32 accumulator tiles, lane-contiguous
+    __shared__ __attribute__((aligned(16))) float Hx[want_h ? 2 : 1][want_h ? NDB : 1][want_h ? 256 : 4];
+    __shared__ __attribute__((aligned(16))) float VNx32[want_h ? 2 : 1][want_h ? 4 : 1][want_h ? 256 : 4];
 
     // XCD-aware placement: each XCD takes a contiguous run of (unit, head,
     // column tile) triples, so the workgroups that read the same K and Q
@@ -448,7 +453,7 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, r = lane & 15, qd = lane >> 4;
     const int kh = h / (Nv / Nk);
-    const bool trans = MODE != kFull16 && bz >= DV / 16;   // transition workgroup
+    const bool trans = MODE == kSegment16 && bz >= DV / 16;   // transition workgroup
     const int nb = trans ? bz - DV / 16 : bz;
     const int NC = trans ? DK : DV;
     float* const STo = trans ? ST2 : ST;
@@ -568,6 +573,10 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
 #pragma unroll
                 for (int kp = 0; kp < NKP; ++kp) *reinterpret_cast<h8*>(&Sx[(c - c0) & 1][kp][lane * 8]) = Sp[kp];
             }
+            if constexpr (want_h) {
+#pragma unroll
+                for (int t = 0; t < NDB; ++t) *reinterpret_cast<f32x4*>(&Hx[(c - c0) & 1][t][lane * 4]) = S[t];
+            }
             f32x4 Y[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b) Y[b] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -628,6 +637,10 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
             if constexpr (want_o) {
                 *reinterpret_cast<h8*>(&VNx[(c - c0) & 1][0][lane * 8]) = pack_pair(VN[0], VN[1]);
                 *reinterpret_cast<h8*>(&VNx[(c - c0) & 1][1][lane * 8]) = pack_pair(VN[2], VN[3]);
+            }
+            if constexpr (want_h) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) *reinterpret_cast<f32x4*>(&VNx32[(c - c0) & 1][b][lane * 4]) = VN[b];
             }
             f32x4 VD[4];
 #pragma unroll
@@ -736,6 +749,27 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
 #pragma unroll
             for (int p = 0; p < 2; ++p) dst[p] = __builtin_bit_cast(h8, buf_load16(rp, (pbase + p) * kFrag * 2 + lane * 16));
         };
+        // kStates16: chunk cc's entering state (wavefronts 2, 3: state tiles of
+        // their half) and V_new (wavefront 1) from LDS to the fp32 pair
+        // fragments in global memory (stored only when cc is one of this
+        // sequence's chunks)
+        auto store_states = [&](int cc, auto parc) {
+            constexpr int PC = decltype(parc)::value;
+            if (cc < c0 || cc >= c1) return;
+            const int64_t unit = ((int64_t)cc * Nv + h) * (DV / 16) + nb;
+            if constexpr (ROLE == 1) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    *reinterpret_cast<f32x4*>(&VNout[(unit * 2 + (b >> 1)) * kFrag + lane * 8 + (b & 1) * 4]) =
+                        *reinterpret_cast<const f32x4*>(&VNx32[PC][b][lane * 4]);
+            } else {
+                constexpr int T0 = ROLE == 2 ? 0 : NDB / 2;
+#pragma unroll
+                for (int t = T0; t < T0 + NDB / 2; ++t)
+                    *reinterpret_cast<f32x4*>(&Hout[(unit * NKP + (t >> 1)) * kFrag + lane * 8 + (t & 1) * 4]) =
+                        *reinterpret_cast<const f32x4*>(&Hx[PC][t][lane * 4]);
+            }
+        };
         // O of chunk cc = scale [exp(G) (Q S_in) + P V_new], formed transposed
         // (stored only when cc is one of this sequence's chunks)
         auto finish = [&](int cc, auto parc) {
@@ -808,8 +842,10 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
                 load_q(c + 1, qraw[PAR ^ 1]);
                 load_eg(c + 1, egraw[PAR ^ 1]);
             }
+            if constexpr (want_h) store_states(c - 1, std::integral_constant<int, PAR ^ 1>{});
             // the copies of chunk c + 2 (issued in step c - 1) have landed
-            constexpr int after = want_o ? NBL + 2 + NBL * NKP + NBL : 0;   // operations per step after the copies
+            constexpr int after = want_o ? NBL + 2 + NBL * NKP + NBL
+                                         : (want_h ? (ROLE == 1 ? 4 : NDB / 2) : 0);   // operations per step after the copies
             if constexpr (NDMA > 0) wait_vmem_but<2 * after + NDMA>();
             lds_barrier();                                                        // end of step c
         };
@@ -825,6 +861,12 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
             if (c1 > c0) {
                 if ((c1 - 1 - c0) & 1) finish(c1 - 1, P1{});
                 else finish(c1 - 1, P0{});
+            }
+        }
+        if constexpr (want_h) {                             // the last chunk's states
+            if (c1 > c0) {
+                if ((c1 - 1 - c0) & 1) store_states(c1 - 1, P1{});
+                else store_states(c1 - 1, P0{});
             }
         }
         wait_vmem();
@@ -854,21 +896,47 @@ static hipError_t launch_dims(const LaunchArgs& a, hipEvent_t* ev) {
         if (a.nseg > 0) {
             k_chunk16<DK, DV, kSegment16><<<dim3(a.nseg, a.Nv, DV / 16 + DK / 16), 256, 0, st>>>(
                 q, k, v, R, Tf, Pf, (const f16*)a.K16, (const f16*)a.Q16, nullptr, a.chunk_start, a.chunk_len,
-                a.seg_first, a.Nk, a.Nv, a.scale, a.out_f32, nullptr, a.Sloc, a.Mseg);
+                a.seg_first, a.Nk, a.Nv, a.scale, a.out_f32, nullptr, a.Sloc, a.Mseg, nullptr, nullptr);
             const hipError_t e = launch_segment_scan(a);
             if (e != hipSuccess) return e;
             k_chunk16<DK, DV, kFull16><<<dim3(a.nseg, a.Nv, DV / 16), 256, 0, st>>>(
                 q, k, v, R, Tf, Pf, (const f16*)a.K16, (const f16*)a.Q16, a.Sstart, a.chunk_start, a.chunk_len,
-                a.seg_first, a.Nk, a.Nv, a.scale, a.out_f32, a.o, nullptr, nullptr);
+                a.seg_first, a.Nk, a.Nv, a.scale, a.out_f32, a.o, nullptr, nullptr, nullptr, nullptr);
         } else {
             k_chunk16<DK, DV, kFull16><<<dim3(a.N, a.Nv, DV / 16), 256, 0, st>>>(
                 q, k, v, R, Tf, Pf, (const f16*)a.K16, (const f16*)a.Q16, a.S0, a.chunk_start, a.chunk_len,
-                a.seq_first, a.Nk, a.Nv, a.scale, a.out_f32, a.o, a.ST, nullptr);
+                a.seq_first, a.Nk, a.Nv, a.scale, a.out_f32, a.o, a.ST, nullptr, nullptr, nullptr);
         }
     }
     mark(5);
     mark(6);
     return hipGetLastError();
+}
+
+template <int DK, int DV>
+static hipError_t launch_states_dims(const LaunchArgs& a) {
+    hipStream_t st = a.stream;
+    const int32_t NT = a.nt;
+    const bf16 *q = (const bf16*)a.q, *k = (const bf16*)a.k, *v = (const bf16*)a.v;
+    if (NT > 0)
+        k_prep<DK><<<dim3(NT, a.Nk), 256, 0, st>>>(k, q, a.beta, a.beta_f32, a.g, a.chunk_start, a.chunk_len, a.Nk,
+                                                     a.Nv, (f16*)a.T16, (f16*)a.P16, a.R16, (f16*)a.K16, (f16*)a.Q16);
+    if (a.N > 0)
+        k_chunk16<DK, DV, kStates16><<<dim3(a.N, a.Nv, DV / 16), 256, 0, st>>>(
+            q, k, v, a.R16, (const f16*)a.T16, (const f16*)a.P16, (const f16*)a.K16, (const f16*)a.Q16, a.S0,
+            a.chunk_start, a.chunk_len, a.seq_first, a.Nk, a.Nv, a.scale, 0, nullptr, nullptr, nullptr,
+            (float*)a.H, (float*)a.VN);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp16_states(const LaunchArgs& a) {
+#define GDR_CASE(DKv, DVv) \
+    if (a.dk == DKv && a.dv == DVv) return launch_states_dims<DKv, DVv>(a);
+    GDR_CASE(32, 32) GDR_CASE(32, 64) GDR_CASE(32, 128)
+    GDR_CASE(64, 32) GDR_CASE(64, 64) GDR_CASE(64, 128)
+    GDR_CASE(128, 32) GDR_CASE(128, 64) GDR_CASE(128, 128)
+#undef GDR_CASE
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_fp16_path(const LaunchArgs& a, hipEvent_t* ev) {

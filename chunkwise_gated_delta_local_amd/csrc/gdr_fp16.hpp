@@ -9,7 +9,9 @@ namespace gdr {
 
 // Modes of the fp16 chunk pass: state and output (serial pass, or the last
 // pass of segment-parallel state passing), or state only (segment passes).
-constexpr int kFull16 = 0, kSegment16 = 1;
+// kStates16: state only, for the backward's recompute: every chunk's entering
+// state and V_new are written (fp32) instead of the output.
+constexpr int kFull16 = 0, kSegment16 = 1, kStates16 = 2;
 
 // Enqueues stages 2..6 of the forward for bf16 inputs with C = 64 (the chunk
 // and segment tables are built by the caller): k_prep, then the chunk pass (or
@@ -17,6 +19,14 @@ constexpr int kFull16 = 0, kSegment16 = 1;
 // [2] .. [6] when `ev` is given. With a.prep_only set, only k_prep runs (the
 // debug entry point's copy of T, P and the decay rows).
 hipError_t launch_fp16_path(const LaunchArgs& a, hipEvent_t* ev);
+
+// The backward's recompute of the chunk states on this path (bf16, C = 64):
+// k_prep, then the chunk pass in kStates16 mode, writing into a.H the
+// chunk-entering states ([NT][Nv][dv/16][dk/32] fp32 pair fragments of H^T,
+// contraction index in natural order: lane 16 qd + r, element e holds dk row
+// 32 kp + 8 qd + e of column 16 nb + r) and into a.VN V_new ([NT][Nv][dv/16][2]
+// fp32 pair fragments of V_new^T, the five-kernel path's layout).
+hipError_t launch_fp16_states(const LaunchArgs& a);
 
 // Segment scan over the segments of every (sequence, value head, 16 columns)
 // (gdr_kernels.hip): S_start[j] and the final state from S0, M and S_loc.

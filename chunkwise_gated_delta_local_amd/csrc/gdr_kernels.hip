@@ -814,7 +814,7 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
     mark(1);
     if constexpr (kFp16) {
         if (!a.reference) return launch_fp16_path(a, ev);
-        if (a.T16) {
+        if (a.T16 && !a.states16) {
             LaunchArgs b = a;
             b.prep_only = true;
             b.nseg = 0;
@@ -837,7 +837,12 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
                                                        (const float*)a.A, a.chunk_start, a.chunk_len, a.Nk, a.Nv,
                                                        (float*)a.W, (float*)a.U, (T*)a.KT);
     mark(4);
-    if (segmented) {
+    if (kFp16 && a.states16) {
+        // backward recompute: H and V_new from the fp16 chunk pass (k_prep and
+        // the chunk pass in kStates16 mode); G, A and W above stay fp32
+        const hipError_t e = launch_fp16_states(a);
+        if (e != hipSuccess) return e;
+    } else if (segmented) {
         // local end states from zero, transitions from I with V = 0, the scan,
         // then the pass from the entering states that writes H and V_new
         const dim3 gs(a.nseg, a.Nv, DV / 16), gm(a.nseg, a.Nv, DK / 16);

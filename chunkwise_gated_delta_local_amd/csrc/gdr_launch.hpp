@@ -33,6 +33,8 @@ struct LaunchArgs {
     void* Q16;                       // Q rows, same layout (fp16 path)
     bool reference;                  // run the five separate kernels even for bf16
     bool prep_only;                  // fp16 path: run k_prep only (debug copies of T, P, R)
+    bool states16;                   // five-kernel run whose state pass is the fp16 chunk pass
+                                     // (backward recompute, bf16 with C = 64): H and VN from it
     // segment-parallel state passing (nseg == 0: one serial pass per sequence)
     int32_t nseg;                    // segment-table capacity: the host's count of segments
     int32_t seg_chunks;              // chunks per segment

@@ -10,7 +10,11 @@ pages' own tests use 0.006-0.008 on a ratio of rms errors, FLA DeltaNet
 article, section 6). Cases: fixed length and variable length (empty,
 one-token, one-chunk and ragged sequences), GQA, chunk sizes 16, 32 and 64,
 the ungated rule (dg is then the gradient at g = 0), a strongly decaying gate,
-every head-dim pair, with and without dL/dS_T, and d_o in fp32.
+every head-dim pair, with and without dL/dS_T, and d_o in fp32. For bf16
+inputs at C = 64 with at least 128 (sequence, value head, 16 dv columns)
+units, the recompute takes its chunk states from the fp16 chunk pass (cases
+bf16_states16_*, the determinism and full-size tests); otherwise from the
+five-kernel state pass.
 """
 import numpy as np
 import pytest
@@ -73,6 +77,11 @@ CASES = {
                             lengths=(1, 63, 64, 65, 130, 0)),
     "bf16_T200_d128": dict(B=1, T=200, Nk=1, Nv=1, dk=128, dv=128, dtype="bf16", s0="zero"),
     "bf16_strong_decay": dict(B=1, T=130, Nk=1, Nv=2, dk=64, dv=32, dtype="bf16", g_mean=-2.0, s0="randn"),
+    # at least 128 (sequence, value head, 16 dv columns) units: the recompute's
+    # chunk states come from the fp16 chunk pass
+    "bf16_states16_varlen": dict(B=1, T=0, Nk=2, Nv=8, dk=64, dv=128, dtype="bf16", s0="randn",
+                                 lengths=(200, 1, 65, 130)),
+    "bf16_states16_B2_d128": dict(B=2, T=150, Nk=4, Nv=8, dk=128, dv=128, dtype="bf16", s0="randn"),
 }
 
 
