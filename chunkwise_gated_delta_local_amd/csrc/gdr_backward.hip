@@ -110,6 +110,22 @@ struct GMat {
         if (es == 4) return __uint_as_float(raw);
         return __uint_as_float(((row * rstride + col) & 1) ? (raw & 0xffff0000u) : (raw << 16));
     }
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    // four elements adjacent in memory from (row, col) (the caller knows they
+    // are), one load: their raw words (fp32), or two words of bf16 pairs
+    __device__ __forceinline__ u32x4 load4(int row, int col, bool ok) const {
+        const int esz = ES ? ES : es;
+        const int off = ok ? (row * rstride + col) * esz : 0x7ffffff0;
+        if (esz == 4) return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
+        return u32x4{w[0], w[1], 0u, 0u};
+    }
+    __device__ __forceinline__ f32x4 conv4(u32x4 raw) const {
+        if ((ES ? ES : es) == 4) return __builtin_bit_cast(f32x4, raw);
+        return f32x4{__uint_as_float(raw[0] << 16), __uint_as_float(raw[0] & 0xffff0000u),
+                     __uint_as_float(raw[1] << 16), __uint_as_float(raw[1] & 0xffff0000u)};
+    }
 };
 template <typename T>
 constexpr int es_of() { return (int)sizeof(T); }
@@ -128,6 +144,30 @@ struct GOp {
     }
     __device__ __forceinline__ float value(uint32_t raw, int row, int k0, int kk) const {
         return fin(row, k0 + kk, TR ? m.conv(raw, k0 + kk, row) : m.conv(raw, row, k0 + kk));
+    }
+    // a group of four: (row, k0 + kk + u) when KC, else (row + u, k0 + kk);
+    // one vector load when the four are adjacent in memory (KC != TR)
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    template <bool KC>
+    __device__ __forceinline__ u32x4 load4(int row, int k0, int kk, bool ok) const {
+        if constexpr (KC != TR) return TR ? m.load4(k0 + kk, row, ok) : m.load4(row, k0 + kk, ok);
+        u32x4 r;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r[u] = KC ? load(row, k0, kk + u, ok) : load(row + u, k0, kk, ok);
+        return r;
+    }
+    template <bool KC>
+    __device__ __forceinline__ f32x4 value4(u32x4 raw, int row, int k0, int kk) const {
+        f32x4 v;
+        if constexpr (KC != TR) {
+            const f32x4 x = m.conv4(raw);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = KC ? fin(row, k0 + kk + u, x[u]) : fin(row + u, k0 + kk, x[u]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = KC ? value(raw[u], row, k0, kk + u) : value(raw[u], row + u, k0, kk);
+        }
+        return v;
     }
 };
 struct Ident {
@@ -154,6 +194,17 @@ struct GCat {
         if (k0 < kc) return x0.value(raw, row, k0, kk);
         return x1.value(raw, row, k0 - kc, kk);
     }
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    template <bool KC>
+    __device__ __forceinline__ u32x4 load4(int row, int k0, int kk, bool ok) const {
+        if (k0 < kc) return x0.template load4<KC>(row, k0, kk, ok);
+        return x1.template load4<KC>(row, k0 - kc, kk, ok);
+    }
+    template <bool KC>
+    __device__ __forceinline__ f32x4 value4(u32x4 raw, int row, int k0, int kk) const {
+        if (k0 < kc) return x0.template value4<KC>(raw, row, k0, kk);
+        return x1.template value4<KC>(raw, row, k0 - kc, kk);
+    }
 };
 template <typename X0, typename X1>
 __device__ __forceinline__ GCat<X0, X1> gcat(const X0& x0, const X1& x1, int kc) {
@@ -166,6 +217,14 @@ struct LOp {
     F f;
     __device__ __forceinline__ uint32_t load(int, int, int, bool) const { return 0u; }
     __device__ __forceinline__ float value(uint32_t, int row, int k0, int kk) const { return f(row, k0 + kk); }
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    template <bool KC>
+    __device__ __forceinline__ f32x4 value4(u32x4, int row, int k0, int kk) const {
+        f32x4 v;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = KC ? f(row, k0 + kk + u) : f(row + u, k0 + kk);
+        return v;
+    }
 };
 template <typename F>
 __device__ __forceinline__ LOp<F> lop(F f) { return LOp<F>{f}; }
@@ -192,8 +251,7 @@ struct StageOp {
             for (int e = 0; e < NE; ++e) {
                 int row, k;
                 const bool ok = coords(e, row, k);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) r[e][u] = KC ? x.load(row, k0, k + u, ok) : x.load(row + u, k0, k, ok);
+                r[e] = x.template load4<KC>(row, k0, k, ok);
             }
         }
     }
@@ -203,10 +261,7 @@ struct StageOp {
         for (int e = 0; e < NE; ++e) {
             int row, k;
             if (coords(e, row, k)) {
-                f32x4 v;
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    v[u] = KC ? x.value(r[e][u], row, k0, k + u) : x.value(r[e][u], row + u, k0, k);
+                const f32x4 v = x.template value4<KC>(r[e], row, k0, k);
                 if (KC) {
 #pragma unroll
                     for (int u = 0; u < 4; ++u) S[off(row, k + u)] = v[u];
