@@ -41,10 +41,6 @@ namespace gdr {
 
 namespace {
 
-// offset of element (row r < 16, contraction index m < 32) inside a pair
-// fragment whose lane 16 qd + r holds m = 8 qd + e (natural order: the fp16
-// chunk pass writes its states so)
-__device__ __forceinline__ int pair_off_nat(int r, int m) { return (16 * (m >> 3) + r) * 8 + (m & 7); }
 // offset of element (row r < 16, contraction index m < 32) inside a pair fragment
 __device__ __forceinline__ int pair_off(int r, int m) {
     const int mm = m & 15;
@@ -437,16 +433,17 @@ __device__ __forceinline__ void gemm_lds_e(int K, float* As, float* Bs, const FA
 
 // ------------------------------------------------------------ preparation
 // One workgroup per (chunk, value head): the forward intermediates in plain
-// row-major layouts (the chunk's entering state h [dk][dv], V_new by token
+// row-major layouts (the chunk's entering state transposed, h^T [dv][dk], V_new by token
 // row, W^T [dk][C] per chunk), the score block P = (Q K^T) (.) D [C][C] (zero above the
 // diagonal and past the chunk end), and the two parts of the reverse state
 // pass that do not depend on the state gradient:
 //   X  = scale P^T dO                                   (into the dV_new buffer)
-//   Y' = Q^T diag(scale exp(G)) dO - W^T X  [dk][dv]    (into the dS buffer)
+//   Y' = Q^T diag(scale exp(G)) dO - W^T X  (into the dS buffer, as Y'^T [dv][dk])
 // so that the serial pass only forms Z = diag(exp(G_last - G)) K dS,
 // dV_new = X + Z and dS <- exp(G_last) dS + Y' - W^T Z.
-// h_nat: the entering states' fragments hold their contraction index in the
-// natural order (written so by the fp16 chunk pass), else in the pair order.
+// h_done: the entering states are already in Hn (written there as H^T by the
+// fp16 chunk pass); otherwise Hn is formed here from the five-kernel path's
+// fragments.
 template <typename T, int DK, int DV, int C>
 __global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ q, const T* __restrict__ k,
                                                    const float* __restrict__ G, const float* __restrict__ Hf,
@@ -456,7 +453,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ q, const
                                                    const int32_t* __restrict__ chunk_len, int32_t Nk, int32_t Nv,
                                                    float* __restrict__ Hn, float* __restrict__ Vn,
                                                    float* __restrict__ WT, float* __restrict__ P,
-                                                   float* __restrict__ X, float* __restrict__ Yp, int h_nat) {
+                                                   float* __restrict__ X, float* __restrict__ Yp, int h_done) {
     constexpr int NKP = DK / 32, NNB = DV / 16, NTB = C / 16, NTP = C < 32 ? 1 : C / 32;
     constexpr int NMAX = (DK > DV ? DK : DV) > C ? (DK > DV ? DK : DV) : C;
     constexpr int KT = 32;                       // deeper tiles: this kernel's LDS has room
@@ -493,11 +490,11 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ q, const
             }
         }
     };
-    batched(std::integral_constant<int, DK * DV>{},
-            [&](int idx) { const int i = idx / DV, j = idx % DV;
-                           return Hf[((ch * NNB + j / 16) * NKP + i / 32) * 512 +
-                                     (h_nat ? pair_off_nat(j % 16, i % 32) : pair_off(j % 16, i % 32))]; },
-            [&](int idx, float x) { Hn[ch * DK * DV + idx] = x; });
+    if (!h_done)                               // H^T [dv][dk] from the fragments
+        batched(std::integral_constant<int, DK * DV>{},
+                [&](int idx) { const int j = idx / DK, i = idx % DK;
+                               return Hf[((ch * NNB + j / 16) * NKP + i / 32) * 512 + pair_off(j % 16, i % 32)]; },
+                [&](int idx, float x) { Hn[ch * DK * DV + idx] = x; });
     batched(std::integral_constant<int, C * DV>{},
             [&](int idx) { const int p = idx / DV, j = idx % DV;
                            return VNf[((ch * NNB + j / 16) * NTP + p / 32) * 512 + pair_off(j % 16, p % 32)]; },
@@ -531,7 +528,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ q, const
     gemm_lds<DK, DV, false, true, (C % 32 == 0 ? KT : 16)>(2 * C, As, Bs,
         gcat(gop<true>(Qm), gop<false>(WTm, [](int, int, float x) { return -x; }), C),
         gcat(gop<true>(dOm, [&](int, int t, float x) { return se[t] * x; }), gop<true>(Xm), C),
-        [&](int m, int j, float x) { Yp[(ch * DK + m) * DV + j] = x; });
+        [&](int m, int j, float x) { Yp[(ch * DV + j) * DK + m] = x; });
 }
 
 // ------------------------------------------------------------ reverse state pass
@@ -619,12 +616,13 @@ __global__ __launch_bounds__(256) void k_bwd_state(const T* __restrict__ k, cons
             const int i = 16 * w + 4 * qd + v;    // rows past the end (or past C) read as zero
             xr[v] = buf_ld_f32(rx, (i * Nv * DV + r) * 4);
         }
-        const auto ry = buf_rsrc(dSY + ((int64_t)c * Nv + h) * DK * DV + nb * 16, (uint32_t)((DK - 1) * DV + 16) * 4);
+        // Y' (and later dS) of the chunk as dS^T [dv][dk]: rows 16 m + 4 qd .. + 3 of
+        // column 16 nb + r are 16 contiguous bytes
+        const auto ry = buf_rsrc(dSY + (((int64_t)c * Nv + h) * DV + nb * 16) * DK, 16 * DK * 4);
 #pragma unroll
         for (int i = 0; i < NBW; ++i) {
             const int m = w + 4 * i;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) yr[i][v] = buf_ld_f32(ry, ((16 * m + 4 * qd + v) * DV + r) * 4);
+            yr[i] = buf_ld_f32x4(ry, m < NB ? (r * DK + 16 * m + 4 * qd) * 4 : 0x7ffffff0);
         }
         const auto rg = buf_rsrc(G + s * Nv + h, L > 0 ? (uint32_t)(((L - 1) * Nv + 1) * 4) : 0u);
         gr = buf_ld_f32(rg, tid * Nv * 4);
@@ -732,9 +730,7 @@ __global__ __launch_bounds__(256) void k_bwd_state(const T* __restrict__ k, cons
                         au[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], b[u], au[u & 1], 0, 0, 0);
                 }
                 const f32x4 acc = au[0] + au[1];
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    dSY[(((int64_t)c * Nv + h) * DK + 16 * m + 4 * qd + v) * DV + nb * 16 + r] = dS[i][v];
+                *reinterpret_cast<f32x4*>(&dSY[(((int64_t)c * Nv + h) * DV + nb * 16 + r) * DK + 16 * m + 4 * qd]) = dS[i];
                 dS[i] = eL * dS[i] + y[i] - acc;
             }
         }
@@ -790,8 +786,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(const T* __restrict__ q, c
     const int L = chunk_len[c];
     if (L <= 0) return;
     const int64_t ch = (int64_t)c * Nv + h;
-    const float* Hc = Hn + ch * DK * DV;          // entering state [dk][dv]
-    const float* dSc = dSout + ch * DK * DV;      // gradient of the outgoing state [dk][dv]
+    const float* Hc = Hn + ch * DK * DV;          // entering state, transposed: [dv][dk]
+    const float* dSc = dSout + ch * DK * DV;      // gradient of the outgoing state, transposed: [dv][dk]
     const float* Pc = P + ch * C * C;
 
     auto row_dk = [&](int i) { return ((s + i) * Nv + h) * DK; };
@@ -806,8 +802,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(const T* __restrict__ q, c
     const auto Vnm = GMat<4>::make(Vn + (s * Nv + h) * DV, (int64_t)Nv * DV, L, DV);
     const auto dVnm = GMat<4>::make(dVn + (s * Nv + h) * DV, (int64_t)Nv * DV, L, DV);
     const auto dWm = GMat<4>::make(dW + (s * Nv + h) * DK, (int64_t)Nv * DK, L, DK);
-    const auto Hm = GMat<4>::make(Hc, DV, DK, DV);
-    const auto dSm = GMat<4>::make(dSc, DV, DK, DV);
+    const auto Hm = GMat<4>::make(Hc, DK, DV, DK);      // Hm(j, m) = h[m][j]
+    const auto dSm = GMat<4>::make(dSc, DK, DV, DK);
     const auto dqvm = GMat<4>::make(dqv + (s * Nv + h) * DK, (int64_t)Nv * DK, L, DK);
     const auto dkvm = GMat<4>::make(dkv + (s * Nv + h) * DK, (int64_t)Nv * DK, L, DK);
 
@@ -851,8 +847,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(const T* __restrict__ q, c
             Xm[i * C + j] = dp * p;
         }, nullptr);
     // dQ = scale diag(exp(G)) dO h^T + dM K (the same thread owns each element in both products)
-    gemm_lds<C, DK, true, false>(DV, As, Bs, gop<false>(dOm, [&](int i, int, float x) { return scale * eg[i] * x; }),
-                                 gop<false>(Hm),
+    gemm_lds<C, DK, true, true>(DV, As, Bs, gop<false>(dOm, [&](int i, int, float x) { return scale * eg[i] * x; }),
+                                gop<true>(Hm),
                                  [&](int i, int m, float x) { if (i < L) dqv[row_dk(i) + m] = x; });
     {   // row and column sums of E, 256 / C threads per position, in a fixed order
         constexpr int TPR = 256 / C;
@@ -874,7 +870,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(const T* __restrict__ q, c
                                            [&](int i, int m, float x, float old) { if (i < L) dqv[row_dk(i) + m] = old + x; },
                                            nullptr);
     // dW = -dV_new h^T
-    gemm_lds<C, DK, true, false>(DV, As, Bs, gop<false>(dVnm), gop<false>(Hm),
+    gemm_lds<C, DK, true, true>(DV, As, Bs, gop<false>(dVnm), gop<true>(Hm),
                                  [&](int i, int m, float x) { if (i < L) dW[row_dk(i) + m] = -x; });
     // dV = diag(beta) A^T dU (dU = dV_new); dbeta += v . (A^T dU)  (row sums in dAm, free until dA)
     float* const red1 = dAm;
@@ -946,7 +942,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(const T* __restrict__ q, c
     // in Xm, free after the dK product above)
     float* const red3 = Xm;
     float* const red4 = Xm + 4 * C;
-    gemm_lds_e<C, DK, true, false, kStageK>(DV, As, Bs, gop<false>(Vnm), gop<false>(dSm), ep_pair(gop<false>(dkvm), gop<false>(Km)),
+    gemm_lds_e<C, DK, true, true, kStageK>(DV, As, Bs, gop<false>(Vnm), gop<true>(dSm), ep_pair(gop<false>(dkvm), gop<false>(Km)),
         [&](int i, int m, float x, float2 e) {
             if (i >= L) return 0.f;
             const float y = elg[i] * x;
@@ -954,7 +950,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(const T* __restrict__ q, c
             return e.y * y;
         }, red3);
     // dG through exp(G) in the inter-chunk output: dG_i += dO_i . (scale exp(G_i) h^T q_i)
-    gemm_lds_e<C, DV, true, true, kStageK>(DK, As, Bs, gop<false>(Qm), gop<true>(Hm), gop<false>(dOm),
+    gemm_lds_e<C, DV, true, false, kStageK>(DK, As, Bs, gop<false>(Qm), gop<false>(Hm), gop<false>(dOm),
         [&](int i, int j, float x, float d) { return i < L ? scale * eg[i] * d * x : 0.f; }, red4);
     // exp(G_last) h in the state update: sum(dS (.) h), per wave then over the waves
     {
@@ -1029,6 +1025,7 @@ hipError_t launch_bwd(const BackwardArgs& b) {
     mark(0);
     LaunchArgs f = a;
     if (!f.states16) f.T16 = nullptr;            // the fp16 path's T, score block and decay rows are not needed
+    else f.H = b.Hn;                             // the fp16 chunk pass writes the states as H^T directly
     hipError_t e = launch_forward(f, nullptr);   // recompute: G, A, W, U, K^T, h, V_new
     if (e != hipSuccess) return e;
     mark(1);

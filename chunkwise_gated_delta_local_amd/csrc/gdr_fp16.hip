@@ -750,9 +750,9 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
             for (int p = 0; p < 2; ++p) dst[p] = __builtin_bit_cast(h8, buf_load16(rp, (pbase + p) * kFrag * 2 + lane * 16));
         };
         // kStates16: chunk cc's entering state (wavefronts 2, 3: state tiles of
-        // their half) and V_new (wavefront 1) from LDS to the fp32 pair
-        // fragments in global memory (stored only when cc is one of this
-        // sequence's chunks)
+        // their half) as H^T [dv][dk] per chunk and head, and V_new (wavefront 1)
+        // as fp32 pair fragments, from LDS to global memory (stored only when cc
+        // is one of this sequence's chunks)
         auto store_states = [&](int cc, auto parc) {
             constexpr int PC = decltype(parc)::value;
             if (cc < c0 || cc >= c1) return;
@@ -764,9 +764,11 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
                         *reinterpret_cast<const f32x4*>(&VNx32[PC][b][lane * 4]);
             } else {
                 constexpr int T0 = ROLE == 2 ? 0 : NDB / 2;
+                // tile t holds dk rows 32 (t / 2) + 8 qd + 4 (t % 2) + j, j = 0..3, of column 16 nb + r
+                float* hc = Hout + (((int64_t)cc * Nv + h) * DV + nb * 16 + r) * DK + 8 * qd;
 #pragma unroll
                 for (int t = T0; t < T0 + NDB / 2; ++t)
-                    *reinterpret_cast<f32x4*>(&Hout[(unit * NKP + (t >> 1)) * kFrag + lane * 8 + (t & 1) * 4]) =
+                    *reinterpret_cast<f32x4*>(&hc[32 * (t >> 1) + 4 * (t & 1)]) =
                         *reinterpret_cast<const f32x4*>(&Hx[PC][t][lane * 4]);
             }
         };

@@ -22,10 +22,9 @@ hipError_t launch_fp16_path(const LaunchArgs& a, hipEvent_t* ev);
 
 // The backward's recompute of the chunk states on this path (bf16, C = 64):
 // k_prep, then the chunk pass in kStates16 mode, writing into a.H the
-// chunk-entering states ([NT][Nv][dv/16][dk/32] fp32 pair fragments of H^T,
-// contraction index in natural order: lane 16 qd + r, element e holds dk row
-// 32 kp + 8 qd + e of column 16 nb + r) and into a.VN V_new ([NT][Nv][dv/16][2]
-// fp32 pair fragments of V_new^T, the five-kernel path's layout).
+// chunk-entering states transposed ([NT][Nv][dv][dk] fp32) and into a.VN
+// V_new ([NT][Nv][dv/16][2] fp32 pair fragments of V_new^T, the five-kernel
+// path's layout).
 hipError_t launch_fp16_states(const LaunchArgs& a);
 
 // Segment scan over the segments of every (sequence, value head, 16 columns)

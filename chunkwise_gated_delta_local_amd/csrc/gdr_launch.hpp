@@ -63,11 +63,11 @@ struct BackwardArgs {
     float* dS0;                // [N][Nv][dk][dv] or NULL
     // workspace (fp32, natural row-major layouts)
     float *P;                  // [NT][Nv][C][C] score block (Q K^T) (.) D
-    float *Hn;                 // [NT][Nv][dk][dv] entering states
+    float *Hn;                 // [NT][Nv][dv][dk] entering states, transposed
     float *Vn, *dVn;           // [Ttot][Nv][dv] V_new and its gradient
     float *WT;                 // [NT][Nv][dk][C] W^T per chunk (zero past the chunk end)
     float *dWs;                // [Ttot][Nv][dk] the gradient of W
-    float *dSout;              // [NT][Nv][dk][dv] gradients of the outgoing states
+    float *dSout;              // [NT][Nv][dv][dk] gradients of the outgoing states, transposed
     float *dqv, *dkv;          // [Ttot][Nv][dk] dq, dk per value head
     hipEvent_t* events;        // NULL, or 6 events: before the forward recompute and after
                                // it, the preparation, the state pass, the per-chunk pass, the sum
