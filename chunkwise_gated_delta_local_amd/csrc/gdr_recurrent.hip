@@ -15,15 +15,17 @@
 // 1e-6) inside the kernel (FLA DeltaNet article, section 5, the in-kernel L2
 // normalisation option).
 //
-// Mapping: one wavefront per (sequence, value head, 256 / RQ columns of dv),
-// RQ = dk / 16. Lane l = RQ cg + rq owns columns 4 cg .. 4 cg + 3 of the state
-// slice over rows 16 rq .. 16 rq + 15: 64 state values in registers, so that
-// four wavefronts fit on a SIMD. S^T k and S^T q are sums over the lane's rows
-// followed by a butterfly over the RQ lanes of a group. Each lane reads its 16
-// elements of q_t and k_t straight from global memory (the lanes of one row
-// range read the same bytes); beta and g are wave-uniform scalar loads. The
-// state moves in and out with 16-byte non-temporal accesses (it is read and
-// written once), four columns of one row per access. The arithmetic is fp32 throughout; o is rounded once, at the store.
+// Mapping: one workgroup per (sequence, value head), one wavefront per 256 / RQ
+// columns of dv (RQ = dk / 16; at most four wavefronts). Lane l = RQ cg + rq
+// owns columns 4 cg .. 4 cg + 3 of its wavefront's column block over rows
+// 16 rq .. 16 rq + 15: 64 state values in registers, so that four wavefronts
+// fit on a SIMD. S^T k and S^T q are sums over the lane's rows followed by a
+// butterfly over the RQ lanes of a group. Each lane reads its 16 elements of
+// q_t and k_t straight from global memory (the lanes of one row range read the
+// same bytes); beta and g are wave-uniform scalar loads. The state moves in
+// and out with 16-byte non-temporal accesses (it is read and written once),
+// four columns of one row per access. The arithmetic is fp32 throughout; o is
+// rounded once, at the store.
 #include "gdr_device.hpp"
 #include "gdr_launch.hpp"
 
@@ -66,7 +68,7 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 
 template <typename T, int DK>
-__global__ __launch_bounds__(64) void k_recurrent(const T* __restrict__ q, const T* __restrict__ k,
+__global__ __launch_bounds__(256, 4) void k_recurrent(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, const void* __restrict__ beta,
                                                    int beta_f32, const float* __restrict__ g,
                                                    const float* __restrict__ S0, const int32_t* __restrict__ cu,
@@ -78,8 +80,8 @@ __global__ __launch_bounds__(64) void k_recurrent(const T* __restrict__ q, const
     constexpr int COLS = 4 * 64 / RQ;            // state columns per wavefront
     static_assert(DK % RPL == 0 && RQ >= 2 && RQ <= 8, "dk");
     const int n = blockIdx.x, h = blockIdx.y;
-    const int lane = threadIdx.x, rq = lane % RQ, cg = lane / RQ;
-    const int j0 = blockIdx.z * COLS + 4 * cg;   // this lane's first state column
+    const int lane = threadIdx.x & 63, rq = lane % RQ, cg = lane / RQ;
+    const int j0 = (threadIdx.x >> 6) * COLS + 4 * cg;   // this lane's first state column (wavefront = column block)
     const bool active = j0 < DV;                 // DV is a multiple of 32: all four columns or none
     const int r0 = rq * RPL;                     // this lane's first state row
     const int kh = h / (Nv / Nk);
@@ -153,10 +155,11 @@ __global__ __launch_bounds__(64) void k_recurrent(const T* __restrict__ q, const
 template <typename T>
 hipError_t dispatch(const RecurrentArgs& a) {
     const int cols = 4 * 64 * kRowsPerLane / a.dk;     // state columns per wavefront
-    const dim3 grid(a.N, a.Nv, (a.dv + cols - 1) / cols);
+    const dim3 grid(a.N, a.Nv);
+    const int threads = 64 * ((a.dv + cols - 1) / cols);   // one wavefront per column block (at most 4)
 #define GDR_REC(DKv)                                                                                              \
     if (a.dk == DKv) {                                                                                            \
-        k_recurrent<T, DKv><<<grid, 64, 0, a.stream>>>((const T*)a.q, (const T*)a.k, (const T*)a.v, a.beta,      \
+        k_recurrent<T, DKv><<<grid, threads, 0, a.stream>>>((const T*)a.q, (const T*)a.k, (const T*)a.v, a.beta,      \
                                                        a.beta_f32, a.g, a.S0, a.cu_dev, a.T_row, a.Ttot, a.Nk,   \
                                                        a.Nv, a.dv, a.scale, a.l2norm, a.out_f32, a.o, a.ST);      \
         return hipGetLastError();                                                                                 \
