@@ -138,7 +138,9 @@ __device__ __forceinline__ int tile_swz(int row) {
 //         FLA DeltaNet article, section 3.2).
 //      d. T = A diag(beta) and P_ij = (q_i . k_j) exp(G_i - G_j) (j <= i < L)
 //         rounded to fp16 pair fragments of the six lower blocks.
-template <int DK>
+// WITH_P false (the backward's recompute of the chunk states, which forms no
+// output): no Q rows, Q tiles or score block.
+template <int DK, bool WITH_P>
 __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, const bf16* __restrict__ q,
                                                   const void* __restrict__ beta, int beta_f32,
                                                   const float* __restrict__ g,
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
             qv[i] = zero_pair<bf16>();
             if (row < L) {
                 kv[i] = *reinterpret_cast<const v8*>(k + ((s + row) * Nk + kh) * DK + seg * 8);
-                qv[i] = *reinterpret_cast<const v8*>(q + ((s + row) * Nk + kh) * DK + seg * 8);
+                if constexpr (WITH_P) qv[i] = *reinterpret_cast<const v8*>(q + ((s + row) * Nk + kh) * DK + seg * 8);
             }
         }
         if (wave == 0) fetch_gates(0);
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
             // down to fp16's subnormal range)
             const int u = (seg ^ tile_swz<DK>(row)) * 8;
             *reinterpret_cast<h8*>(&kt16[row * DK + u]) = bf16x8_to_f16(__builtin_bit_cast(u4, kv[i]));
-            *reinterpret_cast<h8*>(&qt16[row * DK + u]) = bf16x8_to_f16(__builtin_bit_cast(u4, qv[i]));
+            if constexpr (WITH_P) *reinterpret_cast<h8*>(&qt16[row * DK + u]) = bf16x8_to_f16(__builtin_bit_cast(u4, qv[i]));
         }
     }
     __syncthreads();
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
                 const v8 kj = load_pair_row<bf16>(&Ks[(j * 16 + r) * KP + kp * 32], qd);
                 const v8 qw = load_pair_row<bf16>(&Qs[(wave * 16 + r) * KP + kp * 32], qd);
                 kk[j] = mfma_pair(kw, kj, kk[j]);
-                qk[j] = mfma_pair(kj, qw, qk[j]);
+                if constexpr (WITH_P) qk[j] = mfma_pair(kj, qw, qk[j]);
             }
         }
     }
@@ -351,25 +353,27 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
             }
             *reinterpret_cast<h8*>(Tf + (((int64_t)c * Nv + h) * kPairs + p) * kFrag + lane * 8) = pack_pair(x0, x1);
         }
-        //     P pairs of block row `wave` (rows i = 16 wave + r): the transposed
-        //     tiles qk[j] are, stacked two at a time, the pair fragments of P
-        {
-            const int i = wave * 16 + r;
-            f32x4 pt[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int col = j * 16 + 4 * qd + jj;
-                    pt[j][jj] = (j <= wave && col <= i && i < L) ? qk[j][jj] * __expf(gs[i] - gs[col]) : 0.f;
+        if constexpr (WITH_P) {
+            //     P pairs of block row `wave` (rows i = 16 wave + r): the transposed
+            //     tiles qk[j] are, stacked two at a time, the pair fragments of P
+            {
+                const int i = wave * 16 + r;
+                f32x4 pt[4];
+    #pragma unroll
+                for (int j = 0; j < 4; ++j) {
+    #pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int col = j * 16 + 4 * qd + jj;
+                        pt[j][jj] = (j <= wave && col <= i && i < L) ? qk[j][jj] * __expf(gs[i] - gs[col]) : 0.f;
+                    }
                 }
-            }
-            const int pbase = (wave == 0) ? 0 : (wave == 1 ? 1 : (wave == 2 ? 2 : 4));
-#pragma unroll
-            for (int tp = 0; tp < 2; ++tp) {
-                if (2 * tp <= wave)
-                    *reinterpret_cast<h8*>(Pf + (((int64_t)c * Nv + h) * kPairs + pbase + tp) * kFrag + lane * 8) =
-                        pack_pair(pt[2 * tp], pt[2 * tp + 1]);
+                const int pbase = (wave == 0) ? 0 : (wave == 1 ? 1 : (wave == 2 ? 2 : 4));
+    #pragma unroll
+                for (int tp = 0; tp < 2; ++tp) {
+                    if (2 * tp <= wave)
+                        *reinterpret_cast<h8*>(Pf + (((int64_t)c * Nv + h) * kPairs + pbase + tp) * kFrag + lane * 8) =
+                            pack_pair(pt[2 * tp], pt[2 * tp + 1]);
+                }
             }
         }
         __syncthreads();
@@ -890,8 +894,8 @@ static hipError_t launch_dims(const LaunchArgs& a, hipEvent_t* ev) {
     float* R = a.R16;
     mark(2);
     if (NT > 0)
-        k_prep<DK><<<dim3(NT, a.Nk), 256, 0, st>>>(k, q, a.beta, a.beta_f32, a.g, a.chunk_start, a.chunk_len, a.Nk,
-                                                     a.Nv, Tf, Pf, R, (f16*)a.K16, (f16*)a.Q16);
+        k_prep<DK, true><<<dim3(NT, a.Nk), 256, 0, st>>>(k, q, a.beta, a.beta_f32, a.g, a.chunk_start, a.chunk_len,
+                                                           a.Nk, a.Nv, Tf, Pf, R, (f16*)a.K16, (f16*)a.Q16);
     mark(3);
     mark(4);
     if (a.N > 0 && !a.prep_only) {
@@ -921,8 +925,9 @@ static hipError_t launch_states_dims(const LaunchArgs& a) {
     const int32_t NT = a.nt;
     const bf16 *q = (const bf16*)a.q, *k = (const bf16*)a.k, *v = (const bf16*)a.v;
     if (NT > 0)
-        k_prep<DK><<<dim3(NT, a.Nk), 256, 0, st>>>(k, q, a.beta, a.beta_f32, a.g, a.chunk_start, a.chunk_len, a.Nk,
-                                                     a.Nv, (f16*)a.T16, (f16*)a.P16, a.R16, (f16*)a.K16, (f16*)a.Q16);
+        k_prep<DK, false><<<dim3(NT, a.Nk), 256, 0, st>>>(k, q, a.beta, a.beta_f32, a.g, a.chunk_start, a.chunk_len,
+                                                            a.Nk, a.Nv, (f16*)a.T16, (f16*)a.P16, a.R16, (f16*)a.K16,
+                                                            (f16*)a.Q16);
     if (a.N > 0)
         k_chunk16<DK, DV, kStates16><<<dim3(a.N, a.Nv, DV / 16), 256, 0, st>>>(
             q, k, v, a.R16, (const f16*)a.T16, (const f16*)a.P16, (const f16*)a.K16, (const f16*)a.Q16, a.S0,

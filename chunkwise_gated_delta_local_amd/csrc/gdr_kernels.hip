@@ -349,7 +349,8 @@ __global__ __launch_bounds__(256) void k_wu(const T* __restrict__ k, const T* __
                                              const float* __restrict__ G, const float* __restrict__ A,
                                              const int32_t* __restrict__ chunk_start,
                                              const int32_t* __restrict__ chunk_len, int32_t Nk, int32_t Nv,
-                                             float* __restrict__ Wf, float* __restrict__ Uf, T* __restrict__ KTf) {
+                                             float* __restrict__ Wf, float* __restrict__ Uf, T* __restrict__ KTf,
+                                             int w_only) {
     constexpr int NTB = C / 16, NTHR = 64 * NTB;
     constexpr int CP = C < 32 ? 32 : C;        // positions padded to whole pairs
     constexpr int NTP = CP / 32;
@@ -374,8 +375,8 @@ __global__ __launch_bounds__(256) void k_wu(const T* __restrict__ k, const T* __
     }
     __syncthreads();
 
-    // K^T pair fragments for the state pass: [c][kh][db][tp]
-    for (int f = wave; f < (DK / 16) * NTP; f += NTB) {
+    // K^T pair fragments for the state pass: [c][kh][db][tp] (w_only: W alone is wanted)
+    for (int f = wave; f < (w_only ? 0 : (DK / 16) * NTP); f += NTB) {
         const int db = f / NTP, tp = f % NTP;
         v8 val = load_pair_row<T>(&KTs[(db * 16 + r) * MP + tp * 32], qd);
         store_frag<T>(KTf + (((int64_t)c * Nk + kh) * (DK / 16) * NTP + f) * 512, lane, val);
@@ -392,7 +393,7 @@ __global__ __launch_bounds__(256) void k_wu(const T* __restrict__ k, const T* __
             bs[tid] = bm;
             sc[tid] = tid < L ? bm * __expf(G[(s + tid) * Nv + h]) : 0.f;
         }
-        for (int idx = tid; idx < CP * (DV / 8); idx += NTHR) {
+        for (int idx = tid; idx < (w_only ? 0 : CP * (DV / 8)); idx += NTHR) {
             const int m = idx % CP, seg = idx / CP;
             v8 val = zero_pair<T>();
             if (m < L) val = *reinterpret_cast<const v8*>(v + ((s + m) * Nv + h) * DV + seg * 8);
@@ -436,6 +437,7 @@ __global__ __launch_bounds__(256) void k_wu(const T* __restrict__ k, const T* __
             store_pair_half_f32(dst, lane, db & 1, acc);
         }
         // U tiles (tb, nb): rows i, columns dv
+        if (w_only) continue;
 #pragma unroll
         for (int nb = 0; nb < DV / 16; ++nb) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -835,7 +837,7 @@ static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
     if (NT > 0)
         k_wu<T, DK, DV, C><<<dim3(NT, a.Nk), NTHR, 0, st>>>((const T*)a.k, (const T*)a.v, a.beta, a.beta_f32, a.G,
                                                        (const float*)a.A, a.chunk_start, a.chunk_len, a.Nk, a.Nv,
-                                                       (float*)a.W, (float*)a.U, (T*)a.KT);
+                                                       (float*)a.W, (float*)a.U, (T*)a.KT, (int)a.states16);
     mark(4);
     if (kFp16 && a.states16) {
         // backward recompute: H and V_new from the fp16 chunk pass (k_prep and
