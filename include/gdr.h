@@ -283,8 +283,12 @@ gdr_status_t gdr_chunk_fwd_segmented(const gdr_problem_t* problem,
  *                  preparation (layouts, score block), [3] reverse state
  *                  pass, [4] per-chunk gradients, [5] sum of dq and dk over
  *                  the value heads of each q/k head.
- * All arithmetic is fp32 (products on the fp32 matrix cores), and every sum
- * runs in a fixed order: the same inputs give the same bits on every run.
+ * The forward recompute runs the five-kernel path; for bf16 inputs at C = 64
+ * with at least 128 (sequence, value head, 16 dv columns) units its chunk
+ * states and V_new come from the fp16 chunk pass instead (fp16 operands, fp32
+ * sums, as in gdr_chunk_fwd). The backward's own arithmetic is fp32 (products
+ * on the fp32 matrix cores), and every sum runs in a fixed order: the same
+ * inputs give the same bits on every run.
  * Errors as for gdr_chunk_fwd. Asynchronous on `stream`.
  */
 #define GDR_BWD_NUM_STAGES 5
