@@ -437,6 +437,7 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
     // kStates16: the entering state's and V_new's fp32 accumulator tiles, lane-contiguous
     __shared__ __attribute__((aligned(16))) float Hx[want_h ? 2 : 1][want_h ? NDB : 1][want_h ? 256 : 4];
     __shared__ __attribute__((aligned(16))) float VNx32[want_h ? 2 : 1][want_h ? 4 : 1][want_h ? 256 : 4];
+    __shared__ uint32_t pf_sink[64];                                     // checksum of the L2 warm-up loads (never read)
 
     // XCD-aware placement: each XCD takes a contiguous run of (unit, head,
     // column tile) triples, so the workgroups that read the same K and Q
@@ -463,12 +464,16 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
     float* const STo = trans ? ST2 : ST;
     const int c0 = __builtin_amdgcn_readfirstlane(first[n]), c1 = __builtin_amdgcn_readfirstlane(first[n + 1]);
     auto slot4 = [&](int c) { return (c - c0) & 3; };      // K tiles; V, decay rows and T
-    // chunk start and length in scalar registers (uniform buffer descriptors);
-    // a chunk past the sequence's last reads as empty
-    auto chunk_s = [&](int c) { return c < c1 ? (int64_t)__builtin_amdgcn_readfirstlane(chunk_start[c]) : (int64_t)0; };
-    auto chunk_L = [&](int c) {
-        return c < c1 ? max(0, min(C, (int)__builtin_amdgcn_readfirstlane(chunk_len[c]))) : 0;
-    };
+    // chunk start and length in scalar registers (uniform buffer descriptors),
+    // formed from the run's first chunk and its end: the chunks of a run are
+    // consecutive C-token pieces of one sequence (the last may be shorter), so
+    // no step waits for a table load; a chunk past the run's last reads as empty
+    const int64_t run_s = c0 < c1 ? (int64_t)__builtin_amdgcn_readfirstlane(chunk_start[c0]) : 0;
+    const int64_t run_e = c0 < c1 ? (int64_t)__builtin_amdgcn_readfirstlane(chunk_start[c1 - 1]) +
+                                        __builtin_amdgcn_readfirstlane(chunk_len[c1 - 1])
+                                  : 0;
+    auto chunk_s = [&](int c) { return c < c1 ? run_s + (int64_t)(c - c0) * C : (int64_t)0; };
+    auto chunk_L = [&](int c) { return c < c1 ? max(0, min(C, (int)(run_e - chunk_s(c)))) : 0; };
     auto swz = [](int row) { return tile_swz<DK>(row); };
     const int64_t sbase = ((int64_t)n * Nv + h) * DK * NC;
     typedef std::integral_constant<int, 0> P0;
@@ -558,6 +563,69 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
             x.a1 = Rs[sl][C];
             return x;
         };
+        // L2 warm-up. Each chunk's tiles (K16, Q16 per q/k head; T and P pairs,
+        // decay rows and the V rows per value head) are read by every column
+        // tile of a head (and by both value heads of a GQA pair), each time as
+        // an L2 miss if none of them has touched the lines yet. At step c the
+        // chain loads one dword per 128-byte line of chunk c + kAhead, the
+        // lines split over the workgroups that share them (about 45 lines per
+        // workgroup and step at dk = dv = 128): the helpers' copies and loads,
+        // issued three and one steps ahead, then hit the L2. The loads for two
+        // chunks are issued at the start of an even step and folded into a
+        // checksum at the end of the odd step after it (the chain's only wait
+        // for them, two steps after the loads); the checksum goes to an LDS
+        // word that is never read, which keeps the loads.
+        constexpr int kAhead = 8;
+        const char* pf_base = nullptr;           // the tensor; byte offset of chunk cp's line: pf_off + cp pf_stride
+        int64_t pf_off = 0, pf_stride = 0;
+        int pf_row = -1;                         // V lines: the row, valid only below the chunk's length
+        bool pf_on = false;
+        if constexpr (want_o) {
+            constexpr int NB = DV / 16, LT = C * DK * 2 / 128;                  // column tiles; lines of a K/Q tile
+            constexpr int LTP = kPairs * kFrag * 2 / 128, LR = 2 * C * 4 / 128;  // lines of T (and P); of R
+            constexpr int VL = DV * 2 >= 128 ? DV * 2 / 128 : 1;                 // lines of a V row
+            constexpr int NVL = 2 * LTP + LR + C * VL;                           // lines per value head
+            const int G = Nv / Nk, U = G * NB, u = (h % G) * NB + nb;
+            const int cnt_k = u < 2 * LT ? (2 * LT - u + U - 1) / U : 0;
+            const int cnt_v = (NVL - nb + NB - 1) / NB;
+            int idx = lane;
+            if (idx < cnt_k) {
+                const int i = u + U * idx;
+                const f16* t = i < LT ? K16 : Q16;
+                pf_base = reinterpret_cast<const char*>(t);
+                pf_off = (int64_t)kh * C * DK * 2 + (int64_t)(i % LT) * 128;
+                pf_stride = (int64_t)Nk * C * DK * 2;
+                pf_on = true;
+            } else if ((idx -= cnt_k) < cnt_v) {
+                const int j = nb + NB * idx;
+                if (j < 2 * LTP) {
+                    const f16* t = j < LTP ? Tf : Pf;
+                    pf_base = reinterpret_cast<const char*>(t);
+                    pf_off = (int64_t)h * kPairs * kFrag * 2 + (int64_t)(j % LTP) * 128;
+                    pf_stride = (int64_t)Nv * kPairs * kFrag * 2;
+                } else if (j < 2 * LTP + LR) {
+                    pf_base = reinterpret_cast<const char*>(R);
+                    pf_off = (int64_t)h * 2 * C * 4 + (int64_t)(j - 2 * LTP) * 128;
+                    pf_stride = (int64_t)Nv * 2 * C * 4;
+                } else {                         // V row `row` of the chunk: token run_s + (cp - c0) C + row
+                    const int jj = j - 2 * LTP - LR;
+                    pf_row = jj / VL;
+                    pf_base = reinterpret_cast<const char*>(v);
+                    pf_off = (((run_s - (int64_t)c0 * C + pf_row) * Nv + h) * DV) * 2 + (int64_t)(jj % VL) * 128;
+                    pf_stride = (int64_t)C * Nv * DV * 2;
+                }
+                pf_on = true;
+            }
+        }
+        auto prefetch = [&](int c) {
+            const int cp = c + kAhead;
+            float x = 0.f;
+            if (want_o && cp < c1 && pf_on && pf_row < chunk_L(cp))
+                x = *reinterpret_cast<const float*>(pf_base + (pf_off + (int64_t)cp * pf_stride));
+            return x;
+        };
+        uint32_t pf_sum = 0;
+        auto consume = [&](float x) { pf_sum ^= __float_as_uint(x); };
         VR vr;
         TR tr;
         make_pairs();
@@ -567,9 +635,10 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
             vr = read_vr(c0);
             tr = read_tr(c0);
         }
-        auto step = [&](int c) {
+        auto step = [&](int c, auto&& at_start, auto&& at_end) {
             const int s4l = slot4(c);
             const f16* Kb = Ks[s4l];
+            at_start();
             // ---- region 1: S_in's pairs published; Y = K S_in (operands read in the
             //      previous step) with the reads of this chunk's K^T operands and the
             //      scaling of S by exp(G_last) interleaved
@@ -660,9 +729,19 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
             __builtin_amdgcn_sched_barrier(0);
             make_pairs();
             tr = tr_next;
+            at_end();
             lds_barrier();                                                        // end of step c
         };
-        for (int c = c0; c < c1; ++c) step(c);
+        // two steps per iteration: no warm-up value is live across iterations
+        const auto none = [] {};
+        int c = c0;
+        for (; c + 1 < c1; c += 2) {
+            float x0, x1;
+            step(c, [&] { x0 = prefetch(c); x1 = prefetch(c + 1); }, none);
+            step(c + 1, none, [&] { consume(x0); consume(x1); });
+        }
+        if (c < c1) step(c, none, none);
+        pf_sink[lane] = pf_sum;
         if (STo) {
 #pragma unroll
             for (int t = 0; t < NDB; ++t) {
