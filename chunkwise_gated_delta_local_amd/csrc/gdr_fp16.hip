@@ -569,13 +569,14 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
         // an L2 miss if none of them has touched the lines yet. At step c the
         // chain loads one dword per 128-byte line of chunk c + kAhead, the
         // lines split over the workgroups that share them (about 45 lines per
-        // workgroup and step at dk = dv = 128): the helpers' copies and loads,
-        // issued three and one steps ahead, then hit the L2. The loads for two
-        // chunks are issued at the start of an even step and folded into a
-        // checksum at the end of the odd step after it (the chain's only wait
-        // for them, two steps after the loads); the checksum goes to an LDS
-        // word that is never read, which keeps the loads.
-        constexpr int kAhead = 8;
+        // workgroup and chunk at dk = dv = 128): the helpers' copies and
+        // loads, issued three and one steps ahead, then hit the L2. The loads
+        // for two chunks are issued at the start of an even step and folded
+        // into a checksum at the end of the odd step after it (the chain's
+        // only wait for them, two steps after the loads); the checksum goes to
+        // an LDS word that is never read, which keeps the loads. Four to six
+        // steps ahead measured best (eight: 1.5 % slower, twelve: 5 %).
+        constexpr int kAhead = 6;
         const char* pf_base = nullptr;           // the tensor; byte offset of chunk cp's line: pf_off + cp pf_stride
         int64_t pf_off = 0, pf_stride = 0;
         int pf_row = -1;                         // V lines: the row, valid only below the chunk's length
