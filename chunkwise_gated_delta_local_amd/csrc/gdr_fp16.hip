@@ -577,17 +577,20 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
         // an LDS word that is never read, which keeps the loads. Four to six
         // steps ahead measured best (eight: 1.5 % slower, twelve: 5 %).
         constexpr int kAhead = 6;
+        // (the serial pass and the backward's state pass; the latter reads no Q16 or P)
+        constexpr bool want_pf = want_o || want_h;
+        constexpr int NKT = want_o ? 2 : 1, NPT = want_o ? 2 : 1;         // K16 (and Q16); T (and P)
         const char* pf_base = nullptr;           // the tensor; byte offset of chunk cp's line: pf_off + cp pf_stride
         int64_t pf_off = 0, pf_stride = 0;
         int pf_row = -1;                         // V lines: the row, valid only below the chunk's length
         bool pf_on = false;
-        if constexpr (want_o) {
+        if constexpr (want_pf) {
             constexpr int NB = DV / 16, LT = C * DK * 2 / 128;                  // column tiles; lines of a K/Q tile
             constexpr int LTP = kPairs * kFrag * 2 / 128, LR = 2 * C * 4 / 128;  // lines of T (and P); of R
             constexpr int VL = DV * 2 >= 128 ? DV * 2 / 128 : 1;                 // lines of a V row
-            constexpr int NVL = 2 * LTP + LR + C * VL;                           // lines per value head
+            constexpr int NVL = NPT * LTP + LR + C * VL;                         // lines per value head
             const int G = Nv / Nk, U = G * NB, u = (h % G) * NB + nb;
-            const int cnt_k = u < 2 * LT ? (2 * LT - u + U - 1) / U : 0;
+            const int cnt_k = u < NKT * LT ? (NKT * LT - u + U - 1) / U : 0;
             const int cnt_v = (NVL - nb + NB - 1) / NB;
             int idx = lane;
             if (idx < cnt_k) {
@@ -599,17 +602,17 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
                 pf_on = true;
             } else if ((idx -= cnt_k) < cnt_v) {
                 const int j = nb + NB * idx;
-                if (j < 2 * LTP) {
+                if (j < NPT * LTP) {
                     const f16* t = j < LTP ? Tf : Pf;
                     pf_base = reinterpret_cast<const char*>(t);
                     pf_off = (int64_t)h * kPairs * kFrag * 2 + (int64_t)(j % LTP) * 128;
                     pf_stride = (int64_t)Nv * kPairs * kFrag * 2;
-                } else if (j < 2 * LTP + LR) {
+                } else if (j < NPT * LTP + LR) {
                     pf_base = reinterpret_cast<const char*>(R);
-                    pf_off = (int64_t)h * 2 * C * 4 + (int64_t)(j - 2 * LTP) * 128;
+                    pf_off = (int64_t)h * 2 * C * 4 + (int64_t)(j - NPT * LTP) * 128;
                     pf_stride = (int64_t)Nv * 2 * C * 4;
                 } else {                         // V row `row` of the chunk: token run_s + (cp - c0) C + row
-                    const int jj = j - 2 * LTP - LR;
+                    const int jj = j - NPT * LTP - LR;
                     pf_row = jj / VL;
                     pf_base = reinterpret_cast<const char*>(v);
                     pf_off = (((run_s - (int64_t)c0 * C + pf_row) * Nv + h) * DV) * 2 + (int64_t)(jj % VL) * 128;
@@ -618,12 +621,17 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
                 pf_on = true;
             }
         }
-        auto prefetch = [&](int c) {
+        // the lane's line in chunk c0 + kAhead as an address, advanced two chunks
+        // per call; only the run's last chunk can be shorter than C
+        uint64_t pf_addr = (uint64_t)pf_base + (uint64_t)(pf_off + (int64_t)(c0 + kAhead) * pf_stride);
+        const bool pf_last = pf_on && pf_row < chunk_L(c1 - 1);
+        typedef const __attribute__((address_space(1))) float* gptr;   // global loads (not flat: no LDS counter)
+        auto prefetch2 = [&](int c, float& x0, float& x1) {     // chunks c + kAhead and c + kAhead + 1
             const int cp = c + kAhead;
-            float x = 0.f;
-            if (want_o && cp < c1 && pf_on && pf_row < chunk_L(cp))
-                x = *reinterpret_cast<const float*>(pf_base + (pf_off + (int64_t)cp * pf_stride));
-            return x;
+            if (want_pf && cp < c1 && (cp < c1 - 1 ? pf_on : pf_last)) x0 = *(gptr)pf_addr;
+            if (want_pf && cp + 1 < c1 && (cp + 1 < c1 - 1 ? pf_on : pf_last))
+                x1 = *(gptr)(pf_addr + (uint64_t)pf_stride);
+            pf_addr += 2 * (uint64_t)pf_stride;
         };
         uint32_t pf_sum = 0;
         auto consume = [&](float x) { pf_sum ^= __float_as_uint(x); };
@@ -737,8 +745,8 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
         const auto none = [] {};
         int c = c0;
         for (; c + 1 < c1; c += 2) {
-            float x0, x1;
-            step(c, [&] { x0 = prefetch(c); x1 = prefetch(c + 1); }, none);
+            float x0 = 0.f, x1 = 0.f;
+            step(c, [&] { prefetch2(c, x0, x1); }, none);
             step(c + 1, none, [&] { consume(x0); consume(x1); });
         }
         if (c < c1) step(c, none, none);
