@@ -539,14 +539,19 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ q, const
 //   Z = diag(exp(G_last - G)) K dS;  dV_new = X + Z   (overwrites X)
 //   the chunk's outgoing-state gradient dS is stored (over Y', after reading it)
 //   dS <- exp(G_last) dS + Y' - W^T Z
-// Both products run on the fp32 matrix cores (v_mfma_f32_16x16x4_f32):
-// wavefront w forms rows 16 w .. 16 w + 15 of Z (contraction over dk) and the
-// dk row blocks w, w + 4, ... of W^T Z (contraction over the chunk's
-// positions). K (as fp32), W^T, Z^T and dS^T go through LDS; in each group of
-// four products lane (qd, r) takes the contraction indices 16 t + 4 qd + u,
-// u = 0..3, so that each operand of a group is one 16-byte read. The next
-// chunk's K rows, W^T, X, Y' and gate sums are loaded into registers while the
-// current chunk is computed.
+// Wavefront w forms rows 16 w .. 16 w + 15 of Z (contraction over dk) and
+// the dk row blocks w, w + 4, ... of W^T Z (contraction over the chunk's
+// positions); K, W^T, Z^T and dS^T go through LDS. For bf16 inputs (C a
+// multiple of 32) both products run on v_mfma_f32_16x16x32_bf16 with K as it
+// is and dS, W^T and Z split into hi + lo bf16 (three or two products per
+// tile; about 16 bits of each value kept, so the result matches the fp32
+// products to about 1e-5, and scaling the inputs by 2 scales every gradient
+// by exactly 2), lane (qd, r) holding the contraction indices 32 t + 8 qd ..
+// + 7 (one 16-byte read per operand). For fp32 inputs they run on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32) with fp32 tiles, lane (qd, r) taking the
+// contraction indices 16 t + 4 qd + u, u = 0..3, in each group of four
+// products. The next chunk's K rows, W^T, X, Y' and gate sums are loaded into
+// registers while the current chunk is computed.
 template <typename T, int DK, int DV, int C>
 __global__ __launch_bounds__(256) void k_bwd_state(const T* __restrict__ k, const float* __restrict__ G,
                                                     const float* __restrict__ WT, const float* __restrict__ dST,
@@ -563,10 +568,33 @@ __global__ __launch_bounds__(256) void k_bwd_state(const T* __restrict__ k, cons
     constexpr int NK8 = (NSEG + 255) / 256;
     constexpr int NW4 = DK * C / 4;             // 4-float pieces of W^T
     constexpr int NWT = (NW4 + 255) / 256;
-    __shared__ __attribute__((aligned(16))) float Ks[C][KP];
-    __shared__ __attribute__((aligned(16))) float Wt[DK][CP];
-    __shared__ __attribute__((aligned(16))) float dSt[16][KP];
-    __shared__ __attribute__((aligned(16))) float Zt[16][CP];
+    // bf16 inputs (C a multiple of 32): bf16 tiles on v_mfma_f32_16x16x32_bf16,
+    // K as it is (exact) and dS, W^T and Z as hi + lo bf16 pairs (products
+    // K dS_hi + K dS_lo and W_hi Z_hi + W_hi Z_lo + W_lo Z_hi, fp32 sums);
+    // fp32 inputs: fp32 tiles on v_mfma_f32_16x16x4_f32
+    constexpr bool kHalf = sizeof(T) == 2 && C % 32 == 0;
+    constexpr int KPH = DK + 8, CPH = C + 8;    // bf16 pitches (elements)
+    typedef Vec<bf16>::v8 b8;
+    typedef Vec<bf16>::v4 b4;
+    __shared__ __attribute__((aligned(16))) float Ks[kHalf ? 1 : C][KP];
+    __shared__ __attribute__((aligned(16))) float Wt[kHalf ? 1 : DK][CP];
+    __shared__ __attribute__((aligned(16))) float dSt[kHalf ? 1 : 16][KP];
+    __shared__ __attribute__((aligned(16))) float Zt[kHalf ? 1 : 16][CP];
+    __shared__ __attribute__((aligned(16))) bf16 Kb[kHalf ? C : 1][KPH];
+    __shared__ __attribute__((aligned(16))) bf16 Wb[kHalf ? 2 : 1][kHalf ? DK : 1][CPH];     // hi, lo
+    __shared__ __attribute__((aligned(16))) bf16 dSb[kHalf ? 2 : 1][kHalf ? 16 : 1][KPH];
+    __shared__ __attribute__((aligned(16))) bf16 Zb[kHalf ? 2 : 1][kHalf ? 16 : 1][CPH];
+    // four fp32 values -> hi and lo bf16 (x = hi + lo to about 16 bits)
+    auto put_split4 = [](bf16* hi, bf16* lo, const f32x4& x) {
+        b4 h, l;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            h[j] = (bf16)x[j];
+            l[j] = (bf16)(x[j] - (float)h[j]);
+        }
+        *reinterpret_cast<b4*>(hi) = h;
+        *reinterpret_cast<b4*>(lo) = l;
+    };
     __shared__ float gs[256];                   // gate sums (one per thread; C used)
     const int n = blockIdx.x, h = blockIdx.y, nb = blockIdx.z, tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, r = lane & 15, qd = lane >> 4;
@@ -631,7 +659,12 @@ __global__ __launch_bounds__(256) void k_bwd_state(const T* __restrict__ k, cons
 #pragma unroll
         for (int i = 0; i < NBW; ++i) {
             const int m = w + 4 * i;
-            if (m < NB) *reinterpret_cast<f32x4*>(&dSt[r][16 * m + 4 * qd]) = dS[i];
+            if (m < NB) {
+                if constexpr (kHalf)
+                    put_split4(&dSb[0][r][16 * m + 4 * qd], &dSb[1][r][16 * m + 4 * qd], dS[i]);
+                else
+                    *reinterpret_cast<f32x4*>(&dSt[r][16 * m + 4 * qd]) = dS[i];
+            }
         }
     };
     typedef std::integral_constant<int, 0> S0_t;
@@ -666,20 +699,30 @@ __global__ __launch_bounds__(256) void k_bwd_state(const T* __restrict__ k, cons
         for (int e = 0; e < NK8; ++e) {               // K rows and W^T -> LDS
             const int idx = tid + 256 * e, i = idx / (DK / 8), seg = idx % (DK / 8);
             if (NSEG % 256 == 0 || idx < NSEG) {
-                f32x4 a, b;
+                if constexpr (kHalf) {
+                    *reinterpret_cast<b8*>(&Kb[i][seg * 8]) = __builtin_bit_cast(b8, kr[SET][e]);
+                } else {
+                    f32x4 a, b;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    a[t] = to_f(kr[SET][e][t]);
-                    b[t] = to_f(kr[SET][e][4 + t]);
+                    for (int t = 0; t < 4; ++t) {
+                        a[t] = to_f(kr[SET][e][t]);
+                        b[t] = to_f(kr[SET][e][4 + t]);
+                    }
+                    *reinterpret_cast<f32x4*>(&Ks[i][seg * 8]) = a;
+                    *reinterpret_cast<f32x4*>(&Ks[i][seg * 8 + 4]) = b;
                 }
-                *reinterpret_cast<f32x4*>(&Ks[i][seg * 8]) = a;
-                *reinterpret_cast<f32x4*>(&Ks[i][seg * 8 + 4]) = b;
             }
         }
 #pragma unroll
         for (int e = 0; e < NWT; ++e) {
             const int idx = tid + 256 * e;
-            if (NW4 % 256 == 0 || idx < NW4) *reinterpret_cast<f32x4*>(&Wt[idx / (C / 4)][4 * (idx % (C / 4))]) = wr[SET][e];
+            if (NW4 % 256 == 0 || idx < NW4) {
+                const f32x4 x4 = wr[SET][e];
+                if constexpr (kHalf)
+                    put_split4(&Wb[0][idx / (C / 4)][4 * (idx % (C / 4))], &Wb[1][idx / (C / 4)][4 * (idx % (C / 4))], x4);
+                else
+                    *reinterpret_cast<f32x4*>(&Wt[idx / (C / 4)][4 * (idx % (C / 4))]) = x4;
+            }
         }
         gs[tid] = gr;
         const f32x4 x = xr;
@@ -694,24 +737,41 @@ __global__ __launch_bounds__(256) void k_bwd_state(const T* __restrict__ k, cons
         const float gL = gs[L - 1];
         // Z rows 16 w + 4 qd + v, column r; dV_new = X + Z
         if (16 * w < C) {
-            f32x4 zu[4];                              // four independent sums (u), added at the end
+            f32x4 z;
+            if constexpr (kHalf) {                    // lane (qd, r): contraction indices 32 t + 8 qd .. + 7
+                f32x4 zu[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};   // K dS_hi, K dS_lo
 #pragma unroll
-            for (int u = 0; u < 4; ++u) zu[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int t = 0; t < DK / 32; ++t) {
+                    const b8 a = *reinterpret_cast<const b8*>(&Kb[16 * w + r][32 * t + 8 * qd]);
+                    const b8 bh = *reinterpret_cast<const b8*>(&dSb[0][r][32 * t + 8 * qd]);
+                    const b8 bl = *reinterpret_cast<const b8*>(&dSb[1][r][32 * t + 8 * qd]);
+                    zu[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, zu[0], 0, 0, 0);
+                    zu[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, zu[1], 0, 0, 0);
+                }
+                z = zu[0] + zu[1];
+            } else {
+                f32x4 zu[4];                          // four independent sums (u), added at the end
 #pragma unroll
-            for (int t = 0; t < DK / 16; ++t) {
-                const f32x4 a = *reinterpret_cast<const f32x4*>(&Ks[16 * w + r][16 * t + 4 * qd]);
-                const f32x4 b = *reinterpret_cast<const f32x4*>(&dSt[r][16 * t + 4 * qd]);
+                for (int u = 0; u < 4; ++u) zu[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int u = 0; u < 4; ++u) zu[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], b[u], zu[u], 0, 0, 0);
+                for (int t = 0; t < DK / 16; ++t) {
+                    const f32x4 a = *reinterpret_cast<const f32x4*>(&Ks[16 * w + r][16 * t + 4 * qd]);
+                    const f32x4 b = *reinterpret_cast<const f32x4*>(&dSt[r][16 * t + 4 * qd]);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) zu[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], b[u], zu[u], 0, 0, 0);
+                }
+                z = (zu[0] + zu[1]) + (zu[2] + zu[3]);
             }
-            f32x4 z = (zu[0] + zu[1]) + (zu[2] + zu[3]);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int i = 16 * w + 4 * qd + v;
                 z[v] = i < L ? __expf(gL - gs[i]) * z[v] : 0.f;
                 if (i < L) dVX[((s + i) * Nv + h) * DV + nb * 16 + r] = x[v] + z[v];
             }
-            *reinterpret_cast<f32x4*>(&Zt[r][16 * w + 4 * qd]) = z;
+            if constexpr (kHalf)
+                put_split4(&Zb[0][r][16 * w + 4 * qd], &Zb[1][r][16 * w + 4 * qd], z);
+            else
+                *reinterpret_cast<f32x4*>(&Zt[r][16 * w + 4 * qd]) = z;
         }
         lds_barrier();
         // the outgoing-state gradient of this chunk, then dS <- exp(G_last) dS + Y' - W^T Z
@@ -721,13 +781,26 @@ __global__ __launch_bounds__(256) void k_bwd_state(const T* __restrict__ k, cons
             const int m = w + 4 * i;
             if (m < NB) {
                 f32x4 au[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};   // two independent sums
+                if constexpr (kHalf) {
 #pragma unroll
-                for (int t = 0; t < C / 16; ++t) {
-                    const f32x4 a = *reinterpret_cast<const f32x4*>(&Wt[16 * m + r][16 * t + 4 * qd]);
-                    const f32x4 b = *reinterpret_cast<const f32x4*>(&Zt[r][16 * t + 4 * qd]);
+                    for (int t = 0; t < C / 32; ++t) {
+                        const b8 ah = *reinterpret_cast<const b8*>(&Wb[0][16 * m + r][32 * t + 8 * qd]);
+                        const b8 al = *reinterpret_cast<const b8*>(&Wb[1][16 * m + r][32 * t + 8 * qd]);
+                        const b8 bh = *reinterpret_cast<const b8*>(&Zb[0][r][32 * t + 8 * qd]);
+                        const b8 bl = *reinterpret_cast<const b8*>(&Zb[1][r][32 * t + 8 * qd]);
+                        au[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, au[0], 0, 0, 0);
+                        au[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, au[1], 0, 0, 0);
+                        au[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, au[1], 0, 0, 0);
+                    }
+                } else {
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        au[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], b[u], au[u & 1], 0, 0, 0);
+                    for (int t = 0; t < C / 16; ++t) {
+                        const f32x4 a = *reinterpret_cast<const f32x4*>(&Wt[16 * m + r][16 * t + 4 * qd]);
+                        const f32x4 b = *reinterpret_cast<const f32x4*>(&Zt[r][16 * t + 4 * qd]);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            au[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], b[u], au[u & 1], 0, 0, 0);
+                    }
                 }
                 const f32x4 acc = au[0] + au[1];
                 *reinterpret_cast<f32x4*>(&dSY[(((int64_t)c * Nv + h) * DV + nb * 16 + r) * DK + 16 * m + 4 * qd]) = dS[i];
