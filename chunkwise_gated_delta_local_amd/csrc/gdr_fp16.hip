@@ -58,8 +58,11 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 namespace {
 
 constexpr int kPairs = 6;      // lower-triangular (16-row block, 32-position block) pairs of a 64 x 64 block
-__constant__ int kPairTb[kPairs] = {0, 1, 2, 2, 3, 3};
-__constant__ int kPairTp[kPairs] = {0, 0, 0, 1, 0, 1};
+// pair p = 0..5 covers row block tb(p) = 0, 1, 2, 2, 3, 3 and position block
+// tp(p) = 0, 0, 0, 1, 0, 1 (formed arithmetically: a table indexed by a
+// run-time p would be a memory load on the critical path)
+__device__ __forceinline__ int pair_tb(int p) { return p < 2 ? p : (p + 2) >> 1; }
+__device__ __forceinline__ int pair_tp(int p) { return p < 2 ? 0 : (p - 2) & 1; }
 constexpr int kFrag = 512;     // elements of one pair fragment (64 lanes x 8)
 constexpr int kRsrc = 0x00020000;   // buffer descriptor word 3: raw 32-bit access
 
@@ -338,7 +341,7 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
         // 3d. T = A diag(beta): pair p covers rows 16 tb + r and positions
         //     32 tp + m(qd, e) (m = 4 qd + e, or 16 + 4 qd + e - 4); rows past the end are zero
         for (int p = wave; p < kPairs; p += 4) {
-            const int tb = kPairTb[p], tp = kPairTp[p];
+            const int tb = pair_tb(p), tp = pair_tp(p);
             const int row = tb * 16 + r;
             const int m0 = tp * 32 + 4 * qd;
             const f32x4 a0 = *reinterpret_cast<const f32x4*>(&Af[row][m0]);
