@@ -129,7 +129,9 @@ __device__ __forceinline__ int tile_swz(int row) {
 //   2. K K^T and the transposed score tiles K Q^T of block row `wave` on bf16
 //      matrix cores: exact products of the inputs, fp32 sums (FLA DeltaNet
 //      article, section 3.1).
-//   3. Per value head:
+//   3. Per value head (the gates of up to four heads are loaded, scanned and
+//      placed in LDS together, so the per-head phases issue no global load and
+//      their barriers wait for LDS only):
 //      a. G = inclusive prefix sum of g over the chunk (one lane per position,
 //         a shuffle scan in fp32); the decay rows R = (exp(G), exp(G_last - G))
 //         (zero past the chunk end) for the state pass.
@@ -160,7 +162,8 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
     constexpr int LA_BYTES = 2 * C * LP * 4;
     static_assert(SEGS >= 1, "dk");
     __shared__ __attribute__((aligned(16))) char smem[TILE_BYTES > LA_BYTES ? TILE_BYTES : LA_BYTES];
-    __shared__ __attribute__((aligned(16))) float bs[C], gs[C];
+    constexpr int HB = 4;                      // value heads whose gates are prepared together
+    __shared__ __attribute__((aligned(16))) float bsa[HB][C], gsa[HB][C];
     bf16* Ks = reinterpret_cast<bf16*>(smem);
     bf16* Qs = Ks + C * KP;
     float (*Lf)[LP] = reinterpret_cast<float (*)[LP]>(smem);
@@ -173,14 +176,46 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, qd = lane >> 4;
     const int group = Nv / Nk;
 
-    // beta and g of a value head go through registers of wave 0: head 0's are
-    // fetched with the tiles, each next head's while the current one is processed
-    float b_nx = 0.f, g_nx = 0.f;
-    auto fetch_gates = [&](int hh) {
-        const int h = kh * group + hh;
-        const bool on = tid < L;
-        b_nx = on ? load_beta(beta, (s + tid) * Nv + h, beta_f32) : 0.f;
-        g_nx = (on && g) ? g[(s + tid) * Nv + h] : 0.f;
+    // beta and g of up to HB value heads go through registers of wave 0, as
+    // raw bits (no arithmetic on a freshly loaded value): the first batch's are
+    // loaded with the tiles; each batch's prefix sums, decay rows and LDS rows
+    // are formed before its heads are processed, so the per-head phases issue
+    // no global load (and no wait that would drain their stores)
+    uint32_t b_raw[HB];
+    float g_raw[HB];
+    auto fetch_gates = [&](int hb) {           // heads hb .. hb + HB - 1 of the group
+        const int64_t idx = (s + tid) * Nv + kh * group + hb;
+#pragma unroll
+        for (int u = 0; u < HB; ++u) {
+            b_raw[u] = 0;
+            g_raw[u] = 0.f;
+            if (tid < L && hb + u < group) {
+                if (beta_f32) b_raw[u] = reinterpret_cast<const uint32_t*>(beta)[idx + u];
+                else b_raw[u] = reinterpret_cast<const uint16_t*>(beta)[idx + u];
+                if (g) g_raw[u] = g[idx + u];
+            }
+        }
+    };
+    // prefix sums over the 64 positions (wave 0, one lane per position), decay
+    // rows R = (exp(G), exp(G_last - G)) for the chunk pass, and the LDS rows
+    auto prepare_gates = [&](int hb) {
+#pragma unroll
+        for (int u = 0; u < HB; ++u) {
+            if (hb + u >= group) break;
+            float x = g_raw[u];
+#pragma unroll
+            for (int off = 1; off < C; off <<= 1) {
+                const float y = __shfl_up(x, off, C);
+                if (lane >= off) x += y;
+            }
+            const float g_last = __shfl(x, L > 0 ? L - 1 : 0, C);
+            const bool on = lane < L;
+            gsa[u][lane] = on ? x : 0.f;
+            bsa[u][lane] = __uint_as_float(beta_f32 ? b_raw[u] : b_raw[u] << 16);
+            float* Rh = R + ((int64_t)c * Nv + kh * group + hb + u) * 2 * C;
+            Rh[lane] = on ? __expf(x) : 0.f;
+            Rh[C + lane] = on ? __expf(g_last - x) : 0.f;
+        }
     };
 
     // 1. K and Q rows (all loads first)
@@ -211,7 +246,7 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
             if constexpr (WITH_P) *reinterpret_cast<h8*>(&qt16[row * DK + u]) = bf16x8_to_f16(__builtin_bit_cast(u4, qv[i]));
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // 2. kk[j]: K K^T rows 16 wave + 4 qd + jj, column 16 j + r.
     //    qk[j]: k_{16 j + 4 qd + jj} . q_{16 wave + r} (the score block transposed).
@@ -231,7 +266,7 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
             }
         }
     }
-    __syncthreads();                           // tiles consumed: the LDS now holds L and A
+    lds_barrier();                           // tiles consumed: the LDS now holds L and A
     for (int idx = tid; idx < 2 * 256; idx += NTHR) {   // the two strictly-upper blocks the merges read
         const int blk = idx >> 8, e = idx & 255, row = blk * 32 + (e >> 4), col = blk * 32 + 16 + (e & 15);
         Af[row][col] = 0.f;
@@ -239,24 +274,16 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
 
     for (int hh = 0; hh < group; ++hh) {
         const int h = kh * group + hh;
-        // 3a. prefix sum over the 64 positions (wave 0, one lane per position)
-        if (wave == 0) {
-            float x = g_nx;
-#pragma unroll
-            for (int off = 1; off < C; off <<= 1) {
-                const float y = __shfl_up(x, off, C);
-                if (lane >= off) x += y;
+        // 3a. the gates of heads hh .. hh + HB - 1 (wave 0)
+        if (hh % HB == 0) {
+            if (wave == 0) {
+                if (hh > 0) fetch_gates(hh);
+                prepare_gates(hh);
             }
-            const float g_last = __shfl(x, L > 0 ? L - 1 : 0, C);
-            const bool on = lane < L;
-            gs[lane] = on ? x : 0.f;
-            bs[lane] = b_nx;
-            float* Rh = R + ((int64_t)c * Nv + h) * 2 * C;
-            Rh[lane] = on ? __expf(x) : 0.f;
-            Rh[C + lane] = on ? __expf(g_last - x) : 0.f;
-            if (hh + 1 < group) fetch_gates(hh + 1);
+            lds_barrier();
         }
-        __syncthreads();
+        const float* gs = gsa[hh % HB];
+        const float* bs = bsa[hh % HB];
 
         // 3b. strictly lower L
 #pragma unroll
@@ -271,7 +298,7 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // 3c. diagonal block `wave`: lane r < 16 owns column r of the block's
         //     inverse; each substitution step reads row i of L with broadcast reads
@@ -293,7 +320,7 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
                 for (int i = 0; i < 16; ++i) Af[b0 + i][b0 + lane] = x[i];
             }
         }
-        __syncthreads();
+        lds_barrier();
         // A_ij = -A_ii (L_ij A_jj) for (i, j) = (1, 0) [wave 0] and (3, 2) [wave 1]
         if (wave < 2) {
             const int bi = 2 * wave + 1, bj = 2 * wave;
@@ -311,7 +338,7 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) Af[bi * 16 + 4 * qd + jj][bj * 16 + r] = -t2[jj];
         }
-        __syncthreads();
+        lds_barrier();
         // lower-left 32 x 32 block = -A_bot (L_bl A_top); wave w < 2 takes column block w
         if (wave < 2) {
             const int ct = wave;
@@ -336,7 +363,7 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
                 for (int jj = 0; jj < 4; ++jj) Af[32 + 16 * rb + 4 * qd + jj][ct * 16 + r] = -t2[jj];
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // 3d. T = A diag(beta): pair p covers rows 16 tb + r and positions
         //     32 tp + m(qd, e) (m = 4 qd + e, or 16 + 4 qd + e - 4); rows past the end are zero
@@ -379,7 +406,7 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 }
 
