@@ -469,14 +469,33 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
     __shared__ __attribute__((aligned(16))) float VNx32[want_h ? 2 : 1][want_h ? 4 : 1][want_h ? 256 : 4];
     __shared__ uint32_t pf_sink[64];                                     // checksum of the L2 warm-up loads (never read)
 
-    // XCD-aware placement: each XCD takes a contiguous run of (unit, head,
-    // column tile) triples, so the workgroups that read the same K and Q
-    // tiles share one L2.
+    // XCD-aware placement. Workgroups go to the eight XCDs round-robin by
+    // linear id. A unit is the (sequence, q/k head) pair whose workgroups (the
+    // group's value heads x the column tiles) read the same K and Q tiles; the
+    // workgroups of a unit go to one XCD, consecutively, so they share its L2.
+    // Units are dealt to the XCDs in snake order (0..7, 7..0, ...) over
+    // (sequence, q/k head), so every XCD gets the same share of every
+    // sequence's heads and sequences of different lengths do not leave one
+    // XCD with the longest ones. Otherwise (a unit count not a multiple of 8)
+    // each XCD takes a contiguous run of (sequence, head, column tile) triples.
     int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
     {
         const int64_t W = (int64_t)gridDim.x * gridDim.y * gridDim.z;
-        if (W % 8 == 0) {
-            const int64_t lin = bx + (int64_t)gridDim.x * (by + (int64_t)gridDim.y * bz);
+        const int64_t lin = bx + (int64_t)gridDim.x * (by + (int64_t)gridDim.y * bz);
+        const int G = Nv / Nk;
+        const int per_unit = G * gridDim.z;                   // workgroups of a unit
+        const int64_t units = (int64_t)gridDim.x * Nk;
+        if (units % 8 == 0) {
+            const int x = (int)(lin % 8);
+            const int64_t i = lin / 8;                        // position in the XCD's list
+            const int64_t lu = i / per_unit;                  // the XCD's lu-th unit
+            const int j = (int)(i % per_unit);
+            const int64_t rank = lu * 8 + ((lu & 1) ? 7 - x : x);
+            bx = (int)(rank / Nk);
+            const int kh_u = (int)(rank % Nk);
+            by = kh_u * G + j / gridDim.z;
+            bz = j % gridDim.z;
+        } else if (W % 8 == 0) {
             const int64_t work = (lin % 8) * (W / 8) + lin / 8;
             bz = (int)(work % gridDim.z);
             by = (int)((work / gridDim.z) % gridDim.y);
