@@ -8,8 +8,9 @@ bf16 q/k/v/beta, fp32 gates (g = logsigmoid(N(6, 1))) and state, S0 = 0,
 seeded synthetic data. Inputs are resident in HBM before the timed region.
 
 Prints one JSON line with the throughput (tokens/s), the roofline of the
-dominant kernel (its average duration measured with HIP events recorded on
-the launch stream inside the timed region), and the CPU oracle timed on a
+dominant kernel (its average duration measured with the two HIP events that
+each timed step records around it on the launch stream), the per-stage times
+(from steps outside the timed region), and the CPU oracle timed on a
 bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -440,34 +441,35 @@ def bench_recurrent(args) -> None:
     }), flush=True)
 
 
+def _stage_breakdown(fwd, K):
+    """Mean ms of each forward stage (HIP events at every stage boundary)
+    over K calls. Each recorded event adds a few microseconds between two
+    launches, so these calls are kept out of the timed regions."""
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(api.NUM_STAGES + 1)] for _ in range(K)]
+    for row in events:                     # create the HIP events before use
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for s in range(K):
+        fwd.timed(events[s])
+    torch.cuda.synchronize()
+    return np.array([[events[s][i].elapsed_time(events[s][i + 1]) for i in range(api.NUM_STAGES)]
+                     for s in range(K)]).mean(axis=0)
+
+
 def _time_forward(fwd, K, W):
-    """Mean ms per forward and per stage (HIP events) over K timed calls
-    (stages: None for a call that records no stage events)."""
+    """Mean ms per forward over K timed calls (no events inside), and per
+    stage from K more calls (None for a call that records no stage events)."""
     for _ in range(W):
         fwd()
     torch.cuda.synchronize()
-    if not fwd.stage_events:
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record()
-        for _ in range(K):
-            fwd()
-        end.record()
-        torch.cuda.synchronize()
-        return start.elapsed_time(end) / K, None
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(api.NUM_STAGES + 1)] for _ in range(K)]
-    for row in events:
-        for e in row:
-            e.record()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     start.record()
-    for s in range(K):
-        fwd.timed(events[s])
+    for _ in range(K):
+        fwd()
     end.record()
     torch.cuda.synchronize()
-    stage_ms = np.array([[events[s][i].elapsed_time(events[s][i + 1]) for i in range(api.NUM_STAGES)]
-                         for s in range(K)]).mean(axis=0)
-    return start.elapsed_time(end) / K, stage_ms
+    return start.elapsed_time(end) / K, (_stage_breakdown(fwd, K) if fwd.stage_events else None)
 
 
 def bench_chunk_sizes(args) -> None:
@@ -760,32 +762,37 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(api.NUM_STAGES + 1)] for _ in range(K)]
-    for row in events:                     # create the HIP events before timing
-        for e in row:
-            e.record()
+    # per-stage times from K calls outside the timed region; they name the
+    # dominant stage
+    stage_ms = _stage_breakdown(fwd, K)
+    dom = int(np.argmax(stage_ms))
+    # timed region: K calls that record only the two events around the
+    # dominant stage, whose launch time the roofline line divides by
+    pairs = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(K)]
+    for a, b in pairs:
+        a.record()
+        b.record()
+    timed_events = [[None] * dom + [a, b] + [None] * (api.NUM_STAGES - dom - 1) for a, b in pairs]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for s in range(K):
-        fwd.timed(events[s])
+        fwd.timed(timed_events[s])
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / K
-    stage_ms = np.array([[events[s][i].elapsed_time(events[s][i + 1]) for i in range(api.NUM_STAGES)]
-                         for s in range(K)]).mean(axis=0)
+    dom_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
 
     out_bytes = 4 if (args.out_dtype == "f32" or w.dtype == "f32") else 2
     io = stage_io_bytes(w, Ttot, N, NT, out_bytes, inp["S0"] is not None)
     names = FP16_STAGE_KERNELS if w.dtype == "bf16" else STAGE_KERNELS
-    dom = int(np.argmax(stage_ms))
     kname = names[dom]
     bpt = method_bytes_per_token(w, out_bytes)
     fpt = method_flops_per_token(w)
     alg_bytes = bpt * Ttot
     alg_flops = fpt * Ttot
-    achieved = alg_bytes / (stage_ms[dom] * 1e-3) / 1e9
+    achieved = alg_bytes / (dom_ms * 1e-3) / 1e9
     traffic = counter_traffic(kname, "T65536_Nk16_Nv32_d128" if args.workload == 5 else "workload%d" % args.workload)
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
     peaks = measure_peaks() if args.peaks else None
@@ -824,9 +831,9 @@ def main():
         # dominant kernel: the method's algorithmic bytes over its average launch time
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes": alg_bytes, "bytes_per_token": bpt, "avg_ms": float(stage_ms[dom]),
+                     "algorithmic_bytes": alg_bytes, "bytes_per_token": bpt, "avg_ms": dom_ms,
                      "kernel_io_bytes": io[kname],
-                     "mfma_frac": alg_flops / (stage_ms[dom] * 1e-3) / 1e12 / mfma_peak},
+                     "mfma_frac": alg_flops / (dom_ms * 1e-3) / 1e12 / mfma_peak},
         "end_to_end": e2e,
         "measured_peaks": peaks,
         "cpu_baseline": cpu,

@@ -364,8 +364,10 @@ class Backward:
     def timed(self, events):
         """Enqueue one backward and record the BWD_NUM_STAGES + 1
         torch.cuda.Event objects around its stages (recorded once beforehand,
-        so that their HIP handles exist)."""
-        handles = (ctypes.c_void_p * (BWD_NUM_STAGES + 1))(*[e.cuda_event for e in events])
+        so that their HIP handles exist); a None entry is not recorded."""
+        if len(events) != BWD_NUM_STAGES + 1:
+            raise ValueError("timed() takes %d events, got %d" % (BWD_NUM_STAGES + 1, len(events)))
+        handles = (ctypes.c_void_p * (BWD_NUM_STAGES + 1))(*[None if e is None else e.cuda_event for e in events])
         _check(self.lib.gdr_chunk_bwd(*self.args, handles))
 
 
@@ -459,8 +461,10 @@ class Forward:
     def timed(self, events):
         """Enqueue one forward and record the NUM_STAGES + 1 torch.cuda.Event
         objects around its stages (they must have been recorded once, so that
-        their HIP handles exist)."""
-        handles = (ctypes.c_void_p * (NUM_STAGES + 1))(*[e.cuda_event for e in events])
+        their HIP handles exist); a None entry is not recorded."""
+        if len(events) != NUM_STAGES + 1:
+            raise ValueError("timed() takes %d events, got %d" % (NUM_STAGES + 1, len(events)))
+        handles = (ctypes.c_void_p * (NUM_STAGES + 1))(*[None if e is None else e.cuda_event for e in events])
         if self.segment_chunks is None:
             _check(self.lib.gdr_chunk_fwd_timed(*self.args, handles))
         else:

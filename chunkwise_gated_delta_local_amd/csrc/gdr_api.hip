@@ -495,12 +495,8 @@ gdr_status_t gdr_chunk_fwd_segmented(const gdr_problem_t* p, const void* q, cons
                                      void* const* stage_events) {
     if (segment_chunks < 0) return fail(GDR_ERR_SHAPE, "segment_chunks must be >= 0 (got %d)", segment_chunks);
     hipEvent_t ev[GDR_NUM_STAGES + 1];
-    if (stage_events) {
-        for (int i = 0; i <= GDR_NUM_STAGES; ++i) {
-            if (!stage_events[i]) return fail(GDR_ERR_NULL, "stage_events[%d] is NULL", i);
-            ev[i] = static_cast<hipEvent_t>(stage_events[i]);
-        }
-    }
+    if (stage_events)
+        for (int i = 0; i <= GDR_NUM_STAGES; ++i) ev[i] = static_cast<hipEvent_t>(stage_events[i]);
     return run(p, q, k, v, g, beta, scale, initial_state, cu_dev, cu_host, o, final_state, workspace,
                workspace_bytes, stream, stage_events ? ev : nullptr, false, nullptr, nullptr, segment_chunks);
 }
@@ -519,12 +515,8 @@ gdr_status_t gdr_chunk_bwd(const gdr_problem_t* p, const void* q, const void* k,
                            float* dk, float* dv, float* dbeta, float* dg, float* d_initial_state, void* workspace,
                            size_t workspace_bytes, void* stream, void* const* stage_events) {
     hipEvent_t ev[GDR_BWD_NUM_STAGES + 1];
-    if (stage_events) {
-        for (int i = 0; i <= GDR_BWD_NUM_STAGES; ++i) {
-            if (!stage_events[i]) return fail(GDR_ERR_NULL, "stage_events[%d] is NULL", i);
-            ev[i] = static_cast<hipEvent_t>(stage_events[i]);
-        }
-    }
+    if (stage_events)
+        for (int i = 0; i <= GDR_BWD_NUM_STAGES; ++i) ev[i] = static_cast<hipEvent_t>(stage_events[i]);
     gdr_status_t st = check_inputs(p, q, k, v, g, beta, initial_state, cu_dev, cu_host, workspace);
     if (st != GDR_OK) return st;
     const int64_t Ttot = p->batch * p->seq_len;
@@ -591,10 +583,7 @@ gdr_status_t gdr_chunk_fwd_timed(const gdr_problem_t* p, const void* q, const vo
                                  void* workspace, size_t workspace_bytes, void* stream, void* const* stage_events) {
     if (!stage_events) return fail(GDR_ERR_NULL, "stage_events is NULL");
     hipEvent_t ev[GDR_NUM_STAGES + 1];
-    for (int i = 0; i <= GDR_NUM_STAGES; ++i) {
-        if (!stage_events[i]) return fail(GDR_ERR_NULL, "stage_events[%d] is NULL", i);
-        ev[i] = static_cast<hipEvent_t>(stage_events[i]);
-    }
+    for (int i = 0; i <= GDR_NUM_STAGES; ++i) ev[i] = static_cast<hipEvent_t>(stage_events[i]);
     return run(p, q, k, v, g, beta, scale, initial_state, cu_dev, cu_host, o, final_state, workspace,
                workspace_bytes, stream, ev, false, nullptr, nullptr);
 }

@@ -1094,7 +1094,7 @@ template <typename T, int DK, int DV, int C>
 hipError_t launch_bwd(const BackwardArgs& b) {
     const LaunchArgs& a = b.fwd;
     hipStream_t st = a.stream;
-    auto mark = [&](int i) { if (b.events) (void)hipEventRecord(b.events[i], st); };
+    auto mark = [&](int i) { if (b.events && b.events[i]) (void)hipEventRecord(b.events[i], st); };
     mark(0);
     LaunchArgs f = a;
     if (!f.states16) f.T16 = nullptr;            // the fp16 path's T, score block and decay rows are not needed

@@ -1023,7 +1023,7 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
 template <int DK, int DV>
 static hipError_t launch_dims(const LaunchArgs& a, hipEvent_t* ev) {
     hipStream_t st = a.stream;
-    auto mark = [&](int i) { if (ev) (void)hipEventRecord(ev[i], st); };
+    auto mark = [&](int i) { if (ev && ev[i]) (void)hipEventRecord(ev[i], st); };
     const int32_t NT = a.nt;
     const bf16 *q = (const bf16*)a.q, *k = (const bf16*)a.k, *v = (const bf16*)a.v;
     f16* Tf = (f16*)a.T16;

@@ -802,7 +802,7 @@ hipError_t launch_segment_scan(const LaunchArgs& a) {
 template <typename T, int DK, int DV, int C>
 static hipError_t launch_pipeline(const LaunchArgs& a, hipEvent_t* ev) {
     hipStream_t st = a.stream;
-    auto mark = [&](int i) { if (ev) (void)hipEventRecord(ev[i], st); };
+    auto mark = [&](int i) { if (ev && ev[i]) (void)hipEventRecord(ev[i], st); };
     const int32_t cap = a.nt_cap;
     const int32_t NT = a.nt;
     constexpr bool kFp16 = std::is_same<T, bf16>::value && C == 64;

@@ -234,8 +234,8 @@ size_t gdr_chunk_fwd_noalloc_max_workspace(void);
  *                   head_dim_v / 16); otherwise it runs the serial pass.
  *                   When no sequence spans more than one segment, the serial
  *                   pass runs too. Negative: GDR_ERR_SHAPE.
- *   stage_events    NULL, or GDR_NUM_STAGES + 1 events recorded as for
- *                   gdr_chunk_fwd_timed; stage [5] covers all four segment
+ *   stage_events    NULL, or GDR_NUM_STAGES + 1 events (NULL entries
+ *                   skipped) recorded as for gdr_chunk_fwd_timed; stage [5] covers all four segment
  *                   launches (the two side-by-side passes, the scan, the
  *                   output pass).
  *   workspace       at least gdr_chunk_fwd_segmented_workspace_size bytes for
@@ -278,7 +278,7 @@ gdr_status_t gdr_chunk_fwd_segmented(const gdr_problem_t* problem,
  *   d_initial_state [N][Nv][dk][dv] fp32 out, or NULL to skip.
  *   workspace      at least gdr_chunk_bwd_workspace_size bytes, 256-byte aligned.
  *   stage_events   NULL, or GDR_BWD_NUM_STAGES + 1 caller-created events
- *                  recorded on `stream`: [0] before the first kernel and [i]
+ *                  (NULL entries skipped) recorded on `stream`: [0] before the first kernel and [i]
  *                  after stage i: [1] forward recompute (five kernels), [2]
  *                  preparation (layouts, score block), [3] reverse state
  *                  pass, [4] per-chunk gradients, [5] sum of dq and dk over
@@ -387,9 +387,11 @@ gdr_status_t gdr_chunk_fwd_debug(const gdr_problem_t* problem,
  * table, [2] gate prefix sums, [3] A-build + solve, [4] w/u, [5] state pass,
  * [6] output. On the bf16 C = 64 path stages [2], [4] and [6] launch nothing:
  * [3] is the preparation kernel (gate sums included) and [5] the chunk-serial
- * pass with the w/u products and the output. Nothing is synchronised; the caller reads the elapsed
- * times once the stream has passed the last event. Used to time each kernel
- * inside a benchmark's timed region.
+ * pass with the w/u products and the output. A NULL entry is skipped (that
+ * event is not recorded), so a timed loop can bracket one stage alone: each
+ * recorded event puts a few microseconds between two launches. Nothing is
+ * synchronised; the caller reads the elapsed times once the stream has passed
+ * the last event. Used to time each kernel inside a benchmark's timed region.
  */
 gdr_status_t gdr_chunk_fwd_timed(const gdr_problem_t* problem,
                                  const void* q, const void* k, const void* v,
