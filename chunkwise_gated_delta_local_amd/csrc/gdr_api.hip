@@ -7,6 +7,7 @@
 #include <mutex>
 
 #include "gdr.h"
+#include "gdr_fp16.hpp"
 #include "gdr_launch.hpp"
 
 namespace {
@@ -110,7 +111,7 @@ Plan make_plan(const gdr_problem_t* p) {
     pl.off_first = take(((size_t)p->num_seqs + 1) * 4);
     const bool fused = fused_path(p);
     pl.sz_R16 = fused ? Nv * 2 * 64 * 4 : 0;      // exp(G), exp(G_last - G) per position
-    pl.sz_T16 = fused ? Nv * 6 * 512 * 2 : 0;     // six fp16 pair fragments
+    pl.sz_T16 = fused ? Nv * gdr::kPackedPairs * 2 : 0;   // six fp16 pair fragments, two of them halved
     pl.off_R16 = take(cap * pl.sz_R16);
     pl.off_T16 = take(cap * pl.sz_T16);
     pl.off_P16 = take(cap * pl.sz_T16);
@@ -465,13 +466,20 @@ gdr_status_t gdr_chunk_fwd_debug(const gdr_problem_t* p, const void* q, const vo
         {dbg->KT, pl.off_KT, (size_t)nt * pl.sz_KT},
         {dbg->H, pl.off_H, (size_t)nt * pl.sz_H},
         {dbg->VN, pl.off_VN, (size_t)nt * pl.sz_VN},
-        {dbg->T, pl.off_T16, (size_t)nt * pl.sz_T16},
-        {dbg->P, pl.off_P16, (size_t)nt * pl.sz_T16},
         {dbg->R, pl.off_R16, (size_t)nt * pl.sz_R16},
     };
     for (auto& c : copies) {
         if (!c.dst || c.bytes == 0) continue;
         hipError_t e = hipMemcpyAsync(c.dst, w + c.off, c.bytes, hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return fail(GDR_ERR_HIP, "intermediate copy failed: %s", hipGetErrorString(e));
+    }
+    // T and P: the workspace holds the pair sets packed; the copies get all six fragments
+    const struct { void* dst; size_t off; } pairs[] = {{dbg->T, pl.off_T16}, {dbg->P, pl.off_P16}};
+    for (auto& c : pairs) {
+        if (!c.dst || pl.sz_T16 == 0 || nt == 0) continue;
+        if (reinterpret_cast<uintptr_t>(c.dst) % 16)
+            return fail(GDR_ERR_SHAPE, "dbg->T and dbg->P must be 16-byte aligned");
+        hipError_t e = gdr::unpack_pairs16(w + c.off, c.dst, (int64_t)nt * p->num_v_heads, s);
         if (e != hipSuccess) return fail(GDR_ERR_HIP, "intermediate copy failed: %s", hipGetErrorString(e));
     }
     return GDR_OK;

@@ -64,6 +64,14 @@ constexpr int kPairs = 6;      // lower-triangular (16-row block, 32-position bl
 __device__ __forceinline__ int pair_tb(int p) { return p < 2 ? p : (p + 2) >> 1; }
 __device__ __forceinline__ int pair_tp(int p) { return p < 2 ? 0 : (p - 2) & 1; }
 constexpr int kFrag = 512;     // elements of one pair fragment (64 lanes x 8)
+// In global memory the six pairs of one (chunk, value head) are packed
+// (kPackedPairs values): pairs 0 and 3 sit on the diagonal of an even row
+// block, so their positions 16..31 (lane elements 4..7) lie above the
+// diagonal and are zero; each keeps only elements 0..3 of every lane (lane l
+// at values 4 l .. 4 l + 3). Pair p starts at value pair_off(p).
+__host__ __device__ constexpr bool pair_half(int p) { return p == 0 || p == 3; }
+__host__ __device__ constexpr int pair_off(int p) { return 512 * p - (p >= 1 ? 256 : 0) - (p >= 4 ? 256 : 0); }
+static_assert(pair_off(kPairs - 1) + kFrag == kPackedPairs, "packed pair layout");
 constexpr int kRsrc = 0x00020000;   // buffer descriptor word 3: raw 32-bit access
 
 __device__ __forceinline__ f32x4 mfma16(const h8& a, const h8& b, f32x4 c) {
@@ -109,6 +117,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int6
 __device__ __forceinline__ u4 buf_load16(__amdgpu_buffer_rsrc_t rs, int voff) {
     return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
 }
+__device__ __forceinline__ u2 buf_load8(__amdgpu_buffer_rsrc_t rs, int voff) {
+    return __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, 0, 0));
+}
+// a packed half pair's four values per lane -> the lane's pair fragment (elements 4..7 zero)
+__device__ __forceinline__ h8 half_pair(u2 lo) { return __builtin_bit_cast(h8, u4{lo[0], lo[1], 0u, 0u}); }
 
 // fp16 K and Q tiles (64 rows of DK values per chunk and q/k head): the 16-byte
 // unit u of row `row` sits at unit u ^ tile_swz(row), in global memory as in
@@ -381,7 +394,11 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
                 x0[e] = (row < L && m0 + e <= row) ? a0[e] * b0[e] : 0.f;
                 x1[e] = (row < L && m0 + 16 + e <= row) ? a1[e] * b1[e] : 0.f;
             }
-            *reinterpret_cast<h8*>(Tf + (((int64_t)c * Nv + h) * kPairs + p) * kFrag + lane * 8) = pack_pair(x0, x1);
+            f16* dst = Tf + ((int64_t)c * Nv + h) * kPackedPairs + pair_off(p);
+            if (pair_half(p))
+                *reinterpret_cast<u2*>(dst + lane * 4) = pack4(x0);
+            else
+                *reinterpret_cast<h8*>(dst + lane * 8) = pack_pair(x0, x1);
         }
         if constexpr (WITH_P) {
             //     P pairs of block row `wave` (rows i = 16 wave + r): the transposed
@@ -400,9 +417,14 @@ __global__ __launch_bounds__(256, 4) void k_prep(const bf16* __restrict__ k, con
                 const int pbase = (wave == 0) ? 0 : (wave == 1 ? 1 : (wave == 2 ? 2 : 4));
     #pragma unroll
                 for (int tp = 0; tp < 2; ++tp) {
-                    if (2 * tp <= wave)
-                        *reinterpret_cast<h8*>(Pf + (((int64_t)c * Nv + h) * kPairs + pbase + tp) * kFrag + lane * 8) =
-                            pack_pair(pt[2 * tp], pt[2 * tp + 1]);
+                    if (2 * tp <= wave) {
+                        const int p = pbase + tp;
+                        f16* dst = Pf + ((int64_t)c * Nv + h) * kPackedPairs + pair_off(p);
+                        if (pair_half(p))
+                            *reinterpret_cast<u2*>(dst + lane * 4) = pack4(pt[2 * tp]);
+                        else
+                            *reinterpret_cast<h8*>(dst + lane * 8) = pack_pair(pt[2 * tp], pt[2 * tp + 1]);
+                    }
                 }
             }
         }
@@ -602,7 +624,9 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
             TR x;
             const int sl = slot4(c);
 #pragma unroll
-            for (int p = 0; p < kPairs; ++p) x.tf[p] = *reinterpret_cast<const h8*>(&Ts[sl][p * kFrag + lane * 8]);
+            for (int p = 0; p < kPairs; ++p)
+                x.tf[p] = pair_half(p) ? half_pair(*reinterpret_cast<const u2*>(&Ts[sl][p * kFrag + lane * 4]))
+                                       : *reinterpret_cast<const h8*>(&Ts[sl][p * kFrag + lane * 8]);
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 x.eg[b] = *reinterpret_cast<const f32x4*>(&Rs[sl][16 * b + 4 * qd]);
@@ -635,7 +659,7 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
         bool pf_on = false;
         if constexpr (want_pf) {
             constexpr int NB = DV / 16, LT = C * DK * 2 / 128;                  // column tiles; lines of a K/Q tile
-            constexpr int LTP = kPairs * kFrag * 2 / 128, LR = 2 * C * 4 / 128;  // lines of T (and P); of R
+            constexpr int LTP = kPackedPairs * 2 / 128, LR = 2 * C * 4 / 128;    // lines of T (and P); of R
             constexpr int VL = DV * 2 >= 128 ? DV * 2 / 128 : 1;                 // lines of a V row
             constexpr int NVL = NPT * LTP + LR + C * VL;                         // lines per value head
             const int G = Nv / Nk, U = G * NB, u = (h % G) * NB + nb;
@@ -654,8 +678,8 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
                 if (j < NPT * LTP) {
                     const f16* t = j < LTP ? Tf : Pf;
                     pf_base = reinterpret_cast<const char*>(t);
-                    pf_off = (int64_t)h * kPairs * kFrag * 2 + (int64_t)(j % LTP) * 128;
-                    pf_stride = (int64_t)Nv * kPairs * kFrag * 2;
+                    pf_off = (int64_t)h * kPackedPairs * 2 + (int64_t)(j % LTP) * 128;
+                    pf_stride = (int64_t)Nv * kPackedPairs * 2;
                 } else if (j < NPT * LTP + LR) {
                     pf_base = reinterpret_cast<const char*>(R);
                     pf_off = (int64_t)h * 2 * C * 4 + (int64_t)(j - NPT * LTP) * 128;
@@ -849,14 +873,19 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
             const auto rr = rsrc_of(R, (ok ? (int64_t)c * Nv + h : 0) * 2 * C * 4, ok ? 2 * C * 4 : 0u);
             buffer_to_lds16(rr, &Rs[slot4(c)][0], lane * 16);
         };
-        // ---- T pairs of a chunk -> LDS: pairs 0..2 (wavefront 2) or 3..5 (wavefront 3)
+        // ---- T pairs of a chunk -> LDS: pairs 0..2 (wavefront 2) or 3..5 (wavefront 3),
+        //      each into its own 1024-byte slot; a packed half pair (512 bytes)
+        //      comes from lanes 0..31, and lanes 32..63 read past the buffer and
+        //      write zeros to the slot's second half, which nothing reads
         auto copy_t = [&](int c) {
             const bool ok = c < c1;
-            const auto rt = rsrc_of(Tf, (ok ? (int64_t)c * Nv + h : 0) * kPairs * kFrag * 2, ok ? kPairs * kFrag * 2 : 0u);
-            const int p0 = (wv - 2) * (kPairs / 2);
+            const auto rt = rsrc_of(Tf, (ok ? (int64_t)c * Nv + h : 0) * kPackedPairs * 2, ok ? kPackedPairs * 2 : 0u);
+            constexpr int p0 = ROLE == 3 ? kPairs / 2 : 0;
 #pragma unroll
-            for (int p = p0; p < p0 + kPairs / 2; ++p)
-                buffer_to_lds16(rt, &Ts[slot4(c)][p * kFrag], p * kFrag * 2 + lane * 16);
+            for (int p = p0; p < p0 + kPairs / 2; ++p) {
+                const int voff = (pair_half(p) && lane >= 32) ? kPackedPairs * 2 : pair_off(p) * 2 + lane * 16;
+                buffer_to_lds16(rt, &Ts[slot4(c)][p * kFrag], voff);
+            }
         };
         constexpr int NDMA = ROLE == 1 ? 2 + 1 : DK / 16 + kPairs / 2;    // copies per step
         // ---- output operands: the Q rows (fp16 tile) and score pairs of chunk c,
@@ -883,12 +912,15 @@ __global__ __launch_bounds__(256) void k_chunk16(const bf16* __restrict__ q, con
         };
         // the two score pairs this wave needs: blocks 0 and 1 (pairs 0, 1) or
         // block b >= 2 (pairs 2 b - 2, 2 b - 1)
-        const int pbase = NBL == 2 ? 0 : 2 * wv - 2;
+        constexpr int pbase = ROLE == 1 ? 0 : 2 * ROLE - 2;
         auto load_p = [&](int c, h8* dst) {
-            const auto rp = rsrc_of(Pf, (c < c1 ? (int64_t)c * Nv + h : 0) * kPairs * kFrag * 2,
-                                    c < c1 ? kPairs * kFrag * 2 : 0u);
+            const auto rp = rsrc_of(Pf, (c < c1 ? (int64_t)c * Nv + h : 0) * kPackedPairs * 2,
+                                    c < c1 ? kPackedPairs * 2 : 0u);
 #pragma unroll
-            for (int p = 0; p < 2; ++p) dst[p] = __builtin_bit_cast(h8, buf_load16(rp, (pbase + p) * kFrag * 2 + lane * 16));
+            for (int p = 0; p < 2; ++p) {
+                dst[p] = pair_half(pbase + p) ? half_pair(buf_load8(rp, pair_off(pbase + p) * 2 + lane * 8))
+                                              : __builtin_bit_cast(h8, buf_load16(rp, pair_off(pbase + p) * 2 + lane * 16));
+            }
         };
         // kStates16: chunk cc's entering state (wavefronts 2, 3: state tiles of
         // their half) as H^T [dv][dk] per chunk and head, and V_new (wavefront 1)
@@ -1081,6 +1113,27 @@ hipError_t launch_fp16_states(const LaunchArgs& a) {
     GDR_CASE(128, 32) GDR_CASE(128, 64) GDR_CASE(128, 128)
 #undef GDR_CASE
     return hipErrorInvalidValue;
+}
+
+// debug copies: packed pair sets -> six 512-value fragments per set, one
+// 16-byte lane unit per thread
+__global__ __launch_bounds__(256) void k_unpack_pairs(const f16* __restrict__ packed, f16* __restrict__ dense,
+                                                      int64_t units) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= units) return;
+    const int64_t set = i / (kPairs * 64);
+    const int rem = (int)(i % (kPairs * 64)), p = rem / 64, l = rem % 64;
+    const f16* src = packed + set * kPackedPairs + pair_off(p);
+    const u4 x = pair_half(p) ? __builtin_bit_cast(u4, half_pair(*reinterpret_cast<const u2*>(src + l * 4)))
+                              : *reinterpret_cast<const u4*>(src + l * 8);
+    *reinterpret_cast<u4*>(dense + (set * kPairs + p) * kFrag + l * 8) = x;
+}
+
+hipError_t unpack_pairs16(const void* packed, void* dense, int64_t sets, hipStream_t stream) {
+    const int64_t units = sets * kPairs * 64;
+    if (units <= 0) return hipSuccess;
+    k_unpack_pairs<<<dim3((unsigned)((units + 255) / 256)), 256, 0, stream>>>((const f16*)packed, (f16*)dense, units);
+    return hipGetLastError();
 }
 
 hipError_t launch_fp16_path(const LaunchArgs& a, hipEvent_t* ev) {

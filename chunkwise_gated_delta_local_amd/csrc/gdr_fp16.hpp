@@ -13,6 +13,15 @@ namespace gdr {
 // state and V_new are written (fp32) instead of the output.
 constexpr int kFull16 = 0, kSegment16 = 1, kStates16 = 2;
 
+// fp16 values of the six T (or score-block) pair fragments of one (chunk,
+// value head) as the workspace holds them: the two pairs whose second half
+// lies above the diagonal keep only their first half (2 x 256 + 4 x 512).
+constexpr int kPackedPairs = 2560;
+
+// Expands `sets` packed pair sets into the six-fragment layout of the debug
+// intermediates (6 x 512 fp16 values per set, the dropped halves zero).
+hipError_t unpack_pairs16(const void* packed, void* dense, int64_t sets, hipStream_t stream);
+
 // Enqueues stages 2..6 of the forward for bf16 inputs with C = 64 (the chunk
 // and segment tables are built by the caller): k_prep, then the chunk pass (or
 // the two segment passes, the scan and the output pass). Records events
