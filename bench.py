@@ -41,7 +41,7 @@ KERNEL_SOURCES = ("chunkwise_gated_delta_local_amd/csrc/gdr_kernels.hip",
                   "chunkwise_gated_delta_local_amd/csrc/gdr_device.hpp")
 STAGE_KERNELS = ("k_chunk_table", "k_gate_cumsum", "k_build_solve", "k_wu", "k_state", "k_output")
 FP16_STAGE_KERNELS = ("k_chunk_table", "(none)", "k_prep", "(none)", "k_chunk16", "(none)")
-FRAG16_BYTES = 6 * 512 * 2              # six fp16 pair fragments per (chunk, value head): T or the score block
+FRAG16_BYTES = (4 * 512 + 2 * 256) * 2  # fp16 pair fragments per (chunk, value head), two of six halved: T or the score block
 DECAY_ROW_BYTES = 2 * 64 * 4            # exp(G), exp(G_last - G) per (chunk, value head)
 
 
@@ -79,8 +79,9 @@ def stage_io_bytes(w: synth.Workload, Ttot: int, N: int, NT: int, out_bytes: int
         rows = NT * Nv * DECAY_ROW_BYTES
         return {
             "k_chunk_table": 4 * (N + 1) + 16 * NT,
-            "k_prep": 2 * tk * dk * es + tv * (beta_b + 4) + 2 * frag + rows,        # k, q, beta, g in; T, P, R out
-            "k_chunk16": 2 * tk * dk * es + tv * dv * es + rows + 2 * frag             # q, k, v, R, T, P in
+            "k_prep": 2 * tk * dk * es + tv * (beta_b + 4) + 2 * frag + rows         # k, q, beta, g in; T, P, R out
+                      + 2 * NT * Nk * 64 * dk * 2,                                      # fp16 K and Q tiles out
+            "k_chunk16": 2 * NT * Nk * 64 * dk * 2 + tv * dv * es + rows + 2 * frag    # K16, Q16, v, R, T, P in
                          + tv * dv * out_bytes + state * (2 if s0 else 1),             # o, S_T out (S0 in)
             "(none)": 0,
         }
