@@ -449,6 +449,8 @@ gdr_status_t gdr_chunk_fwd_debug(const gdr_problem_t* p, const void* q, const vo
                                  const int32_t* cu_dev, const int32_t* cu_host, void* o, float* final_state,
                                  void* workspace, size_t workspace_bytes, void* stream, gdr_intermediates_t* dbg) {
     if (!dbg) return fail(GDR_ERR_NULL, "dbg is NULL");
+    if (reinterpret_cast<uintptr_t>(dbg->T) % 16 || reinterpret_cast<uintptr_t>(dbg->P) % 16)
+        return fail(GDR_ERR_SHAPE, "dbg->T and dbg->P must be 16-byte aligned");
     Plan pl;
     int32_t nt = 0;
     gdr_status_t st = run(p, q, k, v, g, beta, scale, initial_state, cu_dev, cu_host, o, final_state, workspace,
@@ -477,8 +479,6 @@ gdr_status_t gdr_chunk_fwd_debug(const gdr_problem_t* p, const void* q, const vo
     const struct { void* dst; size_t off; } pairs[] = {{dbg->T, pl.off_T16}, {dbg->P, pl.off_P16}};
     for (auto& c : pairs) {
         if (!c.dst || pl.sz_T16 == 0 || nt == 0) continue;
-        if (reinterpret_cast<uintptr_t>(c.dst) % 16)
-            return fail(GDR_ERR_SHAPE, "dbg->T and dbg->P must be 16-byte aligned");
         hipError_t e = gdr::unpack_pairs16(w + c.off, c.dst, (int64_t)nt * p->num_v_heads, s);
         if (e != hipSuccess) return fail(GDR_ERR_HIP, "intermediate copy failed: %s", hipGetErrorString(e));
     }

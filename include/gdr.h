@@ -337,6 +337,8 @@ gdr_status_t gdr_chunk_bwd(const gdr_problem_t* problem,
  *        m = position) for the blocks (tb, tp) = (0,0) (1,0) (2,0) (2,1)
  *        (3,0) (3,1), each value rounded once from fp32 (the operand of the
  *        production pass). bf16 inputs with C = 64 only (NULL otherwise).
+ *        The buffer must be 16-byte aligned (else GDR_ERR_SHAPE before
+ *        anything runs); so must P's.
  *   P    [NT][Nv][6 pairs] fp16 pair fragments of the score block
  *        P = (Q K^T) (.) D, D_ij = exp(G_i - G_j) for j <= i (rows i, m = j),
  *        same blocks and conditions as T.

@@ -140,6 +140,24 @@ def test_fwd_rejects_before_launch(lib):
     assert lib.gdr_chunk_fwd(*bad, fake, ctypes.c_size_t(1 << 40), None) == 1
 
 
+def test_debug_rejects_misaligned_pair_buffers_before_launch(lib):
+    """gdr_chunk_fwd_debug expands the packed T and score-block pairs with
+    16-byte accesses: a misaligned T or P buffer is refused before any work."""
+    from chunkwise_gated_delta_local_amd import api
+    if torch.cuda.is_available():
+        pytest.skip("passes placeholder addresses; host-logic test for machines without a GPU")
+    p = prob()
+    fake = ctypes.c_void_p(1 << 20)          # never dereferenced: rejected first
+    args = [ctypes.byref(p), fake, fake, fake, None, fake, ctypes.c_float(1.0), None, None, None, fake, None,
+            fake, ctypes.c_size_t(1 << 40), None]
+    for field in ("T", "P"):
+        dbg = api.Intermediates()
+        setattr(dbg, field, (1 << 20) + 8)
+        assert lib.gdr_chunk_fwd_debug(*args, ctypes.byref(dbg)) == 2, field
+        assert b"16-byte aligned" in lib.gdr_last_error_message()
+    assert lib.gdr_chunk_fwd_debug(*args, None) == 1
+
+
 def test_binding_refuses_cpu_tensors(lib):
     from chunkwise_gated_delta_local_amd import api
     q = torch.zeros(1, 8, 1, 32)
